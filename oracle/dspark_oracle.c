@@ -1,0 +1,384 @@
+/*
+ * dspark_oracle.c -- plain, slow CPU oracle for the vanilla DSpark low-rank
+ * Markov head.  TEST INFRASTRUCTURE: only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may call it.  It shares no code with the GPU
+ * library.  Build: gcc -O2 -fopenmp -ffp-contract=off (no fast-math), so that
+ * every float operation below is the IEEE operation it is written as.
+ *
+ * Each function names the passage of the DSpark pages that it follows:
+ *   [P5] third-party markov_head.py (raw page): module docstring,
+ *        _sample_tokens, VanillaMarkov and its methods, build_markov_head.
+ *   [P3] NeMo AutoModel "speculative/dspark/markov_head" API page.
+ *   [P1] NeMo AutoModel "models/deepseek_v41/dspark" API page.
+ * Where the pages are silent the reading taken is stated at the function.
+ */
+#include "dspark_oracle.h"
+
+#include <math.h>
+#include <omp.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* Number formats                                                     */
+/* ------------------------------------------------------------------ */
+
+static float bits_to_float(uint32_t u) {
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+static uint32_t float_to_bits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return u;
+}
+
+/* bfloat16 keeps the upper 16 bits of an IEEE binary32 value. */
+static float bf16_to_float(uint16_t h) { return bits_to_float((uint32_t)h << 16); }
+
+/* Round a binary32 value to the nearest bfloat16, ties to the even
+ * neighbour (the rounding torch uses for .to(torch.bfloat16)); every NaN
+ * becomes the canonical quiet NaN 0x7FC0.  Written from the definition:
+ * keep the upper half, then decide from the discarded lower half. */
+uint16_t dspark_oracle_round_bf16(float x) {
+  uint32_t u = float_to_bits(x);
+  if (isnan(x)) return (uint16_t)0x7FC0u;
+  uint32_t kept = u >> 16;
+  uint32_t dropped = u & 0xFFFFu;
+  if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;
+  return (uint16_t)kept; /* a carry out of the mantissa steps the exponent */
+}
+
+/* Value of element i of an array of dtype `dt`, widened exactly to double. */
+static double load_as_double(const void* p, int dt, int64_t i) {
+  if (dt == ORACLE_F32) return (double)((const float*)p)[i];
+  return (double)bf16_to_float(((const uint16_t*)p)[i]);
+}
+
+static float load_as_float(const void* p, int dt, int64_t i) {
+  if (dt == ORACLE_F32) return ((const float*)p)[i];
+  return bf16_to_float(((const uint16_t*)p)[i]);
+}
+
+/* Round a float to dtype dt and return the rounded value as a float. */
+static float round_to(float x, int dt) {
+  if (dt == ORACLE_F32) return x;
+  return bf16_to_float(dspark_oracle_round_bf16(x));
+}
+
+static void store_from_float(void* p, int dt, int64_t i, float x) {
+  /* x is already representable in dt */
+  if (dt == ORACLE_F32)
+    ((float*)p)[i] = x;
+  else
+    ((uint16_t*)p)[i] = (uint16_t)(float_to_bits(x) >> 16);
+}
+
+static int valid_dtype(int dt) { return dt == ORACLE_F32 || dt == ORACLE_BF16; }
+
+/* ------------------------------------------------------------------ */
+/* The bias and the corrected logit  ([P5] module docstring:          */
+/* B(x_{k-1},:) = W2(W1[x_{k-1}]), corrected logit U_k + B)            */
+/* ------------------------------------------------------------------ */
+
+/* [P5] VanillaMarkov.get_prev_embeddings: e = W1[x]  (Embedding lookup). */
+static void gather_w1_row(const void* w1, int wdt, int64_t r, int64_t x, double* e) {
+  for (int64_t j = 0; j < r; ++j) e[j] = load_as_double(w1, wdt, x * r + j);
+}
+
+/* [P5] VanillaMarkov.project_bias: Linear(r, V, bias=False) applied to e,
+ * i.e. a_v = sum_j e_j * W2w[v, j] with W2w the Linear weight [V, r].
+ * Reading: fp32 accumulation is modelled by its best value, the double sum
+ * (products of bf16/fp32 values are exact in double) rounded once to fp32.
+ * The Linear emits the weight dtype W. */
+static float projected_bias(const double* e, const double* w2_row, int64_t r) {
+  double a = 0.0;
+  for (int64_t j = 0; j < r; ++j) a += e[j] * w2_row[j];
+  return (float)a;
+}
+
+/* [P5] apply_step_logits / apply_block_logits: logits + bias.to(logits.dtype).
+ * Reading: the bias is first rounded to W (Linear output), then to L (the
+ * .to cast), then added in fp32 and rounded once to L (torch's
+ * reduced-precision add: upcast, add, round). */
+static float corrected_value(float base_v, float acc_v, int ldt, int wdt) {
+  float bias = round_to(round_to(acc_v, wdt), ldt);
+  float sum = base_v + bias;
+  return round_to(sum, ldt);
+}
+
+/* W2w converted once to double, [V, r]. */
+static double* w2_as_double(const void* w2, int wdt, int64_t V, int64_t r) {
+  double* d = (double*)malloc((size_t)(V * r) * sizeof(double));
+  if (!d) return NULL;
+  for (int64_t i = 0; i < V * r; ++i) d[i] = load_as_double(w2, wdt, i);
+  return d;
+}
+
+/* One corrected row: base row (length V, dtype ldt) biased by token x.
+ * Writes the L-typed results as floats into out[V]. */
+static void corrected_row(const void* base, int ldt, int64_t base_row,
+                          const void* w1, const double* w2d, int wdt, int64_t V,
+                          int64_t r, int64_t x, double* e, float* out) {
+  gather_w1_row(w1, wdt, r, x, e);
+  for (int64_t v = 0; v < V; ++v) {
+    float acc = projected_bias(e, w2d + v * r, r);
+    float b = load_as_float(base, ldt, base_row * V + v);
+    out[v] = corrected_value(b, acc, ldt, wdt);
+  }
+}
+
+static int n_threads_or_default(int n) { return n > 0 ? n : omp_get_max_threads(); }
+
+/* [P5] VanillaMarkov.apply_block_logits (teacher-forced): every row (b, k)
+ * is biased by its own token_ids[b, k].  Shape-agnostic over leading dims,
+ * so [B, M] rows are processed independently.  An empty input (numel()==0
+ * or M==0) returns the input unchanged: nothing is written.
+ * [P5] VanillaMarkov.__init__ asserts markov_rank > 0: r <= 0 is invalid.
+ * Out-of-range ids (the Embedding lookup would raise) are invalid. */
+int dspark_oracle_apply_block(const void* base_logits, int logits_dtype,
+                              const int64_t* token_ids, const void* w1,
+                              const void* w2, int weight_dtype, int64_t B,
+                              int64_t M, int64_t V, int64_t r,
+                              void* corrected_logits, int n_threads) {
+  if (!valid_dtype(logits_dtype) || !valid_dtype(weight_dtype)) return ORACLE_UNSUPPORTED;
+  if (B < 0 || M < 0 || V < 0 || r <= 0) return ORACLE_INVALID;
+  int64_t rows = B * M;
+  if (rows == 0 || V == 0) return ORACLE_OK; /* numel() == 0: return base */
+  if (!base_logits || !token_ids || !w1 || !w2 || !corrected_logits) return ORACLE_INVALID;
+  for (int64_t n = 0; n < rows; ++n)
+    if (token_ids[n] < 0 || token_ids[n] >= V) return ORACLE_INVALID;
+
+  double* w2d = w2_as_double(w2, weight_dtype, V, r);
+  if (!w2d) return ORACLE_INVALID;
+  int nt = n_threads_or_default(n_threads);
+#pragma omp parallel num_threads(nt)
+  {
+    double* e = (double*)malloc((size_t)r * sizeof(double));
+    float* out = (float*)malloc((size_t)V * sizeof(float));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t n = 0; n < rows; ++n) {
+      corrected_row(base_logits, logits_dtype, n, w1, w2d, weight_dtype, V, r,
+                    token_ids[n], e, out);
+      for (int64_t v = 0; v < V; ++v)
+        store_from_float(corrected_logits, logits_dtype, n * V + v, out[v]);
+    }
+    free(out);
+    free(e);
+  }
+  free(w2d);
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Sampling ([P5] _sample_tokens)                                      */
+/* ------------------------------------------------------------------ */
+
+/* Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and
+ * Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11): ten rounds;
+ * each round multiplies words 0 and 2 by the Philox multipliers, swaps and
+ * xors the high halves with the other words and the round key; the key is
+ * advanced by the Weyl constants (golden ratio, sqrt(3)-1) between rounds. */
+void dspark_oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2],
+                                 uint32_t out[4]) {
+  const uint32_t mul0 = 0xD2511F53u, mul1 = 0xCD9E8D57u;
+  const uint32_t weyl0 = 0x9E3779B9u, weyl1 = 0xBB67AE85u;
+  uint32_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += weyl0;
+      k1 += weyl1;
+    }
+    uint64_t p0 = (uint64_t)mul0 * (uint64_t)x0;
+    uint64_t p2 = (uint64_t)mul1 * (uint64_t)x2;
+    uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    uint32_t hi2 = (uint32_t)(p2 >> 32), lo2 = (uint32_t)p2;
+    uint32_t y0 = hi2 ^ x1 ^ k0;
+    uint32_t y1 = lo2;
+    uint32_t y2 = hi0 ^ x3 ^ k1;
+    uint32_t y3 = lo0;
+    x0 = y0;
+    x1 = y1;
+    x2 = y2;
+    x3 = y3;
+  }
+  out[0] = x0;
+  out[1] = x1;
+  out[2] = x2;
+  out[3] = x3;
+}
+
+/* Base-2 Gumbel noise for vocabulary entry v of row (b_abs, k_abs).
+ * Reading (the pages draw with torch.multinomial, which no two devices
+ * reproduce): the 32-bit word (v mod 4) of Philox4x32-10 with counter
+ * (v div 4, k_abs, b_abs, 0) and key (low, high halves of seed) gives the
+ * odd 24-bit uniform u = (2*(w >> 9) + 1) * 2^-24, which is never 0 or 1;
+ * the noise is -log2(-log2(u)). */
+float dspark_oracle_gumbel2(uint64_t seed, int64_t b_abs, int64_t k_abs, int64_t v) {
+  uint32_t ctr[4] = {(uint32_t)((uint64_t)v >> 2), (uint32_t)k_abs, (uint32_t)b_abs, 0u};
+  uint32_t key[2] = {(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32)};
+  uint32_t w[4];
+  dspark_oracle_philox4x32_10(ctr, key, w);
+  uint32_t word = w[v & 3];
+  float u = ldexpf((float)(2u * (word >> 9) + 1u), -24);
+  return -log2f(-log2f(u));
+}
+
+/* Scale of the base-2 Gumbel-max score: log2(e)/T computed in double and
+ * rounded once to fp32. */
+float dspark_oracle_kappa(double temperature) {
+  return (float)(1.4426950408889634 / temperature);
+}
+
+/* True when a ranks above b under argmax: NaN above everything (torch's
+ * argmax returns a NaN's index), otherwise the usual order; +0 and -0 tie. */
+static int ranks_above(float a, float b) {
+  if (isnan(b)) return 0;
+  if (isnan(a)) return 1;
+  return a > b;
+}
+
+/* [P5] _sample_tokens.  Greedy when temperature < 1e-5 (the pages also map
+ * None to greedy): argmax over the L-typed corrected values, first index on
+ * ties (torch.argmax's convention).  Otherwise the pages draw one sample
+ * from softmax(logits / T); this oracle draws the same law by Gumbel-max:
+ * the smallest v maximising fmaf(c_v, log2(e)/T, g_v), which is argmax of
+ * c_v/T + Gumbel noise scaled by log2(e) (Gumbel 1954; Maddison, Tarlow and
+ * Minka 2014). */
+static void select_from_row(const float* c, int64_t V, double temperature,
+                            uint64_t seed, int64_t b_abs, int64_t k_abs,
+                            int64_t* token, float* best_second, int64_t* second_idx) {
+  int greedy = temperature < 1e-5;
+  float kappa = greedy ? 0.0f : dspark_oracle_kappa(temperature);
+  int64_t best = -1, second = -1;
+  float sb = 0.0f, ss = 0.0f;
+  for (int64_t v = 0; v < V; ++v) {
+    float s = greedy ? c[v] : fmaf(c[v], kappa, dspark_oracle_gumbel2(seed, b_abs, k_abs, v));
+    if (best < 0 || ranks_above(s, sb)) {
+      second = best;
+      ss = sb;
+      best = v;
+      sb = s;
+    } else if (second < 0 || ranks_above(s, ss)) {
+      second = v;
+      ss = s;
+    }
+  }
+  *token = best;
+  if (best_second) {
+    best_second[0] = sb;
+    best_second[1] = ss;
+  }
+  if (second_idx) *second_idx = second;
+}
+
+int dspark_oracle_select_token(const void* row, int logits_dtype, int64_t V,
+                               double temperature, uint64_t seed, int64_t b_abs,
+                               int64_t k_abs, int64_t* token, float* score_out,
+                               int64_t* runner_up) {
+  if (!valid_dtype(logits_dtype)) return ORACLE_UNSUPPORTED;
+  if (!row || !token || V <= 0 || isnan(temperature)) return ORACLE_INVALID;
+  float* c = (float*)malloc((size_t)V * sizeof(float));
+  if (!c) return ORACLE_INVALID;
+  for (int64_t v = 0; v < V; ++v) c[v] = load_as_float(row, logits_dtype, v);
+  select_from_row(c, V, temperature, seed, b_abs, k_abs, token, score_out, runner_up);
+  free(c);
+  return ORACLE_OK;
+}
+
+/* [P5] VanillaMarkov.sample_block_tokens: left to right, step k biases
+ * base[:, k, :] by the previous token (first_prev for k = 0, the token just
+ * drawn at k-1 after that), keeps the corrected row and draws the next token
+ * with _sample_tokens.  proposal_len == 0 returns an empty token array and
+ * the input.  NaN temperature is rejected (reading: the pages would sample
+ * from NaN probabilities). */
+int dspark_oracle_sample_block(const void* base_logits, int logits_dtype,
+                               const int64_t* first_prev_token_ids,
+                               const void* w1, const void* w2, int weight_dtype,
+                               int64_t B, int64_t M, int64_t V, int64_t r,
+                               double temperature, uint64_t seed,
+                               int64_t position_offset, int64_t batch_offset,
+                               int64_t* sampled_tokens, void* corrected_logits,
+                               int n_threads) {
+  if (!valid_dtype(logits_dtype) || !valid_dtype(weight_dtype)) return ORACLE_UNSUPPORTED;
+  if (B < 0 || M < 0 || V < 0 || r <= 0 || isnan(temperature)) return ORACLE_INVALID;
+  if (B == 0 || M == 0) return ORACLE_OK;
+  if (V == 0) return ORACLE_INVALID; /* nothing to draw from */
+  if (!base_logits || !first_prev_token_ids || !w1 || !w2 || !sampled_tokens)
+    return ORACLE_INVALID;
+  for (int64_t b = 0; b < B; ++b)
+    if (first_prev_token_ids[b] < 0 || first_prev_token_ids[b] >= V) return ORACLE_INVALID;
+
+  double* w2d = w2_as_double(w2, weight_dtype, V, r);
+  if (!w2d) return ORACLE_INVALID;
+  int nt = n_threads_or_default(n_threads);
+  for (int64_t k = 0; k < M; ++k) {
+#pragma omp parallel num_threads(nt)
+    {
+      double* e = (double*)malloc((size_t)r * sizeof(double));
+      float* out = (float*)malloc((size_t)V * sizeof(float));
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t b = 0; b < B; ++b) {
+        int64_t prev = (k == 0) ? first_prev_token_ids[b] : sampled_tokens[b * M + k - 1];
+        int64_t row = b * M + k;
+        corrected_row(base_logits, logits_dtype, row, w1, w2d, weight_dtype, V, r, prev, e, out);
+        if (corrected_logits)
+          for (int64_t v = 0; v < V; ++v)
+            store_from_float(corrected_logits, logits_dtype, row * V + v, out[v]);
+        int64_t tok;
+        select_from_row(out, V, temperature, seed, batch_offset + b, position_offset + k,
+                        &tok, NULL, NULL);
+        sampled_tokens[row] = tok;
+      }
+      free(out);
+      free(e);
+    }
+  }
+  free(w2d);
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Admissible interval of one corrected element                        */
+/* ------------------------------------------------------------------ */
+
+/* Reading: a device that accumulates the r products in fp32 in any order
+ * (exact products, up to r roundings) lands within
+ * |acc' - a| <= r * 2^-24 * sum_j |e_j W2w[v,j]|; twice that bound is used.
+ * Every step after the dot product (round to fp32, to W, to L, fp32 add,
+ * round to L) is monotone, so pushing a -/+ delta through it bounds every
+ * admissible result. */
+int dspark_oracle_logit_bounds(const void* base_logits, int logits_dtype,
+                               const int64_t* token_ids, const void* w1,
+                               const void* w2, int weight_dtype, int64_t V,
+                               int64_t r, int64_t n, const int64_t* rows,
+                               const int64_t* cols, float* lo, float* mid,
+                               float* hi) {
+  if (!valid_dtype(logits_dtype) || !valid_dtype(weight_dtype)) return ORACLE_UNSUPPORTED;
+  if (V <= 0 || r <= 0 || n < 0) return ORACLE_INVALID;
+  if (n == 0) return ORACLE_OK;
+  if (!base_logits || !token_ids || !w1 || !w2 || !rows || !cols || !lo || !mid || !hi)
+    return ORACLE_INVALID;
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t row = rows[i], v = cols[i];
+    if (row < 0 || v < 0 || v >= V) return ORACLE_INVALID;
+    int64_t x = token_ids[row];
+    if (x < 0 || x >= V) return ORACLE_INVALID;
+    double a = 0.0, s = 0.0;
+    for (int64_t j = 0; j < r; ++j) {
+      double t = load_as_double(w1, weight_dtype, x * r + j) *
+                 load_as_double(w2, weight_dtype, v * r + j);
+      a += t;
+      s += fabs(t);
+    }
+    double delta = 2.0 * (double)r * ldexp(1.0, -24) * s;
+    float b = load_as_float(base_logits, logits_dtype, row * V + v);
+    lo[i] = corrected_value(b, (float)(a - delta), logits_dtype, weight_dtype);
+    mid[i] = corrected_value(b, (float)a, logits_dtype, weight_dtype);
+    hi[i] = corrected_value(b, (float)(a + delta), logits_dtype, weight_dtype);
+  }
+  return ORACLE_OK;
+}

@@ -1,0 +1,106 @@
+/*
+ * dspark_oracle.h -- plain, slow CPU oracle for the vanilla DSpark low-rank
+ * Markov head.  TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and
+ * the benchmark's CPU-baseline leg call it; the product path never does.
+ * It shares no code, header, table or constant generator with the GPU library.
+ *
+ * Sources (web pages on the DSpark Markov head):
+ *   [P5] raw markov_head.py of a third-party DSpark draft repository:
+ *        module docstring (transition formula B(x_{k-1},:) = W2(W1[x_{k-1}]),
+ *        corrected logit U_k + B), _sample_tokens, VanillaMarkov
+ *        (get_prev_embeddings, project_bias, compute_step_bias,
+ *        apply_step_logits, apply_block_logits, sample_block_tokens),
+ *        build_markov_head.
+ *   [P3] NeMo AutoModel API page "speculative/dspark/markov_head",
+ *        class VanillaMarkov (markov_w1 = nn.Embedding(V, r)).
+ *   [P1] NeMo AutoModel API page "models/deepseek_v41/dspark",
+ *        class _DeepseekV41DSparkMarkovHead.
+ *
+ * Numeric reading (every step is written out in dspark_oracle.c):
+ *   e      = W1[x, :]                                (exact, widened to double)
+ *   a_v    = sum_j e_j * W2w[v, j]   in double, j in index order
+ *   acc_v  = (float) a_v                              (one round to nearest even)
+ *   bias_v = rnd_L(rnd_W(acc_v))                      (Linear emits W, .to(L))
+ *   c_v    = rnd_L((float)base_v + (float)bias_v)     (fp32 add, one rounding)
+ *   greedy (T < 1e-5): smallest v with c_v == max c
+ *   else   : smallest v maximising fmaf(c_v, kappa_T, g_v),
+ *            kappa_T = (float)(log2(e) / T), g_v = -log2f(-log2f(u_v)),
+ *            u_v from Philox4x32-10 (Salmon et al., SC'11).
+ *
+ * Layouts: base/corrected [B, M, V] row-major; token_ids [B, M];
+ * W1 [V, r] (the Embedding weight) and W2w [V, r] (the Linear(r, V) weight,
+ * i.e. the transpose of the mathematical W2) both row-major.
+ * dtype tags: 0 = float32, 1 = bfloat16 (stored as uint16 bit patterns).
+ * Return codes: 0 ok, 1 invalid argument, 2 unsupported dtype pair.
+ */
+#ifndef DSPARK_ORACLE_H
+#define DSPARK_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+#define ORACLE_OK 0
+#define ORACLE_INVALID 1
+#define ORACLE_UNSUPPORTED 2
+
+/* Teacher-forced block bias (VanillaMarkov.apply_block_logits). */
+int dspark_oracle_apply_block(const void* base_logits, int logits_dtype,
+                              const int64_t* token_ids, const void* w1,
+                              const void* w2, int weight_dtype, int64_t B,
+                              int64_t M, int64_t V, int64_t r,
+                              void* corrected_logits, int n_threads);
+
+/* Left-to-right block sampling (VanillaMarkov.sample_block_tokens).
+ * Noise for batch row b, step k uses the absolute indices
+ * (batch_offset + b, position_offset + k).  corrected_logits may be NULL. */
+int dspark_oracle_sample_block(const void* base_logits, int logits_dtype,
+                               const int64_t* first_prev_token_ids,
+                               const void* w1, const void* w2, int weight_dtype,
+                               int64_t B, int64_t M, int64_t V, int64_t r,
+                               double temperature, uint64_t seed,
+                               int64_t position_offset, int64_t batch_offset,
+                               int64_t* sampled_tokens, void* corrected_logits,
+                               int n_threads);
+
+/* The reduction step of _sample_tokens alone, applied to one corrected row
+ * (dtype logits_dtype, length V) that the caller supplies.  Writes the token
+ * and, if score_out is not NULL, the winning and runner-up scores (the
+ * corrected values for greedy, the Gumbel scores otherwise) and the
+ * runner-up index. */
+int dspark_oracle_select_token(const void* row, int logits_dtype, int64_t V,
+                               double temperature, uint64_t seed, int64_t b_abs,
+                               int64_t k_abs, int64_t* token, float* score_out,
+                               int64_t* runner_up);
+
+/* Bounds on one corrected element under any fp32 accumulation order:
+ * for each of n (row, v) pairs, with row indexing the flattened [B*M] rows,
+ * writes lo/hi (as float values of the L-typed results) obtained by pushing
+ * the dot product to a -/+ 2r*2^-24*sum|e_j*W2w[v,j]| through the monotone
+ * rounding chain.  Also writes the oracle's own value to mid. */
+int dspark_oracle_logit_bounds(const void* base_logits, int logits_dtype,
+                               const int64_t* token_ids, const void* w1,
+                               const void* w2, int weight_dtype, int64_t V,
+                               int64_t r, int64_t n, const int64_t* rows,
+                               const int64_t* cols, float* lo, float* mid,
+                               float* hi);
+
+/* Building blocks exposed for pinning. */
+void dspark_oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2],
+                                 uint32_t out[4]);
+float dspark_oracle_gumbel2(uint64_t seed, int64_t b_abs, int64_t k_abs,
+                            int64_t v);
+uint16_t dspark_oracle_round_bf16(float x);
+float dspark_oracle_kappa(double temperature);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,127 @@
+"""Seeded synthetic inputs for the DSpark Markov head.
+
+This module draws random inputs and holds none of the head's arithmetic.
+It is shared by the GPU tests, the oracle tests and the benchmark so that
+both sides read identical bytes.
+
+Shapes follow the DSpark pages: vocabulary 129280, Markov rank 256 and
+block size 5 for DeepSeek-V4.1 (NeMo AutoModel ``deepseek_v41/config`` page,
+``DeepseekV41TextConfig``: ``vocab_size``, ``dspark_markov_rank``,
+``dspark_block_size``; ``initializer_range=0.02`` matches the N(0, 0.02^2)
+weights), many anchors per sequence (``models/deepseek_v41/dspark`` page,
+module summary), and an 8-position block at vocabulary 151936 for the
+second drafter (third-party ``markov_head.py`` page, suffix-decay note).
+The pages name no dataset; real backbone logits and trained weights are
+replaced by normal draws.
+
+Draw order for every workload: base logits, W1, W2w, then the token ids,
+from ``numpy.random.default_rng(seed)``; float32 draws are rounded to
+bfloat16 by torch's own conversion.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+F32 = 0
+BF16 = 1
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int                 # batch rows (B * num_anchors for the training layout)
+    M: int                 # block size / proposal length
+    V: int                 # vocabulary
+    r: int                 # Markov rank
+    dtype: int             # F32 or BF16, both logits and weights
+    base_sigma: float
+    w_sigma: float
+    seed: int
+    mode: str              # "apply", "greedy", "temperature", "apply+greedy"
+    temperature: float = 0.0
+    gumbel_seed: int = 0
+    ids: str = "uniform"   # "uniform" or "zipf1.1"
+    boost: float = 0.0     # added at one random position per (b, k) row
+    return_logits: bool = True
+
+    @property
+    def rows(self) -> int:
+        return self.B * self.M
+
+    @property
+    def elems(self) -> int:
+        return self.B * self.M * self.V
+
+
+WORKLOADS = {
+    # Tiny fp32 check: apply plus greedy left-to-right sampling.
+    "tiny_fp32": Workload("tiny_fp32", B=2, M=5, V=1024, r=16, dtype=F32, base_sigma=1.0,
+                          w_sigma=0.02, seed=0, mode="apply+greedy"),
+    # Teacher-forced training forward: 4 sequences x 16 anchors, block 5.
+    "teacher_forced_320": Workload("teacher_forced_320", B=64, M=5, V=129280, r=256, dtype=BF16,
+                                   base_sigma=2.0, w_sigma=0.02, seed=2, mode="apply"),
+    # Greedy left-to-right draft, batch 64, block 5, corrected logits returned.
+    "greedy_draft_64x5": Workload("greedy_draft_64x5", B=64, M=5, V=129280, r=256, dtype=BF16,
+                                  base_sigma=2.0, w_sigma=0.02, seed=3, mode="greedy",
+                                  boost=6.0),
+    # Temperature draft at the 151936 vocabulary, batch 256, block 8, tokens only.
+    "temperature_draft_256x8": Workload("temperature_draft_256x8", B=256, M=8, V=151936, r=256,
+                                        dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=4,
+                                        mode="temperature", temperature=0.7, gumbel_seed=1234,
+                                        return_logits=False),
+    # Large teacher-forced batch: 8 sequences x 64 anchors, rank 512, Zipf ids.
+    "teacher_forced_2560_zipf": Workload("teacher_forced_2560_zipf", B=512, M=5, V=129280, r=512,
+                                         dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=5,
+                                         mode="apply", ids="zipf1.1"),
+}
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 array -> bfloat16 bit patterns (uint16), via torch's conversion."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def zipf_ids(rng: np.random.Generator, n: int, V: int, s: float) -> np.ndarray:
+    """n draws from P(i) proportional to (i+1)^-s on [0, V), by inverse CDF."""
+    w = np.arange(1, V + 1, dtype=np.float64) ** (-s)
+    cdf = np.cumsum(w)
+    cdf /= cdf[-1]
+    ids = np.searchsorted(cdf, rng.random(n), side="right")
+    return np.minimum(ids, V - 1).astype(np.int64)
+
+
+def make_inputs(w: Workload, *, B: int | None = None, M: int | None = None,
+                V: int | None = None, r: int | None = None, seed: int | None = None):
+    """Draw inputs for workload ``w`` (optionally at other sizes).
+
+    Returns a dict of numpy arrays: base [B, M, V], w1 [V, r], w2 [V, r]
+    (float32 or uint16 bf16 bits), token_ids [B, M] and first_prev [B] (int64).
+    """
+    B = w.B if B is None else B
+    M = w.M if M is None else M
+    V = w.V if V is None else V
+    r = w.r if r is None else r
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    base = rng.standard_normal((B, M, V), dtype=np.float32) * np.float32(w.base_sigma)
+    if w.boost and B * M > 0 and V > 0:
+        pos = rng.integers(0, V, size=(B, M))
+        bi, ki = np.meshgrid(np.arange(B), np.arange(M), indexing="ij")
+        base[bi, ki, pos] += np.float32(w.boost)
+    w1 = rng.standard_normal((V, r), dtype=np.float32) * np.float32(w.w_sigma)
+    w2 = rng.standard_normal((V, r), dtype=np.float32) * np.float32(w.w_sigma)
+    if w.ids == "zipf1.1":
+        token_ids = zipf_ids(rng, B * M, V, 1.1).reshape(B, M) if V > 0 else np.zeros((B, M), np.int64)
+    else:
+        token_ids = rng.integers(0, max(V, 1), size=(B, M), dtype=np.int64)
+    first_prev = rng.integers(0, max(V, 1), size=(B,), dtype=np.int64)
+    if w.dtype == BF16:
+        base, w1, w2 = to_bf16_bits(base), to_bf16_bits(w1), to_bf16_bits(w2)
+    return {"base": base, "w1": w1, "w2": w2, "token_ids": token_ids, "first_prev": first_prev}

@@ -1,0 +1,399 @@
+"""Pins of the CPU oracle against what the DSpark pages and mathematics fix.
+
+Nothing here compares the oracle with itself retyped: each test checks it
+against an exact brute force on inputs where every operation is exact, a
+closed form worked by hand, a published known-answer vector, a library
+routine that the reading reduces to, an invariant the pages state, or a
+statistical law.  A plausible mistake (dropped term, wrong sign, wrong or
+transposed index, a rounding step missing or doubled, a wrong Philox
+constant, a wrong tie-break) fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from rank_markov_draft_amd import workloads as wl
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+# ---------------------------------------------------------------- helpers
+def f32_to_bits(x):
+    return np.asarray(x, dtype=np.float32).view(np.uint32)
+
+
+def as_float(a):
+    """Oracle-typed array (float32 or bf16 bits) -> float32 values."""
+    return wl.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a
+
+
+def dyadic_inputs(rng, B, M, V, r, dtype):
+    """Inputs on which every step of the head is exact in bf16 and fp32:
+    W1 in {-4..4}/8, W2w in {-4..4}/16, base in {-32..32}/32, so every
+    product is k/128 and |base + bias| <= 2 needs at most 8 significant bits."""
+    w1 = rng.integers(-4, 5, size=(V, r)).astype(np.float32) / 8
+    w2 = rng.integers(-4, 5, size=(V, r)).astype(np.float32) / 16
+    base = rng.integers(-32, 33, size=(B, M, V)).astype(np.float32) / 32
+    ids = rng.integers(0, V, size=(B, M)).astype(np.int64)
+    first = rng.integers(0, V, size=(B,)).astype(np.int64)
+    assert r <= 8
+    if dtype == wl.BF16:
+        return wl.to_bf16_bits(base), ids, first, wl.to_bf16_bits(w1), wl.to_bf16_bits(w2)
+    return base, ids, first, w1, w2
+
+
+# ------------------------------------------------- Philox: published KAT
+def test_philox_known_answers(oracle_mod):
+    """Random123 known-answer vectors for Philox4x32-10."""
+    n = 0
+    with open(os.path.join(HERE, "golden", "philox4x32_10_kat.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            words = [int(t, 16) for t in line.split()]
+            ctr, key, want = words[0:4], words[4:6], words[6:10]
+            got = oracle_mod.philox4x32_10(ctr, key)
+            assert [int(x) for x in got] == want, line
+            n += 1
+    assert n == 3
+
+
+def test_gumbel_counter_layout_zero_key(oracle_mod):
+    """seed 0, row (b=0, k=0), v = 0..3 read the four words of the all-zero
+    Philox block (the first KAT line) in order."""
+    words = [0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8]
+    for v, w in enumerate(words):
+        u = (2 * (w >> 9) + 1) * 2.0**-24          # exact in double
+        want = -math.log2(-math.log2(u))
+        assert abs(oracle_mod.gumbel2(0, 0, 0, v) - want) <= 4e-6 * max(1.0, abs(want))
+
+
+def test_gumbel_counter_layout_words(oracle_mod):
+    """Row b, step k and vocab block v>>2 select counter words 2, 1, 0; the
+    seed halves are the key.  Checked against the KAT-pinned block function."""
+    seed = 0x0123456789ABCDEF
+    for (b, k, v) in [(0, 0, 5), (3, 0, 0), (0, 7, 1), (11, 2, 4099), (255, 7, 151935)]:
+        out = oracle_mod.philox4x32_10([v >> 2, k, b, 0], [seed & 0xFFFFFFFF, seed >> 32])
+        w = int(out[v & 3])
+        u = (2 * (w >> 9) + 1) * 2.0**-24
+        want = -math.log2(-math.log2(u))
+        assert abs(oracle_mod.gumbel2(seed, b, k, v) - want) <= 4e-6 * max(1.0, abs(want))
+
+
+def test_gumbel_marginal_is_gumbel(oracle_mod):
+    """g = -log2(-log2 u) is a standard Gumbel G rescaled: G = ln2*(g - log2 ln2).
+    Kolmogorov-Smirnov against exp(-exp(-G))."""
+    from scipy import stats
+    g = np.array([oracle_mod.gumbel2(1234, b, 3, v) for b in range(40) for v in range(2500)])
+    G = math.log(2.0) * (g - math.log2(math.log(2.0)))
+    res = stats.kstest(G, lambda x: np.exp(-np.exp(-x)))
+    assert res.pvalue > 1e-4, res
+    # support of the odd 24-bit uniform: u in [2^-24, 1 - 2^-24]
+    assert g.min() >= -math.log2(24.0) - 1e-4
+    assert g.max() <= -math.log2(-math.log2(1 - 2.0**-24)) + 1e-3
+
+
+# --------------------------------------------- bf16 rounding vs torch
+def test_round_bf16_matches_torch(oracle_mod):
+    rng = np.random.default_rng(7)
+    specials = np.array([0.0, -0.0, 1.0, 1 + 2**-8, 1 + 3 * 2**-8, -(1 + 2**-8), 3.0e38, 3.3895314e38,
+                         3.4e38, np.inf, -np.inf, 1e-40, -1e-40, 2**-126, 2**-133, 65504.0,
+                         1.00390625, 1.01171875, 255.5, 256.5], dtype=np.float32)
+    bits = rng.integers(0, 2**32, size=20000, dtype=np.uint64).astype(np.uint32)
+    rand = bits.view(np.float32)
+    rand = rand[~np.isnan(rand)]
+    vals = np.concatenate([specials, rand, rng.standard_normal(5000).astype(np.float32) * 4])
+    want = wl.to_bf16_bits(vals)
+    got = np.array([oracle_mod.round_bf16(float(x)) for x in vals], dtype=np.uint16)
+    assert np.array_equal(got, want)
+    # NaN stays NaN (torch's vectorised path picks another NaN pattern)
+    assert oracle_mod.round_bf16(float("nan")) == 0x7FC0
+    assert np.isnan(wl.bf16_bits_to_f32(wl.to_bf16_bits(np.array([np.nan], np.float32))))[0]
+
+
+# ------------------------------- exact brute force: dense transition matrix
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_apply_exact_bruteforce(oracle_mod, dtype):
+    """On exact inputs the corrected logits are base + (W1 W2w^T)[x]: the
+    full V x V bigram matrix from a library matmul, indexed by predecessor."""
+    rng = np.random.default_rng(11)
+    B, M, V, r = 3, 4, 64, 8
+    base, ids, _, w1, w2 = dyadic_inputs(rng, B, M, V, r, dtype)
+    T = as_float(w1).astype(np.float64) @ as_float(w2).astype(np.float64).T   # [V, V]
+    want = as_float(base).astype(np.float64) + T[ids]                          # [B, M, V]
+    got = as_float(oracle_mod.apply_block(base, ids, w1, w2)).astype(np.float64)
+    assert np.array_equal(got, want)
+
+
+def test_apply_exact_pure_python_loop(oracle_mod):
+    """Per-element pure-Python sum on a 4 x 6 x 16 toy (exact inputs, r = 5)."""
+    rng = np.random.default_rng(12)
+    B, M, V, r = 4, 6, 16, 5
+    base, ids, _, w1, w2 = dyadic_inputs(rng, B, M, V, r, wl.F32)
+    got = oracle_mod.apply_block(base, ids, w1, w2)
+    for b in range(B):
+        for k in range(M):
+            x = int(ids[b, k])
+            for v in range(V):
+                s = float(base[b, k, v])
+                for j in range(r):
+                    s += float(w1[x, j]) * float(w2[v, j])
+                assert float(got[b, k, v]) == s
+
+
+# ------------------------------------- rounding chain: hand-worked closed forms
+def _one_row(oracle_mod, e, w, base_val, dtype):
+    """V = 2 vocabulary, predecessor 0 with W1[0] = e, W2w[0] = w."""
+    r = len(e)
+    w1 = np.zeros((2, r), np.float32)
+    w2 = np.zeros((2, r), np.float32)
+    w1[0] = e
+    w2[0] = w
+    base = np.array([[[base_val, 0.0]]], np.float32)
+    ids = np.zeros((1, 1), np.int64)
+    if dtype == wl.BF16:
+        base, w1, w2 = wl.to_bf16_bits(base), wl.to_bf16_bits(w1), wl.to_bf16_bits(w2)
+    out = oracle_mod.apply_block(base, ids, w1, w2)
+    return float(as_float(out)[0, 0, 0])
+
+
+def test_bias_rounded_before_add_bf16(oracle_mod):
+    """acc = 1 + 2^-8 rounds (tie, even) to the bf16 bias 1.0; 2^-9 + 1.0 then
+    rounds to 1.0.  Adding the unrounded acc would give 1 + 2^-7."""
+    assert _one_row(oracle_mod, [1.0, 2**-4], [1.0, 2**-4], 2**-9, wl.BF16) == 1.0
+
+
+def test_bias_tie_to_even_upwards_bf16(oracle_mod):
+    """acc = 1 + 3*2^-8 lies halfway between 1 + 2^-7 (odd) and 1 + 2^-6 (even)."""
+    assert _one_row(oracle_mod, [1.0, 2**-4, 2**-4], [1.0, 2**-4, 2**-3], 0.0, wl.BF16) == 1 + 2**-6
+
+
+def test_fp32_accumulation_is_best_value(oracle_mod):
+    """1 + 2^-24 + 2^-24 = 1 + 2^-23 exactly; a left-to-right fp32 sum would
+    lose both small terms.  The best fp32 value of the sum is kept."""
+    got = _one_row(oracle_mod, [1.0, 2**-24, 2**-24], [1.0, 1.0, 1.0], 0.0, wl.F32)
+    assert got == np.float32(1 + 2**-23)
+
+
+def test_fp32_add_single_rounding(oracle_mod):
+    """(F32, F32): c = fl(base + acc): 1 + 2^-24 ties to 1.0, 1 + 3*2^-24 to 1 + 2^-22."""
+    assert _one_row(oracle_mod, [2**-12], [2**-12], 1.0, wl.F32) == 1.0
+    assert _one_row(oracle_mod, [2**-12, 2**-12], [2**-12, 2**-11], 1.0, wl.F32) == np.float32(1 + 2**-22)
+
+
+# ----------------------------------------------------------- invariants
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_equal_predecessor_rows_identical(oracle_mod, dtype):
+    """The vanilla bias is a pure function of the previous token: rows with
+    the same predecessor and the same base row are bit-identical."""
+    w = wl.WORKLOADS["tiny_fp32"]
+    inp = wl.make_inputs(dataclass_replace(w, dtype=dtype), B=4, M=6, V=300, r=12)
+    base = inp["base"].copy()
+    base[:] = base[0, 0]                       # every row the same base row
+    ids = np.array([[5, 7, 5, 9, 7, 5]] * 4, dtype=np.int64)
+    out = oracle_mod.apply_block(base, ids, inp["w1"], inp["w2"])
+    flat = out.reshape(-1, out.shape[-1])
+    fid = ids.reshape(-1)
+    for t in np.unique(fid):
+        rows = flat[fid == t]
+        assert all(np.array_equal(rows[0], x) for x in rows)
+    assert not np.array_equal(flat[0], flat[1])
+
+
+def dataclass_replace(w, **kw):
+    import dataclasses
+    return dataclasses.replace(w, **kw)
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("which", ["w1", "w2"])
+def test_zero_weights_identity(oracle_mod, dtype, which):
+    """W2 = 0 (or W1 = 0) leaves the base logits unchanged (by value)."""
+    w = dataclass_replace(wl.WORKLOADS["tiny_fp32"], dtype=dtype)
+    inp = wl.make_inputs(w, B=3, M=4, V=513, r=16)
+    inp[which] = np.zeros_like(inp[which])
+    out = oracle_mod.apply_block(inp["base"], inp["token_ids"], inp["w1"], inp["w2"])
+    assert np.array_equal(as_float(out), as_float(inp["base"]))
+    toks, corr = oracle_mod.sample_block(inp["base"], inp["first_prev"], inp["w1"], inp["w2"])
+    assert np.array_equal(as_float(corr), as_float(inp["base"]))
+    assert np.array_equal(toks, np.argmax(as_float(inp["base"]), axis=-1))
+
+
+def test_thread_count_does_not_change_results(oracle_mod):
+    w = wl.WORKLOADS["tiny_fp32"]
+    inp = wl.make_inputs(w)
+    a = oracle_mod.apply_block(inp["base"], inp["token_ids"], inp["w1"], inp["w2"], n_threads=1)
+    b = oracle_mod.apply_block(inp["base"], inp["token_ids"], inp["w1"], inp["w2"], n_threads=7)
+    assert np.array_equal(a, b)
+
+
+# --------------------------------------------------- token selection
+def test_greedy_first_index_on_ties(oracle_mod):
+    row = np.array([0.0, 3.0, 1.0, 3.0, 2.0], np.float32)
+    assert oracle_mod.select_token(row)[0] == 1
+    row = np.array([-1.0, -0.0, 0.0, -2.0], np.float32)
+    assert oracle_mod.select_token(row)[0] == 1          # -0 == +0
+    row = np.array([1.0, np.nan, 5.0, np.nan], np.float32)
+    assert oracle_mod.select_token(row)[0] == 1          # NaN ranks first, as torch.argmax
+    bf = wl.to_bf16_bits(np.array([0.5, 2.0, 2.0, -3.0], np.float32))
+    assert oracle_mod.select_token(bf)[0] == 1
+
+
+def test_greedy_matches_numpy_argmax(oracle_mod):
+    """numpy.argmax also returns the first maximal index (library routine)."""
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        row = wl.to_bf16_bits(rng.standard_normal(4096).astype(np.float32) * 2)
+        assert oracle_mod.select_token(row)[0] == int(np.argmax(wl.bf16_bits_to_f32(row)))
+
+
+@pytest.mark.parametrize("T", [0.0, -1.0, 9.999e-6, 1e-9])
+def test_small_temperature_is_greedy(oracle_mod, T):
+    w = wl.WORKLOADS["tiny_fp32"]
+    inp = wl.make_inputs(w)
+    g, cg = oracle_mod.sample_block(inp["base"], inp["first_prev"], inp["w1"], inp["w2"], temperature=0.0)
+    t, ct = oracle_mod.sample_block(inp["base"], inp["first_prev"], inp["w1"], inp["w2"],
+                                    temperature=T, seed=99)
+    assert np.array_equal(g, t) and np.array_equal(cg, ct)
+
+
+def test_temperature_1e5_with_large_gap_is_argmax(oracle_mod):
+    """At T = 1e-5 the score is c * log2(e)/T + g with g in [-4.6, 22.5]: a gap
+    of 0.01 in c is worth 1443 and decides."""
+    rng = np.random.default_rng(5)
+    for b in range(20):
+        row = (rng.integers(-50, 50, size=300) * 0.01).astype(np.float32)
+        win = int(rng.integers(0, 300))
+        row[win] = 1.0
+        assert oracle_mod.select_token(row, temperature=1e-5, seed=4, b_abs=b, k_abs=1)[0] == win
+
+
+def test_gumbel_max_sampling_law(oracle_mod):
+    """Chi-square of 200000 draws against softmax(c / T) (the law of the pages'
+    softmax + multinomial draw) on an 8-entry vocabulary."""
+    from scipy import stats
+    c = np.array([0.5, -1.0, 2.0, 0.0, 1.0, -0.5, 1.5, -2.0], np.float32)
+    T = 0.7
+    N = 200000
+    base = np.broadcast_to(c, (N, 1, 8)).copy()
+    w1 = np.zeros((8, 1), np.float32)
+    w2 = np.zeros((8, 1), np.float32)
+    first = np.zeros(N, np.int64)
+    toks, _ = oracle_mod.sample_block(base, first, w1, w2, temperature=T, seed=1234,
+                                      return_logits=False)
+    counts = np.bincount(toks[:, 0], minlength=8)
+    p = np.exp(c.astype(np.float64) / T)
+    p /= p.sum()
+    chi2 = float(((counts - N * p) ** 2 / (N * p)).sum())
+    assert stats.chi2.sf(chi2, df=7) > 1e-5, (counts, N * p, chi2)
+    # a wrong scale (T instead of 1/T) would be rejected by the same statistic
+    q = np.exp(c.astype(np.float64) * T)
+    q /= q.sum()
+    chi2_wrong = float(((counts - N * q) ** 2 / (N * q)).sum())
+    assert stats.chi2.sf(chi2_wrong, df=7) < 1e-12
+
+
+# ------------------------------------------------------ the chain
+@pytest.mark.parametrize("T", [0.0, 0.7])
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_chain_equals_single_steps(oracle_mod, T, dtype):
+    """sample_block over M positions equals M calls with M = 1, each fed the
+    previous call's token and position_offset = k."""
+    w = dataclass_replace(wl.WORKLOADS["tiny_fp32"], dtype=dtype)
+    inp = wl.make_inputs(w, B=3, M=5, V=777, r=8)
+    full_t, full_c = oracle_mod.sample_block(inp["base"], inp["first_prev"], inp["w1"], inp["w2"],
+                                             temperature=T, seed=77)
+    prev = inp["first_prev"].copy()
+    for k in range(5):
+        t, c = oracle_mod.sample_block(inp["base"][:, k:k + 1], prev, inp["w1"], inp["w2"],
+                                       temperature=T, seed=77, position_offset=k)
+        assert np.array_equal(t[:, 0], full_t[:, k])
+        assert np.array_equal(c[:, 0], full_c[:, k])
+        prev = t[:, 0]
+
+
+@pytest.mark.parametrize("T", [0.0, 0.7])
+def test_chain_equals_teacher_forced_apply(oracle_mod, T):
+    """The left-to-right chain is apply_block with token_ids =
+    [first_prev, tok_0, ..., tok_{M-2}], followed by the token draw."""
+    w = dataclass_replace(wl.WORKLOADS["tiny_fp32"], dtype=wl.BF16)
+    inp = wl.make_inputs(w, B=4, M=5, V=1000, r=16)
+    toks, corr = oracle_mod.sample_block(inp["base"], inp["first_prev"], inp["w1"], inp["w2"],
+                                         temperature=T, seed=5)
+    ids = np.concatenate([inp["first_prev"][:, None], toks[:, :-1]], axis=1)
+    applied = oracle_mod.apply_block(inp["base"], ids, inp["w1"], inp["w2"])
+    assert np.array_equal(applied, corr)
+    for b in range(4):
+        for k in range(5):
+            assert oracle_mod.select_token(corr[b, k], temperature=T, seed=5, b_abs=b, k_abs=k)[0] == toks[b, k]
+    if T == 0.0:
+        assert np.array_equal(toks, np.argmax(wl.bf16_bits_to_f32(corr), axis=-1))
+
+
+def test_batch_offset_selects_noise_rows(oracle_mod):
+    w = dataclass_replace(wl.WORKLOADS["tiny_fp32"], dtype=wl.BF16)
+    inp = wl.make_inputs(w, B=6, M=3, V=500, r=8)
+    full_t, _ = oracle_mod.sample_block(inp["base"], inp["first_prev"], inp["w1"], inp["w2"],
+                                        temperature=1.3, seed=9)
+    part_t, _ = oracle_mod.sample_block(inp["base"][2:5], inp["first_prev"][2:5], inp["w1"], inp["w2"],
+                                        temperature=1.3, seed=9, batch_offset=2)
+    assert np.array_equal(full_t[2:5], part_t)
+
+
+# ------------------------------------------------------------ bounds
+def test_logit_bounds_bracket_oracle(oracle_mod):
+    w = dataclass_replace(wl.WORKLOADS["tiny_fp32"], dtype=wl.BF16)
+    inp = wl.make_inputs(w, B=2, M=5, V=1024, r=16)
+    out = oracle_mod.apply_block(inp["base"], inp["token_ids"], inp["w1"], inp["w2"])
+    rows = np.repeat(np.arange(10), 1024)
+    cols = np.tile(np.arange(1024), 10)
+    lo, mid, hi = oracle_mod.logit_bounds(inp["base"], inp["token_ids"], inp["w1"], inp["w2"], rows, cols)
+    assert np.array_equal(mid, wl.bf16_bits_to_f32(out.reshape(-1)))
+    assert np.all(lo <= mid) and np.all(mid <= hi)
+
+
+# ------------------------------------------------------------ edge cases
+def test_empty_and_invalid(oracle_mod):
+    o = oracle_mod
+    w = wl.WORKLOADS["tiny_fp32"]
+    inp = wl.make_inputs(w, B=2, M=3, V=64, r=4)
+    base, ids, first, w1, w2 = inp["base"], inp["token_ids"], inp["first_prev"], inp["w1"], inp["w2"]
+    # M == 0 and B == 0: empty work is fine
+    st, out = o.apply_block(base[:, :0], ids[:, :0], w1, w2, check=False)
+    assert st == o.OK and out.shape == (2, 0, 64)
+    st, t, c = o.sample_block(base[:, :0], first, w1, w2, check=False)
+    assert st == o.OK and t.shape == (2, 0)
+    st, t, c = o.sample_block(base[:0], first[:0], w1, w2, check=False)
+    assert st == o.OK and t.shape == (0, 3)
+    # rank must be positive
+    st, _ = o.apply_block(base, ids, w1[:, :0], w2[:, :0], check=False)
+    assert st == o.INVALID
+    # out-of-range predecessor ids
+    bad = ids.copy()
+    bad[1, 2] = 64
+    assert o.apply_block(base, bad, w1, w2, check=False)[0] == o.INVALID
+    bad[1, 2] = -1
+    assert o.apply_block(base, bad, w1, w2, check=False)[0] == o.INVALID
+    fb = first.copy()
+    fb[0] = 64
+    assert o.sample_block(base, fb, w1, w2, check=False)[0] == o.INVALID
+    # NaN temperature
+    assert o.sample_block(base, first, w1, w2, temperature=float("nan"), check=False)[0] == o.INVALID
+    # V == 0: apply is an empty op, sampling has nothing to draw from
+    st, _ = o.apply_block(base[..., :0], ids, w1[:0], w2[:0], check=False)
+    assert st == o.OK
+    st, _, _ = o.sample_block(base[..., :0], first, w1[:0], w2[:0], check=False)
+    assert st == o.INVALID
+
+
+def test_sampled_tokens_in_range_and_deterministic(oracle_mod):
+    w = dataclass_replace(wl.WORKLOADS["tiny_fp32"], dtype=wl.BF16)
+    inp = wl.make_inputs(w, B=8, M=5, V=333, r=8)
+    a, _ = oracle_mod.sample_block(inp["base"], inp["first_prev"], inp["w1"], inp["w2"], temperature=0.9, seed=3)
+    b, _ = oracle_mod.sample_block(inp["base"], inp["first_prev"], inp["w1"], inp["w2"], temperature=0.9, seed=3)
+    c, _ = oracle_mod.sample_block(inp["base"], inp["first_prev"], inp["w1"], inp["w2"], temperature=0.9, seed=4)
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
+    assert a.min() >= 0 and a.max() < 333
