@@ -1,0 +1,167 @@
+"""Benchmark of the DSpark Markov head on one MI355X.
+
+One step = one greedy left-to-right draft of 64 sequences x 5 positions at
+vocabulary 129280, rank 256, bf16 (sample_block_tokens with the corrected
+logits returned): every step of the head's hot path (predecessor select,
+W1 gather, low-rank projection, streaming add, argmax, chain).
+
+The timed region starts with all inputs resident in HBM.  Successive steps
+rotate over several input sets whose total exceeds the 256 MB Infinity
+Cache, so every step streams its logits and weights from HBM.
+
+Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+WORKLOAD = "greedy_draft_64x5"
+
+
+def algorithmic_bytes_sample(w, return_logits=True) -> int:
+    """Bytes one sample call must move at least: base logits read, corrected
+    logits written, W2 read once, the gathered W1 rows, tokens and ids."""
+    lb = 2 if w.dtype == 1 else 4
+    elems = w.B * w.M * w.V
+    b = elems * lb * (2 if return_logits else 1)
+    b += w.V * w.r * lb                 # W2 once
+    b += w.B * w.M * w.r * lb           # gathered W1 rows
+    b += w.B * w.M * 8 + w.B * 8        # tokens out, first_prev in
+    return b
+
+
+def algorithmic_bytes_apply(w) -> int:
+    lb = 2 if w.dtype == 1 else 4
+    return w.B * w.M * w.V * lb * 2 + w.V * w.r * lb + w.B * w.M * (w.r * lb + 8)
+
+
+def to_dev(a, torch, np):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def time_calls(fn, n_sets, steps, warmup, torch):
+    """Warm up, then time exactly `steps` calls (rotating over input sets)
+    with events on the current stream; returns (wall seconds, per-call ms)."""
+    for i in range(warmup):
+        fn(i % n_sets)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn(i % n_sets)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, per
+
+
+def cpu_baseline(w, inp, np):
+    """The oracle as it stands, on the host cores, on a bounded sample of the
+    same workload (the first 16 of the 64 chains, all 5 positions)."""
+    from oracle import oracle as orc
+    cores = len(os.sched_getaffinity(0))
+    nb = 16
+    base = np.ascontiguousarray(inp["base"][:nb])
+    first = np.ascontiguousarray(inp["first_prev"][:nb])
+    orc.lib()
+    t0 = time.perf_counter()
+    orc.sample_block(base, first, inp["w1"], inp["w2"], temperature=0.0, n_threads=cores)
+    dt = time.perf_counter() - t0
+    elems = nb * w.M * w.V
+    return {"value": elems / dt, "unit": "corrected-logit elems/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nb} of {w.B} chains x {w.M} positions, V={w.V}, r={w.r}, greedy, "
+                      f"{dt:.2f} s wall", "tokens_per_s": nb * w.M / dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the head's sharding is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rank_markov_draft_amd as rmd
+    from rank_markov_draft_amd import _lib
+    from rank_markov_draft_amd import workloads as wl
+
+    if not os.path.exists(_lib.LIB_PATH):
+        _lib.build()
+    _lib.load()
+    torch.cuda.set_device(0)
+
+    w = wl.WORKLOADS[WORKLOAD]
+    inp = wl.make_inputs(w)
+    n_sets = 4   # 4 x (82.7 + 82.7 + 66.2 + 66.2) MB > 256 MB cache
+    sets = []
+    for i in range(n_sets):
+        d = {k: to_dev(inp[k], torch, np) for k in ("base", "first_prev", "w1", "w2")}
+        if i > 0:
+            d = {k: v.clone() for k, v in d.items()}
+        d["tok"] = torch.empty((w.B, w.M), dtype=torch.int64, device="cuda")
+        d["corr"] = torch.empty_like(d["base"])
+        d["ws"] = rmd.Workspace(w.B, w.M, w.V, w.r, sample=True)
+        sets.append(d)
+
+    def step(i):
+        d = sets[i]
+        rmd.sample_block_tokens(d["base"], d["first_prev"], d["w1"], d["w2"], 0.0, tokens_out=d["tok"],
+                                logits_out=d["corr"], workspace=d["ws"])
+
+    wall, per = time_calls(step, n_sets, args.steps, args.warmup, torch)
+    ms = wall * 1e3 / args.steps
+    elems = w.B * w.M * w.V
+    call_ms = float(np.mean(per))
+    alg = algorithmic_bytes_sample(w)
+    achieved = alg / (call_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "corrected-logit elems/s + draft tokens/s at V=129280; % HBM roofline",
+        "value": elems / (ms * 1e-3),
+        "unit": "corrected-logit elems/s",
+        "draft_tokens_per_s": w.B * w.M / (ms * 1e-3),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{WORKLOAD}: greedy left-to-right draft, batch {w.B}, block {w.M}, "
+                               f"V={w.V}, r={w.r}, bf16 logits and weights, corrected logits returned",
+                   "global_batch": w.B, "block": w.M, "vocab": w.V, "rank": w.r},
+        "roofline": {"bound": "hbm", "kernel": "sample_block call (all kernels of one step)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": alg, "launch_ms": call_ms},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inp, np)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

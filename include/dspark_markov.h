@@ -1,0 +1,137 @@
+/*
+ * dspark_markov.h -- C ABI of the MI355X (gfx950) DSpark low-rank Markov head.
+ *
+ * The vanilla DSpark Markov head adds a first-order token-transition bias to
+ * a block drafter's base logits:
+ *
+ *     B(x_{k-1}, :) = W2 . W1[x_{k-1}],   W1 in R^{V x r},  W2 in R^{r x V}
+ *     corrected_k   = U_k + B(x_{k-1}, :)
+ *
+ * (third-party markov_head.py page, module docstring; NeMo AutoModel
+ * "speculative/dspark/markov_head" page, class VanillaMarkov; NeMo AutoModel
+ * "models/deepseek_v41/dspark" page, class _DeepseekV41DSparkMarkovHead).
+ *
+ * Two operations mirror VanillaMarkov's two methods:
+ *   dspark_markov_apply_block   -- apply_block_logits (teacher-forced: every
+ *                                  row biased by its own given predecessor);
+ *   dspark_markov_sample_block  -- sample_block_tokens (left to right: each
+ *                                  position biased by the token drawn at the
+ *                                  previous position, greedy or temperature).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every pointer argument named as device memory must point to
+ *           memory of the current HIP device; the caller owns all buffers.
+ *           The library never allocates memory visible to the caller.
+ * Streams.  `stream` is a hipStream_t (NULL = the null stream).  All work is
+ *           enqueued asynchronously on it; no entry point synchronises except
+ *           dspark_markov_read_device_error.
+ * Layout.   Contiguous row-major.  base/corrected logits are [B, M, V]; the
+ *           training layout [B, num_anchors, block_size, V] is passed as
+ *           B' = B * num_anchors, M = block_size (the op is row-wise, so the
+ *           result is identical).  W1 is the Embedding weight [V, r]; W2 is
+ *           passed as the Linear(r, V) weight [V, r], i.e. the transpose of
+ *           the mathematical W2.
+ * Dtypes.   (logits, weights) must be (F32, F32) or (BF16, BF16); other
+ *           pairs return DSPARK_ERR_UNSUPPORTED.  Token ids are int64.
+ * Numerics. bias = round_L(round_W(fp32 dot product of W1[x] and W2w[v]));
+ *           corrected = round_L(fp32(base) + fp32(bias))  (Linear output in
+ *           the weight dtype, then .to(logits dtype), then the add).
+ * Errors.   Argument errors are detected on the host before anything is
+ *           enqueued and leave every output untouched.  Token ids outside
+ *           [0, V) are not checked on the host: such a row gets a zero bias
+ *           and is counted in the workspace's device error word (see
+ *           dspark_markov_read_device_error).
+ * Workspace. Device memory of at least dspark_markov_workspace_bytes(...)
+ *           bytes, zero-filled once before its first use (for instance by
+ *           dspark_markov_workspace_init); the library leaves it ready for
+ *           the next call.  Calls that share one workspace must be ordered
+ *           on one stream; calls in flight at the same time need their own.
+ */
+#ifndef DSPARK_MARKOV_H
+#define DSPARK_MARKOV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype_t;
+
+typedef enum {
+  DSPARK_OK = 0,
+  DSPARK_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, r <= 0, NaN temperature, overlap */
+  DSPARK_ERR_UNSUPPORTED = 2,        /* dtype pair or shape the library has no kernel for */
+  DSPARK_ERR_WORKSPACE_TOO_SMALL = 3,
+  DSPARK_ERR_DEVICE = 4              /* a HIP runtime call failed (see dspark_markov_last_error) */
+} dspark_status_t;
+
+/* Bytes of workspace an apply (sample_mode = 0) or sample (sample_mode = 1)
+ * call of these sizes needs.  Pure host function. */
+size_t dspark_markov_workspace_bytes(int64_t B, int64_t M, int64_t V, int64_t r, int sample_mode);
+
+/* Zero-fill `bytes` bytes of workspace on `stream` with a device kernel. */
+dspark_status_t dspark_markov_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* Teacher-forced block bias (VanillaMarkov.apply_block_logits, third-party
+ * markov_head.py page).
+ *   base_logits      device, [B, M, V], logits_dtype.
+ *   token_ids        device, [B, M] int64: the predecessor x_{k-1} of each row.
+ *   w1, w2           device, [V, r] each, weight_dtype.
+ *   corrected_logits device, [B, M, V], logits_dtype; may equal base_logits
+ *                    (in place); any other overlap with an input is invalid.
+ * B, M, V >= 0; r > 0 (the page's constructor asserts a positive rank).
+ * B*M*V == 0 is a successful no-op (the page returns base_logits itself). */
+dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_t logits_dtype,
+                                          const int64_t* token_ids, const void* w1,
+                                          const void* w2, dspark_dtype_t weight_dtype,
+                                          int64_t B, int64_t M, int64_t V, int64_t r,
+                                          void* corrected_logits, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/* Left-to-right block sampling (VanillaMarkov.sample_block_tokens and
+ * _sample_tokens, third-party markov_head.py page).
+ *   base_logits          device, [B, M, V].
+ *   first_prev_token_ids device, [B] int64: the verified token before position 0.
+ *   sampled_tokens       device, [B, M] int64 output.
+ *   corrected_logits     device, [B, M, V] output, or NULL for tokens only.
+ *   temperature          greedy argmax (first index on ties) when < 1e-5,
+ *                        negative values included; NaN is invalid.  Otherwise
+ *                        one draw from softmax(corrected / T) per position by
+ *                        Gumbel-max: the first v maximising
+ *                        fmaf(c_v, (float)(log2(e)/T), -log2(-log2(u_v))),
+ *                        u_v = (2*(w >> 9) + 1) * 2^-24 with w the word (v & 3)
+ *                        of Philox4x32-10 (Salmon et al., SC'11) at counter
+ *                        (v >> 2, position_offset + k, batch_offset + b, 0)
+ *                        and key (seed & 0xffffffff, seed >> 32).
+ *   position_offset,     absolute step and batch indices of position 0 / row 0
+ *   batch_offset         for the noise, so that M one-step calls, or a batch
+ *                        split across calls, reproduce one whole call.
+ * M == 0 or B == 0 is a successful no-op.  V == 0 with B*M > 0 is invalid. */
+dspark_status_t dspark_markov_sample_block(const void* base_logits, dspark_dtype_t logits_dtype,
+                                           const int64_t* first_prev_token_ids, const void* w1,
+                                           const void* w2, dspark_dtype_t weight_dtype,
+                                           int64_t B, int64_t M, int64_t V, int64_t r,
+                                           double temperature, uint64_t seed,
+                                           int64_t position_offset, int64_t batch_offset,
+                                           int64_t* sampled_tokens, void* corrected_logits,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Synchronises `stream`, then returns in *bad_rows the number of rows whose
+ * predecessor id was outside [0, V) in the calls made with this workspace
+ * since the last read, and clears the count. */
+dspark_status_t dspark_markov_read_device_error(void* workspace, void* stream, int64_t* bad_rows);
+
+/* Static description of a status code. */
+const char* dspark_status_string(dspark_status_t status);
+
+/* Message of the last HIP runtime failure seen by this thread ("" if none). */
+const char* dspark_markov_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_MARKOV_H */

@@ -1,0 +1,161 @@
+"""DSpark low-rank Markov head on MI355X (gfx950).
+
+Python binding of libdspark_markov.so with the names of the pages'
+VanillaMarkov methods (third-party markov_head.py page):
+
+* ``apply_block_logits(base_logits, token_ids, w1, w2)`` -- teacher-forced
+  bias of every block position by its given predecessor;
+* ``sample_block_tokens(base_logits, first_prev_token_ids, w1, w2,
+  temperature=0.0, ...)`` -- left-to-right sampling, each position biased by
+  the token drawn at the previous one.
+
+Tensors must live on the current HIP device.  ``w1`` is the Embedding
+weight [V, r]; ``w2`` is the Linear(r, V) weight [V, r].  This module only
+marshals arguments (dtype tags, pointers, sizes, the current stream) and
+allocates outputs and workspace with torch: every step of the computation
+runs in the library's kernels.  There is no fallback path: if the library
+is missing, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+__all__ = ["apply_block_logits", "sample_block_tokens", "Workspace", "read_device_error",
+           "workspace_bytes"]
+
+
+def _dtype_tag(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return _lib.DSPARK_F32
+    if t.dtype == torch.bfloat16:
+        return _lib.DSPARK_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; the head takes float32 or bfloat16")
+
+
+def _stream_handle(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def workspace_bytes(B: int, M: int, V: int, r: int, sample: bool) -> int:
+    return int(_lib.load().dspark_markov_workspace_bytes(B, M, V, r, 1 if sample else 0))
+
+
+class Workspace:
+    """Device workspace for a family of calls of at most the given sizes.
+
+    Zero-filled once at creation; the library leaves it ready for the next
+    call.  Calls sharing one workspace must be ordered on one stream."""
+
+    def __init__(self, B: int, M: int, V: int, r: int, sample: bool, device=None):
+        device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        self.nbytes = max(workspace_bytes(B, M, V, r, sample), 256)
+        self.buffer = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        _lib.check(_lib.load().dspark_markov_workspace_init(
+            _ptr(self.buffer), self.nbytes, _stream_handle(device)), "workspace_init")
+
+    @property
+    def ptr(self):
+        return _ptr(self.buffer)
+
+
+def read_device_error(ws: Workspace) -> int:
+    """Rows with out-of-range predecessor ids since the last read (synchronises)."""
+    n = ctypes.c_int64(0)
+    _lib.check(_lib.load().dspark_markov_read_device_error(
+        ws.ptr, _stream_handle(ws.buffer.device), ctypes.byref(n)), "read_device_error")
+    return int(n.value)
+
+
+def _check_weights(w1: torch.Tensor, w2: torch.Tensor):
+    if w1.dim() != 2 or w2.dim() != 2 or w1.shape != w2.shape:
+        raise ValueError(f"w1 and w2 must both be [V, r], got {tuple(w1.shape)} and {tuple(w2.shape)}")
+    if w1.dtype != w2.dtype:
+        raise TypeError("w1 and w2 must share a dtype")
+
+
+def apply_block_logits(base_logits: torch.Tensor, token_ids: torch.Tensor, w1: torch.Tensor,
+                       w2: torch.Tensor, *, out: torch.Tensor | None = None,
+                       workspace: Workspace | None = None) -> torch.Tensor:
+    """Teacher-forced corrected logits base[..., M, V] + bias(token_ids[..., M]).
+
+    ``out`` may be ``base_logits`` itself (in place).  An empty input returns
+    ``base_logits`` (or ``out`` untouched), as the pages' method does."""
+    _check_weights(w1, w2)
+    if base_logits.dim() < 2:
+        raise ValueError("base_logits must be [..., M, V]")
+    V = base_logits.shape[-1]
+    M = base_logits.shape[-2]
+    B = 1
+    for d in base_logits.shape[:-2]:
+        B *= int(d)
+    if tuple(token_ids.shape) != tuple(base_logits.shape[:-1]):
+        raise ValueError(f"token_ids {tuple(token_ids.shape)} must be base_logits.shape[:-1]")
+    if w1.shape[0] != V:
+        raise ValueError(f"weights have vocabulary {w1.shape[0]}, logits {V}")
+    if base_logits.numel() == 0:
+        return base_logits if out is None else out
+    base_c = base_logits.contiguous()
+    ids = token_ids.to(torch.int64).contiguous()
+    w1c, w2c = w1.contiguous(), w2.contiguous()
+    if out is None:
+        out = torch.empty_like(base_c)
+    elif out.shape != base_logits.shape or out.dtype != base_logits.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like base_logits")
+    r = w1.shape[1]
+    if workspace is None:
+        workspace = Workspace(B, M, V, r, sample=False, device=base_c.device)
+    st = _lib.load().dspark_markov_apply_block(
+        _ptr(base_c), _dtype_tag(base_c), _ptr(ids), _ptr(w1c), _ptr(w2c), _dtype_tag(w1c),
+        B, M, V, r, _ptr(out), workspace.ptr, workspace.nbytes, _stream_handle(base_c.device))
+    _lib.check(st, "apply_block_logits")
+    return out
+
+
+def sample_block_tokens(base_logits: torch.Tensor, first_prev_token_ids: torch.Tensor,
+                        w1: torch.Tensor, w2: torch.Tensor, temperature: float | None = 0.0, *,
+                        seed: int = 0, position_offset: int = 0, batch_offset: int = 0,
+                        return_logits: bool = True, tokens_out: torch.Tensor | None = None,
+                        logits_out: torch.Tensor | None = None,
+                        workspace: Workspace | None = None):
+    """Left-to-right block sampling over base_logits [B, M, V].
+
+    Returns ``(sampled_tokens [B, M] int64, corrected_logits [B, M, V] or None)``.
+    ``temperature`` None or below 1e-5 is greedy argmax; otherwise Gumbel-max
+    with Philox4x32-10 noise keyed by ``seed``."""
+    _check_weights(w1, w2)
+    if base_logits.dim() != 3:
+        raise ValueError("base_logits must be [B, M, V]")
+    B, M, V = base_logits.shape
+    if tuple(first_prev_token_ids.shape) != (B,):
+        raise ValueError("first_prev_token_ids must be [B]")
+    if w1.shape[0] != V:
+        raise ValueError(f"weights have vocabulary {w1.shape[0]}, logits {V}")
+    T = 0.0 if temperature is None else float(temperature)
+    dev = base_logits.device
+    if tokens_out is None:
+        tokens_out = torch.empty((B, M), dtype=torch.int64, device=dev)
+    if M == 0:
+        return tokens_out, (base_logits if return_logits else None)
+    base_c = base_logits.contiguous()
+    first = first_prev_token_ids.to(torch.int64).contiguous()
+    w1c, w2c = w1.contiguous(), w2.contiguous()
+    corrected = None
+    if return_logits:
+        corrected = torch.empty_like(base_c) if logits_out is None else logits_out
+    r = w1.shape[1]
+    if workspace is None:
+        workspace = Workspace(B, M, V, r, sample=True, device=dev)
+    st = _lib.load().dspark_markov_sample_block(
+        _ptr(base_c), _dtype_tag(base_c), _ptr(first), _ptr(w1c), _ptr(w2c), _dtype_tag(w1c),
+        B, M, V, r, T, int(seed) & (2**64 - 1), int(position_offset), int(batch_offset),
+        _ptr(tokens_out), _ptr(corrected), workspace.ptr, workspace.nbytes, _stream_handle(dev))
+    _lib.check(st, "sample_block_tokens")
+    return tokens_out, corrected

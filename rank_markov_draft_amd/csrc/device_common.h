@@ -1,0 +1,103 @@
+// device_common.h -- small device helpers shared by the gfx950 kernels of the
+// DSpark low-rank Markov head: bf16 packing, argmax keys and the Philox4x32-10
+// Gumbel noise.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16
+// A bf16 value is the upper half of a binary32 value.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round two floats to bf16 (nearest, ties to even: v_cvt_pk_bf16_f32) and pack.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t t;
+  t[0] = (__bf16)lo;
+  t[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, t);
+}
+
+// ---------------------------------------------------------------- argmax keys
+// A 64-bit key whose unsigned order is the argmax order of the pages'
+// torch.argmax: larger score first, then the smaller vocabulary index.
+// Scores map to an order-preserving 32-bit code (-0 is folded onto +0 and
+// every NaN ranks above +inf, as torch.argmax returns a NaN's index); the
+// low word holds the complement of the index.
+__device__ __forceinline__ uint32_t ordered_code(float s) {
+  s = s + 0.0f;  // -0 -> +0
+  if (s != s) return 0xFFFFFFFFu;
+  uint32_t b = __float_as_uint(s);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t argmax_key(float s, uint32_t v) {
+  return ((uint64_t)ordered_code(s) << 32) | (uint64_t)(0xFFFFFFFFu - v);
+}
+
+__device__ __forceinline__ int64_t key_index(uint64_t key) {
+  return (int64_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Max over the lanes of groups of `width` consecutive lanes (width a power
+// of two <= 64); every lane of the group gets the result.
+template <int width>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t k) {
+#pragma unroll
+  for (int off = width / 2; off >= 1; off >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)k, off, 64);
+    uint32_t hi = __shfl_xor((uint32_t)(k >> 32), off, 64);
+    k = max_u64(k, ((uint64_t)hi << 32) | lo);
+  }
+  return k;
+}
+
+// ---------------------------------------------------------------- noise
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC'11): ten rounds of two 32x32->64 multiplies by the
+// Philox multipliers, a swap of the high halves xored with the neighbour
+// words and the round key; the key advances by the Weyl constants.
+struct Philox4 {
+  uint32_t x0, x1, x2, x3;
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p2 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p2 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p2;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  return Philox4{c0, c1, c2, c3};
+}
+
+// Base-2 Gumbel noise from one Philox word: u = (2*(w >> 9) + 1) * 2^-24 lies
+// in [2^-24, 1 - 2^-24] (exact in fp32), g = -log2(-log2(u)) with the
+// hardware log2 (v_log_f32).
+__device__ __forceinline__ float gumbel2_from_word(uint32_t w) {
+  const float u = (float)(2u * (w >> 9) + 1u) * 0x1p-24f;
+  return -__builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
+}
+
+}  // namespace dspark

@@ -1,0 +1,235 @@
+// dspark_markov.hip -- host side of the C ABI declared in include/dspark_markov.h:
+// argument validation, workspace layout, kernel selection and launch.
+#include "dspark_markov.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "markov_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+// Workspace: a 256-byte control block (device error word, ...), then the
+// per-row argmax keys of a sampling step.
+constexpr size_t kControlBytes = 256;
+
+struct Control {
+  uint32_t bad_rows;
+};
+
+dspark_status_t device_failure(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return DSPARK_ERR_DEVICE;
+}
+
+bool known_dtype(int d) { return d == DSPARK_F32 || d == DSPARK_BF16; }
+
+size_t dtype_bytes(dspark_dtype_t d) { return d == DSPARK_F32 ? 4 : 2; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Byte ranges [a, a+na) and [b, b+nb) intersect.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int64_t vocab_slices(int64_t V) { return (V + 127) / 128; }
+
+// The generic kernel keeps one gathered W1 row (r floats) in LDS.
+constexpr int64_t kGenericMaxRank = 16384;
+
+// The bf16 tile kernel takes the call when both dtypes are bf16, the rank is
+// a multiple of 8 no larger than 512, rows of logits are whole 16-byte
+// vectors and every streamed pointer is 16-byte aligned.
+bool tile_path(dspark_dtype_t ldt, dspark_dtype_t wdt, int64_t V, int64_t r, const void* base,
+               const void* out, const void* w1, const void* w2) {
+  return ldt == DSPARK_BF16 && wdt == DSPARK_BF16 && r % 8 == 0 &&
+         dspark::tile_ks_for_rank(r) != 0 && V % 8 == 0 && aligned16(base) &&
+         (out == nullptr || aligned16(out)) && aligned16(w1) && aligned16(w2);
+}
+
+// Shared checks of both operations.  Returns DSPARK_OK to proceed, or the
+// status to return; *empty is set when there is no work.
+dspark_status_t check_common(int ldt, int wdt, int64_t B, int64_t M, int64_t V, int64_t r,
+                             int64_t* elems) {
+  if (!known_dtype(ldt) || !known_dtype(wdt)) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (B < 0 || M < 0 || V < 0 || r <= 0) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (ldt != wdt) return DSPARK_ERR_UNSUPPORTED;
+  int64_t rows = 0, e = 0, wv = 0;
+  if (!mul_ok(B, M, &rows) || !mul_ok(rows, V, &e) || !mul_ok(V, r, &wv))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  if (V > (int64_t)0x7FFFFFFF) return DSPARK_ERR_UNSUPPORTED;
+  *elems = e;
+  return DSPARK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dspark_markov_workspace_bytes(int64_t B, int64_t M, int64_t V, int64_t r, int sample_mode) {
+  (void)M;
+  (void)r;
+  if (B < 0 || V < 0) return kControlBytes;
+  size_t bytes = kControlBytes;
+  if (sample_mode) bytes += (size_t)B * (size_t)vocab_slices(V) * sizeof(uint64_t);
+  return bytes;
+}
+
+dspark_status_t dspark_markov_workspace_init(void* workspace, size_t bytes, void* stream) {
+  if (!workspace || bytes == 0) return DSPARK_ERR_INVALID_ARGUMENT;
+  const hipError_t e = dspark::launch_fill_zero(workspace, bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return device_failure(e, "workspace fill");
+  return DSPARK_OK;
+}
+
+dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_t logits_dtype,
+                                          const int64_t* token_ids, const void* w1,
+                                          const void* w2, dspark_dtype_t weight_dtype,
+                                          int64_t B, int64_t M, int64_t V, int64_t r,
+                                          void* corrected_logits, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  int64_t elems = 0;
+  dspark_status_t st = check_common(logits_dtype, weight_dtype, B, M, V, r, &elems);
+  if (st != DSPARK_OK) return st;
+  if (elems == 0) return DSPARK_OK;  // numel() == 0: the input is the result
+  if (!base_logits || !token_ids || !w1 || !w2 || !corrected_logits) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < dspark_markov_workspace_bytes(B, M, V, r, 0))
+    return DSPARK_ERR_WORKSPACE_TOO_SMALL;
+  const size_t lbytes = (size_t)elems * dtype_bytes(logits_dtype);
+  const size_t wbytes = (size_t)(V * r) * dtype_bytes(weight_dtype);
+  const size_t ibytes = (size_t)(B * M) * sizeof(int64_t);
+  if (corrected_logits != base_logits && overlaps(corrected_logits, lbytes, base_logits, lbytes))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  if (overlaps(corrected_logits, lbytes, w1, wbytes) || overlaps(corrected_logits, lbytes, w2, wbytes) ||
+      overlaps(corrected_logits, lbytes, token_ids, ibytes))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+
+  dspark::KernelParams p{};
+  p.base = base_logits;
+  p.out = corrected_logits;
+  p.ids = token_ids;
+  p.w1 = w1;
+  p.w2 = w2;
+  p.bad_rows = &((Control*)workspace)->bad_rows;
+  p.rows = B * M;
+  p.V = V;
+  p.r = r;
+  p.M = M;
+  p.mode = dspark::MODE_APPLY;
+  hipError_t e;
+  const bool tile = tile_path(logits_dtype, weight_dtype, V, r, base_logits, corrected_logits, w1, w2);
+  if (!tile && r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
+  if (tile)
+    e = dspark::launch_tile(p, (hipStream_t)stream);
+  else
+    e = dspark::launch_generic(p, logits_dtype == DSPARK_BF16, weight_dtype == DSPARK_BF16,
+                               (hipStream_t)stream);
+  if (e != hipSuccess) return device_failure(e, "apply launch");
+  return DSPARK_OK;
+}
+
+dspark_status_t dspark_markov_sample_block(const void* base_logits, dspark_dtype_t logits_dtype,
+                                           const int64_t* first_prev_token_ids, const void* w1,
+                                           const void* w2, dspark_dtype_t weight_dtype,
+                                           int64_t B, int64_t M, int64_t V, int64_t r,
+                                           double temperature, uint64_t seed,
+                                           int64_t position_offset, int64_t batch_offset,
+                                           int64_t* sampled_tokens, void* corrected_logits,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t elems = 0;
+  dspark_status_t st = check_common(logits_dtype, weight_dtype, B, M, V, r, &elems);
+  if (st != DSPARK_OK) return st;
+  if (std::isnan(temperature)) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (B == 0 || M == 0) return DSPARK_OK;
+  if (V == 0) return DSPARK_ERR_INVALID_ARGUMENT;  // nothing to draw from
+  if (!base_logits || !first_prev_token_ids || !w1 || !w2 || !sampled_tokens)
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < dspark_markov_workspace_bytes(B, M, V, r, 1))
+    return DSPARK_ERR_WORKSPACE_TOO_SMALL;
+  const size_t lbytes = (size_t)elems * dtype_bytes(logits_dtype);
+  const size_t wbytes = (size_t)(V * r) * dtype_bytes(weight_dtype);
+  const size_t tbytes = (size_t)(B * M) * sizeof(int64_t);
+  const void* ins[4] = {base_logits, w1, w2, first_prev_token_ids};
+  const size_t ins_bytes[4] = {lbytes, wbytes, wbytes, (size_t)B * sizeof(int64_t)};
+  for (int i = 0; i < 4; ++i) {
+    if (overlaps(sampled_tokens, tbytes, ins[i], ins_bytes[i])) return DSPARK_ERR_INVALID_ARGUMENT;
+    if (corrected_logits && overlaps(corrected_logits, lbytes, ins[i], ins_bytes[i]))
+      return DSPARK_ERR_INVALID_ARGUMENT;
+  }
+  if (corrected_logits && overlaps(corrected_logits, lbytes, sampled_tokens, tbytes))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+
+  const bool greedy = temperature < 1e-5;
+  dspark::KernelParams p{};
+  p.base = base_logits;
+  p.out = corrected_logits;
+  p.ids = first_prev_token_ids;
+  p.tokens = sampled_tokens;
+  p.w1 = w1;
+  p.w2 = w2;
+  p.bad_rows = &((Control*)workspace)->bad_rows;
+  p.partials = (uint64_t*)((char*)workspace + kControlBytes);
+  p.rows = B;
+  p.V = V;
+  p.r = r;
+  p.M = M;
+  p.batch_offset = batch_offset;
+  p.mode = greedy ? dspark::MODE_GREEDY : dspark::MODE_TEMPERATURE;
+  p.kappa = greedy ? 0.0f : (float)(1.4426950408889634 / temperature);
+  p.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+  p.seed_hi = (uint32_t)(seed >> 32);
+  const bool tile = tile_path(logits_dtype, weight_dtype, V, r, base_logits, corrected_logits, w1, w2);
+  if (!tile && r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
+  p.nparts = tile ? vocab_slices(V) : (V + 255) / 256;
+  hipStream_t s = (hipStream_t)stream;
+  for (int64_t k = 0; k < M; ++k) {
+    p.k = k;
+    p.k_abs = (uint32_t)(position_offset + k);
+    hipError_t e = tile ? dspark::launch_tile(p, s)
+                        : dspark::launch_generic(p, logits_dtype == DSPARK_BF16,
+                                                 weight_dtype == DSPARK_BF16, s);
+    if (e != hipSuccess) return device_failure(e, "sample step launch");
+    e = dspark::launch_reduce(p.partials, p.nparts, B, M, k, sampled_tokens, s);
+    if (e != hipSuccess) return device_failure(e, "sample reduce launch");
+  }
+  return DSPARK_OK;
+}
+
+dspark_status_t dspark_markov_read_device_error(void* workspace, void* stream, int64_t* bad_rows) {
+  if (!workspace || !bad_rows) return DSPARK_ERR_INVALID_ARGUMENT;
+  hipStream_t s = (hipStream_t)stream;
+  Control c{};
+  hipError_t e = hipMemcpyAsync(&c, workspace, sizeof(c), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return device_failure(e, "read device error");
+  *bad_rows = (int64_t)c.bad_rows;
+  e = dspark::launch_fill_zero(workspace, sizeof(Control), s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return device_failure(e, "clear device error");
+  return DSPARK_OK;
+}
+
+const char* dspark_status_string(dspark_status_t status) {
+  switch (status) {
+    case DSPARK_OK: return "ok";
+    case DSPARK_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case DSPARK_ERR_UNSUPPORTED: return "unsupported dtype pair or shape";
+    case DSPARK_ERR_WORKSPACE_TOO_SMALL: return "workspace missing or too small";
+    case DSPARK_ERR_DEVICE: return "HIP runtime failure";
+  }
+  return "unknown status";
+}
+
+const char* dspark_markov_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// markov_kernels.h -- interface between the C ABI (dspark_markov.hip) and the
+// gfx950 kernels (markov_kernels.hip, markov_chain.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+enum { MODE_APPLY = 0, MODE_GREEDY = 1, MODE_TEMPERATURE = 2 };
+
+// Arguments of one launch.  Apply launches process `rows` = B*M rows whose
+// predecessors are ids[n]; sampling-step launches process the B rows of step
+// k, whose predecessor is ids[b] (first_prev) at k = 0 and tokens[b, k-1]
+// after that.
+struct KernelParams {
+  const void* base;      // [B, M, V] logits
+  void* out;             // [B, M, V] corrected logits, or null (tokens only)
+  const int64_t* ids;    // apply: token_ids [B*M]; sampling: first_prev [B]
+  int64_t* tokens;       // sampling: [B, M]
+  const void* w1;        // [V, r]
+  const void* w2;        // [V, r]
+  uint64_t* partials;    // sampling: [rows, nparts] argmax keys
+  uint32_t* bad_rows;    // device error word
+  int64_t rows;
+  int64_t V;
+  int64_t r;
+  int64_t M;
+  int64_t k;             // sampling step
+  int64_t nparts;        // sampling: vocabulary slices per row
+  int64_t batch_offset;  // absolute batch index of row 0 (noise counter)
+  int mode;
+  float kappa;           // (float)(log2(e) / T)
+  uint32_t k_abs;        // absolute position index of step k (noise counter)
+  uint32_t seed_lo;
+  uint32_t seed_hi;
+};
+
+// Rank blocks (of 16) the tile kernel is instantiated for, covering r; 0 if none.
+int tile_ks_for_rank(int64_t r);
+
+hipError_t launch_tile(const KernelParams& p, hipStream_t s);
+hipError_t launch_generic(const KernelParams& p, bool logits_bf16, bool weights_bf16, hipStream_t s);
+hipError_t launch_reduce(const uint64_t* partials, int64_t nparts, int64_t B, int64_t M, int64_t k,
+                         int64_t* tokens, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace dspark

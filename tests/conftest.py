@@ -17,3 +17,14 @@ def oracle_mod():
     from oracle import oracle as o
     o.lib()
     return o
+
+
+@pytest.fixture(scope="session")
+def native():
+    """The built HIP library on a visible GPU (built in-tree if absent)."""
+    import torch
+    from rank_markov_draft_amd import _lib
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    if not os.path.exists(_lib.LIB_PATH):
+        _lib.build()
+    return _lib.load()

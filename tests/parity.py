@@ -1,0 +1,104 @@
+"""Comparison of GPU outputs with the CPU oracle (test infrastructure).
+
+Corrected logits: every element must be bit-identical to the oracle's, or
+lie in the oracle's admissible interval [lo, hi] -- the result of pushing the
+dot product to -/+ 2r*2^-24*sum|e_j W2w[v,j]| (any fp32 accumulation order)
+through the monotone rounding chain.  Elements outside the stated tolerance
+(fp32: 1e-5 relative; bf16: 2e-2 absolute) but inside the interval are
+rounding flips; they are counted and reported.
+
+Tokens: the GPU token of each (b, k) must be exactly the oracle's selection
+applied to the GPU's own (validated) corrected row; tokens that differ from
+the oracle's selection on the oracle's own row are near-ties, counted.
+Sampling is checked conditionally per step: the oracle is teacher-forced
+with the GPU's previous tokens, so one near-tie cannot cascade.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+from oracle import oracle as orc
+from rank_markov_draft_amd import workloads as wl
+
+
+@dataclasses.dataclass
+class LogitReport:
+    elements: int = 0
+    mismatches: int = 0      # not bit-identical to the oracle
+    flips: int = 0           # beyond the stated tolerance, inside the admissible interval
+    max_abs_diff: float = 0.0
+
+
+@dataclasses.dataclass
+class TokenReport:
+    tokens: int = 0
+    near_ties: int = 0       # GPU token != oracle token on the oracle's own row
+    noise_ties: int = 0      # GPU token == runner-up of a near-tied score on its own row
+
+
+def as_f32(a: np.ndarray) -> np.ndarray:
+    return wl.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a.astype(np.float32)
+
+
+def tolerance_ok(gpu: np.ndarray, ref: np.ndarray, is_bf16: bool) -> np.ndarray:
+    d = np.abs(gpu.astype(np.float64) - ref.astype(np.float64))
+    if is_bf16:
+        return d <= 2e-2
+    return d <= 1e-5 * np.maximum(np.abs(ref.astype(np.float64)), 1e-2)
+
+
+def check_logits(gpu, ref, base, ids, w1, w2, report: LogitReport | None = None) -> LogitReport:
+    """gpu, ref: oracle-typed arrays [R, M, V] (or [N, V]); base/ids/w1/w2 the
+    oracle's inputs for the same rows (ids: the predecessor of every row)."""
+    rep = report or LogitReport()
+    V = gpu.shape[-1]
+    g = as_f32(gpu).reshape(-1, V)
+    o = as_f32(ref).reshape(-1, V)
+    rep.elements += g.size
+    same = (g.view(np.uint32) == o.view(np.uint32)) | (np.isnan(g) & np.isnan(o))
+    bad_r, bad_c = np.nonzero(~same)
+    rep.mismatches += int(bad_r.size)
+    if bad_r.size:
+        rep.max_abs_diff = max(rep.max_abs_diff, float(np.max(np.abs(g[bad_r, bad_c] - o[bad_r, bad_c]))))
+        lo, mid, hi = orc.logit_bounds(base, ids, w1, w2, bad_r, bad_c)
+        gv = g[bad_r, bad_c]
+        assert np.array_equal(mid, o[bad_r, bad_c]), "oracle bounds disagree with oracle values"
+        inside = (lo <= gv) & (gv <= hi)
+        if not inside.all():
+            i = int(np.argmin(inside))
+            raise AssertionError(
+                f"{int((~inside).sum())} of {g.size} corrected logits outside the admissible interval; "
+                f"first at row {bad_r[i]} col {bad_c[i]}: gpu {gv[i]!r} oracle {o[bad_r[i], bad_c[i]]!r} "
+                f"interval [{lo[i]!r}, {hi[i]!r}]")
+        rep.flips += int((~tolerance_ok(gv, o[bad_r, bad_c], gpu.dtype == np.uint16)).sum())
+    return rep
+
+
+def check_tokens(gpu_tokens, gpu_rows, oracle_rows, temperature, seed, b_abs, k_abs,
+                 report: TokenReport | None = None) -> TokenReport:
+    """gpu_tokens [N]; gpu_rows/oracle_rows: oracle-typed [N, V] corrected rows;
+    b_abs/k_abs [N] noise indices of each row.
+
+    Greedy: the GPU token must be exactly the first argmax of its own row.
+    Temperature: it must be the oracle's Gumbel-max selection on that row, or
+    -- the device log2 may differ from libm's by an ulp -- the runner-up when
+    the top-2 scores are within 1e-5 relative (a counted noise near-tie)."""
+    rep = report or TokenReport()
+    greedy = temperature < 1e-5
+    for i in range(len(gpu_tokens)):
+        tg = int(gpu_tokens[i])
+        t_own, best, second, runner = orc.select_token(gpu_rows[i], temperature, seed, b_abs[i], k_abs[i])
+        rep.tokens += 1
+        if tg != t_own:
+            assert not greedy, f"row {i}: GPU token {tg} is not the first argmax {t_own} of its own row"
+            assert runner == tg and abs(best - second) <= 1e-5 * max(1.0, abs(best)), (
+                f"row {i}: GPU token {tg} vs oracle selection {t_own} on the same row is not a near-tie "
+                f"(scores {best!r}, {second!r}, runner-up {runner})")
+            rep.noise_ties += 1
+        if oracle_rows is not None:
+            t_ref = orc.select_token(oracle_rows[i], temperature, seed, b_abs[i], k_abs[i])[0]
+            if t_ref != tg:
+                rep.near_ties += 1
+    return rep

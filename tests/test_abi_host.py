@@ -1,0 +1,109 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol that
+include/dspark_markov.h declares, and rejects bad arguments on the host
+(before any device work) with the documented status codes.  No call here
+reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rank_markov_draft_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark_markov.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        _lib.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings(L):
+    for code in range(5):
+        assert L.dspark_status_string(code)
+    assert L.dspark_status_string(0) == b"ok"
+    assert L.dspark_markov_last_error() == b""
+
+
+def test_workspace_bytes(L):
+    assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 0) == 256
+    assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 1) == 256 + 64 * 1010 * 8
+    assert L.dspark_markov_workspace_bytes(256, 8, 151936, 256, 1) == 256 + 256 * 1187 * 8
+
+
+FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: every call below fails validation
+
+
+@pytest.mark.parametrize("args,code", [
+    # (logits dtype, weight dtype, B, M, V, r) -> status
+    ((1, 1, 2, 3, 64, 0), 1),        # rank must be positive
+    ((1, 1, 2, 3, 64, -4), 1),
+    ((1, 1, -1, 3, 64, 16), 1),      # negative sizes
+    ((1, 1, 2, -3, 64, 16), 1),
+    ((1, 1, 2, 3, -64, 16), 1),
+    ((0, 1, 2, 3, 64, 16), 2),       # mixed dtype pair
+    ((7, 7, 2, 3, 64, 16), 1),       # unknown dtype tag
+    ((1, 1, 2**40, 2**20, 2**20, 16), 1),   # element count overflows int64
+])
+def test_apply_argument_errors(L, args, code):
+    ldt, wdt, B, M, V, r = args
+    st = L.dspark_markov_apply_block(FAKE, ldt, FAKE, FAKE, FAKE, wdt, B, M, V, r, FAKE, FAKE, 1 << 20, None)
+    assert st == code
+
+
+def test_apply_empty_is_ok_and_touches_nothing(L):
+    assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 0, 5, 64, 16, FAKE, None, 0, None) == 0
+    assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 3, 0, 64, 16, FAKE, None, 0, None) == 0
+    assert L.dspark_markov_apply_block(None, 1, None, None, None, 1, 3, 5, 0, 16, None, None, 0, None) == 0
+
+
+def test_apply_null_pointers_and_workspace(L):
+    assert L.dspark_markov_apply_block(None, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, FAKE, 256, None) == 1
+    assert L.dspark_markov_apply_block(FAKE, 1, None, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, FAKE, 256, None) == 1
+    assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, None, FAKE, 256, None) == 1
+    assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, None, 256, None) == 3
+    assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, FAKE, 255, None) == 3
+
+
+def test_apply_overlap_rejected(L):
+    base = 0x200000
+    out = ctypes.c_void_p(base + 64)          # partial overlap with base
+    st = L.dspark_markov_apply_block(ctypes.c_void_p(base), 1, FAKE, ctypes.c_void_p(0x900000),
+                                     ctypes.c_void_p(0xA00000), 1, 2, 3, 64, 16, out, FAKE, 256, None)
+    assert st == 1
+
+
+def _sample(L, T=0.0, B=2, M=3, V=64, r=16, first=FAKE, tok=FAKE, ws=FAKE, wsb=1 << 20):
+    return L.dspark_markov_sample_block(FAKE, 1, first, FAKE, FAKE, 1, B, M, V, r, T, 0, 0, 0, tok, None,
+                                        ws, wsb, None)
+
+
+def test_sample_argument_errors(L):
+    assert _sample(L, T=float("nan")) == 1
+    assert _sample(L, r=0) == 1
+    assert _sample(L, V=0) == 1          # nothing to draw from
+    assert _sample(L, M=0) == 0          # empty work
+    assert _sample(L, B=0) == 0
+    assert _sample(L, first=None) == 1
+    assert _sample(L, tok=None) == 1
+    assert _sample(L, ws=None) == 3
+    assert _sample(L, wsb=256) == 3

@@ -1,0 +1,319 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+The five workloads run at their full sizes in the launch configuration the
+benchmark uses.  Where the oracle would take too long on every row, it is
+run on a sample of rows (all positions of the sampled batch rows for the
+chains).  Element rule: bit-identical to the oracle or inside its admissible
+interval for fp32 accumulation in any order; token rule: exactly the
+selection on the GPU's own validated row (see tests/parity.py).
+"""
+import dataclasses
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import rank_markov_draft_amd as rmd
+from oracle import oracle as orc
+from rank_markov_draft_amd import workloads as wl
+from tests import parity
+from tests.gpu_util import device_inputs, from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+REPORT = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out",
+                      "parity_report.txt")
+
+
+def _report(name, **kw):
+    """Counts of each parity check, appended to gpurun_out/parity_report.txt."""
+    line = f"[parity] {name}: " + ", ".join(f"{k}={v}" for k, v in kw.items())
+    print(line)
+    os.makedirs(os.path.dirname(REPORT), exist_ok=True)
+    with open(REPORT, "a") as f:
+        f.write(line + "\n")
+
+
+def _chain_ids(first_prev, tokens):
+    """Predecessors of a chain given its tokens: [first_prev, tok_0 .. tok_{M-2}]."""
+    return np.concatenate([first_prev[:, None], tokens[:, :-1]], axis=1)
+
+
+def run_apply(inp):
+    d = device_inputs({k: inp[k] for k in ("base", "token_ids", "w1", "w2")})
+    out = rmd.apply_block_logits(d["base"], d["token_ids"], d["w1"], d["w2"])
+    torch.cuda.synchronize()
+    return from_dev(out)
+
+
+def run_sample(inp, T, seed=0, return_logits=True, position_offset=0, batch_offset=0):
+    d = device_inputs({k: inp[k] for k in ("base", "first_prev", "w1", "w2")})
+    tok, corr = rmd.sample_block_tokens(d["base"], d["first_prev"], d["w1"], d["w2"], T, seed=seed,
+                                        return_logits=return_logits, position_offset=position_offset,
+                                        batch_offset=batch_offset)
+    torch.cuda.synchronize()
+    return from_dev(tok), (from_dev(corr) if corr is not None else None)
+
+
+def check_apply(inp, gpu, rows=None, name=""):
+    """Oracle apply on all rows (rows=None) or on the flattened rows given."""
+    B, M, V = inp["base"].shape
+    if rows is None:
+        ref = orc.apply_block(inp["base"], inp["token_ids"], inp["w1"], inp["w2"])
+        rep = parity.check_logits(gpu, ref, inp["base"], inp["token_ids"], inp["w1"], inp["w2"])
+    else:
+        base = inp["base"].reshape(B * M, 1, V)[rows]
+        ids = inp["token_ids"].reshape(B * M, 1)[rows]
+        ref = orc.apply_block(base, ids, inp["w1"], inp["w2"])
+        rep = parity.check_logits(gpu.reshape(B * M, 1, V)[rows], ref, base, ids, inp["w1"], inp["w2"])
+    _report(name, **dataclasses.asdict(rep))
+    return rep
+
+
+def check_chain(inp, T, seed, tok, corr, brows=None, name=""):
+    """Conditional per-step check of a sampled chain on batch rows `brows`."""
+    B, M, V = inp["base"].shape
+    brows = np.arange(B) if brows is None else np.asarray(brows)
+    assert tok.shape == (B, M) and tok.min() >= 0 and tok.max() < V
+    ids = _chain_ids(inp["first_prev"], tok)[brows]
+    base = inp["base"][brows]
+    ref = orc.apply_block(base, ids, inp["w1"], inp["w2"])
+    lrep = parity.check_logits(corr[brows], ref, base, ids, inp["w1"], inp["w2"])
+    b_abs = np.repeat(brows, M)
+    k_abs = np.tile(np.arange(M), len(brows))
+    trep = parity.check_tokens(tok[brows].reshape(-1), corr[brows].reshape(-1, V), ref.reshape(-1, V),
+                               T, seed, b_abs, k_abs)
+    _report(name, **dataclasses.asdict(lrep), **dataclasses.asdict(trep))
+    return lrep, trep
+
+
+# ------------------------------------------------------------ the five workloads
+def test_tiny_fp32_apply_and_greedy(native):
+    w = wl.WORKLOADS["tiny_fp32"]
+    inp = wl.make_inputs(w)
+    check_apply(inp, run_apply(inp), name=w.name + " apply")
+    tok, corr = run_sample(inp, 0.0)
+    check_chain(inp, 0.0, 0, tok, corr, name=w.name + " greedy")
+
+
+def test_teacher_forced_320(native):
+    w = wl.WORKLOADS["teacher_forced_320"]
+    inp = wl.make_inputs(w)
+    rep = check_apply(inp, run_apply(inp), name=w.name)
+    assert rep.mismatches <= 1e-4 * rep.elements
+
+
+def test_greedy_draft_64x5(native):
+    w = wl.WORKLOADS["greedy_draft_64x5"]
+    inp = wl.make_inputs(w)
+    tok, corr = run_sample(inp, 0.0)
+    lrep, trep = check_chain(inp, 0.0, 0, tok, corr, name=w.name)
+    assert lrep.mismatches <= 1e-4 * lrep.elements
+    # tokens-only call draws the same tokens
+    tok2, none = run_sample(inp, 0.0, return_logits=False)
+    assert none is None and np.array_equal(tok, tok2)
+
+
+def test_temperature_draft_256x8(native):
+    w = wl.WORKLOADS["temperature_draft_256x8"]
+    inp = wl.make_inputs(w)
+    tok, corr = run_sample(inp, w.temperature, seed=w.gumbel_seed)
+    brows = np.linspace(0, w.B - 1, 24).astype(np.int64)
+    lrep, trep = check_chain(inp, w.temperature, w.gumbel_seed, tok, corr, brows=brows, name=w.name)
+    assert trep.noise_ties <= 2
+    # the timed configuration returns tokens only: same draws
+    tok2, _ = run_sample(inp, w.temperature, seed=w.gumbel_seed, return_logits=False)
+    assert np.array_equal(tok, tok2)
+
+
+def test_teacher_forced_2560_zipf(native):
+    w = wl.WORKLOADS["teacher_forced_2560_zipf"]
+    inp = wl.make_inputs(w)
+    gpu = run_apply(inp)
+    flat_ids = inp["token_ids"].reshape(-1)
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([
+        rng.choice(flat_ids.size, 96, replace=False),
+        np.nonzero(flat_ids == 0)[0][:8],              # the most frequent predecessor
+        np.array([0, 31, 32, flat_ids.size - 1])]))    # tile edges
+    check_apply(inp, gpu, rows=rows, name=w.name)
+
+
+# ------------------------------------------------------------ shapes and edges
+@pytest.mark.parametrize("B,M,V,r,dtype", [
+    (3, 7, 1000, 24, wl.BF16),      # ragged rows and last vocabulary tile, rank padded to 32
+    (1, 1, 8, 8, wl.BF16),          # smallest tile case
+    (2, 33, 4104, 40, wl.BF16),     # 66 rows (two tiles + 2), rank 40 -> 64
+    (5, 5, 1001, 16, wl.BF16),      # V not a multiple of 8: generic kernel
+    (2, 3, 640, 520, wl.BF16),      # rank above the tile kernel's 512: generic kernel
+    (4, 6, 777, 12, wl.F32),        # fp32 generic kernel
+    (2, 5, 2048, 512, wl.BF16),     # rank 512 tile kernel
+])
+def test_apply_shapes(native, B, M, V, r, dtype):
+    w = dataclasses.replace(wl.WORKLOADS["teacher_forced_320"], dtype=dtype)
+    inp = wl.make_inputs(w, B=B, M=M, V=V, r=r, seed=B * 1000 + V)
+    check_apply(inp, run_apply(inp), name=f"apply B{B} M{M} V{V} r{r} dt{dtype}")
+
+
+@pytest.mark.parametrize("T", [0.0, 0.8])
+@pytest.mark.parametrize("B,M,V,r,dtype", [
+    (3, 4, 1000, 24, wl.BF16),
+    (33, 2, 4104, 64, wl.BF16),
+    (2, 3, 1001, 16, wl.BF16),
+    (4, 5, 777, 12, wl.F32),
+])
+def test_sample_shapes(native, T, B, M, V, r, dtype):
+    w = dataclasses.replace(wl.WORKLOADS["greedy_draft_64x5"], dtype=dtype)
+    inp = wl.make_inputs(w, B=B, M=M, V=V, r=r, seed=7 + B + V)
+    tok, corr = run_sample(inp, T, seed=11)
+    check_chain(inp, T, 11, tok, corr, name=f"sample T{T} B{B} M{M} V{V} r{r} dt{dtype}")
+
+
+def test_in_place_apply(native):
+    w = wl.WORKLOADS["teacher_forced_320"]
+    inp = wl.make_inputs(w, B=4, M=5, V=4096, r=256)
+    d = device_inputs(inp)
+    expect = from_dev(rmd.apply_block_logits(d["base"], d["token_ids"], d["w1"], d["w2"]))
+    rmd.apply_block_logits(d["base"], d["token_ids"], d["w1"], d["w2"], out=d["base"])
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(d["base"]), expect)
+
+
+def test_empty_inputs(native):
+    w = wl.WORKLOADS["teacher_forced_320"]
+    inp = wl.make_inputs(w, B=2, M=3, V=64, r=16)
+    d = device_inputs(inp)
+    out = rmd.apply_block_logits(d["base"][:, :0], d["token_ids"][:, :0], d["w1"], d["w2"])
+    assert out.shape == (2, 0, 64)
+    tok, corr = rmd.sample_block_tokens(d["base"][:, :0], d["first_prev"], d["w1"], d["w2"])
+    assert tok.shape == (2, 0)
+    tok, corr = rmd.sample_block_tokens(d["base"][:0], d["first_prev"][:0], d["w1"], d["w2"])
+    assert tok.shape == (0, 3)
+
+
+def test_out_of_range_ids_flag_device_error(native):
+    w = wl.WORKLOADS["teacher_forced_320"]
+    inp = wl.make_inputs(w, B=2, M=4, V=1024, r=32)
+    ids = inp["token_ids"].copy()
+    ids[0, 1] = 1024
+    ids[1, 3] = -5
+    d = device_inputs(dict(inp, token_ids=ids))
+    ws = rmd.Workspace(2, 4, 1024, 32, sample=False)
+    out = from_dev(rmd.apply_block_logits(d["base"], d["token_ids"], d["w1"], d["w2"], workspace=ws))
+    assert rmd.read_device_error(ws) == 2
+    assert rmd.read_device_error(ws) == 0            # the read clears the count
+    # a bad row keeps its base logits (zero bias); good rows match the oracle
+    assert np.array_equal(out[0, 1], inp["base"][0, 1]) and np.array_equal(out[1, 3], inp["base"][1, 3])
+    good = np.array([0, 2, 3, 4, 5, 6])
+    check_apply(dict(inp, token_ids=ids), out, rows=good, name="apply good rows beside bad ids")
+
+
+def test_invalid_arguments_rejected_on_host(native):
+    from rank_markov_draft_amd import _lib
+    L = native
+    w = wl.WORKLOADS["teacher_forced_320"]
+    inp = wl.make_inputs(w, B=2, M=2, V=64, r=16)
+    d = device_inputs(inp)
+    ws = rmd.Workspace(2, 2, 64, 16, sample=True)
+    out = torch.zeros_like(d["base"])
+    p = lambda t: t.data_ptr()
+    s = torch.cuda.current_stream().cuda_stream
+    # r <= 0
+    assert L.dspark_markov_apply_block(p(d["base"]), 1, p(d["token_ids"]), p(d["w1"]), p(d["w2"]), 1,
+                                       2, 2, 64, 0, p(out), ws.ptr, ws.nbytes, s) == 1
+    # mixed dtype pair
+    assert L.dspark_markov_apply_block(p(d["base"]), 0, p(d["token_ids"]), p(d["w1"]), p(d["w2"]), 1,
+                                       2, 2, 64, 16, p(out), ws.ptr, ws.nbytes, s) == 2
+    # workspace too small
+    assert L.dspark_markov_apply_block(p(d["base"]), 1, p(d["token_ids"]), p(d["w1"]), p(d["w2"]), 1,
+                                       2, 2, 64, 16, p(out), ws.ptr, 8, s) == 3
+    # partial overlap of output and input
+    assert L.dspark_markov_apply_block(p(d["base"]), 1, p(d["token_ids"]), p(d["w1"]), p(d["w2"]), 1,
+                                       2, 2, 64, 16, p(d["base"]) + 2, ws.ptr, ws.nbytes, s) == 1
+    # NaN temperature
+    tok = torch.zeros((2, 2), dtype=torch.int64, device="cuda")
+    assert L.dspark_markov_sample_block(p(d["base"]), 1, p(d["first_prev"]), p(d["w1"]), p(d["w2"]), 1,
+                                        2, 2, 64, 16, float("nan"), 0, 0, 0, p(tok), None, ws.ptr,
+                                        ws.nbytes, s) == 1
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0      # nothing was written
+
+
+# ------------------------------------------------------------ invariants on the GPU
+def test_equal_predecessors_identical_rows(native):
+    """The vanilla bias is a pure function of the previous token: rows with
+    equal predecessor and equal base rows are bit-identical, across row
+    tiles and vocabulary slices."""
+    w = wl.WORKLOADS["teacher_forced_320"]
+    inp = wl.make_inputs(w, B=20, M=5, V=8192, r=256)
+    base = inp["base"].copy()
+    base[:] = base[0, 0]
+    rng = np.random.default_rng(0)
+    ids = rng.choice(np.array([3, 77, 8191]), size=(20, 5)).astype(np.int64)
+    out = run_apply(dict(inp, base=base, token_ids=ids)).reshape(100, -1)
+    for t in (3, 77, 8191):
+        rows = out[ids.reshape(-1) == t]
+        assert all(np.array_equal(rows[0], x) for x in rows[1:])
+
+
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_zero_w2_is_identity(native, dtype):
+    w = dataclasses.replace(wl.WORKLOADS["teacher_forced_320"], dtype=dtype)
+    inp = wl.make_inputs(w, B=3, M=5, V=4096, r=64)
+    inp["w2"] = np.zeros_like(inp["w2"])
+    out = run_apply(inp)
+    assert np.array_equal(parity.as_f32(out), parity.as_f32(inp["base"]))
+    tok, corr = run_sample(inp, 0.0)
+    assert np.array_equal(parity.as_f32(corr), parity.as_f32(inp["base"]))
+    assert np.array_equal(tok, np.argmax(parity.as_f32(inp["base"]), axis=-1))
+
+
+@pytest.mark.parametrize("T", [0.0, 9.99e-6, -2.0])
+def test_small_temperature_is_greedy(native, T):
+    w = wl.WORKLOADS["greedy_draft_64x5"]
+    inp = wl.make_inputs(w, B=16, M=5, V=8192, r=256)
+    g, cg = run_sample(inp, 0.0)
+    t, ct = run_sample(inp, T, seed=5)
+    assert np.array_equal(g, t) and np.array_equal(cg, ct)
+
+
+@pytest.mark.parametrize("T", [0.0, 0.7])
+def test_chain_equals_single_steps(native, T):
+    """One M-step call equals M one-step calls fed the previous tokens with
+    position_offset = k (GPU against GPU, bitwise)."""
+    w = wl.WORKLOADS["greedy_draft_64x5"]
+    inp = wl.make_inputs(w, B=8, M=5, V=8192, r=256)
+    full_t, full_c = run_sample(inp, T, seed=3)
+    prev = inp["first_prev"].copy()
+    for k in range(5):
+        step = dict(inp, base=np.ascontiguousarray(inp["base"][:, k:k + 1]), first_prev=prev)
+        t, c = run_sample(step, T, seed=3, position_offset=k)
+        assert np.array_equal(t[:, 0], full_t[:, k]) and np.array_equal(c[:, 0], full_c[:, k])
+        prev = t[:, 0].copy()
+
+
+def test_batch_split_equals_whole(native):
+    w = wl.WORKLOADS["temperature_draft_256x8"]
+    inp = wl.make_inputs(w, B=12, M=3, V=8192, r=256)
+    whole, _ = run_sample(inp, 0.7, seed=9)
+    part = dict(inp, base=np.ascontiguousarray(inp["base"][4:10]),
+                first_prev=np.ascontiguousarray(inp["first_prev"][4:10]))
+    t, _ = run_sample(part, 0.7, seed=9, batch_offset=4)
+    assert np.array_equal(t, whole[4:10])
+
+
+def test_deterministic_and_workspace_reuse(native):
+    w = wl.WORKLOADS["greedy_draft_64x5"]
+    inp = wl.make_inputs(w, B=32, M=5, V=16384, r=256)
+    d = device_inputs(inp)
+    ws = rmd.Workspace(32, 5, 16384, 256, sample=True)
+    outs = []
+    for T in (0.0, 0.9, 0.0, 0.9):
+        tok, corr = rmd.sample_block_tokens(d["base"], d["first_prev"], d["w1"], d["w2"], T, seed=1,
+                                            workspace=ws)
+        outs.append((from_dev(tok), from_dev(corr)))
+    assert np.array_equal(outs[0][0], outs[2][0]) and np.array_equal(outs[0][1], outs[2][1])
+    assert np.array_equal(outs[1][0], outs[3][0]) and np.array_equal(outs[1][1], outs[3][1])
+    assert rmd.read_device_error(ws) == 0
