@@ -70,21 +70,58 @@ def time_calls(fn, n_sets, steps, warmup, torch):
 
 
 def cpu_baseline(w, inp, np):
-    """The oracle as it stands, on the host cores, on a bounded sample of the
-    same workload (the first 16 of the 64 chains, all 5 positions)."""
+    """The oracle as it stands, on the host cores: the same workload, timed
+    over a few whole calls (a bounded sample of seconds of CPU work)."""
     from oracle import oracle as orc
     cores = len(os.sched_getaffinity(0))
-    nb = 16
-    base = np.ascontiguousarray(inp["base"][:nb])
-    first = np.ascontiguousarray(inp["first_prev"][:nb])
+    reps = 3
     orc.lib()
     t0 = time.perf_counter()
-    orc.sample_block(base, first, inp["w1"], inp["w2"], temperature=0.0, n_threads=cores)
-    dt = time.perf_counter() - t0
-    elems = nb * w.M * w.V
+    for _ in range(reps):
+        orc.sample_block(inp["base"], inp["first_prev"], inp["w1"], inp["w2"], temperature=0.0,
+                         n_threads=cores)
+    dt = (time.perf_counter() - t0) / reps
+    elems = w.B * w.M * w.V
     return {"value": elems / dt, "unit": "corrected-logit elems/s", "cores": cores, "kind": "oracle",
-            "sample": f"{nb} of {w.B} chains x {w.M} positions, V={w.V}, r={w.r}, greedy, "
-                      f"{dt:.2f} s wall", "tokens_per_s": nb * w.M / dt}
+            "sample": f"the whole workload ({w.B} chains x {w.M} positions, V={w.V}, r={w.r}, greedy), "
+                      f"{reps} calls, {dt:.2f} s wall each", "tokens_per_s": w.B * w.M / dt}
+
+
+def measure_extra(name, rmd, wl, torch, np, steps=10, warmup=3):
+    """Time one other workload (a parity case, reported beside the main line)."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    per_set = 2 * w.B * w.M * w.V * 2 + 2 * w.V * w.r * 2
+    n_sets = max(2, int(np.ceil(600e6 / per_set)))
+    sets = []
+    for i in range(n_sets):
+        d = {k: to_dev(inp[k], torch, np) for k in ("base", "first_prev", "token_ids", "w1", "w2")}
+        d["out"] = torch.empty_like(d["base"]) if (w.mode == "apply" or w.return_logits) else None
+        d["tok"] = torch.empty((w.B, w.M), dtype=torch.int64, device="cuda")
+        d["ws"] = rmd.Workspace(w.B, w.M, w.V, w.r, sample=(w.mode != "apply"))
+        sets.append(d)
+    del inp
+
+    def call(i):
+        d = sets[i]
+        if w.mode == "apply":
+            rmd.apply_block_logits(d["base"], d["token_ids"], d["w1"], d["w2"], out=d["out"], workspace=d["ws"])
+        else:
+            rmd.sample_block_tokens(d["base"], d["first_prev"], d["w1"], d["w2"], w.temperature,
+                                    seed=w.gumbel_seed, return_logits=w.return_logits, tokens_out=d["tok"],
+                                    logits_out=d["out"], workspace=d["ws"])
+
+    wall, per = time_calls(call, n_sets, steps, warmup, torch)
+    ms = float(np.mean(per))
+    alg = algorithmic_bytes_apply(w) if w.mode == "apply" else algorithmic_bytes_sample(w, w.return_logits)
+    res = {"ms_per_call": ms, "elems_per_s": w.B * w.M * w.V / (ms * 1e-3),
+           "algorithmic_GBps": alg / (ms * 1e-3) / 1e9,
+           "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": alg}
+    if w.mode != "apply":
+        res["tokens_per_s"] = w.B * w.M / (ms * 1e-3)
+    del sets
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -93,6 +130,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' timings")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -158,6 +196,11 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "algorithmic_bytes_per_launch": alg, "launch_ms": call_ms},
     }
+    del sets
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        result["other_workloads"] = {n: measure_extra(n, rmd, wl, torch, np) for n in
+                                     ("teacher_forced_320", "teacher_forced_2560_zipf", "temperature_draft_256x8")}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, np)
     print(json.dumps(result))

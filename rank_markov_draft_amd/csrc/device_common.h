@@ -27,6 +27,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, t);
 }
 
+// corrected = round(fp32(base) + fp32(bias)) for a pair of bf16 logits, with
+// the bias first rounded to bf16 (the Linear's output dtype).
+__device__ __forceinline__ uint32_t add_bias_pair(uint32_t base2, float acc_lo, float acc_hi) {
+  const uint32_t bias2 = pack_bf16x2(acc_lo, acc_hi);
+  return pack_bf16x2(bf16_lo(base2) + bf16_lo(bias2), bf16_hi(base2) + bf16_hi(bias2));
+}
+
 // ---------------------------------------------------------------- argmax keys
 // A 64-bit key whose unsigned order is the argmax order of the pages'
 // torch.argmax: larger score first, then the smaller vocabulary index.
@@ -61,6 +68,26 @@ __device__ __forceinline__ uint64_t group_max_u64(uint64_t k) {
     k = max_u64(k, ((uint64_t)hi << 32) | lo);
   }
   return k;
+}
+
+// Order-preserving 16-bit code of a bf16 value (-0 folded onto +0, every
+// NaN above +inf), for reductions that only ever compare bf16 values.
+__device__ __forceinline__ uint32_t ordered_code_bf16(uint32_t bits16) {
+  if (bits16 == 0x8000u) bits16 = 0u;                                  // -0 -> +0
+  if ((bits16 & 0x7F80u) == 0x7F80u && (bits16 & 0x007Fu)) return 0xFFFFu;  // NaN
+  return (bits16 & 0x8000u) ? (~bits16 & 0xFFFFu) : (bits16 | 0x8000u);
+}
+
+// Unsigned max over the 64 lanes of a wave with DPP moves (no LDS traffic);
+// the result is valid in lane 63.
+__device__ __forceinline__ uint32_t wave_max_u32_to_lane63(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return v;
 }
 
 // ---------------------------------------------------------------- noise

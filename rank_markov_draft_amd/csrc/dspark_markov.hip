@@ -14,13 +14,49 @@ namespace {
 
 thread_local std::string g_last_error;
 
-// Workspace: a 256-byte control block (device error word, ...), then the
-// per-row argmax keys of a sampling step.
+// Workspace layout:
+//   [0, 256)      control block: the device error word, the grid arrival
+//                 counter and the synchronisation-failure count of the
+//                 persistent chain, each on its own 64-byte line;
+//   partials      per-(row, vocabulary slice) argmax keys of one sampling
+//                 step (step-by-step path), B * ceil(V/128) words;
+//   chain sync    arrival counters and release words of the persistent
+//                 chain (kChainSyncBytes);
+//   keys          device-wide argmax keys of the persistent chain, per
+//                 (step, key group, row): M * 8 * 64 * kKeyPad words.
 constexpr size_t kControlBytes = 256;
 
 struct Control {
   uint32_t bad_rows;
+  uint32_t pad0[15];
+  uint32_t sync_failures;
+  uint32_t pad1[15];
 };
+static_assert(sizeof(Control) <= kControlBytes, "control block");
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t partials_bytes(int64_t B, int64_t V) {
+  return align256((size_t)B * (size_t)((V + 127) / 128) * sizeof(uint64_t));
+}
+
+size_t chain_keys_bytes(int64_t M) {
+  return dspark::kChainSyncBytes + (size_t)M * (size_t)dspark::chain_key_groups() *
+                                       (size_t)dspark::chain_max_rows() * dspark::kKeyPad * sizeof(uint64_t);
+}
+
+// Compute units of the current device, cached per device.
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+    cache[dev] = prop.multiProcessorCount;
+  }
+  return cache[dev];
+}
 
 dspark_status_t device_failure(hipError_t e, const char* what) {
   g_last_error = std::string(what) + ": " + hipGetErrorString(e);
@@ -77,11 +113,10 @@ dspark_status_t check_common(int ldt, int wdt, int64_t B, int64_t M, int64_t V, 
 extern "C" {
 
 size_t dspark_markov_workspace_bytes(int64_t B, int64_t M, int64_t V, int64_t r, int sample_mode) {
-  (void)M;
   (void)r;
-  if (B < 0 || V < 0) return kControlBytes;
+  if (B < 0 || V < 0 || M < 0) return kControlBytes;
   size_t bytes = kControlBytes;
-  if (sample_mode) bytes += (size_t)B * (size_t)vocab_slices(V) * sizeof(uint64_t);
+  if (sample_mode) bytes += partials_bytes(B, V) + chain_keys_bytes(M);
   return bytes;
 }
 
@@ -192,6 +227,32 @@ dspark_status_t dspark_markov_sample_block(const void* base_logits, dspark_dtype
   if (!tile && r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
   p.nparts = tile ? vocab_slices(V) : (V + 255) / 256;
   hipStream_t s = (hipStream_t)stream;
+  Control* ctl = (Control*)workspace;
+
+  // Greedy bf16 chains that fit the persistent kernel run in one launch.
+  const int cus = device_cus();
+  if (tile && greedy && cus > 0 && B <= dspark::chain_max_rows() &&
+      (V + 31) / 32 <= (int64_t)cus * dspark::chain_waves_per_group()) {
+    dspark::ChainParams c{};
+    c.base = (const uint16_t*)base_logits;
+    c.out = (uint16_t*)corrected_logits;
+    c.first_prev = first_prev_token_ids;
+    c.tokens = sampled_tokens;
+    c.w1 = (const uint16_t*)w1;
+    c.w2 = (const uint16_t*)w2;
+    c.sync = (uint32_t*)((char*)workspace + kControlBytes + partials_bytes(B, V));
+    c.keys = (uint64_t*)((char*)c.sync + dspark::kChainSyncBytes);
+    c.bad_rows = &ctl->bad_rows;
+    c.sync_failures = &ctl->sync_failures;
+    c.B = B;
+    c.M = M;
+    c.V = V;
+    c.r = r;
+    c.S = (V + 31) / 32;
+    const hipError_t e = dspark::launch_chain_greedy(c, cus, s);
+    if (e == hipSuccess) return DSPARK_OK;
+    (void)hipGetLastError();  // not launchable here: take the step-by-step path
+  }
   for (int64_t k = 0; k < M; ++k) {
     p.k = k;
     p.k_abs = (uint32_t)(position_offset + k);
@@ -216,6 +277,11 @@ dspark_status_t dspark_markov_read_device_error(void* workspace, void* stream, i
   e = dspark::launch_fill_zero(workspace, sizeof(Control), s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return device_failure(e, "clear device error");
+  if (c.sync_failures != 0) {
+    g_last_error = "the persistent chain timed out waiting for its workgroups; "
+                   "zero-fill the workspace before reusing it";
+    return DSPARK_ERR_DEVICE;
+  }
   return DSPARK_OK;
 }
 

@@ -44,10 +44,18 @@ def test_status_strings(L):
     assert L.dspark_markov_last_error() == b""
 
 
+def _align256(x):
+    return (x + 255) // 256 * 256
+
+
 def test_workspace_bytes(L):
+    """Control block, then step partials (B * ceil(V/128) keys), then the
+    chain's 2 KB synchronisation area and its keys (M steps * 8 groups *
+    64 rows, 64 bytes apart)."""
     assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 0) == 256
-    assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 1) == 256 + 64 * 1010 * 8
-    assert L.dspark_markov_workspace_bytes(256, 8, 151936, 256, 1) == 256 + 256 * 1187 * 8
+    chain = lambda M: 2048 + M * 8 * 64 * 64
+    assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 1) == 256 + _align256(64 * 1010 * 8) + chain(5)
+    assert L.dspark_markov_workspace_bytes(256, 8, 151936, 256, 1) == 256 + _align256(256 * 1187 * 8) + chain(8)
 
 
 FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: every call below fails validation

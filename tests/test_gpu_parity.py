@@ -50,10 +50,12 @@ def run_apply(inp):
 
 def run_sample(inp, T, seed=0, return_logits=True, position_offset=0, batch_offset=0):
     d = device_inputs({k: inp[k] for k in ("base", "first_prev", "w1", "w2")})
+    B, M, V = inp["base"].shape
+    ws = rmd.Workspace(B, M, V, inp["w1"].shape[1], sample=True)
     tok, corr = rmd.sample_block_tokens(d["base"], d["first_prev"], d["w1"], d["w2"], T, seed=seed,
                                         return_logits=return_logits, position_offset=position_offset,
-                                        batch_offset=batch_offset)
-    torch.cuda.synchronize()
+                                        batch_offset=batch_offset, workspace=ws)
+    assert rmd.read_device_error(ws) == 0      # synchronises; raises on a chain timeout
     return from_dev(tok), (from_dev(corr) if corr is not None else None)
 
 
