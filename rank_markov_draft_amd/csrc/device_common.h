@@ -90,6 +90,119 @@ __device__ __forceinline__ uint32_t wave_max_u32_to_lane63(uint32_t v) {
   return v;
 }
 
+// Float max over the 64 lanes of a wave with DPP moves; valid in lane 63.
+// Lanes without a source take -inf.  NaN operands are ignored (v_max_f32).
+__device__ __forceinline__ float wave_max_f32_to_lane63(float v) {
+  const int ninf = (int)0xFF800000u;
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x111, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x112, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x114, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x118, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x142, 0xA, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x143, 0xC, 0xF, false)));
+  return v;
+}
+
+// Unsigned min over the 64 lanes of a wave with DPP moves; valid in lane 63.
+__device__ __forceinline__ uint32_t wave_min_u32_to_lane63(uint32_t v) {
+  const int big = -1;
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(big, (int)v, 0x111, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(big, (int)v, 0x112, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(big, (int)v, 0x114, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(big, (int)v, 0x118, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(big, (int)v, 0x142, 0xA, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(big, (int)v, 0x143, 0xC, 0xF, false));
+  return v;
+}
+
+// Order codes of the two bf16 values of a word, one per half: sign set ->
+// all bits flipped, else the sign bit set (packed 16-bit shift, then one
+// and-or and one xor for both halves).  -0 sorts just below +0 and NaNs sit
+// at the ends; callers treat both cases separately.
+__device__ __forceinline__ uint32_t pair_order_codes(uint32_t w) {
+  typedef short s16x2_t __attribute__((ext_vector_type(2)));
+  const s16x2_t sh = __builtin_bit_cast(s16x2_t, w) >> (short)15;
+  const uint32_t t = __builtin_bit_cast(uint32_t, sh);
+  return w ^ ((t & 0x7FFF7FFFu) | 0x80008000u);
+}
+
+// Max over the 64 lanes of a wave with DPP (v_max_u32_dpp); valid in lane 63.
+__device__ __forceinline__ uint32_t wave_max_u32_lane63(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+  return v;
+}
+
+// Min over the 64 lanes of a wave with DPP (v_min_u32_dpp); valid in lane 63.
+__device__ __forceinline__ uint32_t wave_min_u32_lane63(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x111, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x112, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x114, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x118, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x142, 0xA, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x143, 0xC, 0xF, false));
+  return v;
+}
+
+// First argmax of a row of bf16 values spread over a wave: lane l holds the
+// 8 columns 8l .. 8l+7 as the 4 words o (column 2q in the low half of word
+// q), valid when ok; maybe_nan is the lane's hint that one of its values
+// may be NaN (from its fp32 sums).  Returns the winning column (< 512, or
+// 0xFFFF if no lane is valid) and the 16-bit order code of its value.  NaN
+// ranks above everything (torch.argmax returns a NaN's index); -0 and +0 tie
+// (the first of them wins).
+//
+// Fast path: per value a 32-bit key (order code << 16 | 0xFFFF - column),
+// the lane's max of 8 keys, one DPP max over the wave.  A row holding a NaN,
+// or whose maximum is a zero, takes an exact second pass.
+__device__ __forceinline__ void wave_row_argmax_bf16(const u32x4_t o, bool ok, bool maybe_nan,
+                                                     uint32_t lane, uint32_t* col, uint32_t* code) {
+  const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+  const uint32_t c0 = 8u * lane;
+  const bool nan_hint = __ballot(ok && maybe_nan) != 0;
+  uint32_t kmax = 0;
+  if (ok) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t c2 = pair_order_codes(w[q]);
+      const uint32_t klo = (c2 << 16) | (0xFFFFu - (c0 + 2u * q));
+      const uint32_t khi = (c2 & 0xFFFF0000u) | (0xFFFFu - (c0 + 2u * q + 1u));
+      kmax = max(kmax, max(klo, khi));
+    }
+  }
+  const uint32_t K = (uint32_t)__builtin_amdgcn_readlane((int)wave_max_u32_lane63(kmax), 63);
+  uint32_t best_code = K >> 16;
+  uint32_t best_col = 0xFFFFu - (K & 0xFFFFu);
+  const bool zero_max = (best_code == 0x8000u || best_code == 0x7FFFu);
+  if (nan_hint || zero_max) {
+    // exact pass: first NaN column if any, else first column equal to +-0
+    uint32_t nan_idx = 0xFFFFFFFFu, zero_idx = 0xFFFFFFFFu;
+    if (ok) {
+#pragma unroll
+      for (int i = 7; i >= 0; --i) {
+        const uint32_t hb = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+        const uint32_t mag = hb & 0x7FFFu;
+        if (mag > 0x7F80u) nan_idx = c0 + (uint32_t)i;
+        if (mag == 0u) zero_idx = c0 + (uint32_t)i;
+      }
+    }
+    const uint32_t first_nan = (uint32_t)__builtin_amdgcn_readlane((int)wave_min_u32_lane63(nan_idx), 63);
+    if (first_nan != 0xFFFFFFFFu) {
+      best_col = first_nan;
+      best_code = 0xFFFFu;
+    } else if (zero_max) {
+      best_col = (uint32_t)__builtin_amdgcn_readlane((int)wave_min_u32_lane63(zero_idx), 63);
+      best_code = 0x8000u;  // the code of +0
+    }
+  }
+  *col = best_col;
+  *code = best_code;
+}
+
 // ---------------------------------------------------------------- noise
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
 // Easy as 1, 2, 3", SC'11): ten rounds of two 32x32->64 multiplies by the

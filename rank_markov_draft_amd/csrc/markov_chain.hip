@@ -151,6 +151,22 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
                  : u32x4_t{0u, 0u, 0u, 0u};
   }
 
+  // Stores the wave's corrected rows of step kd (held in pre[]) and requests
+  // its base logits of step kd + 1.
+  auto drain = [&](int64_t kd) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const uint32_t b = RPW * wave + i;
+      if (b >= B) break;
+      if (out != nullptr && col_ok)
+        __builtin_nontemporal_store(pre[i], (u32x4_t*)(out + (b * (uint32_t)M + (uint32_t)kd) * (uint32_t)V + vl));
+      if (kd + 1 < M)
+        pre[i] = col_ok ? __builtin_nontemporal_load(
+                              (const u32x4_t*)(base + (b * (uint32_t)M + (uint32_t)kd + 1u) * (uint32_t)V + vl))
+                        : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+
   for (int64_t k = 0; k < M; ++k) {
     // A1: predecessors of step k: first_prev, or the merge of the eight
     // group slots of step k-1.
@@ -178,8 +194,13 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     }
     __syncthreads();
 
-    // A2: gather the W1 rows (zero rows for padding and invalid ids).
-    for (int c = tid; c < nchunks * 32 * CPR; c += kThreads) {
+    // Wave 0 drains the previous step now, after its low-latency loads.
+    if (wave == 0 && k > 0) drain(k - 1);
+
+    // A2: gather the W1 rows (zero rows for padding and invalid ids), by
+    // waves 1.. (wave 0's loads are queued behind its drain).
+    for (int c = tid - 64; c < nchunks * 32 * CPR; c += kThreads - 64) {
+      if (c < 0) break;
       const int row = c / CPR;
       const int part = c - row * CPR;
       const int64_t x = lds_tok[row];
@@ -232,28 +253,27 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
       if (b >= B) break;  // uniform over the wave
       const u32x4_t bb = pre[i];
       const u32x4_t bs = *(const u32x4_t*)(lds_b + b * BSTRIDE + lane * 16);
+      float c[8];
+      c[0] = bf16_lo(bb.x) + bf16_lo(bs.x);
+      c[1] = bf16_hi(bb.x) + bf16_hi(bs.x);
+      c[2] = bf16_lo(bb.y) + bf16_lo(bs.y);
+      c[3] = bf16_hi(bb.y) + bf16_hi(bs.y);
+      c[4] = bf16_lo(bb.z) + bf16_lo(bs.z);
+      c[5] = bf16_hi(bb.z) + bf16_hi(bs.z);
+      c[6] = bf16_lo(bb.w) + bf16_lo(bs.w);
+      c[7] = bf16_hi(bb.w) + bf16_hi(bs.w);
       u32x4_t o;
-      o.x = pack_bf16x2(bf16_lo(bb.x) + bf16_lo(bs.x), bf16_hi(bb.x) + bf16_hi(bs.x));
-      o.y = pack_bf16x2(bf16_lo(bb.y) + bf16_lo(bs.y), bf16_hi(bb.y) + bf16_hi(bs.y));
-      o.z = pack_bf16x2(bf16_lo(bb.z) + bf16_lo(bs.z), bf16_hi(bb.z) + bf16_hi(bs.z));
-      o.w = pack_bf16x2(bf16_lo(bb.w) + bf16_lo(bs.w), bf16_hi(bb.w) + bf16_hi(bs.w));
+      o.x = pack_bf16x2(c[0], c[1]);
+      o.y = pack_bf16x2(c[2], c[3]);
+      o.z = pack_bf16x2(c[4], c[5]);
+      o.w = pack_bf16x2(c[6], c[7]);
       pre[i] = o;
-      // 32-bit key: 16-bit value code, then the complement of the column
-      // within the workgroup (first index wins ties).
-      uint32_t key = 0;
-      if (col_ok) {
-        const uint32_t w4[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t c0 = (ordered_code_bf16(w4[q] & 0xFFFFu) << 16) | (0xFFFFu - (8u * lane + 2u * q));
-          const uint32_t c1 = (ordered_code_bf16(w4[q] >> 16) << 16) | (0xFFFFu - (8u * lane + 2u * q + 1u));
-          key = max(key, max(c0, c1));
-        }
-      }
-      key = wave_max_u32_to_lane63(key);
-      if (lane == 63)
-        lds_key[b] = key ? (((uint64_t)(key >> 16) << 32) | (uint64_t)(0xFFFFFFFFu - (vbeg + (0xFFFFu - (key & 0xFFFFu)))))
-                         : 0;
+      // a NaN among the fp32 sums makes this NaN (+inf + -inf too: rechecked)
+      const float s8 = ((c[0] + c[1]) + (c[2] + c[3])) + ((c[4] + c[5]) + (c[6] + c[7]));
+      uint32_t col, code;
+      wave_row_argmax_bf16(o, col_ok, s8 != s8, (uint32_t)lane, &col, &code);
+      if (lane == 0)
+        lds_key[b] = (col < 0xFFFFu) ? (((uint64_t)code << 32) | (uint64_t)(0xFFFFFFFFu - (vbeg + col))) : 0;
     }
     __syncthreads();
 
@@ -268,19 +288,11 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
       __builtin_amdgcn_s_waitcnt(0);
     }
     if (tid == 0) arrive(p.sync, g, G, k);
-    // Corrected logits out and the next step's base logits in, while the
-    // exchange completes.
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const uint32_t b = RPW * wave + i;
-      if (b >= B) break;
-      if (out != nullptr && col_ok)
-        __builtin_nontemporal_store(pre[i], (u32x4_t*)(out + (b * (uint32_t)M + (uint32_t)k) * (uint32_t)V + vl));
-      if (k + 1 < M)
-        pre[i] = col_ok ? __builtin_nontemporal_load(
-                              (const u32x4_t*)(base + (b * (uint32_t)M + (uint32_t)k + 1u) * (uint32_t)V + vl))
-                        : u32x4_t{0u, 0u, 0u, 0u};
-    }
+    // Waves 1.. write their corrected rows and request the next step's base
+    // logits while the exchange completes.  Wave 0 keeps its memory queue
+    // empty until it has read the next tokens: its polls and key loads would
+    // otherwise wait behind these (the vector memory counter is in order).
+    if (wave != 0) drain(k);
     if (tid == 0) {
       const bool ok = wait_word(release_word(p.sync, xg), (uint32_t)(k + 1));
       if (!ok) atomicAdd(p.sync_failures, 1u);
@@ -289,6 +301,8 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     __syncthreads();
     if (!lds_flag) return;
   }
+
+  if (wave == 0) drain(M - 1);
 
   // Tokens of the last step.
   if (tid < B && g == 0) {

@@ -319,3 +319,45 @@ def test_deterministic_and_workspace_reuse(native):
     assert np.array_equal(outs[0][0], outs[2][0]) and np.array_equal(outs[0][1], outs[2][1])
     assert np.array_equal(outs[1][0], outs[3][0]) and np.array_equal(outs[1][1], outs[3][1])
     assert rmd.read_device_error(ws) == 0
+
+
+@pytest.mark.parametrize("B", [8, 70])   # 8: persistent chain; 70: step-by-step kernels
+def test_greedy_special_values(native, B):
+    """Argmax semantics on planted values (W2 = 0, so corrected = base):
+    NaN ranks first (first NaN wins), exact ties go to the first column --
+    within a lane, across lanes and across workgroups -- and +-inf order."""
+    V, M, r = 8192, 2, 32
+    w = wl.WORKLOADS["greedy_draft_64x5"]
+    inp = wl.make_inputs(w, B=B, M=M, V=V, r=r, seed=21)
+    base = wl.bf16_bits_to_f32(inp["base"]).copy()
+    nan, inf = np.float32(np.nan), np.float32(np.inf)
+    for b in range(B):
+        kind = b % 8
+        row = base[b]                       # [M, V] view
+        if kind == 0:
+            row[:, 3] = 100.0
+            row[:, 777] = nan
+            row[:, 5000] = nan
+        elif kind == 1:
+            row[:, [9, 4000, 4001]] = 50.0   # first of equal maxima
+            row[:, 10] = 50.0                # same lane as column 9
+        elif kind == 2:
+            row[:, [7000, 6000]] = inf
+        elif kind == 3:
+            row[:] = -inf
+            row[:, 8191] = -1e30
+        elif kind == 4:
+            row[:] = -inf                    # all equal: column 0
+        elif kind == 5:
+            row[:] = -np.abs(row) - 1.0
+            row[:, [300, 299]] = 0.0
+        elif kind == 6:
+            row[:, 8191] = nan
+    inp["base"] = wl.to_bf16_bits(base)
+    inp["w2"] = np.zeros_like(inp["w2"])
+    tok, corr = run_sample(inp, 0.0)
+    expect = {0: 777, 1: 9, 2: 6000, 3: 8191, 4: 0, 5: 299, 6: 8191}
+    for b in range(B):
+        if b % 8 in expect:
+            assert (tok[b] == expect[b % 8]).all(), (b, tok[b])
+    check_chain(inp, 0.0, 0, tok, corr, name=f"greedy special values B{B}")
