@@ -116,7 +116,10 @@ size_t dspark_markov_workspace_bytes(int64_t B, int64_t M, int64_t V, int64_t r,
   (void)r;
   if (B < 0 || V < 0 || M < 0) return kControlBytes;
   size_t bytes = kControlBytes;
-  if (sample_mode) bytes += partials_bytes(B, V) + chain_keys_bytes(M);
+  if (sample_mode)
+    bytes += partials_bytes(B, V) + chain_keys_bytes(M);
+  else
+    bytes += dspark::apply_sink_bytes();
   return bytes;
 }
 
@@ -164,9 +167,14 @@ dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_
   hipError_t e;
   const bool tile = tile_path(logits_dtype, weight_dtype, V, r, base_logits, corrected_logits, w1, w2);
   if (!tile && r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
-  if (tile)
-    e = dspark::launch_tile(p, (hipStream_t)stream);
-  else
+  p.sink = (char*)workspace + kControlBytes;
+  if (tile) {
+    e = dspark::launch_apply_wide(p, (hipStream_t)stream);
+    if (e == hipErrorNotSupported) {  // element offsets beyond 31 bits
+      (void)hipGetLastError();
+      e = dspark::launch_tile(p, (hipStream_t)stream);
+    }
+  } else
     e = dspark::launch_generic(p, logits_dtype == DSPARK_BF16, weight_dtype == DSPARK_BF16,
                                (hipStream_t)stream);
   if (e != hipSuccess) return device_failure(e, "apply launch");

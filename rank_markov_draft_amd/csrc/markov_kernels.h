@@ -22,6 +22,7 @@ struct KernelParams {
   const void* w2;        // [V, r]
   uint64_t* partials;    // sampling: [rows, nparts] argmax keys
   uint32_t* bad_rows;    // device error word
+  void* sink;            // apply: 16 bytes per thread of scratch for stores past the edges
   int64_t rows;
   int64_t V;
   int64_t r;
@@ -70,6 +71,10 @@ hipError_t launch_chain_greedy(const ChainParams& p, int num_cus, hipStream_t s)
 int tile_ks_for_rank(int64_t r);
 
 hipError_t launch_tile(const KernelParams& p, hipStream_t s);
+// Streaming teacher-forced apply (bf16); needs rows * V < 2^31 and a sink of
+// apply_sink_bytes() bytes.
+hipError_t launch_apply_wide(const KernelParams& p, hipStream_t s);
+size_t apply_sink_bytes();
 hipError_t launch_generic(const KernelParams& p, bool logits_bf16, bool weights_bf16, hipStream_t s);
 hipError_t launch_reduce(const uint64_t* partials, int64_t nparts, int64_t B, int64_t M, int64_t k,
                          int64_t* tokens, hipStream_t s);

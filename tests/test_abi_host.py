@@ -49,10 +49,11 @@ def _align256(x):
 
 
 def test_workspace_bytes(L):
-    """Control block, then step partials (B * ceil(V/128) keys), then the
-    chain's 2 KB synchronisation area and its keys (M steps * 8 groups *
+    """Apply: control block, then a 16 KB store sink for lanes past the edges.
+    Sample: control block, then step partials (B * ceil(V/128) keys), then
+    the chain's 2 KB synchronisation area and its keys (M steps * 8 groups *
     64 rows, 64 bytes apart)."""
-    assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 0) == 256
+    assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 0) == 256 + 16384
     chain = lambda M: 2048 + M * 8 * 64 * 64
     assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 1) == 256 + _align256(64 * 1010 * 8) + chain(5)
     assert L.dspark_markov_workspace_bytes(256, 8, 151936, 256, 1) == 256 + _align256(256 * 1187 * 8) + chain(8)
@@ -85,18 +86,18 @@ def test_apply_empty_is_ok_and_touches_nothing(L):
 
 
 def test_apply_null_pointers_and_workspace(L):
-    assert L.dspark_markov_apply_block(None, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, FAKE, 256, None) == 1
-    assert L.dspark_markov_apply_block(FAKE, 1, None, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, FAKE, 256, None) == 1
-    assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, None, FAKE, 256, None) == 1
-    assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, None, 256, None) == 3
-    assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, FAKE, 255, None) == 3
+    assert L.dspark_markov_apply_block(None, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, FAKE, 1 << 20, None) == 1
+    assert L.dspark_markov_apply_block(FAKE, 1, None, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, FAKE, 1 << 20, None) == 1
+    assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, None, FAKE, 1 << 20, None) == 1
+    assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, None, 1 << 20, None) == 3
+    assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, FAKE, 16639, None) == 3
 
 
 def test_apply_overlap_rejected(L):
     base = 0x200000
     out = ctypes.c_void_p(base + 64)          # partial overlap with base
     st = L.dspark_markov_apply_block(ctypes.c_void_p(base), 1, FAKE, ctypes.c_void_p(0x900000),
-                                     ctypes.c_void_p(0xA00000), 1, 2, 3, 64, 16, out, FAKE, 256, None)
+                                     ctypes.c_void_p(0xA00000), 1, 2, 3, 64, 16, out, FAKE, 1 << 20, None)
     assert st == 1
 
 
