@@ -25,6 +25,73 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 WORKLOAD = "greedy_draft_64x5"
+DOMINANT_KERNEL = "markov_chain_greedy_bf16"   # the whole sample call is this one launch
+KERNEL_SOURCE = os.path.join(ROOT, "rank_markov_draft_amd", "csrc", "markov_chain.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_hash(path: str) -> str:
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    runs (profiles/traffic.json), or None once the kernel source changed."""
+    import json as _json
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = _json.load(f)
+    if t.get("kernel_source_sha256_16") != source_hash(KERNEL_SOURCE):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy(torch):
+    """A plain device copy of known size for scaling the byte counters:
+    256 MiB read + 256 MiB written per launch, 3 launches."""
+    src = torch.empty(128 * 1024 * 1024, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"calibration copy: {src.numel() * 2} bytes read and written per launch, 3 launches",
+          file=sys.stderr)
+
+
+def write_traffic(fetch_csv: str, write_csv: str) -> dict:
+    """Turn two rocprofv3 counter runs of `bench.py --calibrate-copy` (one with
+    FETCH_SIZE, one with WRITE_SIZE, KiB per dispatch) into HBM bytes per
+    launch of the dominant kernel.  Each counter is scaled by what it reads
+    for the calibration copy (the first three copy dispatches of the run, of
+    known size) and the result goes to profiles/traffic.json, tagged with a
+    hash of the kernel source so a later kernel change voids it."""
+    import csv
+    known_kib = 128 * 1024 * 1024 * 2 / 1024.0
+    out = {}
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][:3]
+        kern = [float(r["Counter_Value"]) for r in rows if DOMINANT_KERNEL in r["Kernel_Name"]]
+        if len(copies) < 3 or not kern:
+            raise SystemExit(f"{path}: calibration copies or {DOMINANT_KERNEL} dispatches missing")
+        scale = known_kib / (sum(copies) / len(copies))
+        out[counter] = {"kib_per_dispatch": sum(kern) / len(kern), "dispatches": len(kern),
+                        "copy_kib_per_dispatch": sum(copies) / len(copies), "scale": scale,
+                        "bytes_per_launch": sum(kern) / len(kern) * 1024.0 * scale}
+    t = {"kernel": DOMINANT_KERNEL, "workload": WORKLOAD,
+         "kernel_source_sha256_16": source_hash(KERNEL_SOURCE),
+         "hbm_read_bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"],
+         "hbm_write_bytes_per_launch": out["WRITE_SIZE"]["bytes_per_launch"],
+         "hbm_bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"],
+         "counters": out}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1)
+        f.write("\n")
+    return t
 
 
 def algorithmic_bytes_sample(w, return_logits=True) -> int:
@@ -131,7 +198,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' timings")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain copy of known size (for scaling byte counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two counter runs and exit (no GPU)")
     args = ap.parse_args()
+    if args.write_traffic:
+        print(json.dumps(write_traffic(*args.write_traffic)))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the head's sharding is described in DESIGN.md)", file=sys.stderr)
@@ -148,6 +222,9 @@ def main():
         _lib.build()
     _lib.load()
     torch.cuda.set_device(0)
+
+    if args.calibrate_copy:
+        calibrate_copy(torch)
 
     w = wl.WORKLOADS[WORKLOAD]
     inp = wl.make_inputs(w)
@@ -191,9 +268,9 @@ def main():
         "config": {"workload": f"{WORKLOAD}: greedy left-to-right draft, batch {w.B}, block {w.M}, "
                                f"V={w.V}, r={w.r}, bf16 logits and weights, corrected logits returned",
                    "global_batch": w.B, "block": w.M, "vocab": w.V, "rank": w.r},
-        "roofline": {"bound": "hbm", "kernel": "sample_block call (all kernels of one step)",
+        "roofline": {"bound": "hbm", "kernel": DOMINANT_KERNEL,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": alg, "launch_ms": call_ms},
     }
     del sets
