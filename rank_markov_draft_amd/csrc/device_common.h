@@ -14,6 +14,37 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+// ---------------------------------------------------------------- buffers
+// Raw buffer loads and stores: a 128-bit resource in scalar registers plus a
+// 32-bit byte offset per lane.  The hardware drops a store and returns zeros
+// for a load whose offset lies beyond the resource's size, and an offset of
+// kBufferOob always does when the size is at most 2^31 bytes.  Kernels use
+// that for masked-off lanes instead of branches, so every memory operation
+// is unconditional and the compiler keeps exact counts of the ones in
+// flight.  kNonTemporal is the streaming cache policy.
+constexpr uint32_t kBufferOob = 0x80000000u;
+constexpr int kNonTemporal = 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  // word 3: 32-bit data format, as the gfx9 family expects for raw access
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
+}
+__device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kNonTemporal);
+}
+// A device-coherent 8-byte load (the sc1 policy, as a relaxed device-scope
+// atomic load uses).  Unlike atomic loads, several of these are issued
+// back to back before the first is waited for.
+constexpr int kDeviceCoherent = 16;
+__device__ __forceinline__ uint64_t buffer_load8_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kDeviceCoherent);
+  return ((uint64_t)v.y << 32) | v.x;
+}
+
 // ---------------------------------------------------------------- bf16
 // A bf16 value is the upper half of a binary32 value.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -4,27 +4,36 @@
 // sequential loop over the M block positions: position k is biased by the
 // token drawn at k-1.  Launching a kernel per position re-reads W2 (66 MB at
 // V=129280, r=256) every step and pays a launch plus a separate reduction per
-// step.  This kernel runs the whole chain in one cooperative launch:
+// step.  This kernel runs the whole chain in one launch, one workgroup of 16
+// waves per CU:
 //
-//   * one workgroup of 16 waves per CU; the vocabulary is cut into 32-column
-//     slices and each wave owns at most one slice, whose W2w rows it keeps in
-//     VGPRs for all M steps (W2 is read from HBM once per call);
-//   * per step every workgroup gathers the W1 rows of the B current
-//     predecessors into LDS and multiplies them on the matrix cores
-//     (v_mfma_f32_32x32x16_bf16, vocabulary on M, batch rows on N); the
-//     rounded bias goes to LDS row-major, and each wave then streams whole
-//     rows of the workgroup's columns (one 1 KB row segment per wave
-//     instruction): base logits in, corrected logits out, and the row's
-//     argmax key folded across the wave;
-//   * the base logits of step k+1 are requested right after step k's are
-//     consumed, so they arrive while the device-wide token exchange runs;
-//   * the exchange: each workgroup merges its per-row keys into a device-wide
-//     key per (step, row) with a 64-bit atomic max, then arrives on a counter;
-//     the next step starts when all workgroups have arrived.  Every wait is
-//     bounded: a workgroup that waits too long records a failure in the
-//     workspace and leaves, so no launch can hang.
-// The last workgroup to leave clears the keys and the counter, so the
-// workspace is ready for the next call.
+//   * the vocabulary is cut into 32-column slices; each wave owns at most one
+//     slice and keeps its W2w rows in VGPRs for all M steps, so W2 is read
+//     from HBM once per call;
+//   * the batch rows are independent chains.  They are dealt into four row
+//     groups of up to 16, and the workgroup works through units (step k,
+//     group g) in the order (0,0) (0,1) (0,2) (0,3) (1,0) ...  A group's
+//     next step needs the tokens of its current one from every workgroup,
+//     so each device-wide exchange has three other units' work to hide in;
+//   * a unit: every wave multiplies the group's gathered W1 rows by its
+//     slice on the matrix cores (v_mfma_f32_16x16x32_bf16), rounds the bias
+//     to bf16, adds it to the group's base logits staged in LDS, writes the
+//     corrected values back in place and folds each row's best column into
+//     a per-row LDS key; then the corrected rows go to HBM and the group's
+//     base logits of its next step are loaded straight into the same LDS
+//     rows (buffer loads to LDS, three units ahead of use);
+//   * waves 0 and 1 carry the exchange, staged across units so that no wave
+//     waits on a round trip it could have started earlier: wave 0 publishes
+//     a unit's row keys (a 64-bit atomic max per row into one of eight key
+//     slots) and, a unit later, counts the workgroup in; wave 1 polls a
+//     group's arrival counts, reads the merged keys a unit later and, a unit
+//     after that, gathers the W1 rows of the new tokens into LDS.
+// Every wait on other workgroups is bounded: a workgroup that waits too long
+// records a failure in the workspace and leaves, so no launch can hang.  The
+// last workgroup to leave clears the keys and counters, so the workspace is
+// ready for the next call.
+#include <type_traits>
+
 #include "device_common.h"
 #include "markov_kernels.h"
 
@@ -34,296 +43,441 @@ namespace {
 
 constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
-constexpr int kMaxRows = 64;                 // batch rows per call of this kernel
-constexpr int kGroups = 8;                   // key slots / arrival groups (one per XCD)
-constexpr uint64_t kSpinTicks = 100000000;   // 1 s of the 100 MHz realtime clock
+constexpr int kRowGroups = 4;                 // pipelined row groups
+constexpr int kGroupRows = 16;                // rows of a group at most (the MFMA N tile)
+constexpr int kMaxRows = kRowGroups * kGroupRows;
+constexpr int kGroups = 8;                    // key slots / arrival counters per row group
+constexpr int kPitch = 2 * 32 * kWaves + 16;  // LDS bytes of a staged row (512 columns + pad)
+constexpr uint64_t kSpinTicks = 100000000;    // 1 s of the 100 MHz realtime clock
 
-// Words of the synchronisation area (one 64-byte line each).
-__device__ __forceinline__ uint32_t* group_counter(uint32_t* sync, int x) { return sync + 16 * x; }
-__device__ __forceinline__ uint32_t* global_counter(uint32_t* sync) { return sync + 16 * kGroups; }
-__device__ __forceinline__ uint32_t* release_word(uint32_t* sync, int x) { return sync + 16 * (kGroups + 1 + x); }
-__device__ __forceinline__ uint32_t* exit_counter(uint32_t* sync) { return sync + 16 * (2 * kGroups + 1); }
+// Synchronisation area, one 64-byte line per word: the arrival counters
+// [kRowGroups][kGroups] (cumulative over steps), then the exit counter.
+static_assert((kRowGroups * kGroups + 1) * 64 <= (int)kChainSyncBytes, "sync area");
+__device__ __forceinline__ uint32_t* arrival_counter(uint32_t* sync, int rg, int x) {
+  return sync + 16 * (rg * kGroups + x);
+}
+__device__ __forceinline__ uint32_t* exit_counter(uint32_t* sync) { return sync + 16 * (kRowGroups * kGroups); }
 
-__device__ __forceinline__ uint64_t* key_slot(uint64_t* keys, int64_t k, int x, int b) {
-  return keys + ((k * kGroups + x) * kMaxRows + b) * kKeyPad;
+// Byte offset of the key slot of (step k, key group x, row b).
+__device__ __forceinline__ uint32_t key_offset(int k, int x, int b) {
+  return (uint32_t)(((k * kGroups + x) * kMaxRows + b) * kKeyPad * 8);
 }
 
-__device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// s_waitcnt on the vector memory counter only (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Waits until *w >= target.  Returns false after kSpinTicks.  The polls are
-// relaxed device-scope loads: everything exchanged between workgroups (keys,
-// counters, release words) goes through device-scope atomics, so no acquire
-// (which would invalidate this XCD's L2 on every poll) is needed.
-__device__ bool wait_word(const uint32_t* w, uint32_t target) {
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  while (__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-    __builtin_amdgcn_s_sleep(1);
-    if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) return false;
-  }
-  return true;
+// Order code of a bf16 value for argmax (16 bits, larger = later in the
+// order): every NaN ranks highest (torch.argmax reports a NaN), -0 and +0
+// share one code, otherwise the IEEE order.
+__device__ __forceinline__ uint32_t argmax_code_bf16(uint32_t h) {
+  const uint32_t mag = h & 0x7FFFu;
+  uint32_t c = (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+  c = (mag == 0u) ? 0x8000u : c;
+  c = (mag > 0x7F80u) ? 0xFFFFu : c;
+  return c;
 }
 
-// Two-level arrival of workgroup g for step k (one thread): the last
-// arrival of g's group bumps the global counter, and the last group to arrive
-// publishes k+1 in every group's release word; the workgroup then waits on
-// its own group's word (wait_word(release_word(sync, g % kGroups), k + 1)).
-// With a single counter and a single word, 256 workgroups contend on one
-// address; this halves the cost of a round on MI355X (measured).
-__device__ void arrive(uint32_t* sync, int g, int G, int64_t k) {
-  const int ngroups = G < kGroups ? G : kGroups;
-  const int x = g % kGroups;
-  const uint32_t in_group = (uint32_t)((G - x + kGroups - 1) / kGroups);
-  const uint32_t step = (uint32_t)(k + 1);
-  if (atomic_add_agent(group_counter(sync, x), 1u) == in_group * step - 1u) {
-    if (atomic_add_agent(global_counter(sync), 1u) == (uint32_t)ngroups * step - 1u)
-      for (int y = 0; y < ngroups; ++y)
-        __hip_atomic_store(release_word(sync, y), step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+// Workgroup barrier for LDS data only.  __syncthreads() also orders global
+// memory at workgroup scope, which makes the compiler wait for every buffer
+// load to LDS in flight: the staging loads of later units would then be
+// waited for at every barrier.  Here each wave finishes its own LDS
+// accesses (lgkmcnt) and the staging loads are waited for explicitly, by
+// count, where their data is needed.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+
+// Buffer load of 16 bytes per lane straight into LDS: lane l's bytes land at
+// LDS address lds + 16 l (lds must be uniform over the wave).  Written as
+// inline assembly so that the compiler does not track these loads: it would
+// otherwise make every later LDS read of a wave that took any path through
+// such a load wait for all of them.  Their completion is waited for
+// explicitly, by count (wait_vmcnt), before the LDS data is used.  POLICY is
+// the cache policy: 0, "nt" (streaming) or "sc1" (device-coherent).  M0 is
+// saved and restored around the load.
+struct BufferWords {
+  u32x4_t w;  // V# of a raw buffer: base, stride 0, size in bytes, 32-bit data format
+};
+__device__ __forceinline__ BufferWords buffer_words(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  return BufferWords{u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u}};
+}
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+__device__ __forceinline__ void load_lds16(const BufferWords& r, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  __asm__ volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0"
+                   : "=&s"(saved) : "v"(off), "s"(r.w), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void load_lds16_nt(const BufferWords& r, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  __asm__ volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds\n\ts_mov_b32 m0, %0"
+                   : "=&s"(saved) : "v"(off), "s"(r.w), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void load_lds16_coherent(const BufferWords& r, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  __asm__ volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %1, %2, 0 offen sc1 lds\n\ts_mov_b32 m0, %0"
+                   : "=&s"(saved) : "v"(off), "s"(r.w), "s"(lds) : "memory");
+}
+
+template <int N>
+using IC = std::integral_constant<int, N>;
 
 }  // namespace
 
-template <int KS>
+template <int K32>
 __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams p) {
-  constexpr int CPR = 2 * KS;               // 16-byte chunks per gathered W1 row
-  constexpr int ESTRIDE = 32 * KS + 16;     // LDS bytes per gathered row
-  constexpr int COLS = 32 * kWaves;         // columns of a workgroup (at most)
-  constexpr int BSTRIDE = 2 * COLS + 16;    // LDS bytes per bias row
-  constexpr int RPW = kMaxRows / kWaves;    // rows streamed per wave
-  __shared__ __attribute__((aligned(16))) unsigned char lds_e[kMaxRows * ESTRIDE];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_b[kMaxRows * BSTRIDE];
-  __shared__ uint64_t lds_key[kMaxRows];
-  __shared__ int64_t lds_tok[kMaxRows];
+  // Gathered W1 rows of each group, in the B-operand order of the matrix
+  // instruction: block kk holds at lane l's 16 bytes row l % 16, rank
+  // elements 32 kk + 8 (l / 16) .. +7.  One array per group, so the
+  // compiler tracks the loads into each separately.
+  __shared__ __attribute__((aligned(16))) unsigned char lds_e0[K32 * 1024];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_e1[K32 * 1024];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_e2[K32 * 1024];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_e3[K32 * 1024];
+  // Staged logits of each group: base, then corrected in place.
+  __shared__ __attribute__((aligned(16))) unsigned char lds_x0[kGroupRows * kPitch];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_x1[kGroupRows * kPitch];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_x2[kGroupRows * kPitch];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_x3[kGroupRows * kPitch];
+  __shared__ uint32_t lds_key[kRowGroups][kGroupRows];
+  // Key slots read for the next token merge: [2][lane] 16 bytes each, the
+  // key in the first 8 (row l % 16, key group 2 (l / 16) + j).
+  __shared__ __attribute__((aligned(16))) unsigned char lds_kv[2 * 1024];
   __shared__ int lds_flag;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int lane = tid & 63;
-  const int m = lane & 31;
-  const int h = lane >> 5;
+  const int n16 = lane & 15;
+  const int g4 = lane >> 4;
   const int G = gridDim.x;
   const int g = blockIdx.x;
   const int xg = g % kGroups;
-  const int64_t B = p.B, M = p.M, V = p.V, r = p.r;
-  const int nchunks = (int)((B + 31) / 32);
-  const uint16_t* __restrict__ w1 = p.w1;
-  const uint16_t* __restrict__ base = p.base;
-  uint16_t* __restrict__ out = p.out;
+  // The host guarantees B <= 64, V <= 32 * 16 * CUs, B*M*V < 2^30 and
+  // M <= 4096, so every index below fits in 32 bits.
+  const int B = (int)p.B, M = (int)p.M, V = (int)p.V, r = (int)p.r;
+  const int rpg = (B + kRowGroups - 1) / kRowGroups;  // rows per group
+  uint32_t* const sync = p.sync;
+
+  auto lds_e = [&](auto gc) __attribute__((always_inline)) -> unsigned char* {
+    constexpr int GG = decltype(gc)::value;
+    return GG == 0 ? lds_e0 : GG == 1 ? lds_e1 : GG == 2 ? lds_e2 : lds_e3;
+  };
+  auto lds_x = [&](auto gc) __attribute__((always_inline)) -> unsigned char* {
+    constexpr int GG = decltype(gc)::value;
+    return GG == 0 ? lds_x0 : GG == 1 ? lds_x1 : GG == 2 ? lds_x2 : lds_x3;
+  };
 
   // The workgroup's columns [vbeg, vend): slices s_begin .. s_end-1.
-  const int64_t s_begin = ((int64_t)g * p.S) / G;
-  const int64_t s_end = ((int64_t)(g + 1) * p.S) / G;
+  const int s_begin = (int)(((int64_t)g * p.S) / G);
+  const int s_end = (int)(((int64_t)(g + 1) * p.S) / G);
   const uint32_t vbeg = (uint32_t)(s_begin * 32);
   const uint32_t vend = (uint32_t)(s_end * 32 < V ? s_end * 32 : V);
-  // This wave's slice for the matrix work.
-  const int64_t slice = s_begin + wave;
+  const int slice = s_begin + wave;
   const bool has = slice < s_end;
 
-  // A operand (W2w rows of the slice), permuted so that the lane's 16
-  // accumulators are the 16 consecutive columns slice*32 + 16h + i.
-  bf16x8_t a[KS];
-  {
-    const int perm = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
-    const int64_t vrow = slice * 32 + perm;
+  const uint32_t bytes = (uint32_t)(B * M * V * 2);
+  const BufferWords bw_base = buffer_words(p.base, bytes);
+  const __amdgpu_buffer_rsrc_t rs_out = buffer_rsrc(p.out, p.out != nullptr ? bytes : 0u);
+  const BufferWords bw_w1 = buffer_words(p.w1, (uint32_t)(V * r * 2));
+  const BufferWords bw_keys = buffer_words(p.keys, (uint32_t)(M * kGroups * kMaxRows * kKeyPad * 8));
+
+  // A operands (columns on M, rows on N, rank on K): the slice's 32 columns
+  // are two 16-column tiles t.  Lane (n16, g4) supplies W2w[col(t, n16)]
+  // [32 kk + 8 g4 .. +7]; the map col(t, m) = 8 (m / 4) + 4 t + m % 4 makes
+  // a lane's 4 + 4 accumulators the 8 consecutive columns 8 g4 .. 8 g4 + 7.
+  bf16x8_t a[2][K32];
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const int64_t kof = kk * 16 + 8 * h;
-      if (has && vrow < V && kof < r)
-        a[kk] = *(const bf16x8_t*)(p.w2 + vrow * r + kof);
-      else
-        a[kk] = bf16x8_t{};
+  for (int t = 0; t < 2; ++t) {
+    const int vrow = slice * 32 + 8 * (n16 >> 2) + 4 * t + (n16 & 3);
+#pragma unroll
+    for (int kk = 0; kk < K32; ++kk) {
+      const int kof = kk * 32 + 8 * g4;
+      a[t][kk] = (has && vrow < V && kof < r) ? *(const bf16x8_t*)(p.w2 + (uint32_t)(vrow * r + kof)) : bf16x8_t{};
     }
   }
 
-  // Streaming: wave w handles rows RPW*w + i; lane l the 8 columns
-  // vbeg + 8l .. +7 of them (whole 16-byte vectors since V % 8 == 0).
-  // Element offsets fit in 32 bits (the host requires B*M*V < 2^31).
-  const uint32_t vl = vbeg + 8u * (uint32_t)lane;
-  const bool col_ok = vl < vend;
-  u32x4_t pre[RPW];
-#pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const uint32_t b = RPW * wave + i;
-    pre[i] = (b < B && col_ok)
-                 ? __builtin_nontemporal_load((const u32x4_t*)(base + (b * (uint32_t)M) * (uint32_t)V + vl))
-                 : u32x4_t{0u, 0u, 0u, 0u};
-  }
+  // ---- row staging (waves 2..15).  Wave w moves rows w - 2 and, for w < 4,
+  // also w + 12 of a group: one 1 KB row segment per instruction, lane l the
+  // 8 columns vbeg + 8 l .. +7.  Offsets of masked-off lanes, rows or steps
+  // point past the buffer (see buffer_rsrc).
+  const bool col_ok = vbeg + 8u * (uint32_t)lane < vend;
+  const uint32_t lane_off = 2u * (vbeg + 8u * (uint32_t)lane);
+  auto row_offset = [&](int gg, int i, int kd) __attribute__((always_inline)) -> uint32_t {
+    const int b = gg * rpg + i;
+    const bool ok = i < rpg && b < B && kd < M && col_ok;
+    return ok ? (uint32_t)((b * M + kd) * V) * 2u + lane_off : kBufferOob;
+  };
+  // Base logits of (step kd, group GG) for row i into its staging row.
+  auto stage_row = [&](auto gc, int i, int kd) __attribute__((always_inline)) {
+    constexpr int GG = decltype(gc)::value;
+    load_lds16_nt(bw_base, row_offset(GG, i, kd), lds_address(lds_x(gc) + i * kPitch));
+  };
+  // Corrected row i of (step kd, group GG) to HBM, then its base logits of
+  // step kd + 1 into the same staging row (the LDS read completes before
+  // the store issues, so before the load can overwrite the row).
+  auto flush_row = [&](auto gc, int i, int kd) __attribute__((always_inline)) {
+    constexpr int GG = decltype(gc)::value;
+    const u32x4_t v = *(const u32x4_t*)(lds_x(gc) + i * kPitch + lane * 16);
+    buffer_store16(rs_out, row_offset(GG, i, kd), v);
+    stage_row(gc, i, kd + 1);
+  };
+  const int srow0 = wave - 2;       // this wave's first staging row (waves 2..15)
+  const bool two_rows = wave < 4;   // waves 2 and 3 also move rows 14 and 15 (srow0 + 14)
 
-  // Stores the wave's corrected rows of step kd (held in pre[]) and requests
-  // its base logits of step kd + 1.
-  auto drain = [&](int64_t kd) {
+  // ---- gather (wave 1): W1 rows of tokens x (lane l: the token of row
+  // l % 16 of group GG, or -1 for a zero row) into lds_e(GG).
+  auto gather = [&](auto gc, int x) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const uint32_t b = RPW * wave + i;
-      if (b >= B) break;
-      if (out != nullptr && col_ok)
-        __builtin_nontemporal_store(pre[i], (u32x4_t*)(out + (b * (uint32_t)M + (uint32_t)kd) * (uint32_t)V + vl));
-      if (kd + 1 < M)
-        pre[i] = col_ok ? __builtin_nontemporal_load(
-                              (const u32x4_t*)(base + (b * (uint32_t)M + (uint32_t)kd + 1u) * (uint32_t)V + vl))
-                        : u32x4_t{0u, 0u, 0u, 0u};
+    for (int kk = 0; kk < K32; ++kk) {
+      const int kof = 32 * kk + 8 * g4;
+      const uint32_t off = (x >= 0 && kof < r) ? 2u * (uint32_t)(x * r + kof) : kBufferOob;
+      load_lds16(bw_w1, off, lds_address(lds_e(gc) + kk * 1024));
     }
   };
 
-  for (int64_t k = 0; k < M; ++k) {
-    // A1: predecessors of step k: first_prev, or the merge of the eight
-    // group slots of step k-1.
-    if (tid < kMaxRows) {
-      int64_t x = -1;
-      if (tid < B) {
-        if (k == 0) {
-          x = p.first_prev[tid];
-          if (x < 0 || x >= V) {
-            if (g == 0) atomicAdd(p.bad_rows, 1u);
-            x = -1;
-          }
-        } else {
-          uint64_t best = 0;
-#pragma unroll
-          for (int y = 0; y < kGroups; ++y)
-            best = max_u64(best, __hip_atomic_load(key_slot(p.keys, k - 1, y, tid), __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT));
-          x = key_index(best);
-          if (g == 0) p.tokens[tid * M + k - 1] = x;
-          if (x < 0 || x >= V) x = -1;  // never after a complete exchange
-        }
+  // ---- prologue: stage step 0 of every group, gather the first tokens.
+  if (wave >= 2) {
+    stage_row(IC<0>{}, srow0, 0);
+    stage_row(IC<1>{}, srow0, 0);
+    stage_row(IC<2>{}, srow0, 0);
+    stage_row(IC<3>{}, srow0, 0);
+    if (two_rows) {
+      stage_row(IC<0>{}, srow0 + 14, 0);
+      stage_row(IC<1>{}, srow0 + 14, 0);
+      stage_row(IC<2>{}, srow0 + 14, 0);
+      stage_row(IC<3>{}, srow0 + 14, 0);
+    }
+  } else if (wave == 1) {
+    auto first = [&](auto gc) __attribute__((always_inline)) {
+      constexpr int GG = decltype(gc)::value;
+      const int b = GG * rpg + n16;
+      int x = -1;
+      if (n16 < rpg && b < B) {
+        const int64_t x0 = p.first_prev[(uint32_t)b];
+        if (x0 >= 0 && x0 < V) x = (int)x0;
+        else if (g == 0 && g4 == 0) atomicAdd(p.bad_rows, 1u);
       }
-      lds_tok[tid] = x;
-    }
-    __syncthreads();
+      gather(gc, x);
+    };
+    first(IC<0>{});
+    first(IC<1>{});
+    first(IC<2>{});
+    first(IC<3>{});
+  } else {
+    if (lane < kRowGroups * kGroupRows) lds_key[lane / kGroupRows][lane % kGroupRows] = 0u;
+    if (lane == 0) lds_flag = 1;
+  }
+  wait_vmcnt<0>();
+  lds_barrier();
 
-    // Wave 0 drains the previous step now, after its low-latency loads.
-    if (wave == 0 && k > 0) drain(k - 1);
+  // ---- exchange state carried across units (wave 1)
+  bool ok = true;  // no exchange wait of this wave (wave 1) has timed out
 
-    // A2: gather the W1 rows (zero rows for padding and invalid ids), by
-    // waves 1.. (wave 0's loads are queued behind its drain).
-    for (int c = tid - 64; c < nchunks * 32 * CPR; c += kThreads - 64) {
-      if (c < 0) break;
-      const int row = c / CPR;
-      const int part = c - row * CPR;
-      const int64_t x = lds_tok[row];
-      u32x4_t d = u32x4_t{0u, 0u, 0u, 0u};
-      if (x >= 0 && part * 8 < r) d = *(const u32x4_t*)(w1 + x * r + part * 8);
-      *(u32x4_t*)(lds_e + row * ESTRIDE + part * 16) = d;
-    }
-    __syncthreads();
-
-    // A3: the bias of the wave's slice for every row, rounded to bf16 (the
-    // Linear's output dtype), into LDS row-major.
+  // One unit: step k of group GG.
+  auto unit = [&](auto gc, int k) __attribute__((always_inline)) {
+    constexpr int GG = decltype(gc)::value;
+    // P1: bias of the wave's slice for the group's rows, added to the staged
+    // base logits in place; each row's best column into lds_key.
     if (has) {
+      f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{};
+      const unsigned char* eb = lds_e(gc) + lane * 16;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        if (c >= nchunks) break;
-        f32x16_t acc = f32x16_t{};
-        const unsigned char* eb = lds_e + (32 * c + m) * ESTRIDE + h * 16;
+      for (int kk = 0; kk < K32; ++kk) {
+        const bf16x8_t bop = *(const bf16x8_t*)(eb + kk * 1024);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0][kk], bop, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1][kk], bop, acc1, 0, 0, 0);
+      }
+      // bias rounded to bf16 (the Linear's output dtype)
+      const uint32_t bw[4] = {pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
+                              pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
+      const int colw = wave * 32 + 8 * g4;  // first of the lane's 8 columns in the workgroup
+      unsigned char* xp = lds_x(gc) + n16 * kPitch + colw * 2;
+      const u32x4_t bb = *(const u32x4_t*)xp;
+      const uint32_t xw[4] = {bb.x, bb.y, bb.z, bb.w};
+      uint32_t ow[4];
+      uint32_t key = 0;
+      float sum = 0.0f;  // NaN if a value is NaN (or +inf and -inf meet): exact pass below
 #pragma unroll
-        for (int k2 = 0; k2 < KS; k2 += 2) {
-          bf16x8_t bop[2];
+      for (int q = 0; q < 4; ++q) {
+        const float lo = bf16_lo(xw[q]) + bf16_lo(bw[q]);
+        const float hi = bf16_hi(xw[q]) + bf16_hi(bw[q]);
+        ow[q] = pack_bf16x2(lo, hi);
+        __asm__("" : "+v"(ow[q]));  // keep the packed word (else the codes below repack it)
+        sum += lo + hi;
+        // order codes of both values at once; key = code << 16 | (0xFFFF - column)
+        const uint32_t c2 = pair_order_codes(ow[q]);
+        const uint32_t klo = (c2 << 16) | (0xFFFFu - (uint32_t)(colw + 2 * q));
+        const uint32_t khi = (c2 & 0xFFFF0000u) | (0xFFFFu - (uint32_t)(colw + 2 * q + 1));
+        key = max(key, max(klo, khi));
+      }
+      *(u32x4_t*)xp = u32x4_t{ow[0], ow[1], ow[2], ow[3]};
+      // The plain order codes rank -0 below +0 and order NaNs by payload.  A
+      // lane whose best value is a zero or that may hold a NaN recomputes
+      // its key with the exact codes (NaN highest, -0 == +0).
+      const uint32_t cm = key >> 16;
+      if (sum != sum || cm == 0x7FFFu || cm == 0x8000u) {
+        key = 0;
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            if (k2 + j < KS) bop[j] = *(const bf16x8_t*)(eb + (k2 + j) * 32);
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            if (k2 + j < KS) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[k2 + j], bop[j], acc, 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t klo = (argmax_code_bf16(ow[q] & 0xFFFFu) << 16) | (0xFFFFu - (uint32_t)(colw + 2 * q));
+          const uint32_t khi = (argmax_code_bf16(ow[q] >> 16) << 16) | (0xFFFFu - (uint32_t)(colw + 2 * q + 1));
+          key = max(key, max(klo, khi));
         }
-        u32x4_t lo, hi;
-        lo.x = pack_bf16x2(acc[0], acc[1]);
-        lo.y = pack_bf16x2(acc[2], acc[3]);
-        lo.z = pack_bf16x2(acc[4], acc[5]);
-        lo.w = pack_bf16x2(acc[6], acc[7]);
-        hi.x = pack_bf16x2(acc[8], acc[9]);
-        hi.y = pack_bf16x2(acc[10], acc[11]);
-        hi.z = pack_bf16x2(acc[12], acc[13]);
-        hi.w = pack_bf16x2(acc[14], acc[15]);
-        unsigned char* bp = lds_b + (32 * c + m) * BSTRIDE + (wave * 32 + 16 * h) * 2;
-        *(u32x4_t*)bp = lo;
-        *(u32x4_t*)(bp + 16) = hi;
+      }
+      if (vbeg + (uint32_t)colw < vend) atomicMax(&lds_key[GG][n16], key);
+    }
+    lds_barrier();
+
+    // P2.
+    if (wave >= 2) {
+      flush_row(gc, srow0, k);
+      if (two_rows) flush_row(gc, srow0 + 14, k);
+      // The group after this one reads staging rows loaded three units ago:
+      // at most three units of later operations may still be outstanding.
+      if (two_rows) wait_vmcnt<12>();
+      else wait_vmcnt<6>();
+    } else if (wave == 0) {
+      // Publish this unit's row keys, wait until the atomics are performed,
+      // then count this workgroup in for the unit.
+      if (lane < kGroupRows) {
+        const uint32_t kw = lds_key[GG][lane];
+        lds_key[GG][lane] = 0u;
+        const int b = GG * rpg + lane;
+        if (kw != 0u && lane < rpg && b < B) {
+          const uint64_t code = kw >> 16;
+          const uint32_t col = vbeg + (0xFFFFu - (kw & 0xFFFFu));
+          __hip_atomic_fetch_max((uint64_t*)((unsigned char*)p.keys + key_offset(k, xg, b)),
+                                 (code << 32) | (uint64_t)(0xFFFFFFFFu - col), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      wait_vmcnt<0>();
+      if (lane == 0)
+        __hip_atomic_fetch_add(arrival_counter(sync, GG, xg), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      // Wave 1 prepares later units of the other groups (this is unit
+      // u = 4k + GG; a group's units are four apart):
+      //   u+3: wait until every workgroup has counted in the group's
+      //        previous step (unit u-1), then load its key slots into LDS;
+      //   u+2: merge the key slots loaded a unit ago into tokens and gather
+      //        the tokens' W1 rows into LDS.
+      // The poll's wait also completes everything this wave issued a unit
+      // ago: the key slots merged below and the gather of unit u+1.  Units
+      // of step 0 were gathered in the prologue.
+      constexpr int G2 = (GG + 2) & 3, G3 = (GG + 3) & 3;
+      const int k2 = k + (GG + 2) / 4, k3 = k + (GG + 3) / 4;
+      const bool do2 = k2 >= 1 && k2 < M;
+      const bool do3 = ok && k3 >= 1 && k3 < M;
+      if (do3) {
+        const uint32_t target = (uint32_t)k3 * (uint32_t)G;
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (true) {
+          uint32_t v = lane < kGroups ? __hip_atomic_load(arrival_counter(sync, G3, lane), __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT)
+                                      : 0u;
+#pragma unroll
+          for (int d = 1; d < kGroups; d <<= 1) v += (uint32_t)__shfl_xor((int)v, d);
+          if ((uint32_t)__builtin_amdgcn_readfirstlane(v) >= target) break;  // uniform decision
+          if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+            ok = false;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      wait_vmcnt<0>();
+      if (do2) {
+        const uint64_t k0 = *(const uint64_t*)(lds_kv + lane * 16);
+        const uint64_t k1 = *(const uint64_t*)(lds_kv + 1024 + lane * 16);
+        const uint64_t best = max_u64(k0, k1);
+        const uint64_t b2 = max_u64(best, (uint64_t)__shfl_xor((long long)best, 16));
+        const uint64_t merged = max_u64(b2, (uint64_t)__shfl_xor((long long)b2, 32));
+        const int b = G2 * rpg + n16;
+        const bool row_ok = n16 < rpg && b < B;
+        const int64_t t = key_index(merged);
+        if (g == 0 && g4 == 0 && row_ok) p.tokens[(uint32_t)(b * M + k2 - 1)] = t;
+        // (t is used below, so the LDS reads above have completed)
+        gather(IC<G2>{}, (row_ok && t >= 0 && t < V) ? (int)t : -1);
+      }
+      if (do3 && ok) {
+        const int b = G3 * rpg + n16;
+        const bool row_ok = n16 < rpg && b < B;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          load_lds16_coherent(bw_keys, row_ok ? key_offset(k3 - 1, 2 * g4 + j, b) : kBufferOob,
+                              lds_address(lds_kv + j * 1024));
+      }
+      if (!ok && lane == 0) {
+        atomicAdd(p.sync_failures, 1u);
+        lds_flag = 0;
       }
     }
-    __syncthreads();
+    lds_barrier();
+  };
 
-    // A4 + A5: corrected rows (kept in registers until the keys are out) and
-    // each row's best column of this workgroup.
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const uint32_t b = RPW * wave + i;
-      if (b >= B) break;  // uniform over the wave
-      const u32x4_t bb = pre[i];
-      const u32x4_t bs = *(const u32x4_t*)(lds_b + b * BSTRIDE + lane * 16);
-      float c[8];
-      c[0] = bf16_lo(bb.x) + bf16_lo(bs.x);
-      c[1] = bf16_hi(bb.x) + bf16_hi(bs.x);
-      c[2] = bf16_lo(bb.y) + bf16_lo(bs.y);
-      c[3] = bf16_hi(bb.y) + bf16_hi(bs.y);
-      c[4] = bf16_lo(bb.z) + bf16_lo(bs.z);
-      c[5] = bf16_hi(bb.z) + bf16_hi(bs.z);
-      c[6] = bf16_lo(bb.w) + bf16_lo(bs.w);
-      c[7] = bf16_hi(bb.w) + bf16_hi(bs.w);
-      u32x4_t o;
-      o.x = pack_bf16x2(c[0], c[1]);
-      o.y = pack_bf16x2(c[2], c[3]);
-      o.z = pack_bf16x2(c[4], c[5]);
-      o.w = pack_bf16x2(c[6], c[7]);
-      pre[i] = o;
-      // a NaN among the fp32 sums makes this NaN (+inf + -inf too: rechecked)
-      const float s8 = ((c[0] + c[1]) + (c[2] + c[3])) + ((c[4] + c[5]) + (c[6] + c[7]));
-      uint32_t col, code;
-      wave_row_argmax_bf16(o, col_ok, s8 != s8, (uint32_t)lane, &col, &code);
-      if (lane == 0)
-        lds_key[b] = (col < 0xFFFFu) ? (((uint64_t)code << 32) | (uint64_t)(0xFFFFFFFFu - (vbeg + col))) : 0;
-    }
-    __syncthreads();
-
-    // Exchange.  Wave 0 merges the row keys into this group's slots and
-    // waits until its atomics are performed, then one thread arrives.  (No
-    // release fence: it would write back the XCD's whole L2, dirty with
-    // corrected logits, twice per step and workgroup.)
-    if (wave == 0) {
-      if (lane < B && vbeg < vend)
-        __hip_atomic_fetch_max(key_slot(p.keys, k, xg, lane), lds_key[lane], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_s_waitcnt(0);
-    }
-    if (tid == 0) arrive(p.sync, g, G, k);
-    // Waves 1.. write their corrected rows and request the next step's base
-    // logits while the exchange completes.  Wave 0 keeps its memory queue
-    // empty until it has read the next tokens: its polls and key loads would
-    // otherwise wait behind these (the vector memory counter is in order).
-    if (wave != 0) drain(k);
-    if (tid == 0) {
-      const bool ok = wait_word(release_word(p.sync, xg), (uint32_t)(k + 1));
-      if (!ok) atomicAdd(p.sync_failures, 1u);
-      lds_flag = ok ? 1 : 0;
-    }
-    __syncthreads();
-    if (!lds_flag) return;
+  for (int k = 0; k < M; ++k) {
+    unit(IC<0>{}, k);
+    unit(IC<1>{}, k);
+    unit(IC<2>{}, k);
+    unit(IC<3>{}, k);
+    if (!lds_flag) break;
   }
 
-  if (wave == 0) drain(M - 1);
-
-  // Tokens of the last step.
-  if (tid < B && g == 0) {
-    uint64_t best = 0;
+  // Workgroup 0 writes the last step's tokens once every workgroup has
+  // counted in every group.
+  if (g == 0 && wave == 1 && lds_flag) {
+    const uint32_t target = (uint32_t)M * (uint32_t)G;
+    bool fin = true;
+    for (int gg = 0; gg < kRowGroups; ++gg) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (true) {
+        uint32_t v = lane < kGroups ? __hip_atomic_load(arrival_counter(sync, gg, lane), __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT)
+                                    : 0u;
 #pragma unroll
-    for (int y = 0; y < kGroups; ++y)
-      best = max_u64(best, __hip_atomic_load(key_slot(p.keys, M - 1, y, tid), __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT));
-    p.tokens[tid * M + M - 1] = key_index(best);
+        for (int d = 1; d < kGroups; d <<= 1) v += (uint32_t)__shfl_xor((int)v, d);
+        if ((uint32_t)__builtin_amdgcn_readfirstlane(v) >= target) break;  // uniform decision
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+          fin = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      const int b = gg * rpg + n16;
+      const bool row_ok = n16 < rpg && b < B;
+      const uint64_t k0 = row_ok ? __hip_atomic_load((uint64_t*)((unsigned char*)p.keys + key_offset(M - 1, 2 * g4, b)),
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                 : 0;
+      const uint64_t k1 = row_ok ? __hip_atomic_load((uint64_t*)((unsigned char*)p.keys + key_offset(M - 1, 2 * g4 + 1, b)),
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                 : 0;
+      const uint64_t best = max_u64(k0, k1);
+      const uint64_t b2 = max_u64(best, (uint64_t)__shfl_xor((long long)best, 16));
+      const uint64_t merged = max_u64(b2, (uint64_t)__shfl_xor((long long)b2, 32));
+      if (g4 == 0 && n16 < rpg && b < B) p.tokens[(uint32_t)(b * M + M - 1)] = key_index(merged);
+    }
+    if (!fin && lane == 0) atomicAdd(p.sync_failures, 1u);
+    wait_vmcnt<0>();
   }
-  __syncthreads();
+  lds_barrier();
 
-  // Leave; the last workgroup out clears the keys and the synchronisation
-  // words (every other workgroup has passed its last wait and read).
-  if (tid == 0) lds_flag = (atomic_add_agent(exit_counter(p.sync), 1u) == (uint32_t)(G - 1)) ? 1 : 0;
-  __syncthreads();
+  // Leave; the last workgroup out clears the keys and the counters (every
+  // other workgroup has passed its last wait and read).
+  if (tid == 0) lds_flag = (__hip_atomic_fetch_add(exit_counter(sync), 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(G - 1)) ? 1 : 0;
+  lds_barrier();
   if (lds_flag) {
-    for (int64_t i = tid; i < M * kGroups * kMaxRows; i += kThreads)
-      __hip_atomic_store(p.keys + i * kKeyPad, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid < 2 * kGroups + 2)
-      __hip_atomic_store(p.sync + 16 * tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = tid; i < M * kGroups * kMaxRows; i += kThreads)
+      __hip_atomic_store(p.keys + (uint32_t)(i * kKeyPad), (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < kRowGroups * kGroups + 1)
+      __hip_atomic_store(sync + 16 * tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -336,9 +490,9 @@ namespace {
 // of extra launch latency measured on MI355X).  If a workgroup cannot start
 // while the others wait, their bounded waits end the launch with a recorded
 // synchronisation failure instead of a hang.
-template <int KS>
-hipError_t launch_chain_ks(const ChainParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((markov_chain_greedy_bf16<KS>), dim3(grid), dim3(kThreads), 0, s, p);
+template <int K32>
+hipError_t launch_chain_k(const ChainParams& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((markov_chain_greedy_bf16<K32>), dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -352,14 +506,15 @@ int chain_waves_per_group() { return kWaves; }
 hipError_t launch_chain_greedy(const ChainParams& p, int num_cus, hipStream_t s) {
   const int ks = tile_ks_for_rank(p.r);
   if (p.B > kMaxRows || ks == 0 || ks > 16) return hipErrorNotSupported;
-  if (p.B * p.M * p.V >= ((int64_t)1 << 31)) return hipErrorNotSupported;
+  if (p.B * p.M * p.V >= ((int64_t)1 << 30)) return hipErrorNotSupported;  // byte offsets below 2^31
+  if (p.M > 4096) return hipErrorNotSupported;                              // key area below 2^31 bytes
   if (p.S > (int64_t)num_cus * kWaves) return hipErrorNotSupported;
-  switch (ks) {
-    case 1: return launch_chain_ks<1>(p, num_cus, s);
-    case 2: return launch_chain_ks<2>(p, num_cus, s);
-    case 4: return launch_chain_ks<4>(p, num_cus, s);
-    case 8: return launch_chain_ks<8>(p, num_cus, s);
-    case 16: return launch_chain_ks<16>(p, num_cus, s);
+  switch (ks) {  // rank blocks of 16 -> blocks of 32 (zero-padded)
+    case 1:
+    case 2: return launch_chain_k<1>(p, num_cus, s);
+    case 4: return launch_chain_k<2>(p, num_cus, s);
+    case 8: return launch_chain_k<4>(p, num_cus, s);
+    case 16: return launch_chain_k<8>(p, num_cus, s);
     default: return hipErrorNotSupported;
   }
 }

@@ -42,7 +42,7 @@ struct KernelParams {
 // holds the arrival counters and release words (kChainSyncBytes); both are
 // zero between calls.
 constexpr int kKeyPad = 8;
-constexpr size_t kChainSyncBytes = 2048;
+constexpr size_t kChainSyncBytes = 4096;
 
 struct ChainParams {
   const uint16_t* base;       // [B, M, V]

@@ -54,7 +54,7 @@ def test_workspace_bytes(L):
     the chain's 2 KB synchronisation area and its keys (M steps * 8 groups *
     64 rows, 64 bytes apart)."""
     assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 0) == 256 + 16384
-    chain = lambda M: 2048 + M * 8 * 64 * 64
+    chain = lambda M: 4096 + M * 8 * 64 * 64
     assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 1) == 256 + _align256(64 * 1010 * 8) + chain(5)
     assert L.dspark_markov_workspace_bytes(256, 8, 151936, 256, 1) == 256 + _align256(256 * 1187 * 8) + chain(8)
 
