@@ -10,30 +10,32 @@
 //   * the vocabulary is cut into 32-column slices; each wave owns at most one
 //     slice and keeps its W2w rows in VGPRs for all M steps, so W2 is read
 //     from HBM once per call;
-//   * the batch rows are independent chains.  They are dealt into four row
-//     groups of up to 16, and the workgroup works through units (step k,
-//     group g) in the order (0,0) (0,1) (0,2) (0,3) (1,0) ...  A group's
-//     next step needs the tokens of its current one from every workgroup,
-//     so each device-wide exchange has three other units' work to hide in;
-//   * a unit: every wave multiplies the group's gathered W1 rows by its
+//   * the batch rows are independent chains.  They are dealt into six row
+//     groups of up to 12, and the workgroup works through units u = 6k + g
+//     (step k of group g) one per window.  A group's next step needs the
+//     tokens of its current one from every workgroup, so each device-wide
+//     exchange has five windows of other work to hide in;
+//   * window w: every wave multiplies group g's gathered W1 rows by its
 //     slice on the matrix cores (v_mfma_f32_16x16x32_bf16), rounds the bias
 //     to bf16, adds it to the group's base logits staged in LDS, writes the
 //     corrected values back in place and folds each row's best column into
-//     a per-row LDS key; then the corrected rows go to HBM and the group's
-//     base logits of its next step are loaded straight into the same LDS
-//     rows (buffer loads to LDS, three units ahead of use);
-//   * waves 0 and 1 carry the exchange, staged across units so that no wave
-//     waits on a round trip it could have started earlier: wave 0 publishes
-//     a unit's row keys (a 64-bit atomic max per row into one of eight key
-//     slots) and, a unit later, counts the workgroup in; wave 1 polls a
-//     group's arrival counts, reads the merged keys a unit later and, a unit
-//     after that, gathers the W1 rows of the new tokens into LDS.
+//     a per-row LDS key.  One barrier ends the window;
+//   * everything else is issued at the start of a window and overlaps the
+//     matrix work of the other waves: the corrected rows of unit w-1 go to
+//     HBM and the base logits that group needs next are loaded (into
+//     registers, written to the freed LDS rows a window later, four windows
+//     ahead of use); wave 0 publishes the row keys of unit w-1 (a 64-bit
+//     atomic max per row into one of eight key slots) and counts the
+//     workgroup in for unit w-2, whose atomics it issued a window earlier;
+//     wave 1 checks the arrival counts it polled a window ago for unit w+2's
+//     previous step, loads those key slots into LDS, merges the slots it
+//     loaded a window ago into the tokens of unit w+1, gathers their W1
+//     rows (in LDS before the barrier) and polls for unit w+3.  Waves 0 and
+//     1 run at raised issue priority.
 // Every wait on other workgroups is bounded: a workgroup that waits too long
 // records a failure in the workspace and leaves, so no launch can hang.  The
 // last workgroup to leave clears the keys and counters, so the workspace is
 // ready for the next call.
-#include <type_traits>
-
 #include "device_common.h"
 #include "markov_kernels.h"
 
@@ -43,12 +45,13 @@ namespace {
 
 constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowGroups = 4;                 // pipelined row groups
-constexpr int kGroupRows = 16;                // rows of a group at most (the MFMA N tile)
-constexpr int kMaxRows = kRowGroups * kGroupRows;
+constexpr int kRowGroups = 6;                 // pipelined row groups
+constexpr int kGroupRows = 12;                // staged rows of a group at most
+constexpr int kMaxRows = 64;                  // batch rows of one call
 constexpr int kGroups = 8;                    // key slots / arrival counters per row group
 constexpr int kPitch = 2 * 32 * kWaves + 16;  // LDS bytes of a staged row (512 columns + pad)
 constexpr uint64_t kSpinTicks = 100000000;    // 1 s of the 100 MHz realtime clock
+static_assert(kRowGroups * kGroupRows >= kMaxRows, "row groups");
 
 // Synchronisation area, one 64-byte line per word: the arrival counters
 // [kRowGroups][kGroups] (cumulative over steps), then the exit counter.
@@ -82,11 +85,9 @@ __device__ __forceinline__ uint32_t argmax_code_bf16(uint32_t h) {
 }
 
 // Workgroup barrier for LDS data only.  __syncthreads() also orders global
-// memory at workgroup scope, which makes the compiler wait for every buffer
-// load to LDS in flight: the staging loads of later units would then be
-// waited for at every barrier.  Here each wave finishes its own LDS
-// accesses (lgkmcnt) and the staging loads are waited for explicitly, by
-// count, where their data is needed.
+// memory at workgroup scope, which would wait for every load in flight.
+// Here each wave finishes its own LDS accesses (lgkmcnt); the buffer loads
+// to LDS are waited for explicitly, by count, where their data is needed.
 __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -94,11 +95,9 @@ __device__ __forceinline__ void lds_barrier() {
 // Buffer load of 16 bytes per lane straight into LDS: lane l's bytes land at
 // LDS address lds + 16 l (lds must be uniform over the wave).  Written as
 // inline assembly so that the compiler does not track these loads: it would
-// otherwise make every later LDS read of a wave that took any path through
-// such a load wait for all of them.  Their completion is waited for
-// explicitly, by count (wait_vmcnt), before the LDS data is used.  POLICY is
-// the cache policy: 0, "nt" (streaming) or "sc1" (device-coherent).  M0 is
-// saved and restored around the load.
+// otherwise make later LDS reads of every wave wait for all of them.  Their
+// completion is waited for explicitly (wait_vmcnt) before the data is used.
+// M0 is saved and restored around the load.
 struct BufferWords {
   u32x4_t w;  // V# of a raw buffer: base, stride 0, size in bytes, 32-bit data format
 };
@@ -114,41 +113,55 @@ __device__ __forceinline__ void load_lds16(const BufferWords& r, uint32_t off, u
   __asm__ volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0"
                    : "=&s"(saved) : "v"(off), "s"(r.w), "s"(lds) : "memory");
 }
-__device__ __forceinline__ void load_lds16_nt(const BufferWords& r, uint32_t off, uint32_t lds) {
-  uint32_t saved;
-  __asm__ volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds\n\ts_mov_b32 m0, %0"
-                   : "=&s"(saved) : "v"(off), "s"(r.w), "s"(lds) : "memory");
-}
 __device__ __forceinline__ void load_lds16_coherent(const BufferWords& r, uint32_t off, uint32_t lds) {
   uint32_t saved;
   __asm__ volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %1, %2, 0 offen sc1 lds\n\ts_mov_b32 m0, %0"
                    : "=&s"(saved) : "v"(off), "s"(r.w), "s"(lds) : "memory");
 }
 
-template <int N>
-using IC = std::integral_constant<int, N>;
+// Arrival counters of row group rg: lanes 0..kGroups-1 load one each
+// (arrival_load), arrival_sum adds them up, uniform over the wave.  Split so
+// that a poll can be issued early and summed later.
+__device__ __forceinline__ uint32_t arrival_load(uint32_t* sync, int rg, int lane) {
+  return lane < kGroups ? __hip_atomic_load(arrival_counter(sync, rg, lane), __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT)
+                        : 0u;
+}
+__device__ __forceinline__ uint32_t arrival_sum(uint32_t v) {
+#pragma unroll
+  for (int d = 1; d < kGroups; d <<= 1) v += (uint32_t)__shfl_xor((int)v, d);
+  return (uint32_t)__builtin_amdgcn_readfirstlane(v);
+}
+__device__ __forceinline__ uint32_t arrivals(uint32_t* sync, int rg, int lane) {
+  return arrival_sum(arrival_load(sync, rg, lane));
+}
+
+// Spins until the arrival counters of row group rg sum to at least target;
+// false after kSpinTicks.
+__device__ bool wait_arrivals(uint32_t* sync, int rg, int lane, uint32_t target) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (arrivals(sync, rg, lane) < target) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
 
 }  // namespace
 
 template <int K32>
 __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams p) {
-  // Gathered W1 rows of each group, in the B-operand order of the matrix
+  // Gathered W1 rows per group, in the B-operand order of the matrix
   // instruction: block kk holds at lane l's 16 bytes row l % 16, rank
-  // elements 32 kk + 8 (l / 16) .. +7.  One array per group, so the
-  // compiler tracks the loads into each separately.
-  __shared__ __attribute__((aligned(16))) unsigned char lds_e0[K32 * 1024];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_e1[K32 * 1024];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_e2[K32 * 1024];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_e3[K32 * 1024];
-  // Staged logits of each group: base, then corrected in place.
-  __shared__ __attribute__((aligned(16))) unsigned char lds_x0[kGroupRows * kPitch];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_x1[kGroupRows * kPitch];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_x2[kGroupRows * kPitch];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_x3[kGroupRows * kPitch];
-  __shared__ uint32_t lds_key[kRowGroups][kGroupRows];
-  // Key slots read for the next token merge: [2][lane] 16 bytes each, the
-  // key in the first 8 (row l % 16, key group 2 (l / 16) + j).
-  __shared__ __attribute__((aligned(16))) unsigned char lds_kv[2 * 1024];
+  // elements 32 kk + 8 (l / 16) .. +7.
+  __shared__ __attribute__((aligned(16))) unsigned char lds_e[kRowGroups][K32 * 1024];
+  // Staged logits per group: base, then corrected in place.
+  __shared__ __attribute__((aligned(16))) unsigned char lds_x[kRowGroups][kGroupRows * kPitch];
+  __shared__ uint32_t lds_key[kRowGroups][16];
+  // Key slots loaded for a token merge, two buffers of [lane] 16 bytes each,
+  // the key in the first 8 (row l % 16, key group 2 (l / 16) + j).
+  __shared__ __attribute__((aligned(16))) unsigned char lds_kv[2][2 * 1024];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_poll[64 * 16];  // polled counter lines
   __shared__ int lds_flag;
 
   const int tid = threadIdx.x;
@@ -162,17 +175,9 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   // The host guarantees B <= 64, V <= 32 * 16 * CUs, B*M*V < 2^30 and
   // M <= 4096, so every index below fits in 32 bits.
   const int B = (int)p.B, M = (int)p.M, V = (int)p.V, r = (int)p.r;
-  const int rpg = (B + kRowGroups - 1) / kRowGroups;  // rows per group
+  const int rpg = (B + kRowGroups - 1) / kRowGroups;  // rows per group (<= kGroupRows)
+  const int U = M * kRowGroups;                        // units
   uint32_t* const sync = p.sync;
-
-  auto lds_e = [&](auto gc) __attribute__((always_inline)) -> unsigned char* {
-    constexpr int GG = decltype(gc)::value;
-    return GG == 0 ? lds_e0 : GG == 1 ? lds_e1 : GG == 2 ? lds_e2 : lds_e3;
-  };
-  auto lds_x = [&](auto gc) __attribute__((always_inline)) -> unsigned char* {
-    constexpr int GG = decltype(gc)::value;
-    return GG == 0 ? lds_x0 : GG == 1 ? lds_x1 : GG == 2 ? lds_x2 : lds_x3;
-  };
 
   // The workgroup's columns [vbeg, vend): slices s_begin .. s_end-1.
   const int s_begin = (int)(((int64_t)g * p.S) / G);
@@ -183,10 +188,11 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   const bool has = slice < s_end;
 
   const uint32_t bytes = (uint32_t)(B * M * V * 2);
-  const BufferWords bw_base = buffer_words(p.base, bytes);
+  const __amdgpu_buffer_rsrc_t rs_base = buffer_rsrc(p.base, bytes);
   const __amdgpu_buffer_rsrc_t rs_out = buffer_rsrc(p.out, p.out != nullptr ? bytes : 0u);
   const BufferWords bw_w1 = buffer_words(p.w1, (uint32_t)(V * r * 2));
   const BufferWords bw_keys = buffer_words(p.keys, (uint32_t)(M * kGroups * kMaxRows * kKeyPad * 8));
+  const BufferWords bw_sync = buffer_words(sync, (uint32_t)kChainSyncBytes);
 
   // A operands (columns on M, rows on N, rank on K): the slice's 32 columns
   // are two 16-column tiles t.  Lane (n16, g4) supplies W2w[col(t, n16)]
@@ -203,232 +209,268 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     }
   }
 
-  // ---- row staging (waves 2..15).  Wave w moves rows w - 2 and, for w < 4,
-  // also w + 12 of a group: one 1 KB row segment per instruction, lane l the
-  // 8 columns vbeg + 8 l .. +7.  Offsets of masked-off lanes, rows or steps
-  // point past the buffer (see buffer_rsrc).
+  // ---- row staging: wave w = 2..13 moves row w - 2 of every group, one
+  // 1 KB row segment per instruction, lane l the 8 columns vbeg + 8 l .. +7.
+  // Offsets of masked-off lanes, rows or steps point past the buffer (see
+  // buffer_rsrc), so every instruction is issued unconditionally.
+  const int srow = wave - 2;
+  const bool stager = srow >= 0 && srow < kGroupRows;
   const bool col_ok = vbeg + 8u * (uint32_t)lane < vend;
   const uint32_t lane_off = 2u * (vbeg + 8u * (uint32_t)lane);
-  auto row_offset = [&](int gg, int i, int kd) __attribute__((always_inline)) -> uint32_t {
-    const int b = gg * rpg + i;
-    const bool ok = i < rpg && b < B && kd < M && col_ok;
+  auto row_offset = [&](int gg, int kd) __attribute__((always_inline)) -> uint32_t {
+    const int b = gg * rpg + srow;
+    const bool ok = srow < rpg && b < B && kd < M && col_ok;
     return ok ? (uint32_t)((b * M + kd) * V) * 2u + lane_off : kBufferOob;
   };
-  // Base logits of (step kd, group GG) for row i into its staging row.
-  auto stage_row = [&](auto gc, int i, int kd) __attribute__((always_inline)) {
-    constexpr int GG = decltype(gc)::value;
-    load_lds16_nt(bw_base, row_offset(GG, i, kd), lds_address(lds_x(gc) + i * kPitch));
+  // The bulk rows travel through registers (plain buffer loads issue far
+  // faster than loads to LDS): a base row is loaded into pre in one window
+  // and written to its LDS row at the start of the next.
+  u32x4_t pre = u32x4_t{0u, 0u, 0u, 0u};
+  auto load_row = [&](int gg, int kd) __attribute__((always_inline)) {
+    pre = buffer_load16(rs_base, row_offset(gg, kd));
   };
-  // Corrected row i of (step kd, group GG) to HBM, then its base logits of
-  // step kd + 1 into the same staging row (the LDS read completes before
-  // the store issues, so before the load can overwrite the row).
-  auto flush_row = [&](auto gc, int i, int kd) __attribute__((always_inline)) {
-    constexpr int GG = decltype(gc)::value;
-    const u32x4_t v = *(const u32x4_t*)(lds_x(gc) + i * kPitch + lane * 16);
-    buffer_store16(rs_out, row_offset(GG, i, kd), v);
-    stage_row(gc, i, kd + 1);
+  auto store_row_lds = [&](int gg) __attribute__((always_inline)) {
+    *(u32x4_t*)&lds_x[gg][srow * kPitch + lane * 16] = pre;
   };
-  const int srow0 = wave - 2;       // this wave's first staging row (waves 2..15)
-  const bool two_rows = wave < 4;   // waves 2 and 3 also move rows 14 and 15 (srow0 + 14)
 
   // ---- gather (wave 1): W1 rows of tokens x (lane l: the token of row
-  // l % 16 of group GG, or -1 for a zero row) into lds_e(GG).
-  auto gather = [&](auto gc, int x) __attribute__((always_inline)) {
+  // l % 16 of group gg, or -1 for a zero row) into lds_e[gg].
+  auto gather = [&](int gg, int x) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < K32; ++kk) {
       const int kof = 32 * kk + 8 * g4;
       const uint32_t off = (x >= 0 && kof < r) ? 2u * (uint32_t)(x * r + kof) : kBufferOob;
-      load_lds16(bw_w1, off, lds_address(lds_e(gc) + kk * 1024));
+      load_lds16(bw_w1, off, lds_address(&lds_e[gg][kk * 1024]));
     }
+  };
+  // Merge of the key slots in lds_kv[buf] into the tokens of group gg's
+  // step kt, written to tokens[:, kt] (workgroup 0); returns lane l's token
+  // (row l % 16) for the gather, or -1.  Every lane reads the eight slots of
+  // its row itself (all in flight at once).
+  auto merge = [&](int buf, int gg, int kt) __attribute__((always_inline)) -> int {
+    uint64_t kv[8];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) kv[4 * j + q] = *(const uint64_t*)&lds_kv[buf][j * 1024 + (n16 + 16 * q) * 16];
+    uint64_t merged = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) merged = max_u64(merged, kv[i]);
+    const int b = gg * rpg + n16;
+    const bool row_ok = n16 < rpg && b < B;
+    const int64_t t = key_index(merged);
+    if (g == 0 && g4 == 0 && row_ok) p.tokens[(uint32_t)(b * M + kt)] = t;
+    return (row_ok && t >= 0 && t < V) ? (int)t : -1;
+  };
+  // Key slots of group gg's step kt into lds_kv[buf].
+  auto load_keys = [&](int buf, int gg, int kt) __attribute__((always_inline)) {
+    const int b = gg * rpg + n16;
+    const bool row_ok = n16 < rpg && b < B;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      load_lds16_coherent(bw_keys, row_ok ? key_offset(kt, 2 * g4 + j, b) : kBufferOob,
+                          lds_address(&lds_kv[buf][j * 1024]));
   };
 
   // ---- prologue: stage step 0 of every group, gather the first tokens.
-  if (wave >= 2) {
-    stage_row(IC<0>{}, srow0, 0);
-    stage_row(IC<1>{}, srow0, 0);
-    stage_row(IC<2>{}, srow0, 0);
-    stage_row(IC<3>{}, srow0, 0);
-    if (two_rows) {
-      stage_row(IC<0>{}, srow0 + 14, 0);
-      stage_row(IC<1>{}, srow0 + 14, 0);
-      stage_row(IC<2>{}, srow0 + 14, 0);
-      stage_row(IC<3>{}, srow0 + 14, 0);
+  if (stager) {
+    for (int gg = 0; gg < kRowGroups; ++gg) {
+      load_row(gg, 0);
+      store_row_lds(gg);
     }
   } else if (wave == 1) {
-    auto first = [&](auto gc) __attribute__((always_inline)) {
-      constexpr int GG = decltype(gc)::value;
-      const int b = GG * rpg + n16;
+    for (int gg = 0; gg < kRowGroups; ++gg) {
+      const int b = gg * rpg + n16;
       int x = -1;
       if (n16 < rpg && b < B) {
         const int64_t x0 = p.first_prev[(uint32_t)b];
         if (x0 >= 0 && x0 < V) x = (int)x0;
         else if (g == 0 && g4 == 0) atomicAdd(p.bad_rows, 1u);
       }
-      gather(gc, x);
-    };
-    first(IC<0>{});
-    first(IC<1>{});
-    first(IC<2>{});
-    first(IC<3>{});
-  } else {
-    if (lane < kRowGroups * kGroupRows) lds_key[lane / kGroupRows][lane % kGroupRows] = 0u;
+      gather(gg, x);
+    }
+  } else if (wave == 0) {
+    if (lane < 16) {
+#pragma unroll
+      for (int gg = 0; gg < kRowGroups; ++gg) lds_key[gg][lane] = 0u;
+    }
     if (lane == 0) lds_flag = 1;
   }
   wait_vmcnt<0>();
   lds_barrier();
 
-  // ---- exchange state carried across units (wave 1)
-  bool ok = true;  // no exchange wait of this wave (wave 1) has timed out
+  bool ok = true;  // wave 1: no exchange wait has timed out
+  // The exchange's memory operations are few and latency-bound; the bulk
+  // traffic fills this CU's memory queue.  Waves 0 and 1 issue first.
+  if (wave < 2) __builtin_amdgcn_s_setprio(3);
 
-  // One unit: step k of group GG.
-  auto unit = [&](auto gc, int k) __attribute__((always_inline)) {
-    constexpr int GG = decltype(gc)::value;
-    // P1: bias of the wave's slice for the group's rows, added to the staged
-    // base logits in place; each row's best column into lds_key.
+  // ---- windows.  Window w starts with the exchange and bulk work for
+  // earlier units, which overlaps the matrix work of the other waves, then
+  // computes unit w = 6k + g (step k of group g); one barrier ends it.
+  for (int w = 0; w < U; ++w) {
+    const int gc = w % kRowGroups;  // group of unit w
+    int after_gather = 0;           // wave 1
+    if (stager) {
+      // the base row loaded a window ago (unit w+4, group (w-2) % 6) into
+      // its LDS row; the corrected row of unit w-1 to HBM; then that
+      // group's next base row (unit w+5) into registers
+      if (w >= 2) store_row_lds((w - 2) % kRowGroups);
+      if (w >= 1) {
+        const int gp = (w - 1) % kRowGroups, kp = (w - 1) / kRowGroups;
+        const u32x4_t v = *(const u32x4_t*)&lds_x[gp][srow * kPitch + lane * 16];
+        buffer_store16(rs_out, row_offset(gp, kp), v);
+        load_row(gp, kp + 1);
+      }
+    } else if (wave == 0) {
+      // count this workgroup in for unit w-2 (its key atomics were issued a
+      // window ago), then publish the row keys of unit w-1
+      wait_vmcnt<0>();
+      if (w >= 2 && lane == 0)
+        __hip_atomic_fetch_add(arrival_counter(sync, (w - 2) % kRowGroups, xg), 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      if (w >= 1 && lane < 16) {
+        const int gp = (w - 1) % kRowGroups, kp = (w - 1) / kRowGroups;
+        const uint32_t kw = lds_key[gp][lane];
+        lds_key[gp][lane] = 0u;
+        const int b = gp * rpg + lane;
+        if (kw != 0u && lane < rpg && b < B) {
+          const uint64_t code = kw >> 16;
+          const uint32_t col = vbeg + (0xFFFFu - (kw & 0xFFFFu));
+          __hip_atomic_fetch_max((uint64_t*)((unsigned char*)p.keys + key_offset(kp, xg, b)),
+                                 (code << 32) | (uint64_t)(0xFFFFFFFFu - col), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    } else if (wave == 1) {
+      // Targets: unit w+2 (poll issued a window ago; key slots) and unit w+1
+      // (key slots loaded a window ago; merge and gather).  The wait below
+      // completes the poll and key slots issued a window ago.
+      const int u2 = w + 2, u1 = w + 1;
+      const bool do2 = ok && u2 < U && u2 >= kRowGroups;
+      const bool do1 = u1 < U && u1 >= kRowGroups;
+      wait_vmcnt<0>();
+      if (do2) {
+        // complete when every workgroup has counted in unit u2 - kRowGroups
+        const uint32_t target = (uint32_t)(u2 / kRowGroups) * (uint32_t)G;
+        uint32_t seen = 0;  // every lane adds the polled counters (broadcast reads)
+#pragma unroll
+        for (int x = 0; x < kGroups; ++x) seen += *(const uint32_t*)&lds_poll[x * 16];
+        seen = (uint32_t)__builtin_amdgcn_readfirstlane(seen);
+        if (seen < target) ok = wait_arrivals(sync, u2 % kRowGroups, lane, target);
+      }
+      if (do1) gather(u1 % kRowGroups, merge(u1 & 1, u1 % kRowGroups, u1 / kRowGroups - 1));
+      if (do2 && ok) load_keys(u2 & 1, u2 % kRowGroups, u2 / kRowGroups - 1);
+      // poll the arrivals of unit w+3's previous step into LDS (lane
+      // l < kGroups loads counter line l)
+      const int u3 = w + 3;
+      const bool do3 = ok && u3 < U && u3 >= kRowGroups;
+      if (do3)
+        load_lds16_coherent(bw_sync, lane < kGroups ? (uint32_t)(4 * 16 * ((u3 % kRowGroups) * kGroups + lane)) : kBufferOob,
+                            lds_address(&lds_poll[0]));
+      // operations issued after the gather (waited for before the barrier)
+      after_gather = (do2 && ok ? 2 : 0) + (do3 ? 1 : 0);
+      if (!ok && lane == 0) {
+        atomicAdd(p.sync_failures, 1u);
+        lds_flag = 0;
+      }
+    }
+
+    // -- unit w: bias of the wave's slice for the group's rows, added to the
+    // staged base logits in place; each row's best column into lds_key.
     if (has) {
       f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{};
-      const unsigned char* eb = lds_e(gc) + lane * 16;
+      const unsigned char* eb = &lds_e[gc][lane * 16];
 #pragma unroll
       for (int kk = 0; kk < K32; ++kk) {
         const bf16x8_t bop = *(const bf16x8_t*)(eb + kk * 1024);
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0][kk], bop, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1][kk], bop, acc1, 0, 0, 0);
       }
-      // bias rounded to bf16 (the Linear's output dtype)
-      const uint32_t bw[4] = {pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
-                              pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
       const int colw = wave * 32 + 8 * g4;  // first of the lane's 8 columns in the workgroup
-      unsigned char* xp = lds_x(gc) + n16 * kPitch + colw * 2;
-      const u32x4_t bb = *(const u32x4_t*)xp;
-      const uint32_t xw[4] = {bb.x, bb.y, bb.z, bb.w};
-      uint32_t ow[4];
-      uint32_t key = 0;
-      float sum = 0.0f;  // NaN if a value is NaN (or +inf and -inf meet): exact pass below
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float lo = bf16_lo(xw[q]) + bf16_lo(bw[q]);
-        const float hi = bf16_hi(xw[q]) + bf16_hi(bw[q]);
-        ow[q] = pack_bf16x2(lo, hi);
-        __asm__("" : "+v"(ow[q]));  // keep the packed word (else the codes below repack it)
-        sum += lo + hi;
-        // order codes of both values at once; key = code << 16 | (0xFFFF - column)
-        const uint32_t c2 = pair_order_codes(ow[q]);
-        const uint32_t klo = (c2 << 16) | (0xFFFFu - (uint32_t)(colw + 2 * q));
-        const uint32_t khi = (c2 & 0xFFFF0000u) | (0xFFFFu - (uint32_t)(colw + 2 * q + 1));
-        key = max(key, max(klo, khi));
-      }
-      *(u32x4_t*)xp = u32x4_t{ow[0], ow[1], ow[2], ow[3]};
-      // The plain order codes rank -0 below +0 and order NaNs by payload.  A
-      // lane whose best value is a zero or that may hold a NaN recomputes
-      // its key with the exact codes (NaN highest, -0 == +0).
-      const uint32_t cm = key >> 16;
-      if (sum != sum || cm == 0x7FFFu || cm == 0x8000u) {
-        key = 0;
+      // lanes of padding rows (past the group's rows or the batch) stay idle:
+      // their all-zero values would send the wave down the exact pass below
+      if (n16 < rpg && gc * rpg + n16 < B) {
+        // bias rounded to bf16 (the Linear's output dtype)
+        const uint32_t bw[4] = {pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
+                                pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
+        unsigned char* xp = &lds_x[gc][n16 * kPitch + colw * 2];
+        const u32x4_t bb = *(const u32x4_t*)xp;
+        const uint32_t xw[4] = {bb.x, bb.y, bb.z, bb.w};
+        uint32_t ow[4];
+        uint32_t key = 0;
+        float sum = 0.0f;  // NaN if a value is NaN (or +inf and -inf meet): exact pass below
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t klo = (argmax_code_bf16(ow[q] & 0xFFFFu) << 16) | (0xFFFFu - (uint32_t)(colw + 2 * q));
-          const uint32_t khi = (argmax_code_bf16(ow[q] >> 16) << 16) | (0xFFFFu - (uint32_t)(colw + 2 * q + 1));
+          const float lo = bf16_lo(xw[q]) + bf16_lo(bw[q]);
+          const float hi = bf16_hi(xw[q]) + bf16_hi(bw[q]);
+          ow[q] = pack_bf16x2(lo, hi);
+          __asm__("" : "+v"(ow[q]));  // keep the packed word (else the codes below repack it)
+          sum += lo + hi;
+          // order codes of both values at once; key = code << 16 | (0xFFFF - column)
+          const uint32_t c2 = pair_order_codes(ow[q]);
+          const uint32_t klo = (c2 << 16) | (0xFFFFu - (uint32_t)(colw + 2 * q));
+          const uint32_t khi = (c2 & 0xFFFF0000u) | (0xFFFFu - (uint32_t)(colw + 2 * q + 1));
           key = max(key, max(klo, khi));
         }
+        *(u32x4_t*)xp = u32x4_t{ow[0], ow[1], ow[2], ow[3]};
+        // The plain order codes rank -0 below +0 and order NaNs by payload.
+        // A lane whose best value is a zero or that may hold a NaN recomputes
+        // its key with the exact codes (NaN highest, -0 == +0).
+        const uint32_t cm = key >> 16;
+        if (sum != sum || cm == 0x7FFFu || cm == 0x8000u) {
+          key = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t klo = (argmax_code_bf16(ow[q] & 0xFFFFu) << 16) | (0xFFFFu - (uint32_t)(colw + 2 * q));
+            const uint32_t khi = (argmax_code_bf16(ow[q] >> 16) << 16) | (0xFFFFu - (uint32_t)(colw + 2 * q + 1));
+            key = max(key, max(klo, khi));
+          }
+        }
+        if (vbeg + (uint32_t)colw < vend) atomicMax(&lds_key[gc][n16], key);
       }
-      if (vbeg + (uint32_t)colw < vend) atomicMax(&lds_key[GG][n16], key);
+    }
+    // wave 1: the gather of unit w+1 (issued this window, before the key
+    // slots and the poll) is in LDS before the barrier
+    if (wave == 1) {
+      if (after_gather == 3) wait_vmcnt<3>();
+      else if (after_gather == 2) wait_vmcnt<2>();
+      else if (after_gather == 1) wait_vmcnt<1>();
+      else wait_vmcnt<0>();
     }
     lds_barrier();
-
-    // P2.
-    if (wave >= 2) {
-      flush_row(gc, srow0, k);
-      if (two_rows) flush_row(gc, srow0 + 14, k);
-      // The group after this one reads staging rows loaded three units ago:
-      // at most three units of later operations may still be outstanding.
-      if (two_rows) wait_vmcnt<12>();
-      else wait_vmcnt<6>();
+    if (!lds_flag) break;
+  }
+  // after the last window: corrected rows of the last unit, the keys of the
+  // last unit, and the last two arrivals
+  if (lds_flag) {
+    if (stager) {
+      const int gp = (U - 1) % kRowGroups, kp = (U - 1) / kRowGroups;
+      const u32x4_t v = *(const u32x4_t*)&lds_x[gp][srow * kPitch + lane * 16];
+      buffer_store16(rs_out, row_offset(gp, kp), v);
     } else if (wave == 0) {
-      // Publish this unit's row keys, wait until the atomics are performed,
-      // then count this workgroup in for the unit.
-      if (lane < kGroupRows) {
-        const uint32_t kw = lds_key[GG][lane];
-        lds_key[GG][lane] = 0u;
-        const int b = GG * rpg + lane;
+      wait_vmcnt<0>();
+      if (lane == 0 && U >= 2)
+        __hip_atomic_fetch_add(arrival_counter(sync, (U - 2) % kRowGroups, xg), 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      if (lane < 16) {
+        const int gp = (U - 1) % kRowGroups, kp = (U - 1) / kRowGroups;
+        const uint32_t kw = lds_key[gp][lane];
+        const int b = gp * rpg + lane;
         if (kw != 0u && lane < rpg && b < B) {
           const uint64_t code = kw >> 16;
           const uint32_t col = vbeg + (0xFFFFu - (kw & 0xFFFFu));
-          __hip_atomic_fetch_max((uint64_t*)((unsigned char*)p.keys + key_offset(k, xg, b)),
+          __hip_atomic_fetch_max((uint64_t*)((unsigned char*)p.keys + key_offset(kp, xg, b)),
                                  (code << 32) | (uint64_t)(0xFFFFFFFFu - col), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
         }
       }
       wait_vmcnt<0>();
       if (lane == 0)
-        __hip_atomic_fetch_add(arrival_counter(sync, GG, xg), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      // Wave 1 prepares later units of the other groups (this is unit
-      // u = 4k + GG; a group's units are four apart):
-      //   u+3: wait until every workgroup has counted in the group's
-      //        previous step (unit u-1), then load its key slots into LDS;
-      //   u+2: merge the key slots loaded a unit ago into tokens and gather
-      //        the tokens' W1 rows into LDS.
-      // The poll's wait also completes everything this wave issued a unit
-      // ago: the key slots merged below and the gather of unit u+1.  Units
-      // of step 0 were gathered in the prologue.
-      constexpr int G2 = (GG + 2) & 3, G3 = (GG + 3) & 3;
-      const int k2 = k + (GG + 2) / 4, k3 = k + (GG + 3) / 4;
-      const bool do2 = k2 >= 1 && k2 < M;
-      const bool do3 = ok && k3 >= 1 && k3 < M;
-      if (do3) {
-        const uint32_t target = (uint32_t)k3 * (uint32_t)G;
-        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        while (true) {
-          uint32_t v = lane < kGroups ? __hip_atomic_load(arrival_counter(sync, G3, lane), __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT)
-                                      : 0u;
-#pragma unroll
-          for (int d = 1; d < kGroups; d <<= 1) v += (uint32_t)__shfl_xor((int)v, d);
-          if ((uint32_t)__builtin_amdgcn_readfirstlane(v) >= target) break;  // uniform decision
-          if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
-            ok = false;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-      }
-      wait_vmcnt<0>();
-      if (do2) {
-        const uint64_t k0 = *(const uint64_t*)(lds_kv + lane * 16);
-        const uint64_t k1 = *(const uint64_t*)(lds_kv + 1024 + lane * 16);
-        const uint64_t best = max_u64(k0, k1);
-        const uint64_t b2 = max_u64(best, (uint64_t)__shfl_xor((long long)best, 16));
-        const uint64_t merged = max_u64(b2, (uint64_t)__shfl_xor((long long)b2, 32));
-        const int b = G2 * rpg + n16;
-        const bool row_ok = n16 < rpg && b < B;
-        const int64_t t = key_index(merged);
-        if (g == 0 && g4 == 0 && row_ok) p.tokens[(uint32_t)(b * M + k2 - 1)] = t;
-        // (t is used below, so the LDS reads above have completed)
-        gather(IC<G2>{}, (row_ok && t >= 0 && t < V) ? (int)t : -1);
-      }
-      if (do3 && ok) {
-        const int b = G3 * rpg + n16;
-        const bool row_ok = n16 < rpg && b < B;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          load_lds16_coherent(bw_keys, row_ok ? key_offset(k3 - 1, 2 * g4 + j, b) : kBufferOob,
-                              lds_address(lds_kv + j * 1024));
-      }
-      if (!ok && lane == 0) {
-        atomicAdd(p.sync_failures, 1u);
-        lds_flag = 0;
-      }
+        __hip_atomic_fetch_add(arrival_counter(sync, (U - 1) % kRowGroups, xg), 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
-    lds_barrier();
-  };
-
-  for (int k = 0; k < M; ++k) {
-    unit(IC<0>{}, k);
-    unit(IC<1>{}, k);
-    unit(IC<2>{}, k);
-    unit(IC<3>{}, k);
-    if (!lds_flag) break;
   }
+  if (wave < 2) __builtin_amdgcn_s_setprio(0);
 
   // Workgroup 0 writes the last step's tokens once every workgroup has
   // counted in every group.
@@ -436,20 +478,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     const uint32_t target = (uint32_t)M * (uint32_t)G;
     bool fin = true;
     for (int gg = 0; gg < kRowGroups; ++gg) {
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (true) {
-        uint32_t v = lane < kGroups ? __hip_atomic_load(arrival_counter(sync, gg, lane), __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT)
-                                    : 0u;
-#pragma unroll
-        for (int d = 1; d < kGroups; d <<= 1) v += (uint32_t)__shfl_xor((int)v, d);
-        if ((uint32_t)__builtin_amdgcn_readfirstlane(v) >= target) break;  // uniform decision
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
-          fin = false;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
+      fin = fin && wait_arrivals(sync, gg, lane, target);
       const int b = gg * rpg + n16;
       const bool row_ok = n16 < rpg && b < B;
       const uint64_t k0 = row_ok ? __hip_atomic_load((uint64_t*)((unsigned char*)p.keys + key_offset(M - 1, 2 * g4, b)),
@@ -461,11 +490,12 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
       const uint64_t best = max_u64(k0, k1);
       const uint64_t b2 = max_u64(best, (uint64_t)__shfl_xor((long long)best, 16));
       const uint64_t merged = max_u64(b2, (uint64_t)__shfl_xor((long long)b2, 32));
-      if (g4 == 0 && n16 < rpg && b < B) p.tokens[(uint32_t)(b * M + M - 1)] = key_index(merged);
+      if (g4 == 0 && row_ok) p.tokens[(uint32_t)(b * M + M - 1)] = key_index(merged);
     }
     if (!fin && lane == 0) atomicAdd(p.sync_failures, 1u);
     wait_vmcnt<0>();
   }
+  wait_vmcnt<0>();
   lds_barrier();
 
   // Leave; the last workgroup out clears the keys and the counters (every
