@@ -45,13 +45,14 @@ namespace {
 
 constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowGroups = 6;                 // pipelined row groups
-constexpr int kGroupRows = 12;                // staged rows of a group at most
+constexpr int kRowGroups = 6;                 // pipeline slots per step (row groups + idle slots)
+constexpr int kMaxGroups = 4;                 // row groups of a call at most
+constexpr int kGroupRows = 16;                // rows of a group at most (the MFMA N tile)
 constexpr int kMaxRows = 64;                  // batch rows of one call
 constexpr int kGroups = 8;                    // key slots / arrival counters per row group
 constexpr int kPitch = 2 * 32 * kWaves + 16;  // LDS bytes of a staged row (512 columns + pad)
 constexpr uint64_t kSpinTicks = 100000000;    // 1 s of the 100 MHz realtime clock
-static_assert(kRowGroups * kGroupRows >= kMaxRows, "row groups");
+static_assert(kMaxGroups * kGroupRows >= kMaxRows && kMaxGroups <= kRowGroups, "row groups");
 
 // Synchronisation area, one 64-byte line per word: the arrival counters
 // [kRowGroups][kGroups] (cumulative over steps), then the exit counter.
@@ -154,10 +155,10 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   // Gathered W1 rows per group, in the B-operand order of the matrix
   // instruction: block kk holds at lane l's 16 bytes row l % 16, rank
   // elements 32 kk + 8 (l / 16) .. +7.
-  __shared__ __attribute__((aligned(16))) unsigned char lds_e[kRowGroups][K32 * 1024];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_e[kMaxGroups][K32 * 1024];
   // Staged logits per group: base, then corrected in place.
-  __shared__ __attribute__((aligned(16))) unsigned char lds_x[kRowGroups][kGroupRows * kPitch];
-  __shared__ uint32_t lds_key[kRowGroups][16];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_x[kMaxGroups][kGroupRows * kPitch];
+  __shared__ uint32_t lds_key[kMaxGroups][16];
   // Key slots loaded for a token merge, two buffers of [lane] 16 bytes each,
   // the key in the first 8 (row l % 16, key group 2 (l / 16) + j).
   __shared__ __attribute__((aligned(16))) unsigned char lds_kv[2][2 * 1024];
@@ -175,8 +176,13 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   // The host guarantees B <= 64, V <= 32 * 16 * CUs, B*M*V < 2^30 and
   // M <= 4096, so every index below fits in 32 bits.
   const int B = (int)p.B, M = (int)p.M, V = (int)p.V, r = (int)p.r;
-  const int rpg = (B + kRowGroups - 1) / kRowGroups;  // rows per group (<= kGroupRows)
-  const int U = M * kRowGroups;                        // units
+  // Rows are dealt into NR <= kMaxGroups groups of rpg <= 16.  A step has
+  // kRowGroups slots; slots NR.. are idle windows that give each group's
+  // exchange time to complete (a group's steps are kRowGroups windows apart).
+  const int NR = (B + kGroupRows - 1) / kGroupRows;
+  const int rpg = (B + NR - 1) / NR;
+  const int U = M * kRowGroups;  // windows
+  auto real = [&](int u) __attribute__((always_inline)) { return u % kRowGroups < NR; };
   uint32_t* const sync = p.sync;
 
   // The workgroup's columns [vbeg, vend): slices s_begin .. s_end-1.
@@ -209,12 +215,11 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     }
   }
 
-  // ---- row staging: wave w = 2..13 moves row w - 2 of every group, one
-  // 1 KB row segment per instruction, lane l the 8 columns vbeg + 8 l .. +7.
-  // Offsets of masked-off lanes, rows or steps point past the buffer (see
+  // ---- row staging: wave w moves row w of every group, one 1 KB row
+  // segment per instruction, lane l the 8 columns vbeg + 8 l .. +7.  Offsets
+  // of masked-off lanes, rows or steps point past the buffer (see
   // buffer_rsrc), so every instruction is issued unconditionally.
-  const int srow = wave - 2;
-  const bool stager = srow >= 0 && srow < kGroupRows;
+  const int srow = wave;
   const bool col_ok = vbeg + 8u * (uint32_t)lane < vend;
   const uint32_t lane_off = 2u * (vbeg + 8u * (uint32_t)lane);
   auto row_offset = [&](int gg, int kd) __attribute__((always_inline)) -> uint32_t {
@@ -273,13 +278,12 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   };
 
   // ---- prologue: stage step 0 of every group, gather the first tokens.
-  if (stager) {
-    for (int gg = 0; gg < kRowGroups; ++gg) {
-      load_row(gg, 0);
-      store_row_lds(gg);
-    }
-  } else if (wave == 1) {
-    for (int gg = 0; gg < kRowGroups; ++gg) {
+  for (int gg = 0; gg < NR; ++gg) {
+    load_row(gg, 0);
+    store_row_lds(gg);
+  }
+  if (wave == 1) {
+    for (int gg = 0; gg < NR; ++gg) {
       const int b = gg * rpg + n16;
       int x = -1;
       if (n16 < rpg && b < B) {
@@ -292,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   } else if (wave == 0) {
     if (lane < 16) {
 #pragma unroll
-      for (int gg = 0; gg < kRowGroups; ++gg) lds_key[gg][lane] = 0u;
+      for (int gg = 0; gg < kMaxGroups; ++gg) lds_key[gg][lane] = 0u;
     }
     if (lane == 0) lds_flag = 1;
   }
@@ -308,27 +312,31 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   // earlier units, which overlaps the matrix work of the other waves, then
   // computes unit w = 6k + g (step k of group g); one barrier ends it.
   for (int w = 0; w < U; ++w) {
-    const int gc = w % kRowGroups;  // group of unit w
+    const int gc = w % kRowGroups;  // slot of unit w (its group when real)
     int after_gather = 0;           // wave 1
-    if (stager) {
-      // the base row loaded a window ago (unit w+4, group (w-2) % 6) into
-      // its LDS row; the corrected row of unit w-1 to HBM; then that
-      // group's next base row (unit w+5) into registers
-      if (w >= 2) store_row_lds((w - 2) % kRowGroups);
-      if (w >= 1) {
-        const int gp = (w - 1) % kRowGroups, kp = (w - 1) / kRowGroups;
-        const u32x4_t v = *(const u32x4_t*)&lds_x[gp][srow * kPitch + lane * 16];
-        buffer_store16(rs_out, row_offset(gp, kp), v);
-        load_row(gp, kp + 1);
-      }
-    } else if (wave == 0) {
+
+    // Bulk rows first: the base row loaded a window ago (unit w+4) into its
+    // LDS row, the corrected row of unit w-1 to HBM, then that group's next
+    // base row (unit w+5) into registers.  It drains during the matrix work.
+    if (w >= 2 && real(w - 2)) store_row_lds((w - 2) % kRowGroups);
+    const bool flush = w >= 1 && real(w - 1);
+    if (flush) {
+      const int gp = (w - 1) % kRowGroups, kp = (w - 1) / kRowGroups;
+      const u32x4_t v = *(const u32x4_t*)&lds_x[gp][srow * kPitch + lane * 16];
+      buffer_store16(rs_out, row_offset(gp, kp), v);
+      load_row(gp, kp + 1);
+    }
+
+    if (wave == 0) {
       // count this workgroup in for unit w-2 (its key atomics were issued a
-      // window ago), then publish the row keys of unit w-1
-      wait_vmcnt<0>();
-      if (w >= 2 && lane == 0)
+      // window ago; the two bulk operations just issued may stay in flight),
+      // then publish the row keys of unit w-1
+      if (flush) wait_vmcnt<2>();
+      else wait_vmcnt<0>();
+      if (w >= 2 && real(w - 2) && lane == 0)
         __hip_atomic_fetch_add(arrival_counter(sync, (w - 2) % kRowGroups, xg), 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-      if (w >= 1 && lane < 16) {
+      if (w >= 1 && real(w - 1) && lane < 16) {
         const int gp = (w - 1) % kRowGroups, kp = (w - 1) / kRowGroups;
         const uint32_t kw = lds_key[gp][lane];
         lds_key[gp][lane] = 0u;
@@ -344,31 +352,34 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     } else if (wave == 1) {
       // Targets: unit w+2 (poll issued a window ago; key slots) and unit w+1
       // (key slots loaded a window ago; merge and gather).  The wait below
-      // completes the poll and key slots issued a window ago.
-      const int u2 = w + 2, u1 = w + 1;
-      const bool do2 = ok && u2 < U && u2 >= kRowGroups;
-      const bool do1 = u1 < U && u1 >= kRowGroups;
-      wait_vmcnt<0>();
+      // completes the poll and key slots issued a window ago (the two bulk
+      // operations just issued may stay in flight).
+      const int u2 = w + 2, u1 = w + 1, u3 = w + 3;
+      const bool do2 = ok && u2 < U && u2 >= kRowGroups && real(u2);
+      const bool do1 = u1 < U && u1 >= kRowGroups && real(u1);
+      const bool do3 = u3 < U && u3 >= kRowGroups && real(u3);
+      if (flush) wait_vmcnt<2>();
+      else wait_vmcnt<0>();
+      // the gather first: its round trip has the rest of the window
+      if (do1) gather(u1 % kRowGroups, merge(u1 & 1, u1 % kRowGroups, u1 / kRowGroups - 1));
       if (do2) {
         // complete when every workgroup has counted in unit u2 - kRowGroups
         const uint32_t target = (uint32_t)(u2 / kRowGroups) * (uint32_t)G;
-        uint32_t seen = 0;  // every lane adds the polled counters (broadcast reads)
+        // lane x < kGroups reads counter x; the sum goes through scalar registers
+        const uint32_t cx = lane < kGroups ? *(const uint32_t*)&lds_poll[lane * 16] : 0u;
+        uint32_t seen = 0;
 #pragma unroll
-        for (int x = 0; x < kGroups; ++x) seen += *(const uint32_t*)&lds_poll[x * 16];
-        seen = (uint32_t)__builtin_amdgcn_readfirstlane(seen);
+        for (int x = 0; x < kGroups; ++x) seen += (uint32_t)__builtin_amdgcn_readlane((int)cx, x);
         if (seen < target) ok = wait_arrivals(sync, u2 % kRowGroups, lane, target);
       }
-      if (do1) gather(u1 % kRowGroups, merge(u1 & 1, u1 % kRowGroups, u1 / kRowGroups - 1));
       if (do2 && ok) load_keys(u2 & 1, u2 % kRowGroups, u2 / kRowGroups - 1);
       // poll the arrivals of unit w+3's previous step into LDS (lane
       // l < kGroups loads counter line l)
-      const int u3 = w + 3;
-      const bool do3 = ok && u3 < U && u3 >= kRowGroups;
-      if (do3)
+      if (do3 && ok)
         load_lds16_coherent(bw_sync, lane < kGroups ? (uint32_t)(4 * 16 * ((u3 % kRowGroups) * kGroups + lane)) : kBufferOob,
                             lds_address(&lds_poll[0]));
       // operations issued after the gather (waited for before the barrier)
-      after_gather = (do2 && ok ? 2 : 0) + (do3 ? 1 : 0);
+      after_gather = (do2 && ok ? 2 : 0) + (do3 && ok ? 1 : 0);
       if (!ok && lane == 0) {
         atomicAdd(p.sync_failures, 1u);
         lds_flag = 0;
@@ -377,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
 
     // -- unit w: bias of the wave's slice for the group's rows, added to the
     // staged base logits in place; each row's best column into lds_key.
-    if (has) {
+    if (has && real(w)) {
       f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{};
       const unsigned char* eb = &lds_e[gc][lane * 16];
 #pragma unroll
@@ -432,10 +443,14 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     // wave 1: the gather of unit w+1 (issued this window, before the key
     // slots and the poll) is in LDS before the barrier
     if (wave == 1) {
-      if (after_gather == 3) wait_vmcnt<3>();
-      else if (after_gather == 2) wait_vmcnt<2>();
-      else if (after_gather == 1) wait_vmcnt<1>();
-      else wait_vmcnt<0>();
+      switch (after_gather) {
+        case 5: wait_vmcnt<5>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case 3: wait_vmcnt<3>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 1: wait_vmcnt<1>(); break;
+        default: wait_vmcnt<0>(); break;
+      }
     }
     lds_barrier();
     if (!lds_flag) break;
@@ -443,31 +458,34 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   // after the last window: corrected rows of the last unit, the keys of the
   // last unit, and the last two arrivals
   if (lds_flag) {
-    if (stager) {
+    if (real(U - 1)) {
       const int gp = (U - 1) % kRowGroups, kp = (U - 1) / kRowGroups;
       const u32x4_t v = *(const u32x4_t*)&lds_x[gp][srow * kPitch + lane * 16];
       buffer_store16(rs_out, row_offset(gp, kp), v);
-    } else if (wave == 0) {
+    }
+    if (wave == 0) {
       wait_vmcnt<0>();
-      if (lane == 0 && U >= 2)
+      if (lane == 0 && U >= 2 && real(U - 2))
         __hip_atomic_fetch_add(arrival_counter(sync, (U - 2) % kRowGroups, xg), 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-      if (lane < 16) {
-        const int gp = (U - 1) % kRowGroups, kp = (U - 1) / kRowGroups;
-        const uint32_t kw = lds_key[gp][lane];
-        const int b = gp * rpg + lane;
-        if (kw != 0u && lane < rpg && b < B) {
-          const uint64_t code = kw >> 16;
-          const uint32_t col = vbeg + (0xFFFFu - (kw & 0xFFFFu));
-          __hip_atomic_fetch_max((uint64_t*)((unsigned char*)p.keys + key_offset(kp, xg, b)),
-                                 (code << 32) | (uint64_t)(0xFFFFFFFFu - col), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+      if (real(U - 1)) {
+        if (lane < 16) {
+          const int gp = (U - 1) % kRowGroups, kp = (U - 1) / kRowGroups;
+          const uint32_t kw = lds_key[gp][lane];
+          const int b = gp * rpg + lane;
+          if (kw != 0u && lane < rpg && b < B) {
+            const uint64_t code = kw >> 16;
+            const uint32_t col = vbeg + (0xFFFFu - (kw & 0xFFFFu));
+            __hip_atomic_fetch_max((uint64_t*)((unsigned char*)p.keys + key_offset(kp, xg, b)),
+                                   (code << 32) | (uint64_t)(0xFFFFFFFFu - col), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
+        wait_vmcnt<0>();
+        if (lane == 0)
+          __hip_atomic_fetch_add(arrival_counter(sync, (U - 1) % kRowGroups, xg), 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
       }
-      wait_vmcnt<0>();
-      if (lane == 0)
-        __hip_atomic_fetch_add(arrival_counter(sync, (U - 1) % kRowGroups, xg), 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (wave < 2) __builtin_amdgcn_s_setprio(0);
@@ -477,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   if (g == 0 && wave == 1 && lds_flag) {
     const uint32_t target = (uint32_t)M * (uint32_t)G;
     bool fin = true;
-    for (int gg = 0; gg < kRowGroups; ++gg) {
+    for (int gg = 0; gg < NR; ++gg) {
       fin = fin && wait_arrivals(sync, gg, lane, target);
       const int b = gg * rpg + n16;
       const bool row_ok = n16 < rpg && b < B;
