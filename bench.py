@@ -26,14 +26,25 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 WORKLOAD = "greedy_draft_64x5"
 DOMINANT_KERNEL = "markov_chain_greedy_bf16"   # the whole sample call is this one launch
-KERNEL_SOURCE = os.path.join(ROOT, "rank_markov_draft_amd", "csrc", "markov_chain.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "rank_markov_draft_amd", "csrc", name)
+                  for name in ("markov_chain.hip", "device_common.h", "markov_kernels.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def source_hash(path: str) -> str:
+def source_hash(paths) -> str:
+    """Hash of the code of the dominant kernel's sources with comments and
+    whitespace removed, so that documentation edits keep the counters valid
+    while any code change invalidates them."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    import re
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "r", encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
@@ -44,7 +55,7 @@ def measured_traffic():
         return None
     with open(TRAFFIC_FILE) as f:
         t = _json.load(f)
-    if t.get("kernel_source_sha256_16") != source_hash(KERNEL_SOURCE):
+    if t.get("kernel_source_sha256_16") != source_hash(KERNEL_SOURCES):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -83,7 +94,7 @@ def write_traffic(fetch_csv: str, write_csv: str) -> dict:
                         "copy_kib_per_dispatch": sum(copies) / len(copies), "scale": scale,
                         "bytes_per_launch": sum(kern) / len(kern) * 1024.0 * scale}
     t = {"kernel": DOMINANT_KERNEL, "workload": WORKLOAD,
-         "kernel_source_sha256_16": source_hash(KERNEL_SOURCE),
+         "kernel_source_sha256_16": source_hash(KERNEL_SOURCES),
          "hbm_read_bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"],
          "hbm_write_bytes_per_launch": out["WRITE_SIZE"]["bytes_per_launch"],
          "hbm_bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"],

@@ -10,11 +10,12 @@
 //   * the vocabulary is cut into 32-column slices; each wave owns at most one
 //     slice and keeps its W2w rows in VGPRs for all M steps, so W2 is read
 //     from HBM once per call;
-//   * the batch rows are independent chains.  They are dealt into six row
-//     groups of up to 12, and the workgroup works through units u = 6k + g
-//     (step k of group g) one per window.  A group's next step needs the
-//     tokens of its current one from every workgroup, so each device-wide
-//     exchange has five windows of other work to hide in;
+//   * the batch rows are independent chains.  They are dealt into at most
+//     four row groups of up to 16 (the MFMA N tile), and the workgroup works
+//     through units u = 6k + g (step k of the group in slot g) one per
+//     window; slots g >= the number of groups are idle windows.  A group's
+//     next step needs the tokens of its current one from every workgroup, so
+//     each device-wide exchange has five windows of other work to hide in;
 //   * window w: every wave multiplies group g's gathered W1 rows by its
 //     slice on the matrix cores (v_mfma_f32_16x16x32_bf16), rounds the bias
 //     to bf16, adds it to the group's base logits staged in LDS, writes the
