@@ -45,6 +45,49 @@ __device__ __forceinline__ uint64_t buffer_load8_coherent(__amdgpu_buffer_rsrc_t
   return ((uint64_t)v.y << 32) | v.x;
 }
 
+// ---------------------------------------------------------------- waits and loads to LDS
+// s_waitcnt on the vector memory counter only (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS data only.  __syncthreads() also orders global
+// memory at workgroup scope, which would wait for every load in flight.
+// Here each wave finishes its own LDS accesses (lgkmcnt); the buffer loads
+// to LDS are waited for explicitly, by count, where their data is needed.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Buffer load of 16 bytes per lane straight into LDS: lane l's bytes land at
+// LDS address lds + 16 l (lds must be uniform over the wave).  Written as
+// inline assembly so that the compiler does not track these loads: it would
+// otherwise make later LDS reads of every wave wait for all of them.  Their
+// completion is waited for explicitly (wait_vmcnt) before the data is used.
+// M0 is saved and restored around the load.
+struct BufferWords {
+  u32x4_t w;  // V# of a raw buffer: base, stride 0, size in bytes, 32-bit data format
+};
+__device__ __forceinline__ BufferWords buffer_words(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  return BufferWords{u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u}};
+}
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+__device__ __forceinline__ void load_lds16(const BufferWords& r, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  __asm__ volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0"
+                   : "=&s"(saved) : "v"(off), "s"(r.w), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void load_lds16_coherent(const BufferWords& r, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  __asm__ volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %1, %2, 0 offen sc1 lds\n\ts_mov_b32 m0, %0"
+                   : "=&s"(saved) : "v"(off), "s"(r.w), "s"(lds) : "memory");
+}
+
 // ---------------------------------------------------------------- bf16
 // A bf16 value is the upper half of a binary32 value.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -143,6 +186,19 @@ __device__ __forceinline__ uint32_t wave_min_u32_to_lane63(uint32_t v) {
   v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(big, (int)v, 0x118, 0xF, 0xF, false));
   v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(big, (int)v, 0x142, 0xA, 0xF, false));
   v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(big, (int)v, 0x143, 0xC, 0xF, false));
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: row shifts by
+// 1, 2, 4 and 8 within each row of 16 lanes, then the broadcasts of lane 15
+// (into rows 1 and 3) and lane 31 (into rows 2 and 3).
+__device__ __forceinline__ uint32_t wave_inclusive_sum_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return v;
 }
 

@@ -169,7 +169,13 @@ dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_
   if (!tile && r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
   p.sink = (char*)workspace + kControlBytes;
   if (tile) {
-    e = dspark::launch_apply_wide(p, (hipStream_t)stream);
+    // grouped form (one bias per distinct predecessor) when the plan fits
+    // in LDS, else the streaming form, else the tile kernel
+    e = dspark::launch_apply_grouped(p, (hipStream_t)stream);
+    if (e == hipErrorNotSupported) {
+      (void)hipGetLastError();
+      e = dspark::launch_apply_wide(p, (hipStream_t)stream);
+    }
     if (e == hipErrorNotSupported) {  // element offsets beyond 31 bits
       (void)hipGetLastError();
       e = dspark::launch_tile(p, (hipStream_t)stream);

@@ -68,13 +68,6 @@ __device__ __forceinline__ uint32_t key_offset(int k, int x, int b) {
   return (uint32_t)(((k * kGroups + x) * kMaxRows + b) * kKeyPad * 8);
 }
 
-// s_waitcnt on the vector memory counter only (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Order code of a bf16 value for argmax (16 bits, larger = later in the
 // order): every NaN ranks highest (torch.argmax reports a NaN), -0 and +0
 // share one code, otherwise the IEEE order.
@@ -84,41 +77,6 @@ __device__ __forceinline__ uint32_t argmax_code_bf16(uint32_t h) {
   c = (mag == 0u) ? 0x8000u : c;
   c = (mag > 0x7F80u) ? 0xFFFFu : c;
   return c;
-}
-
-// Workgroup barrier for LDS data only.  __syncthreads() also orders global
-// memory at workgroup scope, which would wait for every load in flight.
-// Here each wave finishes its own LDS accesses (lgkmcnt); the buffer loads
-// to LDS are waited for explicitly, by count, where their data is needed.
-__device__ __forceinline__ void lds_barrier() {
-  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Buffer load of 16 bytes per lane straight into LDS: lane l's bytes land at
-// LDS address lds + 16 l (lds must be uniform over the wave).  Written as
-// inline assembly so that the compiler does not track these loads: it would
-// otherwise make later LDS reads of every wave wait for all of them.  Their
-// completion is waited for explicitly (wait_vmcnt) before the data is used.
-// M0 is saved and restored around the load.
-struct BufferWords {
-  u32x4_t w;  // V# of a raw buffer: base, stride 0, size in bytes, 32-bit data format
-};
-__device__ __forceinline__ BufferWords buffer_words(const void* p, uint32_t bytes) {
-  const uint64_t a = (uint64_t)p;
-  return BufferWords{u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u}};
-}
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
-}
-__device__ __forceinline__ void load_lds16(const BufferWords& r, uint32_t off, uint32_t lds) {
-  uint32_t saved;
-  __asm__ volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0"
-                   : "=&s"(saved) : "v"(off), "s"(r.w), "s"(lds) : "memory");
-}
-__device__ __forceinline__ void load_lds16_coherent(const BufferWords& r, uint32_t off, uint32_t lds) {
-  uint32_t saved;
-  __asm__ volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %1, %2, 0 offen sc1 lds\n\ts_mov_b32 m0, %0"
-                   : "=&s"(saved) : "v"(off), "s"(r.w), "s"(lds) : "memory");
 }
 
 // Arrival counters of row group rg: lanes 0..kGroups-1 load one each

@@ -75,6 +75,9 @@ hipError_t launch_tile(const KernelParams& p, hipStream_t s);
 // apply_sink_bytes() bytes.
 hipError_t launch_apply_wide(const KernelParams& p, hipStream_t s);
 size_t apply_sink_bytes();
+// Grouped teacher-forced apply (bf16): each distinct predecessor's bias is
+// computed once; needs 1024 <= rows <= 4096 and rows * V * 2, V * r * 2 <= 2^31.
+hipError_t launch_apply_grouped(const KernelParams& p, hipStream_t s);
 hipError_t launch_generic(const KernelParams& p, bool logits_bf16, bool weights_bf16, hipStream_t s);
 hipError_t launch_reduce(const uint64_t* partials, int64_t nparts, int64_t B, int64_t M, int64_t k,
                          int64_t* tokens, hipStream_t s);

@@ -159,6 +159,50 @@ def test_apply_shapes(native, B, M, V, r, dtype):
     check_apply(inp, run_apply(inp), name=f"apply B{B} M{M} V{V} r{r} dt{dtype}")
 
 
+def _grouped_ids(kind, rng, n, V):
+    if kind == "zipf":
+        return wl.zipf_ids(rng, n, V, 1.1)
+    if kind == "same":
+        return np.full(n, V // 3, dtype=np.int64)
+    if kind == "distinct":
+        return rng.permutation(V)[:n].astype(np.int64)
+    if kind == "bad-mix":                       # Zipf ids, one in eight out of range
+        ids = wl.zipf_ids(rng, n, V, 1.1)
+        bad = rng.random(n) < 0.125
+        ids[bad] = np.where(rng.random(bad.sum()) < 0.5, -1, V + 5)
+        return ids
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("B,M,V,r,kind", [
+    (64, 64, 1024, 64, "zipf"),        # 4096 rows: the largest grouped call
+    (17, 241, 512, 32, "zipf"),        # 4097 rows: the row-order kernel instead
+    (31, 33, 700, 16, "zipf"),         # 1023 rows: the row-order kernel instead
+    (32, 33, 1000, 24, "same"),        # 1056 rows, one distinct token, rank padded to 32
+    (2, 512, 4104, 40, "distinct"),    # 1024 rows: every chunk of 32 rows adds two tiles
+    (5, 205, 2048, 512, "bad-mix"),    # rank 512, ids outside [0, V)
+    (1024, 1, 8, 8, "zipf"),           # one 8-column slice
+    (9, 115, 3000, 256, "zipf"),       # rank 256, ragged last chunk and vocabulary slice
+])
+def test_apply_repeated_predecessors(native, B, M, V, r, kind):
+    """Batches whose rows share predecessors (one bias per distinct token)."""
+    w = wl.WORKLOADS["teacher_forced_2560_zipf"]
+    inp = wl.make_inputs(w, B=B, M=M, V=V, r=r, seed=B * 7 + V)
+    rng = np.random.default_rng(B + M + V)
+    ids = _grouped_ids(kind, rng, B * M, V).reshape(B, M)
+    inp = dict(inp, token_ids=ids)
+    d = device_inputs({k: inp[k] for k in ("base", "token_ids", "w1", "w2")})
+    ws = rmd.Workspace(B, M, V, r, sample=False)
+    out = from_dev(rmd.apply_block_logits(d["base"], d["token_ids"], d["w1"], d["w2"], workspace=ws))
+    flat = ids.reshape(-1)
+    bad = (flat < 0) | (flat >= V)
+    assert rmd.read_device_error(ws) == int(bad.sum())
+    flat_out = out.reshape(B * M, V)
+    assert np.array_equal(flat_out[bad], inp["base"].reshape(B * M, V)[bad])
+    good = np.nonzero(~bad)[0]
+    check_apply(inp, out, rows=good, name=f"apply {kind} B{B} M{M} V{V} r{r}")
+
+
 @pytest.mark.parametrize("T", [0.0, 0.8])
 @pytest.mark.parametrize("B,M,V,r,dtype", [
     (3, 4, 1000, 24, wl.BF16),
