@@ -202,6 +202,26 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum_u32(uint32_t v) {
   return v;
 }
 
+// Unsigned 64-bit max over the 64 lanes of a wave with DPP moves of both
+// halves (row shifts, then the row broadcasts); the result is valid in
+// lane 63.  Lanes without a source see 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_u64_step(uint64_t k) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, ROW_MASK, 0xF, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > k ? o : k;
+}
+__device__ __forceinline__ uint64_t wave_max_u64_lane63(uint64_t k) {
+  k = dpp_max_u64_step<0x111, 0xF>(k);  // row_shr:1
+  k = dpp_max_u64_step<0x112, 0xF>(k);  // row_shr:2
+  k = dpp_max_u64_step<0x114, 0xF>(k);  // row_shr:4
+  k = dpp_max_u64_step<0x118, 0xF>(k);  // row_shr:8
+  k = dpp_max_u64_step<0x142, 0xA>(k);  // row_bcast:15
+  k = dpp_max_u64_step<0x143, 0xC>(k);  // row_bcast:31
+  return k;
+}
+
 // Order codes of the two bf16 values of a word, one per half: sign set ->
 // all bits flipped, else the sign bit set (packed 16-bit shift, then one
 // and-or and one xor for both halves).  -0 sorts just below +0 and NaNs sit
@@ -309,8 +329,9 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     }
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     const uint64_t p2 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(p2 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    // three-way xors in one v_bitop3_b32 each (truth table 0x96)
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p2 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     c1 = (uint32_t)p2;
     c3 = (uint32_t)p0;
     c0 = n0;

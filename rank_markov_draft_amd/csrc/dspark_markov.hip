@@ -270,9 +270,19 @@ dspark_status_t dspark_markov_sample_block(const void* base_logits, dspark_dtype
   for (int64_t k = 0; k < M; ++k) {
     p.k = k;
     p.k_abs = (uint32_t)(position_offset + k);
-    hipError_t e = tile ? dspark::launch_tile(p, s)
-                        : dspark::launch_generic(p, logits_dtype == DSPARK_BF16,
-                                                 weight_dtype == DSPARK_BF16, s);
+    hipError_t e;
+    if (tile) {
+      // the persistent step kernel where the shape fits, else the tile kernel
+      p.nparts = dspark::sample_step_parts(V);
+      e = dspark::launch_sample_step(p, cus, s);
+      if (e == hipErrorNotSupported) {
+        (void)hipGetLastError();
+        p.nparts = vocab_slices(V);
+        e = dspark::launch_tile(p, s);
+      }
+    } else {
+      e = dspark::launch_generic(p, logits_dtype == DSPARK_BF16, weight_dtype == DSPARK_BF16, s);
+    }
     if (e != hipSuccess) return device_failure(e, "sample step launch");
     e = dspark::launch_reduce(p.partials, p.nparts, B, M, k, sampled_tokens, s);
     if (e != hipSuccess) return device_failure(e, "sample reduce launch");

@@ -78,6 +78,12 @@ size_t apply_sink_bytes();
 // Grouped teacher-forced apply (bf16): each distinct predecessor's bias is
 // computed once; needs 1024 <= rows <= 4096 and rows * V * 2, V * r * 2 <= 2^31.
 hipError_t launch_apply_grouped(const KernelParams& p, hipStream_t s);
+// One bf16 sampling step (greedy or temperature) of the p.rows = B rows at
+// position p.k: argmax keys per (row, 512-column block) into p.partials with
+// p.nparts = sample_step_parts(V); one workgroup per CU.  Needs r <= 256,
+// B <= 4096 and B * M * V * 2, V * r * 2 <= 2^31 (hipErrorNotSupported).
+int64_t sample_step_parts(int64_t V);
+hipError_t launch_sample_step(const KernelParams& p, int num_cus, hipStream_t s);
 hipError_t launch_generic(const KernelParams& p, bool logits_bf16, bool weights_bf16, hipStream_t s);
 hipError_t launch_reduce(const uint64_t* partials, int64_t nparts, int64_t B, int64_t M, int64_t k,
                          int64_t* tokens, hipStream_t s);

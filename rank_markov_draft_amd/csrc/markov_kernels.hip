@@ -38,23 +38,6 @@ __device__ __forceinline__ int64_t base_row_offset(const KernelParams& p, int64_
   return (p.mode == MODE_APPLY ? n : n * p.M + p.k) * p.V;
 }
 
-// Noise for 8 consecutive vocabulary entries v0..v0+7 (v0 % 8 == 0) of row
-// (b_abs, k_abs): words (v & 3) of the Philox blocks v0/4 and v0/4 + 1.
-__device__ __forceinline__ void gumbel8(const KernelParams& p, int64_t b_abs, int64_t v0,
-                                        float g[8]) {
-  const uint32_t cb = (uint32_t)((uint64_t)v0 >> 2);
-  const Philox4 q0 = philox4x32_10(cb, p.k_abs, (uint32_t)b_abs, 0u, p.seed_lo, p.seed_hi);
-  const Philox4 q1 = philox4x32_10(cb + 1u, p.k_abs, (uint32_t)b_abs, 0u, p.seed_lo, p.seed_hi);
-  g[0] = gumbel2_from_word(q0.x0);
-  g[1] = gumbel2_from_word(q0.x1);
-  g[2] = gumbel2_from_word(q0.x2);
-  g[3] = gumbel2_from_word(q0.x3);
-  g[4] = gumbel2_from_word(q1.x0);
-  g[5] = gumbel2_from_word(q1.x1);
-  g[6] = gumbel2_from_word(q1.x2);
-  g[7] = gumbel2_from_word(q1.x3);
-}
-
 // ---------------------------------------------------------------- tile kernel
 // KS = rank / 16 rounded up to an instantiated value; rank entries past r are
 // zero on both operands.
@@ -181,23 +164,46 @@ __global__ __launch_bounds__(256) void markov_tile_bf16(KernelParams p) {
       if (ok && out != nullptr)
         __builtin_nontemporal_store(o, (u32x4_t*)(out + base_row_offset(p, n) + v0 + ec));
       if constexpr (MODE != MODE_APPLY) {
-        // Selection runs on the L-typed corrected values.
-        float cv[8] = {bf16_lo(o.x), bf16_hi(o.x), bf16_lo(o.y), bf16_hi(o.y),
-                       bf16_lo(o.z), bf16_hi(o.z), bf16_lo(o.w), bf16_hi(o.w)};
-        uint64_t key = 0;
-        if (ok) {
-          const int64_t vv = v0 + ec;
+        // Selection runs on the L-typed corrected values: the thread's best
+        // score (first column on ties) in fp32, one key per thread.
+        const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+        const uint32_t vv = (uint32_t)(v0 + ec);
+        float best = 0.0f, sumc = 0.0f;
+        uint32_t bi = 0;
+        // four columns per Philox block (words 0..3 = columns vv + 4 j ..)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float sc[4] = {bf16_lo(ow[2 * j]), bf16_hi(ow[2 * j]), bf16_lo(ow[2 * j + 1]), bf16_hi(ow[2 * j + 1])};
+          sumc += (sc[0] + sc[1]) + (sc[2] + sc[3]);
           if constexpr (MODE == MODE_TEMPERATURE) {
-            float g[8];
-            gumbel8(p, p.batch_offset + n, vv, g);
+            const Philox4 q4 = philox4x32_10((vv >> 2) + (uint32_t)j, p.k_abs, (uint32_t)(p.batch_offset + n), 0u,
+                                             p.seed_lo, p.seed_hi);
+            sc[0] = __builtin_fmaf(sc[0], p.kappa, gumbel2_from_word(q4.x0));
+            sc[1] = __builtin_fmaf(sc[1], p.kappa, gumbel2_from_word(q4.x1));
+            sc[2] = __builtin_fmaf(sc[2], p.kappa, gumbel2_from_word(q4.x2));
+            sc[3] = __builtin_fmaf(sc[3], p.kappa, gumbel2_from_word(q4.x3));
+          }
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-              key = max_u64(key, argmax_key(__builtin_fmaf(cv[i], p.kappa, g[i]), (uint32_t)(vv + i)));
-          } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) key = max_u64(key, argmax_key(cv[i], (uint32_t)(vv + i)));
+          for (int i = 0; i < 4; ++i) {
+            const bool gt = (j == 0 && i == 0) || sc[i] > best;
+            best = gt ? sc[i] : best;
+            bi = gt ? (uint32_t)(4 * j + i) : bi;
           }
         }
+        uint64_t key = argmax_key(best, vv + bi);
+        if (sumc != sumc) {
+          // A score is NaN exactly when its corrected value is (the noise is
+          // finite): the first NaN wins, as a NaN's key ranks above all.
+          // Without one (+inf met -inf in the sum) the scan above stands.
+          uint32_t first = 8;
+#pragma unroll
+          for (int i = 7; i >= 0; --i) {
+            const uint32_t hb = (i & 1) ? (ow[i >> 1] >> 16) : (ow[i >> 1] & 0xFFFFu);
+            if ((hb & 0x7FFFu) > 0x7F80u) first = (uint32_t)i;
+          }
+          if (first < 8) key = (0xFFFFFFFFull << 32) | (uint64_t)(0xFFFFFFFFu - (vv + first));
+        }
+        key = ok ? key : 0ull;
         key = group_max_u64<16>(key);
         if ((tid & 15) == 0 && n < rows) p.partials[n * p.nparts + blockIdx.x] = key;
       }
