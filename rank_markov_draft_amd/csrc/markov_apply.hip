@@ -243,11 +243,14 @@ __global__ __launch_bounds__(WAVES * 64) void markov_apply_wide_bf16(KernelParam
 constexpr int kGroupedMaxRows = 4096;   // rows of one call (plan arrays in LDS)
 constexpr int kGroupedHash = 8192;      // hash slots (load factor <= 1/2)
 // Below this many rows the plan costs more than the repeats save (measured
-// at V = 129280: 320 rows with distinct ids run faster in the row-order
-// streaming kernel), and the row-order kernel takes the call.
+// at V = 129280 with 320 rows of distinct ids), and the rows keep their
+// own order.
 constexpr int kGroupedMinRows = 1024;
 
-template <int K32, int WAVES, int D, int KB>
+// DEDUP: plan with the hash table (one bias per distinct token); without
+// it every row is its own token id (rows in their own order), which costs
+// nothing to plan and suits batches with few repeats.
+template <int K32, int WAVES, int D, int KB, bool DEDUP>
 __global__ __launch_bounds__(WAVES * 64) void markov_apply_grouped_bf16(KernelParams p) {
   constexpr int THREADS = WAVES * 64;
   constexpr int RC = 32;                       // sorted rows per chunk
@@ -320,125 +323,145 @@ __global__ __launch_bounds__(WAVES * 64) void markov_apply_grouped_bf16(KernelPa
   };
   load_w2(0);
 
-  // ---- plan.  Invalid ids (outside [0, V)) become the key V, one more
-  // group with a zero bias.
-  uint32_t* const htab = (uint32_t*)lds_u;                                  // [kGroupedHash] key or ~0
-  uint16_t* const huid = (uint16_t*)(lds_u + kGroupedHash * 4);             // [kGroupedHash] u of a slot
-  uint32_t* const cnt = (uint32_t*)(lds_u + kGroupedHash * 6);              // [kGroupedMaxRows] rows of u
-  for (int i = tid; i < kGroupedHash; i += THREADS) htab[i] = 0xFFFFFFFFu;
-  for (int i = tid; i < kGroupedMaxRows; i += THREADS) cnt[i] = 0u;
-  lds_barrier();
-  load_w2(1);
-  uint32_t bad = 0;
-  uint32_t key[IPT], slot[IPT];
+  if constexpr (DEDUP) {
+    // ---- plan.  Invalid ids (outside [0, V)) become the key V, one more
+    // group with a zero bias.
+    uint32_t* const htab = (uint32_t*)lds_u;                                  // [kGroupedHash] key or ~0
+    uint16_t* const huid = (uint16_t*)(lds_u + kGroupedHash * 4);             // [kGroupedHash] u of a slot
+    uint32_t* const cnt = (uint32_t*)(lds_u + kGroupedHash * 6);              // [kGroupedMaxRows] rows of u
+    for (int i = tid; i < kGroupedHash; i += THREADS) htab[i] = 0xFFFFFFFFu;
+    for (int i = tid; i < kGroupedMaxRows; i += THREADS) cnt[i] = 0u;
+    lds_barrier();
+    load_w2(1);
+    uint32_t bad = 0;
+    uint32_t key[IPT], slot[IPT];
 #pragma unroll
-  for (int k = 0; k < IPT; ++k) {
-    const int i = tid + k * THREADS;
-    const bool ok = idv[k] >= 0 && idv[k] < (int64_t)V;
-    key[k] = ok ? (uint32_t)idv[k] : V;
-    if (i < rows) {
-      bad += ok ? 0u : 1u;
-      uint32_t s = (key[k] * 0x9E3779B1u) >> (32 - 13);
-      // at most rows < kGroupedHash keys: an empty slot always exists
-      for (int probe = 0; probe < kGroupedHash; ++probe) {
-        const uint32_t old = atomicCAS(&htab[s], 0xFFFFFFFFu, key[k]);
-        if (old == 0xFFFFFFFFu || old == key[k]) break;
-        s = (s + 1) & (kGroupedHash - 1);
+    for (int k = 0; k < IPT; ++k) {
+      const int i = tid + k * THREADS;
+      const bool ok = idv[k] >= 0 && idv[k] < (int64_t)V;
+      key[k] = ok ? (uint32_t)idv[k] : V;
+      if (i < rows) {
+        bad += ok ? 0u : 1u;
+        uint32_t s = (key[k] * 0x9E3779B1u) >> (32 - 13);
+        // at most rows < kGroupedHash keys: an empty slot always exists
+        for (int probe = 0; probe < kGroupedHash; ++probe) {
+          const uint32_t old = atomicCAS(&htab[s], 0xFFFFFFFFu, key[k]);
+          if (old == 0xFFFFFFFFu || old == key[k]) break;
+          s = (s + 1) & (kGroupedHash - 1);
+        }
+        slot[k] = s;
       }
-      slot[k] = s;
     }
-  }
-  if (blockIdx.x == 0 && bad) atomicAdd(p.bad_rows, bad);
-  lds_barrier();
-  load_w2(2);
-  // Dense ids u in slot order.  Wave w owns slots [w SPW, (w + 1) SPW),
-  // read 64 consecutive slots at a time (no bank conflicts); the ballot of
-  // the occupied ones ranks them.
-  constexpr int SPW = kGroupedHash / WAVES;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes under this one
-  {
-    uint32_t cw = 0;
+    if (blockIdx.x == 0 && bad) atomicAdd(p.bad_rows, bad);
+    lds_barrier();
+    load_w2(2);
+    // Dense ids u in slot order.  Wave w owns slots [w SPW, (w + 1) SPW),
+    // read 64 consecutive slots at a time (no bank conflicts); the ballot of
+    // the occupied ones ranks them.
+    constexpr int SPW = kGroupedHash / WAVES;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes under this one
+    {
+      uint32_t cw = 0;
 #pragma unroll
-    for (int j = 0; j < SPW / 64; ++j)
-      cw += (uint32_t)__builtin_popcountll(__ballot(htab[wave * SPW + j * 64 + lane] != 0xFFFFFFFFu));
-    if (lane == 0) lds_part[wave] = cw;
-  }
-  lds_barrier();
-  load_w2(3);
-  uint32_t U = 0, run = 0;
-  for (int w = 0; w < WAVES; ++w) {
-    const uint32_t pw = lds_part[w];
-    run += w < wave ? pw : 0u;
-    U += pw;
-  }
-  U = __builtin_amdgcn_readfirstlane(U);
-  uint32_t hk[SPW / 64];
-#pragma unroll
-  for (int j = 0; j < SPW / 64; ++j) hk[j] = htab[wave * SPW + j * 64 + lane];
-#pragma unroll
-  for (int j = 0; j < SPW / 64; ++j) {
-    const int sl = wave * SPW + j * 64 + lane;
-    const uint32_t kk = hk[j];
-    const uint64_t m = __ballot(kk != 0xFFFFFFFFu);
-    if (kk != 0xFFFFFFFFu) {
-      const uint32_t u = run + (uint32_t)__builtin_popcountll(m & below);
-      huid[sl] = (uint16_t)u;
-      plan_tok[u] = kk < V ? (int32_t)kk : -1;
+      for (int j = 0; j < SPW / 64; ++j)
+        cw += (uint32_t)__builtin_popcountll(__ballot(htab[wave * SPW + j * 64 + lane] != 0xFFFFFFFFu));
+      if (lane == 0) lds_part[wave] = cw;
     }
-    run += (uint32_t)__builtin_popcountll(m);
-  }
-  if (tid < 16) plan_tok[U + tid] = -1;  // the last tile's padding
-  lds_barrier();
-  load_w2(4);
-  // counting sort of the rows by u
-  uint32_t ru[IPT];
-#pragma unroll
-  for (int k = 0; k < IPT; ++k) {
-    const int i = tid + k * THREADS;
-    if (i < rows) {
-      ru[k] = huid[slot[k]];
-      atomicAdd(&cnt[ru[k]], 1u);
+    lds_barrier();
+    load_w2(3);
+    uint32_t U = 0, run = 0;
+    for (int w = 0; w < WAVES; ++w) {
+      const uint32_t pw = lds_part[w];
+      run += w < wave ? pw : 0u;
+      U += pw;
     }
-  }
-  lds_barrier();
-  load_w2(5);
-  // exclusive scan of cnt[0 .. kGroupedMaxRows) in place, wave w owning
-  // [w CPW, (w + 1) CPW) in runs of 64
-  constexpr int CPW = kGroupedMaxRows / WAVES;
-  {
-    uint32_t tot = 0;
+    U = __builtin_amdgcn_readfirstlane(U);
+    uint32_t hk[SPW / 64];
 #pragma unroll
-    for (int j = 0; j < CPW / 64; ++j) tot += cnt[wave * CPW + j * 64 + lane];
-    tot = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_sum_u32(tot), 63);
-    if (lane == 0) lds_part2[wave] = tot;
-  }
-  lds_barrier();
-  load_w2(6);
-  {
-    uint32_t base = 0;
-    for (int w = 0; w < wave; ++w) base += lds_part2[w];
-    uint32_t v[CPW / 64];
+    for (int j = 0; j < SPW / 64; ++j) hk[j] = htab[wave * SPW + j * 64 + lane];
 #pragma unroll
-    for (int j = 0; j < CPW / 64; ++j) v[j] = cnt[wave * CPW + j * 64 + lane];
-#pragma unroll
-    for (int j = 0; j < CPW / 64; ++j) {
-      const uint32_t incl = wave_inclusive_sum_u32(v[j]);
-      cnt[wave * CPW + j * 64 + lane] = base + incl - v[j];
-      base += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    for (int j = 0; j < SPW / 64; ++j) {
+      const int sl = wave * SPW + j * 64 + lane;
+      const uint32_t kk = hk[j];
+      const uint64_t m = __ballot(kk != 0xFFFFFFFFu);
+      if (kk != 0xFFFFFFFFu) {
+        const uint32_t u = run + (uint32_t)__builtin_popcountll(m & below);
+        huid[sl] = (uint16_t)u;
+        plan_tok[u] = kk < V ? (int32_t)kk : -1;
+      }
+      run += (uint32_t)__builtin_popcountll(m);
     }
-  }
-  lds_barrier();
-  load_w2(7);
+    if (tid < 16) plan_tok[U + tid] = -1;  // the last tile's padding
+    lds_barrier();
+    load_w2(4);
+    // counting sort of the rows by u
+    uint32_t ru[IPT];
 #pragma unroll
-  for (int k = 0; k < IPT; ++k) {
-    const int i = tid + k * THREADS;
-    if (i < rows) {
-      const uint32_t pos = atomicAdd(&cnt[ru[k]], 1u);
-      plan_row[pos] = (uint16_t)i;
-      plan_uid[pos] = (uint16_t)ru[k];
+    for (int k = 0; k < IPT; ++k) {
+      const int i = tid + k * THREADS;
+      if (i < rows) {
+        ru[k] = huid[slot[k]];
+        atomicAdd(&cnt[ru[k]], 1u);
+      }
     }
+    lds_barrier();
+    load_w2(5);
+    // exclusive scan of cnt[0 .. kGroupedMaxRows) in place, wave w owning
+    // [w CPW, (w + 1) CPW) in runs of 64
+    constexpr int CPW = kGroupedMaxRows / WAVES;
+    {
+      uint32_t tot = 0;
+#pragma unroll
+      for (int j = 0; j < CPW / 64; ++j) tot += cnt[wave * CPW + j * 64 + lane];
+      tot = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_sum_u32(tot), 63);
+      if (lane == 0) lds_part2[wave] = tot;
+    }
+    lds_barrier();
+    load_w2(6);
+    {
+      uint32_t base = 0;
+      for (int w = 0; w < wave; ++w) base += lds_part2[w];
+      uint32_t v[CPW / 64];
+#pragma unroll
+      for (int j = 0; j < CPW / 64; ++j) v[j] = cnt[wave * CPW + j * 64 + lane];
+#pragma unroll
+      for (int j = 0; j < CPW / 64; ++j) {
+        const uint32_t incl = wave_inclusive_sum_u32(v[j]);
+        cnt[wave * CPW + j * 64 + lane] = base + incl - v[j];
+        base += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      }
+    }
+    lds_barrier();
+    load_w2(7);
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      const int i = tid + k * THREADS;
+      if (i < rows) {
+        const uint32_t pos = atomicAdd(&cnt[ru[k]], 1u);
+        plan_row[pos] = (uint16_t)i;
+        plan_uid[pos] = (uint16_t)ru[k];
+      }
+    }
+    lds_barrier();
+  } else {
+#pragma unroll
+    for (int g = 1; g < 8; ++g) load_w2(g);
+    uint32_t bad = 0;
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      const int i = tid + k * THREADS;
+      if (i < rows) {
+        const bool ok = idv[k] >= 0 && idv[k] < (int64_t)V;
+        bad += ok ? 0u : 1u;
+        plan_row[i] = (uint16_t)i;
+        plan_uid[i] = (uint16_t)i;
+        plan_tok[i] = ok ? (int32_t)idv[k] : -1;
+      }
+    }
+    if (blockIdx.x == 0 && bad) atomicAdd(p.bad_rows, bad);
+    if (tid < 16) plan_tok[rows + tid] = -1;  // the last tile's padding
+    lds_barrier();
   }
-  lds_barrier();
 
   // ---- chunk loop over the sorted rows
   // Gathered tile t (slot t % 4): block kk holds at lane l's 16 bytes the
@@ -588,16 +611,19 @@ template <int K32, int WAVES, int D, int KB>
 hipError_t launch_grouped(const KernelParams& p, hipStream_t s) {
   const int64_t S = (p.V + 31) / 32;
   const dim3 grid((unsigned)((S + WAVES - 1) / WAVES));
-  hipLaunchKernelGGL((markov_apply_grouped_bf16<K32, WAVES, D, KB>), grid, dim3(WAVES * 64), 0, s, p);
+  if (p.rows >= kGroupedMinRows)
+    hipLaunchKernelGGL((markov_apply_grouped_bf16<K32, WAVES, D, KB, true>), grid, dim3(WAVES * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((markov_apply_grouped_bf16<K32, WAVES, D, KB, false>), grid, dim3(WAVES * 64), 0, s, p);
   return hipGetLastError();
 }
 }  // namespace
 
-// Grouped teacher-forced apply (bf16): kGroupedMinRows <= rows <=
-// kGroupedMaxRows, rows * V * 2 and V * r * 2 at most 2^31 bytes;
-// hipErrorNotSupported otherwise.
+// Grouped teacher-forced apply (bf16): 1 <= rows <= kGroupedMaxRows (the
+// plan deduplicates from kGroupedMinRows rows), rows * V * 2 and V * r * 2
+// at most 2^31 bytes; hipErrorNotSupported otherwise.
 hipError_t launch_apply_grouped(const KernelParams& p, hipStream_t s) {
-  if (p.rows < kGroupedMinRows || p.rows > kGroupedMaxRows) return hipErrorNotSupported;
+  if (p.rows < 1 || p.rows > kGroupedMaxRows) return hipErrorNotSupported;
   if (p.rows * p.V * 2 > ((int64_t)1 << 31) || p.V * p.r * 2 > ((int64_t)1 << 31)) return hipErrorNotSupported;
   switch (tile_ks_for_rank(p.r)) {
     case 1:

@@ -177,7 +177,7 @@ def _grouped_ids(kind, rng, n, V):
 @pytest.mark.parametrize("B,M,V,r,kind", [
     (64, 64, 1024, 64, "zipf"),        # 4096 rows: the largest grouped call
     (17, 241, 512, 32, "zipf"),        # 4097 rows: the row-order kernel instead
-    (31, 33, 700, 16, "zipf"),         # 1023 rows: the row-order kernel instead
+    (31, 33, 700, 16, "zipf"),         # 1023 rows: no plan, rows in their own order
     (32, 33, 1000, 24, "same"),        # 1056 rows, one distinct token, rank padded to 32
     (2, 512, 4104, 40, "distinct"),    # 1024 rows: every chunk of 32 rows adds two tiles
     (5, 205, 2048, 512, "bad-mix"),    # rank 512, ids outside [0, V)
