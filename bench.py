@@ -118,8 +118,9 @@ def algorithmic_bytes_sample(w, return_logits=True) -> int:
 
 
 def algorithmic_bytes_apply(w) -> int:
-    lb = 2 if w.dtype == 1 else 4
-    return w.B * w.M * w.V * lb * 2 + w.V * w.r * lb + w.B * w.M * (w.r * lb + 8)
+    lb = 2 if w.ldtype == 1 else 4   # logits
+    wb = 2 if w.dtype == 1 else 4    # weights
+    return w.B * w.M * w.V * lb * 2 + w.V * w.r * wb + w.B * w.M * (w.r * wb + 8)
 
 
 def to_dev(a, torch, np):
@@ -288,7 +289,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extra:
         result["other_workloads"] = {n: measure_extra(n, rmd, wl, torch, np) for n in
-                                     ("teacher_forced_320", "teacher_forced_2560_zipf", "temperature_draft_256x8")}
+                                     ("teacher_forced_320", "teacher_forced_2560_zipf", "temperature_draft_256x8",
+                                      "teacher_forced_320_f32logits")}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, np)
     print(json.dumps(result))

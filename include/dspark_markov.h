@@ -32,8 +32,10 @@
  *           result is identical).  W1 is the Embedding weight [V, r]; W2 is
  *           passed as the Linear(r, V) weight [V, r], i.e. the transpose of
  *           the mathematical W2.
- * Dtypes.   (logits, weights) must be (F32, F32) or (BF16, BF16); other
- *           pairs return DSPARK_ERR_UNSUPPORTED.  Token ids are int64.
+ * Dtypes.   (logits, weights) may be any pair of F32 and BF16; the
+ *           roundings below follow each tensor's own dtype (the pages'
+ *           bias.to(logits.dtype) defines the mixed case).  Token ids are
+ *           int64.
  * Numerics. bias = round_L(round_W(fp32 dot product of W1[x] and W2w[v]));
  *           corrected = round_L(fp32(base) + fp32(bias))  (Linear output in
  *           the weight dtype, then .to(logits dtype), then the add).

@@ -99,7 +99,6 @@ dspark_status_t check_common(int ldt, int wdt, int64_t B, int64_t M, int64_t V, 
                              int64_t* elems) {
   if (!known_dtype(ldt) || !known_dtype(wdt)) return DSPARK_ERR_INVALID_ARGUMENT;
   if (B < 0 || M < 0 || V < 0 || r <= 0) return DSPARK_ERR_INVALID_ARGUMENT;
-  if (ldt != wdt) return DSPARK_ERR_UNSUPPORTED;
   int64_t rows = 0, e = 0, wv = 0;
   if (!mul_ok(B, M, &rows) || !mul_ok(rows, V, &e) || !mul_ok(V, r, &wv))
     return DSPARK_ERR_INVALID_ARGUMENT;
@@ -166,12 +165,22 @@ dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_
   p.mode = dspark::MODE_APPLY;
   hipError_t e;
   const bool tile = tile_path(logits_dtype, weight_dtype, V, r, base_logits, corrected_logits, w1, w2);
-  if (!tile && r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
+  // fp32 logits with bf16 weights stream through the grouped kernel too
+  const bool f32_tile = tile_path(DSPARK_BF16, weight_dtype, V, r, base_logits, corrected_logits, w1, w2) &&
+                        logits_dtype == DSPARK_F32;
+  if (!tile && !f32_tile && r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
   p.sink = (char*)workspace + kControlBytes;
-  if (tile) {
+  e = hipErrorNotSupported;
+  if (f32_tile) {
+    e = dspark::launch_apply_grouped(p, true, (hipStream_t)stream);
+    if (e == hipErrorNotSupported) {
+      (void)hipGetLastError();
+      e = dspark::launch_generic(p, false, true, (hipStream_t)stream);
+    }
+  } else if (tile) {
     // grouped form (one bias per distinct predecessor) when the plan fits
     // in LDS, else the streaming form, else the tile kernel
-    e = dspark::launch_apply_grouped(p, (hipStream_t)stream);
+    e = dspark::launch_apply_grouped(p, false, (hipStream_t)stream);
     if (e == hipErrorNotSupported) {
       (void)hipGetLastError();
       e = dspark::launch_apply_wide(p, (hipStream_t)stream);

@@ -250,8 +250,12 @@ constexpr int kGroupedMinRows = 1024;
 // DEDUP: plan with the hash table (one bias per distinct token); without
 // it every row is its own token id (rows in their own order), which costs
 // nothing to plan and suits batches with few repeats.
-template <int K32, int WAVES, int D, int KB, bool DEDUP>
+// LF32: fp32 logits (the weights stay bf16); each 8-column vector of a row
+// is then two 16-byte pieces, the sum is not rounded again.
+template <int K32, int WAVES, int D, int KB, bool DEDUP, bool LF32>
 __global__ __launch_bounds__(WAVES * 64) void markov_apply_grouped_bf16(KernelParams p) {
+  constexpr int NV = LF32 ? 2 : 1;             // 16-byte pieces per 8-column vector
+  constexpr uint32_t LB = LF32 ? 4u : 2u;      // bytes per logit
   constexpr int THREADS = WAVES * 64;
   constexpr int RC = 32;                       // sorted rows per chunk
   constexpr int COLS = 32 * WAVES;             // columns of the workgroup
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(WAVES * 64) void markov_apply_grouped_bf16(KernelPa
   const uint32_t vend = (vbeg + COLS < V) ? vbeg + COLS : V;
   const uint32_t S = (V + 31) / 32;
   const bool has = blockIdx.x * WAVES + wave < S;
-  const uint32_t lbytes = (uint32_t)rows * V * 2u;  // <= 2^31 (host)
+  const uint32_t lbytes = (uint32_t)rows * V * LB;  // <= 2^31 (host)
   const __amdgpu_buffer_rsrc_t rs_base = buffer_rsrc(p.base, lbytes);
   const __amdgpu_buffer_rsrc_t rs_out = buffer_rsrc(p.out, lbytes);
   const BufferWords bw_w1 = buffer_words(p.w1, V * (uint32_t)r * 2u);
@@ -481,7 +485,7 @@ __global__ __launch_bounds__(WAVES * 64) void markov_apply_grouped_bf16(KernelPa
   const bool col_ok = col < vend;
   auto prow = [&](int q) __attribute__((always_inline)) { return (tid + q * THREADS) / VPR; };
   auto base_off = [&](int pos) __attribute__((always_inline)) -> uint32_t {
-    return (pos < rows && col_ok) ? ((uint32_t)plan_row[pos] * V + col) * 2u : kBufferOob;
+    return (pos < rows && col_ok) ? ((uint32_t)plan_row[pos] * V + col) * LB : kBufferOob;
   };
   // waves GW and GW - 1: W1 rows of tiles t0 .. t0 + nn - 1 into their LDS
   // slots, the even rank blocks by GW and the odd ones by GW - 1
@@ -503,13 +507,17 @@ __global__ __launch_bounds__(WAVES * 64) void markov_apply_grouped_bf16(KernelPa
   // The ring is filled in the loop's own pattern of a store and a load per
   // vector (the stores here land past the buffer and are dropped), so the
   // compiler's count of the operations after each ring load is the loop's.
-  u32x4_t ring[D][VPT];
+  u32x4_t ring[D][VPT][NV];
 #pragma unroll
   for (int d = 0; d < D; ++d)
 #pragma unroll
     for (int q = 0; q < VPT; ++q) {
-      buffer_store16(rs_out, kBufferOob + 16u * (uint32_t)(d * VPT + q), u32x4_t{0u, 0u, 0u, 0u});
-      ring[d][q] = buffer_load16(rs_base, base_off(RC * d + prow(q)));
+#pragma unroll
+      for (int h = 0; h < NV; ++h)
+        buffer_store16(rs_out, kBufferOob + 16u * (uint32_t)((d * VPT + q) * NV + h), u32x4_t{0u, 0u, 0u, 0u});
+      const uint32_t off = base_off(RC * d + prow(q));
+#pragma unroll
+      for (int h = 0; h < NV; ++h) ring[d][q][h] = buffer_load16(rs_base, off + 16u * h);
     }
   // W2 is complete before the chunk loop (the ring stays in flight), so that
   // no wait inside the loop is held back by it.
@@ -561,7 +569,7 @@ __global__ __launch_bounds__(WAVES * 64) void markov_apply_grouped_bf16(KernelPa
   // stream chunk c (its bias was written a chunk ago).  One barrier.  Live
   // tiles: gathered slots lt(c)+1 .. lt(c+2) (at most four), bias tiles
   // lt(c)-2 .. lt(c+1) (at most five).
-  auto chunk = [&](int c, u32x4_t pre[VPT]) __attribute__((always_inline)) {
+  auto chunk = [&](int c, u32x4_t pre[VPT][NV]) __attribute__((always_inline)) {
     const int l1 = last_tile(c + 1);
     if (wave >= GW - 1) gather(l1 + 1, last_tile(c + 2) - l1);
     multiply(lt_done + 1, l1);
@@ -574,20 +582,36 @@ __global__ __launch_bounds__(WAVES * 64) void markov_apply_grouped_bf16(KernelPa
       const int pc = pos < rows ? pos : rows - 1;
       const uint32_t row = plan_row[pc];
       const uint32_t u = plan_uid[pc];
-      const u32x4_t bb = pre[q];
       const u32x4_t bs = *(const u32x4_t*)(lds_b + (16u * ((u >> 4) % kBiasTiles) + (u & 15u)) * BSTRIDE + vi * 16);
-      u32x4_t o;
-      o.x = pack_bf16x2(bf16_lo(bb.x) + bf16_lo(bs.x), bf16_hi(bb.x) + bf16_hi(bs.x));
-      o.y = pack_bf16x2(bf16_lo(bb.y) + bf16_lo(bs.y), bf16_hi(bb.y) + bf16_hi(bs.y));
-      o.z = pack_bf16x2(bf16_lo(bb.z) + bf16_lo(bs.z), bf16_hi(bb.z) + bf16_hi(bs.z));
-      o.w = pack_bf16x2(bf16_lo(bb.w) + bf16_lo(bs.w), bf16_hi(bb.w) + bf16_hi(bs.w));
-      buffer_store16(rs_out, (pos < rows && col_ok) ? (row * V + col) * 2u : kBufferOob, o);
+      const uint32_t ooff = (pos < rows && col_ok) ? (row * V + col) * LB : kBufferOob;
+      if constexpr (LF32) {
+        // fp32 logits: the bf16 bias widened exactly, one fp32 add
+        const u32x4_t b0 = pre[q][0], b1 = pre[q][1];
+        const float bias[8] = {bf16_lo(bs.x), bf16_hi(bs.x), bf16_lo(bs.y), bf16_hi(bs.y),
+                               bf16_lo(bs.z), bf16_hi(bs.z), bf16_lo(bs.w), bf16_hi(bs.w)};
+        const u32x4_t o0 = u32x4_t{__float_as_uint(__uint_as_float(b0.x) + bias[0]), __float_as_uint(__uint_as_float(b0.y) + bias[1]),
+                                   __float_as_uint(__uint_as_float(b0.z) + bias[2]), __float_as_uint(__uint_as_float(b0.w) + bias[3])};
+        const u32x4_t o1 = u32x4_t{__float_as_uint(__uint_as_float(b1.x) + bias[4]), __float_as_uint(__uint_as_float(b1.y) + bias[5]),
+                                   __float_as_uint(__uint_as_float(b1.z) + bias[6]), __float_as_uint(__uint_as_float(b1.w) + bias[7])};
+        buffer_store16(rs_out, ooff, o0);
+        buffer_store16(rs_out, ooff + 16u, o1);
+      } else {
+        const u32x4_t bb = pre[q][0];
+        u32x4_t o;
+        o.x = pack_bf16x2(bf16_lo(bb.x) + bf16_lo(bs.x), bf16_hi(bb.x) + bf16_hi(bs.x));
+        o.y = pack_bf16x2(bf16_lo(bb.y) + bf16_lo(bs.y), bf16_hi(bb.y) + bf16_hi(bs.y));
+        o.z = pack_bf16x2(bf16_lo(bb.z) + bf16_lo(bs.z), bf16_hi(bb.z) + bf16_hi(bs.z));
+        o.w = pack_bf16x2(bf16_lo(bb.w) + bf16_lo(bs.w), bf16_hi(bb.w) + bf16_hi(bs.w));
+        buffer_store16(rs_out, ooff, o);
+      }
       // refilled after its last use, so the new value can take its registers
-      pre[q] = buffer_load16(rs_base, base_off(pos + RC * D));
+      const uint32_t noff = base_off(pos + RC * D);
+#pragma unroll
+      for (int h = 0; h < NV; ++h) pre[q][h] = buffer_load16(rs_base, noff + 16u * h);
     }
     // the gathered rows are in LDS before the barrier (the stream's loads
     // and stores issued after them may stay in flight)
-    if (wave >= GW - 1) wait_vmcnt<2 * VPT>();
+    if (wave >= GW - 1) wait_vmcnt<2 * NV * VPT>();
     lds_barrier();
   };
 
@@ -607,32 +631,47 @@ hipError_t launch_wide(const KernelParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int K32, int WAVES, int D, int KB>
+template <int K32, int WAVES, int D, int KB, bool LF32>
 hipError_t launch_grouped(const KernelParams& p, hipStream_t s) {
   const int64_t S = (p.V + 31) / 32;
   const dim3 grid((unsigned)((S + WAVES - 1) / WAVES));
   if (p.rows >= kGroupedMinRows)
-    hipLaunchKernelGGL((markov_apply_grouped_bf16<K32, WAVES, D, KB, true>), grid, dim3(WAVES * 64), 0, s, p);
+    hipLaunchKernelGGL((markov_apply_grouped_bf16<K32, WAVES, D, KB, true, LF32>), grid, dim3(WAVES * 64), 0, s, p);
   else
-    hipLaunchKernelGGL((markov_apply_grouped_bf16<K32, WAVES, D, KB, false>), grid, dim3(WAVES * 64), 0, s, p);
+    hipLaunchKernelGGL((markov_apply_grouped_bf16<K32, WAVES, D, KB, false, LF32>), grid, dim3(WAVES * 64), 0, s, p);
   return hipGetLastError();
 }
 }  // namespace
 
-// Grouped teacher-forced apply (bf16): 1 <= rows <= kGroupedMaxRows (the
-// plan deduplicates from kGroupedMinRows rows), rows * V * 2 and V * r * 2
-// at most 2^31 bytes; hipErrorNotSupported otherwise.
-hipError_t launch_apply_grouped(const KernelParams& p, hipStream_t s) {
+// Grouped teacher-forced apply (bf16 weights; bf16 or fp32 logits):
+// 1 <= rows <= kGroupedMaxRows (the plan deduplicates from kGroupedMinRows
+// rows), the logits and V * r * 2 at most 2^31 bytes; hipErrorNotSupported
+// otherwise.
+hipError_t launch_apply_grouped(const KernelParams& p, bool logits_f32, hipStream_t s) {
   if (p.rows < 1 || p.rows > kGroupedMaxRows) return hipErrorNotSupported;
-  if (p.rows * p.V * 2 > ((int64_t)1 << 31) || p.V * p.r * 2 > ((int64_t)1 << 31)) return hipErrorNotSupported;
+  if (p.rows * p.V * (logits_f32 ? 4 : 2) > ((int64_t)1 << 31) || p.V * p.r * 2 > ((int64_t)1 << 31))
+    return hipErrorNotSupported;
+  // fp32 logits take twice the ring registers per chunk: half the depth
+  if (logits_f32) {
+    switch (tile_ks_for_rank(p.r)) {
+      case 1:
+      case 2: return launch_grouped<1, 16, 2, 1, true>(p, s);
+      case 4: return launch_grouped<2, 16, 2, 2, true>(p, s);
+      case 8: return launch_grouped<4, 16, 2, 2, true>(p, s);
+      case 16: return launch_grouped<8, 16, 1, 4, true>(p, s);
+      case 24: return launch_grouped<12, 8, 2, 4, true>(p, s);
+      case 32: return launch_grouped<16, 8, 2, 8, true>(p, s);
+      default: return hipErrorNotSupported;
+    }
+  }
   switch (tile_ks_for_rank(p.r)) {
     case 1:
-    case 2: return launch_grouped<1, 16, 4, 1>(p, s);
-    case 4: return launch_grouped<2, 16, 4, 2>(p, s);
-    case 8: return launch_grouped<4, 16, 4, 2>(p, s);
-    case 16: return launch_grouped<8, 16, 2, 4>(p, s);
-    case 24: return launch_grouped<12, 8, 4, 4>(p, s);
-    case 32: return launch_grouped<16, 8, 4, 8>(p, s);
+    case 2: return launch_grouped<1, 16, 4, 1, false>(p, s);
+    case 4: return launch_grouped<2, 16, 4, 2, false>(p, s);
+    case 8: return launch_grouped<4, 16, 4, 2, false>(p, s);
+    case 16: return launch_grouped<8, 16, 2, 4, false>(p, s);
+    case 24: return launch_grouped<12, 8, 4, 4, false>(p, s);
+    case 32: return launch_grouped<16, 8, 4, 8, false>(p, s);
     default: return hipErrorNotSupported;
   }
 }

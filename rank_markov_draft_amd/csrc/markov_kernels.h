@@ -75,10 +75,11 @@ hipError_t launch_tile(const KernelParams& p, hipStream_t s);
 // apply_sink_bytes() bytes.
 hipError_t launch_apply_wide(const KernelParams& p, hipStream_t s);
 size_t apply_sink_bytes();
-// Grouped teacher-forced apply (bf16): from 1024 rows each distinct
-// predecessor's bias is computed once; needs 1 <= rows <= 4096 and
-// rows * V * 2, V * r * 2 <= 2^31.
-hipError_t launch_apply_grouped(const KernelParams& p, hipStream_t s);
+// Grouped teacher-forced apply (bf16 weights; bf16 logits, or fp32 logits
+// when logits_f32): from 1024 rows each distinct predecessor's bias is
+// computed once; needs 1 <= rows <= 4096 and the logits and V * r * 2 at
+// most 2^31 bytes.
+hipError_t launch_apply_grouped(const KernelParams& p, bool logits_f32, hipStream_t s);
 // One bf16 sampling step (greedy or temperature) of the p.rows = B rows at
 // position p.k: argmax keys per (row, 512-column block) into p.partials with
 // p.nparts = sample_step_parts(V); one workgroup per CU.  Needs r <= 256,

@@ -46,6 +46,11 @@ class Workload:
     ids: str = "uniform"   # "uniform" or "zipf1.1"
     boost: float = 0.0     # added at one random position per (b, k) row
     return_logits: bool = True
+    logits_dtype: int = -1  # the logits' dtype when it differs from the weights' (-1: same)
+
+    @property
+    def ldtype(self) -> int:
+        return self.dtype if self.logits_dtype < 0 else self.logits_dtype
 
     @property
     def rows(self) -> int:
@@ -72,6 +77,11 @@ WORKLOADS = {
                                         dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=4,
                                         mode="temperature", temperature=0.7, gumbel_seed=1234,
                                         return_logits=False),
+    # The 320-row teacher-forced batch with fp32 base logits (an fp32 LM head
+    # output) and bf16 weights.
+    "teacher_forced_320_f32logits": Workload("teacher_forced_320_f32logits", B=64, M=5, V=129280,
+                                             r=256, dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=2,
+                                             mode="apply", logits_dtype=F32),
     # Large teacher-forced batch: 8 sequences x 64 anchors, rank 512, Zipf ids.
     "teacher_forced_2560_zipf": Workload("teacher_forced_2560_zipf", B=512, M=5, V=129280, r=512,
                                          dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=5,
@@ -122,6 +132,8 @@ def make_inputs(w: Workload, *, B: int | None = None, M: int | None = None,
     else:
         token_ids = rng.integers(0, max(V, 1), size=(B, M), dtype=np.int64)
     first_prev = rng.integers(0, max(V, 1), size=(B,), dtype=np.int64)
+    if w.ldtype == BF16:
+        base = to_bf16_bits(base)
     if w.dtype == BF16:
-        base, w1, w2 = to_bf16_bits(base), to_bf16_bits(w1), to_bf16_bits(w2)
+        w1, w2 = to_bf16_bits(w1), to_bf16_bits(w2)
     return {"base": base, "w1": w1, "w2": w2, "token_ids": token_ids, "first_prev": first_prev}

@@ -69,7 +69,6 @@ FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: every call below fails 
     ((1, 1, -1, 3, 64, 16), 1),      # negative sizes
     ((1, 1, 2, -3, 64, 16), 1),
     ((1, 1, 2, 3, -64, 16), 1),
-    ((0, 1, 2, 3, 64, 16), 2),       # mixed dtype pair
     ((7, 7, 2, 3, 64, 16), 1),       # unknown dtype tag
     ((1, 1, 2**40, 2**20, 2**20, 16), 1),   # element count overflows int64
 ])
@@ -77,6 +76,15 @@ def test_apply_argument_errors(L, args, code):
     ldt, wdt, B, M, V, r = args
     st = L.dspark_markov_apply_block(FAKE, ldt, FAKE, FAKE, FAKE, wdt, B, M, V, r, FAKE, FAKE, 1 << 20, None)
     assert st == code
+
+
+def test_mixed_dtype_pairs_pass_validation(L):
+    """Both mixed (logits, weights) pairs are accepted: with no workspace the
+    call stops at the workspace check, before anything is enqueued."""
+    for ldt, wdt in ((0, 1), (1, 0)):
+        assert L.dspark_markov_apply_block(FAKE, ldt, FAKE, FAKE, FAKE, wdt, 2, 3, 64, 16, FAKE, None, 0, None) == 3
+        assert L.dspark_markov_sample_block(FAKE, ldt, FAKE, FAKE, FAKE, wdt, 2, 3, 64, 16, 0.0, 0, 0, 0,
+                                            FAKE, FAKE, None, 0, None) == 3
 
 
 def test_apply_empty_is_ok_and_touches_nothing(L):

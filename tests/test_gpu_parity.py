@@ -107,6 +107,14 @@ def test_teacher_forced_320(native):
     assert rep.mismatches <= 1e-4 * rep.elements
 
 
+def test_teacher_forced_320_f32logits(native):
+    w = wl.WORKLOADS["teacher_forced_320_f32logits"]
+    inp = wl.make_inputs(w)
+    assert inp["base"].dtype == np.float32 and inp["w1"].dtype == np.uint16
+    rep = check_apply(inp, run_apply(inp), name=w.name)
+    assert rep.mismatches <= 1e-4 * rep.elements
+
+
 def test_greedy_draft_64x5(native):
     w = wl.WORKLOADS["greedy_draft_64x5"]
     inp = wl.make_inputs(w)
@@ -203,6 +211,31 @@ def test_apply_repeated_predecessors(native, B, M, V, r, kind):
     check_apply(inp, out, rows=good, name=f"apply {kind} B{B} M{M} V{V} r{r}")
 
 
+@pytest.mark.parametrize("B,M,V,r,kind", [
+    (4, 300, 5000, 256, "zipf"),       # 1200 rows: one bias per distinct token
+    (32, 33, 1000, 24, "same"),        # 1056 rows, one distinct token
+    (31, 33, 700, 16, "zipf"),         # 1023 rows: no plan
+    (9, 115, 3000, 512, "bad-mix"),    # rank 512, ids outside [0, V)
+])
+def test_apply_repeated_predecessors_f32_logits(native, B, M, V, r, kind):
+    """fp32 logits with bf16 weights on the grouped path."""
+    inp = _mixed_inputs(wl.F32, wl.BF16, B, M, V, r, seed=B * 5 + V)
+    rng = np.random.default_rng(B + M + V + 1)
+    ids = _grouped_ids(kind, rng, B * M, V).reshape(B, M)
+    inp = dict(inp, token_ids=ids)
+    d = device_inputs({k: inp[k] for k in ("base", "token_ids", "w1", "w2")})
+    ws = rmd.Workspace(B, M, V, r, sample=False)
+    out = from_dev(rmd.apply_block_logits(d["base"], d["token_ids"], d["w1"], d["w2"], workspace=ws))
+    assert out.dtype == np.float32
+    flat = ids.reshape(-1)
+    bad = (flat < 0) | (flat >= V)
+    assert rmd.read_device_error(ws) == int(bad.sum())
+    flat_out = out.reshape(B * M, V)
+    assert np.array_equal(flat_out[bad], inp["base"].reshape(B * M, V)[bad])
+    good = np.nonzero(~bad)[0]
+    check_apply(inp, out, rows=good, name=f"apply f32-logits {kind} B{B} M{M} V{V} r{r}")
+
+
 @pytest.mark.parametrize("T", [0.0, 0.8])
 @pytest.mark.parametrize("B,M,V,r,dtype", [
     (3, 4, 1000, 24, wl.BF16),
@@ -215,6 +248,32 @@ def test_sample_shapes(native, T, B, M, V, r, dtype):
     inp = wl.make_inputs(w, B=B, M=M, V=V, r=r, seed=7 + B + V)
     tok, corr = run_sample(inp, T, seed=11)
     check_chain(inp, T, 11, tok, corr, name=f"sample T{T} B{B} M{M} V{V} r{r} dt{dtype}")
+
+
+def _mixed_inputs(ldt, wdt, B, M, V, r, seed):
+    """Workload-shaped inputs with the logits in ldt and the weights in wdt."""
+    w = dataclasses.replace(wl.WORKLOADS["teacher_forced_320"], dtype=wl.F32)
+    inp = wl.make_inputs(w, B=B, M=M, V=V, r=r, seed=seed)
+    if ldt == wl.BF16:
+        inp["base"] = wl.to_bf16_bits(inp["base"])
+    if wdt == wl.BF16:
+        inp["w1"], inp["w2"] = wl.to_bf16_bits(inp["w1"]), wl.to_bf16_bits(inp["w2"])
+    return inp
+
+
+@pytest.mark.parametrize("ldt,wdt", [(wl.F32, wl.BF16), (wl.BF16, wl.F32)])
+@pytest.mark.parametrize("B,M,V,r", [(3, 5, 1000, 24), (2, 33, 4104, 64)])
+def test_apply_mixed_dtypes(native, ldt, wdt, B, M, V, r):
+    inp = _mixed_inputs(ldt, wdt, B, M, V, r, seed=B + V)
+    check_apply(inp, run_apply(inp), name=f"apply mixed L{ldt} W{wdt} B{B} M{M} V{V} r{r}")
+
+
+@pytest.mark.parametrize("T", [0.0, 0.8])
+@pytest.mark.parametrize("ldt,wdt", [(wl.F32, wl.BF16), (wl.BF16, wl.F32)])
+def test_sample_mixed_dtypes(native, T, ldt, wdt):
+    inp = _mixed_inputs(ldt, wdt, 5, 4, 2048, 32, seed=99)
+    tok, corr = run_sample(inp, T, seed=5)
+    check_chain(inp, T, 5, tok, corr, name=f"sample mixed T{T} L{ldt} W{wdt}")
 
 
 def test_in_place_apply(native):
@@ -269,9 +328,6 @@ def test_invalid_arguments_rejected_on_host(native):
     # r <= 0
     assert L.dspark_markov_apply_block(p(d["base"]), 1, p(d["token_ids"]), p(d["w1"]), p(d["w2"]), 1,
                                        2, 2, 64, 0, p(out), ws.ptr, ws.nbytes, s) == 1
-    # mixed dtype pair
-    assert L.dspark_markov_apply_block(p(d["base"]), 0, p(d["token_ids"]), p(d["w1"]), p(d["w2"]), 1,
-                                       2, 2, 64, 16, p(out), ws.ptr, ws.nbytes, s) == 2
     # workspace too small
     assert L.dspark_markov_apply_block(p(d["base"]), 1, p(d["token_ids"]), p(d["w1"]), p(d["w2"]), 1,
                                        2, 2, 64, 16, p(out), ws.ptr, 8, s) == 3

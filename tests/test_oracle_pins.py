@@ -184,6 +184,61 @@ def test_fp32_add_single_rounding(oracle_mod):
     assert _one_row(oracle_mod, [2**-12, 2**-12], [2**-12, 2**-11], 1.0, wl.F32) == np.float32(1 + 2**-22)
 
 
+# ------------------------- mixed (logits, weights) dtypes: closed forms
+def _one_row_pair(oracle_mod, e, w, base_val, ldt, wdt):
+    """As _one_row, with the logits in dtype ldt and the weights in wdt."""
+    r = len(e)
+    w1 = np.zeros((2, r), np.float32)
+    w2 = np.zeros((2, r), np.float32)
+    w1[0] = e
+    w2[0] = w
+    base = np.array([[[base_val, 0.0]]], np.float32)
+    ids = np.zeros((1, 1), np.int64)
+    if ldt == wl.BF16:
+        base = wl.to_bf16_bits(base)
+    if wdt == wl.BF16:
+        w1, w2 = wl.to_bf16_bits(w1), wl.to_bf16_bits(w2)
+    out = oracle_mod.apply_block(base, ids, w1, w2)
+    assert out.dtype == base.dtype
+    return float(as_float(out)[0, 0, 0])
+
+
+def test_mixed_f32_logits_bf16_weights(oracle_mod):
+    """(F32, BF16): the Linear rounds its output to bf16, the add is an fp32
+    add with no further rounding.  acc = 1 + 2^-8 ties to the bias 1.0, so
+    c = 2^-9 + 1 exactly: skipping the weight rounding gives 1 + 3*2^-9,
+    rounding the sum to bf16 gives 1.0."""
+    assert _one_row_pair(oracle_mod, [1.0, 2**-4], [1.0, 2**-4], 2**-9, wl.F32, wl.BF16) == 1 + 2**-9
+
+
+def test_mixed_bf16_logits_f32_weights(oracle_mod):
+    """(BF16, F32): the fp32 bias is cast to bf16 before the add and the sum
+    is rounded to bf16.  acc = 1 + 2^-8 casts (tie, even) to 1.0, so
+    c = bf16(2^-9 + 1) = 1.0 (uncast: bf16(1 + 3*2^-9) = 1 + 2^-7); and
+    c = bf16(1 + 2^-24) = 1.0 (an unrounded sum would stay 1 + 2^-24)."""
+    assert _one_row_pair(oracle_mod, [1.0, 2**-4], [1.0, 2**-4], 2**-9, wl.BF16, wl.F32) == 1.0
+    assert _one_row_pair(oracle_mod, [2**-12], [2**-12], 1.0, wl.BF16, wl.F32) == 1.0
+    # the fp32 bias itself is exact here: 2^-7 + 2^-8 is a bf16 value
+    assert _one_row_pair(oracle_mod, [2**-4, 2**-4], [2**-3, 2**-4], 0.0, wl.BF16, wl.F32) == 2**-7 + 2**-8
+
+
+@pytest.mark.parametrize("ldt,wdt", [(wl.F32, wl.BF16), (wl.BF16, wl.F32)])
+def test_mixed_apply_exact_bruteforce(oracle_mod, ldt, wdt):
+    """Mixed pairs on exact inputs: base + (W1 W2w^T)[x] from a library
+    matmul, as for the single-dtype pairs."""
+    rng = np.random.default_rng(13)
+    B, M, V, r = 3, 4, 64, 8
+    base, ids, _, w1, w2 = dyadic_inputs(rng, B, M, V, r, wl.F32)
+    T = w1.astype(np.float64) @ w2.astype(np.float64).T
+    want = base.astype(np.float64) + T[ids]
+    if ldt == wl.BF16:
+        base = wl.to_bf16_bits(base)
+    if wdt == wl.BF16:
+        w1, w2 = wl.to_bf16_bits(w1), wl.to_bf16_bits(w2)
+    got = as_float(oracle_mod.apply_block(base, ids, w1, w2)).astype(np.float64)
+    assert np.array_equal(got, want)
+
+
 # ----------------------------------------------------------- invariants
 @pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
 def test_equal_predecessor_rows_identical(oracle_mod, dtype):
@@ -208,12 +263,18 @@ def dataclass_replace(w, **kw):
     return dataclasses.replace(w, **kw)
 
 
-@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16, "f32-logits", "bf16-logits"])
 @pytest.mark.parametrize("which", ["w1", "w2"])
 def test_zero_weights_identity(oracle_mod, dtype, which):
-    """W2 = 0 (or W1 = 0) leaves the base logits unchanged (by value)."""
-    w = dataclass_replace(wl.WORKLOADS["tiny_fp32"], dtype=dtype)
+    """W2 = 0 (or W1 = 0) leaves the base logits unchanged (by value), also
+    with mixed dtypes ("f32-logits": fp32 logits, bf16 weights)."""
+    mixed = dtype in ("f32-logits", "bf16-logits")
+    w = dataclass_replace(wl.WORKLOADS["tiny_fp32"], dtype=wl.F32 if dtype == "f32-logits" else
+                          wl.BF16 if dtype == "bf16-logits" else dtype)
     inp = wl.make_inputs(w, B=3, M=4, V=513, r=16)
+    if mixed:   # the weights in the other dtype
+        conv = wl.to_bf16_bits if dtype == "f32-logits" else wl.bf16_bits_to_f32
+        inp["w1"], inp["w2"] = conv(inp["w1"]), conv(inp["w2"])
     inp[which] = np.zeros_like(inp[which])
     out = oracle_mod.apply_block(inp["base"], inp["token_ids"], inp["w1"], inp["w2"])
     assert np.array_equal(as_float(out), as_float(inp["base"]))
