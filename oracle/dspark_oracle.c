@@ -117,18 +117,27 @@ static double* w2_as_double(const void* w2, int wdt, int64_t V, int64_t r) {
   return d;
 }
 
-/* One corrected row: base row (length V, dtype ldt) biased by token x.
- * Writes the L-typed results as floats into out[V]. */
-static void corrected_row(const void* base, int ldt, int64_t base_row,
-                          const void* w1, const double* w2d, int wdt, int64_t V,
-                          int64_t r, int64_t x, double* e, float* out) {
-  gather_w1_row(w1, wdt, r, x, e);
+/* One corrected row: base row (length V, dtype ldt) biased by the
+ * projection of the latent row e[r] (W1[x] for the vanilla head).  Writes
+ * the L-typed results as floats into out[V]. */
+static void corrected_row_from(const void* base, int ldt, int64_t base_row,
+                               const double* w2d, int wdt, int64_t V, int64_t r,
+                               const double* e, float* out) {
   for (int64_t v = 0; v < V; ++v) {
     float acc = projected_bias(e, w2d + v * r, r);
     float b = load_as_float(base, ldt, base_row * V + v);
     out[v] = corrected_value(b, acc, ldt, wdt);
   }
 }
+
+/* One corrected row biased by token x (vanilla head). */
+static void corrected_row(const void* base, int ldt, int64_t base_row,
+                          const void* w1, const double* w2d, int wdt, int64_t V,
+                          int64_t r, int64_t x, double* e, float* out) {
+  gather_w1_row(w1, wdt, r, x, e);
+  corrected_row_from(base, ldt, base_row, w2d, wdt, V, r, e, out);
+}
+
 
 static int n_threads_or_default(int n) { return n > 0 ? n : omp_get_max_threads(); }
 
@@ -380,5 +389,268 @@ int dspark_oracle_logit_bounds(const void* base_logits, int logits_dtype,
     mid[i] = corrected_value(b, (float)a, logits_dtype, weight_dtype);
     hi[i] = corrected_value(b, (float)(a + delta), logits_dtype, weight_dtype);
   }
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Gated head ([P5] / [P3] GatedMarkovHead)                            */
+/* ------------------------------------------------------------------ */
+
+/* Logistic function of a W-typed value, evaluated in double and rounded
+ * once to fp32 (torch's sigmoid on a reduced-precision tensor computes in
+ * fp32), then to W. */
+static float gate_value(float z, int wdt) {
+  double s = 1.0 / (1.0 + exp(-(double)z));
+  return round_to((float)s, wdt);
+}
+
+/* [P5] GatedMarkovHead.compute_gate and compute_step_bias, for one row:
+ *   in   = [h.to(W); W1[x].to(W)]            (concatenation, hidden first)
+ *   z_j  = gate_proj(in)_j = sum_i in_i Gw[j, i] + gb_j   (Linear(d + r, r))
+ *   g_j  = sigmoid(z_j)                       (then .to(e.dtype) = W)
+ *   u_j  = g_j * e_j                          (what project_bias receives)
+ * Reading: the Linear's fp32 accumulator (bias included) is modelled by
+ * its best value, the double sum rounded once to fp32, then rounded to W;
+ * the sigmoid as in gate_value; the product in fp32, then rounded to W.
+ * When lo/hi are given they receive the admissible interval of u_j: the
+ * sum pushed to -/+ 2 (d + r + 1) 2^-24 (sum_i |in_i Gw[j, i]| + |gb_j|)
+ * (fp32 accumulation in any order, split or not) and the fp32 sigmoid
+ * widened by a relative 2^-20, through the monotone chain. */
+static void gated_row(const void* hidden, int hdt, int64_t h_row, int64_t d,
+                      const void* w1, int64_t x, const void* gw, const void* gb,
+                      int wdt, int64_t r, double* in, float* u, float* lo, float* hi) {
+  const int64_t K = d + r;
+  for (int64_t i = 0; i < d; ++i)
+    in[i] = (double)round_to(load_as_float(hidden, hdt, h_row * d + i), wdt);
+  for (int64_t j = 0; j < r; ++j) in[d + j] = load_as_double(w1, wdt, x * r + j);
+  for (int64_t j = 0; j < r; ++j) {
+    double a = 0.0, s = 0.0;
+    for (int64_t i = 0; i < K; ++i) {
+      double t = in[i] * load_as_double(gw, wdt, j * K + i);
+      a += t;
+      s += fabs(t);
+    }
+    const double bj = load_as_double(gb, wdt, j);
+    const float ej = (float)in[d + j];
+    const float z = round_to((float)(a + bj), wdt);
+    const float g = gate_value(z, wdt);
+    u[j] = round_to(g * ej, wdt);
+    if (lo && hi) {
+      const double delta = 2.0 * (double)(K + 1) * ldexp(1.0, -24) * (s + fabs(bj));
+      const float zl = round_to((float)(a + bj - delta), wdt);
+      const float zh = round_to((float)(a + bj + delta), wdt);
+      const double sl = (1.0 / (1.0 + exp(-(double)zl))) * (1.0 - ldexp(1.0, -20));
+      const double sh = (1.0 / (1.0 + exp(-(double)zh))) * (1.0 + ldexp(1.0, -20));
+      const float gl = round_to((float)sl, wdt), gh = round_to((float)sh, wdt);
+      const float ul = round_to(gl * ej, wdt), uh = round_to(gh * ej, wdt);
+      lo[j] = ul < uh ? ul : uh;
+      hi[j] = ul < uh ? uh : ul;
+    }
+  }
+}
+
+static int gated_args_ok(int hdt, int wdt, int64_t d, int64_t r) {
+  return valid_dtype(hdt) && valid_dtype(wdt) && d > 0 && r > 0;
+}
+
+/* Latent rows u[n, :] of the gated head for rows n with hidden state
+ * hidden[n, :] ([rows, d]) and predecessor token_ids[n].  Gw is the
+ * gate_proj weight [r, d + r], gb its bias [r]; both in the weight dtype.
+ * latent [rows, r] in the weight dtype; lo/hi [rows, r] float or NULL. */
+int dspark_oracle_gated_latent(const void* hidden, int hidden_dtype, int64_t d,
+                               const int64_t* token_ids, const void* w1,
+                               const void* gate_w, const void* gate_b,
+                               int weight_dtype, int64_t rows, int64_t V,
+                               int64_t r, void* latent, float* lo, float* hi,
+                               int n_threads) {
+  if (!gated_args_ok(hidden_dtype, weight_dtype, d, r)) return ORACLE_INVALID;
+  if (rows < 0 || V <= 0) return ORACLE_INVALID;
+  if (rows == 0) return ORACLE_OK;
+  if (!hidden || !token_ids || !w1 || !gate_w || !gate_b || !latent) return ORACLE_INVALID;
+  for (int64_t n = 0; n < rows; ++n)
+    if (token_ids[n] < 0 || token_ids[n] >= V) return ORACLE_INVALID;
+  int nt = n_threads_or_default(n_threads);
+#pragma omp parallel num_threads(nt)
+  {
+    double* in = (double*)malloc((size_t)(d + r) * sizeof(double));
+    float* u = (float*)malloc((size_t)r * sizeof(float));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t n = 0; n < rows; ++n) {
+      gated_row(hidden, hidden_dtype, n, d, w1, token_ids[n], gate_w, gate_b, weight_dtype, r,
+                in, u, lo ? lo + n * r : NULL, hi ? hi + n * r : NULL);
+      for (int64_t j = 0; j < r; ++j) store_from_float(latent, weight_dtype, n * r + j, u[j]);
+    }
+    free(u);
+    free(in);
+  }
+  return ORACLE_OK;
+}
+
+/* [P5] project_bias applied to given latent rows, then the add of
+ * apply_block_logits: row n of base [rows, V] is biased by latent[n, :]. */
+int dspark_oracle_apply_rows(const void* base_logits, int logits_dtype,
+                             const void* latent, const void* w2, int weight_dtype,
+                             int64_t rows, int64_t V, int64_t r,
+                             void* corrected_logits, int n_threads) {
+  if (!valid_dtype(logits_dtype) || !valid_dtype(weight_dtype)) return ORACLE_UNSUPPORTED;
+  if (rows < 0 || V < 0 || r <= 0) return ORACLE_INVALID;
+  if (rows == 0 || V == 0) return ORACLE_OK;
+  if (!base_logits || !latent || !w2 || !corrected_logits) return ORACLE_INVALID;
+  double* w2d = w2_as_double(w2, weight_dtype, V, r);
+  if (!w2d) return ORACLE_INVALID;
+  int nt = n_threads_or_default(n_threads);
+#pragma omp parallel num_threads(nt)
+  {
+    double* e = (double*)malloc((size_t)r * sizeof(double));
+    float* out = (float*)malloc((size_t)V * sizeof(float));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t n = 0; n < rows; ++n) {
+      gather_w1_row(latent, weight_dtype, r, n, e);
+      corrected_row_from(base_logits, logits_dtype, n, w2d, weight_dtype, V, r, e, out);
+      for (int64_t v = 0; v < V; ++v)
+        store_from_float(corrected_logits, logits_dtype, n * V + v, out[v]);
+    }
+    free(out);
+    free(e);
+  }
+  free(w2d);
+  return ORACLE_OK;
+}
+
+/* dspark_oracle_logit_bounds for elements biased by latent rows:
+ * element i is (rows[i], cols[i]) of base [*, V], biased by latent[rows[i]]. */
+int dspark_oracle_logit_bounds_rows(const void* base_logits, int logits_dtype,
+                                    const void* latent, const void* w2,
+                                    int weight_dtype, int64_t V, int64_t r,
+                                    int64_t n, const int64_t* rows,
+                                    const int64_t* cols, float* lo, float* mid,
+                                    float* hi) {
+  if (!valid_dtype(logits_dtype) || !valid_dtype(weight_dtype)) return ORACLE_UNSUPPORTED;
+  if (V <= 0 || r <= 0 || n < 0) return ORACLE_INVALID;
+  if (n == 0) return ORACLE_OK;
+  if (!base_logits || !latent || !w2 || !rows || !cols || !lo || !mid || !hi)
+    return ORACLE_INVALID;
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t row = rows[i], v = cols[i];
+    if (row < 0 || v < 0 || v >= V) return ORACLE_INVALID;
+    double a = 0.0, s = 0.0;
+    for (int64_t j = 0; j < r; ++j) {
+      double t = load_as_double(latent, weight_dtype, row * r + j) *
+                 load_as_double(w2, weight_dtype, v * r + j);
+      a += t;
+      s += fabs(t);
+    }
+    double delta = 2.0 * (double)r * ldexp(1.0, -24) * s;
+    float b = load_as_float(base_logits, logits_dtype, row * V + v);
+    lo[i] = corrected_value(b, (float)(a - delta), logits_dtype, weight_dtype);
+    mid[i] = corrected_value(b, (float)a, logits_dtype, weight_dtype);
+    hi[i] = corrected_value(b, (float)(a + delta), logits_dtype, weight_dtype);
+  }
+  return ORACLE_OK;
+}
+
+/* [P5] GatedMarkovHead through VanillaMarkov.apply_block_logits: every row
+ * (b, k) is biased by project_bias(gate * W1[token_ids[b, k]]), the gate
+ * from hidden_states[b, k, :] ([B, M, d]).  hidden_states NULL is the
+ * vanilla fallback of compute_step_bias.  latent_out [B, M, r] (weight
+ * dtype, may be NULL) receives what project_bias consumed. */
+int dspark_oracle_apply_block_gated(const void* base_logits, int logits_dtype,
+                                    const int64_t* token_ids, const void* hidden,
+                                    int hidden_dtype, int64_t d, const void* w1,
+                                    const void* w2, const void* gate_w,
+                                    const void* gate_b, int weight_dtype, int64_t B,
+                                    int64_t M, int64_t V, int64_t r,
+                                    void* corrected_logits, void* latent_out,
+                                    int n_threads) {
+  if (!valid_dtype(logits_dtype) || !valid_dtype(weight_dtype)) return ORACLE_UNSUPPORTED;
+  if (B < 0 || M < 0 || V < 0 || r <= 0) return ORACLE_INVALID;
+  int64_t rows = B * M;
+  if (rows == 0 || V == 0) return ORACLE_OK;
+  if (!base_logits || !token_ids || !w1 || !w2 || !corrected_logits) return ORACLE_INVALID;
+  for (int64_t n = 0; n < rows; ++n)
+    if (token_ids[n] < 0 || token_ids[n] >= V) return ORACLE_INVALID;
+  size_t wb = weight_dtype == ORACLE_F32 ? 4 : 2;
+  void* lat = malloc((size_t)(rows * r) * wb);
+  if (!lat) return ORACLE_INVALID;
+  int st = ORACLE_OK;
+  if (hidden) {
+    st = dspark_oracle_gated_latent(hidden, hidden_dtype, d, token_ids, w1, gate_w, gate_b,
+                                    weight_dtype, rows, V, r, lat, NULL, NULL, n_threads);
+  } else {
+    for (int64_t n = 0; n < rows; ++n)
+      memcpy((char*)lat + (size_t)(n * r) * wb, (const char*)w1 + (size_t)(token_ids[n] * r) * wb,
+             (size_t)r * wb);
+  }
+  if (st == ORACLE_OK)
+    st = dspark_oracle_apply_rows(base_logits, logits_dtype, lat, w2, weight_dtype, rows, V, r,
+                                  corrected_logits, n_threads);
+  if (st == ORACLE_OK && latent_out) memcpy(latent_out, lat, (size_t)(rows * r) * wb);
+  free(lat);
+  return st;
+}
+
+/* [P5] VanillaMarkov.sample_block_tokens with a GatedMarkovHead: step k
+ * gates with hidden_states[:, k, :] and the previous token (first_prev at
+ * k = 0, the token drawn at k - 1 after that).  hidden NULL is the vanilla
+ * fallback.  latent_out [B, M, r] may be NULL. */
+int dspark_oracle_sample_block_gated(const void* base_logits, int logits_dtype,
+                                     const int64_t* first_prev_token_ids,
+                                     const void* hidden, int hidden_dtype, int64_t d,
+                                     const void* w1, const void* w2, const void* gate_w,
+                                     const void* gate_b, int weight_dtype, int64_t B,
+                                     int64_t M, int64_t V, int64_t r, double temperature,
+                                     uint64_t seed, int64_t position_offset,
+                                     int64_t batch_offset, int64_t* sampled_tokens,
+                                     void* corrected_logits, void* latent_out,
+                                     int n_threads) {
+  if (!valid_dtype(logits_dtype) || !valid_dtype(weight_dtype)) return ORACLE_UNSUPPORTED;
+  if (B < 0 || M < 0 || V < 0 || r <= 0 || isnan(temperature)) return ORACLE_INVALID;
+  if (hidden && !gated_args_ok(hidden_dtype, weight_dtype, d, r)) return ORACLE_INVALID;
+  if (B == 0 || M == 0) return ORACLE_OK;
+  if (V == 0) return ORACLE_INVALID;
+  if (!base_logits || !first_prev_token_ids || !w1 || !w2 || !sampled_tokens)
+    return ORACLE_INVALID;
+  if (hidden && (!gate_w || !gate_b)) return ORACLE_INVALID;
+  for (int64_t b = 0; b < B; ++b)
+    if (first_prev_token_ids[b] < 0 || first_prev_token_ids[b] >= V) return ORACLE_INVALID;
+  double* w2d = w2_as_double(w2, weight_dtype, V, r);
+  if (!w2d) return ORACLE_INVALID;
+  int nt = n_threads_or_default(n_threads);
+  for (int64_t k = 0; k < M; ++k) {
+#pragma omp parallel num_threads(nt)
+    {
+      double* in = (double*)malloc((size_t)((hidden ? d : 0) + r) * sizeof(double));
+      double* e = (double*)malloc((size_t)r * sizeof(double));
+      float* u = (float*)malloc((size_t)r * sizeof(float));
+      float* out = (float*)malloc((size_t)V * sizeof(float));
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t b = 0; b < B; ++b) {
+        int64_t prev = (k == 0) ? first_prev_token_ids[b] : sampled_tokens[b * M + k - 1];
+        int64_t row = b * M + k;
+        if (hidden) {
+          gated_row(hidden, hidden_dtype, row, d, w1, prev, gate_w, gate_b, weight_dtype, r, in,
+                    u, NULL, NULL);
+          for (int64_t j = 0; j < r; ++j) e[j] = (double)u[j];
+        } else {
+          gather_w1_row(w1, weight_dtype, r, prev, e);
+        }
+        if (latent_out)
+          for (int64_t j = 0; j < r; ++j) store_from_float(latent_out, weight_dtype, row * r + j, (float)e[j]);
+        corrected_row_from(base_logits, logits_dtype, row, w2d, weight_dtype, V, r, e, out);
+        if (corrected_logits)
+          for (int64_t v = 0; v < V; ++v)
+            store_from_float(corrected_logits, logits_dtype, row * V + v, out[v]);
+        int64_t tok;
+        select_from_row(out, V, temperature, seed, batch_offset + b, position_offset + k,
+                        &tok, NULL, NULL);
+        sampled_tokens[row] = tok;
+      }
+      free(out);
+      free(u);
+      free(e);
+      free(in);
+    }
+  }
+  free(w2d);
   return ORACLE_OK;
 }

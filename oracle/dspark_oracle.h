@@ -15,6 +15,8 @@
  *        class VanillaMarkov (markov_w1 = nn.Embedding(V, r)).
  *   [P1] NeMo AutoModel API page "models/deepseek_v41/dspark",
  *        class _DeepseekV41DSparkMarkovHead.
+ *   Gated head: [P5] GatedMarkovHead (compute_gate, compute_step_bias) and
+ *        the [P3] API page's GatedMarkovHead (gate_proj = Linear(d + r, r)).
  *
  * Numeric reading (every step is written out in dspark_oracle.c):
  *   e      = W1[x, :]                                (exact, widened to double)
@@ -90,6 +92,54 @@ int dspark_oracle_logit_bounds(const void* base_logits, int logits_dtype,
                                int64_t r, int64_t n, const int64_t* rows,
                                const int64_t* cols, float* lo, float* mid,
                                float* hi);
+
+/* Gated head ([P5]/[P3] GatedMarkovHead): hidden [rows, d] (or [B, M, d]),
+ * gate_w = gate_proj.weight [r, d + r], gate_b = gate_proj.bias [r], both
+ * in the weight dtype.  The latent row u = sigmoid(gate_proj([h; e])) * e,
+ * e = W1[x], is what project_bias consumes.  lo/hi (may be NULL) receive
+ * each latent element's admissible interval for a device that accumulates
+ * in fp32 in any order. */
+int dspark_oracle_gated_latent(const void* hidden, int hidden_dtype, int64_t d,
+                               const int64_t* token_ids, const void* w1,
+                               const void* gate_w, const void* gate_b,
+                               int weight_dtype, int64_t rows, int64_t V,
+                               int64_t r, void* latent, float* lo, float* hi,
+                               int n_threads);
+
+/* Row n of base [rows, V] biased by project_bias(latent[n, :]). */
+int dspark_oracle_apply_rows(const void* base_logits, int logits_dtype,
+                             const void* latent, const void* w2, int weight_dtype,
+                             int64_t rows, int64_t V, int64_t r,
+                             void* corrected_logits, int n_threads);
+
+/* dspark_oracle_logit_bounds with row rows[i] biased by latent[rows[i]]. */
+int dspark_oracle_logit_bounds_rows(const void* base_logits, int logits_dtype,
+                                    const void* latent, const void* w2,
+                                    int weight_dtype, int64_t V, int64_t r,
+                                    int64_t n, const int64_t* rows,
+                                    const int64_t* cols, float* lo, float* mid,
+                                    float* hi);
+
+/* apply_block_logits / sample_block_tokens of a GatedMarkovHead; hidden
+ * NULL is the vanilla fallback.  latent_out [B, M, r] may be NULL. */
+int dspark_oracle_apply_block_gated(const void* base_logits, int logits_dtype,
+                                    const int64_t* token_ids, const void* hidden,
+                                    int hidden_dtype, int64_t d, const void* w1,
+                                    const void* w2, const void* gate_w,
+                                    const void* gate_b, int weight_dtype, int64_t B,
+                                    int64_t M, int64_t V, int64_t r,
+                                    void* corrected_logits, void* latent_out,
+                                    int n_threads);
+int dspark_oracle_sample_block_gated(const void* base_logits, int logits_dtype,
+                                     const int64_t* first_prev_token_ids,
+                                     const void* hidden, int hidden_dtype, int64_t d,
+                                     const void* w1, const void* w2, const void* gate_w,
+                                     const void* gate_b, int weight_dtype, int64_t B,
+                                     int64_t M, int64_t V, int64_t r, double temperature,
+                                     uint64_t seed, int64_t position_offset,
+                                     int64_t batch_offset, int64_t* sampled_tokens,
+                                     void* corrected_logits, void* latent_out,
+                                     int n_threads);
 
 /* Building blocks exposed for pinning. */
 void dspark_oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2],

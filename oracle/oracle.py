@@ -7,7 +7,8 @@ CPU-baseline leg of ``bench.py`` may import this module; the product path
 The oracle follows the DSpark pages step by step (see ``dspark_oracle.c``):
 the third-party ``markov_head.py`` page (module docstring, ``_sample_tokens``,
 ``VanillaMarkov.apply_block_logits`` / ``sample_block_tokens``) and the NeMo
-AutoModel ``speculative/dspark/markov_head`` API page.
+AutoModel ``speculative/dspark/markov_head`` API page; the gated head
+follows ``GatedMarkovHead`` on both pages.
 
 Arrays are numpy: float32 for fp32 data, uint16 bit patterns for bfloat16,
 int64 for token ids.  W1 and W2w are both [V, r] (Embedding weight and
@@ -61,6 +62,21 @@ def lib():
         L.dspark_oracle_logit_bounds.argtypes = [
             _p, _int, _p, _p, _p, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p]
         L.dspark_oracle_logit_bounds.restype = _int
+        L.dspark_oracle_gated_latent.argtypes = [
+            _p, _int, _i64, _p, _p, _p, _p, _int, _i64, _i64, _i64, _p, _p, _p, _int]
+        L.dspark_oracle_gated_latent.restype = _int
+        L.dspark_oracle_apply_rows.argtypes = [_p, _int, _p, _p, _int, _i64, _i64, _i64, _p, _int]
+        L.dspark_oracle_apply_rows.restype = _int
+        L.dspark_oracle_logit_bounds_rows.argtypes = [
+            _p, _int, _p, _p, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p]
+        L.dspark_oracle_logit_bounds_rows.restype = _int
+        L.dspark_oracle_apply_block_gated.argtypes = [
+            _p, _int, _p, _p, _int, _i64, _p, _p, _p, _p, _int, _i64, _i64, _i64, _i64, _p, _p, _int]
+        L.dspark_oracle_apply_block_gated.restype = _int
+        L.dspark_oracle_sample_block_gated.argtypes = [
+            _p, _int, _p, _p, _int, _i64, _p, _p, _p, _p, _int, _i64, _i64, _i64, _i64,
+            ctypes.c_double, ctypes.c_uint64, _i64, _i64, _p, _p, _p, _int]
+        L.dspark_oracle_sample_block_gated.restype = _int
         L.dspark_oracle_philox4x32_10.argtypes = [_p, _p, _p]
         L.dspark_oracle_philox4x32_10.restype = None
         L.dspark_oracle_gumbel2.argtypes = [ctypes.c_uint64, _i64, _i64, _i64]
@@ -166,6 +182,96 @@ def logit_bounds(base, token_ids, w1, w2, rows, cols):
         _ptr(base), _dtype_tag(base), _ptr(token_ids), _ptr(w1), _ptr(w2), _dtype_tag(w1),
         base.shape[-1], w1.shape[1], n, _ptr(rows), _ptr(cols), _ptr(lo), _ptr(mid), _ptr(hi)))
     return lo, mid, hi
+
+
+def _c(a, dtype=None):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def gated_latent(hidden, token_ids, w1, gate_w, gate_b, bounds: bool = False, n_threads: int = 0):
+    """Latent rows sigmoid(gate_proj([h; W1[x]])) * W1[x] of the gated head for
+    hidden [..., d] and token_ids [...] (flattened); returns latent [rows, r]
+    (weight dtype), plus (lo, hi) float32 [rows, r] when bounds is set."""
+    w1, gate_w, gate_b = _c(w1), _c(gate_w), _c(gate_b)
+    d = hidden.shape[-1]
+    hidden = _c(hidden).reshape(-1, d)
+    ids = _c(token_ids, np.int64).reshape(-1)
+    rows, r = ids.shape[0], w1.shape[1]
+    lat = np.zeros((rows, r), dtype=w1.dtype)
+    lo = np.zeros((rows, r), dtype=np.float32) if bounds else None
+    hi = np.zeros((rows, r), dtype=np.float32) if bounds else None
+    _check(lib().dspark_oracle_gated_latent(
+        _ptr(hidden), _dtype_tag(hidden), d, _ptr(ids), _ptr(w1), _ptr(gate_w), _ptr(gate_b),
+        _dtype_tag(w1), rows, w1.shape[0], r, _ptr(lat), _ptr(lo), _ptr(hi), n_threads))
+    return (lat, lo, hi) if bounds else lat
+
+
+def apply_rows(base, latent, w2, n_threads: int = 0):
+    """Corrected rows: base [..., V] row n biased by project_bias(latent[n])."""
+    base, latent, w2 = _c(base), _c(latent), _c(w2)
+    V = base.shape[-1]
+    rows = base.size // V if V else 0
+    out = base.copy()
+    _check(lib().dspark_oracle_apply_rows(
+        _ptr(base), _dtype_tag(base), _ptr(latent), _ptr(w2), _dtype_tag(w2), rows, V,
+        w2.shape[1], _ptr(out), n_threads))
+    return out
+
+
+def logit_bounds_rows(base, latent, w2, rows, cols):
+    """logit_bounds with every row biased by its own latent row."""
+    base, latent, w2 = _c(base), _c(latent), _c(w2)
+    rows, cols = _c(rows, np.int64), _c(cols, np.int64)
+    n = rows.shape[0]
+    lo, mid, hi = (np.zeros(n, dtype=np.float32) for _ in range(3))
+    _check(lib().dspark_oracle_logit_bounds_rows(
+        _ptr(base), _dtype_tag(base), _ptr(latent), _ptr(w2), _dtype_tag(w2), base.shape[-1],
+        w2.shape[1], n, _ptr(rows), _ptr(cols), _ptr(lo), _ptr(mid), _ptr(hi)))
+    return lo, mid, hi
+
+
+def apply_block_gated(base, token_ids, hidden, w1, w2, gate_w, gate_b, n_threads: int = 0,
+                      check: bool = True):
+    """Gated teacher-forced corrected logits; returns (corrected, latent [B, M, r]).
+    hidden None is the vanilla fallback."""
+    base, w1, w2 = _c(base), _c(w1), _c(w2)
+    ids = _c(token_ids, np.int64)
+    hidden, gate_w, gate_b = _c(hidden), _c(gate_w), _c(gate_b)
+    V, M = base.shape[-1], base.shape[-2]
+    B = int(np.prod(base.shape[:-2]))
+    r = w1.shape[1]
+    d = hidden.shape[-1] if hidden is not None else 0
+    out = base.copy()
+    lat = np.zeros(base.shape[:-1] + (r,), dtype=w1.dtype)
+    st = lib().dspark_oracle_apply_block_gated(
+        _ptr(base), _dtype_tag(base), _ptr(ids), _ptr(hidden),
+        _dtype_tag(hidden) if hidden is not None else 0, d, _ptr(w1), _ptr(w2), _ptr(gate_w),
+        _ptr(gate_b), _dtype_tag(w1), B, M, V, r, _ptr(out), _ptr(lat), n_threads)
+    if check:
+        _check(st)
+        return out, lat
+    return st, out, lat
+
+
+def sample_block_gated(base, first_prev, hidden, w1, w2, gate_w, gate_b, temperature=0.0, seed=0,
+                       position_offset=0, batch_offset=0, n_threads: int = 0):
+    """Gated left-to-right sampling; returns (tokens [B, M], corrected, latent [B, M, r])."""
+    base, w1, w2 = _c(base), _c(w1), _c(w2)
+    first = _c(first_prev, np.int64)
+    hidden, gate_w, gate_b = _c(hidden), _c(gate_w), _c(gate_b)
+    B, M, V = base.shape
+    r = w1.shape[1]
+    d = hidden.shape[-1] if hidden is not None else 0
+    tokens = np.zeros((B, M), dtype=np.int64)
+    corrected = base.copy()
+    lat = np.zeros((B, M, r), dtype=w1.dtype)
+    _check(lib().dspark_oracle_sample_block_gated(
+        _ptr(base), _dtype_tag(base), _ptr(first), _ptr(hidden),
+        _dtype_tag(hidden) if hidden is not None else 0, d, _ptr(w1), _ptr(w2), _ptr(gate_w),
+        _ptr(gate_b), _dtype_tag(w1), B, M, V, r, float(temperature), int(seed) & (2**64 - 1),
+        int(position_offset), int(batch_offset), _ptr(tokens), _ptr(corrected), _ptr(lat),
+        n_threads))
+    return tokens, corrected, lat
 
 
 def philox4x32_10(ctr, key):

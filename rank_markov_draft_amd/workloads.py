@@ -47,6 +47,7 @@ class Workload:
     boost: float = 0.0     # added at one random position per (b, k) row
     return_logits: bool = True
     logits_dtype: int = -1  # the logits' dtype when it differs from the weights' (-1: same)
+    hidden: int = 0         # gated head: backbone hidden size d (0: vanilla head)
 
     @property
     def ldtype(self) -> int:
@@ -82,6 +83,14 @@ WORKLOADS = {
     "teacher_forced_320_f32logits": Workload("teacher_forced_320_f32logits", B=64, M=5, V=129280,
                                              r=256, dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=2,
                                              mode="apply", logits_dtype=F32),
+    # Gated head (GatedMarkovHead) at the DeepSeek-V4.1 hidden size 5120:
+    # teacher-forced 320 rows, and a greedy draft of batch 64, block 5.
+    "gated_teacher_forced_320": Workload("gated_teacher_forced_320", B=64, M=5, V=129280, r=256,
+                                         dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=6,
+                                         mode="apply", hidden=5120),
+    "gated_greedy_draft_64x5": Workload("gated_greedy_draft_64x5", B=64, M=5, V=129280, r=256,
+                                        dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=7,
+                                        mode="greedy", boost=6.0, hidden=5120),
     # Large teacher-forced batch: 8 sequences x 64 anchors, rank 512, Zipf ids.
     "teacher_forced_2560_zipf": Workload("teacher_forced_2560_zipf", B=512, M=5, V=129280, r=512,
                                          dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=5,
@@ -109,16 +118,23 @@ def zipf_ids(rng: np.random.Generator, n: int, V: int, s: float) -> np.ndarray:
 
 
 def make_inputs(w: Workload, *, B: int | None = None, M: int | None = None,
-                V: int | None = None, r: int | None = None, seed: int | None = None):
+                V: int | None = None, r: int | None = None, seed: int | None = None,
+                hidden: int | None = None):
     """Draw inputs for workload ``w`` (optionally at other sizes).
 
     Returns a dict of numpy arrays: base [B, M, V], w1 [V, r], w2 [V, r]
     (float32 or uint16 bf16 bits), token_ids [B, M] and first_prev [B] (int64).
+    With a hidden size d (gated head) it also holds hidden [B, M, d] ~ N(0, 1)
+    (a normalised backbone state) and the gate_proj weight [r, d + r] and
+    bias [r], both U(-1/sqrt(d + r), 1/sqrt(d + r)) (nn.Linear's default
+    initialisation), drawn after everything else in that order, in the
+    weight dtype.
     """
     B = w.B if B is None else B
     M = w.M if M is None else M
     V = w.V if V is None else V
     r = w.r if r is None else r
+    d = w.hidden if hidden is None else hidden
     rng = np.random.default_rng(w.seed if seed is None else seed)
     base = rng.standard_normal((B, M, V), dtype=np.float32) * np.float32(w.base_sigma)
     if w.boost and B * M > 0 and V > 0:
@@ -132,8 +148,18 @@ def make_inputs(w: Workload, *, B: int | None = None, M: int | None = None,
     else:
         token_ids = rng.integers(0, max(V, 1), size=(B, M), dtype=np.int64)
     first_prev = rng.integers(0, max(V, 1), size=(B,), dtype=np.int64)
+    out = {"token_ids": token_ids, "first_prev": first_prev}
+    if d:
+        bound = np.float32(1.0 / np.sqrt(d + r))
+        hid = rng.standard_normal((B, M, d), dtype=np.float32)
+        gw = (rng.random((r, d + r), dtype=np.float32) * 2 - 1) * bound
+        gb = (rng.random((r,), dtype=np.float32) * 2 - 1) * bound
+        if w.dtype == BF16:
+            hid, gw, gb = to_bf16_bits(hid), to_bf16_bits(gw), to_bf16_bits(gb)
+        out.update(hidden=hid, gate_w=gw, gate_b=gb)
     if w.ldtype == BF16:
         base = to_bf16_bits(base)
     if w.dtype == BF16:
         w1, w2 = to_bf16_bits(w1), to_bf16_bits(w2)
-    return {"base": base, "w1": w1, "w2": w2, "token_ids": token_ids, "first_prev": first_prev}
+    out.update(base=base, w1=w1, w2=w2)
+    return out

@@ -458,3 +458,191 @@ def test_sampled_tokens_in_range_and_deterministic(oracle_mod):
     c, _ = oracle_mod.sample_block(inp["base"], inp["first_prev"], inp["w1"], inp["w2"], temperature=0.9, seed=4)
     assert np.array_equal(a, b) and not np.array_equal(a, c)
     assert a.min() >= 0 and a.max() < 333
+
+
+# ------------------------------------------------- gated head (GatedMarkovHead)
+def _gated_case(dtype, B=3, M=4, V=300, r=16, d=40, seed=3, hidden_dtype=None):
+    """Small gated-head inputs in `dtype` (weights, logits, hidden unless
+    hidden_dtype says otherwise) with the gate weights zeroed; the tests set
+    the gate entries they need."""
+    w = dataclass_replace(wl.WORKLOADS["gated_teacher_forced_320"], dtype=dtype)
+    inp = wl.make_inputs(w, B=B, M=M, V=V, r=r, hidden=d, seed=seed)
+    inp["gate_w"] = np.zeros_like(inp["gate_w"])
+    inp["gate_b"] = np.zeros_like(inp["gate_b"])
+    if hidden_dtype is not None and hidden_dtype != dtype:
+        conv = wl.to_bf16_bits if hidden_dtype == wl.BF16 else wl.bf16_bits_to_f32
+        inp["hidden"] = conv(inp["hidden"])
+    return inp
+
+
+def _wvals(a, dtype):
+    """float32 values -> arrays of the weight dtype."""
+    a = np.asarray(a, dtype=np.float32)
+    return wl.to_bf16_bits(a) if dtype == wl.BF16 else a
+
+
+def _round_w(x, dtype):
+    """float64 values rounded to fp32, then (bf16) by torch's conversion."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    return as_float(wl.to_bf16_bits(x32)) if dtype == wl.BF16 else x32
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_gated_zero_gate_halves_the_embedding(oracle_mod, dtype):
+    """gate_proj = 0: sigmoid(0) = 1/2 exactly, so the latent is W1[x] / 2 and
+    the corrected logits equal the vanilla head's with W2 halved (exact)."""
+    inp = _gated_case(dtype)
+    lat = oracle_mod.gated_latent(inp["hidden"], inp["token_ids"], inp["w1"], inp["gate_w"], inp["gate_b"])
+    e = as_float(inp["w1"])[inp["token_ids"].reshape(-1)]
+    assert np.array_equal(as_float(lat), e / 2)
+    out, lat2 = oracle_mod.apply_block_gated(inp["base"], inp["token_ids"], inp["hidden"], inp["w1"],
+                                             inp["w2"], inp["gate_w"], inp["gate_b"])
+    van = oracle_mod.apply_block(inp["base"], inp["token_ids"], inp["w1"], _wvals(as_float(inp["w2"]) / 2, dtype))
+    assert np.array_equal(as_float(out), as_float(van))
+    assert np.array_equal(as_float(lat2).reshape(lat.shape), as_float(lat))
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_gated_open_gate_is_vanilla(oracle_mod, dtype):
+    """gate bias +40: sigmoid rounds to 1 in fp32, so the gated head is the
+    vanilla head (apply and sampling); hidden_states None is the vanilla
+    fallback whatever the gate."""
+    inp = _gated_case(dtype)
+    inp["gate_b"] = _wvals(np.full(inp["gate_b"].shape, 40.0), dtype)
+    out, lat = oracle_mod.apply_block_gated(inp["base"], inp["token_ids"], inp["hidden"], inp["w1"],
+                                            inp["w2"], inp["gate_w"], inp["gate_b"])
+    van = oracle_mod.apply_block(inp["base"], inp["token_ids"], inp["w1"], inp["w2"])
+    assert np.array_equal(as_float(out), as_float(van))
+    assert np.array_equal(as_float(lat), as_float(inp["w1"])[inp["token_ids"]])
+    for T in (0.0, 0.7):
+        tv, cv = oracle_mod.sample_block(inp["base"], inp["first_prev"], inp["w1"], inp["w2"], T, seed=5)
+        tg, cg, _ = oracle_mod.sample_block_gated(inp["base"], inp["first_prev"], inp["hidden"], inp["w1"],
+                                                  inp["w2"], inp["gate_w"], inp["gate_b"], T, seed=5)
+        assert np.array_equal(tv, tg) and np.array_equal(as_float(cv), as_float(cg))
+    rng = np.random.default_rng(0)
+    inp["gate_w"] = _wvals(rng.standard_normal(inp["gate_w"].shape), dtype)
+    out0, lat0 = oracle_mod.apply_block_gated(inp["base"], inp["token_ids"], None, inp["w1"], inp["w2"],
+                                              inp["gate_w"], inp["gate_b"])
+    assert np.array_equal(as_float(out0), as_float(van))
+    assert np.array_equal(as_float(lat0), as_float(inp["w1"])[inp["token_ids"]])
+    tv, cv = oracle_mod.sample_block(inp["base"], inp["first_prev"], inp["w1"], inp["w2"], 0.0)
+    tg, cg, _ = oracle_mod.sample_block_gated(inp["base"], inp["first_prev"], None, inp["w1"], inp["w2"],
+                                              inp["gate_w"], inp["gate_b"], 0.0)
+    assert np.array_equal(tv, tg) and np.array_equal(as_float(cv), as_float(cg))
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_gated_closed_gate_leaves_base(oracle_mod, dtype):
+    """gate bias -40: the gate is sigmoid(-40) ~ 4.2e-18 (not 1 - that: the
+    sign of the logistic is pinned), the latent keeps the sign of W1[x] at
+    that scale, and the corrected logits equal the base logits."""
+    inp = _gated_case(dtype)
+    inp["gate_b"] = _wvals(np.full(inp["gate_b"].shape, -40.0), dtype)
+    out, lat = oracle_mod.apply_block_gated(inp["base"], inp["token_ids"], inp["hidden"], inp["w1"],
+                                            inp["w2"], inp["gate_w"], inp["gate_b"])
+    e = as_float(inp["w1"])[inp["token_ids"]]
+    u = as_float(lat)
+    assert np.all(np.sign(u) == np.sign(e))
+    assert np.all(np.abs(u) <= 5e-18 * np.abs(e)) and np.all(np.abs(u) >= 3e-18 * np.abs(e))
+    assert np.array_equal(as_float(out), as_float(inp["base"]))
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("part", ["hidden-first", "hidden-last", "emb-first", "emb-last"])
+@pytest.mark.parametrize("j0", [0, 15])
+def test_gated_single_gate_entry(oracle_mod, dtype, part, j0):
+    """One nonzero gate_proj weight Gw[j0, i0]: output j0 sees z = c * in[i0]
+    with in = [h; W1[x]] (hidden first), every other output sees z = 0.  The
+    logistic is torch.sigmoid in float64, then the fp32 and bf16 roundings
+    by torch's conversion.  Pins the concatenation order, the orientation of
+    Gw, both ends of the K range and the row of h each (b, k) uses."""
+    B, M, V, r, d = 3, 4, 300, 16, 40
+    inp = _gated_case(dtype, B=B, M=M, V=V, r=r, d=d)
+    i0 = {"hidden-first": 0, "hidden-last": d - 1, "emb-first": d, "emb-last": d + r - 1}[part]
+    c = 0.75
+    gw = np.zeros((r, d + r), dtype=np.float32)
+    gw[j0, i0] = c
+    inp["gate_w"] = _wvals(gw, dtype)
+    lat = as_float(oracle_mod.gated_latent(inp["hidden"], inp["token_ids"], inp["w1"], inp["gate_w"],
+                                           inp["gate_b"]))
+    ids = inp["token_ids"].reshape(-1)
+    e = as_float(inp["w1"])[ids]
+    h = as_float(inp["hidden"]).reshape(-1, d)
+    x_in = h[:, i0] if i0 < d else e[:, i0 - d]
+    z = _round_w(np.float64(c) * x_in.astype(np.float64), dtype)
+    g = _round_w(torch.sigmoid(torch.from_numpy(z.astype(np.float64))).numpy(), dtype)
+    want = e / 2
+    want[:, j0] = _round_w(g.astype(np.float64) * e[:, j0].astype(np.float64), dtype)
+    assert np.array_equal(lat, want)
+    # sampling: step k of row b gates with hidden[b, k] and the previous token
+    toks, _, slat = oracle_mod.sample_block_gated(inp["base"], inp["first_prev"], inp["hidden"], inp["w1"],
+                                                  inp["w2"], inp["gate_w"], inp["gate_b"], 0.0)
+    prev = np.concatenate([inp["first_prev"][:, None], toks[:, :-1]], axis=1).reshape(-1)
+    e = as_float(inp["w1"])[prev]
+    x_in = h[:, i0] if i0 < d else e[:, i0 - d]
+    z = _round_w(np.float64(c) * x_in.astype(np.float64), dtype)
+    g = _round_w(torch.sigmoid(torch.from_numpy(z.astype(np.float64))).numpy(), dtype)
+    want = e / 2
+    want[:, j0] = _round_w(g.astype(np.float64) * e[:, j0].astype(np.float64), dtype)
+    assert np.array_equal(as_float(slat).reshape(-1, r), want)
+
+
+def test_gated_hidden_cast_to_weight_dtype(oracle_mod):
+    """fp32 hidden states with bf16 weights are rounded to bf16 before the
+    gate (compute_gate casts both concatenated operands to the gate weight's
+    dtype): h0 = 1 + 2^-8 + 2^-12 becomes 1 + 2^-7, so with Gw[0, 0] = 8,
+    Gw[0, 1] = -8 and h1 = 1 the gate input is exactly 1/16."""
+    inp = _gated_case(wl.BF16, hidden_dtype=wl.F32)
+    h = inp["hidden"]
+    h[..., 0] = np.float32(1 + 2**-8 + 2**-12)
+    h[..., 1] = 1.0
+    gw = np.zeros(inp["gate_w"].shape, dtype=np.float32)
+    gw[0, 0], gw[0, 1] = 8.0, -8.0
+    inp["gate_w"] = wl.to_bf16_bits(gw)
+    lat = as_float(oracle_mod.gated_latent(h, inp["token_ids"], inp["w1"], inp["gate_w"], inp["gate_b"]))
+    e = as_float(inp["w1"])[inp["token_ids"].reshape(-1)]
+    g = _round_w(1.0 / (1.0 + math.exp(-1.0 / 16)), wl.BF16)
+    assert float(g.item()) == 0.515625   # bf16 of sigmoid(1/16); sigmoid(0.0332) would give 0.5078
+    assert np.array_equal(lat[:, 0], _round_w(np.float64(g.item()) * e[:, 0].astype(np.float64), wl.BF16))
+    # bf16 hidden with fp32 weights: widened exactly
+    inp2 = _gated_case(wl.F32, hidden_dtype=wl.BF16)
+    a = oracle_mod.gated_latent(inp2["hidden"], inp2["token_ids"], inp2["w1"], inp2["gate_w"], inp2["gate_b"])
+    b = oracle_mod.gated_latent(wl.bf16_bits_to_f32(inp2["hidden"]), inp2["token_ids"], inp2["w1"],
+                                inp2["gate_w"], inp2["gate_b"])
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_gated_latent_bounds_bracket(oracle_mod, dtype):
+    """With random gate weights the latent's admissible interval brackets the
+    oracle's own value and stays narrow: bf16 latents are mostly pinned to
+    one value, fp32 ones to a relative width under 1e-3."""
+    w = dataclass_replace(wl.WORKLOADS["gated_teacher_forced_320"], dtype=dtype)
+    inp = wl.make_inputs(w, B=2, M=3, V=500, r=32, hidden=256, seed=9)
+    lat, lo, hi = oracle_mod.gated_latent(inp["hidden"], inp["token_ids"], inp["w1"], inp["gate_w"],
+                                          inp["gate_b"], bounds=True)
+    u = as_float(lat)
+    assert np.all(lo <= u) and np.all(u <= hi)
+    if dtype == wl.BF16:
+        assert np.mean(lo == hi) > 0.9
+    else:
+        assert np.all(hi - lo <= 1e-3 * np.abs(u))
+    # the gate is not degenerate: latent / embedding spreads inside (0, 1)
+    e = as_float(inp["w1"])[inp["token_ids"].reshape(-1)]
+    ratio = u[e != 0] / e[e != 0]
+    assert 0.05 < ratio.min() and ratio.max() < 0.95 and ratio.std() > 0.05
+
+
+@pytest.mark.parametrize("T", [0.0, 0.7])
+def test_gated_chain_equals_teacher_forced(oracle_mod, T):
+    """A gated chain's corrected logits equal the gated teacher-forced apply
+    on its own predecessors (first_prev, then the drawn tokens)."""
+    w = wl.WORKLOADS["gated_teacher_forced_320"]
+    inp = wl.make_inputs(w, B=3, M=4, V=700, r=16, hidden=64, seed=4)
+    toks, corr, lat = oracle_mod.sample_block_gated(inp["base"], inp["first_prev"], inp["hidden"], inp["w1"],
+                                                    inp["w2"], inp["gate_w"], inp["gate_b"], T, seed=3)
+    prev = np.concatenate([inp["first_prev"][:, None], toks[:, :-1]], axis=1)
+    out, lat2 = oracle_mod.apply_block_gated(inp["base"], prev, inp["hidden"], inp["w1"], inp["w2"],
+                                             inp["gate_w"], inp["gate_b"])
+    assert np.array_equal(as_float(corr), as_float(out))
+    assert np.array_equal(as_float(lat), as_float(lat2))
