@@ -123,6 +123,15 @@ def algorithmic_bytes_apply(w) -> int:
     return w.B * w.M * w.V * lb * 2 + w.V * w.r * wb + w.B * w.M * (w.r * wb + 8)
 
 
+def algorithmic_bytes_gate(w) -> int:
+    """Extra bytes of the gated head: hidden states read, gate_proj weight and
+    bias read once (the latent rows stay in cache-sized scratch)."""
+    if not w.hidden:
+        return 0
+    wb = 2 if w.dtype == 1 else 4
+    return w.B * w.M * w.hidden * wb + w.r * (w.hidden + w.r) * wb + w.r * wb
+
+
 def to_dev(a, torch, np):
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
@@ -174,16 +183,24 @@ def measure_extra(name, rmd, wl, torch, np, steps=10, warmup=3):
     n_sets = max(2, int(np.ceil(600e6 / per_set)))
     sets = []
     for i in range(n_sets):
-        d = {k: to_dev(inp[k], torch, np) for k in ("base", "first_prev", "token_ids", "w1", "w2")}
+        keys = ("base", "first_prev", "token_ids", "w1", "w2") + (("hidden", "gate_w", "gate_b") if w.hidden else ())
+        d = {k: to_dev(inp[k], torch, np) for k in keys}
         d["out"] = torch.empty_like(d["base"]) if (w.mode == "apply" or w.return_logits) else None
         d["tok"] = torch.empty((w.B, w.M), dtype=torch.int64, device="cuda")
-        d["ws"] = rmd.Workspace(w.B, w.M, w.V, w.r, sample=(w.mode != "apply"))
+        d["ws"] = rmd.Workspace(w.B, w.M, w.V, w.r, sample=(w.mode != "apply"), hidden=w.hidden or None)
         sets.append(d)
     del inp
 
     def call(i):
         d = sets[i]
-        if w.mode == "apply":
+        if w.hidden and w.mode == "apply":
+            rmd.apply_block_logits_gated(d["base"], d["token_ids"], d["w1"], d["w2"], d["gate_w"], d["gate_b"],
+                                         d["hidden"], out=d["out"], workspace=d["ws"])
+        elif w.hidden:
+            rmd.sample_block_tokens_gated(d["base"], d["first_prev"], d["w1"], d["w2"], d["gate_w"], d["gate_b"],
+                                          d["hidden"], w.temperature, seed=w.gumbel_seed,
+                                          return_logits=w.return_logits, workspace=d["ws"])
+        elif w.mode == "apply":
             rmd.apply_block_logits(d["base"], d["token_ids"], d["w1"], d["w2"], out=d["out"], workspace=d["ws"])
         else:
             rmd.sample_block_tokens(d["base"], d["first_prev"], d["w1"], d["w2"], w.temperature,
@@ -193,6 +210,7 @@ def measure_extra(name, rmd, wl, torch, np, steps=10, warmup=3):
     wall, per = time_calls(call, n_sets, steps, warmup, torch)
     ms = float(np.mean(per))
     alg = algorithmic_bytes_apply(w) if w.mode == "apply" else algorithmic_bytes_sample(w, w.return_logits)
+    alg += algorithmic_bytes_gate(w)
     res = {"ms_per_call": ms, "elems_per_s": w.B * w.M * w.V / (ms * 1e-3),
            "algorithmic_GBps": alg / (ms * 1e-3) / 1e9,
            "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": alg}
@@ -290,7 +308,8 @@ def main():
     if not args.no_extra:
         result["other_workloads"] = {n: measure_extra(n, rmd, wl, torch, np) for n in
                                      ("teacher_forced_320", "teacher_forced_2560_zipf", "temperature_draft_256x8",
-                                      "teacher_forced_320_f32logits")}
+                                      "teacher_forced_320_f32logits", "gated_teacher_forced_320",
+                                      "gated_greedy_draft_64x5")}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, np)
     print(json.dumps(result))

@@ -11,7 +11,8 @@
  * "speculative/dspark/markov_head" page, class VanillaMarkov; NeMo AutoModel
  * "models/deepseek_v41/dspark" page, class _DeepseekV41DSparkMarkovHead).
  *
- * Two operations mirror VanillaMarkov's two methods:
+ * Two operations mirror VanillaMarkov's two methods (each also has a gated
+ * form for GatedMarkovHead, declared further down):
  *   dspark_markov_apply_block   -- apply_block_logits (teacher-forced: every
  *                                  row biased by its own given predecessor);
  *   dspark_markov_sample_block  -- sample_block_tokens (left to right: each
@@ -120,6 +121,53 @@ dspark_status_t dspark_markov_sample_block(const void* base_logits, dspark_dtype
                                            int64_t position_offset, int64_t batch_offset,
                                            int64_t* sampled_tokens, void* corrected_logits,
                                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Gated head (GatedMarkovHead, on the third-party markov_head.py page and
+ * the NeMo AutoModel "speculative/dspark/markov_head" page).  The bias of a
+ * row is W2 . u with the latent row
+ *     u = sigmoid(gate_proj([h; W1[x]])) * W1[x],
+ * gate_proj = Linear(d + r, r) with a bias; h is the row's backbone hidden
+ * state [d] and both concatenated operands are cast to the weight dtype
+ * (compute_gate).  Rounding (weight dtype W): the gate's fp32 accumulator
+ * plus bias rounded to W, the fp32 logistic of that rounded to W, the fp32
+ * product with W1[x] rounded to W; then the vanilla numerics with u in place
+ * of W1[x].  hidden_states NULL is the pages' vanilla fallback (u = W1[x]);
+ * gate_weight and gate_bias are then ignored and may be NULL.
+ *   hidden_states  device, [B, M, d], hidden_dtype (F32 or BF16): row (b, k)
+ *                  gates position k of row b.
+ *   gate_weight    device, [r, d + r] (the Linear weight), weight_dtype.
+ *   gate_bias      device, [r], weight_dtype.
+ *   latent_out     device, [B, M, r], weight_dtype, or NULL: receives u
+ *                  (the vector project_bias consumed) for every row; for
+ *                  the vanilla fallback that is the embedding W1[x] the
+ *                  DeepSeek-V4.1 head returns beside its logits.
+ * Token ids outside [0, V) give u = 0 (a zero bias) and are counted as in
+ * the vanilla calls.  Other arguments as in dspark_markov_apply_block and
+ * dspark_markov_sample_block; d > 0 when hidden_states is given.  The
+ * workspace must hold dspark_markov_gated_workspace_bytes(...) bytes; the
+ * gated calls need it zero-filled once, like the vanilla ones. */
+size_t dspark_markov_gated_workspace_bytes(int64_t B, int64_t M, int64_t V, int64_t r, int64_t d,
+                                           int sample_mode);
+
+dspark_status_t dspark_markov_apply_block_gated(
+    const void* base_logits, dspark_dtype_t logits_dtype, const int64_t* token_ids,
+    const void* hidden_states, dspark_dtype_t hidden_dtype, int64_t d, const void* w1,
+    const void* w2, const void* gate_weight, const void* gate_bias, dspark_dtype_t weight_dtype,
+    int64_t B, int64_t M, int64_t V, int64_t r, void* corrected_logits, void* latent_out,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Left-to-right sampling with the gated head: step k gates with
+ * hidden_states[:, k, :] and the previous token (sample_block_tokens hands
+ * each step its position's hidden state).  Noise and outputs as in
+ * dspark_markov_sample_block; latent_out [B, M, r] or NULL. */
+dspark_status_t dspark_markov_sample_block_gated(
+    const void* base_logits, dspark_dtype_t logits_dtype, const int64_t* first_prev_token_ids,
+    const void* hidden_states, dspark_dtype_t hidden_dtype, int64_t d, const void* w1,
+    const void* w2, const void* gate_weight, const void* gate_bias, dspark_dtype_t weight_dtype,
+    int64_t B, int64_t M, int64_t V, int64_t r, double temperature, uint64_t seed,
+    int64_t position_offset, int64_t batch_offset, int64_t* sampled_tokens,
+    void* corrected_logits, void* latent_out, void* workspace, size_t workspace_bytes,
+    void* stream);
 
 /* Synchronises `stream`, then returns in *bad_rows the number of rows whose
  * predecessor id was outside [0, V) in the calls made with this workspace

@@ -9,6 +9,10 @@ VanillaMarkov methods (third-party markov_head.py page):
   temperature=0.0, ...)`` -- left-to-right sampling, each position biased by
   the token drawn at the previous one.
 
+The gated head (the pages' GatedMarkovHead) has the same two operations,
+``apply_block_logits_gated`` and ``sample_block_tokens_gated``, which also
+take the backbone hidden states and the gate_proj weight and bias.
+
 Tensors must live on the current HIP device.  ``w1`` is the Embedding
 weight [V, r]; ``w2`` is the Linear(r, V) weight [V, r].  This module only
 marshals arguments (dtype tags, pointers, sizes, the current stream) and
@@ -24,8 +28,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["apply_block_logits", "sample_block_tokens", "Workspace", "read_device_error",
-           "workspace_bytes"]
+__all__ = ["apply_block_logits", "sample_block_tokens", "apply_block_logits_gated",
+           "sample_block_tokens_gated", "Workspace", "read_device_error", "workspace_bytes"]
 
 
 def _dtype_tag(t: torch.Tensor) -> int:
@@ -44,19 +48,25 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def workspace_bytes(B: int, M: int, V: int, r: int, sample: bool) -> int:
-    return int(_lib.load().dspark_markov_workspace_bytes(B, M, V, r, 1 if sample else 0))
+def workspace_bytes(B: int, M: int, V: int, r: int, sample: bool, hidden: int | None = None) -> int:
+    """Workspace bytes of a call; ``hidden`` (the hidden size d, or 0 for the
+    gated calls' vanilla fallback) sizes it for the gated calls."""
+    if hidden is None:
+        return int(_lib.load().dspark_markov_workspace_bytes(B, M, V, r, 1 if sample else 0))
+    return int(_lib.load().dspark_markov_gated_workspace_bytes(B, M, V, r, hidden, 1 if sample else 0))
 
 
 class Workspace:
-    """Device workspace for a family of calls of at most the given sizes.
+    """Device workspace for a family of calls of at most the given sizes
+    (``hidden``: the hidden size of gated calls).
 
     Zero-filled once at creation; the library leaves it ready for the next
     call.  Calls sharing one workspace must be ordered on one stream."""
 
-    def __init__(self, B: int, M: int, V: int, r: int, sample: bool, device=None):
+    def __init__(self, B: int, M: int, V: int, r: int, sample: bool, device=None,
+                 hidden: int | None = None):
         device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-        self.nbytes = max(workspace_bytes(B, M, V, r, sample), 256)
+        self.nbytes = max(workspace_bytes(B, M, V, r, sample, hidden), 256)
         self.buffer = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
         _lib.check(_lib.load().dspark_markov_workspace_init(
             _ptr(self.buffer), self.nbytes, _stream_handle(device)), "workspace_init")
@@ -159,3 +169,112 @@ def sample_block_tokens(base_logits: torch.Tensor, first_prev_token_ids: torch.T
         _ptr(tokens_out), _ptr(corrected), workspace.ptr, workspace.nbytes, _stream_handle(dev))
     _lib.check(st, "sample_block_tokens")
     return tokens_out, corrected
+
+
+def _check_gate(hidden_states, gate_weight, gate_bias, lead, d_expected_rows, r, wdtype):
+    if hidden_states is None:
+        return 0
+    if tuple(hidden_states.shape[:-1]) != tuple(lead):
+        raise ValueError(f"hidden_states {tuple(hidden_states.shape)} must be {tuple(lead)} + (d,)")
+    d = hidden_states.shape[-1]
+    if gate_weight is None or gate_bias is None:
+        raise ValueError("the gated head needs gate_weight [r, d + r] and gate_bias [r]")
+    if tuple(gate_weight.shape) != (r, d + r) or tuple(gate_bias.shape) != (r,):
+        raise ValueError(f"gate_weight must be [{r}, {d + r}] and gate_bias [{r}]")
+    if gate_weight.dtype != wdtype or gate_bias.dtype != wdtype:
+        raise TypeError("gate_weight and gate_bias must have the dtype of w1 and w2")
+    return d
+
+
+def apply_block_logits_gated(base_logits: torch.Tensor, token_ids: torch.Tensor, w1: torch.Tensor,
+                             w2: torch.Tensor, gate_weight: torch.Tensor | None,
+                             gate_bias: torch.Tensor | None, hidden_states: torch.Tensor | None, *,
+                             out: torch.Tensor | None = None, return_latent: bool = False,
+                             workspace: Workspace | None = None):
+    """Teacher-forced corrected logits of the gated head (GatedMarkovHead):
+    base[..., M, V] + W2 (sigmoid(gate_proj([h; W1[x]])) * W1[x]).
+
+    ``hidden_states`` [..., M, d]; None is the pages' vanilla fallback.
+    Returns the corrected logits, and with ``return_latent`` also the latent
+    rows [..., M, r] the projection consumed."""
+    _check_weights(w1, w2)
+    if base_logits.dim() < 2:
+        raise ValueError("base_logits must be [..., M, V]")
+    V, M = base_logits.shape[-1], base_logits.shape[-2]
+    B = 1
+    for s_ in base_logits.shape[:-2]:
+        B *= int(s_)
+    if tuple(token_ids.shape) != tuple(base_logits.shape[:-1]):
+        raise ValueError(f"token_ids {tuple(token_ids.shape)} must be base_logits.shape[:-1]")
+    if w1.shape[0] != V:
+        raise ValueError(f"weights have vocabulary {w1.shape[0]}, logits {V}")
+    r = w1.shape[1]
+    d = _check_gate(hidden_states, gate_weight, gate_bias, base_logits.shape[:-1], None, r, w1.dtype)
+    dev = base_logits.device
+    latent = torch.empty(tuple(base_logits.shape[:-1]) + (r,), dtype=w1.dtype, device=dev) if return_latent else None
+    if base_logits.numel() == 0:
+        res = base_logits if out is None else out
+        return (res, latent) if return_latent else res
+    base_c = base_logits.contiguous()
+    ids = token_ids.to(torch.int64).contiguous()
+    w1c, w2c = w1.contiguous(), w2.contiguous()
+    hc = hidden_states.contiguous() if hidden_states is not None else None
+    gwc = gate_weight.contiguous() if hc is not None else None
+    gbc = gate_bias.contiguous() if hc is not None else None
+    if out is None:
+        out = torch.empty_like(base_c)
+    elif out.shape != base_logits.shape or out.dtype != base_logits.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like base_logits")
+    if workspace is None:
+        workspace = Workspace(B, M, V, r, sample=False, device=dev, hidden=d)
+    st = _lib.load().dspark_markov_apply_block_gated(
+        _ptr(base_c), _dtype_tag(base_c), _ptr(ids), _ptr(hc), _dtype_tag(hc) if hc is not None else 0, d,
+        _ptr(w1c), _ptr(w2c), _ptr(gwc), _ptr(gbc), _dtype_tag(w1c), B, M, V, r, _ptr(out), _ptr(latent),
+        workspace.ptr, workspace.nbytes, _stream_handle(dev))
+    _lib.check(st, "apply_block_logits_gated")
+    return (out, latent) if return_latent else out
+
+
+def sample_block_tokens_gated(base_logits: torch.Tensor, first_prev_token_ids: torch.Tensor,
+                              w1: torch.Tensor, w2: torch.Tensor, gate_weight: torch.Tensor | None,
+                              gate_bias: torch.Tensor | None, hidden_states: torch.Tensor | None,
+                              temperature: float | None = 0.0, *, seed: int = 0, position_offset: int = 0,
+                              batch_offset: int = 0, return_logits: bool = True,
+                              return_latent: bool = False, workspace: Workspace | None = None):
+    """Left-to-right sampling with the gated head; step k gates with
+    hidden_states[:, k, :] ([B, M, d]; None: vanilla fallback) and the token
+    drawn at k - 1.  Returns (tokens [B, M], corrected [B, M, V] or None) and,
+    with ``return_latent``, the latent rows [B, M, r] as a third item."""
+    _check_weights(w1, w2)
+    if base_logits.dim() != 3:
+        raise ValueError("base_logits must be [B, M, V]")
+    B, M, V = base_logits.shape
+    if tuple(first_prev_token_ids.shape) != (B,):
+        raise ValueError("first_prev_token_ids must be [B]")
+    if w1.shape[0] != V:
+        raise ValueError(f"weights have vocabulary {w1.shape[0]}, logits {V}")
+    r = w1.shape[1]
+    d = _check_gate(hidden_states, gate_weight, gate_bias, (B, M), None, r, w1.dtype)
+    T = 0.0 if temperature is None else float(temperature)
+    dev = base_logits.device
+    tokens = torch.empty((B, M), dtype=torch.int64, device=dev)
+    latent = torch.empty((B, M, r), dtype=w1.dtype, device=dev) if return_latent else None
+    if M == 0 or B == 0:
+        res = (tokens, base_logits if return_logits else None)
+        return res + (latent,) if return_latent else res
+    base_c = base_logits.contiguous()
+    first = first_prev_token_ids.to(torch.int64).contiguous()
+    w1c, w2c = w1.contiguous(), w2.contiguous()
+    hc = hidden_states.contiguous() if hidden_states is not None else None
+    gwc = gate_weight.contiguous() if hc is not None else None
+    gbc = gate_bias.contiguous() if hc is not None else None
+    corrected = torch.empty_like(base_c) if return_logits else None
+    if workspace is None:
+        workspace = Workspace(B, M, V, r, sample=True, device=dev, hidden=d)
+    st = _lib.load().dspark_markov_sample_block_gated(
+        _ptr(base_c), _dtype_tag(base_c), _ptr(first), _ptr(hc), _dtype_tag(hc) if hc is not None else 0, d,
+        _ptr(w1c), _ptr(w2c), _ptr(gwc), _ptr(gbc), _dtype_tag(w1c), B, M, V, r, T, int(seed) & (2**64 - 1),
+        int(position_offset), int(batch_offset), _ptr(tokens), _ptr(corrected), _ptr(latent),
+        workspace.ptr, workspace.nbytes, _stream_handle(dev))
+    _lib.check(st, "sample_block_tokens_gated")
+    return (tokens, corrected, latent) if return_latent else (tokens, corrected)

@@ -107,6 +107,55 @@ dspark_status_t check_common(int ldt, int wdt, int64_t B, int64_t M, int64_t V, 
   return DSPARK_OK;
 }
 
+// ---- gated head
+// Gated-call workspace past the vanilla layout: the latent rows of one
+// launch (fp32 or bf16, [rows, r]), then the split-K partial sums of the
+// gate GEMM ([S][rows][r] fp32).
+size_t gated_region_bytes(int64_t rows, int64_t r, int64_t d) {
+  int64_t kchunk = 0;
+  const int S = d > 0 ? dspark::gate_splits(rows, r, d, &kchunk) : 0;
+  return align256((size_t)(rows * r) * 4) + align256((size_t)S * (size_t)(rows * r) * 4);
+}
+
+dspark_status_t check_gate_args(bool gated, int hdt, int64_t d, const void* gw, const void* gb, int64_t rows,
+                                int64_t r) {
+  if (!gated) return DSPARK_OK;
+  if (!known_dtype(hdt) || d <= 0) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!gw || !gb) return DSPARK_ERR_INVALID_ARGUMENT;
+  int64_t t = 0, k = 0;
+  if (!mul_ok(rows, d, &t) || !mul_ok(t, 4, &t) || !mul_ok(d + r, r, &k)) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (d > (int64_t)0x7FFFFFFF || k > (int64_t)0x3FFFFFFF) return DSPARK_ERR_UNSUPPORTED;
+  return DSPARK_OK;
+}
+
+// Gate launch of `rows` rows: apply (ids = token_ids, hidden row n) or
+// sampling step k (first_prev / tokens, hidden row b * M + k).  `region` is
+// the gated workspace region: latent scratch first, then the partials.
+void fill_gate(dspark::GateParams& g, const void* hidden, dspark_dtype_t hdt, int64_t d, const int64_t* ids,
+               const int64_t* tokens, const void* w1, const void* gw, const void* gb, int64_t rows, int64_t V,
+               int64_t r, int64_t M, int64_t k, char* region, void* latent, int64_t latent_ld, int mode,
+               bool gated) {
+  g.hidden = hidden;
+  g.ids = ids;
+  g.tokens = tokens;
+  g.w1 = w1;
+  g.gw = gw;
+  g.gb = gb;
+  g.latent = latent;
+  g.rows = rows;
+  g.V = V;
+  g.r = r;
+  g.d = gated ? d : 0;
+  g.M = M;
+  g.k = k;
+  g.latent_ld = latent_ld;
+  g.mode = mode;
+  g.gated = gated ? 1 : 0;
+  g.partials = (float*)(region + align256((size_t)(rows * r) * 4));
+  g.hidden_bytes = gated ? (mode == dspark::MODE_APPLY ? rows : rows * M) * d * (int64_t)dtype_bytes(hdt) : 0;
+  g.S = gated ? dspark::gate_splits(rows, r, d, &g.kchunk) : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -293,6 +342,208 @@ dspark_status_t dspark_markov_sample_block(const void* base_logits, dspark_dtype
       e = dspark::launch_generic(p, logits_dtype == DSPARK_BF16, weight_dtype == DSPARK_BF16, s);
     }
     if (e != hipSuccess) return device_failure(e, "sample step launch");
+    e = dspark::launch_reduce(p.partials, p.nparts, B, M, k, sampled_tokens, s);
+    if (e != hipSuccess) return device_failure(e, "sample reduce launch");
+  }
+  return DSPARK_OK;
+}
+
+size_t dspark_markov_gated_workspace_bytes(int64_t B, int64_t M, int64_t V, int64_t r, int64_t d,
+                                           int sample_mode) {
+  const size_t base = align256(dspark_markov_workspace_bytes(B, M, V, r, sample_mode));
+  if (B < 0 || M < 0 || V < 0 || r <= 0 || d < 0) return base;
+  return base + gated_region_bytes(sample_mode ? B : B * M, r, d);
+}
+
+dspark_status_t dspark_markov_apply_block_gated(
+    const void* base_logits, dspark_dtype_t logits_dtype, const int64_t* token_ids,
+    const void* hidden_states, dspark_dtype_t hidden_dtype, int64_t d, const void* w1,
+    const void* w2, const void* gate_weight, const void* gate_bias, dspark_dtype_t weight_dtype,
+    int64_t B, int64_t M, int64_t V, int64_t r, void* corrected_logits, void* latent_out,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t elems = 0;
+  dspark_status_t st = check_common(logits_dtype, weight_dtype, B, M, V, r, &elems);
+  if (st != DSPARK_OK) return st;
+  const bool gated = hidden_states != nullptr;
+  st = check_gate_args(gated, hidden_dtype, d, gate_weight, gate_bias, B * M, r);
+  if (st != DSPARK_OK) return st;
+  if (elems == 0) return DSPARK_OK;
+  if (!gated && !latent_out)  // the vanilla fallback
+    return dspark_markov_apply_block(base_logits, logits_dtype, token_ids, w1, w2, weight_dtype, B, M, V,
+                                     r, corrected_logits, workspace, workspace_bytes, stream);
+  if (!base_logits || !token_ids || !w1 || !w2 || !corrected_logits) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < dspark_markov_gated_workspace_bytes(B, M, V, r, gated ? d : 0, 0))
+    return DSPARK_ERR_WORKSPACE_TOO_SMALL;
+  const int64_t rows = B * M;
+  const size_t lbytes = (size_t)elems * dtype_bytes(logits_dtype);
+  const size_t wbytes = (size_t)(V * r) * dtype_bytes(weight_dtype);
+  const size_t ubytes = (size_t)(rows * r) * dtype_bytes(weight_dtype);
+  const size_t hbytes = gated ? (size_t)(rows * d) * dtype_bytes(hidden_dtype) : 0;
+  const size_t gwbytes = gated ? (size_t)(r * (d + r)) * dtype_bytes(weight_dtype) : 0;
+  const size_t gbbytes = gated ? (size_t)r * dtype_bytes(weight_dtype) : 0;
+  const void* ins[6] = {w1, w2, token_ids, hidden_states, gate_weight, gate_bias};
+  const size_t ins_bytes[6] = {wbytes, wbytes, (size_t)rows * sizeof(int64_t), hbytes, gwbytes, gbbytes};
+  if (corrected_logits != base_logits && overlaps(corrected_logits, lbytes, base_logits, lbytes))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < 6; ++i) {
+    if (overlaps(corrected_logits, lbytes, ins[i], ins_bytes[i])) return DSPARK_ERR_INVALID_ARGUMENT;
+    if (latent_out && overlaps(latent_out, ubytes, ins[i], ins_bytes[i])) return DSPARK_ERR_INVALID_ARGUMENT;
+  }
+  if (latent_out && (overlaps(latent_out, ubytes, corrected_logits, lbytes) ||
+                     overlaps(latent_out, ubytes, base_logits, lbytes)))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* const region = (char*)workspace + align256(dspark_markov_workspace_bytes(B, M, V, r, 0));
+  void* const latent = latent_out ? latent_out : (void*)region;
+  dspark::GateParams g{};
+  fill_gate(g, hidden_states, hidden_dtype, d, token_ids, nullptr, w1, gate_weight, gate_bias, rows, V, r, 1, 0,
+            region, latent, r, dspark::MODE_APPLY, gated);
+  hipError_t e = dspark::launch_gate(g, weight_dtype == DSPARK_BF16, hidden_dtype == DSPARK_F32, s);
+  if (e != hipSuccess) return device_failure(e, "gate launch");
+
+  dspark::KernelParams p{};
+  p.base = base_logits;
+  p.out = corrected_logits;
+  p.ids = token_ids;
+  p.w1 = w1;
+  p.w2 = w2;
+  p.bad_rows = &((Control*)workspace)->bad_rows;
+  p.sink = (char*)workspace + kControlBytes;
+  p.latent = latent;
+  p.latent_ld = r;
+  p.rows = rows;
+  p.V = V;
+  p.r = r;
+  p.M = M;
+  p.mode = dspark::MODE_APPLY;
+  // bf16 weights: the grouped kernel (rows in their own order, one
+  // launch per block of rows the kernel takes); otherwise the generic one
+  const bool fast = tile_path(DSPARK_BF16, weight_dtype, V, r, base_logits, corrected_logits, w1, w2) &&
+                    aligned16(latent);
+  if (fast) {
+    const size_t lb = dtype_bytes(logits_dtype);
+    int64_t blk = dspark::kGroupedApplyMaxRows;
+    const int64_t fit = ((int64_t)1 << 31) / (V * (int64_t)lb);
+    if (fit < blk) blk = fit;
+    for (int64_t off = 0; off < rows && blk > 0; off += blk) {
+      dspark::KernelParams q = p;
+      q.rows = rows - off < blk ? rows - off : blk;
+      q.base = (const char*)base_logits + (size_t)(off * V) * lb;
+      q.out = (char*)corrected_logits + (size_t)(off * V) * lb;
+      q.ids = token_ids + off;
+      q.latent = (const char*)latent + (size_t)(off * r) * 2;
+      e = dspark::launch_apply_grouped(q, logits_dtype == DSPARK_F32, s);
+      if (e == hipErrorNotSupported) {
+        (void)hipGetLastError();
+        e = dspark::launch_generic(q, logits_dtype == DSPARK_BF16, true, s);
+      }
+      if (e != hipSuccess) return device_failure(e, "gated apply launch");
+    }
+    if (blk > 0) return DSPARK_OK;
+  }
+  if (r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
+  e = dspark::launch_generic(p, logits_dtype == DSPARK_BF16, weight_dtype == DSPARK_BF16, s);
+  if (e != hipSuccess) return device_failure(e, "gated apply launch");
+  return DSPARK_OK;
+}
+
+dspark_status_t dspark_markov_sample_block_gated(
+    const void* base_logits, dspark_dtype_t logits_dtype, const int64_t* first_prev_token_ids,
+    const void* hidden_states, dspark_dtype_t hidden_dtype, int64_t d, const void* w1,
+    const void* w2, const void* gate_weight, const void* gate_bias, dspark_dtype_t weight_dtype,
+    int64_t B, int64_t M, int64_t V, int64_t r, double temperature, uint64_t seed,
+    int64_t position_offset, int64_t batch_offset, int64_t* sampled_tokens,
+    void* corrected_logits, void* latent_out, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  int64_t elems = 0;
+  dspark_status_t st = check_common(logits_dtype, weight_dtype, B, M, V, r, &elems);
+  if (st != DSPARK_OK) return st;
+  if (std::isnan(temperature)) return DSPARK_ERR_INVALID_ARGUMENT;
+  const bool gated = hidden_states != nullptr;
+  st = check_gate_args(gated, hidden_dtype, d, gate_weight, gate_bias, B * M, r);
+  if (st != DSPARK_OK) return st;
+  if (B == 0 || M == 0) return DSPARK_OK;
+  if (V == 0) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!gated && !latent_out)  // the vanilla fallback
+    return dspark_markov_sample_block(base_logits, logits_dtype, first_prev_token_ids, w1, w2, weight_dtype,
+                                      B, M, V, r, temperature, seed, position_offset, batch_offset,
+                                      sampled_tokens, corrected_logits, workspace, workspace_bytes, stream);
+  if (!base_logits || !first_prev_token_ids || !w1 || !w2 || !sampled_tokens)
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < dspark_markov_gated_workspace_bytes(B, M, V, r, gated ? d : 0, 1))
+    return DSPARK_ERR_WORKSPACE_TOO_SMALL;
+  const size_t lbytes = (size_t)elems * dtype_bytes(logits_dtype);
+  const size_t wbytes = (size_t)(V * r) * dtype_bytes(weight_dtype);
+  const size_t tbytes = (size_t)(B * M) * sizeof(int64_t);
+  const size_t ubytes = (size_t)(B * M * r) * dtype_bytes(weight_dtype);
+  const size_t hbytes = gated ? (size_t)(B * M * d) * dtype_bytes(hidden_dtype) : 0;
+  const size_t gwbytes = gated ? (size_t)(r * (d + r)) * dtype_bytes(weight_dtype) : 0;
+  const size_t gbbytes = gated ? (size_t)r * dtype_bytes(weight_dtype) : 0;
+  const void* ins[7] = {base_logits, w1, w2, first_prev_token_ids, hidden_states, gate_weight, gate_bias};
+  const size_t ins_bytes[7] = {lbytes, wbytes, wbytes, (size_t)B * sizeof(int64_t), hbytes, gwbytes, gbbytes};
+  for (int i = 0; i < 7; ++i) {
+    if (overlaps(sampled_tokens, tbytes, ins[i], ins_bytes[i])) return DSPARK_ERR_INVALID_ARGUMENT;
+    if (corrected_logits && overlaps(corrected_logits, lbytes, ins[i], ins_bytes[i]))
+      return DSPARK_ERR_INVALID_ARGUMENT;
+    if (latent_out && overlaps(latent_out, ubytes, ins[i], ins_bytes[i])) return DSPARK_ERR_INVALID_ARGUMENT;
+  }
+  if (corrected_logits && overlaps(corrected_logits, lbytes, sampled_tokens, tbytes))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  if (latent_out && (overlaps(latent_out, ubytes, sampled_tokens, tbytes) ||
+                     (corrected_logits && overlaps(latent_out, ubytes, corrected_logits, lbytes))))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+
+  const bool greedy = temperature < 1e-5;
+  hipStream_t s = (hipStream_t)stream;
+  char* const region = (char*)workspace + align256(dspark_markov_workspace_bytes(B, M, V, r, 1));
+  dspark::KernelParams p{};
+  p.base = base_logits;
+  p.out = corrected_logits;
+  p.ids = first_prev_token_ids;
+  p.tokens = sampled_tokens;
+  p.w1 = w1;
+  p.w2 = w2;
+  p.bad_rows = &((Control*)workspace)->bad_rows;
+  p.partials = (uint64_t*)((char*)workspace + kControlBytes);
+  p.rows = B;
+  p.V = V;
+  p.r = r;
+  p.M = M;
+  p.batch_offset = batch_offset;
+  p.mode = greedy ? dspark::MODE_GREEDY : dspark::MODE_TEMPERATURE;
+  p.kappa = greedy ? 0.0f : (float)(1.4426950408889634 / temperature);
+  p.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+  p.seed_hi = (uint32_t)(seed >> 32);
+  // each step's latent rows: straight into latent_out[:, k, :], else a scratch [B, r]
+  const int64_t lld = latent_out ? M * r : r;
+  const bool tile = tile_path(logits_dtype, weight_dtype, V, r, base_logits, corrected_logits, w1, w2) &&
+                    (latent_out == nullptr || aligned16(latent_out));
+  if (!tile && r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
+  const int cus = device_cus();
+  for (int64_t k = 0; k < M; ++k) {
+    void* const latent = latent_out ? (void*)((char*)latent_out + (size_t)(k * r) * dtype_bytes(weight_dtype))
+                                    : (void*)region;
+    dspark::GateParams g{};
+    fill_gate(g, hidden_states, hidden_dtype, d, first_prev_token_ids, sampled_tokens, w1, gate_weight, gate_bias,
+              B, V, r, M, k, region, latent, lld, p.mode, gated);
+    hipError_t e = dspark::launch_gate(g, weight_dtype == DSPARK_BF16, hidden_dtype == DSPARK_F32, s);
+    if (e != hipSuccess) return device_failure(e, "gate launch");
+    p.k = k;
+    p.k_abs = (uint32_t)(position_offset + k);
+    p.latent = latent;
+    p.latent_ld = lld;
+    e = hipErrorNotSupported;
+    if (tile) {
+      p.nparts = dspark::sample_step_parts(V);
+      e = dspark::launch_sample_step(p, cus, s);
+      if (e == hipErrorNotSupported) (void)hipGetLastError();
+    }
+    if (e == hipErrorNotSupported) {
+      p.nparts = (V + 255) / 256;
+      e = dspark::launch_generic(p, logits_dtype == DSPARK_BF16, weight_dtype == DSPARK_BF16, s);
+    }
+    if (e != hipSuccess) return device_failure(e, "gated sample step launch");
     e = dspark::launch_reduce(p.partials, p.nparts, B, M, k, sampled_tokens, s);
     if (e != hipSuccess) return device_failure(e, "sample reduce launch");
   }

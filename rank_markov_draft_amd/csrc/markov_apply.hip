@@ -44,8 +44,6 @@ __global__ __launch_bounds__(WAVES * 64) void markov_apply_wide_bf16(KernelParam
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int m = lane & 31;
-  const int h = lane >> 5;
   const int64_t V = p.V, r = p.r, rows = p.rows;
   const int64_t S = (V + 31) / 32;
   const int64_t vbeg = (int64_t)blockIdx.x * COLS;
@@ -298,7 +296,11 @@ __global__ __launch_bounds__(WAVES * 64) void markov_apply_grouped_bf16(KernelPa
   const uint32_t lbytes = (uint32_t)rows * V * LB;  // <= 2^31 (host)
   const __amdgpu_buffer_rsrc_t rs_base = buffer_rsrc(p.base, lbytes);
   const __amdgpu_buffer_rsrc_t rs_out = buffer_rsrc(p.out, lbytes);
-  const BufferWords bw_w1 = buffer_words(p.w1, V * (uint32_t)r * 2u);
+  // gated head: the gathered row of row i is latent row i (rows in their own
+  // order; the host never plans a gated call)
+  const bool lat = p.latent != nullptr;
+  const BufferWords bw_w1 = lat ? buffer_words(p.latent, (uint32_t)rows * (uint32_t)r * 2u)
+                                : buffer_words(p.w1, V * (uint32_t)r * 2u);
   constexpr int GW = WAVES - 1;  // the gathering waves: GW and GW - 1
 
   // ids first; the W2 loads are issued in eight groups between the plan's
@@ -459,7 +461,7 @@ __global__ __launch_bounds__(WAVES * 64) void markov_apply_grouped_bf16(KernelPa
         bad += ok ? 0u : 1u;
         plan_row[i] = (uint16_t)i;
         plan_uid[i] = (uint16_t)i;
-        plan_tok[i] = ok ? (int32_t)idv[k] : -1;
+        plan_tok[i] = ok ? (lat ? i : (int32_t)idv[k]) : -1;
       }
     }
     if (blockIdx.x == 0 && bad) atomicAdd(p.bad_rows, bad);
@@ -635,7 +637,7 @@ template <int K32, int WAVES, int D, int KB, bool LF32>
 hipError_t launch_grouped(const KernelParams& p, hipStream_t s) {
   const int64_t S = (p.V + 31) / 32;
   const dim3 grid((unsigned)((S + WAVES - 1) / WAVES));
-  if (p.rows >= kGroupedMinRows)
+  if (p.rows >= kGroupedMinRows && p.latent == nullptr)
     hipLaunchKernelGGL((markov_apply_grouped_bf16<K32, WAVES, D, KB, true, LF32>), grid, dim3(WAVES * 64), 0, s, p);
   else
     hipLaunchKernelGGL((markov_apply_grouped_bf16<K32, WAVES, D, KB, false, LF32>), grid, dim3(WAVES * 64), 0, s, p);
@@ -648,7 +650,9 @@ hipError_t launch_grouped(const KernelParams& p, hipStream_t s) {
 // rows), the logits and V * r * 2 at most 2^31 bytes; hipErrorNotSupported
 // otherwise.
 hipError_t launch_apply_grouped(const KernelParams& p, bool logits_f32, hipStream_t s) {
+  static_assert(kGroupedMaxRows == kGroupedApplyMaxRows, "row limit");
   if (p.rows < 1 || p.rows > kGroupedMaxRows) return hipErrorNotSupported;
+  if (p.latent != nullptr && p.latent_ld != p.r) return hipErrorNotSupported;
   if (p.rows * p.V * (logits_f32 ? 4 : 2) > ((int64_t)1 << 31) || p.V * p.r * 2 > ((int64_t)1 << 31))
     return hipErrorNotSupported;
   // fp32 logits take twice the ring registers per chunk: half the depth
@@ -681,6 +685,7 @@ size_t apply_sink_bytes() { return 1024 * 16; }
 // Teacher-forced bf16 apply with the streaming kernel; hipErrorNotSupported
 // if the rank has no instance or the element offsets need more than 31 bits.
 hipError_t launch_apply_wide(const KernelParams& p, hipStream_t s) {
+  if (p.latent != nullptr) return hipErrorNotSupported;  // vanilla head only
   if (p.rows * p.V >= ((int64_t)1 << 31)) return hipErrorNotSupported;
   // rank blocks of 32 (the rank is zero-padded to a multiple of 32)
   switch (tile_ks_for_rank(p.r)) {

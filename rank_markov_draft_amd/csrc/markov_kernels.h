@@ -23,6 +23,12 @@ struct KernelParams {
   uint64_t* partials;    // sampling: [rows, nparts] argmax keys
   uint32_t* bad_rows;    // device error word
   void* sink;            // apply: 16 bytes per thread of scratch for stores past the edges
+  // Gated head: when latent is set, row n (apply) or batch row b (sampling
+  // step) is biased by the projection of latent row n (b) -- [rows] rows of
+  // latent_ld elements in the weight dtype -- instead of W1[predecessor];
+  // the predecessor still decides whether the row is valid.
+  const void* latent;
+  int64_t latent_ld;
   int64_t rows;
   int64_t V;
   int64_t r;
@@ -62,6 +68,42 @@ struct ChainParams {
   int64_t S;                  // 32-column vocabulary slices
 };
 
+// The gate of the gated head, one launch pair per call (apply) or per step
+// (sampling): the split-K products of the gate GEMM into partials, then the
+// latent rows u = rnd_W(rnd_W(sigmoid(rnd_W(z))) * e), z = the sum of the
+// splits plus the gate bias, e = W1[predecessor] (zero for invalid ids).
+struct GateParams {
+  const void* hidden;      // rows of d elements: apply row n, step (b, k) at b * M + k
+  const int64_t* ids;      // apply: token_ids [rows]; sampling: first_prev [B]
+  const int64_t* tokens;   // sampling: [B, M]
+  const void* w1;          // [V, r]
+  const void* gw;          // gate_proj weight [r, d + r]
+  const void* gb;          // gate_proj bias [r]
+  float* partials;         // [S][rows][r]
+  void* latent;            // [rows] rows of latent_ld elements
+  int64_t rows;
+  int64_t V;
+  int64_t r;
+  int64_t d;
+  int64_t M;
+  int64_t k;               // sampling step
+  int64_t latent_ld;
+  int64_t hidden_bytes;    // extent of the hidden tensor
+  int64_t kchunk;          // gate-input columns of one split (multiple of 256)
+  int S;                   // splits
+  int mode;                // MODE_APPLY or a sampling mode
+  int gated;               // 0: no hidden states (vanilla fallback), u = e
+};
+
+// Splits of the gate GEMM for `rows` rows (kchunk written to *kchunk).
+int gate_splits(int64_t rows, int64_t r, int64_t d, int64_t* kchunk);
+// Gate of the gated head: weights bf16 or fp32, hidden bf16 or fp32.  The
+// matrix-core form needs bf16 weights, d % 8 == 0, r % 8 == 0 and 16-byte
+// aligned hidden, W1 and gate weight; otherwise a scalar form runs.
+hipError_t launch_gate(const GateParams& g, bool weights_bf16, bool hidden_f32, hipStream_t s);
+// Gated head without hidden states: latent rows u = W1[predecessor].
+hipError_t launch_gate_embeddings(const GateParams& g, bool weights_bf16, hipStream_t s);
+
 int chain_max_rows();
 int chain_key_groups();
 int chain_waves_per_group();
@@ -80,6 +122,7 @@ size_t apply_sink_bytes();
 // computed once; needs 1 <= rows <= 4096 and the logits and V * r * 2 at
 // most 2^31 bytes.
 hipError_t launch_apply_grouped(const KernelParams& p, bool logits_f32, hipStream_t s);
+constexpr int64_t kGroupedApplyMaxRows = 4096;
 // One bf16 sampling step (greedy or temperature) of the p.rows = B rows at
 // position p.k: argmax keys per (row, 512-column block) into p.partials with
 // p.nparts = sample_step_parts(V); one workgroup per CU.  Needs r <= 256,

@@ -234,8 +234,11 @@ __global__ __launch_bounds__(256) void markov_generic(KernelParams p) {
   const int64_t x = predecessor(p, n);
   const bool ok = (x >= 0) && (x < V);
   if (!ok && tid == 0 && count_bad) atomicAdd(p.bad_rows, 1u);
+  // gated head: latent row n instead of W1[x]
+  const void* const erow = p.latent != nullptr ? p.latent : p.w1;
+  const int64_t ebase = p.latent != nullptr ? n * p.latent_ld : x * r;
   for (int64_t j = tid; j < r; j += 256)
-    lds_row[j] = ok ? (W_BF16 ? load_bf16(p.w1, x * r + j) : load_f32(p.w1, x * r + j)) : 0.0f;
+    lds_row[j] = ok ? (W_BF16 ? load_bf16(erow, ebase + j) : load_f32(erow, ebase + j)) : 0.0f;
   __syncthreads();
 
   uint64_t key = 0;
@@ -337,6 +340,7 @@ int tile_ks_for_rank(int64_t r) {
 }
 
 hipError_t launch_tile(const KernelParams& p, hipStream_t s) {
+  if (p.latent != nullptr) return hipErrorNotSupported;  // vanilla head only
   const int ks = tile_ks_for_rank(p.r);
   if (p.mode == MODE_APPLY) return launch_tile_mode<MODE_APPLY>(p, ks, s);
   if (p.mode == MODE_GREEDY) return launch_tile_mode<MODE_GREEDY>(p, ks, s);

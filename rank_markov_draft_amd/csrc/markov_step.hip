@@ -83,7 +83,11 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_bf16(KernelParams p)
   const __amdgpu_buffer_rsrc_t rs_base = buffer_rsrc(p.base, lbytes);
   const __amdgpu_buffer_rsrc_t rs_out = buffer_rsrc(p.out, p.out != nullptr ? lbytes : 0u);
   const __amdgpu_buffer_rsrc_t rs_part = buffer_rsrc(p.partials, (uint32_t)B * (uint32_t)p.nparts * 8u);
-  const __amdgpu_buffer_rsrc_t rs_w1 = buffer_rsrc(p.w1, V * (uint32_t)r * 2u);
+  // gated head: the gathered row of batch row b is latent row b
+  const bool lat = p.latent != nullptr;
+  const uint32_t eld = lat ? (uint32_t)p.latent_ld : (uint32_t)r;
+  const __amdgpu_buffer_rsrc_t rs_w1 =
+      lat ? buffer_rsrc(p.latent, ((uint32_t)(B - 1) * eld + (uint32_t)r) * 2u) : buffer_rsrc(p.w1, V * (uint32_t)r * 2u);
   const __amdgpu_buffer_rsrc_t rs_w2 = buffer_rsrc(p.w2, V * (uint32_t)r * 2u);
 
   // unit u = block * nch + chunk
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_bf16(KernelParams p)
       const int kof = 32 * kk + 8 * (l >> 4);
       const int x = (live && e < EUNIT / 16 && row < B) ? lds_tok[row] : -1;
       gv[q] = __builtin_amdgcn_raw_buffer_load_b128(
-          rs_w1, (x >= 0 && kof < r) ? ((uint32_t)x * (uint32_t)r + kof) * 2u : kBufferOob, 0, 0);
+          rs_w1, (x >= 0 && kof < r) ? ((uint32_t)x * eld + kof) * 2u : kBufferOob, 0, 0);
     }
   };
   auto gather_to_lds = [&](int slot, const u32x4_t gv[GPT]) __attribute__((always_inline)) {
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_bf16(KernelParams p)
       const bool ok = tokv[k] >= 0 && tokv[k] < (int64_t)V;
       if (i < B) {
         bad += ok ? 0u : 1u;
-        lds_tok[i] = ok ? (int32_t)tokv[k] : -1;
+        lds_tok[i] = ok ? (lat ? i : (int32_t)tokv[k]) : -1;
       }
     }
     if (blockIdx.x == 0 && kstep == 0 && bad) atomicAdd(p.bad_rows, bad);
@@ -318,6 +322,8 @@ hipError_t launch_sample_step(const KernelParams& p, int num_cus, hipStream_t s)
   if (p.rows < 1 || p.rows > kStepMaxB || num_cus < 1 || p.nparts != sample_step_parts(p.V))
     return hipErrorNotSupported;
   if (p.rows * p.M * p.V * 2 > ((int64_t)1 << 31) || p.V * p.r * 2 > ((int64_t)1 << 31)) return hipErrorNotSupported;
+  if (p.latent != nullptr && (p.latent_ld < p.r || p.rows * p.latent_ld * 2 > ((int64_t)1 << 31)))
+    return hipErrorNotSupported;
   const int64_t units = ((p.rows + kStepRows - 1) / kStepRows) * sample_step_parts(p.V);
   const int grid = (int)(units < num_cus ? units : num_cus);
   const bool t = p.mode == MODE_TEMPERATURE;

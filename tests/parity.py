@@ -49,9 +49,12 @@ def tolerance_ok(gpu: np.ndarray, ref: np.ndarray, is_bf16: bool) -> np.ndarray:
     return d <= 1e-5 * np.maximum(np.abs(ref.astype(np.float64)), 1e-2)
 
 
-def check_logits(gpu, ref, base, ids, w1, w2, report: LogitReport | None = None) -> LogitReport:
+def check_logits(gpu, ref, base, ids, w1, w2, report: LogitReport | None = None,
+                 latent=None) -> LogitReport:
     """gpu, ref: oracle-typed arrays [R, M, V] (or [N, V]); base/ids/w1/w2 the
-    oracle's inputs for the same rows (ids: the predecessor of every row)."""
+    oracle's inputs for the same rows (ids: the predecessor of every row).
+    With ``latent`` [N, r] (gated head) row n is biased by latent[n] instead
+    of w1[ids[n]], and ids/w1 are not used."""
     rep = report or LogitReport()
     V = gpu.shape[-1]
     g = as_f32(gpu).reshape(-1, V)
@@ -62,7 +65,11 @@ def check_logits(gpu, ref, base, ids, w1, w2, report: LogitReport | None = None)
     rep.mismatches += int(bad_r.size)
     if bad_r.size:
         rep.max_abs_diff = max(rep.max_abs_diff, float(np.max(np.abs(g[bad_r, bad_c] - o[bad_r, bad_c]))))
-        lo, mid, hi = orc.logit_bounds(base, ids, w1, w2, bad_r, bad_c)
+        if latent is None:
+            lo, mid, hi = orc.logit_bounds(base, ids, w1, w2, bad_r, bad_c)
+        else:
+            lo, mid, hi = orc.logit_bounds_rows(base.reshape(-1, V), latent.reshape(-1, latent.shape[-1]),
+                                                w2, bad_r, bad_c)
         gv = g[bad_r, bad_c]
         assert np.array_equal(mid, o[bad_r, bad_c]), "oracle bounds disagree with oracle values"
         inside = (lo <= gv) & (gv <= hi)
@@ -73,6 +80,42 @@ def check_logits(gpu, ref, base, ids, w1, w2, report: LogitReport | None = None)
                 f"first at row {bad_r[i]} col {bad_c[i]}: gpu {gv[i]!r} oracle {o[bad_r[i], bad_c[i]]!r} "
                 f"interval [{lo[i]!r}, {hi[i]!r}]")
         rep.flips += int((~tolerance_ok(gv, o[bad_r, bad_c], gpu.dtype == np.uint16)).sum())
+    return rep
+
+
+@dataclasses.dataclass
+class LatentReport:
+    elements: int = 0
+    mismatches: int = 0      # not bit-identical to the oracle's latent
+    max_rel_diff: float = 0.0
+
+
+def check_latent(gpu_latent, hidden, ids, w1, gate_w, gate_b, report: LatentReport | None = None) -> LatentReport:
+    """Gated head: the GPU's latent rows [N, r] against the oracle's for the
+    same hidden rows [N, d] and predecessors [N].  Every element must lie in
+    the oracle's admissible interval (fp32 accumulation of the gate in any
+    order, fp32 logistic within 2^-20 relative); fp32 latents must also be
+    within 1e-5 relative of the oracle's."""
+    rep = report or LatentReport()
+    r = w1.shape[1]
+    lat, lo, hi = orc.gated_latent(hidden, ids, w1, gate_w, gate_b, bounds=True)
+    g = as_f32(gpu_latent).reshape(-1, r)
+    o = as_f32(lat).reshape(-1, r)
+    rep.elements += g.size
+    rep.mismatches += int((g.view(np.uint32) != o.view(np.uint32)).sum())
+    inside = (lo <= g) & (g <= hi)
+    if not inside.all():
+        i, j = (int(t[0]) for t in np.nonzero(~inside))
+        raise AssertionError(f"{int((~inside).sum())} of {g.size} latent elements outside the admissible "
+                             f"interval; first at row {i} col {j}: gpu {g[i, j]!r} oracle {o[i, j]!r} "
+                             f"interval [{lo[i, j]!r}, {hi[i, j]!r}]")
+    rel = np.abs(g.astype(np.float64) - o) / np.maximum(np.abs(o.astype(np.float64)), 1e-30)
+    rel[(g == o)] = 0.0
+    rep.max_rel_diff = max(rep.max_rel_diff, float(rel.max()) if rel.size else 0.0)
+    if gpu_latent.dtype != np.uint16:
+        e = as_f32(w1)[np.asarray(ids).reshape(-1)]
+        ok = np.abs(g - o) <= 1e-5 * np.maximum(np.abs(o), 1e-6 * np.abs(e))
+        assert ok.all(), f"{int((~ok).sum())} fp32 latent elements beyond 1e-5 relative"
     return rep
 
 

@@ -124,3 +124,73 @@ def test_sample_argument_errors(L):
     assert _sample(L, tok=None) == 1
     assert _sample(L, ws=None) == 3
     assert _sample(L, wsb=256) == 3
+
+
+# ------------------------------------------------------------ gated head
+def _gate_splits(rows, r, d):
+    """Split count of the gate GEMM: 256-column blocks of d + r, about 512
+    workgroups of 32 rows x 64 outputs in all."""
+    K = d + r
+    tiles = ((rows + 31) // 32) * ((r + 63) // 64)
+    blocks = (K + 255) // 256
+    want = min(max((512 + tiles - 1) // tiles, 1), blocks)
+    kchunk = (blocks + want - 1) // want * 256
+    return (K + kchunk - 1) // kchunk
+
+
+def test_gated_workspace_bytes(L):
+    """Gated calls: the vanilla layout, then the latent rows of one launch
+    (4 bytes per element at most) and the gate GEMM's split partial sums."""
+    for B, M, V, r, d, sample in ((64, 5, 129280, 256, 5120, 0), (64, 5, 129280, 256, 5120, 1),
+                                  (512, 5, 129280, 512, 5120, 0), (3, 4, 700, 16, 40, 1)):
+        rows = B if sample else B * M
+        want = (_align256(L.dspark_markov_workspace_bytes(B, M, V, r, sample)) + _align256(rows * r * 4)
+                + _align256(_gate_splits(rows, r, d) * rows * r * 4))
+        assert L.dspark_markov_gated_workspace_bytes(B, M, V, r, d, sample) == want
+    assert _gate_splits(320, 256, 5120) == 11
+    # vanilla fallback (d = 0): the latent rows only
+    assert L.dspark_markov_gated_workspace_bytes(2, 3, 64, 16, 0, 0) == \
+        _align256(L.dspark_markov_workspace_bytes(2, 3, 64, 16, 0)) + _align256(6 * 16 * 4)
+
+
+def _gapply(L, ldt=1, hdt=1, d=32, B=2, M=3, V=64, r=16, hidden=FAKE, gw=FAKE, gb=FAKE, out=FAKE,
+            latent=None, ws=FAKE, wsb=1 << 24, base=FAKE):
+    return L.dspark_markov_apply_block_gated(base, ldt, FAKE, hidden, hdt, d, FAKE, FAKE, gw, gb, 1,
+                                             B, M, V, r, out, latent, ws, wsb, None)
+
+
+def _gsample(L, T=0.0, hdt=1, d=32, B=2, M=3, V=64, r=16, hidden=FAKE, gw=FAKE, gb=FAKE, ws=FAKE, wsb=1 << 24):
+    return L.dspark_markov_sample_block_gated(FAKE, 1, FAKE, hidden, hdt, d, FAKE, FAKE, gw, gb, 1,
+                                              B, M, V, r, T, 0, 0, 0, FAKE, None, None, ws, wsb, None)
+
+
+def test_gated_argument_errors(L):
+    assert _gapply(L, d=0) == 1                 # a hidden state needs d > 0
+    assert _gapply(L, d=-5) == 1
+    assert _gapply(L, hdt=9) == 1               # unknown hidden dtype
+    assert _gapply(L, gw=None) == 1             # gate weight and bias required
+    assert _gapply(L, gb=None) == 1
+    assert _gapply(L, r=0) == 1
+    assert _gapply(L, out=None) == 1
+    assert _gapply(L, ws=None) == 3
+    assert _gapply(L, wsb=1024) == 3
+    assert _gapply(L, B=0) == 0                 # empty work
+    assert _gapply(L, V=0) == 0
+    # vanilla fallback: the gate arguments are not looked at
+    assert _gapply(L, hidden=None, d=0, gw=None, gb=None, ws=None) == 3
+    assert _gsample(L, T=float("nan")) == 1
+    assert _gsample(L, d=0) == 1
+    assert _gsample(L, gw=None) == 1
+    assert _gsample(L, V=0) == 1
+    assert _gsample(L, M=0) == 0
+    assert _gsample(L, ws=None) == 3
+    assert _gsample(L, hidden=None, d=0, gw=None, gb=None, ws=None) == 3
+
+
+def test_gated_overlaps_rejected(L):
+    base = 0x200000
+    # latent rows written over the base logits, or over the hidden states
+    assert _gapply(L, base=ctypes.c_void_p(base), latent=ctypes.c_void_p(base + 32)) == 1
+    assert _gapply(L, hidden=ctypes.c_void_p(0x400000), latent=ctypes.c_void_p(0x400000 + 64)) == 1
+    # corrected logits over the gate weight
+    assert _gapply(L, gw=ctypes.c_void_p(0x600000), out=ctypes.c_void_p(0x600000 + 16)) == 1

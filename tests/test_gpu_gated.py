@@ -1,0 +1,206 @@
+"""GPU parity of the gated head (GatedMarkovHead) against the CPU oracle,
+through the C ABI.
+
+Two checks per call: the GPU's latent rows u = sigmoid(gate_proj([h; e])) * e
+against the oracle's (inside its admissible interval for fp32 accumulation
+of the gate GEMM in any order), then the corrected logits against the
+oracle's projection of the GPU's own latent rows (the vanilla element
+rule).  Sampling is checked per step on the GPU's own previous tokens.
+"""
+import dataclasses
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import rank_markov_draft_amd as rmd
+from oracle import oracle as orc
+from rank_markov_draft_amd import workloads as wl
+from tests import parity
+from tests.gpu_util import device_inputs, from_dev
+
+pytestmark = pytest.mark.gpu
+
+REPORT = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out",
+                      "parity_report.txt")
+
+
+def _report(name, **kw):
+    line = f"[parity] {name}: " + ", ".join(f"{k}={v}" for k, v in kw.items())
+    print(line, flush=True)
+    os.makedirs(os.path.dirname(REPORT), exist_ok=True)
+    with open(REPORT, "a") as f:
+        f.write(line + "\n")
+
+
+KEYS = ("base", "token_ids", "first_prev", "hidden", "w1", "w2", "gate_w", "gate_b")
+
+
+def _inputs(dtype=wl.BF16, ldt=None, hdt=None, seed=0, **sizes):
+    w = dataclasses.replace(wl.WORKLOADS["gated_teacher_forced_320"], dtype=dtype,
+                            logits_dtype=-1 if ldt is None else ldt)
+    inp = wl.make_inputs(w, seed=seed, **sizes)
+    if hdt is not None and hdt != dtype:
+        conv = wl.to_bf16_bits if hdt == wl.BF16 else wl.bf16_bits_to_f32
+        inp["hidden"] = conv(inp["hidden"])
+    return inp
+
+
+def run_apply(inp, hidden=True, ws=None):
+    d = device_inputs({k: inp[k] for k in KEYS if k in inp})
+    out, lat = rmd.apply_block_logits_gated(d["base"], d["token_ids"], d["w1"], d["w2"], d["gate_w"], d["gate_b"],
+                                            d["hidden"] if hidden else None, return_latent=True, workspace=ws)
+    torch.cuda.synchronize()
+    return from_dev(out), from_dev(lat)
+
+
+def check_apply(inp, out, lat, rows=None, name=""):
+    B, M, V = inp["base"].shape
+    r = inp["w1"].shape[1]
+    d = inp["hidden"].shape[-1]
+    rows = np.arange(B * M) if rows is None else np.asarray(rows)
+    ids = inp["token_ids"].reshape(-1)[rows]
+    glat = lat.reshape(B * M, r)[rows]
+    lrep = parity.check_latent(glat, inp["hidden"].reshape(-1, d)[rows], ids, inp["w1"], inp["gate_w"],
+                               inp["gate_b"])
+    base = inp["base"].reshape(B * M, V)[rows]
+    ref = orc.apply_rows(base, glat, inp["w2"])
+    rep = parity.check_logits(out.reshape(B * M, V)[rows], ref, base, None, None, inp["w2"], latent=glat)
+    _report(name, **{"latent_" + k: v for k, v in dataclasses.asdict(lrep).items()}, **dataclasses.asdict(rep))
+    return lrep, rep
+
+
+def test_gated_teacher_forced_320(native):
+    w = wl.WORKLOADS["gated_teacher_forced_320"]
+    inp = wl.make_inputs(w)
+    out, lat = run_apply(inp)
+    lrep, rep = check_apply(inp, out, lat, name=w.name)
+    assert lrep.mismatches <= 0.01 * lrep.elements
+    assert rep.mismatches <= 1e-4 * rep.elements
+
+
+@pytest.mark.parametrize("B,M,V,r,d,dtype,ldt,hdt", [
+    (3, 5, 1000, 24, 40, wl.BF16, None, None),        # grouped kernel, rank padded to 32
+    (2, 33, 4104, 64, 256, wl.BF16, None, wl.F32),    # fp32 hidden states, rounded to bf16
+    (5, 205, 2048, 512, 128, wl.BF16, wl.F32, None),  # 1025 rows, fp32 logits, rank 512
+    (1100, 4, 520, 16, 64, wl.BF16, None, None),      # 4400 rows: two row blocks
+    (2, 3, 1001, 16, 48, wl.BF16, None, None),        # V % 8 != 0: generic kernel
+    (3, 4, 777, 12, 20, wl.F32, None, None),          # fp32, d % 8 != 0: scalar gate
+    (2, 5, 640, 16, 24, wl.F32, wl.BF16, wl.BF16),    # bf16 logits and hidden, fp32 weights
+])
+def test_gated_apply_shapes(native, B, M, V, r, d, dtype, ldt, hdt):
+    inp = _inputs(dtype, ldt, hdt, seed=B + V + d, B=B, M=M, V=V, r=r, hidden=d)
+    out, lat = run_apply(inp)
+    rows = None
+    if B * M > 600:
+        rng = np.random.default_rng(B)
+        rows = np.unique(np.concatenate([rng.choice(B * M, 200, replace=False), [0, B * M - 1, 4095, 4096]]))
+        rows = rows[rows < B * M]
+    check_apply(inp, out, lat, rows=rows, name=f"gated apply B{B} M{M} V{V} r{r} d{d} W{dtype} L{ldt} H{hdt}")
+
+
+def test_gated_bad_ids_and_fallback(native):
+    """Ids outside [0, V) get a zero latent and a zero bias and are counted;
+    without hidden states the gated call is the vanilla head (bit-identical
+    logits, latent = W1[x])."""
+    B, M, V, r, d = 4, 9, 3000, 64, 96
+    inp = _inputs(seed=5, B=B, M=M, V=V, r=r, hidden=d)
+    ids = inp["token_ids"].copy()
+    ids[0, 0], ids[1, 3], ids[3, 8] = -1, V, 2**40
+    inp["token_ids"] = ids
+    ws = rmd.Workspace(B, M, V, r, sample=False, hidden=d)
+    out, lat = run_apply(inp, ws=ws)
+    flat = ids.reshape(-1)
+    bad = (flat < 0) | (flat >= V)
+    assert rmd.read_device_error(ws) == int(bad.sum())
+    assert np.all(lat.reshape(B * M, r)[bad] == 0)
+    assert np.array_equal(out.reshape(B * M, V)[bad], inp["base"].reshape(B * M, V)[bad])
+    check_apply(inp, out, lat, rows=np.nonzero(~bad)[0], name="gated apply bad ids")
+    # vanilla fallback
+    good = dict(inp, token_ids=np.where((ids >= 0) & (ids < V), ids, 0))
+    out0, lat0 = run_apply(good, hidden=False)
+    dv = device_inputs({k: good[k] for k in ("base", "token_ids", "w1", "w2")})
+    van = from_dev(rmd.apply_block_logits(dv["base"], dv["token_ids"], dv["w1"], dv["w2"]))
+    assert np.array_equal(out0, van)
+    assert np.array_equal(lat0, good["w1"][good["token_ids"]])
+
+
+def test_gated_open_gate_equals_vanilla_on_gpu(native):
+    """A saturated gate (bias +40) gives u = W1[x] exactly, so the gated call
+    returns the vanilla call's logits bit for bit."""
+    inp = _inputs(seed=8, B=8, M=5, V=4104, r=256, hidden=128)
+    inp["gate_b"] = wl.to_bf16_bits(np.full(inp["gate_b"].shape, 40.0, dtype=np.float32))
+    out, lat = run_apply(inp)
+    dv = device_inputs({k: inp[k] for k in ("base", "token_ids", "w1", "w2")})
+    van = from_dev(rmd.apply_block_logits(dv["base"], dv["token_ids"], dv["w1"], dv["w2"]))
+    assert np.array_equal(lat, inp["w1"][inp["token_ids"]])
+    assert np.array_equal(out, van)
+
+
+# ------------------------------------------------------------ sampling
+def run_sample(inp, T, seed=0, hidden=True):
+    d = device_inputs({k: inp[k] for k in KEYS if k in inp})
+    B, M, V = inp["base"].shape
+    r = inp["w1"].shape[1]
+    ws = rmd.Workspace(B, M, V, r, sample=True, hidden=inp["hidden"].shape[-1] if hidden else 0)
+    tok, corr, lat = rmd.sample_block_tokens_gated(d["base"], d["first_prev"], d["w1"], d["w2"], d["gate_w"],
+                                                   d["gate_b"], d["hidden"] if hidden else None, T, seed=seed,
+                                                   return_latent=True, workspace=ws)
+    assert rmd.read_device_error(ws) == 0
+    return from_dev(tok), from_dev(corr), from_dev(lat)
+
+
+def check_sample(inp, T, seed, tok, corr, lat, brows=None, name=""):
+    B, M, V = inp["base"].shape
+    r = inp["w1"].shape[1]
+    d = inp["hidden"].shape[-1]
+    brows = np.arange(B) if brows is None else np.asarray(brows)
+    assert tok.shape == (B, M) and tok.min() >= 0 and tok.max() < V
+    prev = np.concatenate([inp["first_prev"][:, None], tok[:, :-1]], axis=1)[brows].reshape(-1)
+    glat = lat[brows].reshape(-1, r)
+    lrep = parity.check_latent(glat, inp["hidden"][brows].reshape(-1, d), prev, inp["w1"], inp["gate_w"],
+                               inp["gate_b"])
+    base = inp["base"][brows].reshape(-1, V)
+    ref = orc.apply_rows(base, glat, inp["w2"])
+    grows = corr[brows].reshape(-1, V)
+    rep = parity.check_logits(grows, ref, base, None, None, inp["w2"], latent=glat)
+    trep = parity.check_tokens(tok[brows].reshape(-1), grows, ref, T, seed, np.repeat(brows, M),
+                               np.tile(np.arange(M), len(brows)))
+    _report(name, **{"latent_" + k: v for k, v in dataclasses.asdict(lrep).items()}, **dataclasses.asdict(rep),
+            **dataclasses.asdict(trep))
+    return lrep, rep, trep
+
+
+@pytest.mark.parametrize("T", [0.0, 0.8])
+@pytest.mark.parametrize("B,M,V,r,d,dtype", [
+    (5, 4, 2048, 32, 64, wl.BF16),      # step kernel
+    (3, 3, 1001, 16, 40, wl.BF16),      # V % 8 != 0: generic kernel
+    (4, 3, 777, 12, 20, wl.F32),        # fp32: generic kernel, scalar gate
+])
+def test_gated_sample_shapes(native, T, B, M, V, r, d, dtype):
+    inp = _inputs(dtype, seed=B * M + V, B=B, M=M, V=V, r=r, hidden=d)
+    tok, corr, lat = run_sample(inp, T, seed=3)
+    check_sample(inp, T, 3, tok, corr, lat, name=f"gated sample T{T} B{B} M{M} V{V} r{r} d{d} W{dtype}")
+
+
+def test_gated_greedy_draft_64x5(native):
+    w = wl.WORKLOADS["gated_greedy_draft_64x5"]
+    inp = wl.make_inputs(w)
+    tok, corr, lat = run_sample(inp, 0.0)
+    brows = np.linspace(0, w.B - 1, 12).astype(np.int64)
+    lrep, rep, trep = check_sample(inp, 0.0, 0, tok, corr, lat, brows=brows, name=w.name)
+    assert rep.mismatches <= 1e-4 * rep.elements
+
+
+def test_gated_sample_fallback_is_vanilla(native):
+    """No hidden states: the gated sampling call draws the vanilla tokens and
+    returns W1 of each step's predecessor as its latent rows."""
+    inp = _inputs(seed=4, B=6, M=4, V=2048, r=32, hidden=64)
+    for T in (0.0, 0.8):
+        tok, corr, lat = run_sample(inp, T, seed=9, hidden=False)
+        dv = device_inputs({k: inp[k] for k in ("base", "first_prev", "w1", "w2")})
+        tv, cv = rmd.sample_block_tokens(dv["base"], dv["first_prev"], dv["w1"], dv["w2"], T, seed=9)
+        assert np.array_equal(tok, from_dev(tv)) and np.array_equal(corr, from_dev(cv))
+        prev = np.concatenate([inp["first_prev"][:, None], tok[:, :-1]], axis=1)
+        assert np.array_equal(lat, inp["w1"][prev])
