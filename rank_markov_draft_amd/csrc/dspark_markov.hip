@@ -108,13 +108,13 @@ dspark_status_t check_common(int ldt, int wdt, int64_t B, int64_t M, int64_t V, 
 }
 
 // ---- gated head
-// Gated-call workspace past the vanilla layout: the latent rows of one
-// launch (fp32 or bf16, [rows, r]), then the split-K partial sums of the
-// gate GEMM ([S][rows][r] fp32).
+// Gated-call workspace past the vanilla layout: the latent rows of the call
+// ([rows, r], at most 4 bytes per element), then the gate GEMM's split sums
+// ([S][rows][r] fp32) when it splits its inner dimension.
 size_t gated_region_bytes(int64_t rows, int64_t r, int64_t d) {
   int64_t kchunk = 0;
-  const int S = d > 0 ? dspark::gate_splits(rows, r, d, &kchunk) : 0;
-  return align256((size_t)(rows * r) * 4) + align256((size_t)S * (size_t)(rows * r) * 4);
+  const int S = d > 0 ? dspark::gate_splits(rows, r, d, &kchunk) : 1;
+  return align256((size_t)(rows * r) * 4) + (S > 1 ? align256((size_t)S * (size_t)(rows * r) * 4) : 0);
 }
 
 dspark_status_t check_gate_args(bool gated, int hdt, int64_t d, const void* gw, const void* gb, int64_t rows,
@@ -128,14 +128,17 @@ dspark_status_t check_gate_args(bool gated, int hdt, int64_t d, const void* gw, 
   return DSPARK_OK;
 }
 
-// Gate launch of `rows` rows: apply (ids = token_ids, hidden row n) or
-// sampling step k (first_prev / tokens, hidden row b * M + k).  `region` is
-// the gated workspace region: latent scratch first, then the partials.
-void fill_gate(dspark::GateParams& g, const void* hidden, dspark_dtype_t hdt, int64_t d, const int64_t* ids,
-               const int64_t* tokens, const void* w1, const void* gw, const void* gb, int64_t rows, int64_t V,
-               int64_t r, int64_t M, int64_t k, char* region, void* latent, int64_t latent_ld, int mode,
-               bool gated) {
-  g.hidden = hidden;
+// The gate of `rows` rows: apply (ids = token_ids, hidden row n) or
+// sampling step k (ids = first_prev, tokens, hidden row b * M + k); latent
+// rows go to `latent` (row stride latent_ld elements).  `region` is the
+// gated workspace region (latent scratch, then the split sums).
+hipError_t run_gate(char* region, const void* hidden, dspark_dtype_t hdt, int64_t d, const int64_t* ids,
+                    const int64_t* tokens, const void* w1, const void* gw, const void* gb, dspark_dtype_t wdt,
+                    int64_t rows, int64_t V, int64_t r, int64_t M, int64_t k, void* latent, int64_t latent_ld,
+                    int mode, bool gated, hipStream_t s) {
+  dspark::GateParams g{};
+  g.partials = (float*)(region + align256((size_t)(rows * r) * 4));
+  g.hidden = gated ? hidden : nullptr;
   g.ids = ids;
   g.tokens = tokens;
   g.w1 = w1;
@@ -151,9 +154,8 @@ void fill_gate(dspark::GateParams& g, const void* hidden, dspark_dtype_t hdt, in
   g.latent_ld = latent_ld;
   g.mode = mode;
   g.gated = gated ? 1 : 0;
-  g.partials = (float*)(region + align256((size_t)(rows * r) * 4));
-  g.hidden_bytes = gated ? (mode == dspark::MODE_APPLY ? rows : rows * M) * d * (int64_t)dtype_bytes(hdt) : 0;
-  g.S = gated ? dspark::gate_splits(rows, r, d, &g.kchunk) : 0;
+  g.hidden_bytes = gated ? rows * (mode == dspark::MODE_APPLY ? 1 : M) * d * (int64_t)dtype_bytes(hdt) : 0;
+  return dspark::launch_gate(g, wdt == DSPARK_BF16, hdt == DSPARK_F32, s);
 }
 
 }  // namespace
@@ -396,10 +398,8 @@ dspark_status_t dspark_markov_apply_block_gated(
   hipStream_t s = (hipStream_t)stream;
   char* const region = (char*)workspace + align256(dspark_markov_workspace_bytes(B, M, V, r, 0));
   void* const latent = latent_out ? latent_out : (void*)region;
-  dspark::GateParams g{};
-  fill_gate(g, hidden_states, hidden_dtype, d, token_ids, nullptr, w1, gate_weight, gate_bias, rows, V, r, 1, 0,
-            region, latent, r, dspark::MODE_APPLY, gated);
-  hipError_t e = dspark::launch_gate(g, weight_dtype == DSPARK_BF16, hidden_dtype == DSPARK_F32, s);
+  hipError_t e = run_gate(region, hidden_states, hidden_dtype, d, token_ids, nullptr, w1, gate_weight, gate_bias,
+                          weight_dtype, rows, V, r, M, 0, latent, r, dspark::MODE_APPLY, gated, s);
   if (e != hipSuccess) return device_failure(e, "gate launch");
 
   dspark::KernelParams p{};
@@ -524,10 +524,8 @@ dspark_status_t dspark_markov_sample_block_gated(
   for (int64_t k = 0; k < M; ++k) {
     void* const latent = latent_out ? (void*)((char*)latent_out + (size_t)(k * r) * dtype_bytes(weight_dtype))
                                     : (void*)region;
-    dspark::GateParams g{};
-    fill_gate(g, hidden_states, hidden_dtype, d, first_prev_token_ids, sampled_tokens, w1, gate_weight, gate_bias,
-              B, V, r, M, k, region, latent, lld, p.mode, gated);
-    hipError_t e = dspark::launch_gate(g, weight_dtype == DSPARK_BF16, hidden_dtype == DSPARK_F32, s);
+    hipError_t e = run_gate(region, hidden_states, hidden_dtype, d, first_prev_token_ids, sampled_tokens, w1, gate_weight,
+                            gate_bias, weight_dtype, B, V, r, M, k, latent, lld, p.mode, gated, s);
     if (e != hipSuccess) return device_failure(e, "gate launch");
     p.k = k;
     p.k_abs = (uint32_t)(position_offset + k);

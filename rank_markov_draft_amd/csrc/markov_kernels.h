@@ -68,10 +68,10 @@ struct ChainParams {
   int64_t S;                  // 32-column vocabulary slices
 };
 
-// The gate of the gated head, one launch pair per call (apply) or per step
-// (sampling): the split-K products of the gate GEMM into partials, then the
-// latent rows u = rnd_W(rnd_W(sigmoid(rnd_W(z))) * e), z = the sum of the
-// splits plus the gate bias, e = W1[predecessor] (zero for invalid ids).
+// The gate of the gated head, one launch per call (apply) or per step
+// (sampling): the latent rows u = rnd_W(rnd_W(sigmoid(rnd_W(z + b))) * e),
+// z = gate_proj's product with [h; e], e = W1[predecessor] (zero for
+// invalid ids); without hidden states (gated == 0) u = e.
 struct GateParams {
   const void* hidden;      // rows of d elements: apply row n, step (b, k) at b * M + k
   const int64_t* ids;      // apply: token_ids [rows]; sampling: first_prev [B]
@@ -79,8 +79,8 @@ struct GateParams {
   const void* w1;          // [V, r]
   const void* gw;          // gate_proj weight [r, d + r]
   const void* gb;          // gate_proj bias [r]
-  float* partials;         // [S][rows][r]
   void* latent;            // [rows] rows of latent_ld elements
+  float* partials;         // [S][rows][r] split sums (workspace), when S > 1
   int64_t rows;
   int64_t V;
   int64_t r;
@@ -89,20 +89,19 @@ struct GateParams {
   int64_t k;               // sampling step
   int64_t latent_ld;
   int64_t hidden_bytes;    // extent of the hidden tensor
-  int64_t kchunk;          // gate-input columns of one split (multiple of 256)
-  int S;                   // splits
+  int64_t kchunk;          // inner columns of one split (set by launch_gate)
+  int S;                   // splits (set by launch_gate)
   int mode;                // MODE_APPLY or a sampling mode
   int gated;               // 0: no hidden states (vanilla fallback), u = e
 };
 
-// Splits of the gate GEMM for `rows` rows (kchunk written to *kchunk).
+// Splits of the gate GEMM for `rows` rows (their column count in *kchunk).
 int gate_splits(int64_t rows, int64_t r, int64_t d, int64_t* kchunk);
+
 // Gate of the gated head: weights bf16 or fp32, hidden bf16 or fp32.  The
 // matrix-core form needs bf16 weights, d % 8 == 0, r % 8 == 0 and 16-byte
 // aligned hidden, W1 and gate weight; otherwise a scalar form runs.
 hipError_t launch_gate(const GateParams& g, bool weights_bf16, bool hidden_f32, hipStream_t s);
-// Gated head without hidden states: latent rows u = W1[predecessor].
-hipError_t launch_gate_embeddings(const GateParams& g, bool weights_bf16, hipStream_t s);
 
 int chain_max_rows();
 int chain_key_groups();

@@ -48,15 +48,18 @@ def _align256(x):
     return (x + 255) // 256 * 256
 
 
+HEAD = 256   # control block
+
+
 def test_workspace_bytes(L):
-    """Apply: control block, then a 16 KB store sink for lanes past the edges.
-    Sample: control block, then step partials (B * ceil(V/128) keys), then
-    the chain's 2 KB synchronisation area and its keys (M steps * 8 groups *
-    64 rows, 64 bytes apart)."""
-    assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 0) == 256 + 16384
+    """Apply: the head, then a 16 KB store sink for lanes past the edges.
+    Sample: the head, then step partials (B * ceil(V/128) keys), then the
+    chain's 2 KB synchronisation area and its keys (M steps * 8 groups * 64
+    rows, 64 bytes apart)."""
+    assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 0) == HEAD + 16384
     chain = lambda M: 4096 + M * 8 * 64 * 64
-    assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 1) == 256 + _align256(64 * 1010 * 8) + chain(5)
-    assert L.dspark_markov_workspace_bytes(256, 8, 151936, 256, 1) == 256 + _align256(256 * 1187 * 8) + chain(8)
+    assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 1) == HEAD + _align256(64 * 1010 * 8) + chain(5)
+    assert L.dspark_markov_workspace_bytes(256, 8, 151936, 256, 1) == HEAD + _align256(256 * 1187 * 8) + chain(8)
 
 
 FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: every call below fails validation
@@ -98,7 +101,7 @@ def test_apply_null_pointers_and_workspace(L):
     assert L.dspark_markov_apply_block(FAKE, 1, None, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, FAKE, 1 << 20, None) == 1
     assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, None, FAKE, 1 << 20, None) == 1
     assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, None, 1 << 20, None) == 3
-    assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, FAKE, 16639, None) == 3
+    assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, FAKE, HEAD + 16383, None) == 3
 
 
 def test_apply_overlap_rejected(L):
@@ -128,29 +131,29 @@ def test_sample_argument_errors(L):
 
 # ------------------------------------------------------------ gated head
 def _gate_splits(rows, r, d):
-    """Split count of the gate GEMM: 256-column blocks of d + r, about 512
-    workgroups of 32 rows x 64 outputs in all."""
+    """Splits of the gate GEMM's inner dimension: about 256 workgroups of
+    64 x 64 output tiles, at most 32 splits, whole 32-column steps."""
     K = d + r
-    tiles = ((rows + 31) // 32) * ((r + 63) // 64)
-    blocks = (K + 255) // 256
-    want = min(max((512 + tiles - 1) // tiles, 1), blocks)
-    kchunk = (blocks + want - 1) // want * 256
+    tiles = ((rows + 63) // 64) * ((r + 63) // 64)
+    steps = (K + 31) // 32
+    want = max(min((256 + tiles - 1) // tiles, 32, steps), 1)
+    kchunk = (steps + want - 1) // want * 32
     return (K + kchunk - 1) // kchunk
 
 
 def test_gated_workspace_bytes(L):
-    """Gated calls: the vanilla layout, then the latent rows of one launch
-    (4 bytes per element at most) and the gate GEMM's split partial sums."""
+    """Gated calls: the vanilla layout, then the latent rows of the call (4
+    bytes per element at most) and, when the gate GEMM splits, its split
+    sums."""
     for B, M, V, r, d, sample in ((64, 5, 129280, 256, 5120, 0), (64, 5, 129280, 256, 5120, 1),
-                                  (512, 5, 129280, 512, 5120, 0), (3, 4, 700, 16, 40, 1)):
+                                  (512, 5, 129280, 512, 5120, 0), (3, 4, 700, 16, 40, 1), (2, 3, 64, 16, 0, 0)):
         rows = B if sample else B * M
+        S = _gate_splits(rows, r, d) if d else 1
         want = (_align256(L.dspark_markov_workspace_bytes(B, M, V, r, sample)) + _align256(rows * r * 4)
-                + _align256(_gate_splits(rows, r, d) * rows * r * 4))
+                + (_align256(S * rows * r * 4) if S > 1 else 0))
         assert L.dspark_markov_gated_workspace_bytes(B, M, V, r, d, sample) == want
-    assert _gate_splits(320, 256, 5120) == 11
-    # vanilla fallback (d = 0): the latent rows only
-    assert L.dspark_markov_gated_workspace_bytes(2, 3, 64, 16, 0, 0) == \
-        _align256(L.dspark_markov_workspace_bytes(2, 3, 64, 16, 0)) + _align256(6 * 16 * 4)
+    assert _gate_splits(320, 256, 5120) == 13 and _gate_splits(64, 256, 5120) == 28
+    assert _gate_splits(2560, 512, 5120) == 1
 
 
 def _gapply(L, ldt=1, hdt=1, d=32, B=2, M=3, V=64, r=16, hidden=FAKE, gw=FAKE, gb=FAKE, out=FAKE,
