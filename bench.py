@@ -27,7 +27,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 WORKLOAD = "greedy_draft_64x5"
 DOMINANT_KERNEL = "markov_chain_greedy_bf16"   # the whole sample call is this one launch
 KERNEL_SOURCES = [os.path.join(ROOT, "rank_markov_draft_amd", "csrc", name)
-                  for name in ("markov_chain.hip", "device_common.h", "markov_kernels.h")]
+                  for name in ("markov_chain.hip", "device_common.h", "markov_chain.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

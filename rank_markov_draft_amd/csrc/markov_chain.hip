@@ -38,7 +38,7 @@
 // last workgroup to leave clears the keys and counters, so the workspace is
 // ready for the next call.
 #include "device_common.h"
-#include "markov_kernels.h"
+#include "markov_chain.h"
 
 namespace dspark {
 

@@ -1,9 +1,12 @@
 // markov_kernels.h -- interface between the C ABI (dspark_markov.hip) and the
-// gfx950 kernels (markov_kernels.hip, markov_chain.hip).
+// gfx950 kernels (markov_kernels.hip, markov_apply.hip, markov_step.hip,
+// markov_gate.hip; the chain's own interface is markov_chain.h).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "markov_chain.h"
 
 namespace dspark {
 
@@ -43,30 +46,7 @@ struct KernelParams {
   uint32_t seed_hi;
 };
 
-// Arguments of the persistent greedy chain (bf16).  keys holds one 64-bit
-// argmax key per (step, key group, row) at a stride of kKeyPad words; sync
-// holds the arrival counters and release words (kChainSyncBytes); both are
-// zero between calls.
-constexpr int kKeyPad = 8;
-constexpr size_t kChainSyncBytes = 4096;
 
-struct ChainParams {
-  const uint16_t* base;       // [B, M, V]
-  uint16_t* out;              // [B, M, V] or null
-  const int64_t* first_prev;  // [B]
-  int64_t* tokens;            // [B, M]
-  const uint16_t* w1;         // [V, r]
-  const uint16_t* w2;         // [V, r]
-  uint64_t* keys;             // [M][chain_key_groups()][chain_max_rows()] * kKeyPad
-  uint32_t* sync;             // kChainSyncBytes
-  uint32_t* bad_rows;
-  uint32_t* sync_failures;
-  int64_t B;
-  int64_t M;
-  int64_t V;
-  int64_t r;
-  int64_t S;                  // 32-column vocabulary slices
-};
 
 // The gate of the gated head, one launch per call (apply) or per step
 // (sampling): the latent rows u = rnd_W(rnd_W(sigmoid(rnd_W(z + b))) * e),
@@ -102,14 +82,6 @@ int gate_splits(int64_t rows, int64_t r, int64_t d, int64_t* kchunk);
 // matrix-core form needs bf16 weights, d % 8 == 0, r % 8 == 0 and 16-byte
 // aligned hidden, W1 and gate weight; otherwise a scalar form runs.
 hipError_t launch_gate(const GateParams& g, bool weights_bf16, bool hidden_f32, hipStream_t s);
-
-int chain_max_rows();
-int chain_key_groups();
-int chain_waves_per_group();
-hipError_t launch_chain_greedy(const ChainParams& p, int num_cus, hipStream_t s);
-
-// Rank blocks (of 16) the tile kernel is instantiated for, covering r; 0 if none.
-int tile_ks_for_rank(int64_t r);
 
 hipError_t launch_tile(const KernelParams& p, hipStream_t s);
 // Streaming teacher-forced apply (bf16); needs rows * V < 2^31 and a sink of
