@@ -654,3 +654,142 @@ int dspark_oracle_sample_block_gated(const void* base_logits, int logits_dtype,
   free(w2d);
   return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* Backward of the teacher-forced apply ([P5] module docstring: at     */
+/* train time the head runs teacher-forced; autograd of                 */
+/* apply_block_logits: logits + bias.to(logits.dtype), the Linear and  */
+/* the Embedding)                                                       */
+/* ------------------------------------------------------------------ */
+
+/* Given G = dloss/dcorrected [rows, V] (logits dtype L):
+ *   g[n, v]   = G[n, v] cast to W          (backward of the .to(L) cast)
+ *   dW2w[v, j] = sum_n g[n, v] e_n[j]       (Linear weight gradient, W)
+ *   de[n, j]  = sum_v g[n, v] W2w[v, j]     (Linear input gradient, W)
+ *   dW1[x, j] = sum over rows n with x_n = x of de[n, j]   (Embedding, W)
+ * Reading: each sum is modelled by its best fp32 value (double sum rounded
+ * once to fp32) and rounded to W; the Embedding gradient adds the W-typed
+ * de rows in row order; rows of W1 no id refers to get zero.  The base
+ * logits' gradient is G itself and is not computed. */
+static float grad_in_w(const void* grad, int ldt, int wdt, int64_t i) {
+  return round_to(load_as_float(grad, ldt, i), wdt);
+}
+
+int dspark_oracle_apply_block_backward(const void* grad, int logits_dtype,
+                                       const int64_t* token_ids, const void* w1,
+                                       const void* w2, int weight_dtype, int64_t rows,
+                                       int64_t V, int64_t r, void* dw1, void* dw2,
+                                       int n_threads) {
+  if (!valid_dtype(logits_dtype) || !valid_dtype(weight_dtype)) return ORACLE_UNSUPPORTED;
+  if (rows < 0 || V <= 0 || r <= 0) return ORACLE_INVALID;
+  if (!dw1 || !dw2 || (rows > 0 && (!grad || !token_ids || !w1 || !w2))) return ORACLE_INVALID;
+  for (int64_t n = 0; n < rows; ++n)
+    if (token_ids[n] < 0 || token_ids[n] >= V) return ORACLE_INVALID;
+  const int ldt = logits_dtype, wdt = weight_dtype;
+  int nt = n_threads_or_default(n_threads);
+  /* g in double, [rows, V] */
+  double* g = (double*)malloc((size_t)(rows * V + 1) * sizeof(double));
+  double* de = (double*)malloc((size_t)(rows * r + 1) * sizeof(double));
+  if (!g || !de) {
+    free(g);
+    free(de);
+    return ORACLE_INVALID;
+  }
+  for (int64_t i = 0; i < rows * V; ++i) g[i] = (double)grad_in_w(grad, ldt, wdt, i);
+  /* dW2w */
+#pragma omp parallel for num_threads(nt) schedule(static)
+  for (int64_t v = 0; v < V; ++v)
+    for (int64_t j = 0; j < r; ++j) {
+      double a = 0.0;
+      for (int64_t n = 0; n < rows; ++n) a += g[n * V + v] * load_as_double(w1, wdt, token_ids[n] * r + j);
+      store_from_float(dw2, wdt, v * r + j, round_to((float)a, wdt));
+    }
+  /* de, rounded to W */
+#pragma omp parallel for num_threads(nt) schedule(static)
+  for (int64_t n = 0; n < rows; ++n)
+    for (int64_t j = 0; j < r; ++j) {
+      double a = 0.0;
+      for (int64_t v = 0; v < V; ++v) a += g[n * V + v] * load_as_double(w2, wdt, v * r + j);
+      de[n * r + j] = (double)round_to((float)a, wdt);
+    }
+  /* dW1: zero, then the rows of each id summed in row order */
+  for (int64_t i = 0; i < V * r; ++i) store_from_float(dw1, wdt, i, 0.0f);
+  for (int64_t n = 0; n < rows; ++n) {
+    int first = 1;
+    for (int64_t m = 0; m < n; ++m)
+      if (token_ids[m] == token_ids[n]) first = 0;
+    if (!first) continue;
+    for (int64_t j = 0; j < r; ++j) {
+      double a = 0.0;
+      for (int64_t m = n; m < rows; ++m)
+        if (token_ids[m] == token_ids[n]) a += de[m * r + j];
+      store_from_float(dw1, wdt, token_ids[n] * r + j, round_to((float)a, wdt));
+    }
+  }
+  free(de);
+  free(g);
+  return ORACLE_OK;
+}
+
+/* Admissible intervals of the backward's outputs for a device that sums in
+ * fp32 in any order (twice Higham's bound, as for the forward):
+ *  dW2 element (v, j): the row sum pushed to -/+ 2 rows 2^-24 sum_n|g e|;
+ *  dW1 element (x, j): each contributing de[n, j] pushed to -/+ 2 V 2^-24
+ *  sum_v|g w| and rounded to W, the ends summed and widened by
+ *  2 cnt 2^-24 sum|de| for the fp32 row sum, then rounded to W.
+ * kind 2: elements are (v, j) of dW2; kind 1: (x, j) of dW1.  mid is the
+ * oracle's own value. */
+int dspark_oracle_backward_bounds(const void* grad, int logits_dtype,
+                                  const int64_t* token_ids, const void* w1,
+                                  const void* w2, int weight_dtype, int64_t rows,
+                                  int64_t V, int64_t r, int kind, int64_t n,
+                                  const int64_t* which, const int64_t* cols, float* lo,
+                                  float* mid, float* hi) {
+  if (!valid_dtype(logits_dtype) || !valid_dtype(weight_dtype)) return ORACLE_UNSUPPORTED;
+  if (rows < 0 || V <= 0 || r <= 0 || n < 0 || (kind != 1 && kind != 2)) return ORACLE_INVALID;
+  if (n == 0) return ORACLE_OK;
+  if (!grad || !token_ids || !w1 || !w2 || !which || !cols || !lo || !mid || !hi) return ORACLE_INVALID;
+  const int ldt = logits_dtype, wdt = weight_dtype;
+  const double u = ldexp(1.0, -24);
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t a0 = which[i], j = cols[i];
+    if (j < 0 || j >= r || a0 < 0 || a0 >= V) return ORACLE_INVALID;
+    if (kind == 2) {
+      double a = 0.0, s = 0.0;
+      for (int64_t m = 0; m < rows; ++m) {
+        double t = (double)grad_in_w(grad, ldt, wdt, m * V + a0) *
+                   load_as_double(w1, wdt, token_ids[m] * r + j);
+        a += t;
+        s += fabs(t);
+      }
+      const double d = 2.0 * (double)rows * u * s;
+      lo[i] = round_to((float)(a - d), wdt);
+      mid[i] = round_to((float)a, wdt);
+      hi[i] = round_to((float)(a + d), wdt);
+    } else {
+      double sl = 0.0, sm = 0.0, sh = 0.0, sa = 0.0;
+      int64_t cnt = 0;
+      for (int64_t m = 0; m < rows; ++m) {
+        if (token_ids[m] != a0) continue;
+        double a = 0.0, s = 0.0;
+        for (int64_t v = 0; v < V; ++v) {
+          double t = (double)grad_in_w(grad, ldt, wdt, m * V + v) * load_as_double(w2, wdt, v * r + j);
+          a += t;
+          s += fabs(t);
+        }
+        const double d = 2.0 * (double)V * u * s;
+        const double l = round_to((float)(a - d), wdt), h = round_to((float)(a + d), wdt);
+        sl += l;
+        sh += h;
+        sm += round_to((float)a, wdt);
+        sa += fabs(l) > fabs(h) ? fabs(l) : fabs(h);
+        ++cnt;
+      }
+      const double d2 = 2.0 * (double)cnt * u * sa;
+      lo[i] = round_to((float)(sl - d2), wdt);
+      mid[i] = round_to((float)sm, wdt);
+      hi[i] = round_to((float)(sh + d2), wdt);
+    }
+  }
+  return ORACLE_OK;
+}

@@ -17,6 +17,8 @@
  *        class _DeepseekV41DSparkMarkovHead.
  *   Gated head: [P5] GatedMarkovHead (compute_gate, compute_step_bias) and
  *        the [P3] API page's GatedMarkovHead (gate_proj = Linear(d + r, r)).
+ *   Backward: [P5] module docstring (train time is teacher-forced), taken
+ *        through autograd of apply_block_logits.
  *
  * Numeric reading (every step is written out in dspark_oracle.c):
  *   e      = W1[x, :]                                (exact, widened to double)
@@ -140,6 +142,24 @@ int dspark_oracle_sample_block_gated(const void* base_logits, int logits_dtype,
                                      int64_t batch_offset, int64_t* sampled_tokens,
                                      void* corrected_logits, void* latent_out,
                                      int n_threads);
+
+/* Backward of the teacher-forced apply (training): given the gradient of
+ * the loss w.r.t. the corrected logits, grad [rows, V] (logits dtype), the
+ * gradients of W1 (dense [V, r], zero where no id refers) and of W2w
+ * ([V, r]), both in the weight dtype.  The base logits' gradient is grad. */
+int dspark_oracle_apply_block_backward(const void* grad, int logits_dtype,
+                                       const int64_t* token_ids, const void* w1,
+                                       const void* w2, int weight_dtype, int64_t rows,
+                                       int64_t V, int64_t r, void* dw1, void* dw2,
+                                       int n_threads);
+/* Admissible intervals of chosen backward outputs: kind 2 = dW2w elements
+ * (which[i] = v), kind 1 = dW1 elements (which[i] = token x); cols[i] = j. */
+int dspark_oracle_backward_bounds(const void* grad, int logits_dtype,
+                                  const int64_t* token_ids, const void* w1,
+                                  const void* w2, int weight_dtype, int64_t rows,
+                                  int64_t V, int64_t r, int kind, int64_t n,
+                                  const int64_t* which, const int64_t* cols, float* lo,
+                                  float* mid, float* hi);
 
 /* Building blocks exposed for pinning. */
 void dspark_oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2],

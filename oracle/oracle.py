@@ -77,6 +77,11 @@ def lib():
             _p, _int, _p, _p, _int, _i64, _p, _p, _p, _p, _int, _i64, _i64, _i64, _i64,
             ctypes.c_double, ctypes.c_uint64, _i64, _i64, _p, _p, _p, _int]
         L.dspark_oracle_sample_block_gated.restype = _int
+        L.dspark_oracle_apply_block_backward.argtypes = [_p, _int, _p, _p, _p, _int, _i64, _i64, _i64, _p, _p, _int]
+        L.dspark_oracle_apply_block_backward.restype = _int
+        L.dspark_oracle_backward_bounds.argtypes = [
+            _p, _int, _p, _p, _p, _int, _i64, _i64, _i64, _int, _i64, _p, _p, _p, _p, _p]
+        L.dspark_oracle_backward_bounds.restype = _int
         L.dspark_oracle_philox4x32_10.argtypes = [_p, _p, _p]
         L.dspark_oracle_philox4x32_10.restype = None
         L.dspark_oracle_gumbel2.argtypes = [ctypes.c_uint64, _i64, _i64, _i64]
@@ -272,6 +277,35 @@ def sample_block_gated(base, first_prev, hidden, w1, w2, gate_w, gate_b, tempera
         int(position_offset), int(batch_offset), _ptr(tokens), _ptr(corrected), _ptr(lat),
         n_threads))
     return tokens, corrected, lat
+
+
+def apply_block_backward(grad, token_ids, w1, w2, n_threads: int = 0):
+    """Gradients (dW1 [V, r], dW2w [V, r]) of the teacher-forced apply for the
+    upstream gradient grad [..., V] of the corrected logits."""
+    grad, w1, w2 = _c(grad), _c(w1), _c(w2)
+    ids = _c(token_ids, np.int64).reshape(-1)
+    V, r = w1.shape
+    dw1 = np.zeros_like(w1)
+    dw2 = np.zeros_like(w2)
+    _check(lib().dspark_oracle_apply_block_backward(
+        _ptr(grad), _dtype_tag(grad), _ptr(ids), _ptr(w1), _ptr(w2), _dtype_tag(w1), ids.shape[0], V, r,
+        _ptr(dw1), _ptr(dw2), n_threads))
+    return dw1, dw2
+
+
+def backward_bounds(grad, token_ids, w1, w2, kind, which, cols):
+    """Admissible [lo, hi] and the oracle's value for backward outputs:
+    kind "dw2" (which = vocabulary rows v) or "dw1" (which = token ids x)."""
+    grad, w1, w2 = _c(grad), _c(w1), _c(w2)
+    ids = _c(token_ids, np.int64).reshape(-1)
+    which, cols = _c(which, np.int64), _c(cols, np.int64)
+    n = which.shape[0]
+    lo, mid, hi = (np.zeros(n, dtype=np.float32) for _ in range(3))
+    V, r = w1.shape
+    _check(lib().dspark_oracle_backward_bounds(
+        _ptr(grad), _dtype_tag(grad), _ptr(ids), _ptr(w1), _ptr(w2), _dtype_tag(w1), ids.shape[0], V, r,
+        2 if kind == "dw2" else 1, n, _ptr(which), _ptr(cols), _ptr(lo), _ptr(mid), _ptr(hi)))
+    return lo, mid, hi
 
 
 def philox4x32_10(ctr, key):

@@ -646,3 +646,100 @@ def test_gated_chain_equals_teacher_forced(oracle_mod, T):
                                              inp["gate_w"], inp["gate_b"])
     assert np.array_equal(as_float(corr), as_float(out))
     assert np.array_equal(as_float(lat), as_float(lat2))
+
+
+# ------------------------------------------------- backward (training)
+def _torch_backward_f64(grad, ids, w1, w2):
+    """The pages' teacher-forced forward (Embedding, Linear, add) built from
+    torch modules in float64, differentiated by autograd for the loss
+    sum(grad * corrected)."""
+    V, r = w1.shape
+    emb = torch.nn.Embedding(V, r, dtype=torch.float64)
+    lin = torch.nn.Linear(r, V, bias=False, dtype=torch.float64)
+    with torch.no_grad():
+        emb.weight.copy_(torch.from_numpy(np.asarray(w1, dtype=np.float64)))
+        lin.weight.copy_(torch.from_numpy(np.asarray(w2, dtype=np.float64)))
+    base = torch.zeros(grad.shape, dtype=torch.float64)
+    out = base + lin(emb(torch.from_numpy(ids)))
+    (out * torch.from_numpy(np.asarray(grad, dtype=np.float64))).sum().backward()
+    return emb.weight.grad.numpy(), lin.weight.grad.numpy()
+
+
+def test_backward_matches_autograd(oracle_mod):
+    """fp32: the oracle's gradients equal torch autograd's (float64) of the
+    literal Embedding + Linear forward, to fp32 rounding; repeated ids add."""
+    rng = np.random.default_rng(11)
+    B, M, V, r = 3, 4, 257, 24
+    w1 = rng.standard_normal((V, r)).astype(np.float32) * 0.05
+    w2 = rng.standard_normal((V, r)).astype(np.float32) * 0.05
+    ids = rng.integers(0, 40, size=(B, M)).astype(np.int64)   # repeats
+    grad = rng.standard_normal((B, M, V)).astype(np.float32)
+    dw1, dw2 = oracle_mod.apply_block_backward(grad, ids, w1, w2)
+    t1, t2 = _torch_backward_f64(grad, ids, w1, w2)
+    assert np.allclose(dw2, t2, rtol=1e-6, atol=1e-7)
+    assert np.allclose(dw1, t1, rtol=1e-5, atol=1e-6)
+    untouched = np.setdiff1d(np.arange(V), ids)
+    assert np.all(dw1[untouched] == 0)
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_backward_exact_dyadic(oracle_mod, dtype):
+    """Dyadic inputs on which every sum is exact: dW2w = g^T E, de = g W2w,
+    dW1 = the de rows added per id (numpy matmul and add.at)."""
+    rng = np.random.default_rng(5)
+    rows, V, r = 12, 40, 8
+    w1 = rng.integers(-4, 5, size=(V, r)).astype(np.float32) / 8
+    w2 = rng.integers(-4, 5, size=(V, r)).astype(np.float32) / 16
+    grad = rng.integers(-8, 9, size=(rows, V)).astype(np.float32) / 8
+    ids = rng.integers(0, 6, size=rows).astype(np.int64)
+    E = w1[ids]
+    want2 = grad.T.astype(np.float64) @ E
+    de = grad.astype(np.float64) @ w2
+    want1 = np.zeros((V, r))
+    np.add.at(want1, ids, de)
+    conv = (lambda a: wl.to_bf16_bits(a)) if dtype == wl.BF16 else (lambda a: a)
+    dw1, dw2 = oracle_mod.apply_block_backward(conv(grad), ids, conv(w1), conv(w2))
+    assert np.array_equal(as_float(dw2), want2.astype(np.float32))
+    assert np.array_equal(as_float(dw1), want1.astype(np.float32))
+
+
+def test_backward_roundings(oracle_mod):
+    """bf16 weights with fp32 gradients: the gradient is cast to bf16 before
+    the products (the backward of .to(logits.dtype)), and each row's input
+    gradient de is rounded to bf16 before the rows of one id are added.
+    Both cases use cancellation so that the missing rounding shows."""
+    V, r = 8, 2
+    w1 = np.zeros((V, r), np.float32)
+    w1[3] = [1.0, 0.0]
+    w2 = np.zeros((V, r), np.float32)
+    w2[5] = [1.0, 0.0]
+    w2[6] = [5 * 2.0**-10, 0.0]
+    grad = np.zeros((4, V), np.float32)
+    grad[0, 5] = 1 + 2**-10            # cast: 1
+    grad[1, 5] = -1.0                  # rows 0, 1: id 3, e = (1, 0)
+    grad[2, 5] = 1.0
+    grad[2, 6] = 1.0                   # de[2, 0] = 1 + 5 2^-10, rounded to 1 + 2^-7
+    grad[3, 5] = -1.0                  # rows 2, 3: id 4, e = 0
+    ids = np.array([3, 3, 4, 4], np.int64)
+    dw1, dw2 = oracle_mod.apply_block_backward(grad, ids, wl.to_bf16_bits(w1), wl.to_bf16_bits(w2))
+    assert as_float(dw2)[5, 0] == 0.0            # 1 * 1 + (-1) * 1; uncast: 2^-10
+    assert as_float(dw1)[3, 0] == 0.0
+    assert as_float(dw1)[4, 0] == 2.0**-7        # (1 + 2^-7) - 1; unrounded de: 5 2^-10
+    assert np.all(as_float(dw1)[[0, 1, 2, 5, 6, 7]] == 0)
+
+
+def test_backward_zero_gradient_and_bounds(oracle_mod):
+    w = wl.WORKLOADS["teacher_forced_320"]
+    inp = wl.make_inputs(w, B=2, M=3, V=300, r=16, seed=3)
+    dw1, dw2 = oracle_mod.apply_block_backward(np.zeros_like(inp["base"]), inp["token_ids"], inp["w1"], inp["w2"])
+    assert not as_float(dw1).any() and not as_float(dw2).any()
+    grad = inp["base"]
+    dw1, dw2 = oracle_mod.apply_block_backward(grad, inp["token_ids"], inp["w1"], inp["w2"])
+    rng = np.random.default_rng(0)
+    v = rng.integers(0, 300, 50)
+    j = rng.integers(0, 16, 50)
+    lo, mid, hi = oracle_mod.backward_bounds(grad, inp["token_ids"], inp["w1"], inp["w2"], "dw2", v, j)
+    assert np.array_equal(mid, as_float(dw2)[v, j]) and np.all(lo <= mid) and np.all(mid <= hi)
+    x = inp["token_ids"].reshape(-1)[rng.integers(0, 6, 50)]
+    lo, mid, hi = oracle_mod.backward_bounds(grad, inp["token_ids"], inp["w1"], inp["w2"], "dw1", x, j)
+    assert np.array_equal(mid, as_float(dw1)[x, j]) and np.all(lo <= mid) and np.all(mid <= hi)
