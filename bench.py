@@ -123,6 +123,14 @@ def algorithmic_bytes_apply(w) -> int:
     return w.B * w.M * w.V * lb * 2 + w.V * w.r * wb + w.B * w.M * (w.r * wb + 8)
 
 
+def algorithmic_bytes_backward(w) -> int:
+    """Bytes the backward must move at least: the gradient of the logits
+    read, W2 read, the gathered W1 rows, dW2 and the dense dW1 written."""
+    lb = 2 if w.ldtype == 1 else 4
+    wb = 2 if w.dtype == 1 else 4
+    return w.B * w.M * w.V * lb + 3 * w.V * w.r * wb + w.B * w.M * (w.r * wb + 8)
+
+
 def algorithmic_bytes_gate(w) -> int:
     """Extra bytes of the gated head: hidden states read, gate_proj weight and
     bias read once (the latent rows stay in cache-sized scratch)."""
@@ -183,17 +191,21 @@ def measure_extra(name, rmd, wl, torch, np, steps=10, warmup=3):
     n_sets = max(2, int(np.ceil(600e6 / per_set)))
     sets = []
     for i in range(n_sets):
-        keys = ("base", "first_prev", "token_ids", "w1", "w2") + (("hidden", "gate_w", "gate_b") if w.hidden else ())
+        keys = ("base", "first_prev", "token_ids", "w1", "w2") + (("hidden", "gate_w", "gate_b") if w.hidden else ()) \
+            + (("grad",) if w.mode == "backward" else ())
         d = {k: to_dev(inp[k], torch, np) for k in keys}
         d["out"] = torch.empty_like(d["base"]) if (w.mode == "apply" or w.return_logits) else None
         d["tok"] = torch.empty((w.B, w.M), dtype=torch.int64, device="cuda")
-        d["ws"] = rmd.Workspace(w.B, w.M, w.V, w.r, sample=(w.mode != "apply"), hidden=w.hidden or None)
+        d["ws"] = rmd.Workspace(w.B, w.M, w.V, w.r, sample=(w.mode not in ("apply", "backward")),
+                                hidden=w.hidden or None, backward=(w.mode == "backward"))
         sets.append(d)
     del inp
 
     def call(i):
         d = sets[i]
-        if w.hidden and w.mode == "apply":
+        if w.mode == "backward":
+            rmd.apply_block_logits_backward(d["grad"], d["token_ids"], d["w1"], d["w2"], workspace=d["ws"])
+        elif w.hidden and w.mode == "apply":
             rmd.apply_block_logits_gated(d["base"], d["token_ids"], d["w1"], d["w2"], d["gate_w"], d["gate_b"],
                                          d["hidden"], out=d["out"], workspace=d["ws"])
         elif w.hidden:
@@ -209,12 +221,17 @@ def measure_extra(name, rmd, wl, torch, np, steps=10, warmup=3):
 
     wall, per = time_calls(call, n_sets, steps, warmup, torch)
     ms = float(np.mean(per))
-    alg = algorithmic_bytes_apply(w) if w.mode == "apply" else algorithmic_bytes_sample(w, w.return_logits)
+    if w.mode == "backward":
+        alg = algorithmic_bytes_backward(w)
+    elif w.mode == "apply":
+        alg = algorithmic_bytes_apply(w)
+    else:
+        alg = algorithmic_bytes_sample(w, w.return_logits)
     alg += algorithmic_bytes_gate(w)
     res = {"ms_per_call": ms, "elems_per_s": w.B * w.M * w.V / (ms * 1e-3),
            "algorithmic_GBps": alg / (ms * 1e-3) / 1e9,
            "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": alg}
-    if w.mode != "apply":
+    if w.mode not in ("apply", "backward"):
         res["tokens_per_s"] = w.B * w.M / (ms * 1e-3)
     del sets
     torch.cuda.empty_cache()
@@ -309,7 +326,7 @@ def main():
         result["other_workloads"] = {n: measure_extra(n, rmd, wl, torch, np) for n in
                                      ("teacher_forced_320", "teacher_forced_2560_zipf", "temperature_draft_256x8",
                                       "teacher_forced_320_f32logits", "gated_teacher_forced_320",
-                                      "gated_greedy_draft_64x5")}
+                                      "gated_greedy_draft_64x5", "teacher_forced_320_backward")}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, np)
     print(json.dumps(result))

@@ -169,6 +169,31 @@ dspark_status_t dspark_markov_sample_block_gated(
     void* corrected_logits, void* latent_out, void* workspace, size_t workspace_bytes,
     void* stream);
 
+/* Backward of the teacher-forced apply (training; the third-party
+ * markov_head.py page trains the head teacher-forced, through
+ * apply_block_logits).  Given the gradient of the loss w.r.t. the corrected
+ * logits, grad_corrected (device, [B, M, V], logits_dtype), writes
+ *   grad_w2 [V, r] (the Linear weight's gradient):  sum_n g[n, v] W1[x_n],
+ *   grad_w1 [V, r] (the Embedding's gradient, dense): for each id x the sum
+ *           over its rows n of de[n] = sum_v g[n, v] W2w[v], zero for ids
+ *           no row refers to,
+ * both in weight_dtype, with g = grad_corrected cast to the weight dtype,
+ * each product summed in fp32 and rounded once to the weight dtype (de
+ * too, before the rows of one id are added in row order).  The base
+ * logits' gradient is grad_corrected itself.  Rows whose id is outside
+ * [0, V) contribute nothing and are counted in the device error word.
+ * B*M == 0 writes zero gradients.  The workspace must hold
+ * dspark_markov_backward_workspace_bytes(...) bytes (no zero fill
+ * needed beyond the vanilla rule for the error word).  Outputs must not
+ * overlap inputs or each other. */
+size_t dspark_markov_backward_workspace_bytes(int64_t B, int64_t M, int64_t V, int64_t r);
+
+dspark_status_t dspark_markov_apply_block_backward(const void* grad_corrected, dspark_dtype_t logits_dtype,
+                                                   const int64_t* token_ids, const void* w1, const void* w2,
+                                                   dspark_dtype_t weight_dtype, int64_t B, int64_t M, int64_t V,
+                                                   int64_t r, void* grad_w1, void* grad_w2, void* workspace,
+                                                   size_t workspace_bytes, void* stream);
+
 /* Synchronises `stream`, then returns in *bad_rows the number of rows whose
  * predecessor id was outside [0, V) in the calls made with this workspace
  * since the last read, and clears the count. */

@@ -9,6 +9,9 @@ VanillaMarkov methods (third-party markov_head.py page):
   temperature=0.0, ...)`` -- left-to-right sampling, each position biased by
   the token drawn at the previous one.
 
+``apply_block_logits_backward`` gives the gradients of W1 and W2 for a
+gradient of the teacher-forced corrected logits (training).
+
 The gated head (the pages' GatedMarkovHead) has the same two operations,
 ``apply_block_logits_gated`` and ``sample_block_tokens_gated``, which also
 take the backbone hidden states and the gate_proj weight and bias.
@@ -29,7 +32,8 @@ import torch
 from . import _lib
 
 __all__ = ["apply_block_logits", "sample_block_tokens", "apply_block_logits_gated",
-           "sample_block_tokens_gated", "Workspace", "read_device_error", "workspace_bytes"]
+           "sample_block_tokens_gated", "apply_block_logits_backward", "Workspace", "read_device_error",
+           "workspace_bytes"]
 
 
 def _dtype_tag(t: torch.Tensor) -> int:
@@ -58,15 +62,18 @@ def workspace_bytes(B: int, M: int, V: int, r: int, sample: bool, hidden: int | 
 
 class Workspace:
     """Device workspace for a family of calls of at most the given sizes
-    (``hidden``: the hidden size of gated calls).
+    (``hidden``: the hidden size of gated calls; ``backward``: sized for the
+    backward as well).
 
     Zero-filled once at creation; the library leaves it ready for the next
     call.  Calls sharing one workspace must be ordered on one stream."""
 
     def __init__(self, B: int, M: int, V: int, r: int, sample: bool, device=None,
-                 hidden: int | None = None):
+                 hidden: int | None = None, backward: bool = False):
         device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
         self.nbytes = max(workspace_bytes(B, M, V, r, sample, hidden), 256)
+        if backward:
+            self.nbytes = max(self.nbytes, int(_lib.load().dspark_markov_backward_workspace_bytes(B, M, V, r)))
         self.buffer = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
         _lib.check(_lib.load().dspark_markov_workspace_init(
             _ptr(self.buffer), self.nbytes, _stream_handle(device)), "workspace_init")
@@ -278,3 +285,35 @@ def sample_block_tokens_gated(base_logits: torch.Tensor, first_prev_token_ids: t
         workspace.ptr, workspace.nbytes, _stream_handle(dev))
     _lib.check(st, "sample_block_tokens_gated")
     return (tokens, corrected, latent) if return_latent else (tokens, corrected)
+
+
+def apply_block_logits_backward(grad_corrected: torch.Tensor, token_ids: torch.Tensor, w1: torch.Tensor,
+                                w2: torch.Tensor, *, workspace: Workspace | None = None):
+    """Gradients (grad_w1 [V, r], grad_w2 [V, r]) of the teacher-forced apply
+    for the gradient of the corrected logits grad_corrected [..., M, V]; the
+    base logits' gradient is grad_corrected itself."""
+    _check_weights(w1, w2)
+    if grad_corrected.dim() < 2:
+        raise ValueError("grad_corrected must be [..., M, V]")
+    V, M = grad_corrected.shape[-1], grad_corrected.shape[-2]
+    B = 1
+    for s_ in grad_corrected.shape[:-2]:
+        B *= int(s_)
+    if tuple(token_ids.shape) != tuple(grad_corrected.shape[:-1]):
+        raise ValueError(f"token_ids {tuple(token_ids.shape)} must be grad_corrected.shape[:-1]")
+    if w1.shape[0] != V:
+        raise ValueError(f"weights have vocabulary {w1.shape[0]}, logits {V}")
+    r = w1.shape[1]
+    dev = grad_corrected.device
+    g = grad_corrected.contiguous()
+    ids = token_ids.to(torch.int64).contiguous()
+    w1c, w2c = w1.contiguous(), w2.contiguous()
+    gw1 = torch.empty_like(w1c)
+    gw2 = torch.empty_like(w2c)
+    if workspace is None:
+        workspace = Workspace(B, M, V, r, sample=False, device=dev, backward=True)
+    st = _lib.load().dspark_markov_apply_block_backward(
+        _ptr(g), _dtype_tag(g), _ptr(ids), _ptr(w1c), _ptr(w2c), _dtype_tag(w1c), B, M, V, r, _ptr(gw1), _ptr(gw2),
+        workspace.ptr, workspace.nbytes, _stream_handle(dev))
+    _lib.check(st, "apply_block_logits_backward")
+    return gw1, gw2

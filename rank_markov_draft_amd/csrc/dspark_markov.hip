@@ -548,6 +548,66 @@ dspark_status_t dspark_markov_sample_block_gated(
   return DSPARK_OK;
 }
 
+size_t dspark_markov_backward_workspace_bytes(int64_t B, int64_t M, int64_t V, int64_t r) {
+  if (B < 0 || M < 0 || V < 0 || r <= 0) return kControlBytes;
+  const int64_t rows = B * M;
+  int64_t sl = 0;
+  const int64_t S = V > 0 ? dspark::backward_slices(V, &sl) : 0;
+  return kControlBytes + align256((size_t)(rows * r) * 4) + align256((size_t)S * (size_t)(rows * r) * 4) +
+         align256((size_t)rows * 8);
+}
+
+dspark_status_t dspark_markov_apply_block_backward(const void* grad_corrected, dspark_dtype_t logits_dtype,
+                                                   const int64_t* token_ids, const void* w1, const void* w2,
+                                                   dspark_dtype_t weight_dtype, int64_t B, int64_t M, int64_t V,
+                                                   int64_t r, void* grad_w1, void* grad_w2, void* workspace,
+                                                   size_t workspace_bytes, void* stream) {
+  int64_t elems = 0;
+  dspark_status_t st = check_common(logits_dtype, weight_dtype, B, M, V, r, &elems);
+  if (st != DSPARK_OK) return st;
+  if (V == 0) return DSPARK_OK;   // no parameters
+  if (!w1 || !w2 || !grad_w1 || !grad_w2) return DSPARK_ERR_INVALID_ARGUMENT;
+  const int64_t rows = B * M;
+  if (rows > 0 && (!grad_corrected || !token_ids)) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < dspark_markov_backward_workspace_bytes(B, M, V, r))
+    return DSPARK_ERR_WORKSPACE_TOO_SMALL;
+  const size_t lbytes = (size_t)elems * dtype_bytes(logits_dtype);
+  const size_t wbytes = (size_t)(V * r) * dtype_bytes(weight_dtype);
+  const void* ins[4] = {grad_corrected, token_ids, w1, w2};
+  const size_t ins_bytes[4] = {lbytes, (size_t)rows * sizeof(int64_t), wbytes, wbytes};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(grad_w1, wbytes, ins[i], ins_bytes[i]) || overlaps(grad_w2, wbytes, ins[i], ins_bytes[i]))
+      return DSPARK_ERR_INVALID_ARGUMENT;
+  if (overlaps(grad_w1, wbytes, grad_w2, wbytes)) return DSPARK_ERR_INVALID_ARGUMENT;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (rows == 0) {   // no rows: both gradients are zero
+    e = dspark::launch_fill_zero(grad_w1, wbytes, s);
+    if (e == hipSuccess) e = dspark::launch_fill_zero(grad_w2, wbytes, s);
+    if (e != hipSuccess) return device_failure(e, "backward fill");
+    return DSPARK_OK;
+  }
+  dspark::BwdParams p{};
+  p.grad = grad_corrected;
+  p.ids = token_ids;
+  p.w1 = w1;
+  p.w2 = w2;
+  p.dw1 = grad_w1;
+  p.dw2 = grad_w2;
+  char* const region = (char*)workspace + kControlBytes;
+  p.de = region;
+  p.S = dspark::backward_slices(V, &p.SL);
+  p.partials = (float*)(region + align256((size_t)(rows * r) * 4));
+  p.link = (int32_t*)((char*)p.partials + align256((size_t)p.S * (size_t)(rows * r) * 4));
+  p.bad_rows = &((Control*)workspace)->bad_rows;
+  p.rows = rows;
+  p.V = V;
+  p.r = r;
+  e = dspark::launch_backward(p, logits_dtype == DSPARK_BF16, weight_dtype == DSPARK_BF16, s);
+  if (e != hipSuccess) return device_failure(e, "backward launch");
+  return DSPARK_OK;
+}
+
 dspark_status_t dspark_markov_read_device_error(void* workspace, void* stream, int64_t* bad_rows) {
   if (!workspace || !bad_rows) return DSPARK_ERR_INVALID_ARGUMENT;
   hipStream_t s = (hipStream_t)stream;

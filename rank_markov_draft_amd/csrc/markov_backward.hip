@@ -1,0 +1,428 @@
+// markov_backward.hip -- backward of the teacher-forced apply (training): the
+// head is trained teacher-forced (the markov_head.py page's module
+// docstring), so its gradients are those of apply_block_logits,
+//   corrected = base + (W2w . W1[x]).to(L).
+// Given G = dloss/dcorrected [rows, V]:
+//   g          = G cast to the weight dtype W (backward of the cast)
+//   dW2w[v, :] = sum_n g[n, v] W1[x_n]           (rounded once to W)
+//   de[n, :]   = sum_v g[n, v] W2w[v, :]         (rounded once to W)
+//   dW1[x, :]  = sum over rows n with x_n = x of de[n, :], in row order
+// and the base logits' gradient is G itself (nothing to compute).
+//
+// Four launches on the bf16-weight path:
+//   markov_bwd_dw2_bf16   V-sliced: each workgroup streams its 256 columns of
+//                         g for all rows, with g and the gathered W1 rows
+//                         staged transposed through LDS, and keeps its
+//                         [256 x r] gradient block in registers;
+//   markov_bwd_de_bf16    g . W2w split along V: each workgroup multiplies its
+//                         rows by one 1024-column slice of W2w (staged
+//                         transposed through LDS) into fp32 partial sums;
+//   markov_bwd_de_finish  the slices' partial sums added in slice order;
+//   markov_bwd_dw1        the de rows of each id added in row order (after a
+//                         pass that links the rows of equal ids).
+// Scalar forms cover fp32 weights and other shapes.
+#include "device_common.h"
+#include "markov_kernels.h"
+
+namespace dspark {
+
+namespace {
+
+__device__ __forceinline__ float bf16_value(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ float round_to_bf16(float x) { return (float)(__bf16)x; }
+__device__ __forceinline__ uint16_t bf16_bits(float x) { return (uint16_t)(__float_as_uint(round_to_bf16(x)) >> 16); }
+
+// 8 values of g (columns c .. c + 7 of row n) as bf16, from bf16 or fp32 G.
+template <bool LF32>
+__device__ __forceinline__ u32x4_t load_g8(const void* grad, int64_t off) {
+  if constexpr (LF32) {
+    const u32x4_t lo = *(const u32x4_t*)((const float*)grad + off);
+    const u32x4_t hi = *(const u32x4_t*)((const float*)grad + off + 4);
+    return u32x4_t{pack_bf16x2(__uint_as_float(lo.x), __uint_as_float(lo.y)),
+                   pack_bf16x2(__uint_as_float(lo.z), __uint_as_float(lo.w)),
+                   pack_bf16x2(__uint_as_float(hi.x), __uint_as_float(hi.y)),
+                   pack_bf16x2(__uint_as_float(hi.z), __uint_as_float(hi.w))};
+  } else {
+    return *(const u32x4_t*)((const uint16_t*)grad + off);
+  }
+}
+
+// Store two source rows' 8 bf16 values (a: row 2 np, b: row 2 np + 1) as the
+// 32-bit column pair np of 8 consecutive rows of a transposed LDS tile (row
+// stride `stride` bytes).  Lanes of a wave take 16 column pairs and 4
+// pieces, so one 32-bit store per lane meets at most 2-way bank conflicts.
+__device__ __forceinline__ void store_t8x2(unsigned char* base, int stride, int np, u32x4_t a, u32x4_t b) {
+  const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
+  const uint32_t wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t lo = (c & 1) ? wa[c >> 1] >> 16 : wa[c >> 1] & 0xFFFFu;
+    const uint32_t hi = (c & 1) ? wb[c >> 1] >> 16 : wb[c >> 1] & 0xFFFFu;
+    *(uint32_t*)(base + c * stride + np * 4) = lo | (hi << 16);
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- dW2 (bf16)
+// Workgroup: columns v0 .. v0 + 255 (8 waves x 32).  Chunks of 32 rows: the
+// g tile [32 x 256] and the gathered rows E = W1[x_n] [32 x r] go to LDS as
+// gT [256][32] and eT [r][32] (rows of 64 bytes plus 16 of padding), then
+// wave w multiplies D[j][v] += eT[j][n] gT[v][n] over the chunk's 32 rows
+// for its v blocks 2w, 2w + 1 and every 16-unit block of r
+// (v_mfma_f32_16x16x32_bf16: rank units on M, columns on N, rows on K).
+constexpr int kBwdStride = 80;    // LDS bytes per transposed row (32 bf16 + pad)
+
+template <int JB, bool LF32>
+__global__ __launch_bounds__(512) void markov_bwd_dw2_bf16(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds_g[256 * kBwdStride];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_e[JB * 16 * kBwdStride];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int64_t V = p.V;
+  const int r = (int)p.r;
+  const int rows = (int)p.rows;
+  const int64_t v0 = (int64_t)blockIdx.x * 256;
+  constexpr int EP = JB * 2;          // 16-byte pieces per gathered row (JB*16 units), <= 32
+
+  f32x4_t acc[JB][2];
+#pragma unroll
+  for (int jb = 0; jb < JB; ++jb) acc[jb][0] = acc[jb][1] = f32x4_t{};
+
+  // thread t: row pair np = t % 16 (rows n0 + 2 np, + 1) and piece t / 16
+  // (8 columns of g: 32 pieces; 8 units of W1: EP pieces)
+  const int np = tid & 15;
+  const int pq = tid >> 4;
+  auto load_chunk = [&](int n0, u32x4_t gv[2], u32x4_t ev[2]) __attribute__((always_inline)) {
+    const int64_t c = v0 + 8 * pq;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n = n0 + 2 * np + h;
+      gv[h] = (n < rows && c < V) ? load_g8<LF32>(p.grad, (int64_t)n * V + c) : u32x4_t{0u, 0u, 0u, 0u};
+      ev[h] = u32x4_t{0u, 0u, 0u, 0u};
+      if (pq < EP && n < rows && 8 * pq < r) {
+        const int64_t x = p.ids[n];
+        if (x >= 0 && x < V) ev[h] = *(const u32x4_t*)((const uint16_t*)p.w1 + x * r + 8 * pq);
+      }
+    }
+  };
+  u32x4_t gv[2], ev[2];
+  load_chunk(0, gv, ev);
+  for (int n0 = 0; n0 < rows; n0 += 32) {
+    __syncthreads();   // the previous chunk's products are done with LDS
+    store_t8x2(lds_g + (8 * pq) * kBwdStride, kBwdStride, np, gv[0], gv[1]);
+    if (pq < EP) store_t8x2(lds_e + (8 * pq) * kBwdStride, kBwdStride, np, ev[0], ev[1]);
+    __syncthreads();
+    if (n0 + 32 < rows) load_chunk(n0 + 32, gv, ev);   // next chunk in flight
+    bf16x8_t b[2];
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+      b[vb] = *(const bf16x8_t*)(lds_g + ((2 * wave + vb) * 16 + n16) * kBwdStride + g4 * 16);
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      const bf16x8_t a = *(const bf16x8_t*)(lds_e + (jb * 16 + n16) * kBwdStride + g4 * 16);
+      acc[jb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[0], acc[jb][0], 0, 0, 0);
+      acc[jb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[1], acc[jb][1], 0, 0, 0);
+    }
+  }
+  // lane: column v = v0 + 32 wave + 16 vb + n16, units 16 jb + 4 g4 .. + 3
+#pragma unroll
+  for (int vb = 0; vb < 2; ++vb) {
+    const int64_t v = v0 + 32 * wave + 16 * vb + n16;
+    if (v >= V) continue;
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      const int j = 16 * jb + 4 * g4;
+      if (j >= r) continue;
+      const f32x4_t a = acc[jb][vb];
+      uint2 w;
+      w.x = pack_bf16x2(a[0], a[1]);
+      w.y = pack_bf16x2(a[2], a[3]);
+      *(uint2*)((uint16_t*)p.dw2 + v * r + j) = w;   // r % 8 == 0: 4 units stay in the row
+    }
+  }
+}
+
+// ---------------------------------------------------------------- de (bf16)
+// Workgroup (slice s, row group): rows 256 rg .. + 255 (wave w: 16 rows),
+// columns [s SL, (s + 1) SL).  Chunks of 32 columns: W2w[32 x r] goes to LDS
+// transposed as w2T[r][32]; wave w multiplies D[n][j] += g[n][c] w2T[j][c]
+// (rows on M, rank units on N, columns on K), its g pieces loaded straight
+// from memory one chunk ahead.  Partial sums [S][rows][r] fp32.
+template <int JB, bool LF32>
+__global__ __launch_bounds__(1024) void markov_bwd_de_bf16(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds_w[JB * 16 * kBwdStride];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int64_t V = p.V;
+  const int r = (int)p.r;
+  const int rows = (int)p.rows;
+  const int s = (int)(blockIdx.x % (unsigned)p.S);
+  const int rg = (int)(blockIdx.x / (unsigned)p.S);
+  const int64_t c0 = (int64_t)s * p.SL;
+  const int64_t c1 = (c0 + p.SL < V) ? c0 + p.SL : V;
+  const int n = rg * 256 + 16 * wave + n16;   // A row of this lane
+  const bool nrow = n < rows;
+  constexpr int WP = JB * 2;                  // 16-byte pieces per W2w row (<= 32)
+  // W2w staging: thread t < 16 WP takes row pair t % 16 of the chunk's 32
+  // rows and piece t / 16
+  const int np = tid & 15;
+  const int pq = tid >> 4;
+  const bool wthread = pq < WP;
+
+  f32x4_t acc[JB];
+#pragma unroll
+  for (int jb = 0; jb < JB; ++jb) acc[jb] = f32x4_t{};
+
+  auto load_a = [&](int64_t c) __attribute__((always_inline)) -> u32x4_t {
+    const int64_t col = c + 8 * g4;
+    return (nrow && col < c1) ? load_g8<LF32>(p.grad, (int64_t)n * V + col) : u32x4_t{0u, 0u, 0u, 0u};
+  };
+  auto load_w = [&](int64_t c, u32x4_t wv[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t v = c + 2 * np + h;
+      wv[h] = (wthread && v < c1 && 8 * pq < r) ? *(const u32x4_t*)((const uint16_t*)p.w2 + v * r + 8 * pq)
+                                                 : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  u32x4_t av = load_a(c0);
+  u32x4_t wv[2];
+  load_w(c0, wv);
+  for (int64_t c = c0; c < c1; c += 32) {
+    __syncthreads();
+    if (wthread) store_t8x2(lds_w + (8 * pq) * kBwdStride, kBwdStride, np, wv[0], wv[1]);
+    __syncthreads();
+    const u32x4_t a = av;
+    if (c + 32 < c1) {   // next chunk in flight during the products
+      av = load_a(c + 32);
+      load_w(c + 32, wv);
+    }
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      const bf16x8_t b = *(const bf16x8_t*)(lds_w + (jb * 16 + n16) * kBwdStride + g4 * 16);
+      acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), b, acc[jb], 0, 0, 0);
+    }
+  }
+  // lane: unit j = 16 jb + n16, rows n0 + 4 g4 .. + 3 of the wave's 16
+  float* const part = p.partials + (int64_t)s * rows * r;
+#pragma unroll
+  for (int jb = 0; jb < JB; ++jb) {
+    const int j = 16 * jb + n16;
+    if (j >= r) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = rg * 256 + 16 * wave + 4 * g4 + i;
+      if (row < rows) part[(int64_t)row * r + j] = acc[jb][i];
+    }
+  }
+}
+
+// de[n][j] = rnd_W(sum of the S slices' partial sums, in slice order).
+template <bool W_BF16>
+__global__ __launch_bounds__(256) void markov_bwd_de_finish(BwdParams p) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = p.rows * p.r;
+  if (t >= total) return;
+  float part[16];
+  float z = 0.0f;
+  for (int64_t s0 = 0; s0 < p.S; s0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part[i] = s0 + i < p.S ? p.partials[(s0 + i) * total + t] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (s0 + i < p.S) z += part[i];
+  }
+  if (W_BF16)
+    ((uint16_t*)p.de)[t] = bf16_bits(z);
+  else
+    ((float*)p.de)[t] = z;
+}
+
+// ---------------------------------------------------------------- scalar forms
+template <bool L_BF16, bool W_BF16>
+__device__ __forceinline__ float g_value(const BwdParams& p, int64_t i) {
+  const float x = L_BF16 ? bf16_value(((const uint16_t*)p.grad)[i]) : ((const float*)p.grad)[i];
+  return W_BF16 ? round_to_bf16(x) : x;
+}
+template <bool W_BF16>
+__device__ __forceinline__ float w_value(const void* w, int64_t i) {
+  return W_BF16 ? bf16_value(((const uint16_t*)w)[i]) : ((const float*)w)[i];
+}
+
+// Compensated fp32 sum (Kahan): the scalar forms reduce over up to V
+// products, and fp32 weights keep their result to fp32 accuracy.
+struct KahanSum {
+  float s = 0.0f, c = 0.0f;
+  __device__ __forceinline__ void add(float x) {
+    const float y = x - c;
+    const float t = s + y;
+    c = (t - s) - y;
+    s = t;
+  }
+};
+
+// dW2w[v][j], one thread each, rows in order.
+template <bool L_BF16, bool W_BF16>
+__global__ __launch_bounds__(256) void markov_bwd_dw2_scalar(BwdParams p) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= p.V * p.r) return;
+  const int64_t v = t / p.r, j = t % p.r;
+  KahanSum k;
+  for (int64_t n = 0; n < p.rows; ++n) {
+    const int64_t x = p.ids[n];
+    if (x < 0 || x >= p.V) continue;
+    k.add(g_value<L_BF16, W_BF16>(p, n * p.V + v) * w_value<W_BF16>(p.w1, x * p.r + j));
+  }
+  const float a = k.s;
+  if (W_BF16)
+    ((uint16_t*)p.dw2)[t] = bf16_bits(a);
+  else
+    ((float*)p.dw2)[t] = a;
+}
+
+// de[n][j], one thread each, columns in order.
+template <bool L_BF16, bool W_BF16>
+__global__ __launch_bounds__(256) void markov_bwd_de_scalar(BwdParams p) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= p.rows * p.r) return;
+  const int64_t n = t / p.r, j = t % p.r;
+  KahanSum k;
+  for (int64_t v = 0; v < p.V; ++v) k.add(g_value<L_BF16, W_BF16>(p, n * p.V + v) * w_value<W_BF16>(p.w2, v * p.r + j));
+  const float a = k.s;
+  if (W_BF16)
+    ((uint16_t*)p.de)[t] = bf16_bits(a);
+  else
+    ((float*)p.de)[t] = a;
+}
+
+// ---------------------------------------------------------------- dW1
+// Row links: link[n] = -2 unless n is the first row of its (valid) id;
+// link[rows + n] = the next row with the same valid id (-1: none).  Invalid
+// ids are counted in the device error word.  One wave per row n: the lanes
+// compare the ids 64 at a time; a ballot finds an earlier equal id and a
+// wave minimum the next one.
+__global__ __launch_bounds__(256) void markov_bwd_link(BwdParams p) {
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (n >= p.rows) return;
+  const int64_t x = p.ids[n];
+  const bool ok = x >= 0 && x < p.V;
+  bool earlier = false;
+  int64_t next = INT64_MAX;
+  if (ok) {
+    for (int64_t m0 = 0; m0 < p.rows; m0 += 64) {
+      const int64_t m = m0 + lane;
+      const bool same = m < p.rows && m != n && p.ids[m] == x;
+      earlier = earlier || __ballot(same && m < n) != 0ull;
+      if (same && m > n && m < next) next = m;
+    }
+    // wave minimum of next
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const int64_t o = __shfl_xor(next, off, 64);
+      next = o < next ? o : next;
+    }
+  }
+  if (lane != 0) return;
+  if (!ok) atomicAdd(p.bad_rows, 1u);
+  p.link[n] = (ok && !earlier) ? 0 : -2;
+  p.link[p.rows + n] = (ok && next != INT64_MAX) ? (int32_t)next : -1;
+}
+
+// dW1[x_n][j] for the first row n of each id: its rows' de summed in row
+// order (fp32), rounded to W.  dW1 is zero-filled before.
+template <bool W_BF16>
+__global__ __launch_bounds__(256) void markov_bwd_dw1(BwdParams p) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= p.rows * p.r) return;
+  const int64_t n = t / p.r, j = t % p.r;
+  if (p.link[n] == -2) return;
+  KahanSum k;
+  for (int64_t m = n; m >= 0; m = p.link[p.rows + m]) k.add(w_value<W_BF16>(p.de, m * p.r + j));
+  const float a = k.s;
+  const int64_t x = p.ids[n];
+  if (W_BF16)
+    ((uint16_t*)p.dw1)[x * p.r + j] = bf16_bits(a);
+  else
+    ((float*)p.dw1)[x * p.r + j] = a;
+}
+
+// ---------------------------------------------------------------- launcher
+namespace {
+template <int JB, bool LF32>
+hipError_t launch_bwd_fast(const BwdParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((markov_bwd_dw2_bf16<JB, LF32>), dim3((unsigned)((p.V + 255) / 256)), dim3(512), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned groups = (unsigned)((p.rows + 255) / 256);
+  hipLaunchKernelGGL((markov_bwd_de_bf16<JB, LF32>), dim3((unsigned)p.S * groups), dim3(1024), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((markov_bwd_de_finish<true>), dim3((unsigned)((p.rows * p.r + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+}  // namespace
+
+int64_t backward_slices(int64_t V, int64_t* slice_cols) {
+  *slice_cols = 1024;
+  return (V + 1023) / 1024;
+}
+
+hipError_t launch_backward(const BwdParams& p, bool logits_bf16, bool weights_bf16, hipStream_t s) {
+  if (p.rows <= 0) return hipSuccess;
+  const int64_t blocks = (p.r + 15) / 16;
+  const bool fast = weights_bf16 && p.r % 8 == 0 && p.r <= 256 && p.S == (p.V + p.SL - 1) / p.SL &&
+                    p.partials != nullptr && ((uintptr_t)p.grad & 15u) == 0 && ((uintptr_t)p.w1 & 15u) == 0 &&
+                    ((uintptr_t)p.w2 & 15u) == 0 && ((uintptr_t)p.dw2 & 7u) == 0 && p.V % 8 == 0 &&
+                    p.rows <= ((int64_t)1 << 24);
+  hipError_t e = hipSuccess;
+  if (fast) {
+    const bool f = !logits_bf16;
+    switch (blocks) {
+      case 1: e = f ? launch_bwd_fast<1, true>(p, s) : launch_bwd_fast<1, false>(p, s); break;
+      case 2: e = f ? launch_bwd_fast<2, true>(p, s) : launch_bwd_fast<2, false>(p, s); break;
+      case 3:
+      case 4: e = f ? launch_bwd_fast<4, true>(p, s) : launch_bwd_fast<4, false>(p, s); break;
+      case 5: case 6: case 7:
+      case 8: e = f ? launch_bwd_fast<8, true>(p, s) : launch_bwd_fast<8, false>(p, s); break;
+      default: e = f ? launch_bwd_fast<16, true>(p, s) : launch_bwd_fast<16, false>(p, s); break;
+    }
+  } else {
+    const dim3 g2((unsigned)((p.V * p.r + 255) / 256)), ge((unsigned)((p.rows * p.r + 255) / 256));
+    if (logits_bf16 && weights_bf16) {
+      hipLaunchKernelGGL((markov_bwd_dw2_scalar<true, true>), g2, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((markov_bwd_de_scalar<true, true>), ge, dim3(256), 0, s, p);
+    } else if (logits_bf16) {
+      hipLaunchKernelGGL((markov_bwd_dw2_scalar<true, false>), g2, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((markov_bwd_de_scalar<true, false>), ge, dim3(256), 0, s, p);
+    } else if (weights_bf16) {
+      hipLaunchKernelGGL((markov_bwd_dw2_scalar<false, true>), g2, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((markov_bwd_de_scalar<false, true>), ge, dim3(256), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((markov_bwd_dw2_scalar<false, false>), g2, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((markov_bwd_de_scalar<false, false>), ge, dim3(256), 0, s, p);
+    }
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(markov_bwd_link, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_fill_zero(p.dw1, (size_t)(p.V * p.r) * (weights_bf16 ? 2 : 4), s);
+  if (e != hipSuccess) return e;
+  const dim3 ge((unsigned)((p.rows * p.r + 255) / 256));
+  if (weights_bf16)
+    hipLaunchKernelGGL((markov_bwd_dw1<true>), ge, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((markov_bwd_dw1<false>), ge, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace dspark

@@ -83,6 +83,32 @@ int gate_splits(int64_t rows, int64_t r, int64_t d, int64_t* kchunk);
 // aligned hidden, W1 and gate weight; otherwise a scalar form runs.
 hipError_t launch_gate(const GateParams& g, bool weights_bf16, bool hidden_f32, hipStream_t s);
 
+// Backward of the teacher-forced apply (training).
+struct BwdParams {
+  const void* grad;        // [rows, V] gradient of the corrected logits (L)
+  const int64_t* ids;      // [rows] predecessors
+  const void* w1;          // [V, r] (W)
+  const void* w2;          // [V, r] (W)
+  void* dw1;               // [V, r] output (W): zero where no valid id refers
+  void* dw2;               // [V, r] output (W)
+  float* partials;         // [S][rows][r] fp32 split sums of de (workspace)
+  void* de;                // [rows, r] (W) input gradient of the Linear (workspace)
+  int32_t* link;           // [2 rows] row links of equal ids (workspace)
+  uint32_t* bad_rows;      // device error word
+  int64_t rows;
+  int64_t V;
+  int64_t r;
+  int64_t S;               // vocabulary slices of the de product
+  int64_t SL;              // columns per slice
+};
+
+// Vocabulary slices of the de product (columns per slice in *slice_cols).
+int64_t backward_slices(int64_t V, int64_t* slice_cols);
+// dW2w, then de, then dW1 (zero-filled, then the rows of each id).  The
+// matrix-core form needs bf16 weights, r % 8 == 0, r <= 256, V % 8 == 0 and
+// 16-byte aligned G, W1 and W2w; scalar forms run otherwise.  rows > 0.
+hipError_t launch_backward(const BwdParams& p, bool logits_bf16, bool weights_bf16, hipStream_t s);
+
 hipError_t launch_tile(const KernelParams& p, hipStream_t s);
 // Streaming teacher-forced apply (bf16); needs rows * V < 2^31 and a sink of
 // apply_sink_bytes() bytes.

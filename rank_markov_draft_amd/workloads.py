@@ -40,7 +40,7 @@ class Workload:
     base_sigma: float
     w_sigma: float
     seed: int
-    mode: str              # "apply", "greedy", "temperature", "apply+greedy"
+    mode: str              # "apply", "greedy", "temperature", "apply+greedy", "backward"
     temperature: float = 0.0
     gumbel_seed: int = 0
     ids: str = "uniform"   # "uniform" or "zipf1.1"
@@ -91,6 +91,11 @@ WORKLOADS = {
     "gated_greedy_draft_64x5": Workload("gated_greedy_draft_64x5", B=64, M=5, V=129280, r=256,
                                         dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=7,
                                         mode="greedy", boost=6.0, hidden=5120),
+    # Backward of the 320-row teacher-forced batch (training): a gradient of
+    # the corrected logits per element.
+    "teacher_forced_320_backward": Workload("teacher_forced_320_backward", B=64, M=5, V=129280, r=256,
+                                            dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=8,
+                                            mode="backward"),
     # Large teacher-forced batch: 8 sequences x 64 anchors, rank 512, Zipf ids.
     "teacher_forced_2560_zipf": Workload("teacher_forced_2560_zipf", B=512, M=5, V=129280, r=512,
                                          dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=5,
@@ -149,6 +154,11 @@ def make_inputs(w: Workload, *, B: int | None = None, M: int | None = None,
         token_ids = rng.integers(0, max(V, 1), size=(B, M), dtype=np.int64)
     first_prev = rng.integers(0, max(V, 1), size=(B,), dtype=np.int64)
     out = {"token_ids": token_ids, "first_prev": first_prev}
+    if w.mode == "backward":
+        # gradient of the loss w.r.t. the corrected logits, N(0, 1), in the
+        # logits dtype, drawn after the ids
+        g = rng.standard_normal((B, M, V), dtype=np.float32)
+        out["grad"] = to_bf16_bits(g) if w.ldtype == BF16 else g
     if d:
         bound = np.float32(1.0 / np.sqrt(d + r))
         hid = rng.standard_normal((B, M, d), dtype=np.float32)

@@ -197,3 +197,36 @@ def test_gated_overlaps_rejected(L):
     assert _gapply(L, hidden=ctypes.c_void_p(0x400000), latent=ctypes.c_void_p(0x400000 + 64)) == 1
     # corrected logits over the gate weight
     assert _gapply(L, gw=ctypes.c_void_p(0x600000), out=ctypes.c_void_p(0x600000 + 16)) == 1
+
+
+# ------------------------------------------------------------ backward
+def test_backward_workspace_bytes(L):
+    """Control block, the de rows (4 bytes per element at most), the split
+    sums of the de product over 1024-column slices of V, and two row links."""
+    for B, M, V, r in ((64, 5, 129280, 256), (3, 4, 700, 16), (0, 5, 64, 8)):
+        rows = B * M
+        S = (V + 1023) // 1024
+        want = 256 + _align256(rows * r * 4) + _align256(S * rows * r * 4) + _align256(rows * 8)
+        assert L.dspark_markov_backward_workspace_bytes(B, M, V, r) == want
+
+
+def _bwd(L, B=2, M=3, V=64, r=16, grad=FAKE, ids=FAKE, gw1=ctypes.c_void_p(0x700000),
+         gw2=ctypes.c_void_p(0x800000), ws=FAKE, wsb=1 << 24, wdt=1):
+    return L.dspark_markov_apply_block_backward(grad, 1, ids, ctypes.c_void_p(0x500000), ctypes.c_void_p(0x600000),
+                                                wdt, B, M, V, r, gw1, gw2, ws, wsb, None)
+
+
+def test_backward_argument_errors(L):
+    assert _bwd(L, r=0) == 1
+    assert _bwd(L, B=-1) == 1
+    assert _bwd(L, grad=None) == 1
+    assert _bwd(L, ids=None) == 1
+    assert _bwd(L, gw1=None) == 1
+    assert _bwd(L, gw2=None) == 1
+    assert _bwd(L, ws=None) == 3
+    assert _bwd(L, wsb=256) == 3
+    assert _bwd(L, V=0) == 0                                    # no parameters: nothing to do
+    assert _bwd(L, wdt=7) == 1
+    # gradients over each other or over an input
+    assert _bwd(L, gw1=ctypes.c_void_p(0x700000), gw2=ctypes.c_void_p(0x700000 + 64)) == 1
+    assert _bwd(L, gw1=ctypes.c_void_p(0x500000 + 16)) == 1    # over W1
