@@ -29,6 +29,9 @@ DOMINANT_KERNEL = "markov_chain_greedy_bf16"   # the whole sample call is this o
 KERNEL_SOURCES = [os.path.join(ROOT, "rank_markov_draft_amd", "csrc", name)
                   for name in ("markov_chain.hip", "device_common.h", "markov_chain.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+EXTRA_WORKLOADS = ("teacher_forced_320", "teacher_forced_2560_zipf", "temperature_draft_256x8",
+                   "teacher_forced_320_f32logits", "gated_teacher_forced_320", "gated_greedy_draft_64x5",
+                   "teacher_forced_320_backward")
 
 
 def source_hash(paths) -> str:
@@ -245,6 +248,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' timings")
+    ap.add_argument("--extra", default=",".join(EXTRA_WORKLOADS),
+                    help="comma-separated other workloads to time (default: all)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain copy of known size (for scaling byte counters)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -323,10 +328,11 @@ def main():
     del sets
     torch.cuda.empty_cache()
     if not args.no_extra:
-        result["other_workloads"] = {n: measure_extra(n, rmd, wl, torch, np) for n in
-                                     ("teacher_forced_320", "teacher_forced_2560_zipf", "temperature_draft_256x8",
-                                      "teacher_forced_320_f32logits", "gated_teacher_forced_320",
-                                      "gated_greedy_draft_64x5", "teacher_forced_320_backward")}
+        names = [n for n in args.extra.split(",") if n]
+        unknown = [n for n in names if n not in wl.WORKLOADS]
+        if unknown:
+            raise SystemExit(f"unknown workloads: {unknown}")
+        result["other_workloads"] = {n: measure_extra(n, rmd, wl, torch, np) for n in names}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, np)
     print(json.dumps(result))

@@ -32,25 +32,34 @@ __device__ __forceinline__ float bf16_value(uint16_t h) { return __uint_as_float
 __device__ __forceinline__ float round_to_bf16(float x) { return (float)(__bf16)x; }
 __device__ __forceinline__ uint16_t bf16_bits(float x) { return (uint16_t)(__float_as_uint(round_to_bf16(x)) >> 16); }
 
-// 8 values of g (columns c .. c + 7 of row n) as bf16, from bf16 or fp32 G.
+__device__ __forceinline__ u32x4_t load16_default(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// 8 values of g at element offset off of G through a buffer resource
+// (offset kBufferOob: zeros), as bf16.  Default cache policy: a 128-byte
+// line of g is read by several instructions (16 to 64 bytes of it each),
+// which the streaming policy would refetch from HBM.
 template <bool LF32>
-__device__ __forceinline__ u32x4_t load_g8(const void* grad, int64_t off) {
+__device__ __forceinline__ u32x4_t buffer_g8(__amdgpu_buffer_rsrc_t rs, uint32_t eoff, bool in) {
   if constexpr (LF32) {
-    const u32x4_t lo = *(const u32x4_t*)((const float*)grad + off);
-    const u32x4_t hi = *(const u32x4_t*)((const float*)grad + off + 4);
+    const uint32_t off = in ? eoff * 4u : kBufferOob;
+    const u32x4_t lo = load16_default(rs, off);
+    const u32x4_t hi = load16_default(rs, in ? off + 16u : kBufferOob);
     return u32x4_t{pack_bf16x2(__uint_as_float(lo.x), __uint_as_float(lo.y)),
                    pack_bf16x2(__uint_as_float(lo.z), __uint_as_float(lo.w)),
                    pack_bf16x2(__uint_as_float(hi.x), __uint_as_float(hi.y)),
                    pack_bf16x2(__uint_as_float(hi.z), __uint_as_float(hi.w))};
   } else {
-    return *(const u32x4_t*)((const uint16_t*)grad + off);
+    return load16_default(rs, in ? eoff * 2u : kBufferOob);
   }
 }
 
 // Store two source rows' 8 bf16 values (a: row 2 np, b: row 2 np + 1) as the
 // 32-bit column pair np of 8 consecutive rows of a transposed LDS tile (row
-// stride `stride` bytes).  Lanes of a wave take 16 column pairs and 4
-// pieces, so one 32-bit store per lane meets at most 2-way bank conflicts.
+// stride `stride` bytes).  Lanes of a wave take the 32 column pairs of two
+// pieces: with a 144-byte stride one 32-bit store per lane is free of bank
+// conflicts.
 __device__ __forceinline__ void store_t8x2(unsigned char* base, int stride, int np, u32x4_t a, u32x4_t b) {
   const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
   const uint32_t wb[4] = {b.x, b.y, b.z, b.w};
@@ -65,18 +74,25 @@ __device__ __forceinline__ void store_t8x2(unsigned char* base, int stride, int 
 }  // namespace
 
 // ---------------------------------------------------------------- dW2 (bf16)
-// Workgroup: columns v0 .. v0 + 255 (8 waves x 32).  Chunks of 32 rows: the
-// g tile [32 x 256] and the gathered rows E = W1[x_n] [32 x r] go to LDS as
-// gT [256][32] and eT [r][32] (rows of 64 bytes plus 16 of padding), then
-// wave w multiplies D[j][v] += eT[j][n] gT[v][n] over the chunk's 32 rows
+// Workgroup: columns v0 .. v0 + 255 (8 waves x 32).  Chunks of 64 rows: the
+// g tile [64 x 256] and the gathered rows E = W1[x_n] [64 x r] go to LDS as
+// gT [256][64] and eT [r][64] (rows of 128 bytes plus 16 of padding), then
+// wave w multiplies D[j][v] += eT[j][n] gT[v][n] over the chunk's 64 rows
 // for its v blocks 2w, 2w + 1 and every 16-unit block of r
 // (v_mfma_f32_16x16x32_bf16: rank units on M, columns on N, rows on K).
-constexpr int kBwdStride = 80;    // LDS bytes per transposed row (32 bf16 + pad)
+constexpr int kBwdChunk = 64;                    // columns per LDS chunk of the de product
+constexpr int kBwdStride = kBwdChunk * 2 + 16;   // LDS bytes per transposed row (+ pad)
+constexpr int kDw2Chunk = 64;                    // rows per LDS chunk of the dW2 product
+constexpr int kDw2Stride = kDw2Chunk * 2 + 16;
+
+constexpr int kBwdMaxRows = 4096;   // rows of the matrix-core backward (W1 offsets in LDS)
 
 template <int JB, bool LF32>
 __global__ __launch_bounds__(512) void markov_bwd_dw2_bf16(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds_g[256 * kBwdStride];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_e[JB * 16 * kBwdStride];
+  constexpr int CH = kDw2Chunk;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_g[256 * kDw2Stride];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_e[JB * 16 * kDw2Stride];
+  __shared__ int32_t lds_xr[kBwdMaxRows];   // W1 element offset x r of each row, -1: invalid id
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -92,40 +108,71 @@ __global__ __launch_bounds__(512) void markov_bwd_dw2_bf16(BwdParams p) {
 #pragma unroll
   for (int jb = 0; jb < JB; ++jb) acc[jb][0] = acc[jb][1] = f32x4_t{};
 
-  // thread t: row pair np = t % 16 (rows n0 + 2 np, + 1) and piece t / 16
-  // (8 columns of g: 32 pieces; 8 units of W1: EP pieces)
-  const int np = tid & 15;
-  const int pq = tid >> 4;
-  auto load_chunk = [&](int n0, u32x4_t gv[2], u32x4_t ev[2]) __attribute__((always_inline)) {
-    const int64_t c = v0 + 8 * pq;
+  // unit u = t + 512 i (i = 0, 1): row pair np = u % 32 (rows n0 + 2 np, + 1)
+  // and piece pq = u / 32 (8 columns of g: 32 pieces; 8 units of W1: EP)
+  // The rows' W1 offsets go to LDS once; every load is unconditional
+  // (buffer offsets past the end read zeros), so one wait per chunk suffices.
+  for (int n = tid; n < rows; n += 512) {
+    const int64_t x = p.ids[n];
+    lds_xr[n] = (x >= 0 && x < V) ? (int32_t)(x * r) : -1;
+  }
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t rs_g = buffer_rsrc(p.grad, (uint32_t)(p.rows * V * (LF32 ? 4 : 2)));
+  const __amdgpu_buffer_rsrc_t rs_w1 = buffer_rsrc(p.w1, (uint32_t)(V * r * 2));
+  // unit u = t + 512 i: row pair np = u % 64 (rows n0 + 2 np, + 1) and piece
+  // pq = u / 64 (8 columns of g: 32 pieces; 8 units of W1: EP pieces)
+  constexpr int NP = CH / 2;           // row pairs per chunk
+  constexpr int UPT = NP * 32 / 512;          // units per thread
+  auto load_chunk = [&](int n0, u32x4_t gv[UPT][2], u32x4_t ev[UPT][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int n = n0 + 2 * np + h;
-      gv[h] = (n < rows && c < V) ? load_g8<LF32>(p.grad, (int64_t)n * V + c) : u32x4_t{0u, 0u, 0u, 0u};
-      ev[h] = u32x4_t{0u, 0u, 0u, 0u};
-      if (pq < EP && n < rows && 8 * pq < r) {
-        const int64_t x = p.ids[n];
-        if (x >= 0 && x < V) ev[h] = *(const u32x4_t*)((const uint16_t*)p.w1 + x * r + 8 * pq);
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + 512 * i;
+      const int np = u % NP, pq = u / NP;
+      const int64_t c = v0 + 8 * pq;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int n = n0 + 2 * np + h;
+        gv[i][h] = buffer_g8<LF32>(rs_g, (uint32_t)(n * V + c), n < rows && c < V);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + 512 * i;
+      const int np = u % NP, pq = u / NP;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int n = n0 + 2 * np + h;
+        const int32_t xr = n < rows ? lds_xr[n] : -1;
+        const bool ein = pq < EP && xr >= 0 && 8 * pq < r;
+        ev[i][h] = load16_default(rs_w1, ein ? (uint32_t)(xr + 8 * pq) * 2u : kBufferOob);
       }
     }
   };
-  u32x4_t gv[2], ev[2];
+  u32x4_t gv[UPT][2], ev[UPT][2];
   load_chunk(0, gv, ev);
-  for (int n0 = 0; n0 < rows; n0 += 32) {
+  for (int n0 = 0; n0 < rows; n0 += CH) {
     __syncthreads();   // the previous chunk's products are done with LDS
-    store_t8x2(lds_g + (8 * pq) * kBwdStride, kBwdStride, np, gv[0], gv[1]);
-    if (pq < EP) store_t8x2(lds_e + (8 * pq) * kBwdStride, kBwdStride, np, ev[0], ev[1]);
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + 512 * i;
+      const int np = u % NP, pq = u / NP;
+      store_t8x2(lds_g + (8 * pq) * kDw2Stride, kDw2Stride, np, gv[i][0], gv[i][1]);
+      if (pq < EP) store_t8x2(lds_e + (8 * pq) * kDw2Stride, kDw2Stride, np, ev[i][0], ev[i][1]);
+    }
     __syncthreads();
-    if (n0 + 32 < rows) load_chunk(n0 + 32, gv, ev);   // next chunk in flight
-    bf16x8_t b[2];
+    if (n0 + CH < rows) load_chunk(n0 + CH, gv, ev);   // next chunk in flight
 #pragma unroll
-    for (int vb = 0; vb < 2; ++vb)
-      b[vb] = *(const bf16x8_t*)(lds_g + ((2 * wave + vb) * 16 + n16) * kBwdStride + g4 * 16);
+    for (int t = 0; t < CH / 32; ++t) {
+      bf16x8_t b[2];
 #pragma unroll
-    for (int jb = 0; jb < JB; ++jb) {
-      const bf16x8_t a = *(const bf16x8_t*)(lds_e + (jb * 16 + n16) * kBwdStride + g4 * 16);
-      acc[jb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[0], acc[jb][0], 0, 0, 0);
-      acc[jb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[1], acc[jb][1], 0, 0, 0);
+      for (int vb = 0; vb < 2; ++vb)
+        b[vb] = *(const bf16x8_t*)(lds_g + ((2 * wave + vb) * 16 + n16) * kDw2Stride + t * 64 + g4 * 16);
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+        const bf16x8_t a = *(const bf16x8_t*)(lds_e + (jb * 16 + n16) * kDw2Stride + t * 64 + g4 * 16);
+        acc[jb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[0], acc[jb][0], 0, 0, 0);
+        acc[jb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[1], acc[jb][1], 0, 0, 0);
+      }
     }
   }
   // lane: column v = v0 + 32 wave + 16 vb + n16, units 16 jb + 4 g4 .. + 3
@@ -147,13 +194,16 @@ __global__ __launch_bounds__(512) void markov_bwd_dw2_bf16(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- de (bf16)
-// Workgroup (slice s, row group): rows 256 rg .. + 255 (wave w: 16 rows),
-// columns [s SL, (s + 1) SL).  Chunks of 32 columns: W2w[32 x r] goes to LDS
-// transposed as w2T[r][32]; wave w multiplies D[n][j] += g[n][c] w2T[j][c]
-// (rows on M, rank units on N, columns on K), its g pieces loaded straight
-// from memory one chunk ahead.  Partial sums [S][rows][r] fp32.
+// Workgroup (slice s, row group): rows 256 rg .. + 255, 8 waves of 32 rows
+// (2 row blocks each, so that every W2w operand read from LDS serves two
+// products), columns [s SL, (s + 1) SL).  Chunks of 64 columns: W2w[64 x r]
+// goes to LDS transposed as w2T[r][64]; wave w multiplies
+// D[n][j] += g[n][c] w2T[j][c] (rows on M, rank units on N, columns on K),
+// its g pieces loaded straight from memory one chunk ahead.  Partial sums
+// [S][rows][r] fp32.
 template <int JB, bool LF32>
-__global__ __launch_bounds__(1024) void markov_bwd_de_bf16(BwdParams p) {
+__global__ __launch_bounds__(512) void markov_bwd_de_bf16(BwdParams p) {
+  constexpr int NB = 2;                       // row blocks of 16 per wave
   __shared__ __attribute__((aligned(16))) unsigned char lds_w[JB * 16 * kBwdStride];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -167,60 +217,90 @@ __global__ __launch_bounds__(1024) void markov_bwd_de_bf16(BwdParams p) {
   const int rg = (int)(blockIdx.x / (unsigned)p.S);
   const int64_t c0 = (int64_t)s * p.SL;
   const int64_t c1 = (c0 + p.SL < V) ? c0 + p.SL : V;
-  const int n = rg * 256 + 16 * wave + n16;   // A row of this lane
-  const bool nrow = n < rows;
+  const int nbase = rg * 256 + 32 * wave;     // first row of the wave
   constexpr int WP = JB * 2;                  // 16-byte pieces per W2w row (<= 32)
-  // W2w staging: thread t < 16 WP takes row pair t % 16 of the chunk's 32
-  // rows and piece t / 16
-  const int np = tid & 15;
-  const int pq = tid >> 4;
-  const bool wthread = pq < WP;
+  constexpr int WU = 32 * WP;                 // (row pair, piece) units of a chunk
+  constexpr int WPT = (WU + 511) / 512;
 
-  f32x4_t acc[JB];
+  f32x4_t acc[NB][JB];
 #pragma unroll
-  for (int jb = 0; jb < JB; ++jb) acc[jb] = f32x4_t{};
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) acc[b][jb] = f32x4_t{};
 
-  auto load_a = [&](int64_t c) __attribute__((always_inline)) -> u32x4_t {
-    const int64_t col = c + 8 * g4;
-    return (nrow && col < c1) ? load_g8<LF32>(p.grad, (int64_t)n * V + col) : u32x4_t{0u, 0u, 0u, 0u};
+  // unconditional loads: buffer offsets past the end read zeros
+  const __amdgpu_buffer_rsrc_t rs_g = buffer_rsrc(p.grad, (uint32_t)(p.rows * V * (LF32 ? 4 : 2)));
+  const __amdgpu_buffer_rsrc_t rs_w2 = buffer_rsrc(p.w2, (uint32_t)(V * r * 2));
+  auto load_a = [&](int64_t c, u32x4_t av[NB][kBwdChunk / 32]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int t = 0; t < kBwdChunk / 32; ++t) {
+        const int n = nbase + 16 * b + n16;
+        const int64_t col = c + 32 * t + 8 * g4;
+        av[b][t] = buffer_g8<LF32>(rs_g, (uint32_t)((int64_t)n * V + col), n < rows && col < c1);
+      }
   };
-  auto load_w = [&](int64_t c, u32x4_t wv[2]) __attribute__((always_inline)) {
+  // W2w staging: unit u = t + 512 i: row pair u % 32 of the chunk's 64 rows,
+  // piece u / 32
+  auto load_w = [&](int64_t c, u32x4_t wv[WPT][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t v = c + 2 * np + h;
-      wv[h] = (wthread && v < c1 && 8 * pq < r) ? *(const u32x4_t*)((const uint16_t*)p.w2 + v * r + 8 * pq)
-                                                 : u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < WPT; ++i) {
+      const int u = tid + 512 * i;
+      const int np = u & 31, pq = u >> 5;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t v = c + 2 * np + h;
+        const bool in = u < WU && v < c1 && 8 * pq < r;
+        wv[i][h] = load16_default(rs_w2, in ? (uint32_t)(v * r + 8 * pq) * 2u : kBufferOob);
+      }
     }
   };
-  u32x4_t av = load_a(c0);
-  u32x4_t wv[2];
+  u32x4_t av[NB][kBwdChunk / 32];
+  u32x4_t wv[WPT][2];
+  load_a(c0, av);
   load_w(c0, wv);
-  for (int64_t c = c0; c < c1; c += 32) {
+  for (int64_t c = c0; c < c1; c += kBwdChunk) {
     __syncthreads();
-    if (wthread) store_t8x2(lds_w + (8 * pq) * kBwdStride, kBwdStride, np, wv[0], wv[1]);
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int u = tid + 512 * i;
+      if (u < WU) store_t8x2(lds_w + (8 * (u >> 5)) * kBwdStride, kBwdStride, u & 31, wv[i][0], wv[i][1]);
+    }
     __syncthreads();
-    const u32x4_t a = av;
-    if (c + 32 < c1) {   // next chunk in flight during the products
-      av = load_a(c + 32);
-      load_w(c + 32, wv);
+    u32x4_t a[NB][kBwdChunk / 32];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int t = 0; t < kBwdChunk / 32; ++t) a[b][t] = av[b][t];
+    if (c + kBwdChunk < c1) {   // next chunk in flight during the products
+      load_a(c + kBwdChunk, av);
+      load_w(c + kBwdChunk, wv);
     }
 #pragma unroll
-    for (int jb = 0; jb < JB; ++jb) {
-      const bf16x8_t b = *(const bf16x8_t*)(lds_w + (jb * 16 + n16) * kBwdStride + g4 * 16);
-      acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), b, acc[jb], 0, 0, 0);
-    }
+    for (int t = 0; t < kBwdChunk / 32; ++t)
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+        const bf16x8_t w = *(const bf16x8_t*)(lds_w + (jb * 16 + n16) * kBwdStride + t * 64 + g4 * 16);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[b][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[b][t]), w,
+                                                              acc[b][jb], 0, 0, 0);
+      }
   }
-  // lane: unit j = 16 jb + n16, rows n0 + 4 g4 .. + 3 of the wave's 16
+  // lane: unit j = 16 jb + n16, rows nbase + 16 b + 4 g4 .. + 3
   float* const part = p.partials + (int64_t)s * rows * r;
 #pragma unroll
   for (int jb = 0; jb < JB; ++jb) {
     const int j = 16 * jb + n16;
     if (j >= r) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = rg * 256 + 16 * wave + 4 * g4 + i;
-      if (row < rows) part[(int64_t)row * r + j] = acc[jb][i];
-    }
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = nbase + 16 * b + 4 * g4 + i;
+        if (row < rows) part[(int64_t)row * r + j] = acc[b][jb][i];
+      }
   }
 }
 
@@ -362,7 +442,7 @@ hipError_t launch_bwd_fast(const BwdParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned groups = (unsigned)((p.rows + 255) / 256);
-  hipLaunchKernelGGL((markov_bwd_de_bf16<JB, LF32>), dim3((unsigned)p.S * groups), dim3(1024), 0, s, p);
+  hipLaunchKernelGGL((markov_bwd_de_bf16<JB, LF32>), dim3((unsigned)p.S * groups), dim3(512), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((markov_bwd_de_finish<true>), dim3((unsigned)((p.rows * p.r + 255) / 256)), dim3(256), 0, s, p);
@@ -379,9 +459,10 @@ hipError_t launch_backward(const BwdParams& p, bool logits_bf16, bool weights_bf
   if (p.rows <= 0) return hipSuccess;
   const int64_t blocks = (p.r + 15) / 16;
   const bool fast = weights_bf16 && p.r % 8 == 0 && p.r <= 256 && p.S == (p.V + p.SL - 1) / p.SL &&
+                    p.rows * p.V * (logits_bf16 ? 2 : 4) <= ((int64_t)1 << 31) && p.V * p.r * 2 <= ((int64_t)1 << 31) &&
                     p.partials != nullptr && ((uintptr_t)p.grad & 15u) == 0 && ((uintptr_t)p.w1 & 15u) == 0 &&
                     ((uintptr_t)p.w2 & 15u) == 0 && ((uintptr_t)p.dw2 & 7u) == 0 && p.V % 8 == 0 &&
-                    p.rows <= ((int64_t)1 << 24);
+                    p.rows <= kBwdMaxRows;
   hipError_t e = hipSuccess;
   if (fast) {
     const bool f = !logits_bf16;
