@@ -29,6 +29,14 @@ DOMINANT_KERNEL = "markov_chain_greedy_bf16"   # the whole sample call is this o
 KERNEL_SOURCES = [os.path.join(ROOT, "rank_markov_draft_amd", "csrc", name)
                   for name in ("markov_chain.hip", "device_common.h", "markov_chain.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+VALU_FILE = os.path.join(ROOT, "profiles", "valu.json")
+VALU_KERNEL = "markov_step_bf16<8, 2, 1>"      # temperature steps at rank 256
+VALU_SOURCES = [os.path.join(ROOT, "rank_markov_draft_amd", "csrc", name)
+                for name in ("markov_step.hip", "device_common.h", "markov_kernels.h")]
+# Vector issue: 256 CUs x 4 SIMDs at 2.4 GHz; a wave64 VALU instruction holds
+# its SIMD for 4 cycles (16 lanes per cycle, the non-packed rate behind the
+# 157.3 TFLOP/s fp32 vector peak), a transcendental one for 16 (quarter rate).
+SIMD_CYCLES_PEAK_G = 256 * 4 * 2.4
 EXTRA_WORKLOADS = ("teacher_forced_320", "teacher_forced_2560_zipf", "temperature_draft_256x8",
                    "teacher_forced_320_f32logits", "gated_teacher_forced_320", "gated_greedy_draft_64x5",
                    "teacher_forced_320_backward")
@@ -106,6 +114,44 @@ def write_traffic(fetch_csv: str, write_csv: str) -> dict:
         json.dump(t, f, indent=1)
         f.write("\n")
     return t
+
+
+def write_valu(csv_path: str) -> dict:
+    """profiles/valu.json from one SQ_INSTS_VALU / SQ_INSTS_VALU_TRANS_F32 /
+    SQ_INSTS_VALU_MFMA_BF16 counter run: the step kernel's vector issue
+    cycles per dispatch."""
+    import collections
+    import csv
+    import json as _json
+    acc = collections.defaultdict(list)
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if VALU_KERNEL in row["Kernel_Name"]:
+                acc[row["Counter_Name"]].append(float(row["Counter_Value"]))
+    avg = {k: sum(v) / len(v) for k, v in acc.items()}
+    valu, trans, mfma = avg["SQ_INSTS_VALU"], avg["SQ_INSTS_VALU_TRANS_F32"], avg["SQ_INSTS_VALU_MFMA_BF16"]
+    t = {"kernel": VALU_KERNEL, "workload": "temperature_draft_256x8",
+         "kernel_source_sha256_16": source_hash(VALU_SOURCES),
+         "dispatches": len(acc["SQ_INSTS_VALU"]),
+         "valu_wave_insts": valu, "trans_wave_insts": trans, "mfma_wave_insts": mfma,
+         "simd_issue_cycles": (valu - mfma - trans) * 4 + trans * 16}
+    with open(VALU_FILE, "w") as f:
+        _json.dump(t, f, indent=1)
+        f.write("\n")
+    return t
+
+
+def measured_valu():
+    """Vector issue cycles per step-kernel dispatch (profiles/valu.json), or
+    None once the step kernel's source changed."""
+    import json as _json
+    if not os.path.exists(VALU_FILE):
+        return None
+    with open(VALU_FILE) as f:
+        t = _json.load(f)
+    if t.get("kernel_source_sha256_16") != source_hash(VALU_SOURCES):
+        return None
+    return t.get("simd_issue_cycles")
 
 
 def algorithmic_bytes_sample(w, return_logits=True) -> int:
@@ -236,6 +282,14 @@ def measure_extra(name, rmd, wl, torch, np, steps=10, warmup=3):
            "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": alg}
     if w.mode not in ("apply", "backward"):
         res["tokens_per_s"] = w.B * w.M / (ms * 1e-3)
+    cycles = measured_valu() if name == "temperature_draft_256x8" else None
+    if cycles:
+        # vector-issue roofline of the whole call (M step kernels; the
+        # reductions and launch gaps count against it)
+        achieved = cycles * w.M / (ms * 1e-3) / 1e9
+        res["roofline"] = {"bound": "alu", "kernel": "markov_step_bf16 (one per step)", "achieved": achieved,
+                           "peak": SIMD_CYCLES_PEAK_G, "unit": "G SIMD issue cycles/s",
+                           "frac": achieved / SIMD_CYCLES_PEAK_G}
     del sets
     torch.cuda.empty_cache()
     return res
@@ -254,9 +308,14 @@ def main():
                     help="also run a plain copy of known size (for scaling byte counters)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two counter runs and exit (no GPU)")
+    ap.add_argument("--write-valu", metavar="VALU_CSV",
+                    help="write profiles/valu.json from a vector-instruction counter run and exit (no GPU)")
     args = ap.parse_args()
     if args.write_traffic:
         print(json.dumps(write_traffic(*args.write_traffic)))
+        return
+    if args.write_valu:
+        print(json.dumps(write_valu(args.write_valu)))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
