@@ -85,14 +85,14 @@ constexpr int kBwdStride = kBwdChunk * 2 + 16;   // LDS bytes per transposed row
 constexpr int kDw2Chunk = 64;                    // rows per LDS chunk of the dW2 product
 constexpr int kDw2Stride = kDw2Chunk * 2 + 16;
 
-constexpr int kBwdMaxRows = 4096;   // rows of the matrix-core backward (W1 offsets in LDS)
+constexpr int kBwdRowBlock = 4096;  // rows whose W1 offsets sit in LDS at a time
 
 template <int JB, bool LF32>
 __global__ __launch_bounds__(512) void markov_bwd_dw2_bf16(BwdParams p) {
   constexpr int CH = kDw2Chunk;
   __shared__ __attribute__((aligned(16))) unsigned char lds_g[256 * kDw2Stride];
   __shared__ __attribute__((aligned(16))) unsigned char lds_e[JB * 16 * kDw2Stride];
-  __shared__ int32_t lds_xr[kBwdMaxRows];   // W1 element offset x r of each row, -1: invalid id
+  __shared__ int32_t lds_xr[kBwdRowBlock];  // W1 element offset x r of each row, -1: invalid id
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -108,21 +108,16 @@ __global__ __launch_bounds__(512) void markov_bwd_dw2_bf16(BwdParams p) {
 #pragma unroll
   for (int jb = 0; jb < JB; ++jb) acc[jb][0] = acc[jb][1] = f32x4_t{};
 
-  // unit u = t + 512 i (i = 0, 1): row pair np = u % 32 (rows n0 + 2 np, + 1)
-  // and piece pq = u / 32 (8 columns of g: 32 pieces; 8 units of W1: EP)
-  // The rows' W1 offsets go to LDS once; every load is unconditional
-  // (buffer offsets past the end read zeros), so one wait per chunk suffices.
-  for (int n = tid; n < rows; n += 512) {
-    const int64_t x = p.ids[n];
-    lds_xr[n] = (x >= 0 && x < V) ? (int32_t)(x * r) : -1;
-  }
-  __syncthreads();
+  // The W1 offsets of a block of rows go to LDS once; every load is
+  // unconditional (buffer offsets past the end read zeros), so one wait per
+  // chunk suffices.
   const __amdgpu_buffer_rsrc_t rs_g = buffer_rsrc(p.grad, (uint32_t)(p.rows * V * (LF32 ? 4 : 2)));
   const __amdgpu_buffer_rsrc_t rs_w1 = buffer_rsrc(p.w1, (uint32_t)(V * r * 2));
   // unit u = t + 512 i: row pair np = u % 64 (rows n0 + 2 np, + 1) and piece
   // pq = u / 64 (8 columns of g: 32 pieces; 8 units of W1: EP pieces)
   constexpr int NP = CH / 2;           // row pairs per chunk
   constexpr int UPT = NP * 32 / 512;          // units per thread
+  int rb0 = 0;   // first row of the block in LDS
   auto load_chunk = [&](int n0, u32x4_t gv[UPT][2], u32x4_t ev[UPT][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
@@ -142,36 +137,45 @@ __global__ __launch_bounds__(512) void markov_bwd_dw2_bf16(BwdParams p) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int n = n0 + 2 * np + h;
-        const int32_t xr = n < rows ? lds_xr[n] : -1;
+        const int32_t xr = n < rows ? lds_xr[n - rb0] : -1;
         const bool ein = pq < EP && xr >= 0 && 8 * pq < r;
         ev[i][h] = load16_default(rs_w1, ein ? (uint32_t)(xr + 8 * pq) * 2u : kBufferOob);
       }
     }
   };
   u32x4_t gv[UPT][2], ev[UPT][2];
-  load_chunk(0, gv, ev);
-  for (int n0 = 0; n0 < rows; n0 += CH) {
-    __syncthreads();   // the previous chunk's products are done with LDS
-#pragma unroll
-    for (int i = 0; i < UPT; ++i) {
-      const int u = tid + 512 * i;
-      const int np = u % NP, pq = u / NP;
-      store_t8x2(lds_g + (8 * pq) * kDw2Stride, kDw2Stride, np, gv[i][0], gv[i][1]);
-      if (pq < EP) store_t8x2(lds_e + (8 * pq) * kDw2Stride, kDw2Stride, np, ev[i][0], ev[i][1]);
+  for (; rb0 < rows; rb0 += kBwdRowBlock) {
+    const int rb1 = (rb0 + kBwdRowBlock < rows) ? rb0 + kBwdRowBlock : rows;
+    __syncthreads();   // the previous block's last chunk is done with the table
+    for (int n = rb0 + tid; n < rb1; n += 512) {
+      const int64_t x = p.ids[n];
+      lds_xr[n - rb0] = (x >= 0 && x < V) ? (int32_t)(x * r) : -1;
     }
     __syncthreads();
-    if (n0 + CH < rows) load_chunk(n0 + CH, gv, ev);   // next chunk in flight
+    load_chunk(rb0, gv, ev);
+    for (int n0 = rb0; n0 < rb1; n0 += CH) {
+      __syncthreads();   // the previous chunk's products are done with LDS
 #pragma unroll
-    for (int t = 0; t < CH / 32; ++t) {
-      bf16x8_t b[2];
+      for (int i = 0; i < UPT; ++i) {
+        const int u = tid + 512 * i;
+        const int np = u % NP, pq = u / NP;
+        store_t8x2(lds_g + (8 * pq) * kDw2Stride, kDw2Stride, np, gv[i][0], gv[i][1]);
+        if (pq < EP) store_t8x2(lds_e + (8 * pq) * kDw2Stride, kDw2Stride, np, ev[i][0], ev[i][1]);
+      }
+      __syncthreads();
+      if (n0 + CH < rb1) load_chunk(n0 + CH, gv, ev);   // next chunk in flight
 #pragma unroll
-      for (int vb = 0; vb < 2; ++vb)
-        b[vb] = *(const bf16x8_t*)(lds_g + ((2 * wave + vb) * 16 + n16) * kDw2Stride + t * 64 + g4 * 16);
+      for (int t = 0; t < CH / 32; ++t) {
+        bf16x8_t b[2];
 #pragma unroll
-      for (int jb = 0; jb < JB; ++jb) {
-        const bf16x8_t a = *(const bf16x8_t*)(lds_e + (jb * 16 + n16) * kDw2Stride + t * 64 + g4 * 16);
-        acc[jb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[0], acc[jb][0], 0, 0, 0);
-        acc[jb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[1], acc[jb][1], 0, 0, 0);
+        for (int vb = 0; vb < 2; ++vb)
+          b[vb] = *(const bf16x8_t*)(lds_g + ((2 * wave + vb) * 16 + n16) * kDw2Stride + t * 64 + g4 * 16);
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+          const bf16x8_t a = *(const bf16x8_t*)(lds_e + (jb * 16 + n16) * kDw2Stride + t * 64 + g4 * 16);
+          acc[jb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[0], acc[jb][0], 0, 0, 0);
+          acc[jb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[1], acc[jb][1], 0, 0, 0);
+        }
       }
     }
   }
@@ -462,7 +466,7 @@ hipError_t launch_backward(const BwdParams& p, bool logits_bf16, bool weights_bf
                     p.rows * p.V * (logits_bf16 ? 2 : 4) <= ((int64_t)1 << 31) && p.V * p.r * 2 <= ((int64_t)1 << 31) &&
                     p.partials != nullptr && ((uintptr_t)p.grad & 15u) == 0 && ((uintptr_t)p.w1 & 15u) == 0 &&
                     ((uintptr_t)p.w2 & 15u) == 0 && ((uintptr_t)p.dw2 & 7u) == 0 && p.V % 8 == 0 &&
-                    p.rows <= kBwdMaxRows;
+                    p.rows <= ((int64_t)1 << 24);
   hipError_t e = hipSuccess;
   if (fast) {
     const bool f = !logits_bf16;

@@ -121,6 +121,16 @@ def test_backward_shapes(native, B, M, V, r, dtype, ldt, ids):
     check_backward(inp, gdw1, gdw2, name=f"backward B{B} M{M} V{V} r{r} W{dtype} L{ldt} {ids}")
 
 
+def test_backward_rows_beyond_one_block(native):
+    """4400 rows: the dW2 kernel walks two blocks of row offsets; sampled
+    elements of both gradients."""
+    inp = _inputs(seed=4, B=1100, M=4, V=1024, r=64)
+    rng = np.random.default_rng(1)
+    inp["token_ids"] = rng.integers(0, 300, size=(1100, 4)).astype(np.int64)
+    gdw1, gdw2 = run_backward(inp)
+    check_backward(inp, gdw1, gdw2, n_dw2=3000, n_dw1=400, name="backward 4400 rows")
+
+
 def test_backward_bad_ids_and_empty(native):
     """Ids outside [0, V) contribute nothing and are counted; no rows gives
     zero gradients."""
