@@ -105,8 +105,9 @@ struct BwdParams {
 // Vocabulary slices of the de product (columns per slice in *slice_cols).
 int64_t backward_slices(int64_t V, int64_t* slice_cols);
 // dW2w, then de, then dW1 (zero-filled, then the rows of each id).  The
-// matrix-core form needs bf16 weights, r % 8 == 0, r <= 256, V % 8 == 0 and
-// 16-byte aligned G, W1 and W2w; scalar forms run otherwise.  rows > 0.
+// matrix-core form needs bf16 weights, r % 8 == 0, r <= 256, V % 8 == 0,
+// G and V * r * 2 within 2^31 bytes and 16-byte aligned G, W1 and W2w;
+// scalar forms (compensated sums) run otherwise.  rows > 0.
 hipError_t launch_backward(const BwdParams& p, bool logits_bf16, bool weights_bf16, hipStream_t s);
 
 hipError_t launch_tile(const KernelParams& p, hipStream_t s);
