@@ -204,3 +204,20 @@ def test_gated_sample_fallback_is_vanilla(native):
         assert np.array_equal(tok, from_dev(tv)) and np.array_equal(corr, from_dev(cv))
         prev = np.concatenate([inp["first_prev"][:, None], tok[:, :-1]], axis=1)
         assert np.array_equal(lat, inp["w1"][prev])
+
+
+def test_gated_empty_inputs(native):
+    """No rows: the gated apply returns the base logits (and an empty latent),
+    the gated sampling returns empty tokens; nothing is launched."""
+    inp = _inputs(seed=2, B=3, M=4, V=1024, r=32, hidden=64)
+    d = device_inputs({k: inp[k] for k in KEYS if k in inp})
+    base0, ids0, hid0 = d["base"][:, :0], d["token_ids"][:, :0], d["hidden"][:, :0]
+    out, lat = rmd.apply_block_logits_gated(base0, ids0, d["w1"], d["w2"], d["gate_w"], d["gate_b"], hid0,
+                                            return_latent=True)
+    assert out.shape == (3, 0, 1024) and lat.shape == (3, 0, 32)
+    tok, corr = rmd.sample_block_tokens_gated(base0, d["first_prev"], d["w1"], d["w2"], d["gate_w"], d["gate_b"],
+                                              hid0, 0.0)
+    assert tok.shape == (3, 0)
+    with pytest.raises(ValueError):   # hidden states of the wrong shape
+        rmd.apply_block_logits_gated(d["base"], d["token_ids"], d["w1"], d["w2"], d["gate_w"], d["gate_b"],
+                                     d["hidden"][:, :2])
