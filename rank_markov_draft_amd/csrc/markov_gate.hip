@@ -242,12 +242,14 @@ __global__ __launch_bounds__(256) void markov_gate_scalar(GateParams g) {
 }
 
 // ---------------------------------------------------------------- launcher
-// Splits of the inner dimension: enough workgroups to cover the CUs (about
-// 256), at most 32 splits and at least 32 columns per split.
+// Splits of the inner dimension: as many as keep the grid within two
+// workgroups per CU (512), so that a small call's workgroups each load one
+// or two LDS chunks in a single round; at most 32 splits and at least 32
+// columns per split.
 int gate_splits(int64_t rows, int64_t r, int64_t d, int64_t* kchunk) {
   const int64_t K = d + r;
   const int64_t tiles = ((rows + kGateTile - 1) / kGateTile) * ((r + kGateTile - 1) / kGateTile);
-  int64_t want = (256 + tiles - 1) / tiles;
+  int64_t want = 512 / tiles;
   if (want > 32) want = 32;
   const int64_t steps = (K + 31) / 32;
   if (want > steps) want = steps;

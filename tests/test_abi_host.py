@@ -131,12 +131,12 @@ def test_sample_argument_errors(L):
 
 # ------------------------------------------------------------ gated head
 def _gate_splits(rows, r, d):
-    """Splits of the gate GEMM's inner dimension: about 256 workgroups of
+    """Splits of the gate GEMM's inner dimension: at most 512 workgroups of
     64 x 64 output tiles, at most 32 splits, whole 32-column steps."""
     K = d + r
     tiles = ((rows + 63) // 64) * ((r + 63) // 64)
     steps = (K + 31) // 32
-    want = max(min((256 + tiles - 1) // tiles, 32, steps), 1)
+    want = max(min(512 // tiles, 32, steps), 1)
     kchunk = (steps + want - 1) // want * 32
     return (K + kchunk - 1) // kchunk
 
@@ -152,7 +152,7 @@ def test_gated_workspace_bytes(L):
         want = (_align256(L.dspark_markov_workspace_bytes(B, M, V, r, sample)) + _align256(rows * r * 4)
                 + (_align256(S * rows * r * 4) if S > 1 else 0))
         assert L.dspark_markov_gated_workspace_bytes(B, M, V, r, d, sample) == want
-    assert _gate_splits(320, 256, 5120) == 13 and _gate_splits(64, 256, 5120) == 28
+    assert _gate_splits(320, 256, 5120) == 24 and _gate_splits(64, 256, 5120) == 28
     assert _gate_splits(2560, 512, 5120) == 1
 
 
