@@ -83,6 +83,20 @@ def calibrate_copy(torch):
           file=sys.stderr)
 
 
+def copy_ceiling(torch, np):
+    """The practical HBM ceiling: a plain device-to-device copy of 512 MiB
+    (read and written), 3 warm-up and 10 timed copies with events."""
+    src = torch.empty(256 * 1024 * 1024, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    nbytes = 2 * src.numel() * 2
+    _, per = time_calls(lambda i: dst.copy_(src), 1, 10, 3, torch)
+    ms = float(np.median(per))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"GBps": gbs, "bytes_per_copy": nbytes, "ms_per_copy": ms, "frac_of_peak": gbs / HBM_PEAK_GBS}
+
+
 def write_traffic(fetch_csv: str, write_csv: str) -> dict:
     """Turn two rocprofv3 counter runs of `bench.py --calibrate-copy` (one with
     FETCH_SIZE, one with WRITE_SIZE, KiB per dispatch) into HBM bytes per
@@ -386,6 +400,9 @@ def main():
     }
     del sets
     torch.cuda.empty_cache()
+    ceiling = copy_ceiling(torch, np)
+    result["copy_ceiling"] = ceiling
+    result["roofline"]["frac_of_copy_ceiling"] = achieved / ceiling["GBps"]
     if not args.no_extra:
         names = [n for n in args.extra.split(",") if n]
         unknown = [n for n in names if n not in wl.WORKLOADS]
