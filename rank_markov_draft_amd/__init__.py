@@ -117,6 +117,7 @@ def apply_block_logits(base_logits: torch.Tensor, token_ids: torch.Tensor, w1: t
         raise ValueError(f"token_ids {tuple(token_ids.shape)} must be base_logits.shape[:-1]")
     if w1.shape[0] != V:
         raise ValueError(f"weights have vocabulary {w1.shape[0]}, logits {V}")
+    _check_device(base_logits.device, workspace, token_ids=token_ids, w1=w1, w2=w2, out=out)
     if base_logits.numel() == 0:
         return base_logits if out is None else out
     base_c = base_logits.contiguous()
@@ -157,6 +158,15 @@ def sample_block_tokens(base_logits: torch.Tensor, first_prev_token_ids: torch.T
         raise ValueError(f"weights have vocabulary {w1.shape[0]}, logits {V}")
     T = 0.0 if temperature is None else float(temperature)
     dev = base_logits.device
+    _check_device(dev, workspace, first_prev_token_ids=first_prev_token_ids, w1=w1, w2=w2,
+                  tokens_out=tokens_out, logits_out=logits_out if return_logits else None)
+    if tokens_out is not None and (tuple(tokens_out.shape) != (B, M) or tokens_out.dtype != torch.int64
+                                   or not tokens_out.is_contiguous()):
+        raise ValueError(f"tokens_out must be a contiguous int64 tensor of shape {(B, M)}")
+    if return_logits and logits_out is not None and (
+            logits_out.shape != base_logits.shape or logits_out.dtype != base_logits.dtype
+            or not logits_out.is_contiguous()):
+        raise ValueError("logits_out must be a contiguous tensor shaped and typed like base_logits")
     if tokens_out is None:
         tokens_out = torch.empty((B, M), dtype=torch.int64, device=dev)
     if M == 0:
@@ -176,6 +186,18 @@ def sample_block_tokens(base_logits: torch.Tensor, first_prev_token_ids: torch.T
         _ptr(tokens_out), _ptr(corrected), workspace.ptr, workspace.nbytes, _stream_handle(dev))
     _lib.check(st, "sample_block_tokens")
     return tokens_out, corrected
+
+
+def _check_device(dev: torch.device, workspace: "Workspace | None" = None, **tensors):
+    """Every tensor the kernels read or write must live on the GPU that holds
+    the logits: a host or foreign-device pointer would reach the kernels."""
+    if dev.type != "cuda":
+        raise ValueError(f"the head runs on a GPU; the logits are on {dev}")
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the logits on {dev}")
+    if workspace is not None and workspace.buffer.device != dev:
+        raise ValueError(f"the workspace is on {workspace.buffer.device}, the logits on {dev}")
 
 
 def _check_gate(hidden_states, gate_weight, gate_bias, lead, d_expected_rows, r, wdtype):
@@ -218,6 +240,9 @@ def apply_block_logits_gated(base_logits: torch.Tensor, token_ids: torch.Tensor,
     r = w1.shape[1]
     d = _check_gate(hidden_states, gate_weight, gate_bias, base_logits.shape[:-1], None, r, w1.dtype)
     dev = base_logits.device
+    gated = hidden_states is not None
+    _check_device(dev, workspace, token_ids=token_ids, w1=w1, w2=w2, hidden_states=hidden_states, out=out,
+                  gate_weight=gate_weight if gated else None, gate_bias=gate_bias if gated else None)
     latent = torch.empty(tuple(base_logits.shape[:-1]) + (r,), dtype=w1.dtype, device=dev) if return_latent else None
     if base_logits.numel() == 0:
         res = base_logits if out is None else out
@@ -264,6 +289,10 @@ def sample_block_tokens_gated(base_logits: torch.Tensor, first_prev_token_ids: t
     d = _check_gate(hidden_states, gate_weight, gate_bias, (B, M), None, r, w1.dtype)
     T = 0.0 if temperature is None else float(temperature)
     dev = base_logits.device
+    gated = hidden_states is not None
+    _check_device(dev, workspace, first_prev_token_ids=first_prev_token_ids, w1=w1, w2=w2,
+                  hidden_states=hidden_states, gate_weight=gate_weight if gated else None,
+                  gate_bias=gate_bias if gated else None)
     tokens = torch.empty((B, M), dtype=torch.int64, device=dev)
     latent = torch.empty((B, M, r), dtype=w1.dtype, device=dev) if return_latent else None
     if M == 0 or B == 0:
@@ -305,6 +334,7 @@ def apply_block_logits_backward(grad_corrected: torch.Tensor, token_ids: torch.T
         raise ValueError(f"weights have vocabulary {w1.shape[0]}, logits {V}")
     r = w1.shape[1]
     dev = grad_corrected.device
+    _check_device(dev, workspace, token_ids=token_ids, w1=w1, w2=w2)
     g = grad_corrected.contiguous()
     ids = token_ids.to(torch.int64).contiguous()
     w1c, w2c = w1.contiguous(), w2.contiguous()
