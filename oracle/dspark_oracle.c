@@ -749,6 +749,8 @@ int dspark_oracle_backward_bounds(const void* grad, int logits_dtype,
   if (rows < 0 || V <= 0 || r <= 0 || n < 0 || (kind != 1 && kind != 2)) return ORACLE_INVALID;
   if (n == 0) return ORACLE_OK;
   if (!grad || !token_ids || !w1 || !w2 || !which || !cols || !lo || !mid || !hi) return ORACLE_INVALID;
+  for (int64_t m = 0; m < rows; ++m)
+    if (token_ids[m] < 0 || token_ids[m] >= V) return ORACLE_INVALID;   /* Embedding lookup would raise */
   const int ldt = logits_dtype, wdt = weight_dtype;
   const double u = ldexp(1.0, -24);
   for (int64_t i = 0; i < n; ++i) {
