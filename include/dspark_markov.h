@@ -61,9 +61,18 @@
 extern "C" {
 #endif
 
-typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype_t;
+/* In C++ the enums below have int as their underlying type, so every int a
+ * C caller passes is a valid value for the library to inspect (and reject
+ * when it names no dtype or status); C sees plain enums of int size. */
+#ifdef __cplusplus
+#define DSPARK_ENUM_BASE : int
+#else
+#define DSPARK_ENUM_BASE
+#endif
 
-typedef enum {
+typedef enum DSPARK_ENUM_BASE { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype_t;
+
+typedef enum DSPARK_ENUM_BASE {
   DSPARK_OK = 0,
   DSPARK_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, r <= 0, NaN temperature, overlap */
   DSPARK_ERR_UNSUPPORTED = 2,        /* dtype pair or shape the library has no kernel for */
@@ -72,7 +81,9 @@ typedef enum {
 } dspark_status_t;
 
 /* Bytes of workspace an apply (sample_mode = 0) or sample (sample_mode = 1)
- * call of these sizes needs.  Pure host function. */
+ * call of these sizes needs.  Pure host function.  This and the gated and
+ * backward size queries return SIZE_MAX when the sizes cannot be
+ * represented (no buffer can then satisfy the call). */
 size_t dspark_markov_workspace_bytes(int64_t B, int64_t M, int64_t V, int64_t r, int sample_mode);
 
 /* Zero-fill `bytes` bytes of workspace on `stream` with a device kernel. */

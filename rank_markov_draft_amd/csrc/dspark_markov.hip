@@ -34,15 +34,26 @@ struct Control {
 };
 static_assert(sizeof(Control) <= kControlBytes, "control block");
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+// Size arithmetic of the workspace queries saturates at SIZE_MAX, the
+// answer for sizes that cannot be represented.
+size_t add_sz(size_t a, size_t b) {
+  size_t o;
+  return __builtin_add_overflow(a, b, &o) ? SIZE_MAX : o;
+}
+size_t mul_sz(size_t a, size_t b) {
+  size_t o;
+  return __builtin_mul_overflow(a, b, &o) ? SIZE_MAX : o;
+}
+size_t align256(size_t x) { return x > SIZE_MAX - 255 ? SIZE_MAX : (x + 255) & ~(size_t)255; }
 
 size_t partials_bytes(int64_t B, int64_t V) {
-  return align256((size_t)B * (size_t)((V + 127) / 128) * sizeof(uint64_t));
+  return align256(mul_sz(mul_sz((size_t)B, (size_t)((V + 127) / 128)), sizeof(uint64_t)));
 }
 
 size_t chain_keys_bytes(int64_t M) {
-  return dspark::kChainSyncBytes + (size_t)M * (size_t)dspark::chain_key_groups() *
-                                       (size_t)dspark::chain_max_rows() * dspark::kKeyPad * sizeof(uint64_t);
+  return add_sz(dspark::kChainSyncBytes,
+                mul_sz((size_t)M, (size_t)dspark::chain_key_groups() * (size_t)dspark::chain_max_rows() *
+                                      dspark::kKeyPad * sizeof(uint64_t)));
 }
 
 // Compute units of the current device, cached per device.
@@ -112,9 +123,12 @@ dspark_status_t check_common(int ldt, int wdt, int64_t B, int64_t M, int64_t V, 
 // ([rows, r], at most 4 bytes per element), then the gate GEMM's split sums
 // ([S][rows][r] fp32) when it splits its inner dimension.
 size_t gated_region_bytes(int64_t rows, int64_t r, int64_t d) {
+  int64_t rr = 0, t = 0;
+  if (!mul_ok(rows, r, &rr) || !mul_ok(rows, d, &t) || d > (int64_t)0x7FFFFFFF) return SIZE_MAX;
   int64_t kchunk = 0;
   const int S = d > 0 ? dspark::gate_splits(rows, r, d, &kchunk) : 1;
-  return align256((size_t)(rows * r) * 4) + (S > 1 ? align256((size_t)S * (size_t)(rows * r) * 4) : 0);
+  const size_t lat = align256(mul_sz((size_t)rr, 4));
+  return S > 1 ? add_sz(lat, align256(mul_sz(mul_sz((size_t)S, (size_t)rr), 4))) : lat;
 }
 
 dspark_status_t check_gate_args(bool gated, int hdt, int64_t d, const void* gw, const void* gb, int64_t rows,
@@ -165,12 +179,8 @@ extern "C" {
 size_t dspark_markov_workspace_bytes(int64_t B, int64_t M, int64_t V, int64_t r, int sample_mode) {
   (void)r;
   if (B < 0 || V < 0 || M < 0) return kControlBytes;
-  size_t bytes = kControlBytes;
-  if (sample_mode)
-    bytes += partials_bytes(B, V) + chain_keys_bytes(M);
-  else
-    bytes += dspark::apply_sink_bytes();
-  return bytes;
+  if (sample_mode) return add_sz(add_sz(kControlBytes, partials_bytes(B, V)), chain_keys_bytes(M));
+  return kControlBytes + dspark::apply_sink_bytes();
 }
 
 dspark_status_t dspark_markov_workspace_init(void* workspace, size_t bytes, void* stream) {
@@ -354,7 +364,9 @@ size_t dspark_markov_gated_workspace_bytes(int64_t B, int64_t M, int64_t V, int6
                                            int sample_mode) {
   const size_t base = align256(dspark_markov_workspace_bytes(B, M, V, r, sample_mode));
   if (B < 0 || M < 0 || V < 0 || r <= 0 || d < 0) return base;
-  return base + gated_region_bytes(sample_mode ? B : B * M, r, d);
+  int64_t rows = B;
+  if (!sample_mode && !mul_ok(B, M, &rows)) return SIZE_MAX;
+  return add_sz(base, gated_region_bytes(rows, r, d));
 }
 
 dspark_status_t dspark_markov_apply_block_gated(
@@ -550,11 +562,13 @@ dspark_status_t dspark_markov_sample_block_gated(
 
 size_t dspark_markov_backward_workspace_bytes(int64_t B, int64_t M, int64_t V, int64_t r) {
   if (B < 0 || M < 0 || V < 0 || r <= 0) return kControlBytes;
-  const int64_t rows = B * M;
+  int64_t rows = 0, rr = 0;
+  if (!mul_ok(B, M, &rows) || !mul_ok(rows, r, &rr)) return SIZE_MAX;
   int64_t sl = 0;
   const int64_t S = V > 0 ? dspark::backward_slices(V, &sl) : 0;
-  return kControlBytes + align256((size_t)(rows * r) * 4) + align256((size_t)S * (size_t)(rows * r) * 4) +
-         align256((size_t)rows * 8);
+  const size_t de = align256(mul_sz((size_t)rr, 4));
+  const size_t parts = align256(mul_sz(mul_sz((size_t)S, (size_t)rr), 4));
+  return add_sz(add_sz(add_sz(kControlBytes, de), parts), align256(mul_sz((size_t)rows, 8)));
 }
 
 dspark_status_t dspark_markov_apply_block_backward(const void* grad_corrected, dspark_dtype_t logits_dtype,
