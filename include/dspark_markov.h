@@ -89,6 +89,14 @@ size_t dspark_markov_workspace_bytes(int64_t B, int64_t M, int64_t V, int64_t r,
 /* Zero-fill `bytes` bytes of workspace on `stream` with a device kernel. */
 dspark_status_t dspark_markov_workspace_init(void* workspace, size_t bytes, void* stream);
 
+/* Device-to-device copy of `bytes` bytes with the streaming cache policy the
+ * head's kernels use for logits.  Not a step of the head: a bandwidth
+ * reference, timed beside the head's calls as the practical HBM ceiling.
+ * dst and src device pointers, 16-byte aligned, not overlapping; bytes a
+ * multiple of 16 (0 is a no-op).  DSPARK_ERR_INVALID_ARGUMENT otherwise.
+ * Asynchronous on `stream`; the caller owns both buffers. */
+dspark_status_t dspark_markov_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
+
 /* Teacher-forced block bias (VanillaMarkov.apply_block_logits, third-party
  * markov_head.py page).
  *   base_logits      device, [B, M, V], logits_dtype.

@@ -31,6 +31,7 @@ STATUS = {
 EXPORTS = (
     "dspark_markov_workspace_bytes",
     "dspark_markov_workspace_init",
+    "dspark_markov_stream_copy",
     "dspark_markov_apply_block",
     "dspark_markov_sample_block",
     "dspark_markov_gated_workspace_bytes",
@@ -75,6 +76,8 @@ def load():
     L.dspark_markov_workspace_bytes.restype = sz
     L.dspark_markov_workspace_init.argtypes = [p, sz, p]
     L.dspark_markov_workspace_init.restype = i32
+    L.dspark_markov_stream_copy.argtypes = [p, p, sz, p]
+    L.dspark_markov_stream_copy.restype = i32
     L.dspark_markov_apply_block.argtypes = [p, i32, p, p, p, i32, i64, i64, i64, i64, p, p, sz, p]
     L.dspark_markov_apply_block.restype = i32
     L.dspark_markov_sample_block.argtypes = [p, i32, p, p, p, i32, i64, i64, i64, i64,

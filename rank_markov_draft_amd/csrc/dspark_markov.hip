@@ -190,6 +190,15 @@ dspark_status_t dspark_markov_workspace_init(void* workspace, size_t bytes, void
   return DSPARK_OK;
 }
 
+dspark_status_t dspark_markov_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (bytes == 0) return DSPARK_OK;
+  if (!dst || !src || !aligned16(dst) || !aligned16(src) || bytes % 16 != 0 || overlaps(dst, bytes, src, bytes))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  const hipError_t e = dspark::launch_copy_stream(dst, src, bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return device_failure(e, "stream copy");
+  return DSPARK_OK;
+}
+
 dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_t logits_dtype,
                                           const int64_t* token_ids, const void* w1,
                                           const void* w2, dspark_dtype_t weight_dtype,

@@ -131,5 +131,7 @@ hipError_t launch_generic(const KernelParams& p, bool logits_bf16, bool weights_
 hipError_t launch_reduce(const uint64_t* partials, int64_t nparts, int64_t B, int64_t M, int64_t k,
                          int64_t* tokens, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// Streaming-policy device copy (bytes % 16 == 0, 16-byte aligned, no overlap).
+hipError_t launch_copy_stream(void* dst, const void* src, size_t bytes, hipStream_t s);
 
 }  // namespace dspark

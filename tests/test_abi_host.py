@@ -230,3 +230,18 @@ def test_backward_argument_errors(L):
     # gradients over each other or over an input
     assert _bwd(L, gw1=ctypes.c_void_p(0x700000), gw2=ctypes.c_void_p(0x700000 + 64)) == 1
     assert _bwd(L, gw1=ctypes.c_void_p(0x500000 + 16)) == 1    # over W1
+
+
+def test_stream_copy_argument_errors(L):
+    """The streaming copy (a bandwidth reference) takes 16-byte aligned,
+    non-overlapping buffers and whole 16-byte pieces; zero bytes is a no-op.
+    Every call here is rejected before any launch."""
+    a, b = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    bad = 1   # DSPARK_ERR_INVALID_ARGUMENT
+    assert L.dspark_markov_stream_copy(b, a, 0, None) == 0
+    assert L.dspark_markov_stream_copy(None, a, 4096, None) == bad
+    assert L.dspark_markov_stream_copy(b, None, 4096, None) == bad
+    assert L.dspark_markov_stream_copy(ctypes.c_void_p(0x200008), a, 4096, None) == bad
+    assert L.dspark_markov_stream_copy(b, ctypes.c_void_p(0x100004), 4096, None) == bad
+    assert L.dspark_markov_stream_copy(b, a, 4100, None) == bad
+    assert L.dspark_markov_stream_copy(ctypes.c_void_p(0x100800), a, 4096, None) == bad   # overlap

@@ -63,3 +63,20 @@ def test_unused_gate_tensors_are_not_checked(native):
     ref = rmd.apply_block_logits(t["base"], t["ids"], t["w1"], t["w2"])
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+def test_stream_copy_is_exact(native):
+    """The streaming copy that bench.py times as the HBM ceiling moves the
+    bytes exactly, including a partial last pass of its workgroups."""
+    import ctypes
+    from rank_markov_draft_amd import _lib
+    lib = _lib.load()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for n in (16, 4096 + 16, (1 << 20) + 48, 64 << 20):
+        src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+        dst = torch.zeros(n + 64, dtype=torch.uint8, device="cuda")
+        assert lib.dspark_markov_stream_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()), n,
+                                             stream) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(dst[:n], src), n
+        assert not dst[n:].any(), "bytes past the end were written"
