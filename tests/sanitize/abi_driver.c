@@ -98,6 +98,13 @@ int main(void) {
                                                                         (char*)F + 2048, F, 8, NULL),
          DSPARK_ERR_WORKSPACE_TOO_SMALL);
 
+  /* streaming copy (bandwidth reference) */
+  expect("copy misaligned", dspark_markov_stream_copy((char*)F + 8, (char*)F + 2048, 1024, NULL),
+         DSPARK_ERR_INVALID_ARGUMENT);
+  expect("copy overlap", dspark_markov_stream_copy(F, (char*)F + 1024, 2048, NULL), DSPARK_ERR_INVALID_ARGUMENT);
+  expect("copy ragged", dspark_markov_stream_copy(F, (char*)F + 2048, 1000, NULL), DSPARK_ERR_INVALID_ARGUMENT);
+  expect("copy nothing", dspark_markov_stream_copy(F, (char*)F + 2048, 0, NULL), DSPARK_OK);
+
   /* status strings, including an unknown code */
   for (int s = 0; s <= 5; ++s)
     if (!dspark_status_string((dspark_status_t)s)) ++failures;
