@@ -461,3 +461,38 @@ def test_greedy_special_values(native, B):
         if b % 8 in expect:
             assert (tok[b] == expect[b % 8]).all(), (b, tok[b])
     check_chain(inp, 0.0, 0, tok, corr, name=f"greedy special values B{B}")
+
+
+def test_apply_beyond_31_bit_offsets(native):
+    """16640 rows at V = 129280 (2.15e9 bf16 logits, 4.3 GB): element offsets
+    pass 2^31, so the apply leaves the grouped and row-order kernels for the
+    tile kernel with 64-bit offsets.  The base logits come from a seeded torch
+    generator on the device; rows at the start, on both sides of element 2^31
+    and at the end are copied back and checked against the oracle."""
+    B, M, V, r = 3328, 5, 129280, 256
+    n_rows = B * M
+    assert n_rows * V > 2**31
+    w = wl.WORKLOADS["teacher_forced_320"]
+    small = wl.make_inputs(w)                  # W1 and W2 at this V and r
+    assert small["w1"].shape == (V, r)
+    ids = np.random.default_rng(12).integers(0, V, size=(B, M)).astype(np.int64)
+    gen = torch.Generator(device="cuda").manual_seed(12)
+    base = torch.empty((B, M, V), dtype=torch.bfloat16, device="cuda")
+    for b0 in range(0, B, 256):                # slices bound the fp32 temporary
+        nb = min(256, B - b0)
+        base[b0:b0 + nb] = (2.0 * torch.randn((nb, M, V), generator=gen, device="cuda")).to(torch.bfloat16)
+    d = device_inputs({"token_ids": ids, "w1": small["w1"], "w2": small["w2"]})
+    out = rmd.apply_block_logits(base, d["token_ids"], d["w1"], d["w2"])
+    torch.cuda.synchronize()
+    edge = 2**31 // V                          # the row that holds element 2^31
+    rows = np.array([0, 1, edge - 1, edge, edge + 1, n_rows - 2, n_rows - 1])
+    sel = torch.as_tensor(rows, device="cuda")
+    base_s = from_dev(base.view(n_rows, V).index_select(0, sel)).reshape(len(rows), 1, V)
+    out_s = from_dev(out.view(n_rows, V).index_select(0, sel)).reshape(len(rows), 1, V)
+    del base, out
+    torch.cuda.empty_cache()
+    ids_s = ids.reshape(n_rows, 1)[rows]
+    ref = orc.apply_block(base_s, ids_s, small["w1"], small["w2"])
+    rep = parity.check_logits(out_s, ref, base_s, ids_s, small["w1"], small["w2"])
+    _report("apply beyond 2^31 elements", **dataclasses.asdict(rep))
+    assert rep.mismatches <= 1e-4 * rep.elements
