@@ -496,3 +496,16 @@ def test_apply_beyond_31_bit_offsets(native):
     rep = parity.check_logits(out_s, ref, base_s, ids_s, small["w1"], small["w2"])
     _report("apply beyond 2^31 elements", **dataclasses.asdict(rep))
     assert rep.mismatches <= 1e-4 * rep.elements
+
+
+@pytest.mark.parametrize("B", [4096, 4097])
+@pytest.mark.parametrize("T", [0.0, 0.7])
+def test_sample_at_the_step_kernel_row_limit(native, B, T):
+    """4096 batch rows are the most the step kernel stages in LDS; 4097 take
+    the tile kernel.  Sampled batch rows (the first and last among them) are
+    checked step by step against the oracle."""
+    w = wl.WORKLOADS["temperature_draft_256x8"]
+    inp = wl.make_inputs(w, B=B, M=2, V=512, r=64, seed=B)
+    tok, corr = run_sample(inp, T, seed=3)
+    rows = np.unique(np.concatenate([np.random.default_rng(B).choice(B, 60, replace=False), [0, B - 1]]))
+    check_chain(inp, T, 3, tok, corr, brows=rows, name=f"sample B{B} T{T} at the step kernel's row limit")
