@@ -298,6 +298,34 @@ int dspark_oracle_select_token(const void* row, int logits_dtype, int64_t V,
   return ORACLE_OK;
 }
 
+/* dspark_oracle_select_token for n rows [n, V] at once (rows in parallel):
+ * row i draws with noise indices (b_abs[i], k_abs[i]); scores [n, 2] and
+ * runner_up [n] may be NULL. */
+int dspark_oracle_select_tokens(const void* rows, int logits_dtype, int64_t n, int64_t V,
+                                double temperature, uint64_t seed, const int64_t* b_abs,
+                                const int64_t* k_abs, int64_t* tokens, float* scores,
+                                int64_t* runner_up, int n_threads) {
+  if (!valid_dtype(logits_dtype)) return ORACLE_UNSUPPORTED;
+  if (n < 0 || V <= 0 || isnan(temperature)) return ORACLE_INVALID;
+  if (n == 0) return ORACLE_OK;
+  if (!rows || !b_abs || !k_abs || !tokens) return ORACLE_INVALID;
+  const size_t esz = logits_dtype == ORACLE_F32 ? 4 : 2;
+  int nt = n_threads_or_default(n_threads);
+#pragma omp parallel num_threads(nt)
+  {
+    float* c = (float*)malloc((size_t)V * sizeof(float));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; ++i) {
+      const void* row = (const char*)rows + (size_t)(i * V) * esz;
+      for (int64_t v = 0; v < V; ++v) c[v] = load_as_float(row, logits_dtype, v);
+      select_from_row(c, V, temperature, seed, b_abs[i], k_abs[i], tokens + i,
+                      scores ? scores + 2 * i : NULL, runner_up ? runner_up + i : NULL);
+    }
+    free(c);
+  }
+  return ORACLE_OK;
+}
+
 /* [P5] VanillaMarkov.sample_block_tokens: left to right, step k biases
  * base[:, k, :] by the previous token (first_prev for k = 0, the token just
  * drawn at k-1 after that), keeps the corrected row and draws the next token

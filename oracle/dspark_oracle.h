@@ -83,6 +83,14 @@ int dspark_oracle_select_token(const void* row, int logits_dtype, int64_t V,
                                int64_t k_abs, int64_t* token, float* score_out,
                                int64_t* runner_up);
 
+/* dspark_oracle_select_token over n rows [n, V] (rows in parallel, n_threads
+ * 0 = all cores); row i uses noise indices (b_abs[i], k_abs[i]).  scores
+ * [n, 2] and runner_up [n] may be NULL. */
+int dspark_oracle_select_tokens(const void* rows, int logits_dtype, int64_t n, int64_t V,
+                                double temperature, uint64_t seed, const int64_t* b_abs,
+                                const int64_t* k_abs, int64_t* tokens, float* scores,
+                                int64_t* runner_up, int n_threads);
+
 /* Bounds on one corrected element under any fp32 accumulation order:
  * for each of n (row, v) pairs, with row indexing the flattened [B*M] rows,
  * writes lo/hi (as float values of the L-typed results) obtained by pushing

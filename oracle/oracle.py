@@ -59,6 +59,9 @@ def lib():
         L.dspark_oracle_select_token.argtypes = [
             _p, _int, _i64, ctypes.c_double, ctypes.c_uint64, _i64, _i64, _p, _p, _p]
         L.dspark_oracle_select_token.restype = _int
+        L.dspark_oracle_select_tokens.argtypes = [
+            _p, _int, _i64, _i64, ctypes.c_double, ctypes.c_uint64, _p, _p, _p, _p, _p, _int]
+        L.dspark_oracle_select_tokens.restype = _int
         L.dspark_oracle_logit_bounds.argtypes = [
             _p, _int, _p, _p, _p, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p]
         L.dspark_oracle_logit_bounds.restype = _int
@@ -168,6 +171,24 @@ def select_token(row, temperature=0.0, seed=0, b_abs=0, k_abs=0):
         _ptr(row), _dtype_tag(row), row.shape[-1], float(temperature),
         int(seed) & (2**64 - 1), int(b_abs), int(k_abs), _ptr(tok), _ptr(sc), _ptr(ru)))
     return int(tok[0]), float(sc[0]), float(sc[1]), int(ru[0])
+
+
+def select_tokens(rows, temperature=0.0, seed=0, b_abs=None, k_abs=None, n_threads: int = 0):
+    """select_token over rows [n, V] at once; returns (tokens [n], scores [n, 2]
+    (winner, runner-up), runner_up [n])."""
+    rows = np.ascontiguousarray(rows)
+    V = rows.shape[-1]
+    rows = rows.reshape(-1, V)
+    n = rows.shape[0]
+    b_abs = np.ascontiguousarray(np.zeros(n) if b_abs is None else b_abs, dtype=np.int64)
+    k_abs = np.ascontiguousarray(np.zeros(n) if k_abs is None else k_abs, dtype=np.int64)
+    tok = np.zeros(n, dtype=np.int64)
+    sc = np.zeros((n, 2), dtype=np.float32)
+    ru = np.zeros(n, dtype=np.int64)
+    _check(lib().dspark_oracle_select_tokens(
+        _ptr(rows), _dtype_tag(rows), n, V, float(temperature), int(seed) & (2**64 - 1),
+        _ptr(b_abs), _ptr(k_abs), _ptr(tok), _ptr(sc), _ptr(ru), n_threads))
+    return tok, sc, ru
 
 
 def logit_bounds(base, token_ids, w1, w2, rows, cols):

@@ -743,3 +743,17 @@ def test_backward_zero_gradient_and_bounds(oracle_mod):
     x = inp["token_ids"].reshape(-1)[rng.integers(0, 6, 50)]
     lo, mid, hi = oracle_mod.backward_bounds(grad, inp["token_ids"], inp["w1"], inp["w2"], "dw1", x, j)
     assert np.array_equal(mid, as_float(dw1)[x, j]) and np.all(lo <= mid) and np.all(mid <= hi)
+
+
+def test_select_tokens_equals_single_rows(oracle_mod):
+    """The batched selection is select_token row by row (greedy and
+    temperature, with each row's own noise indices)."""
+    rng = np.random.default_rng(3)
+    rows = wl.to_bf16_bits(rng.standard_normal((12, 300), dtype=np.float32) * 2)
+    b_abs = rng.integers(0, 50, 12)
+    k_abs = rng.integers(0, 8, 12)
+    for T in (0.0, 0.9):
+        tok, sc, ru = oracle_mod.select_tokens(rows, T, 77, b_abs, k_abs)
+        for i in range(12):
+            t1, best, second, r1 = oracle_mod.select_token(rows[i], T, 77, b_abs[i], k_abs[i])
+            assert (tok[i], sc[i, 0], sc[i, 1], ru[i]) == (t1, np.float32(best), np.float32(second), r1)
