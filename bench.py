@@ -83,10 +83,14 @@ def calibrate_copy(torch):
           file=sys.stderr)
 
 
-def copy_ceiling(torch, np, lib):
-    """The practical HBM ceiling: the library's streaming-policy device copy
-    of 1 GiB (read and written), 3 warm-up and 10 timed copies with events
-    on the current stream; torch's copy_ of the same buffers beside it."""
+def copy_ceiling(torch, np, bw):
+    """The practical HBM ceilings, from the bandwidth probes of
+    libdspark_bandwidth.so (streaming policy, not steps of the head), each
+    timed with events on the current stream (3 warm-up and 10 timed runs,
+    median): a 1 GiB copy (read and written, 1 : 1), and a read-mix pass that
+    reads 1.8 bytes per byte written, the head's own mix (base logits and W2
+    read, corrected logits written); torch's copy_ of the 1 GiB buffers
+    beside them."""
     import ctypes
     src = torch.empty(512 * 1024 * 1024, dtype=torch.bfloat16, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
@@ -96,9 +100,9 @@ def copy_ceiling(torch, np, lib):
     sp, dp = ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr())
 
     def stream_copy(i):
-        st = lib.dspark_markov_stream_copy(dp, sp, size, stream)
+        st = bw.dspark_bandwidth_copy(dp, sp, size, stream)
         if st != 0:
-            raise RuntimeError(f"dspark_markov_stream_copy: status {st}")
+            raise RuntimeError(f"dspark_bandwidth_copy: status {st}")
 
     _, per = time_calls(stream_copy, 1, 10, 3, torch)
     ms = float(np.median(per))
@@ -106,11 +110,23 @@ def copy_ceiling(torch, np, lib):
     ms_t = float(np.median(per_t))
     if not torch.equal(dst, src):
         raise RuntimeError("the reference copy is wrong")
+    wbytes = (int(size / 1.8) // 16) * 16          # written; reads all `size` source bytes
+
+    def read_mix(i):
+        st = bw.dspark_bandwidth_read_mix(dp, wbytes, sp, size, stream)
+        if st != 0:
+            raise RuntimeError(f"dspark_bandwidth_read_mix: status {st}")
+
+    _, per_m = time_calls(read_mix, 1, 10, 3, torch)
+    ms_m = float(np.median(per_m))
     del src, dst
     torch.cuda.empty_cache()
     gbs = nbytes / (ms * 1e-3) / 1e9
+    gbs_m = (size + wbytes) / (ms_m * 1e-3) / 1e9
     return {"GBps": gbs, "bytes_per_copy": nbytes, "ms_per_copy": ms, "frac_of_peak": gbs / HBM_PEAK_GBS,
-            "kind": "streaming-policy device copy (dspark_markov_stream_copy)",
+            "kind": "streaming-policy device copy (dspark_bandwidth_copy, libdspark_bandwidth.so)",
+            "read_mix_GBps": gbs_m, "read_mix_read_per_write": size / wbytes,
+            "read_mix_frac_of_peak": gbs_m / HBM_PEAK_GBS,
             "torch_copy_GBps": nbytes / (ms_t * 1e-3) / 1e9}
 
 
@@ -417,9 +433,10 @@ def main():
     }
     del sets
     torch.cuda.empty_cache()
-    ceiling = copy_ceiling(torch, np, _lib.load())
+    ceiling = copy_ceiling(torch, np, _lib.load_bandwidth())
     result["copy_ceiling"] = ceiling
     result["roofline"]["frac_of_copy_ceiling"] = achieved / ceiling["GBps"]
+    result["roofline"]["frac_of_read_mix_ceiling"] = achieved / ceiling["read_mix_GBps"]
     if not args.no_extra:
         names = [n for n in args.extra.split(",") if n]
         unknown = [n for n in names if n not in wl.WORKLOADS]

@@ -89,14 +89,6 @@ size_t dspark_markov_workspace_bytes(int64_t B, int64_t M, int64_t V, int64_t r,
 /* Zero-fill `bytes` bytes of workspace on `stream` with a device kernel. */
 dspark_status_t dspark_markov_workspace_init(void* workspace, size_t bytes, void* stream);
 
-/* Device-to-device copy of `bytes` bytes with the streaming cache policy the
- * head's kernels use for logits.  Not a step of the head: a bandwidth
- * reference, timed beside the head's calls as the practical HBM ceiling.
- * dst and src device pointers, 16-byte aligned, not overlapping; bytes a
- * multiple of 16 (0 is a no-op).  DSPARK_ERR_INVALID_ARGUMENT otherwise.
- * Asynchronous on `stream`; the caller owns both buffers. */
-dspark_status_t dspark_markov_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
-
 /* Teacher-forced block bias (VanillaMarkov.apply_block_logits, third-party
  * markov_head.py page).
  *   base_logits      device, [B, M, V], logits_dtype.
@@ -131,7 +123,21 @@ dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_
  *   position_offset,     absolute step and batch indices of position 0 / row 0
  *   batch_offset         for the noise, so that M one-step calls, or a batch
  *                        split across calls, reproduce one whole call.
- * M == 0 or B == 0 is a successful no-op.  V == 0 with B*M > 0 is invalid. */
+ * M == 0 or B == 0 is a successful no-op.  V == 0 with B*M > 0 is invalid.
+ *
+ * Greedy bf16 calls with B <= 64 and r <= 256 run as one persistent launch
+ * whose workgroups (one per CU) exchange each step's tokens through the
+ * workspace; the host takes that path only when the occupancy query says a
+ * CU can hold one of its workgroups.  Should a workgroup still be unable to
+ * start (CUs held by other streams' kernels), the others give up waiting
+ * after 1 s instead of hanging: the call then writes -1 to every token of
+ * sampled_tokens (corrected_logits is then undefined) and records the
+ * failure in the workspace.  Until dspark_markov_read_device_error reads
+ * and clears that record, every later persistent launch on the same
+ * workspace does no work and also returns -1 tokens, so a failure cannot
+ * pass unnoticed.  The word at byte 128 of the workspace is a test hook:
+ * nonzero makes every such wait give up at once (the failure path without a
+ * stall); zero-filled workspaces leave it off. */
 dspark_status_t dspark_markov_sample_block(const void* base_logits, dspark_dtype_t logits_dtype,
                                            const int64_t* first_prev_token_ids, const void* w1,
                                            const void* w2, dspark_dtype_t weight_dtype,
@@ -215,7 +221,10 @@ dspark_status_t dspark_markov_apply_block_backward(const void* grad_corrected, d
 
 /* Synchronises `stream`, then returns in *bad_rows the number of rows whose
  * predecessor id was outside [0, V) in the calls made with this workspace
- * since the last read, and clears the count. */
+ * since the last read, and clears the count.  Returns DSPARK_ERR_DEVICE when
+ * a persistent sampling launch on this workspace failed since the last read
+ * (its tokens were -1, see dspark_markov_sample_block); the failure record
+ * is cleared too, so the next call runs normally. */
 dspark_status_t dspark_markov_read_device_error(void* workspace, void* stream, int64_t* bad_rows);
 
 /* Static description of a status code. */

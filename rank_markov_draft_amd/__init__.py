@@ -82,9 +82,17 @@ class Workspace:
     def ptr(self):
         return _ptr(self.buffer)
 
+    def set_chain_test_hook(self, on: bool):
+        """Tests of the failure path: with the hook on, the persistent chain's
+        device-wide waits give up at once, so the call returns -1 tokens and
+        records a failure without a stall (control word at byte 128)."""
+        self.buffer[128:132].view(torch.int32).fill_(1 if on else 0)
+
 
 def read_device_error(ws: Workspace) -> int:
-    """Rows with out-of-range predecessor ids since the last read (synchronises)."""
+    """Rows with out-of-range predecessor ids since the last read (synchronises).
+    Raises DeviceError when a persistent sampling launch on ``ws`` failed since
+    the last read (its tokens were -1); the record is cleared either way."""
     n = ctypes.c_int64(0)
     _lib.check(_lib.load().dspark_markov_read_device_error(
         ws.ptr, _stream_handle(ws.buffer.device), ctypes.byref(n)), "read_device_error")
@@ -142,12 +150,18 @@ def sample_block_tokens(base_logits: torch.Tensor, first_prev_token_ids: torch.T
                         seed: int = 0, position_offset: int = 0, batch_offset: int = 0,
                         return_logits: bool = True, tokens_out: torch.Tensor | None = None,
                         logits_out: torch.Tensor | None = None,
-                        workspace: Workspace | None = None):
+                        workspace: Workspace | None = None, check: bool = False):
     """Left-to-right block sampling over base_logits [B, M, V].
 
     Returns ``(sampled_tokens [B, M] int64, corrected_logits [B, M, V] or None)``.
     ``temperature`` None or below 1e-5 is greedy argmax; otherwise Gumbel-max
-    with Philox4x32-10 noise keyed by ``seed``."""
+    with Philox4x32-10 noise keyed by ``seed``.
+
+    Greedy bf16 calls of up to 64 rows run as one persistent launch.  If its
+    workgroups cannot all run (CUs held by other work), it gives up after 1 s
+    and every token is -1; later persistent calls on the same workspace also
+    return -1 tokens until ``read_device_error`` (which raises) clears the
+    record.  ``check=True`` synchronises after the call and raises at once."""
     _check_weights(w1, w2)
     if base_logits.dim() != 3:
         raise ValueError("base_logits must be [B, M, V]")
@@ -185,6 +199,8 @@ def sample_block_tokens(base_logits: torch.Tensor, first_prev_token_ids: torch.T
         B, M, V, r, T, int(seed) & (2**64 - 1), int(position_offset), int(batch_offset),
         _ptr(tokens_out), _ptr(corrected), workspace.ptr, workspace.nbytes, _stream_handle(dev))
     _lib.check(st, "sample_block_tokens")
+    if check:
+        read_device_error(workspace)
     return tokens_out, corrected
 
 

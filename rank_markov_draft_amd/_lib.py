@@ -18,6 +18,7 @@ CSRC = os.path.join(_HERE, "csrc")
 
 DSPARK_F32 = 0
 DSPARK_BF16 = 1
+DSPARK_ERR_DEVICE = 4
 
 STATUS = {
     0: "DSPARK_OK",
@@ -31,7 +32,6 @@ STATUS = {
 EXPORTS = (
     "dspark_markov_workspace_bytes",
     "dspark_markov_workspace_init",
-    "dspark_markov_stream_copy",
     "dspark_markov_apply_block",
     "dspark_markov_sample_block",
     "dspark_markov_gated_workspace_bytes",
@@ -76,8 +76,6 @@ def load():
     L.dspark_markov_workspace_bytes.restype = sz
     L.dspark_markov_workspace_init.argtypes = [p, sz, p]
     L.dspark_markov_workspace_init.restype = i32
-    L.dspark_markov_stream_copy.argtypes = [p, p, sz, p]
-    L.dspark_markov_stream_copy.restype = i32
     L.dspark_markov_apply_block.argtypes = [p, i32, p, p, p, i32, i64, i64, i64, i64, p, p, sz, p]
     L.dspark_markov_apply_block.restype = i32
     L.dspark_markov_sample_block.argtypes = [p, i32, p, p, p, i32, i64, i64, i64, i64,
@@ -104,6 +102,27 @@ def load():
     L.dspark_markov_last_error.restype = ctypes.c_char_p
     _lib = L
     return L
+
+
+BANDWIDTH_LIB_PATH = os.path.join(_HERE, "libdspark_bandwidth.so")
+_bw = None
+
+
+def load_bandwidth():
+    """The streaming probes the benchmark times as HBM ceilings (not part of
+    the head): dspark_bandwidth_copy and dspark_bandwidth_read_mix."""
+    global _bw
+    if _bw is None:
+        if not os.path.exists(BANDWIDTH_LIB_PATH):
+            raise ImportError(f"{BANDWIDTH_LIB_PATH} is missing: build it first")
+        L = ctypes.CDLL(BANDWIDTH_LIB_PATH)
+        p, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        L.dspark_bandwidth_copy.argtypes = [p, p, sz, p]
+        L.dspark_bandwidth_copy.restype = i32
+        L.dspark_bandwidth_read_mix.argtypes = [p, sz, p, sz, p]
+        L.dspark_bandwidth_read_mix.restype = i32
+        _bw = L
+    return _bw
 
 
 def check(status: int, what: str):

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstddef>
 #include <cstring>
 #include <string>
 
@@ -15,9 +16,9 @@ namespace {
 thread_local std::string g_last_error;
 
 // Workspace layout:
-//   [0, 256)      control block: the device error word, the grid arrival
-//                 counter and the synchronisation-failure count of the
-//                 persistent chain, each on its own 64-byte line;
+//   [0, 256)      control block: the device error word, the
+//                 synchronisation-failure count of the persistent chain and
+//                 its test hook, each on its own 64-byte line;
 //   partials      per-(row, vocabulary slice) argmax keys of one sampling
 //                 step (step-by-step path), B * ceil(V/128) words;
 //   chain sync    arrival counters and release words of the persistent
@@ -27,10 +28,12 @@ thread_local std::string g_last_error;
 constexpr size_t kControlBytes = 256;
 
 struct Control {
-  uint32_t bad_rows;
+  uint32_t bad_rows;       // byte 0: rows with out-of-range ids
   uint32_t pad0[15];
-  uint32_t sync_failures;
+  uint32_t sync_failures;  // byte 64: failed device-wide waits of the persistent chain
   uint32_t pad1[15];
+  uint32_t chain_test_hook;  // byte 128: nonzero makes the chain's waits give up at once
+  uint32_t pad2[15];
 };
 static_assert(sizeof(Control) <= kControlBytes, "control block");
 
@@ -190,15 +193,6 @@ dspark_status_t dspark_markov_workspace_init(void* workspace, size_t bytes, void
   return DSPARK_OK;
 }
 
-dspark_status_t dspark_markov_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
-  if (bytes == 0) return DSPARK_OK;
-  if (!dst || !src || !aligned16(dst) || !aligned16(src) || bytes % 16 != 0 || overlaps(dst, bytes, src, bytes))
-    return DSPARK_ERR_INVALID_ARGUMENT;
-  const hipError_t e = dspark::launch_copy_stream(dst, src, bytes, (hipStream_t)stream);
-  if (e != hipSuccess) return device_failure(e, "stream copy");
-  return DSPARK_OK;
-}
-
 dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_t logits_dtype,
                                           const int64_t* token_ids, const void* w1,
                                           const void* w2, dspark_dtype_t weight_dtype,
@@ -337,6 +331,7 @@ dspark_status_t dspark_markov_sample_block(const void* base_logits, dspark_dtype
     c.keys = (uint64_t*)((char*)c.sync + dspark::kChainSyncBytes);
     c.bad_rows = &ctl->bad_rows;
     c.sync_failures = &ctl->sync_failures;
+    c.test_hook = &ctl->chain_test_hook;
     c.B = B;
     c.M = M;
     c.V = V;
@@ -639,12 +634,13 @@ dspark_status_t dspark_markov_read_device_error(void* workspace, void* stream, i
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return device_failure(e, "read device error");
   *bad_rows = (int64_t)c.bad_rows;
-  e = dspark::launch_fill_zero(workspace, sizeof(Control), s);
+  // clear the error words; the test hook (third line) stays as the caller set it
+  e = dspark::launch_fill_zero(workspace, offsetof(Control, chain_test_hook), s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return device_failure(e, "clear device error");
   if (c.sync_failures != 0) {
-    g_last_error = "the persistent chain timed out waiting for its workgroups; "
-                   "zero-fill the workspace before reusing it";
+    g_last_error = "the persistent chain timed out waiting for its workgroups and returned -1 tokens; "
+                   "the failure count is now cleared";
     return DSPARK_ERR_DEVICE;
   }
   return DSPARK_OK;

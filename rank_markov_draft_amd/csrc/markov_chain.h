@@ -29,7 +29,8 @@ struct ChainParams {
   uint64_t* keys;             // [M][chain_key_groups()][chain_max_rows()] * kKeyPad
   uint32_t* sync;             // kChainSyncBytes
   uint32_t* bad_rows;
-  uint32_t* sync_failures;
+  uint32_t* sync_failures;    // failed device-wide waits; nonzero at entry: the workspace is poisoned
+  const uint32_t* test_hook;  // nonzero: every device-wide wait gives up at once (tests of the failure path)
   int64_t B;
   int64_t M;
   int64_t V;
@@ -40,6 +41,8 @@ struct ChainParams {
 int chain_max_rows();
 int chain_key_groups();
 int chain_waves_per_group();
+// hipErrorNotSupported when the shape does not fit the kernel or the device
+// cannot hold one of its workgroups per CU.
 hipError_t launch_chain_greedy(const ChainParams& p, int num_cus, hipStream_t s);
 
 }  // namespace dspark

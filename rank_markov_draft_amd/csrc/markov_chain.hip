@@ -36,7 +36,10 @@
 // Every wait on other workgroups is bounded: a workgroup that waits too long
 // records a failure in the workspace and leaves, so no launch can hang.  The
 // last workgroup to leave clears the keys and counters, so the workspace is
-// ready for the next call.
+// ready for the next call, and when any wait failed it overwrites every token
+// of the call with -1, so a failed chain never returns plausible tokens.  A
+// launch that finds the failure count already nonzero (a failure nobody has
+// read back and cleared) does no work and also returns -1 tokens.
 #include "device_common.h"
 #include "markov_chain.h"
 
@@ -132,6 +135,12 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   const int G = gridDim.x;
   const int g = blockIdx.x;
   const int xg = g % kGroups;
+  // A workspace whose failure count is nonzero stays poisoned until the host
+  // reads and clears it: skip all work (the exit below writes -1 tokens).
+  const bool poisoned =
+      __builtin_amdgcn_readfirstlane((int)__hip_atomic_load(p.sync_failures, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT)) != 0;
+  const bool force_timeout = __builtin_amdgcn_readfirstlane((int)*p.test_hook) != 0;
   // The host guarantees B <= 64, V <= 32 * 16 * CUs, B*M*V < 2^30 and
   // M <= 4096, so every index below fits in 32 bits.
   const int B = (int)p.B, M = (int)p.M, V = (int)p.V, r = (int)p.r;
@@ -241,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     load_row(gg, 0);
     store_row_lds(gg);
   }
-  if (wave == 1) {
+  if (wave == 1 && !poisoned) {
     for (int gg = 0; gg < NR; ++gg) {
       const int b = gg * rpg + n16;
       int x = -1;
@@ -257,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
 #pragma unroll
       for (int gg = 0; gg < kMaxGroups; ++gg) lds_key[gg][lane] = 0u;
     }
-    if (lane == 0) lds_flag = 1;
+    if (lane == 0) lds_flag = poisoned ? 0 : 1;
   }
   wait_vmcnt<0>();
   lds_barrier();
@@ -270,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   // ---- windows.  Window w starts with the exchange and bulk work for
   // earlier units, which overlaps the matrix work of the other waves, then
   // computes unit w = 6k + g (step k of group g); one barrier ends it.
-  for (int w = 0; w < U; ++w) {
+  for (int w = 0; w < (poisoned ? 0 : U); ++w) {
     const int gc = w % kRowGroups;  // slot of unit w (its group when real)
     int after_gather = 0;           // wave 1
 
@@ -329,7 +338,8 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
         uint32_t seen = 0;
 #pragma unroll
         for (int x = 0; x < kGroups; ++x) seen += (uint32_t)__builtin_amdgcn_readlane((int)cx, x);
-        if (seen < target) ok = wait_arrivals(sync, u2 % kRowGroups, lane, target);
+        if (force_timeout) ok = false;
+        else if (seen < target) ok = wait_arrivals(sync, u2 % kRowGroups, lane, target);
       }
       if (do2 && ok) load_keys(u2 & 1, u2 % kRowGroups, u2 / kRowGroups - 1);
       // poll the arrivals of unit w+3's previous step into LDS (lane
@@ -455,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     const uint32_t target = (uint32_t)M * (uint32_t)G;
     bool fin = true;
     for (int gg = 0; gg < NR; ++gg) {
-      fin = fin && wait_arrivals(sync, gg, lane, target);
+      fin = fin && !force_timeout && wait_arrivals(sync, gg, lane, target);
       const int b = gg * rpg + n16;
       const bool row_ok = n16 < rpg && b < B;
       const uint64_t k0 = row_ok ? __hip_atomic_load((uint64_t*)((unsigned char*)p.keys + key_offset(M - 1, 2 * g4, b)),
@@ -476,8 +486,9 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   lds_barrier();
 
   // Leave; the last workgroup out clears the keys and the counters (every
-  // other workgroup has passed its last wait and read).
-  if (tid == 0) lds_flag = (__hip_atomic_fetch_add(exit_counter(sync), 1u, __ATOMIC_RELAXED,
+  // other workgroup has passed its last wait and read, and its token writes
+  // and failure counts are ordered before its exit count).
+  if (tid == 0) lds_flag = (__hip_atomic_fetch_add(exit_counter(sync), 1u, __ATOMIC_ACQ_REL,
                                                    __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(G - 1)) ? 1 : 0;
   lds_barrier();
   if (lds_flag) {
@@ -485,6 +496,9 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
       __hip_atomic_store(p.keys + (uint32_t)(i * kKeyPad), (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid < kRowGroups * kGroups + 1)
       __hip_atomic_store(sync + 16 * tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // a failed or refused chain: no token of the call is trustworthy
+    if (__hip_atomic_load(p.sync_failures, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != 0u)
+      for (int i = tid; i < B * M; i += kThreads) p.tokens[(uint32_t)i] = -1;
   }
 }
 
@@ -494,11 +508,33 @@ namespace {
 // A plain launch of one 1024-thread workgroup per CU: the kernel's LDS and
 // VGPR use admit one workgroup per CU, so on an idle device all of them are
 // resident together (a cooperative launch would guarantee it, at about 17 us
-// of extra launch latency measured on MI355X).  If a workgroup cannot start
-// while the others wait, their bounded waits end the launch with a recorded
-// synchronisation failure instead of a hang.
+// of extra launch latency measured on MI355X).  The host declines the chain
+// when the occupancy query says a CU cannot hold a workgroup.  If a
+// workgroup still cannot start while the others wait (CUs held by other
+// streams' kernels), their bounded waits end the launch with a recorded
+// synchronisation failure and -1 tokens instead of a hang.
+// Workgroups of markov_chain_greedy_bf16<K32> one CU of the current device
+// can hold, cached per device; the chain needs at least one.
+template <int K32>
+int chain_occupancy() {
+  static int cache[64];
+  static bool known[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!known[dev]) {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, markov_chain_greedy_bf16<K32>, kThreads, 0) !=
+        hipSuccess)
+      blocks = 0;
+    cache[dev] = blocks;
+    known[dev] = true;
+  }
+  return cache[dev];
+}
+
 template <int K32>
 hipError_t launch_chain_k(const ChainParams& p, int grid, hipStream_t s) {
+  if (chain_occupancy<K32>() < 1) return hipErrorNotSupported;
   hipLaunchKernelGGL((markov_chain_greedy_bf16<K32>), dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }

@@ -308,28 +308,6 @@ __global__ void fill_zero_kernel(u32x4_t* __restrict__ p, int64_t n16, unsigned 
   if (i < ntail) tail[i] = 0;
 }
 
-// Device copy with the streaming (non-temporal) cache policy that the
-// kernels above use for logits: each thread has four 16-byte vectors in
-// flight per pass, all loaded before any is stored.  A bandwidth reference
-// for the measurements, not a step of the head.
-__global__ __launch_bounds__(256) void copy_stream_kernel(const u32x4_t* __restrict__ src,
-                                                          u32x4_t* __restrict__ dst, int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * 1024;
-  for (int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x; base < n; base += stride) {
-    u32x4_t v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = base + 256 * u;
-      v[u] = i < n ? __builtin_nontemporal_load(src + i) : u32x4_t{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = base + 256 * u;
-      if (i < n) __builtin_nontemporal_store(v[u], dst + i);
-    }
-  }
-}
-
 // ---------------------------------------------------------------- launchers
 template <int MODE>
 static hipError_t launch_tile_mode(const KernelParams& p, int ks, hipStream_t s) {
@@ -395,16 +373,6 @@ hipError_t launch_reduce(const uint64_t* partials, int64_t nparts, int64_t B, in
                          int64_t* tokens, hipStream_t s) {
   hipLaunchKernelGGL(reduce_row_keys, dim3((unsigned)B), dim3(256), 0, s, partials, nparts, M, k,
                      tokens);
-  return hipGetLastError();
-}
-
-hipError_t launch_copy_stream(void* dst, const void* src, size_t bytes, hipStream_t s) {
-  const int64_t n = (int64_t)(bytes / 16);
-  if (n == 0) return hipSuccess;
-  int64_t blocks = (n + 1023) / 1024;
-  if (blocks > 8192) blocks = 8192;   // measured best: 4096 - 8192 workgroups of 256
-  hipLaunchKernelGGL(copy_stream_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const u32x4_t*)src,
-                     (u32x4_t*)dst, n);
   return hipGetLastError();
 }
 

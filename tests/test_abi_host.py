@@ -232,16 +232,27 @@ def test_backward_argument_errors(L):
     assert _bwd(L, gw1=ctypes.c_void_p(0x500000 + 16)) == 1    # over W1
 
 
-def test_stream_copy_argument_errors(L):
-    """The streaming copy (a bandwidth reference) takes 16-byte aligned,
-    non-overlapping buffers and whole 16-byte pieces; zero bytes is a no-op.
-    Every call here is rejected before any launch."""
+def test_bandwidth_probe_argument_errors():
+    """The bandwidth probes (a separate library, not the head's ABI) take
+    16-byte aligned, non-overlapping buffers and whole 16-byte pieces; zero
+    bytes is a no-op.  Every call here is rejected before any launch."""
+    from rank_markov_draft_amd import _lib
+    bw = _lib.load_bandwidth()
     a, b = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
-    bad = 1   # DSPARK_ERR_INVALID_ARGUMENT
-    assert L.dspark_markov_stream_copy(b, a, 0, None) == 0
-    assert L.dspark_markov_stream_copy(None, a, 4096, None) == bad
-    assert L.dspark_markov_stream_copy(b, None, 4096, None) == bad
-    assert L.dspark_markov_stream_copy(ctypes.c_void_p(0x200008), a, 4096, None) == bad
-    assert L.dspark_markov_stream_copy(b, ctypes.c_void_p(0x100004), 4096, None) == bad
-    assert L.dspark_markov_stream_copy(b, a, 4100, None) == bad
-    assert L.dspark_markov_stream_copy(ctypes.c_void_p(0x100800), a, 4096, None) == bad   # overlap
+    bad = 1
+    assert bw.dspark_bandwidth_copy(b, a, 0, None) == 0
+    assert bw.dspark_bandwidth_copy(None, a, 4096, None) == bad
+    assert bw.dspark_bandwidth_copy(b, None, 4096, None) == bad
+    assert bw.dspark_bandwidth_copy(ctypes.c_void_p(0x200008), a, 4096, None) == bad
+    assert bw.dspark_bandwidth_copy(b, ctypes.c_void_p(0x100004), 4096, None) == bad
+    assert bw.dspark_bandwidth_copy(b, a, 4100, None) == bad
+    assert bw.dspark_bandwidth_copy(ctypes.c_void_p(0x100800), a, 4096, None) == bad   # overlap
+    assert bw.dspark_bandwidth_read_mix(b, 0, a, 0, None) == 0
+    assert bw.dspark_bandwidth_read_mix(b, 4096, a, 2048, None) == bad                   # reads fewer than writes
+    assert bw.dspark_bandwidth_read_mix(b, 4096, a, 4096 * 5, None) == bad               # more than four passes
+    assert bw.dspark_bandwidth_read_mix(b, 4096, a, 4100, None) == bad
+    assert bw.dspark_bandwidth_read_mix(ctypes.c_void_p(0x100800), 4096, a, 8192, None) == bad
+
+
+def test_product_abi_has_no_benchmark_utility(L):
+    assert not hasattr(L, "dspark_markov_stream_copy")

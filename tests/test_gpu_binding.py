@@ -65,18 +65,30 @@ def test_unused_gate_tensors_are_not_checked(native):
     assert torch.equal(out, ref)
 
 
-def test_stream_copy_is_exact(native):
-    """The streaming copy that bench.py times as the HBM ceiling moves the
-    bytes exactly, including a partial last pass of its workgroups."""
+def test_bandwidth_probes_are_exact(native):
+    """The streaming copy and the read-mix pass that bench.py times as HBM
+    ceilings move the bytes exactly, including a partial last pass of their
+    workgroups, and write nothing past the end."""
     import ctypes
     from rank_markov_draft_amd import _lib
-    lib = _lib.load()
+    bw = _lib.load_bandwidth()
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     for n in (16, 4096 + 16, (1 << 20) + 48, 64 << 20):
-        src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+        src = torch.randint(0, 256, (2 * n,), dtype=torch.uint8, device="cuda")
         dst = torch.zeros(n + 64, dtype=torch.uint8, device="cuda")
-        assert lib.dspark_markov_stream_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()), n,
-                                             stream) == 0
+        assert bw.dspark_bandwidth_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()), n,
+                                        stream) == 0
         torch.cuda.synchronize()
-        assert torch.equal(dst[:n], src), n
+        assert torch.equal(dst[:n], src[:n]), n
         assert not dst[n:].any(), "bytes past the end were written"
+        for m in (n, n + 16 * (n // 32), 2 * n):          # 1, ~1.5 and 2 source bytes per byte written
+            dst.zero_()
+            assert bw.dspark_bandwidth_read_mix(ctypes.c_void_p(dst.data_ptr()), n, ctypes.c_void_p(src.data_ptr()),
+                                                m, stream) == 0
+            torch.cuda.synchronize()
+            s16 = src[:m].view(torch.int32).view(-1, 4).cpu()
+            want = s16[: n // 16].clone()
+            tail = s16[n // 16:]
+            want[: tail.shape[0]] ^= tail
+            assert torch.equal(dst[:n].view(torch.int32).view(-1, 4).cpu(), want), (n, m)
+            assert not dst[n:].any()
