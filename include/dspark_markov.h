@@ -147,6 +147,29 @@ dspark_status_t dspark_markov_sample_block(const void* base_logits, dspark_dtype
                                            int64_t* sampled_tokens, void* corrected_logits,
                                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* dspark_markov_sample_block for callers that cannot allocate: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and kernels, minus the workspace: the library
+ * uses a static scratch array of 4 MiB per GPU (4,194,304 bytes, held until
+ * the process ends) in place of the caller's workspace.  Sizes whose
+ * dspark_markov_workspace_bytes(B, M, V, r, 1) exceeds that are rejected
+ * with DSPARK_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (the
+ * message names both sizes); for instance B = 64, M = 5 at V = 129280 needs
+ * 0.7 MB and B = 256, M = 8 at V = 151936 needs 2.7 MB.  Nothing is
+ * allocated: the first call on a device zero-fills its scratch with a
+ * kernel on `stream`, and every call clears the scratch's error words
+ * first, so out-of-range ids are not counted and a failed persistent chain
+ * shows only as -1 tokens.  Every call on a GPU shares that GPU's scratch,
+ * which keeps the last call's contents: calls that overlap on one GPU (on
+ * different streams or host threads) race and must be ordered by the
+ * caller. */
+dspark_status_t dspark_markov_sample_block_static(const void* base_logits, dspark_dtype_t logits_dtype,
+                                                  const int64_t* first_prev_token_ids, const void* w1,
+                                                  const void* w2, dspark_dtype_t weight_dtype, int64_t B,
+                                                  int64_t M, int64_t V, int64_t r, double temperature,
+                                                  uint64_t seed, int64_t position_offset, int64_t batch_offset,
+                                                  int64_t* sampled_tokens, void* corrected_logits, void* stream);
+
 /* Gated head (GatedMarkovHead, on the third-party markov_head.py page and
  * the NeMo AutoModel "speculative/dspark/markov_head" page).  The bias of a
  * row is W2 . u with the latent row

@@ -34,6 +34,7 @@ EXPORTS = (
     "dspark_markov_workspace_init",
     "dspark_markov_apply_block",
     "dspark_markov_sample_block",
+    "dspark_markov_sample_block_static",
     "dspark_markov_gated_workspace_bytes",
     "dspark_markov_apply_block_gated",
     "dspark_markov_sample_block_gated",
@@ -81,6 +82,9 @@ def load():
     L.dspark_markov_sample_block.argtypes = [p, i32, p, p, p, i32, i64, i64, i64, i64,
                                              ctypes.c_double, u64, i64, i64, p, p, p, sz, p]
     L.dspark_markov_sample_block.restype = i32
+    L.dspark_markov_sample_block_static.argtypes = [p, i32, p, p, p, i32, i64, i64, i64, i64,
+                                                    ctypes.c_double, u64, i64, i64, p, p, p]
+    L.dspark_markov_sample_block_static.restype = i32
     L.dspark_markov_gated_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
     L.dspark_markov_gated_workspace_bytes.restype = sz
     L.dspark_markov_apply_block_gated.argtypes = [p, i32, p, p, i32, i64, p, p, p, p, i32,

@@ -260,14 +260,22 @@ dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_
   return DSPARK_OK;
 }
 
-dspark_status_t dspark_markov_sample_block(const void* base_logits, dspark_dtype_t logits_dtype,
-                                           const int64_t* first_prev_token_ids, const void* w1,
-                                           const void* w2, dspark_dtype_t weight_dtype,
-                                           int64_t B, int64_t M, int64_t V, int64_t r,
-                                           double temperature, uint64_t seed,
-                                           int64_t position_offset, int64_t batch_offset,
-                                           int64_t* sampled_tokens, void* corrected_logits,
-                                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace dspark {
+
+void set_last_error(const std::string& msg) { g_last_error = msg; }
+
+// Left-to-right sampling on a given workspace.  `clear_control` zero-fills
+// the workspace's control block (error words and test hook) on the stream
+// once the arguments have passed validation, before the first kernel: the
+// static-scratch variant starts every call from a clean record.
+dspark_status_t sample_block_impl(const void* base_logits, dspark_dtype_t logits_dtype,
+                                  const int64_t* first_prev_token_ids, const void* w1, const void* w2,
+                                  dspark_dtype_t weight_dtype, int64_t B, int64_t M, int64_t V, int64_t r,
+                                  double temperature, uint64_t seed, int64_t position_offset,
+                                  int64_t batch_offset, int64_t* sampled_tokens, void* corrected_logits,
+                                  void* workspace, size_t workspace_bytes, void* stream, bool clear_control) {
   int64_t elems = 0;
   dspark_status_t st = check_common(logits_dtype, weight_dtype, B, M, V, r, &elems);
   if (st != DSPARK_OK) return st;
@@ -291,6 +299,10 @@ dspark_status_t dspark_markov_sample_block(const void* base_logits, dspark_dtype
   if (corrected_logits && overlaps(corrected_logits, lbytes, sampled_tokens, tbytes))
     return DSPARK_ERR_INVALID_ARGUMENT;
 
+  if (clear_control) {
+    const hipError_t e = dspark::launch_fill_zero(workspace, kControlBytes, (hipStream_t)stream);
+    if (e != hipSuccess) return device_failure(e, "scratch control clear");
+  }
   const bool greedy = temperature < 1e-5;
   dspark::KernelParams p{};
   p.base = base_logits;
@@ -362,6 +374,23 @@ dspark_status_t dspark_markov_sample_block(const void* base_logits, dspark_dtype
     if (e != hipSuccess) return device_failure(e, "sample reduce launch");
   }
   return DSPARK_OK;
+}
+
+}  // namespace dspark
+
+extern "C" {
+
+dspark_status_t dspark_markov_sample_block(const void* base_logits, dspark_dtype_t logits_dtype,
+                                           const int64_t* first_prev_token_ids, const void* w1,
+                                           const void* w2, dspark_dtype_t weight_dtype,
+                                           int64_t B, int64_t M, int64_t V, int64_t r,
+                                           double temperature, uint64_t seed,
+                                           int64_t position_offset, int64_t batch_offset,
+                                           int64_t* sampled_tokens, void* corrected_logits,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+  return dspark::sample_block_impl(base_logits, logits_dtype, first_prev_token_ids, w1, w2, weight_dtype, B, M,
+                                   V, r, temperature, seed, position_offset, batch_offset, sampled_tokens,
+                                   corrected_logits, workspace, workspace_bytes, stream, false);
 }
 
 size_t dspark_markov_gated_workspace_bytes(int64_t B, int64_t M, int64_t V, int64_t r, int64_t d,

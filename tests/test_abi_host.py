@@ -256,3 +256,14 @@ def test_bandwidth_probe_argument_errors():
 
 def test_product_abi_has_no_benchmark_utility(L):
     assert not hasattr(L, "dspark_markov_stream_copy")
+
+
+def test_static_scratch_entry_point_rejects_oversize_on_the_host(L):
+    """dspark_markov_sample_block_static refuses sizes whose workspace exceeds
+    its 4 MiB static scratch before touching the device."""
+    f = ctypes.c_void_p(0x1000)
+    st = L.dspark_markov_sample_block_static(f, 1, f, f, f, 1, 4096, 5, 151936, 256, 0.0, 0, 0, 0, f, None, None)
+    assert st == 3
+    assert b"static scratch" in L.dspark_markov_last_error()
+    # no work at all is a successful no-op, as for the workspace entry point
+    assert L.dspark_markov_sample_block_static(f, 1, f, f, f, 1, 0, 5, 151936, 256, 0.0, 0, 0, 0, f, None, None) == 0
