@@ -323,7 +323,10 @@ dspark_status_t sample_block_impl(const void* base_logits, dspark_dtype_t logits
   p.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
   p.seed_hi = (uint32_t)(seed >> 32);
   const bool tile = tile_path(logits_dtype, weight_dtype, V, r, base_logits, corrected_logits, w1, w2);
-  if (!tile && r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
+  // fp32 logits with bf16 weights sample through the step kernel too
+  const bool f32_tile = logits_dtype == DSPARK_F32 &&
+                        tile_path(DSPARK_BF16, weight_dtype, V, r, base_logits, corrected_logits, w1, w2);
+  if (!tile && !f32_tile && r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
   p.nparts = tile ? vocab_slices(V) : (V + 255) / 256;
   hipStream_t s = (hipStream_t)stream;
   Control* ctl = (Control*)workspace;
@@ -356,17 +359,22 @@ dspark_status_t sample_block_impl(const void* base_logits, dspark_dtype_t logits
   for (int64_t k = 0; k < M; ++k) {
     p.k = k;
     p.k_abs = (uint32_t)(position_offset + k);
-    hipError_t e;
-    if (tile) {
-      // the persistent step kernel where the shape fits, else the tile kernel
+    hipError_t e = hipErrorNotSupported;
+    if (tile || f32_tile) {
+      // the persistent step kernel where the shape fits, else the tile
+      // kernel (bf16 logits) or the generic one
       p.nparts = dspark::sample_step_parts(V);
-      e = dspark::launch_sample_step(p, cus, s);
-      if (e == hipErrorNotSupported) {
+      e = dspark::launch_sample_step(p, f32_tile, cus, s);
+      if (e == hipErrorNotSupported && tile) {
         (void)hipGetLastError();
         p.nparts = vocab_slices(V);
         e = dspark::launch_tile(p, s);
       }
-    } else {
+    }
+    if (e == hipErrorNotSupported) {
+      (void)hipGetLastError();
+      if (r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
+      p.nparts = (V + 255) / 256;
       e = dspark::launch_generic(p, logits_dtype == DSPARK_BF16, weight_dtype == DSPARK_BF16, s);
     }
     if (e != hipSuccess) return device_failure(e, "sample step launch");
@@ -562,9 +570,11 @@ dspark_status_t dspark_markov_sample_block_gated(
   p.seed_hi = (uint32_t)(seed >> 32);
   // each step's latent rows: straight into latent_out[:, k, :], else a scratch [B, r]
   const int64_t lld = latent_out ? M * r : r;
-  const bool tile = tile_path(logits_dtype, weight_dtype, V, r, base_logits, corrected_logits, w1, w2) &&
-                    (latent_out == nullptr || aligned16(latent_out));
-  if (!tile && r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
+  const bool lat_ok = latent_out == nullptr || aligned16(latent_out);
+  const bool tile = tile_path(logits_dtype, weight_dtype, V, r, base_logits, corrected_logits, w1, w2) && lat_ok;
+  const bool f32_tile = logits_dtype == DSPARK_F32 && lat_ok &&
+                        tile_path(DSPARK_BF16, weight_dtype, V, r, base_logits, corrected_logits, w1, w2);
+  if (!tile && !f32_tile && r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
   const int cus = device_cus();
   for (int64_t k = 0; k < M; ++k) {
     void* const latent = latent_out ? (void*)((char*)latent_out + (size_t)(k * r) * dtype_bytes(weight_dtype))
@@ -577,12 +587,13 @@ dspark_status_t dspark_markov_sample_block_gated(
     p.latent = latent;
     p.latent_ld = lld;
     e = hipErrorNotSupported;
-    if (tile) {
+    if (tile || f32_tile) {
       p.nparts = dspark::sample_step_parts(V);
-      e = dspark::launch_sample_step(p, cus, s);
+      e = dspark::launch_sample_step(p, f32_tile, cus, s);
       if (e == hipErrorNotSupported) (void)hipGetLastError();
     }
     if (e == hipErrorNotSupported) {
+      if (r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
       p.nparts = (V + 255) / 256;
       e = dspark::launch_generic(p, logits_dtype == DSPARK_BF16, weight_dtype == DSPARK_BF16, s);
     }

@@ -22,10 +22,10 @@
 //     corrected values back in place and folds each row's best column into
 //     a per-row LDS key.  One barrier ends the window;
 //   * everything else is issued at the start of a window and overlaps the
-//     matrix work of the other waves: the corrected rows of unit w-1 go to
-//     HBM and the base logits that group needs next are loaded (into
-//     registers, written to the freed LDS rows a window later, four windows
-//     ahead of use); wave 0 publishes the row keys of unit w-1 (a 64-bit
+//     matrix work of the other waves: waves 2..15 send the corrected rows of
+//     unit w-1 to HBM and load the base logits that group needs next
+//     straight into the freed LDS rows, five windows ahead of use, so each
+//     load has five windows to arrive; wave 0 publishes the row keys of unit w-1 (a 64-bit
 //     atomic max per row into one of eight key slots) and counts the
 //     workgroup in for unit w-2, whose atomics it issued a window earlier;
 //     wave 1 checks the arrival counts it polled a window ago for unit w+2's
@@ -162,7 +162,6 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   const bool has = slice < s_end;
 
   const uint32_t bytes = (uint32_t)(B * M * V * 2);
-  const __amdgpu_buffer_rsrc_t rs_base = buffer_rsrc(p.base, bytes);
   const __amdgpu_buffer_rsrc_t rs_out = buffer_rsrc(p.out, p.out != nullptr ? bytes : 0u);
   const BufferWords bw_w1 = buffer_words(p.w1, (uint32_t)(V * r * 2));
   const BufferWords bw_keys = buffer_words(p.keys, (uint32_t)(M * kGroups * kMaxRows * kKeyPad * 8));
@@ -183,27 +182,34 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     }
   }
 
-  // ---- row staging: wave w moves row w of every group, one 1 KB row
-  // segment per instruction, lane l the 8 columns vbeg + 8 l .. +7.  Offsets
-  // of masked-off lanes, rows or steps point past the buffer (see
-  // buffer_rsrc), so every instruction is issued unconditionally.
-  const int srow = wave;
+  // ---- row staging.  Waves 2..15 move the bulk rows, one 1 KB row segment
+  // per instruction, lane l the 8 columns vbeg + 8 l .. +7: wave w moves row
+  // w - 2 of every group, and waves 2 and 3 also rows 14 and 15.  Waves 0 and
+  // 1 run the exchange, so their memory counters hold exchange operations
+  // only.  Base rows go straight into LDS (buffer loads to LDS) as soon as a
+  // group's row is flushed, five windows before the group's next unit needs
+  // them; a wave waits for them only at the end of the window before that
+  // unit.  Offsets of masked-off lanes, rows or steps point past the buffer
+  // (see buffer_rsrc), so every instruction is issued unconditionally.
+  const int nbulk = wave >= 2 ? (wave < 4 ? 2 : 1) : 0;
+  const int brow0 = wave - 2, brow1 = wave + 12;
   const bool col_ok = vbeg + 8u * (uint32_t)lane < vend;
   const uint32_t lane_off = 2u * (vbeg + 8u * (uint32_t)lane);
-  auto row_offset = [&](int gg, int kd) __attribute__((always_inline)) -> uint32_t {
-    const int b = gg * rpg + srow;
-    const bool ok = srow < rpg && b < B && kd < M && col_ok;
+  auto row_offset = [&](int gg, int kd, int row) __attribute__((always_inline)) -> uint32_t {
+    const int b = gg * rpg + row;
+    const bool ok = row < rpg && b < B && kd < M && col_ok;
     return ok ? (uint32_t)((b * M + kd) * V) * 2u + lane_off : kBufferOob;
   };
-  // The bulk rows travel through registers (plain buffer loads issue far
-  // faster than loads to LDS): a base row is loaded into pre in one window
-  // and written to its LDS row at the start of the next.
-  u32x4_t pre = u32x4_t{0u, 0u, 0u, 0u};
-  auto load_row = [&](int gg, int kd) __attribute__((always_inline)) {
-    pre = buffer_load16(rs_base, row_offset(gg, kd));
+  const BufferWords bw_base = buffer_words(p.base, bytes);
+  auto load_row_lds = [&](int gg, int kd, int row) __attribute__((always_inline)) {
+    load_lds16(bw_base, row_offset(gg, kd, row), lds_address(&lds_x[gg][row * kPitch]));
   };
-  auto store_row_lds = [&](int gg) __attribute__((always_inline)) {
-    *(u32x4_t*)&lds_x[gg][srow * kPitch + lane * 16] = pre;
+  // Corrected row of unit (gg, kd) from LDS to HBM, then the group's next
+  // base row into the same LDS row (the store needs the LDS data first).
+  auto flush_row = [&](int gg, int kd, int row) __attribute__((always_inline)) {
+    const u32x4_t v = *(const u32x4_t*)&lds_x[gg][row * kPitch + lane * 16];
+    buffer_store16(rs_out, row_offset(gg, kd, row), v);
+    load_row_lds(gg, kd + 1, row);
   };
 
   // ---- gather (wave 1): W1 rows of tokens x (lane l: the token of row
@@ -247,8 +253,8 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
 
   // ---- prologue: stage step 0 of every group, gather the first tokens.
   for (int gg = 0; gg < NR; ++gg) {
-    load_row(gg, 0);
-    store_row_lds(gg);
+    if (nbulk >= 1) load_row_lds(gg, 0, brow0);
+    if (nbulk >= 2) load_row_lds(gg, 0, brow1);
   }
   if (wave == 1 && !poisoned) {
     for (int gg = 0; gg < NR; ++gg) {
@@ -283,24 +289,19 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     const int gc = w % kRowGroups;  // slot of unit w (its group when real)
     int after_gather = 0;           // wave 1
 
-    // Bulk rows first: the base row loaded a window ago (unit w+4) into its
-    // LDS row, the corrected row of unit w-1 to HBM, then that group's next
-    // base row (unit w+5) into registers.  It drains during the matrix work.
-    if (w >= 2 && real(w - 2)) store_row_lds((w - 2) % kRowGroups);
-    const bool flush = w >= 1 && real(w - 1);
-    if (flush) {
+    // Bulk rows first: the corrected rows of unit w-1 to HBM, and that
+    // group's next base rows (unit w+5) into the freed LDS rows.  They drain
+    // during the matrix work and the windows after it.
+    if (w >= 1 && real(w - 1)) {
       const int gp = (w - 1) % kRowGroups, kp = (w - 1) / kRowGroups;
-      const u32x4_t v = *(const u32x4_t*)&lds_x[gp][srow * kPitch + lane * 16];
-      buffer_store16(rs_out, row_offset(gp, kp), v);
-      load_row(gp, kp + 1);
+      if (nbulk >= 1) flush_row(gp, kp, brow0);
+      if (nbulk >= 2) flush_row(gp, kp, brow1);
     }
 
     if (wave == 0) {
       // count this workgroup in for unit w-2 (its key atomics were issued a
-      // window ago; the two bulk operations just issued may stay in flight),
-      // then publish the row keys of unit w-1
-      if (flush) wait_vmcnt<2>();
-      else wait_vmcnt<0>();
+      // window ago), then publish the row keys of unit w-1
+      wait_vmcnt<0>();
       if (w >= 2 && real(w - 2) && lane == 0)
         __hip_atomic_fetch_add(arrival_counter(sync, (w - 2) % kRowGroups, xg), 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
@@ -326,8 +327,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
       const bool do2 = ok && u2 < U && u2 >= kRowGroups && real(u2);
       const bool do1 = u1 < U && u1 >= kRowGroups && real(u1);
       const bool do3 = u3 < U && u3 >= kRowGroups && real(u3);
-      if (flush) wait_vmcnt<2>();
-      else wait_vmcnt<0>();
+      wait_vmcnt<0>();
       // the gather first: its round trip has the rest of the window
       if (do1) gather(u1 % kRowGroups, merge(u1 & 1, u1 % kRowGroups, u1 / kRowGroups - 1));
       if (do2) {
@@ -409,6 +409,22 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
         if (vbeg + (uint32_t)colw < vend) atomicMax(&lds_key[gc][n16], key);
       }
     }
+    // bulk waves: the base rows of unit w+1 (loaded at window w-4, when unit
+    // w-5 was flushed) are in LDS before the barrier.  Each flush window
+    // since then issued a store and a load per row.
+    if (nbulk > 0 && w + 1 < U && w + 1 >= kRowGroups && real(w + 1)) {
+      int later = 0;
+      for (int x = w - 3; x <= w; ++x) later += (x >= 1 && real(x - 1)) ? 1 : 0;
+      switch (later * 2 * nbulk) {
+        case 0: wait_vmcnt<0>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case 6: wait_vmcnt<6>(); break;
+        case 8: wait_vmcnt<8>(); break;
+        case 12: wait_vmcnt<12>(); break;
+        default: wait_vmcnt<16>(); break;
+      }
+    }
     // wave 1: the gather of unit w+1 (issued this window, before the key
     // slots and the poll) is in LDS before the barrier
     if (wave == 1) {
@@ -429,8 +445,10 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   if (lds_flag) {
     if (real(U - 1)) {
       const int gp = (U - 1) % kRowGroups, kp = (U - 1) / kRowGroups;
-      const u32x4_t v = *(const u32x4_t*)&lds_x[gp][srow * kPitch + lane * 16];
-      buffer_store16(rs_out, row_offset(gp, kp), v);
+      if (nbulk >= 1)
+        buffer_store16(rs_out, row_offset(gp, kp, brow0), *(const u32x4_t*)&lds_x[gp][brow0 * kPitch + lane * 16]);
+      if (nbulk >= 2)
+        buffer_store16(rs_out, row_offset(gp, kp, brow1), *(const u32x4_t*)&lds_x[gp][brow1 * kPitch + lane * 16]);
     }
     if (wave == 0) {
       wait_vmcnt<0>();

@@ -121,12 +121,13 @@ size_t apply_sink_bytes();
 // most 2^31 bytes.
 hipError_t launch_apply_grouped(const KernelParams& p, bool logits_f32, hipStream_t s);
 constexpr int64_t kGroupedApplyMaxRows = 4096;
-// One bf16 sampling step (greedy or temperature) of the p.rows = B rows at
+// One sampling step with bf16 weights and bf16 or fp32 (logits_f32) logits
+// (greedy or temperature) of the p.rows = B rows at
 // position p.k: argmax keys per (row, 512-column block) into p.partials with
 // p.nparts = sample_step_parts(V); one workgroup per CU.  Needs r <= 256,
-// B <= 4096 and B * M * V * 2, V * r * 2 <= 2^31 (hipErrorNotSupported).
+// B <= 4096 and the logits and V * r * 2 within 2^31 bytes (hipErrorNotSupported).
 int64_t sample_step_parts(int64_t V);
-hipError_t launch_sample_step(const KernelParams& p, int num_cus, hipStream_t s);
+hipError_t launch_sample_step(const KernelParams& p, bool logits_f32, int num_cus, hipStream_t s);
 hipError_t launch_generic(const KernelParams& p, bool logits_bf16, bool weights_bf16, hipStream_t s);
 hipError_t launch_reduce(const uint64_t* partials, int64_t nparts, int64_t B, int64_t M, int64_t k,
                          int64_t* tokens, hipStream_t s);

@@ -11,7 +11,8 @@
 //
 // Layout of the work:
 //   * the vocabulary is cut into blocks of 512 columns (16 waves x 32) and
-//     the rows into chunks of 32; a unit is one (block, chunk).  The grid
+//     the rows into chunks of 32 (16 for fp32 logits, whose 8 columns per
+//     lane take two 16-byte vectors); a unit is one (block, chunk).  The grid
 //     has one workgroup per CU and workgroup g takes the units
 //     [g U / G, (g + 1) U / G) in block-major order, so every CU gets the
 //     same number of units (a grid of whole blocks would leave most CUs idle
@@ -41,20 +42,24 @@ namespace {
 constexpr int kStepWaves = 16;
 constexpr int kStepThreads = kStepWaves * 64;
 constexpr int kStepCols = 32 * kStepWaves;  // columns of a block
-constexpr int kStepRows = 32;               // rows of a chunk (two MFMA N tiles)
 constexpr int kStepMaxB = 4096;             // rows of a call (tokens staged in LDS)
 }  // namespace
 
 // RD: units of base logits in flight (register ring depth; 1 where the
-// selection's registers leave no room for two)
-template <int K32, int MODE, int RD>
+// selection's registers leave no room for two).  LF32: fp32 logits (the
+// bias is still the bf16 Linear output, widened exactly and added in fp32).
+template <int K32, int MODE, int RD, bool LF32>
 __global__ __launch_bounds__(kStepThreads) void markov_step_bf16(KernelParams p) {
-  constexpr int VPR = kStepCols / 8;                      // 16-byte vectors of a row segment (64)
-  constexpr int VPT = kStepRows * VPR / kStepThreads;     // vectors per thread and unit (2)
+  constexpr int kStepRows = LF32 ? 16 : 32;               // rows of a chunk (MFMA N tiles of 16)
+  constexpr int TILES = kStepRows / 16;
+  constexpr int NV = LF32 ? 2 : 1;                        // 16-byte vectors per lane's 8 columns
+  constexpr uint32_t LB = LF32 ? 4u : 2u;                 // bytes per logit
+  constexpr int VPR = kStepCols / 8;                      // lanes of a row segment (64)
+  constexpr int VPT = kStepRows * VPR / kStepThreads;     // row segments per thread and unit (2; 1 for fp32)
   constexpr int BSTRIDE = 2 * kStepCols + 16;             // LDS bytes per bias row
-  constexpr int EUNIT = 2 * K32 * 1024;                   // gathered W1 rows of a unit (two tiles)
+  constexpr int EUNIT = TILES * K32 * 1024;               // gathered W1 rows of a unit
   constexpr int GPT = EUNIT / 16 / kStepThreads > 0 ? EUNIT / 16 / kStepThreads : 1;  // gathered vectors per thread
-  static_assert(VPT == 2 && VPR == 64, "one wave per row segment");
+  static_assert(VPT * NV == 2 && VPR == 64, "one wave per row segment, two vectors per thread");
   static_assert(GPT * kStepThreads * 16 >= EUNIT, "gather mapping");
 
   // Gathered rows of units u (slot u % 2): tile t, block kk holds at lane l's
@@ -79,7 +84,7 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_bf16(KernelParams p)
   const int u0 = (int)(((int64_t)blockIdx.x * units) / gridDim.x);
   const int u1 = (int)(((int64_t)(blockIdx.x + 1) * units) / gridDim.x);
 
-  const uint32_t lbytes = (uint32_t)B * M * V * 2u;  // <= 2^31 (host)
+  const uint32_t lbytes = (uint32_t)B * M * V * LB;  // <= 2^31 (host)
   const __amdgpu_buffer_rsrc_t rs_base = buffer_rsrc(p.base, lbytes);
   const __amdgpu_buffer_rsrc_t rs_out = buffer_rsrc(p.out, p.out != nullptr ? lbytes : 0u);
   const __amdgpu_buffer_rsrc_t rs_part = buffer_rsrc(p.partials, (uint32_t)B * (uint32_t)p.nparts * 8u);
@@ -151,9 +156,9 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_bf16(KernelParams p)
   };
 
   // ---- bias of tile t of unit u (its gathered rows in slot u % 2) into
-  // bias slot u % 2
+  // bias slot u % 2 (tiles past the chunk's TILES do nothing)
   auto multiply = [&](int u, int t) __attribute__((always_inline)) {
-    if (u >= u1) return;
+    if (u >= u1 || t >= TILES) return;
     const int slot = u & 1;
     const bool has = (uint32_t)ublk(u) * kStepCols + wave * 32u < V;
     if (!has) return;
@@ -173,39 +178,61 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_bf16(KernelParams p)
     *(u32x4_t*)&lds_b[slot][(16 * t + n16) * BSTRIDE + (wave * 32 + 8 * g4) * 2] = w;
   };
 
-  // ---- streamed vector q of a unit: row 16 q + wave of the chunk (wave w
-  // owns rows w and w + 16), the lane's 8 columns 8 lane .. +7 of the block
-  auto base_off = [&](int u, int q) __attribute__((always_inline)) -> uint32_t {
+  // ---- streamed row segment q of a unit: row 16 q + wave of the chunk
+  // (wave w owns rows w and w + 16), the lane's 8 columns 8 lane .. +7 of
+  // the block, 16-byte vector h of them
+  auto base_off = [&](int u, int q, int h) __attribute__((always_inline)) -> uint32_t {
     const uint32_t row = (uint32_t)(uchk(u) * kStepRows + 16 * q + wave);
     const uint32_t col = (uint32_t)ublk(u) * kStepCols + 8u * lane;
-    return (u < u1 && row < (uint32_t)B && col < V) ? ((row * M + kstep) * V + col) * 2u : kBufferOob;
+    return (u < u1 && row < (uint32_t)B && col < V) ? ((row * M + kstep) * V + col) * LB + 16u * (uint32_t)h
+                                                      : kBufferOob;
   };
 
   // ---- selection of vector q of unit u from its base vectors pre[]
   // (refilled with unit u + RD after their last use): corrected values to
   // the output, the row's best key to the partials
-  auto select_unit = [&](int u, u32x4_t pre[VPT], int q) __attribute__((always_inline)) {
+  auto select_unit = [&](int u, u32x4_t pre[VPT][NV], int q) __attribute__((always_inline)) {
     const int slot = u & 1;
     const uint32_t colw = (uint32_t)ublk(u) * kStepCols + 8u * lane;
     {
       const int rr = 16 * q + wave;  // row within the chunk
       const uint32_t row = (uint32_t)(uchk(u) * kStepRows + rr);
       const bool ok = u < u1 && row < (uint32_t)B && colw < V;
-      const u32x4_t bb = pre[q];
       const u32x4_t bs = *(const u32x4_t*)&lds_b[slot][rr * BSTRIDE + lane * 16];
-      u32x4_t o;
-      o.x = pack_bf16x2(bf16_lo(bb.x) + bf16_lo(bs.x), bf16_hi(bb.x) + bf16_hi(bs.x));
-      o.y = pack_bf16x2(bf16_lo(bb.y) + bf16_lo(bs.y), bf16_hi(bb.y) + bf16_hi(bs.y));
-      o.z = pack_bf16x2(bf16_lo(bb.z) + bf16_lo(bs.z), bf16_hi(bb.z) + bf16_hi(bs.z));
-      o.w = pack_bf16x2(bf16_lo(bb.w) + bf16_lo(bs.w), bf16_hi(bb.w) + bf16_hi(bs.w));
-      buffer_store16(rs_out, ok ? ((row * M + kstep) * V + colw) * 2u : kBufferOob, o);
+      const uint32_t out_off = ok ? ((row * M + kstep) * V + colw) * LB : kBufferOob;
+      // corrected values of the lane's 8 columns: bf16 logits round the fp32
+      // sum to bf16; fp32 logits keep it (the bias is exact in fp32)
+      float cv[8];
+      if constexpr (LF32) {
+        const u32x4_t b0 = pre[q][0], b1 = pre[q][1];
+        const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        const uint32_t sw[4] = {bs.x, bs.y, bs.z, bs.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          cv[i] = __uint_as_float(bw[i]) + ((i & 1) ? bf16_hi(sw[i >> 1]) : bf16_lo(sw[i >> 1]));
+        buffer_store16(rs_out, out_off, u32x4_t{__float_as_uint(cv[0]), __float_as_uint(cv[1]),
+                                                __float_as_uint(cv[2]), __float_as_uint(cv[3])});
+        buffer_store16(rs_out, ok ? out_off + 16u : kBufferOob,
+                       u32x4_t{__float_as_uint(cv[4]), __float_as_uint(cv[5]), __float_as_uint(cv[6]),
+                               __float_as_uint(cv[7])});
+      } else {
+        const u32x4_t bb = pre[q][0];
+        u32x4_t o;
+        o.x = pack_bf16x2(bf16_lo(bb.x) + bf16_lo(bs.x), bf16_hi(bb.x) + bf16_hi(bs.x));
+        o.y = pack_bf16x2(bf16_lo(bb.y) + bf16_lo(bs.y), bf16_hi(bb.y) + bf16_hi(bs.y));
+        o.z = pack_bf16x2(bf16_lo(bb.z) + bf16_lo(bs.z), bf16_hi(bb.z) + bf16_hi(bs.z));
+        o.w = pack_bf16x2(bf16_lo(bb.w) + bf16_lo(bs.w), bf16_hi(bb.w) + bf16_hi(bs.w));
+        buffer_store16(rs_out, out_off, o);
+        const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cv[i] = (i & 1) ? bf16_hi(ow[i >> 1]) : bf16_lo(ow[i >> 1]);
+      }
       // the thread's best score of its 8 columns (first column on ties)
-      const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
       float best = 0.0f, sumc = 0.0f;
       uint32_t bi = 0;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        float sc[4] = {bf16_lo(ow[2 * j]), bf16_hi(ow[2 * j]), bf16_lo(ow[2 * j + 1]), bf16_hi(ow[2 * j + 1])};
+        float sc[4] = {cv[4 * j], cv[4 * j + 1], cv[4 * j + 2], cv[4 * j + 3]};
         sumc += (sc[0] + sc[1]) + (sc[2] + sc[3]);
         if constexpr (MODE == MODE_TEMPERATURE) {
           // columns colw + 4 j .. + 3 are the words of one Philox block
@@ -230,10 +257,8 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_bf16(KernelParams p)
         // Without one (+inf met -inf in the sum) the scan above stands.
         uint32_t first = 8;
 #pragma unroll
-        for (int i = 7; i >= 0; --i) {
-          const uint32_t hb = (i & 1) ? (ow[i >> 1] >> 16) : (ow[i >> 1] & 0xFFFFu);
-          if ((hb & 0x7FFFu) > 0x7F80u) first = (uint32_t)i;
-        }
+        for (int i = 7; i >= 0; --i)
+          if (cv[i] != cv[i]) first = (uint32_t)i;
         if (first < 8) key = (0xFFFFFFFFull << 32) | (uint64_t)(0xFFFFFFFFu - (colw + first));
       }
       key = ok ? key : 0ull;
@@ -245,7 +270,8 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_bf16(KernelParams p)
                                                         : kBufferOob,
           0, 0);
       // refilled after its last use, so the new value can take its registers
-      pre[q] = buffer_load16(rs_base, base_off(u + RD, q));
+#pragma unroll
+      for (int h = 0; h < NV; ++h) pre[q][h] = buffer_load16(rs_base, base_off(u + RD, q, h));
     }
   };
 
@@ -253,11 +279,13 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_bf16(KernelParams p)
   // RD - 1 in flight while the predecessors go to LDS and the rows of units
   // u0 and u0 + 1 are gathered; then the bias of unit u0
   load_w2(ublk(u0));
-  u32x4_t ring[RD][VPT];
+  u32x4_t ring[RD][VPT][NV];
 #pragma unroll
   for (int d = 0; d < RD; ++d)
 #pragma unroll
-    for (int q = 0; q < VPT; ++q) ring[d][q] = buffer_load16(rs_base, base_off(u0 + d, q));
+    for (int q = 0; q < VPT; ++q)
+#pragma unroll
+      for (int h = 0; h < NV; ++h) ring[d][q][h] = buffer_load16(rs_base, base_off(u0 + d, q, h));
   {
     uint32_t bad = 0;  // bad ids, counted at step 0
 #pragma unroll
@@ -285,14 +313,14 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_bf16(KernelParams p)
   // ---- unit u: W2 of unit u + 1's block if new (in flight during the
   // selection), the rows of unit u + 2, the selection of unit u, the bias
   // of unit u + 1, then the rows of unit u + 2 into unit u's slot
-  auto step = [&](int u, u32x4_t pre[VPT]) __attribute__((always_inline)) {
+  auto step = [&](int u, u32x4_t pre[VPT][NV]) __attribute__((always_inline)) {
     if (u + 1 < u1 && ublk(u + 1) != ublk(u)) load_w2(ublk(u + 1));
     gather(u + 2, gv);
-    // each bias tile of unit u + 1 follows one selected vector of unit u, so
-    // the matrix instructions run behind the wave's own vector work
+    // each bias tile of unit u + 1 follows one selected row segment of unit
+    // u, so the matrix instructions run behind the wave's own vector work
     select_unit(u, pre, 0);
     multiply(u + 1, 0);
-    select_unit(u, pre, 1);
+    if constexpr (VPT > 1) select_unit(u, pre, 1);
     multiply(u + 1, 1);
     gather_to_lds(u & 1, gv);
     lds_barrier();
@@ -306,35 +334,43 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_bf16(KernelParams p)
 }
 
 namespace {
-template <int K32, int MODE>
+template <int K32, int MODE, bool LF32>
 hipError_t launch_step_k(const KernelParams& p, int grid, hipStream_t s) {
   constexpr int RD = (MODE == MODE_TEMPERATURE && K32 >= 8) ? 1 : 2;
-  hipLaunchKernelGGL((markov_step_bf16<K32, MODE, RD>), dim3(grid), dim3(kStepThreads), 0, s, p);
+  hipLaunchKernelGGL((markov_step_bf16<K32, MODE, RD, LF32>), dim3(grid), dim3(kStepThreads), 0, s, p);
   return hipGetLastError();
+}
+
+template <bool LF32>
+hipError_t launch_step_l(const KernelParams& p, int grid, hipStream_t s) {
+  const bool t = p.mode == MODE_TEMPERATURE;
+  switch (tile_ks_for_rank(p.r)) {  // rank blocks of 16 -> blocks of 32 (zero-padded)
+    case 1:
+    case 2: return t ? launch_step_k<1, MODE_TEMPERATURE, LF32>(p, grid, s) : launch_step_k<1, MODE_GREEDY, LF32>(p, grid, s);
+    case 4: return t ? launch_step_k<2, MODE_TEMPERATURE, LF32>(p, grid, s) : launch_step_k<2, MODE_GREEDY, LF32>(p, grid, s);
+    case 8: return t ? launch_step_k<4, MODE_TEMPERATURE, LF32>(p, grid, s) : launch_step_k<4, MODE_GREEDY, LF32>(p, grid, s);
+    case 16: return t ? launch_step_k<8, MODE_TEMPERATURE, LF32>(p, grid, s) : launch_step_k<8, MODE_GREEDY, LF32>(p, grid, s);
+    default: return hipErrorNotSupported;
+  }
 }
 }  // namespace
 
 int64_t sample_step_parts(int64_t V) { return (V + kStepCols - 1) / kStepCols; }
 
-// One bf16 sampling step; hipErrorNotSupported when the shape does not fit
-// (rank above 256, more than 4096 rows, byte offsets beyond 2^31).
-hipError_t launch_sample_step(const KernelParams& p, int num_cus, hipStream_t s) {
+// One sampling step with bf16 weights and bf16 (logits_f32 false) or fp32
+// logits; hipErrorNotSupported when the shape does not fit (rank above 256,
+// more than 4096 rows, byte offsets beyond 2^31).
+hipError_t launch_sample_step(const KernelParams& p, bool logits_f32, int num_cus, hipStream_t s) {
   if (p.rows < 1 || p.rows > kStepMaxB || num_cus < 1 || p.nparts != sample_step_parts(p.V))
     return hipErrorNotSupported;
-  if (p.rows * p.M * p.V * 2 > ((int64_t)1 << 31) || p.V * p.r * 2 > ((int64_t)1 << 31)) return hipErrorNotSupported;
+  const int64_t lb = logits_f32 ? 4 : 2;
+  if (p.rows * p.M * p.V * lb > ((int64_t)1 << 31) || p.V * p.r * 2 > ((int64_t)1 << 31)) return hipErrorNotSupported;
   if (p.latent != nullptr && (p.latent_ld < p.r || p.rows * p.latent_ld * 2 > ((int64_t)1 << 31)))
     return hipErrorNotSupported;
-  const int64_t units = ((p.rows + kStepRows - 1) / kStepRows) * sample_step_parts(p.V);
+  const int64_t rows_per_chunk = logits_f32 ? 16 : 32;
+  const int64_t units = ((p.rows + rows_per_chunk - 1) / rows_per_chunk) * sample_step_parts(p.V);
   const int grid = (int)(units < num_cus ? units : num_cus);
-  const bool t = p.mode == MODE_TEMPERATURE;
-  switch (tile_ks_for_rank(p.r)) {  // rank blocks of 16 -> blocks of 32 (zero-padded)
-    case 1:
-    case 2: return t ? launch_step_k<1, MODE_TEMPERATURE>(p, grid, s) : launch_step_k<1, MODE_GREEDY>(p, grid, s);
-    case 4: return t ? launch_step_k<2, MODE_TEMPERATURE>(p, grid, s) : launch_step_k<2, MODE_GREEDY>(p, grid, s);
-    case 8: return t ? launch_step_k<4, MODE_TEMPERATURE>(p, grid, s) : launch_step_k<4, MODE_GREEDY>(p, grid, s);
-    case 16: return t ? launch_step_k<8, MODE_TEMPERATURE>(p, grid, s) : launch_step_k<8, MODE_GREEDY>(p, grid, s);
-    default: return hipErrorNotSupported;
-  }
+  return logits_f32 ? launch_step_l<true>(p, grid, s) : launch_step_l<false>(p, grid, s);
 }
 
 }  // namespace dspark

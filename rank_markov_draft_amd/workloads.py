@@ -83,6 +83,15 @@ WORKLOADS = {
     "teacher_forced_320_f32logits": Workload("teacher_forced_320_f32logits", B=64, M=5, V=129280,
                                              r=256, dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=2,
                                              mode="apply", logits_dtype=F32),
+    # The greedy and temperature drafts on fp32 base logits (the fp32 LM head
+    # output of DeepSeek-V4.1's compute_logits) with bf16 weights.
+    "greedy_draft_64x5_f32logits": Workload("greedy_draft_64x5_f32logits", B=64, M=5, V=129280, r=256, dtype=BF16,
+                                            base_sigma=2.0, w_sigma=0.02, seed=3, mode="greedy", boost=6.0,
+                                            logits_dtype=F32),
+    "temperature_draft_256x8_f32logits": Workload("temperature_draft_256x8_f32logits", B=256, M=8, V=151936,
+                                                  r=256, dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=4,
+                                                  mode="temperature", temperature=0.7, gumbel_seed=1234,
+                                                  return_logits=False, logits_dtype=F32),
     # Gated head (GatedMarkovHead) at the DeepSeek-V4.1 hidden size 5120:
     # teacher-forced 320 rows, and a greedy draft of batch 64, block 5.
     "gated_teacher_forced_320": Workload("gated_teacher_forced_320", B=64, M=5, V=129280, r=256,

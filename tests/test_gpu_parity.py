@@ -137,6 +137,21 @@ def test_temperature_draft_256x8(native):
     assert np.array_equal(tok, tok2)
 
 
+@pytest.mark.parametrize("name", ["greedy_draft_64x5_f32logits", "temperature_draft_256x8_f32logits"])
+def test_sampling_on_f32_logits(native, name):
+    """Both drafts on fp32 base logits with bf16 weights, at full size, every
+    row, token and element against the oracle (the step kernel's fp32-logit
+    form: the bf16 bias widened exactly and added in fp32)."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    assert inp["base"].dtype == np.float32 and inp["w1"].dtype == np.uint16
+    tok, corr = run_sample(inp, w.temperature, seed=w.gumbel_seed)
+    lrep, trep = check_chain(inp, w.temperature, w.gumbel_seed, tok, corr, name=w.name)
+    assert trep.tokens == w.B * w.M and lrep.elements == w.elems
+    tok2, _ = run_sample(inp, w.temperature, seed=w.gumbel_seed, return_logits=False)
+    assert np.array_equal(tok, tok2)
+
+
 def test_teacher_forced_2560_zipf(native):
     w = wl.WORKLOADS["teacher_forced_2560_zipf"]
     inp = wl.make_inputs(w)
