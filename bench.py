@@ -38,8 +38,9 @@ VALU_SOURCES = [os.path.join(ROOT, "rank_markov_draft_amd", "csrc", name)
 # 157.3 TFLOP/s fp32 vector peak), a transcendental one for 16 (quarter rate).
 SIMD_CYCLES_PEAK_G = 256 * 4 * 2.4
 EXTRA_WORKLOADS = ("teacher_forced_320", "teacher_forced_2560_zipf", "temperature_draft_256x8",
-                   "teacher_forced_320_f32logits", "gated_teacher_forced_320", "gated_greedy_draft_64x5",
-                   "teacher_forced_320_backward")
+                   "teacher_forced_320_f32logits", "greedy_draft_64x5_f32logits",
+                   "temperature_draft_256x8_f32logits", "greedy_draft_64x5_fp32", "gated_teacher_forced_320",
+                   "gated_greedy_draft_64x5", "teacher_forced_320_backward")
 
 
 def source_hash(paths) -> str:
@@ -204,11 +205,12 @@ def measured_valu():
 def algorithmic_bytes_sample(w, return_logits=True) -> int:
     """Bytes one sample call must move at least: base logits read, corrected
     logits written, W2 read once, the gathered W1 rows, tokens and ids."""
-    lb = 2 if w.dtype == 1 else 4
+    lb = 2 if w.ldtype == 1 else 4
+    wb = 2 if w.dtype == 1 else 4
     elems = w.B * w.M * w.V
     b = elems * lb * (2 if return_logits else 1)
-    b += w.V * w.r * lb                 # W2 once
-    b += w.B * w.M * w.r * lb           # gathered W1 rows
+    b += w.V * w.r * wb                 # W2 once
+    b += w.B * w.M * w.r * wb           # gathered W1 rows
     b += w.B * w.M * 8 + w.B * 8        # tokens out, first_prev in
     return b
 
@@ -283,7 +285,9 @@ def measure_extra(name, rmd, wl, torch, np, steps=10, warmup=3):
     """Time one other workload (a parity case, reported beside the main line)."""
     w = wl.WORKLOADS[name]
     inp = wl.make_inputs(w)
-    per_set = 2 * w.B * w.M * w.V * 2 + 2 * w.V * w.r * 2
+    lbytes = 2 if w.ldtype == 1 else 4
+    wbytes = 2 if w.dtype == 1 else 4
+    per_set = 2 * w.B * w.M * w.V * lbytes + 2 * w.V * w.r * wbytes
     n_sets = max(2, int(np.ceil(600e6 / per_set)))
     sets = []
     for i in range(n_sets):

@@ -327,7 +327,7 @@ dspark_status_t sample_block_impl(const void* base_logits, dspark_dtype_t logits
   const bool f32_tile = logits_dtype == DSPARK_F32 &&
                         tile_path(DSPARK_BF16, weight_dtype, V, r, base_logits, corrected_logits, w1, w2);
   if (!tile && !f32_tile && r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
-  p.nparts = tile ? vocab_slices(V) : (V + 255) / 256;
+  p.nparts = tile ? vocab_slices(V) : dspark::generic_parts(V);
   hipStream_t s = (hipStream_t)stream;
   Control* ctl = (Control*)workspace;
 
@@ -374,7 +374,7 @@ dspark_status_t sample_block_impl(const void* base_logits, dspark_dtype_t logits
     if (e == hipErrorNotSupported) {
       (void)hipGetLastError();
       if (r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
-      p.nparts = (V + 255) / 256;
+      p.nparts = dspark::generic_parts(V);
       e = dspark::launch_generic(p, logits_dtype == DSPARK_BF16, weight_dtype == DSPARK_BF16, s);
     }
     if (e != hipSuccess) return device_failure(e, "sample step launch");
@@ -594,7 +594,7 @@ dspark_status_t dspark_markov_sample_block_gated(
     }
     if (e == hipErrorNotSupported) {
       if (r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
-      p.nparts = (V + 255) / 256;
+      p.nparts = dspark::generic_parts(V);
       e = dspark::launch_generic(p, logits_dtype == DSPARK_BF16, weight_dtype == DSPARK_BF16, s);
     }
     if (e != hipSuccess) return device_failure(e, "gated sample step launch");

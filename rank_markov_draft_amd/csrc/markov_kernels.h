@@ -128,6 +128,10 @@ constexpr int64_t kGroupedApplyMaxRows = 4096;
 // B <= 4096 and the logits and V * r * 2 within 2^31 bytes (hipErrorNotSupported).
 int64_t sample_step_parts(int64_t V);
 hipError_t launch_sample_step(const KernelParams& p, bool logits_f32, int num_cus, hipStream_t s);
+// Row-tile FMA kernel for any dtype pair and rank (32 rows x 128 columns per
+// workgroup, the rank in chunks through LDS); sampling writes
+// generic_parts(V) keys per row (p.nparts must equal it).
+int64_t generic_parts(int64_t V);
 hipError_t launch_generic(const KernelParams& p, bool logits_bf16, bool weights_bf16, hipStream_t s);
 hipError_t launch_reduce(const uint64_t* partials, int64_t nparts, int64_t B, int64_t M, int64_t k,
                          int64_t* tokens, hipStream_t s);

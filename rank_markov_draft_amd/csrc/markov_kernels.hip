@@ -211,8 +211,16 @@ __global__ __launch_bounds__(256) void markov_tile_bf16(KernelParams p) {
   }
 }
 
-// ---------------------------------------------------------------- generic kernel
-// One workgroup per (row, 256-column slice); plain fp32 FMA dot products.
+// ---------------------------------------------------------------- row-tile FMA kernel
+// Any dtype pair and rank (fp32 weights, bf16 logits with fp32 weights,
+// shapes the matrix-core kernels do not take).  A workgroup of 256 threads
+// owns a tile of 32 rows x 128 vocabulary columns.  The rank is walked in
+// chunks of 64: the chunk of the tile's 128 W2w rows and of the 32 rows'
+// gathered W1 rows (or latent rows) is loaded into LDS with coalesced
+// 16-byte loads (the 64 rank elements of a row are contiguous), then thread
+// (ty, tx) accumulates rows 2 ty, 2 ty + 1 and columns 8 tx .. 8 tx + 7 with
+// fp32 FMAs in rank order.  W2w is thus read once per 32 rows, not once per
+// row.  Sampling writes one argmax key per (row, 128-column tile).
 __device__ __forceinline__ float load_f32(const void* p, int64_t i) { return ((const float*)p)[i]; }
 __device__ __forceinline__ float load_bf16(const void* p, int64_t i) {
   return __uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16);
@@ -221,61 +229,166 @@ __device__ __forceinline__ float round_bf16_value(float x) {
   return __uint_as_float(pack_bf16x2(x, 0.0f) << 16);
 }
 
+namespace {
+constexpr int kFmaRows = 32;
+constexpr int kFmaCols = 128;
+constexpr int kFmaK = 64;
+constexpr int kFmaPitch = kFmaK + 1;  // floats per LDS row (odd: conflict-free column walks)
+}  // namespace
+
+// Eight consecutive elements [i, i + 8) of a W-typed array, as floats; the
+// caller guarantees the range is in bounds or passes ok = false (zeros).
+template <bool W_BF16>
+__device__ __forceinline__ void load8(const void* p, int64_t i, bool ok, float out[8]) {
+  if (!ok) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) out[q] = 0.0f;
+    return;
+  }
+  if constexpr (W_BF16) {
+    const u32x4_t v = *(const u32x4_t*)((const uint16_t*)p + i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      out[2 * q] = bf16_lo(w[q]);
+      out[2 * q + 1] = bf16_hi(w[q]);
+    }
+  } else {
+    const f32x4_t a = *(const f32x4_t*)((const float*)p + i);
+    const f32x4_t b = *(const f32x4_t*)((const float*)p + i + 4);
+    out[0] = a[0]; out[1] = a[1]; out[2] = a[2]; out[3] = a[3];
+    out[4] = b[0]; out[5] = b[1]; out[6] = b[2]; out[7] = b[3];
+  }
+}
+
 template <int MODE, bool L_BF16, bool W_BF16>
-__global__ __launch_bounds__(256) void markov_generic(KernelParams p) {
-  extern __shared__ float lds_row[];
-  __shared__ uint64_t lds_key[4];
-  const int64_t n = blockIdx.x;
+__global__ __launch_bounds__(256) void markov_rows_fma(KernelParams p, int64_t chunk0) {
+  __shared__ float lds_w[kFmaCols * kFmaPitch];  // W2w chunk [128 columns][64 rank]
+  __shared__ float lds_e[kFmaRows * kFmaPitch];  // gathered rows [32][64 rank]
+  __shared__ int64_t lds_src[kFmaRows];          // source row of each tile row's E (-1: zero)
   const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
   const int64_t V = p.V, r = p.r;
-  const int64_t v = (int64_t)blockIdx.y * 256 + tid;
-  const bool count_bad = (blockIdx.y == 0) && (MODE == MODE_APPLY || p.k == 0);
-
-  const int64_t x = predecessor(p, n);
-  const bool ok = (x >= 0) && (x < V);
-  if (!ok && tid == 0 && count_bad) atomicAdd(p.bad_rows, 1u);
-  // gated head: latent row n instead of W1[x]
+  const int64_t v0 = (int64_t)blockIdx.x * kFmaCols;
+  const int64_t n0 = (chunk0 + blockIdx.y) * kFmaRows;
+  const bool count_bad = blockIdx.x == 0 && (MODE == MODE_APPLY || p.k == 0);
+  // 16-byte loads of 8-element pieces: rows of a multiple of 8 elements and
+  // 16-byte aligned arrays (else element loads)
   const void* const erow = p.latent != nullptr ? p.latent : p.w1;
-  const int64_t ebase = p.latent != nullptr ? n * p.latent_ld : x * r;
-  for (int64_t j = tid; j < r; j += 256)
-    lds_row[j] = ok ? (W_BF16 ? load_bf16(erow, ebase + j) : load_f32(erow, ebase + j)) : 0.0f;
-  __syncthreads();
+  const int64_t eld = p.latent != nullptr ? p.latent_ld : r;
+  const bool vec_ok = r % 8 == 0 && ((uintptr_t)p.w2 & 15) == 0;
+  const bool evec_ok = r % 8 == 0 && eld % 8 == 0 && ((uintptr_t)erow & 15) == 0;
 
-  uint64_t key = 0;
-  if (v < V) {
-    float acc = 0.0f;
-    for (int64_t j = 0; j < r; ++j) {
-      const float w = W_BF16 ? load_bf16(p.w2, v * r + j) : load_f32(p.w2, v * r + j);
-      acc = __builtin_fmaf(lds_row[j], w, acc);
+  if (tid < kFmaRows) {
+    const int64_t n = n0 + tid;
+    int64_t src = -1;
+    if (n < p.rows) {
+      const int64_t x = predecessor(p, n);
+      const bool ok = x >= 0 && x < V;
+      if (!ok && count_bad) atomicAdd(p.bad_rows, 1u);
+      if (ok) src = p.latent != nullptr ? n * p.latent_ld : x * r;
     }
-    float bias = W_BF16 ? round_bf16_value(acc) : acc;
-    if (L_BF16) bias = round_bf16_value(bias);
-    const int64_t off = base_row_offset(p, n) + v;
-    const float b = L_BF16 ? load_bf16(p.base, off) : load_f32(p.base, off);
-    float c = b + bias;
-    if (L_BF16) c = round_bf16_value(c);
-    if (p.out != nullptr) {
-      if (L_BF16)
-        ((uint16_t*)p.out)[off] = (uint16_t)(__float_as_uint(c) >> 16);
-      else
-        ((float*)p.out)[off] = c;
+    lds_src[tid] = src;
+  }
+
+  float acc[2][8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[i][c] = 0.0f;
+
+  for (int64_t k0 = 0; k0 < r; k0 += kFmaK) {
+    __syncthreads();  // the previous chunk's reads are done (and lds_src is written)
+    // W2w chunk: 128 rows x 64 rank = 1024 pieces of 8; thread t takes pieces t + 256 q
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int piece = tid + 256 * q;
+      const int row = piece >> 3, kp = (piece & 7) * 8;
+      const int64_t v = v0 + row, k = k0 + kp;
+      float w[8];
+      if (vec_ok) {
+        load8<W_BF16>(p.w2, v * r + k, v < V && k < r, w);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          w[c] = (v < V && k + c < r) ? (W_BF16 ? load_bf16(p.w2, v * r + k + c) : load_f32(p.w2, v * r + k + c))
+                                      : 0.0f;
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) lds_w[row * kFmaPitch + kp + c] = w[c];
     }
-    if constexpr (MODE == MODE_GREEDY) key = argmax_key(c, (uint32_t)v);
-    if constexpr (MODE == MODE_TEMPERATURE) {
-      const Philox4 q = philox4x32_10((uint32_t)((uint64_t)v >> 2), p.k_abs,
-                                      (uint32_t)(p.batch_offset + n), 0u, p.seed_lo, p.seed_hi);
-      const uint32_t words[4] = {q.x0, q.x1, q.x2, q.x3};
-      key = argmax_key(__builtin_fmaf(c, p.kappa, gumbel2_from_word(words[v & 3])), (uint32_t)v);
+    // E chunk: 32 rows x 64 rank = 256 pieces of 8, one per thread
+    {
+      const int row = tid >> 3, kp = (tid & 7) * 8;
+      const int64_t src = lds_src[row], k = k0 + kp;
+      float e[8];
+      if (evec_ok) {
+        load8<W_BF16>(erow, src + k, src >= 0 && k < r, e);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          e[c] = (src >= 0 && k + c < r) ? (W_BF16 ? load_bf16(erow, src + k + c) : load_f32(erow, src + k + c))
+                                         : 0.0f;
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) lds_e[row * kFmaPitch + kp + c] = e[c];
+    }
+    __syncthreads();
+    const int kn = (int)(r - k0 < kFmaK ? r - k0 : kFmaK);
+    for (int k = 0; k < kn; ++k) {
+      const float e0 = lds_e[(2 * ty) * kFmaPitch + k];
+      const float e1 = lds_e[(2 * ty + 1) * kFmaPitch + k];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float w = lds_w[(8 * tx + c) * kFmaPitch + k];
+        acc[0][c] = __builtin_fmaf(e0, w, acc[0][c]);
+        acc[1][c] = __builtin_fmaf(e1, w, acc[1][c]);
+      }
     }
   }
-  if constexpr (MODE != MODE_APPLY) {
-    key = group_max_u64<64>(key);
-    if ((tid & 63) == 0) lds_key[tid >> 6] = key;
-    __syncthreads();
-    if (tid == 0) {
-      const uint64_t k01 = max_u64(lds_key[0], lds_key[1]);
-      const uint64_t k23 = max_u64(lds_key[2], lds_key[3]);
-      p.partials[n * p.nparts + blockIdx.y] = max_u64(k01, k23);
+
+  // epilogue: thread (ty, tx) finishes rows n0 + 2 ty + i, columns v0 + 8 tx + c
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t n = n0 + 2 * ty + i;
+    const bool row_ok = n < p.rows;
+    const int64_t rowoff = row_ok ? base_row_offset(p, n) : 0;
+    uint64_t key = 0;
+    uint32_t words[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};  // noise words of the 8 columns
+    if constexpr (MODE == MODE_TEMPERATURE) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // columns 8 tx + 4 h .. + 3 share one Philox block
+        const Philox4 q = philox4x32_10((uint32_t)((uint64_t)(v0 + 8 * tx + 4 * h) >> 2), p.k_abs,
+                                        (uint32_t)(p.batch_offset + n), 0u, p.seed_lo, p.seed_hi);
+        words[4 * h] = q.x0;
+        words[4 * h + 1] = q.x1;
+        words[4 * h + 2] = q.x2;
+        words[4 * h + 3] = q.x3;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int64_t v = v0 + 8 * tx + c;
+      if (!row_ok || v >= V) continue;
+      float bias = W_BF16 ? round_bf16_value(acc[i][c]) : acc[i][c];
+      if (L_BF16) bias = round_bf16_value(bias);
+      const int64_t off = rowoff + v;
+      const float b = L_BF16 ? load_bf16(p.base, off) : load_f32(p.base, off);
+      float cval = b + bias;
+      if (L_BF16) cval = round_bf16_value(cval);
+      if (p.out != nullptr) {
+        if (L_BF16)
+          ((uint16_t*)p.out)[off] = (uint16_t)(__float_as_uint(cval) >> 16);
+        else
+          ((float*)p.out)[off] = cval;
+      }
+      if constexpr (MODE == MODE_GREEDY) key = max_u64(key, argmax_key(cval, (uint32_t)v));
+      if constexpr (MODE == MODE_TEMPERATURE)
+        key = max_u64(key, argmax_key(__builtin_fmaf(cval, p.kappa, gumbel2_from_word(words[c])), (uint32_t)v));
+    }
+    if constexpr (MODE != MODE_APPLY) {
+      key = group_max_u64<16>(key);  // the 16 threads (tx) of row n
+      if (tx == 0 && row_ok) p.partials[n * p.nparts + blockIdx.x] = key;
     }
   }
 }
@@ -347,21 +460,29 @@ hipError_t launch_tile(const KernelParams& p, hipStream_t s) {
   return launch_tile_mode<MODE_TEMPERATURE>(p, ks, s);
 }
 
+template <int MODE, bool LBF, bool WBF>
+static hipError_t launch_rows_fma(const KernelParams& p, hipStream_t s) {
+  const int64_t chunks = (p.rows + kFmaRows - 1) / kFmaRows;
+  const unsigned tiles = (unsigned)((p.V + kFmaCols - 1) / kFmaCols);
+  for (int64_t c0 = 0; c0 < chunks; c0 += 65535) {  // grid.y holds at most 65535 row chunks
+    const int64_t nc = chunks - c0 < 65535 ? chunks - c0 : 65535;
+    hipLaunchKernelGGL((markov_rows_fma<MODE, LBF, WBF>), dim3(tiles, (unsigned)nc), dim3(256), 0, s, p, c0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <int MODE>
 static hipError_t launch_generic_mode(const KernelParams& p, bool lbf, bool wbf, hipStream_t s) {
-  const dim3 grid((unsigned)p.rows, (unsigned)((p.V + 255) / 256));
-  const dim3 block(256);
-  const size_t lds = (size_t)p.r * sizeof(float);
-  if (lbf && wbf)
-    hipLaunchKernelGGL((markov_generic<MODE, true, true>), grid, block, lds, s, p);
-  else if (!lbf && !wbf)
-    hipLaunchKernelGGL((markov_generic<MODE, false, false>), grid, block, lds, s, p);
-  else if (lbf)
-    hipLaunchKernelGGL((markov_generic<MODE, true, false>), grid, block, lds, s, p);
-  else
-    hipLaunchKernelGGL((markov_generic<MODE, false, true>), grid, block, lds, s, p);
-  return hipGetLastError();
+  if (p.mode != MODE_APPLY && p.nparts != generic_parts(p.V)) return hipErrorInvalidValue;
+  if (lbf && wbf) return launch_rows_fma<MODE, true, true>(p, s);
+  if (!lbf && !wbf) return launch_rows_fma<MODE, false, false>(p, s);
+  if (lbf) return launch_rows_fma<MODE, true, false>(p, s);
+  return launch_rows_fma<MODE, false, true>(p, s);
 }
+
+int64_t generic_parts(int64_t V) { return (V + kFmaCols - 1) / kFmaCols; }
 
 hipError_t launch_generic(const KernelParams& p, bool logits_bf16, bool weights_bf16, hipStream_t s) {
   if (p.mode == MODE_APPLY) return launch_generic_mode<MODE_APPLY>(p, logits_bf16, weights_bf16, s);

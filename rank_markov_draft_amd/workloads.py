@@ -92,6 +92,9 @@ WORKLOADS = {
                                                   r=256, dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=4,
                                                   mode="temperature", temperature=0.7, gumbel_seed=1234,
                                                   return_logits=False, logits_dtype=F32),
+    # The greedy draft with fp32 logits and fp32 weights (the row-tile FMA kernel).
+    "greedy_draft_64x5_fp32": Workload("greedy_draft_64x5_fp32", B=64, M=5, V=129280, r=256, dtype=F32,
+                                       base_sigma=2.0, w_sigma=0.02, seed=3, mode="greedy", boost=6.0),
     # Gated head (GatedMarkovHead) at the DeepSeek-V4.1 hidden size 5120:
     # teacher-forced 320 rows, and a greedy draft of batch 64, block 5.
     "gated_teacher_forced_320": Workload("gated_teacher_forced_320", B=64, M=5, V=129280, r=256,

@@ -277,6 +277,23 @@ def test_apply_mixed_dtypes(native, ldt, wdt, B, M, V, r):
     check_apply(inp, run_apply(inp), name=f"apply mixed L{ldt} W{wdt} B{B} M{M} V{V} r{r}")
 
 
+@pytest.mark.parametrize("ldt,wdt,B,M,V,r,T", [
+    (wl.F32, wl.F32, 16, 3, 129280, 256, 0.0),     # fp32 weights at the full vocabulary: row-tile FMA kernel
+    (wl.F32, wl.F32, 8, 3, 129280, 256, 0.7),
+    (wl.BF16, wl.F32, 12, 3, 129280, 256, 0.0),
+    (wl.F32, wl.F32, 3, 4, 3001, 20, 0.7),         # ragged columns and a rank that is not a multiple of 8
+    (wl.F32, wl.F32, 37, 2, 1000, 1040, 0.0),      # rank past 1024: many rank chunks; rows past one tile
+])
+def test_fp32_weight_kernel(native, ldt, wdt, B, M, V, r, T):
+    """fp32 weights (and bf16 logits with fp32 weights) go to the row-tile FMA
+    kernel: sampling and the teacher-forced apply against the oracle on every
+    row."""
+    inp = _mixed_inputs(ldt, wdt, B, M, V, r, seed=B * 31 + V)
+    tok, corr = run_sample(inp, T, seed=3)
+    check_chain(inp, T, 3, tok, corr, name=f"fp32-weight sample L{ldt} B{B} M{M} V{V} r{r} T{T}")
+    check_apply(inp, run_apply(inp), name=f"fp32-weight apply L{ldt} B{B} M{M} V{V} r{r}")
+
+
 @pytest.mark.parametrize("T", [0.0, 0.8])
 @pytest.mark.parametrize("ldt,wdt", [(wl.F32, wl.BF16), (wl.BF16, wl.F32)])
 def test_sample_mixed_dtypes(native, T, ldt, wdt):
