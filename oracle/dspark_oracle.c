@@ -823,3 +823,103 @@ int dspark_oracle_backward_bounds(const void* grad, int logits_dtype,
   }
   return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* LM head fused with the bias ([P1] DeepseekV41DSparkModel.compute_logits */
+/* followed by [P5] apply_block_logits)                                */
+/* ------------------------------------------------------------------ */
+
+/* [P1] compute_logits projects the hidden states through the frozen
+ * vocabulary head in FP32 and returns FP32 logits U [rows, V]; [P5]
+ * apply_block_logits then adds bias.to(U.dtype).  Reading: "in FP32" is an
+ * fp32 accumulation of the products of the hidden row and the head's
+ * weight row ([V, d], the Linear layout) with their values widened exactly;
+ * the oracle models it by its best value, the double sum in index order
+ * rounded once to fp32.  The bias follows the vanilla reading (fp32
+ * accumulator rounded to the weight dtype W, then to fp32), and the
+ * corrected logit is the fp32 sum U + bias. */
+static float lm_head_value(const void* hidden, int hdt, int64_t n, const void* lm, int lmdt, int64_t v,
+                           int64_t d, double* s_abs) {
+  double a = 0.0, s = 0.0;
+  for (int64_t i = 0; i < d; ++i) {
+    const double t = load_as_double(hidden, hdt, n * d + i) * load_as_double(lm, lmdt, v * d + i);
+    a += t;
+    s += fabs(t);
+  }
+  if (s_abs) *s_abs = s;
+  return (float)a;
+}
+
+int dspark_oracle_apply_block_lm_head(const void* hidden, int hidden_dtype, const void* lm_head,
+                                      int lm_dtype, int64_t d, const int64_t* token_ids,
+                                      const void* w1, const void* w2, int weight_dtype, int64_t rows,
+                                      int64_t V, int64_t r, float* corrected, float* base_out,
+                                      int n_threads) {
+  if (!valid_dtype(hidden_dtype) || !valid_dtype(lm_dtype) || !valid_dtype(weight_dtype))
+    return ORACLE_UNSUPPORTED;
+  if (rows < 0 || V < 0 || r <= 0 || d <= 0) return ORACLE_INVALID;
+  if (rows == 0 || V == 0) return ORACLE_OK;
+  if (!hidden || !lm_head || !token_ids || !w1 || !w2 || !corrected) return ORACLE_INVALID;
+  for (int64_t n = 0; n < rows; ++n)
+    if (token_ids[n] < 0 || token_ids[n] >= V) return ORACLE_INVALID;
+  double* w2d = w2_as_double(w2, weight_dtype, V, r);
+  if (!w2d) return ORACLE_INVALID;
+  int nt = n_threads_or_default(n_threads);
+#pragma omp parallel num_threads(nt)
+  {
+    double* e = (double*)malloc((size_t)r * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t n = 0; n < rows; ++n) {
+      gather_w1_row(w1, weight_dtype, r, token_ids[n], e);
+      for (int64_t v = 0; v < V; ++v) {
+        const float u = lm_head_value(hidden, hidden_dtype, n, lm_head, lm_dtype, v, d, NULL);
+        const float acc = projected_bias(e, w2d + v * r, r);
+        corrected[n * V + v] = corrected_value(u, acc, ORACLE_F32, weight_dtype);
+        if (base_out) base_out[n * V + v] = u;
+      }
+    }
+    free(e);
+  }
+  free(w2d);
+  return ORACLE_OK;
+}
+
+/* Admissible interval of fused elements (rows[i], cols[i]) for a device that
+ * accumulates both products in fp32 in any order: U pushed to
+ * -/+ 2 d 2^-24 sum|h w| and the bias accumulator to -/+ 2 r 2^-24 sum|e w2|
+ * (twice Higham's bound each), through the monotone chain (round to fp32,
+ * bias rounded to W then fp32, fp32 add). */
+int dspark_oracle_lm_head_bounds(const void* hidden, int hidden_dtype, const void* lm_head, int lm_dtype,
+                                 int64_t d, const int64_t* token_ids, const void* w1, const void* w2,
+                                 int weight_dtype, int64_t V, int64_t r, int64_t n, const int64_t* rows,
+                                 const int64_t* cols, float* lo, float* mid, float* hi) {
+  if (!valid_dtype(hidden_dtype) || !valid_dtype(lm_dtype) || !valid_dtype(weight_dtype))
+    return ORACLE_UNSUPPORTED;
+  if (V <= 0 || r <= 0 || d <= 0 || n < 0) return ORACLE_INVALID;
+  if (n == 0) return ORACLE_OK;
+  if (!hidden || !lm_head || !token_ids || !w1 || !w2 || !rows || !cols || !lo || !mid || !hi)
+    return ORACLE_INVALID;
+  const double u24 = ldexp(1.0, -24);
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t row = rows[i], v = cols[i];
+    if (row < 0 || v < 0 || v >= V) return ORACLE_INVALID;
+    const int64_t x = token_ids[row];
+    if (x < 0 || x >= V) return ORACLE_INVALID;
+    double a = 0.0, s = 0.0, ub = 0.0, su = 0.0;
+    for (int64_t j = 0; j < r; ++j) {
+      const double t = load_as_double(w1, weight_dtype, x * r + j) * load_as_double(w2, weight_dtype, v * r + j);
+      a += t;
+      s += fabs(t);
+    }
+    for (int64_t k = 0; k < d; ++k) {
+      const double t = load_as_double(hidden, hidden_dtype, row * d + k) * load_as_double(lm_head, lm_dtype, v * d + k);
+      ub += t;
+      su += fabs(t);
+    }
+    const double db = 2.0 * (double)r * u24 * s, du = 2.0 * (double)d * u24 * su;
+    lo[i] = corrected_value((float)(ub - du), (float)(a - db), ORACLE_F32, weight_dtype);
+    mid[i] = corrected_value((float)ub, (float)a, ORACLE_F32, weight_dtype);
+    hi[i] = corrected_value((float)(ub + du), (float)(a + db), ORACLE_F32, weight_dtype);
+  }
+  return ORACLE_OK;
+}

@@ -169,6 +169,23 @@ int dspark_oracle_backward_bounds(const void* grad, int logits_dtype,
                                   const int64_t* which, const int64_t* cols, float* lo,
                                   float* mid, float* hi);
 
+/* LM head fused with the bias: U = the FP32 projection of hidden [rows, d]
+ * through the vocabulary head lm_head [V, d] ([P1] compute_logits), then
+ * corrected = U + bias.to(fp32) with bias = project_bias(W1[token_ids[n]])
+ * ([P5] apply_block_logits).  corrected [rows, V] fp32; base_out [rows, V]
+ * fp32 receives U when not NULL. */
+int dspark_oracle_apply_block_lm_head(const void* hidden, int hidden_dtype, const void* lm_head,
+                                      int lm_dtype, int64_t d, const int64_t* token_ids,
+                                      const void* w1, const void* w2, int weight_dtype, int64_t rows,
+                                      int64_t V, int64_t r, float* corrected, float* base_out,
+                                      int n_threads);
+/* Admissible interval of fused elements (rows[i], cols[i]) under any fp32
+ * accumulation order of both products; mid is the oracle's value. */
+int dspark_oracle_lm_head_bounds(const void* hidden, int hidden_dtype, const void* lm_head, int lm_dtype,
+                                 int64_t d, const int64_t* token_ids, const void* w1, const void* w2,
+                                 int weight_dtype, int64_t V, int64_t r, int64_t n, const int64_t* rows,
+                                 const int64_t* cols, float* lo, float* mid, float* hi);
+
 /* Building blocks exposed for pinning. */
 void dspark_oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2],
                                  uint32_t out[4]);

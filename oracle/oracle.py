@@ -59,6 +59,12 @@ def lib():
         L.dspark_oracle_select_token.argtypes = [
             _p, _int, _i64, ctypes.c_double, ctypes.c_uint64, _i64, _i64, _p, _p, _p]
         L.dspark_oracle_select_token.restype = _int
+        L.dspark_oracle_apply_block_lm_head.argtypes = [_p, _int, _p, _int, _i64, _p, _p, _p, _int, _i64, _i64,
+                                                        _i64, _p, _p, _int]
+        L.dspark_oracle_apply_block_lm_head.restype = _int
+        L.dspark_oracle_lm_head_bounds.argtypes = [_p, _int, _p, _int, _i64, _p, _p, _p, _int, _i64, _i64, _i64,
+                                                   _p, _p, _p, _p, _p]
+        L.dspark_oracle_lm_head_bounds.restype = _int
         L.dspark_oracle_select_tokens.argtypes = [
             _p, _int, _i64, _i64, ctypes.c_double, ctypes.c_uint64, _p, _p, _p, _p, _p, _int]
         L.dspark_oracle_select_tokens.restype = _int
@@ -326,6 +332,38 @@ def backward_bounds(grad, token_ids, w1, w2, kind, which, cols):
     _check(lib().dspark_oracle_backward_bounds(
         _ptr(grad), _dtype_tag(grad), _ptr(ids), _ptr(w1), _ptr(w2), _dtype_tag(w1), ids.shape[0], V, r,
         2 if kind == "dw2" else 1, n, _ptr(which), _ptr(cols), _ptr(lo), _ptr(mid), _ptr(hi)))
+    return lo, mid, hi
+
+
+def apply_block_lm_head(hidden, lm_head, token_ids, w1, w2, n_threads: int = 0, return_base: bool = False):
+    """Fused LM head and bias: hidden [..., d] -> corrected fp32 [..., V] with
+    U = hidden . lm_head^T in FP32 (lm_head [V, d]) plus the bias of token_ids
+    [...]; with return_base also U."""
+    hidden, lm_head, w1, w2 = _c(hidden), _c(lm_head), _c(w1), _c(w2)
+    ids = _c(token_ids, np.int64)
+    d = hidden.shape[-1]
+    V, r = w1.shape
+    rows = ids.size
+    out = np.zeros(ids.shape + (V,), dtype=np.float32)
+    base = np.zeros_like(out) if return_base else None
+    _check(lib().dspark_oracle_apply_block_lm_head(
+        _ptr(hidden), _dtype_tag(hidden), _ptr(lm_head), _dtype_tag(lm_head), d, _ptr(ids), _ptr(w1), _ptr(w2),
+        _dtype_tag(w1), rows, V, r, _ptr(out), _ptr(base), n_threads))
+    return (out, base) if return_base else out
+
+
+def lm_head_bounds(hidden, lm_head, token_ids, w1, w2, rows, cols):
+    """Admissible [lo, hi] and the oracle's value for fused elements (rows[i], cols[i])."""
+    hidden, lm_head, w1, w2 = _c(hidden), _c(lm_head), _c(w1), _c(w2)
+    ids = _c(token_ids, np.int64).reshape(-1)
+    rows, cols = _c(rows, np.int64), _c(cols, np.int64)
+    n = rows.shape[0]
+    lo, mid, hi = (np.zeros(n, dtype=np.float32) for _ in range(3))
+    d = hidden.shape[-1]
+    V, r = w1.shape
+    _check(lib().dspark_oracle_lm_head_bounds(
+        _ptr(hidden), _dtype_tag(hidden), _ptr(lm_head), _dtype_tag(lm_head), d, _ptr(ids), _ptr(w1), _ptr(w2),
+        _dtype_tag(w1), V, r, n, _ptr(rows), _ptr(cols), _ptr(lo), _ptr(mid), _ptr(hi)))
     return lo, mid, hi
 
 
