@@ -24,6 +24,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
 WORKLOAD = "greedy_draft_64x5"
 DOMINANT_KERNEL = "markov_chain_greedy_bf16"   # the whole sample call is this one launch
 KERNEL_SOURCES = [os.path.join(ROOT, "rank_markov_draft_amd", "csrc", name)
@@ -40,7 +41,7 @@ SIMD_CYCLES_PEAK_G = 256 * 4 * 2.4
 EXTRA_WORKLOADS = ("teacher_forced_320", "teacher_forced_2560_zipf", "temperature_draft_256x8",
                    "teacher_forced_320_f32logits", "greedy_draft_64x5_f32logits",
                    "temperature_draft_256x8_f32logits", "greedy_draft_64x5_fp32", "gated_teacher_forced_320",
-                   "gated_greedy_draft_64x5", "teacher_forced_320_backward")
+                   "gated_greedy_draft_64x5", "teacher_forced_320_backward", "lm_head_teacher_forced_320")
 
 
 def source_hash(paths) -> str:
@@ -238,6 +239,14 @@ def algorithmic_bytes_gate(w) -> int:
     return w.B * w.M * w.hidden * wb + w.r * (w.hidden + w.r) * wb + w.r * wb
 
 
+def algorithmic_bytes_lm_head(w) -> int:
+    """Bytes the fused head must move at least: the head's weight and W2 read
+    once, the hidden states and gathered W1 rows, ids, and the fp32 corrected
+    logits written (the base logits never exist)."""
+    rows = w.B * w.M
+    return w.V * w.lm_head * 2 + rows * w.lm_head * 2 + w.V * w.r * 2 + rows * (w.r * 2 + 8) + rows * w.V * 4
+
+
 def to_dev(a, torch, np):
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
@@ -292,9 +301,11 @@ def measure_extra(name, rmd, wl, torch, np, steps=10, warmup=3):
     sets = []
     for i in range(n_sets):
         keys = ("base", "first_prev", "token_ids", "w1", "w2") + (("hidden", "gate_w", "gate_b") if w.hidden else ()) \
-            + (("grad",) if w.mode == "backward" else ())
+            + (("grad",) if w.mode == "backward" else ()) + (("lm_hidden", "lm_head") if w.lm_head else ())
         d = {k: to_dev(inp[k], torch, np) for k in keys}
         d["out"] = torch.empty_like(d["base"]) if (w.mode == "apply" or w.return_logits) else None
+        if w.lm_head:
+            d["out"] = torch.empty(d["base"].shape, dtype=torch.float32, device="cuda")
         d["tok"] = torch.empty((w.B, w.M), dtype=torch.int64, device="cuda")
         d["ws"] = rmd.Workspace(w.B, w.M, w.V, w.r, sample=(w.mode not in ("apply", "backward")),
                                 hidden=w.hidden or None, backward=(w.mode == "backward"))
@@ -303,7 +314,10 @@ def measure_extra(name, rmd, wl, torch, np, steps=10, warmup=3):
 
     def call(i):
         d = sets[i]
-        if w.mode == "backward":
+        if w.lm_head:
+            rmd.apply_block_logits_lm_head(d["lm_hidden"], d["lm_head"], d["token_ids"], d["w1"], d["w2"],
+                                           out=d["out"], workspace=d["ws"])
+        elif w.mode == "backward":
             rmd.apply_block_logits_backward(d["grad"], d["token_ids"], d["w1"], d["w2"], workspace=d["ws"])
         elif w.hidden and w.mode == "apply":
             rmd.apply_block_logits_gated(d["base"], d["token_ids"], d["w1"], d["w2"], d["gate_w"], d["gate_b"],
@@ -321,7 +335,9 @@ def measure_extra(name, rmd, wl, torch, np, steps=10, warmup=3):
 
     wall, per = time_calls(call, n_sets, steps, warmup, torch)
     ms = float(np.mean(per))
-    if w.mode == "backward":
+    if w.lm_head:
+        alg = algorithmic_bytes_lm_head(w)
+    elif w.mode == "backward":
         alg = algorithmic_bytes_backward(w)
     elif w.mode == "apply":
         alg = algorithmic_bytes_apply(w)
@@ -333,6 +349,12 @@ def measure_extra(name, rmd, wl, torch, np, steps=10, warmup=3):
            "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": alg}
     if w.mode not in ("apply", "backward"):
         res["tokens_per_s"] = w.B * w.M / (ms * 1e-3)
+    if w.lm_head:
+        # both products on the matrix cores: bf16 dense peak
+        flops = 2.0 * w.B * w.M * w.V * (w.lm_head + w.r)
+        res["roofline"] = {"bound": "mfma", "kernel": "markov_lm_head_bf16", "achieved": flops / (ms * 1e-3) / 1e12,
+                           "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, "flops_per_call": flops}
     cycles = measured_valu() if name == "temperature_draft_256x8" else None
     if cycles:
         # vector-issue roofline of the whole call (M step kernels; the

@@ -242,6 +242,35 @@ dspark_status_t dspark_markov_apply_block_backward(const void* grad_corrected, d
                                                    int64_t r, void* grad_w1, void* grad_w2, void* workspace,
                                                    size_t workspace_bytes, void* stream);
 
+/* The drafter's vocabulary head fused with the teacher-forced bias: the
+ * base logits U = hidden . lm_head^T are computed in FP32 (NeMo AutoModel
+ * "models/deepseek_v41/dspark" page, DeepseekV41DSparkModel.compute_logits:
+ * the hidden states projected through the frozen vocabulary head in FP32,
+ * FP32 logits out) and the Markov bias is added as in apply_block_logits
+ * (third-party markov_head.py page: U + bias.to(U.dtype)), without U ever
+ * being written:
+ *     corrected[n, v] = fp32( U[n, v] + fp32(round_W(sum_j W1[x_n, j] W2w[v, j])) ),
+ * U[n, v] = the fp32 accumulation of hidden[n, i] * lm_head[v, i] (exact
+ * products of the widened operands).
+ *   hidden_states    device, [B, M, d] (row (b, k) is the drafter's hidden
+ *                    state of block position k), hidden_dtype.
+ *   lm_head_weight   device, [V, d] (the head's Linear weight), lm_head_dtype.
+ *   token_ids        device, [B, M] int64 teacher-forced predecessors.
+ *   w1, w2           device, [V, r] each, weight_dtype.
+ *   corrected_logits device, [B, M, V] float32 output; must not overlap an input.
+ * The kernel takes bf16 hidden states, head and Markov weights with d, r
+ * and V multiples of 8, 16-byte aligned buffers, and each buffer within
+ * 2^31 bytes; other calls return DSPARK_ERR_UNSUPPORTED (the message names
+ * the rule).  B*M*V == 0 is a successful no-op; out-of-range ids give a zero
+ * bias and are counted as in dspark_markov_apply_block.  The workspace is
+ * that of dspark_markov_apply_block (only its error word is used). */
+dspark_status_t dspark_markov_apply_block_lm_head(const void* hidden_states, dspark_dtype_t hidden_dtype, int64_t d,
+                                                  const void* lm_head_weight, dspark_dtype_t lm_head_dtype,
+                                                  const int64_t* token_ids, const void* w1, const void* w2,
+                                                  dspark_dtype_t weight_dtype, int64_t B, int64_t M, int64_t V,
+                                                  int64_t r, float* corrected_logits, void* workspace,
+                                                  size_t workspace_bytes, void* stream);
+
 /* Synchronises `stream`, then returns in *bad_rows the number of rows whose
  * predecessor id was outside [0, V) in the calls made with this workspace
  * since the last read, and clears the count.  Returns DSPARK_ERR_DEVICE when

@@ -901,10 +901,13 @@ int dspark_oracle_lm_head_bounds(const void* hidden, int hidden_dtype, const voi
     return ORACLE_INVALID;
   const double u24 = ldexp(1.0, -24);
   for (int64_t i = 0; i < n; ++i) {
+    if (rows[i] < 0 || cols[i] < 0 || cols[i] >= V) return ORACLE_INVALID;
+    if (token_ids[rows[i]] < 0 || token_ids[rows[i]] >= V) return ORACLE_INVALID;
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
     const int64_t row = rows[i], v = cols[i];
-    if (row < 0 || v < 0 || v >= V) return ORACLE_INVALID;
     const int64_t x = token_ids[row];
-    if (x < 0 || x >= V) return ORACLE_INVALID;
     double a = 0.0, s = 0.0, ub = 0.0, su = 0.0;
     for (int64_t j = 0; j < r; ++j) {
       const double t = load_as_double(w1, weight_dtype, x * r + j) * load_as_double(w2, weight_dtype, v * r + j);

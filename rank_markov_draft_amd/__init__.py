@@ -11,6 +11,8 @@ VanillaMarkov methods (third-party markov_head.py page):
 
 ``apply_block_logits_backward`` gives the gradients of W1 and W2 for a
 gradient of the teacher-forced corrected logits (training).
+``apply_block_logits_lm_head`` fuses the drafter's FP32 vocabulary head
+(the base logits) with the teacher-forced bias.
 
 The gated head (the pages' GatedMarkovHead) has the same two operations,
 ``apply_block_logits_gated`` and ``sample_block_tokens_gated``, which also
@@ -32,8 +34,8 @@ import torch
 from . import _lib
 
 __all__ = ["apply_block_logits", "sample_block_tokens", "apply_block_logits_gated",
-           "sample_block_tokens_gated", "apply_block_logits_backward", "Workspace", "read_device_error",
-           "workspace_bytes"]
+           "sample_block_tokens_gated", "apply_block_logits_backward", "apply_block_logits_lm_head", "Workspace",
+           "read_device_error", "workspace_bytes"]
 
 
 def _dtype_tag(t: torch.Tensor) -> int:
@@ -202,6 +204,50 @@ def sample_block_tokens(base_logits: torch.Tensor, first_prev_token_ids: torch.T
     if check:
         read_device_error(workspace)
     return tokens_out, corrected
+
+
+def apply_block_logits_lm_head(hidden_states: torch.Tensor, lm_head_weight: torch.Tensor,
+                               token_ids: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, *,
+                               out: torch.Tensor | None = None,
+                               workspace: Workspace | None = None) -> torch.Tensor:
+    """The drafter's vocabulary head fused with the teacher-forced bias:
+    hidden_states [..., M, d] and the head's Linear weight [V, d] give FP32
+    base logits U (DeepseekV41DSparkModel.compute_logits), and the result is
+    U + bias(token_ids[..., M]) as apply_block_logits would return it, in
+    float32 [..., M, V], without U being materialised."""
+    _check_weights(w1, w2)
+    if hidden_states.dim() < 2:
+        raise ValueError("hidden_states must be [..., M, d]")
+    d = hidden_states.shape[-1]
+    M = hidden_states.shape[-2]
+    B = 1
+    for x in hidden_states.shape[:-2]:
+        B *= int(x)
+    V, r = w1.shape
+    if lm_head_weight.dim() != 2 or tuple(lm_head_weight.shape) != (V, d):
+        raise ValueError(f"lm_head_weight must be [V, d] = {(V, d)}, got {tuple(lm_head_weight.shape)}")
+    if tuple(token_ids.shape) != tuple(hidden_states.shape[:-1]):
+        raise ValueError(f"token_ids {tuple(token_ids.shape)} must be hidden_states.shape[:-1]")
+    dev = hidden_states.device
+    _check_device(dev, workspace, lm_head_weight=lm_head_weight, token_ids=token_ids, w1=w1, w2=w2, out=out)
+    shape = tuple(hidden_states.shape[:-1]) + (V,)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=dev)
+    elif tuple(out.shape) != shape or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous float32 tensor of shape {shape}")
+    if out.numel() == 0:
+        return out
+    h = hidden_states.contiguous()
+    lm = lm_head_weight.contiguous()
+    ids = token_ids.to(torch.int64).contiguous()
+    w1c, w2c = w1.contiguous(), w2.contiguous()
+    if workspace is None:
+        workspace = Workspace(B, M, V, r, sample=False, device=dev)
+    st = _lib.load().dspark_markov_apply_block_lm_head(
+        _ptr(h), _dtype_tag(h), d, _ptr(lm), _dtype_tag(lm), _ptr(ids), _ptr(w1c), _ptr(w2c), _dtype_tag(w1c),
+        B, M, V, r, _ptr(out), workspace.ptr, workspace.nbytes, _stream_handle(dev))
+    _lib.check(st, "apply_block_logits_lm_head")
+    return out
 
 
 def _check_device(dev: torch.device, workspace: "Workspace | None" = None, **tensors):

@@ -40,6 +40,7 @@ EXPORTS = (
     "dspark_markov_sample_block_gated",
     "dspark_markov_backward_workspace_bytes",
     "dspark_markov_apply_block_backward",
+    "dspark_markov_apply_block_lm_head",
     "dspark_markov_read_device_error",
     "dspark_status_string",
     "dspark_markov_last_error",
@@ -98,6 +99,9 @@ def load():
     L.dspark_markov_backward_workspace_bytes.restype = sz
     L.dspark_markov_apply_block_backward.argtypes = [p, i32, p, p, p, i32, i64, i64, i64, i64, p, p, p, sz, p]
     L.dspark_markov_apply_block_backward.restype = i32
+    L.dspark_markov_apply_block_lm_head.argtypes = [p, i32, i64, p, i32, p, p, p, i32, i64, i64, i64, i64, p, p,
+                                                    sz, p]
+    L.dspark_markov_apply_block_lm_head.restype = i32
     L.dspark_markov_read_device_error.argtypes = [p, p, ctypes.POINTER(i64)]
     L.dspark_markov_read_device_error.restype = i32
     L.dspark_status_string.argtypes = [i32]

@@ -666,6 +666,62 @@ dspark_status_t dspark_markov_apply_block_backward(const void* grad_corrected, d
   return DSPARK_OK;
 }
 
+dspark_status_t dspark_markov_apply_block_lm_head(const void* hidden_states, dspark_dtype_t hidden_dtype, int64_t d,
+                                                  const void* lm_head_weight, dspark_dtype_t lm_head_dtype,
+                                                  const int64_t* token_ids, const void* w1, const void* w2,
+                                                  dspark_dtype_t weight_dtype, int64_t B, int64_t M, int64_t V,
+                                                  int64_t r, float* corrected_logits, void* workspace,
+                                                  size_t workspace_bytes, void* stream) {
+  if (!known_dtype(hidden_dtype) || !known_dtype(lm_head_dtype) || !known_dtype(weight_dtype))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  if (B < 0 || M < 0 || V < 0 || r <= 0 || d <= 0) return DSPARK_ERR_INVALID_ARGUMENT;
+  int64_t rows = 0, elems = 0, t = 0;
+  if (!mul_ok(B, M, &rows) || !mul_ok(rows, V, &elems) || !mul_ok(V, r, &t) || !mul_ok(V, d, &t) ||
+      !mul_ok(rows, d, &t))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  if (elems == 0) return DSPARK_OK;
+  if (!hidden_states || !lm_head_weight || !token_ids || !w1 || !w2 || !corrected_logits)
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < dspark_markov_workspace_bytes(B, M, V, r, 0))
+    return DSPARK_ERR_WORKSPACE_TOO_SMALL;
+  const size_t obytes = (size_t)elems * 4;
+  const void* ins[5] = {hidden_states, lm_head_weight, token_ids, w1, w2};
+  const size_t ins_bytes[5] = {(size_t)(rows * d) * dtype_bytes(hidden_dtype), (size_t)(V * d) * dtype_bytes(lm_head_dtype),
+                               (size_t)rows * sizeof(int64_t), (size_t)(V * r) * dtype_bytes(weight_dtype),
+                               (size_t)(V * r) * dtype_bytes(weight_dtype)};
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(corrected_logits, obytes, ins[i], ins_bytes[i])) return DSPARK_ERR_INVALID_ARGUMENT;
+  // the matrix-core kernel takes bf16 operands, sizes in multiples of 8 and
+  // 16-byte aligned buffers
+  if (hidden_dtype != DSPARK_BF16 || lm_head_dtype != DSPARK_BF16 || weight_dtype != DSPARK_BF16 || d % 8 ||
+      r % 8 || V % 8 || !aligned16(hidden_states) || !aligned16(lm_head_weight) || !aligned16(w1) ||
+      !aligned16(w2) || !aligned16(corrected_logits)) {
+    g_last_error = "apply_block_lm_head: bf16 hidden states, head and Markov weights, d, r and V multiples of 8 "
+                   "and 16-byte aligned buffers";
+    return DSPARK_ERR_UNSUPPORTED;
+  }
+  dspark::LmHeadParams p{};
+  p.hidden = hidden_states;
+  p.lm = lm_head_weight;
+  p.ids = token_ids;
+  p.w1 = w1;
+  p.w2 = w2;
+  p.out = corrected_logits;
+  p.bad_rows = &((Control*)workspace)->bad_rows;
+  p.rows = rows;
+  p.V = V;
+  p.r = r;
+  p.d = d;
+  const hipError_t e = dspark::launch_lm_head(p, device_cus(), (hipStream_t)stream);
+  if (e == hipErrorNotSupported) {
+    (void)hipGetLastError();
+    g_last_error = "apply_block_lm_head: every buffer must fit in 2^31 bytes";
+    return DSPARK_ERR_UNSUPPORTED;
+  }
+  if (e != hipSuccess) return device_failure(e, "lm head launch");
+  return DSPARK_OK;
+}
+
 dspark_status_t dspark_markov_read_device_error(void* workspace, void* stream, int64_t* bad_rows) {
   if (!workspace || !bad_rows) return DSPARK_ERR_INVALID_ARGUMENT;
   hipStream_t s = (hipStream_t)stream;

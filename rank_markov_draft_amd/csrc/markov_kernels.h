@@ -48,6 +48,23 @@ struct KernelParams {
 
 
 
+// The vocabulary head fused with the bias (bf16 operands, fp32 output):
+// out[n, v] = fp32(hidden[n] . lm[v] + fp32(rnd_bf16(W1[ids[n]] . W2w[v]))).
+struct LmHeadParams {
+  const void* hidden;  // [rows, d] bf16
+  const void* lm;      // [V, d] bf16 (the head's Linear weight)
+  const int64_t* ids;  // [rows] predecessors
+  const void* w1;      // [V, r] bf16
+  const void* w2;      // [V, r] bf16
+  float* out;          // [rows, V] fp32
+  uint32_t* bad_rows;  // device error word
+  int64_t rows;
+  int64_t V;
+  int64_t r;
+  int64_t d;
+};
+hipError_t launch_lm_head(const LmHeadParams& p, int num_cus, hipStream_t s);
+
 // The gate of the gated head, one launch per call (apply) or per step
 // (sampling): the latent rows u = rnd_W(rnd_W(sigmoid(rnd_W(z + b))) * e),
 // z = gate_proj's product with [h; e], e = W1[predecessor] (zero for

@@ -48,6 +48,7 @@ class Workload:
     return_logits: bool = True
     logits_dtype: int = -1  # the logits' dtype when it differs from the weights' (-1: same)
     hidden: int = 0         # gated head: backbone hidden size d (0: vanilla head)
+    lm_head: int = 0        # fused vocabulary head: hidden size d (0: base logits given)
 
     @property
     def ldtype(self) -> int:
@@ -108,6 +109,10 @@ WORKLOADS = {
     "teacher_forced_320_backward": Workload("teacher_forced_320_backward", B=64, M=5, V=129280, r=256,
                                             dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=8,
                                             mode="backward"),
+    # The drafter's FP32 vocabulary head fused with the teacher-forced bias:
+    # the 320-row batch from hidden states of size 5120 (DeepSeek-V4.1).
+    "lm_head_teacher_forced_320": Workload("lm_head_teacher_forced_320", B=64, M=5, V=129280, r=256, dtype=BF16,
+                                           base_sigma=2.0, w_sigma=0.02, seed=9, mode="apply", lm_head=5120),
     # Large teacher-forced batch: 8 sequences x 64 anchors, rank 512, Zipf ids.
     "teacher_forced_2560_zipf": Workload("teacher_forced_2560_zipf", B=512, M=5, V=129280, r=512,
                                          dtype=BF16, base_sigma=2.0, w_sigma=0.02, seed=5,
@@ -136,7 +141,7 @@ def zipf_ids(rng: np.random.Generator, n: int, V: int, s: float) -> np.ndarray:
 
 def make_inputs(w: Workload, *, B: int | None = None, M: int | None = None,
                 V: int | None = None, r: int | None = None, seed: int | None = None,
-                hidden: int | None = None):
+                hidden: int | None = None, lm_head: int | None = None):
     """Draw inputs for workload ``w`` (optionally at other sizes).
 
     Returns a dict of numpy arrays: base [B, M, V], w1 [V, r], w2 [V, r]
@@ -145,13 +150,17 @@ def make_inputs(w: Workload, *, B: int | None = None, M: int | None = None,
     (a normalised backbone state) and the gate_proj weight [r, d + r] and
     bias [r], both U(-1/sqrt(d + r), 1/sqrt(d + r)) (nn.Linear's default
     initialisation), drawn after everything else in that order, in the
-    weight dtype.
+    weight dtype.  With a fused vocabulary head (lm_head = d) it holds
+    lm_hidden [B, M, d] ~ N(0, 1) and lm_head [V, d] ~ N(0, 0.02^2), bf16,
+    drawn last.
     """
     B = w.B if B is None else B
     M = w.M if M is None else M
     V = w.V if V is None else V
     r = w.r if r is None else r
     d = w.hidden if hidden is None else hidden
+    if lm_head is not None:
+        w = dataclasses.replace(w, lm_head=lm_head)
     rng = np.random.default_rng(w.seed if seed is None else seed)
     base = rng.standard_normal((B, M, V), dtype=np.float32) * np.float32(w.base_sigma)
     if w.boost and B * M > 0 and V > 0:
@@ -179,6 +188,16 @@ def make_inputs(w: Workload, *, B: int | None = None, M: int | None = None,
         if w.dtype == BF16:
             hid, gw, gb = to_bf16_bits(hid), to_bf16_bits(gw), to_bf16_bits(gb)
         out.update(hidden=hid, gate_w=gw, gate_b=gb)
+    if w.lm_head:
+        # fused head: hidden states N(0, 1) [B, M, d] and the head's weight
+        # [V, d] ~ N(0, 0.02^2) (initializer_range), bf16, drawn last
+        dl = w.lm_head
+        hs = rng.standard_normal((B, M, dl), dtype=np.float32)
+        lw = np.empty((V, dl), dtype=np.uint16)
+        for v0 in range(0, V, 8192):   # in slices: the fp32 draw of the whole head is 2.6 GB
+            v1 = min(V, v0 + 8192)
+            lw[v0:v1] = to_bf16_bits(rng.standard_normal((v1 - v0, dl), dtype=np.float32) * np.float32(w.w_sigma))
+        out.update(lm_hidden=to_bf16_bits(hs), lm_head=lw)
     if w.ldtype == BF16:
         base = to_bf16_bits(base)
     if w.dtype == BF16:

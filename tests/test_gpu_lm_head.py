@@ -1,0 +1,109 @@
+"""GPU parity of the vocabulary head fused with the teacher-forced bias
+(dspark_markov_apply_block_lm_head) against the oracle, through the C ABI.
+
+Rule (fp32 output): each element is bit-identical to the oracle, or within
+1e-5 relative of it (floor 1e-2), or inside the oracle's admissible
+interval for fp32 accumulation of both products in any order."""
+import dataclasses
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import rank_markov_draft_amd as rmd
+from oracle import oracle as orc
+from rank_markov_draft_amd import _lib
+from rank_markov_draft_amd import workloads as wl
+from tests.gpu_util import from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+REPORT = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out",
+                      "parity_report.txt")
+
+
+def _run(inp, ws=None):
+    d = {k: to_dev(inp[k]) for k in ("lm_hidden", "lm_head", "token_ids", "w1", "w2")}
+    out = rmd.apply_block_logits_lm_head(d["lm_hidden"], d["lm_head"], d["token_ids"], d["w1"], d["w2"],
+                                         workspace=ws)
+    torch.cuda.synchronize()
+    return from_dev(out)
+
+
+def _check(inp, gpu, name):
+    V = inp["w1"].shape[0]
+    ids = inp["token_ids"].reshape(-1)
+    ref = orc.apply_block_lm_head(inp["lm_hidden"], inp["lm_head"], inp["token_ids"], inp["w1"], inp["w2"])
+    g = gpu.reshape(-1, V)
+    o = ref.reshape(-1, V)
+    exact = g.view(np.uint32) == o.view(np.uint32)
+    tol = np.abs(g.astype(np.float64) - o) <= 1e-5 * np.maximum(np.abs(o.astype(np.float64)), 1e-2)
+    rr, cc = np.nonzero(~exact & ~tol)
+    if rr.size:
+        lo, mid, hi = orc.lm_head_bounds(inp["lm_hidden"].reshape(-1, inp["lm_hidden"].shape[-1]), inp["lm_head"],
+                                         ids, inp["w1"], inp["w2"], rr, cc)
+        assert np.array_equal(mid, o[rr, cc])
+        gv = g[rr, cc]
+        inside = (lo <= gv) & (gv <= hi)
+        assert inside.all(), (f"{int((~inside).sum())} of {g.size} fused logits outside the interval; first at "
+                              f"{rr[~inside][0]}, {cc[~inside][0]}")
+    line = (f"[parity] {name}: elements={g.size}, exact={int(exact.sum())}, within_1e-5={int((tol & ~exact).sum())}, "
+            f"interval_only={int(rr.size)}, max_abs_diff={float(np.max(np.abs(g - o))) if g.size else 0.0}")
+    print(line)
+    os.makedirs(os.path.dirname(REPORT), exist_ok=True)
+    with open(REPORT, "a") as f:
+        f.write(line + "\n")
+    return rr.size
+
+
+def test_lm_head_teacher_forced_320(native):
+    """The 320-row batch at V = 129280, r = 256, d = 5120, every element."""
+    w = wl.WORKLOADS["lm_head_teacher_forced_320"]
+    inp = wl.make_inputs(w)
+    print(f"[lm head] full size rows={w.rows} V={w.V} d={w.lm_head}", flush=True)
+    _check(inp, _run(inp), w.name)
+
+
+@pytest.mark.parametrize("B,M,V,r,d", [
+    (1, 37, 1000, 40, 1032),      # part of a row band and of a column tile; d and r not multiples of 32
+    (7, 100, 2048, 256, 256),     # 700 rows: three row bands
+    (2, 3, 8, 8, 8),              # the smallest shape
+    (4, 80, 4096, 512, 64),       # rank past the head's inner size
+])
+def test_lm_head_shapes(native, B, M, V, r, d):
+    w = wl.WORKLOADS["lm_head_teacher_forced_320"]
+    inp = wl.make_inputs(w, B=B, M=M, V=V, r=r, lm_head=d, seed=B * 7 + V)
+    _check(inp, _run(inp), f"lm head B{B} M{M} V{V} r{r} d{d}")
+
+
+def test_lm_head_zero_markov_weights_and_bad_ids(native):
+    """W2 = 0 gives the plain FP32 head; out-of-range ids give a zero bias and
+    are counted."""
+    w = wl.WORKLOADS["lm_head_teacher_forced_320"]
+    inp = wl.make_inputs(w, B=3, M=4, V=1024, r=64, lm_head=512, seed=3)
+    inp["w2"] = np.zeros_like(inp["w2"])
+    _check(inp, _run(inp), "lm head W2=0")
+    inp = wl.make_inputs(w, B=3, M=4, V=1024, r=64, lm_head=512, seed=4)
+    ids = inp["token_ids"].copy()
+    ids[0, 1] = -1
+    ids[2, 3] = 1024
+    ws = rmd.Workspace(3, 4, 1024, 64, sample=False)
+    gpu = _run(dict(inp, token_ids=ids), ws)
+    assert rmd.read_device_error(ws) == 2
+    good = dict(inp, token_ids=np.where((ids >= 0) & (ids < 1024), ids, 0))
+    ref_plain = orc.apply_block_lm_head(inp["lm_hidden"], inp["lm_head"], good["token_ids"],
+                                        inp["w1"], np.zeros_like(inp["w2"]))
+    for (b, k) in ((0, 1), (2, 3)):     # bad rows: the plain head within the interval of a zero bias
+        g, o = gpu[b, k], ref_plain[b, k]
+        assert np.all(np.abs(g - o) <= 1e-5 * np.maximum(np.abs(o), 1e-2) + 1e-4)
+
+
+def test_lm_head_rejects_what_it_does_not_take(native):
+    w = wl.WORKLOADS["lm_head_teacher_forced_320"]
+    inp = wl.make_inputs(w, B=1, M=2, V=64, r=8, lm_head=16, seed=1)
+    d = {k: to_dev(inp[k]) for k in ("lm_hidden", "lm_head", "token_ids", "w1", "w2")}
+    with pytest.raises(_lib.DsparkError, match="UNSUPPORTED"):
+        rmd.apply_block_logits_lm_head(d["lm_hidden"].float(), d["lm_head"], d["token_ids"], d["w1"], d["w2"])
+    out = rmd.apply_block_logits_lm_head(d["lm_hidden"][:, :0], d["lm_head"], d["token_ids"][:, :0], d["w1"], d["w2"])
+    assert out.shape == (1, 0, 64)
