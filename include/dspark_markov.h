@@ -48,8 +48,10 @@
  * Workspace. Device memory of at least dspark_markov_workspace_bytes(...)
  *           bytes, zero-filled once before its first use (for instance by
  *           dspark_markov_workspace_init); the library leaves it ready for
- *           the next call.  Calls that share one workspace must be ordered
- *           on one stream; calls in flight at the same time need their own.
+ *           the next call, of any shape and operation that fits it (every
+ *           call uses one layout).  Calls that share one workspace must be
+ *           ordered on one stream; calls in flight at the same time need
+ *           their own.
  */
 #ifndef DSPARK_MARKOV_H
 #define DSPARK_MARKOV_H
@@ -125,7 +127,7 @@ dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_
  *                        split across calls, reproduce one whole call.
  * M == 0 or B == 0 is a successful no-op.  V == 0 with B*M > 0 is invalid.
  *
- * Greedy bf16 calls with B <= 64 and r <= 256 run as one persistent launch
+ * Greedy bf16 calls with B <= 64, M <= 16 and r <= 256 run as one persistent launch
  * whose workgroups (one per CU) exchange each step's tokens through the
  * workspace; the host takes that path only when the occupancy query says a
  * CU can hold one of its workgroups.  Should a workgroup still be unable to
@@ -155,7 +157,7 @@ dspark_status_t dspark_markov_sample_block(const void* base_logits, dspark_dtype
  * dspark_markov_workspace_bytes(B, M, V, r, 1) exceeds that are rejected
  * with DSPARK_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (the
  * message names both sizes); for instance B = 64, M = 5 at V = 129280 needs
- * 0.7 MB and B = 256, M = 8 at V = 151936 needs 2.7 MB.  Nothing is
+ * 1.1 MB and B = 256, M = 8 at V = 151936 needs 3.0 MB.  Nothing is
  * allocated: the first call on a device zero-fills its scratch with a
  * kernel on `stream`, and every call clears the scratch's error words
  * first, so out-of-range ids are not counted and a failed persistent chain

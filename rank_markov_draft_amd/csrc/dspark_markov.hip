@@ -15,17 +15,26 @@ namespace {
 
 thread_local std::string g_last_error;
 
-// Workspace layout:
+// Workspace layout (the same for every call, so calls of different shapes
+// may share a workspace):
 //   [0, 256)      control block: the device error word, the
 //                 synchronisation-failure count of the persistent chain and
 //                 its test hook, each on its own 64-byte line;
-//   partials      per-(row, vocabulary slice) argmax keys of one sampling
-//                 step (step-by-step path), B * ceil(V/128) words;
-//   chain sync    arrival counters and release words of the persistent
-//                 chain (kChainSyncBytes);
-//   keys          device-wide argmax keys of the persistent chain, per
-//                 (step, key group, row): M * 8 * 64 * kKeyPad words.
+//   chain area    arrival counters (kChainSyncBytes), then the device-wide
+//                 argmax keys per (step, key group, row) for up to
+//                 kChainMaxSteps steps.  Only the persistent chain writes
+//                 here, and it leaves the area zeroed: its keys and counters
+//                 must start at zero, so no other path may put data in it;
+//   data          from kDataOffset: the apply kernels' store sink, or the
+//                 sampling steps' per-(row, vocabulary slice) argmax keys
+//                 (B * ceil(V/128) words), or the backward's and the gated
+//                 head's scratch.
 constexpr size_t kControlBytes = 256;
+constexpr int64_t kChainMaxSteps = 16;
+constexpr size_t kChainAreaBytes =
+    dspark::kChainSyncBytes + (size_t)kChainMaxSteps * 8 * 64 * dspark::kKeyPad * sizeof(uint64_t);
+constexpr size_t kDataOffset = kControlBytes + kChainAreaBytes;
+static_assert(kDataOffset % 256 == 0, "data region alignment");
 
 struct Control {
   uint32_t bad_rows;       // byte 0: rows with out-of-range ids
@@ -50,13 +59,7 @@ size_t mul_sz(size_t a, size_t b) {
 size_t align256(size_t x) { return x > SIZE_MAX - 255 ? SIZE_MAX : (x + 255) & ~(size_t)255; }
 
 size_t partials_bytes(int64_t B, int64_t V) {
-  return align256(mul_sz(mul_sz((size_t)B, (size_t)((V + 127) / 128)), sizeof(uint64_t)));
-}
-
-size_t chain_keys_bytes(int64_t M) {
-  return add_sz(dspark::kChainSyncBytes,
-                mul_sz((size_t)M, (size_t)dspark::chain_key_groups() * (size_t)dspark::chain_max_rows() *
-                                      dspark::kKeyPad * sizeof(uint64_t)));
+  return align256(mul_sz(mul_sz((size_t)B, (size_t)(V / 128 + (V % 128 != 0))), sizeof(uint64_t)));
 }
 
 // Compute units of the current device, cached per device.
@@ -181,9 +184,14 @@ extern "C" {
 
 size_t dspark_markov_workspace_bytes(int64_t B, int64_t M, int64_t V, int64_t r, int sample_mode) {
   (void)r;
-  if (B < 0 || V < 0 || M < 0) return kControlBytes;
-  if (sample_mode) return add_sz(add_sz(kControlBytes, partials_bytes(B, V)), chain_keys_bytes(M));
-  return kControlBytes + dspark::apply_sink_bytes();
+  if (B < 0 || V < 0 || M < 0) return kDataOffset;
+  // a sampling workspace also serves the apply of the same sizes
+  const size_t sink = dspark::apply_sink_bytes();
+  if (sample_mode) {
+    const size_t parts = partials_bytes(B, V);
+    return add_sz(kDataOffset, parts > sink ? parts : sink);
+  }
+  return kDataOffset + sink;
 }
 
 dspark_status_t dspark_markov_workspace_init(void* workspace, size_t bytes, void* stream) {
@@ -233,7 +241,7 @@ dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_
   const bool f32_tile = tile_path(DSPARK_BF16, weight_dtype, V, r, base_logits, corrected_logits, w1, w2) &&
                         logits_dtype == DSPARK_F32;
   if (!tile && !f32_tile && r > kGenericMaxRank) return DSPARK_ERR_UNSUPPORTED;
-  p.sink = (char*)workspace + kControlBytes;
+  p.sink = (char*)workspace + kDataOffset;
   e = hipErrorNotSupported;
   if (f32_tile) {
     e = dspark::launch_apply_grouped(p, true, (hipStream_t)stream);
@@ -312,7 +320,7 @@ dspark_status_t sample_block_impl(const void* base_logits, dspark_dtype_t logits
   p.w1 = w1;
   p.w2 = w2;
   p.bad_rows = &((Control*)workspace)->bad_rows;
-  p.partials = (uint64_t*)((char*)workspace + kControlBytes);
+  p.partials = (uint64_t*)((char*)workspace + kDataOffset);
   p.rows = B;
   p.V = V;
   p.r = r;
@@ -333,7 +341,7 @@ dspark_status_t sample_block_impl(const void* base_logits, dspark_dtype_t logits
 
   // Greedy bf16 chains that fit the persistent kernel run in one launch.
   const int cus = device_cus();
-  if (tile && greedy && cus > 0 && B <= dspark::chain_max_rows() &&
+  if (tile && greedy && cus > 0 && B <= dspark::chain_max_rows() && M <= kChainMaxSteps &&
       (V + 31) / 32 <= (int64_t)cus * dspark::chain_waves_per_group()) {
     dspark::ChainParams c{};
     c.base = (const uint16_t*)base_logits;
@@ -342,7 +350,7 @@ dspark_status_t sample_block_impl(const void* base_logits, dspark_dtype_t logits
     c.tokens = sampled_tokens;
     c.w1 = (const uint16_t*)w1;
     c.w2 = (const uint16_t*)w2;
-    c.sync = (uint32_t*)((char*)workspace + kControlBytes + partials_bytes(B, V));
+    c.sync = (uint32_t*)((char*)workspace + kControlBytes);
     c.keys = (uint64_t*)((char*)c.sync + dspark::kChainSyncBytes);
     c.bad_rows = &ctl->bad_rows;
     c.sync_failures = &ctl->sync_failures;
@@ -462,7 +470,7 @@ dspark_status_t dspark_markov_apply_block_gated(
   p.w1 = w1;
   p.w2 = w2;
   p.bad_rows = &((Control*)workspace)->bad_rows;
-  p.sink = (char*)workspace + kControlBytes;
+  p.sink = (char*)workspace + kDataOffset;
   p.latent = latent;
   p.latent_ld = r;
   p.rows = rows;
@@ -558,7 +566,7 @@ dspark_status_t dspark_markov_sample_block_gated(
   p.w1 = w1;
   p.w2 = w2;
   p.bad_rows = &((Control*)workspace)->bad_rows;
-  p.partials = (uint64_t*)((char*)workspace + kControlBytes);
+  p.partials = (uint64_t*)((char*)workspace + kDataOffset);
   p.rows = B;
   p.V = V;
   p.r = r;
@@ -605,14 +613,14 @@ dspark_status_t dspark_markov_sample_block_gated(
 }
 
 size_t dspark_markov_backward_workspace_bytes(int64_t B, int64_t M, int64_t V, int64_t r) {
-  if (B < 0 || M < 0 || V < 0 || r <= 0) return kControlBytes;
+  if (B < 0 || M < 0 || V < 0 || r <= 0) return kDataOffset;
   int64_t rows = 0, rr = 0;
   if (!mul_ok(B, M, &rows) || !mul_ok(rows, r, &rr)) return SIZE_MAX;
   int64_t sl = 0;
   const int64_t S = V > 0 ? dspark::backward_slices(V, &sl) : 0;
   const size_t de = align256(mul_sz((size_t)rr, 4));
   const size_t parts = align256(mul_sz(mul_sz((size_t)S, (size_t)rr), 4));
-  return add_sz(add_sz(add_sz(kControlBytes, de), parts), align256(mul_sz((size_t)rows, 8)));
+  return add_sz(add_sz(add_sz(kDataOffset, de), parts), align256(mul_sz((size_t)rows, 8)));
 }
 
 dspark_status_t dspark_markov_apply_block_backward(const void* grad_corrected, dspark_dtype_t logits_dtype,
@@ -652,7 +660,7 @@ dspark_status_t dspark_markov_apply_block_backward(const void* grad_corrected, d
   p.w2 = w2;
   p.dw1 = grad_w1;
   p.dw2 = grad_w2;
-  char* const region = (char*)workspace + kControlBytes;
+  char* const region = (char*)workspace + kDataOffset;
   p.de = region;
   p.S = dspark::backward_slices(V, &p.SL);
   p.partials = (float*)(region + align256((size_t)(rows * r) * 4));

@@ -35,9 +35,11 @@
 //     1 run at raised issue priority.
 // Every wait on other workgroups is bounded: a workgroup that waits too long
 // records a failure in the workspace and leaves, so no launch can hang.  The
-// last workgroup to leave clears the keys and counters, so the workspace is
-// ready for the next call, and when any wait failed it overwrites every token
-// of the call with -1, so a failed chain never returns plausible tokens.  A
+// last workgroup to leave writes the last step's tokens (every key is in by
+// then, so nobody waits for them), then clears the keys and counters, so the
+// workspace is ready for the next call; when any wait failed it writes -1 to
+// every token of the call instead, so a failed chain never returns plausible
+// tokens.  A
 // launch that finds the failure count already nonzero (a failure nobody has
 // read back and cleared) does no work and also returns -1 tokens.
 #include "device_common.h"
@@ -108,6 +110,29 @@ __device__ bool wait_arrivals(uint32_t* sync, int rg, int lane, uint32_t target)
     __builtin_amdgcn_s_sleep(1);
   }
   return true;
+}
+
+// s_waitcnt vmcnt(n) for a count known only at run time (0..16).
+__device__ __forceinline__ void wait_vmcnt_upto16(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    case 15: wait_vmcnt<15>(); break;
+    default: wait_vmcnt<16>(); break;
+  }
 }
 
 }  // namespace
@@ -274,6 +299,9 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     }
     if (lane == 0) lds_flag = poisoned ? 0 : 1;
   }
+  // Every group's step-0 rows are in before the first window (letting the
+  // later groups' rows arrive during the first windows measured 10 us
+  // slower per call: the windows then wait on loads that compete with W2's).
   wait_vmcnt<0>();
   lds_barrier();
 
@@ -414,16 +442,8 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     // since then issued a store and a load per row.
     if (nbulk > 0 && w + 1 < U && w + 1 >= kRowGroups && real(w + 1)) {
       int later = 0;
-      for (int x = w - 3; x <= w; ++x) later += (x >= 1 && real(x - 1)) ? 1 : 0;
-      switch (later * 2 * nbulk) {
-        case 0: wait_vmcnt<0>(); break;
-        case 2: wait_vmcnt<2>(); break;
-        case 4: wait_vmcnt<4>(); break;
-        case 6: wait_vmcnt<6>(); break;
-        case 8: wait_vmcnt<8>(); break;
-        case 12: wait_vmcnt<12>(); break;
-        default: wait_vmcnt<16>(); break;
-      }
+      for (int x = w - 3; x <= w; ++x) later += (x >= 1 && real(x - 1)) ? 2 * nbulk : 0;
+      wait_vmcnt_upto16(later);
     }
     // wave 1: the gather of unit w+1 (issued this window, before the key
     // slots and the poll) is in LDS before the barrier
@@ -476,14 +496,23 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     }
   }
   if (wave < 2) __builtin_amdgcn_s_setprio(0);
+  wait_vmcnt<0>();
+  lds_barrier();
 
-  // Workgroup 0 writes the last step's tokens once every workgroup has
-  // counted in every group.
-  if (g == 0 && wave == 1 && lds_flag) {
-    const uint32_t target = (uint32_t)M * (uint32_t)G;
-    bool fin = true;
-    for (int gg = 0; gg < NR; ++gg) {
-      fin = fin && !force_timeout && wait_arrivals(sync, gg, lane, target);
+  // Leave.  The last workgroup out (every other one has made its last
+  // publish and count, read its last keys and written its tokens, all
+  // ordered before its exit count) writes the last step's tokens from the
+  // complete keys, then clears the keys and the counters; after a failure
+  // it writes -1 to every token instead.
+  if (tid == 0) lds_flag = (__hip_atomic_fetch_add(exit_counter(sync), 1u, __ATOMIC_ACQ_REL,
+                                                   __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(G - 1)) ? 1 : 0;
+  lds_barrier();
+  if (lds_flag) {
+    const bool failed =
+        poisoned || __hip_atomic_load(p.sync_failures, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+    if (!failed && wave < NR) {
+      // wave gg: group gg's rows, lane (n16, g4) reads key slots 2 g4, 2 g4 + 1 of row n16
+      const int gg = wave;
       const int b = gg * rpg + n16;
       const bool row_ok = n16 < rpg && b < B;
       const uint64_t k0 = row_ok ? __hip_atomic_load((uint64_t*)((unsigned char*)p.keys + key_offset(M - 1, 2 * g4, b)),
@@ -497,25 +526,12 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
       const uint64_t merged = max_u64(b2, (uint64_t)__shfl_xor((long long)b2, 32));
       if (g4 == 0 && row_ok) p.tokens[(uint32_t)(b * M + M - 1)] = key_index(merged);
     }
-    if (!fin && lane == 0) atomicAdd(p.sync_failures, 1u);
-    wait_vmcnt<0>();
-  }
-  wait_vmcnt<0>();
-  lds_barrier();
-
-  // Leave; the last workgroup out clears the keys and the counters (every
-  // other workgroup has passed its last wait and read, and its token writes
-  // and failure counts are ordered before its exit count).
-  if (tid == 0) lds_flag = (__hip_atomic_fetch_add(exit_counter(sync), 1u, __ATOMIC_ACQ_REL,
-                                                   __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(G - 1)) ? 1 : 0;
-  lds_barrier();
-  if (lds_flag) {
+    lds_barrier();  // the last keys are read before they are cleared
     for (int i = tid; i < M * kGroups * kMaxRows; i += kThreads)
       __hip_atomic_store(p.keys + (uint32_t)(i * kKeyPad), (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid < kRowGroups * kGroups + 1)
       __hip_atomic_store(sync + 16 * tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // a failed or refused chain: no token of the call is trustworthy
-    if (__hip_atomic_load(p.sync_failures, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != 0u)
+    if (failed)
       for (int i = tid; i < B * M; i += kThreads) p.tokens[(uint32_t)i] = -1;
   }
 }

@@ -36,12 +36,17 @@ int main(void) {
   }
   /* sizes that cannot be represented: SIZE_MAX, never a wrapped small size */
   if (dspark_markov_workspace_bytes(INT64_MAX / 2, 2, 1 << 20, 512, 1) != SIZE_MAX ||
-      dspark_markov_workspace_bytes(4, INT64_MAX / 2, 1 << 20, 512, 1) != SIZE_MAX ||
+      dspark_markov_workspace_bytes(1 << 20, 2, INT64_MAX, 512, 1) != SIZE_MAX ||
       dspark_markov_gated_workspace_bytes(INT64_MAX / 8, 16, 1 << 20, 512, 1 << 12, 0) != SIZE_MAX ||
       dspark_markov_gated_workspace_bytes(1 << 20, 4, 1 << 20, 512, INT64_MAX / 4, 1) != SIZE_MAX ||
       dspark_markov_backward_workspace_bytes(INT64_MAX / 4, 4, 1 << 20, 512) != SIZE_MAX ||
       dspark_markov_backward_workspace_bytes(1 << 30, 1 << 20, 1 << 20, 512) != SIZE_MAX) {
     fprintf(stderr, "an unrepresentable workspace size did not saturate\n");
+    ++failures;
+  }
+  /* the sampling workspace does not grow with the block length */
+  if (dspark_markov_workspace_bytes(4, INT64_MAX / 2, 1 << 20, 512, 1) != dspark_markov_workspace_bytes(4, 2, 1 << 20, 512, 1)) {
+    fprintf(stderr, "the sampling workspace depends on M\n");
     ++failures;
   }
 

@@ -48,18 +48,22 @@ def _align256(x):
     return (x + 255) // 256 * 256
 
 
-HEAD = 256   # control block
+HEAD = 256                           # control block
+CHAIN = 4096 + 16 * 8 * 64 * 64      # the persistent chain's area: counters, then keys for up to 16 steps
+DATA = HEAD + CHAIN                  # where every call's own data starts
 
 
 def test_workspace_bytes(L):
-    """Apply: the head, then a 16 KB store sink for lanes past the edges.
-    Sample: the head, then step partials (B * ceil(V/128) keys), then the
-    chain's 2 KB synchronisation area and its keys (M steps * 8 groups * 64
-    rows, 64 bytes apart)."""
-    assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 0) == HEAD + 16384
-    chain = lambda M: 4096 + M * 8 * 64 * 64
-    assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 1) == HEAD + _align256(64 * 1010 * 8) + chain(5)
-    assert L.dspark_markov_workspace_bytes(256, 8, 151936, 256, 1) == HEAD + _align256(256 * 1187 * 8) + chain(8)
+    """One layout for every call: the control block, the chain's area (only
+    the chain writes there and leaves it zeroed), then the call's data:
+    apply, a 16 KB store sink for lanes past the edges; sample, the step
+    partials (B * ceil(V/128) keys), at least the sink's size."""
+    assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 0) == DATA + 16384
+    assert L.dspark_markov_workspace_bytes(64, 5, 129280, 256, 1) == DATA + _align256(64 * 1010 * 8)
+    assert L.dspark_markov_workspace_bytes(256, 8, 151936, 256, 1) == DATA + _align256(256 * 1187 * 8)
+    assert DATA % 256 == 0
+    # a sampling workspace holds at least the apply's sink, so it serves the apply too
+    assert L.dspark_markov_workspace_bytes(2, 2, 64, 16, 1) == DATA + 16384
 
 
 FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: every call below fails validation
@@ -101,7 +105,7 @@ def test_apply_null_pointers_and_workspace(L):
     assert L.dspark_markov_apply_block(FAKE, 1, None, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, FAKE, 1 << 20, None) == 1
     assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, None, FAKE, 1 << 20, None) == 1
     assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, None, 1 << 20, None) == 3
-    assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, FAKE, HEAD + 16383, None) == 3
+    assert L.dspark_markov_apply_block(FAKE, 1, FAKE, FAKE, FAKE, 1, 2, 3, 64, 16, FAKE, FAKE, DATA + 16383, None) == 3
 
 
 def test_apply_overlap_rejected(L):
@@ -201,12 +205,13 @@ def test_gated_overlaps_rejected(L):
 
 # ------------------------------------------------------------ backward
 def test_backward_workspace_bytes(L):
-    """Control block, the de rows (4 bytes per element at most), the split
-    sums of the de product over 1024-column slices of V, and two row links."""
+    """The common head (control block and chain area), the de rows (4 bytes
+    per element at most), the split sums of the de product over 1024-column
+    slices of V, and two row links."""
     for B, M, V, r in ((64, 5, 129280, 256), (3, 4, 700, 16), (0, 5, 64, 8)):
         rows = B * M
         S = (V + 1023) // 1024
-        want = 256 + _align256(rows * r * 4) + _align256(S * rows * r * 4) + _align256(rows * 8)
+        want = DATA + _align256(rows * r * 4) + _align256(S * rows * r * 4) + _align256(rows * 8)
         assert L.dspark_markov_backward_workspace_bytes(B, M, V, r) == want
 
 

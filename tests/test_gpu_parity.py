@@ -535,3 +535,36 @@ def test_sample_at_the_step_kernel_row_limit(native, B, T):
     tok, corr = run_sample(inp, T, seed=3)
     rows = np.unique(np.concatenate([np.random.default_rng(B).choice(B, 60, replace=False), [0, B - 1]]))
     check_chain(inp, T, 3, tok, corr, brows=rows, name=f"sample B{B} T{T} at the step kernel's row limit")
+
+
+def test_workspace_shared_across_shapes_and_operations(native):
+    """One workspace serves calls of different shapes and operations in any
+    order (one layout for every call; the chain's area holds nothing else):
+    a temperature step call with more rows and a wider vocabulary, an apply
+    and a backward, then greedy chains, each equal to its result on a fresh
+    workspace."""
+    w = wl.WORKLOADS["greedy_draft_64x5"]
+    big = wl.make_inputs(wl.WORKLOADS["temperature_draft_256x8"], B=96, M=3, V=16384, r=256, seed=31)
+    chain_in = wl.make_inputs(w, B=40, M=4, V=8192, r=256, seed=32)
+    chain2_in = wl.make_inputs(w, B=64, M=7, V=8192, r=256, seed=33)
+    ws = rmd.Workspace(96, 8, 16384, 256, sample=True, backward=True)
+    db = device_inputs({k: big[k] for k in ("base", "first_prev", "token_ids", "w1", "w2")})
+    dc = device_inputs({k: chain_in[k] for k in ("base", "first_prev", "w1", "w2")})
+    dc2 = device_inputs({k: chain2_in[k] for k in ("base", "first_prev", "w1", "w2")})
+
+    def chain(d, workspace=None):
+        tok, corr = rmd.sample_block_tokens(d["base"], d["first_prev"], d["w1"], d["w2"], 0.0, workspace=workspace)
+        torch.cuda.synchronize()
+        return from_dev(tok), from_dev(corr)
+
+    want1, want2 = chain(dc), chain(dc2)
+    rmd.sample_block_tokens(db["base"], db["first_prev"], db["w1"], db["w2"], 0.7, seed=5, workspace=ws)
+    got = chain(dc, ws)
+    assert np.array_equal(got[0], want1[0]) and np.array_equal(got[1], want1[1])
+    rmd.apply_block_logits(db["base"], db["token_ids"], db["w1"], db["w2"], workspace=ws)
+    rmd.apply_block_logits_backward(db["base"], db["token_ids"], db["w1"], db["w2"], workspace=ws)
+    got = chain(dc2, ws)
+    assert np.array_equal(got[0], want2[0]) and np.array_equal(got[1], want2[1])
+    got = chain(dc, ws)
+    assert np.array_equal(got[0], want1[0])
+    assert rmd.read_device_error(ws) == 0
