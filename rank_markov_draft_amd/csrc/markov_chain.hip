@@ -12,27 +12,29 @@
 //     from HBM once per call;
 //   * the batch rows are independent chains.  They are dealt into at most
 //     four row groups of up to 16 (the MFMA N tile), and the workgroup works
-//     through units u = 6k + g (step k of the group in slot g) one per
+//     through units u = 5k + g (step k of the group in slot g) one per
 //     window; slots g >= the number of groups are idle windows.  A group's
 //     next step needs the tokens of its current one from every workgroup, so
-//     each device-wide exchange has five windows of other work to hide in;
+//     each device-wide exchange has the four windows between a group's
+//     units to complete in;
 //   * window w: every wave multiplies group g's gathered W1 rows by its
 //     slice on the matrix cores (v_mfma_f32_16x16x32_bf16), rounds the bias
 //     to bf16, adds it to the group's base logits staged in LDS, writes the
 //     corrected values back in place and folds each row's best column into
 //     a per-row LDS key.  One barrier ends the window;
-//   * everything else is issued at the start of a window and overlaps the
-//     matrix work of the other waves: waves 2..15 send the corrected rows of
-//     unit w-1 to HBM and load the base logits that group needs next
-//     straight into the freed LDS rows, five windows ahead of use, so each
-//     load has five windows to arrive; wave 0 publishes the row keys of unit w-1 (a 64-bit
-//     atomic max per row into one of eight key slots) and counts the
-//     workgroup in for unit w-2, whose atomics it issued a window earlier;
-//     wave 1 checks the arrival counts it polled a window ago for unit w+2's
-//     previous step, loads those key slots into LDS, merges the slots it
-//     loaded a window ago into the tokens of unit w+1, gathers their W1
-//     rows (in LDS before the barrier) and polls for unit w+3.  Waves 0 and
-//     1 run at raised issue priority.
+//   * the memory traffic is issued around the matrix work and overlaps that
+//     of the other waves: waves 2..15 send the corrected rows of unit w-1 to
+//     HBM and load the base logits that group needs next straight into the
+//     freed LDS rows, four windows ahead of use; waves 0 and 1 run the
+//     exchange, taking turns in two roles so that each waits on its own
+//     memory counter only for what it issued.  One of them merges the key
+//     slots of unit w+1 into tokens, gathers their W1 rows (in LDS before
+//     the barrier), publishes the row keys of unit w-1 (a 64-bit atomic max
+//     per row into one of eight key slots) and, after its matrix work,
+//     counts the workgroup in for unit w-1; the other polls the arrival
+//     counts of unit w+2's previous step and, after its matrix work, loads
+//     those key slots into LDS, to merge them itself in the next window.
+//     Waves 0 and 1 run at raised issue priority.
 // Every wait on other workgroups is bounded: a workgroup that waits too long
 // records a failure in the workspace and leaves, so no launch can hang.  The
 // last workgroup to leave writes the last step's tokens (every key is in by
@@ -51,22 +53,25 @@ namespace {
 
 constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowGroups = 6;                 // pipeline slots per step (row groups + idle slots)
+// Pipeline slots per step: row groups plus idle slots.  A group's steps are
+// kSlots windows apart; four (no idle slot for 64 rows) left too little time
+// for the exchange (measured: the polls then wait on the slowest workgroup).
+constexpr int kSlots = 5;
 constexpr int kMaxGroups = 4;                 // row groups of a call at most
 constexpr int kGroupRows = 16;                // rows of a group at most (the MFMA N tile)
 constexpr int kMaxRows = 64;                  // batch rows of one call
 constexpr int kGroups = 8;                    // key slots / arrival counters per row group
 constexpr int kPitch = 2 * 32 * kWaves + 16;  // LDS bytes of a staged row (512 columns + pad)
 constexpr uint64_t kSpinTicks = 100000000;    // 1 s of the 100 MHz realtime clock
-static_assert(kMaxGroups * kGroupRows >= kMaxRows && kMaxGroups <= kRowGroups, "row groups");
+static_assert(kMaxGroups * kGroupRows >= kMaxRows && kMaxGroups <= kSlots, "row groups");
 
 // Synchronisation area, one 64-byte line per word: the arrival counters
-// [kRowGroups][kGroups] (cumulative over steps), then the exit counter.
-static_assert((kRowGroups * kGroups + 1) * 64 <= (int)kChainSyncBytes, "sync area");
+// [kSlots][kGroups] (cumulative over steps), then the exit counter.
+static_assert((kSlots * kGroups + 1) * 64 <= (int)kChainSyncBytes, "sync area");
 __device__ __forceinline__ uint32_t* arrival_counter(uint32_t* sync, int rg, int x) {
   return sync + 16 * (rg * kGroups + x);
 }
-__device__ __forceinline__ uint32_t* exit_counter(uint32_t* sync) { return sync + 16 * (kRowGroups * kGroups); }
+__device__ __forceinline__ uint32_t* exit_counter(uint32_t* sync) { return sync + 16 * (kSlots * kGroups); }
 
 // Byte offset of the key slot of (step k, key group x, row b).
 __device__ __forceinline__ uint32_t key_offset(int k, int x, int b) {
@@ -170,12 +175,12 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   // M <= 4096, so every index below fits in 32 bits.
   const int B = (int)p.B, M = (int)p.M, V = (int)p.V, r = (int)p.r;
   // Rows are dealt into NR <= kMaxGroups groups of rpg <= 16.  A step has
-  // kRowGroups slots; slots NR.. are idle windows that give each group's
-  // exchange time to complete (a group's steps are kRowGroups windows apart).
+  // kSlots slots; slots NR.. are idle windows (a group's steps are kSlots
+  // windows apart, which is the time its exchange has).
   const int NR = (B + kGroupRows - 1) / kGroupRows;
   const int rpg = (B + NR - 1) / NR;
-  const int U = M * kRowGroups;  // windows
-  auto real = [&](int u) __attribute__((always_inline)) { return u % kRowGroups < NR; };
+  const int U = M * kSlots;  // windows
+  auto real = [&](int u) __attribute__((always_inline)) { return u % kSlots < NR; };
   uint32_t* const sync = p.sync;
 
   // The workgroup's columns [vbeg, vend): slices s_begin .. s_end-1.
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   // w - 2 of every group, and waves 2 and 3 also rows 14 and 15.  Waves 0 and
   // 1 run the exchange, so their memory counters hold exchange operations
   // only.  Base rows go straight into LDS (buffer loads to LDS) as soon as a
-  // group's row is flushed, five windows before the group's next unit needs
+  // group's row is flushed, four windows before the group's next unit needs
   // them; a wave waits for them only at the end of the window before that
   // unit.  Offsets of masked-off lanes, rows or steps point past the buffer
   // (see buffer_rsrc), so every instruction is issued unconditionally.
@@ -305,82 +310,77 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   wait_vmcnt<0>();
   lds_barrier();
 
-  bool ok = true;  // wave 1: no exchange wait has timed out
+  bool ok = true;  // this wave's exchange waits have not timed out
   // The exchange's memory operations are few and latency-bound; the bulk
   // traffic fills this CU's memory queue.  Waves 0 and 1 issue first.
   if (wave < 2) __builtin_amdgcn_s_setprio(3);
 
-  // ---- windows.  Window w starts with the exchange and bulk work for
-  // earlier units, which overlaps the matrix work of the other waves, then
-  // computes unit w = 6k + g (step k of group g); one barrier ends it.
+  // Row keys of unit u (lds_key of its group) into this workgroup's key
+  // slots, one 64-bit atomic max per row; the group's next unit reuses
+  // lds_key, so it is cleared here.
+  auto publish = [&](int u) __attribute__((always_inline)) {
+    if (lane < 16) {
+      const int gp = u % kSlots, kp = u / kSlots;
+      const uint32_t kw = lds_key[gp][lane];
+      lds_key[gp][lane] = 0u;
+      const int b = gp * rpg + lane;
+      if (kw != 0u && lane < rpg && b < B) {
+        const uint64_t code = kw >> 16;
+        const uint32_t col = vbeg + (0xFFFFu - (kw & 0xFFFFu));
+        __hip_atomic_fetch_max((uint64_t*)((unsigned char*)p.keys + key_offset(kp, xg, b)),
+                               (code << 32) | (uint64_t)(0xFFFFFFFFu - col), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  };
+  // This workgroup counted in for unit u (its key atomics are complete).
+  auto count_in = [&](int u) __attribute__((always_inline)) {
+    if (lane == 0)
+      __hip_atomic_fetch_add(arrival_counter(sync, u % kSlots, xg), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
+  // ---- windows.  Window w computes unit w = 4k + g (step k of group g).
+  // Waves 0 and 1 take turns in two exchange roles, so that each keeps its
+  // own memory counter over the operations it has to wait for:
+  //   role A (wave (w+1) & 1): merges the key slots of unit w+1 (which it
+  //     loaded a window ago) into tokens and gathers their W1 rows, and
+  //     publishes the row keys of unit w-1; after its matrix work it waits
+  //     for both and counts the workgroup in for unit w-1;
+  //   role B (wave w & 1): polls the arrivals of unit w+2's previous step
+  //     (counted in at the end of the window before), and after its matrix
+  //     work loads that step's key slots, which the same wave merges in the
+  //     next window in role A.
+  // A group's steps are kSlots windows apart: the hand-off of one step
+  // (publish, count in, poll, load keys, merge and gather) takes the windows
+  // between them, with one to spare for the slowest workgroup's count.
   for (int w = 0; w < (poisoned ? 0 : U); ++w) {
-    const int gc = w % kRowGroups;  // slot of unit w (its group when real)
-    int after_gather = 0;           // wave 1
+    const int gc = w % kSlots;  // slot of unit w (its group when real)
+    const bool role_a = wave == ((w + 1) & 1);
+    const bool role_b = wave == (w & 1);
+    const int u1 = w + 1, u2 = w + 2;
+    const bool pub = role_a && w >= 1 && real(w - 1);
+    const bool do1 = role_a && u1 < U && u1 >= kSlots && real(u1);
+    const bool do2 = role_b && ok && u2 < U && u2 >= kSlots && real(u2);
 
     // Bulk rows first: the corrected rows of unit w-1 to HBM, and that
-    // group's next base rows (unit w+5) into the freed LDS rows.  They drain
+    // group's next base rows (unit w+3) into the freed LDS rows.  They drain
     // during the matrix work and the windows after it.
     if (w >= 1 && real(w - 1)) {
-      const int gp = (w - 1) % kRowGroups, kp = (w - 1) / kRowGroups;
+      const int gp = (w - 1) % kSlots, kp = (w - 1) / kSlots;
       if (nbulk >= 1) flush_row(gp, kp, brow0);
       if (nbulk >= 2) flush_row(gp, kp, brow1);
     }
 
-    if (wave == 0) {
-      // count this workgroup in for unit w-2 (its key atomics were issued a
-      // window ago), then publish the row keys of unit w-1
+    if (role_a) {
+      // the key slots of unit w+1 are in LDS; the gather first: its round
+      // trip has the rest of the window
       wait_vmcnt<0>();
-      if (w >= 2 && real(w - 2) && lane == 0)
-        __hip_atomic_fetch_add(arrival_counter(sync, (w - 2) % kRowGroups, xg), 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-      if (w >= 1 && real(w - 1) && lane < 16) {
-        const int gp = (w - 1) % kRowGroups, kp = (w - 1) / kRowGroups;
-        const uint32_t kw = lds_key[gp][lane];
-        lds_key[gp][lane] = 0u;
-        const int b = gp * rpg + lane;
-        if (kw != 0u && lane < rpg && b < B) {
-          const uint64_t code = kw >> 16;
-          const uint32_t col = vbeg + (0xFFFFu - (kw & 0xFFFFu));
-          __hip_atomic_fetch_max((uint64_t*)((unsigned char*)p.keys + key_offset(kp, xg, b)),
-                                 (code << 32) | (uint64_t)(0xFFFFFFFFu - col), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-    } else if (wave == 1) {
-      // Targets: unit w+2 (poll issued a window ago; key slots) and unit w+1
-      // (key slots loaded a window ago; merge and gather).  The wait below
-      // completes the poll and key slots issued a window ago (the two bulk
-      // operations just issued may stay in flight).
-      const int u2 = w + 2, u1 = w + 1, u3 = w + 3;
-      const bool do2 = ok && u2 < U && u2 >= kRowGroups && real(u2);
-      const bool do1 = u1 < U && u1 >= kRowGroups && real(u1);
-      const bool do3 = u3 < U && u3 >= kRowGroups && real(u3);
-      wait_vmcnt<0>();
-      // the gather first: its round trip has the rest of the window
-      if (do1) gather(u1 % kRowGroups, merge(u1 & 1, u1 % kRowGroups, u1 / kRowGroups - 1));
-      if (do2) {
-        // complete when every workgroup has counted in unit u2 - kRowGroups
-        const uint32_t target = (uint32_t)(u2 / kRowGroups) * (uint32_t)G;
-        // lane x < kGroups reads counter x; the sum goes through scalar registers
-        const uint32_t cx = lane < kGroups ? *(const uint32_t*)&lds_poll[lane * 16] : 0u;
-        uint32_t seen = 0;
-#pragma unroll
-        for (int x = 0; x < kGroups; ++x) seen += (uint32_t)__builtin_amdgcn_readlane((int)cx, x);
-        if (force_timeout) ok = false;
-        else if (seen < target) ok = wait_arrivals(sync, u2 % kRowGroups, lane, target);
-      }
-      if (do2 && ok) load_keys(u2 & 1, u2 % kRowGroups, u2 / kRowGroups - 1);
-      // poll the arrivals of unit w+3's previous step into LDS (lane
-      // l < kGroups loads counter line l)
-      if (do3 && ok)
-        load_lds16_coherent(bw_sync, lane < kGroups ? (uint32_t)(4 * 16 * ((u3 % kRowGroups) * kGroups + lane)) : kBufferOob,
-                            lds_address(&lds_poll[0]));
-      // operations issued after the gather (waited for before the barrier)
-      after_gather = (do2 && ok ? 2 : 0) + (do3 && ok ? 1 : 0);
-      if (!ok && lane == 0) {
-        atomicAdd(p.sync_failures, 1u);
-        lds_flag = 0;
-      }
+      if (do1) gather(u1 % kSlots, merge(u1 & 1, u1 % kSlots, u1 / kSlots - 1));
+      if (pub) publish(w - 1);
+    } else if (do2) {
+      // lane l < kGroups loads counter line l of unit w+2's slot
+      load_lds16_coherent(bw_sync, lane < kGroups ? (uint32_t)(4 * 16 * ((u2 % kSlots) * kGroups + lane)) : kBufferOob,
+                          lds_address(&lds_poll[0]));
     }
 
     // -- unit w: bias of the wave's slice for the group's rows, added to the
@@ -388,11 +388,18 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     if (has && real(w)) {
       f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{};
       const unsigned char* eb = &lds_e[gc][lane * 16];
+      constexpr int KB = (K32 < 4) ? K32 : 4;
 #pragma unroll
-      for (int kk = 0; kk < K32; ++kk) {
-        const bf16x8_t bop = *(const bf16x8_t*)(eb + kk * 1024);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0][kk], bop, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1][kk], bop, acc1, 0, 0, 0);
+      for (int k0 = 0; k0 < K32; k0 += KB) {
+        bf16x8_t bop[KB];
+#pragma unroll
+        for (int i = 0; i < KB; ++i) bop[i] = *(const bf16x8_t*)(eb + (k0 + i) * 1024);
+        __builtin_amdgcn_sched_barrier(0);  // the reads ahead of the products (one LDS round trip per KB blocks)
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0][k0 + i], bop[i], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1][k0 + i], bop[i], acc1, 0, 0, 0);
+        }
       }
       const int colw = wave * 32 + 8 * g4;  // first of the lane's 8 columns in the workgroup
       // lanes of padding rows (past the group's rows or the batch) stay idle:
@@ -437,62 +444,53 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
         if (vbeg + (uint32_t)colw < vend) atomicMax(&lds_key[gc][n16], key);
       }
     }
-    // bulk waves: the base rows of unit w+1 (loaded at window w-4, when unit
-    // w-5 was flushed) are in LDS before the barrier.  Each flush window
-    // since then issued a store and a load per row.
-    if (nbulk > 0 && w + 1 < U && w + 1 >= kRowGroups && real(w + 1)) {
-      int later = 0;
-      for (int x = w - 3; x <= w; ++x) later += (x >= 1 && real(x - 1)) ? 2 * nbulk : 0;
-      wait_vmcnt_upto16(later);
-    }
-    // wave 1: the gather of unit w+1 (issued this window, before the key
-    // slots and the poll) is in LDS before the barrier
-    if (wave == 1) {
-      switch (after_gather) {
-        case 5: wait_vmcnt<5>(); break;
-        case 4: wait_vmcnt<4>(); break;
-        case 3: wait_vmcnt<3>(); break;
-        case 2: wait_vmcnt<2>(); break;
-        case 1: wait_vmcnt<1>(); break;
-        default: wait_vmcnt<0>(); break;
+
+    if (role_a) {
+      // the key atomics of unit w-1 and the gather of unit w+1 are complete
+      wait_vmcnt<0>();
+      if (pub) count_in(w - 1);
+    } else if (do2) {
+      // complete when every workgroup has counted in unit w+2 - kSlots
+      wait_vmcnt<0>();
+      const uint32_t target = (uint32_t)(u2 / kSlots) * (uint32_t)G;
+      // lane x < kGroups reads counter x; the sum goes through scalar registers
+      const uint32_t cx = lane < kGroups ? *(const uint32_t*)&lds_poll[lane * 16] : 0u;
+      uint32_t seen = 0;
+#pragma unroll
+      for (int x = 0; x < kGroups; ++x) seen += (uint32_t)__builtin_amdgcn_readlane((int)cx, x);
+      if (force_timeout) ok = false;
+      else if (seen < target) ok = wait_arrivals(sync, u2 % kSlots, lane, target);
+      // the key slots arrive during the next window
+      if (ok) load_keys(u2 & 1, u2 % kSlots, u2 / kSlots - 1);
+      else if (lane == 0) {
+        atomicAdd(p.sync_failures, 1u);
+        lds_flag = 0;
       }
+    }
+    // bulk waves: the base rows of unit w+1 (loaded at window w-3, when unit
+    // w-4 was flushed) are in LDS before the barrier.  Each flush window
+    // since then issued a store and a load per row.
+    if (nbulk > 0 && w + 1 < U && w + 1 >= kSlots && real(w + 1)) {
+      int later = 0;
+      for (int x = w - kSlots + 3; x <= w; ++x) later += (x >= 1 && real(x - 1)) ? 2 * nbulk : 0;
+      wait_vmcnt_upto16(later);
     }
     lds_barrier();
     if (!lds_flag) break;
   }
-  // after the last window: corrected rows of the last unit, the keys of the
-  // last unit, and the last two arrivals
-  if (lds_flag) {
-    if (real(U - 1)) {
-      const int gp = (U - 1) % kRowGroups, kp = (U - 1) / kRowGroups;
-      if (nbulk >= 1)
-        buffer_store16(rs_out, row_offset(gp, kp, brow0), *(const u32x4_t*)&lds_x[gp][brow0 * kPitch + lane * 16]);
-      if (nbulk >= 2)
-        buffer_store16(rs_out, row_offset(gp, kp, brow1), *(const u32x4_t*)&lds_x[gp][brow1 * kPitch + lane * 16]);
-    }
+  // after the last window: corrected rows of the last unit, then its keys
+  // and count (the last arrival)
+  if (lds_flag && real(U - 1)) {
+    const int gp = (U - 1) % kSlots, kp = (U - 1) / kSlots;
+    if (nbulk >= 1)
+      buffer_store16(rs_out, row_offset(gp, kp, brow0), *(const u32x4_t*)&lds_x[gp][brow0 * kPitch + lane * 16]);
+    if (nbulk >= 2)
+      buffer_store16(rs_out, row_offset(gp, kp, brow1), *(const u32x4_t*)&lds_x[gp][brow1 * kPitch + lane * 16]);
     if (wave == 0) {
       wait_vmcnt<0>();
-      if (lane == 0 && U >= 2 && real(U - 2))
-        __hip_atomic_fetch_add(arrival_counter(sync, (U - 2) % kRowGroups, xg), 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-      if (real(U - 1)) {
-        if (lane < 16) {
-          const int gp = (U - 1) % kRowGroups, kp = (U - 1) / kRowGroups;
-          const uint32_t kw = lds_key[gp][lane];
-          const int b = gp * rpg + lane;
-          if (kw != 0u && lane < rpg && b < B) {
-            const uint64_t code = kw >> 16;
-            const uint32_t col = vbeg + (0xFFFFu - (kw & 0xFFFFu));
-            __hip_atomic_fetch_max((uint64_t*)((unsigned char*)p.keys + key_offset(kp, xg, b)),
-                                   (code << 32) | (uint64_t)(0xFFFFFFFFu - col), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-        wait_vmcnt<0>();
-        if (lane == 0)
-          __hip_atomic_fetch_add(arrival_counter(sync, (U - 1) % kRowGroups, xg), 1u, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-      }
+      publish(U - 1);
+      wait_vmcnt<0>();
+      count_in(U - 1);
     }
   }
   if (wave < 2) __builtin_amdgcn_s_setprio(0);
@@ -529,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     lds_barrier();  // the last keys are read before they are cleared
     for (int i = tid; i < M * kGroups * kMaxRows; i += kThreads)
       __hip_atomic_store(p.keys + (uint32_t)(i * kKeyPad), (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid < kRowGroups * kGroups + 1)
+    if (tid < kSlots * kGroups + 1)
       __hip_atomic_store(sync + 16 * tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (failed)
       for (int i = tid; i < B * M; i += kThreads) p.tokens[(uint32_t)i] = -1;
