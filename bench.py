@@ -28,7 +28,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
 WORKLOAD = "greedy_draft_64x5"
 DOMINANT_KERNEL = "markov_chain_greedy_bf16"   # the whole sample call is this one launch
 KERNEL_SOURCES = [os.path.join(ROOT, "rank_markov_draft_amd", "csrc", name)
-                  for name in ("markov_chain.hip", "device_common.h", "markov_chain.h")]
+                  for name in ("markov_chain.hip", "chain_common.h", "device_common.h", "markov_chain.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 VALU_FILE = os.path.join(ROOT, "profiles", "valu.json")
 VALU_KERNEL = "markov_step_bf16<8, 2, 1, false>"  # temperature steps at rank 256, bf16 logits

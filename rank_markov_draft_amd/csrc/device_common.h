@@ -340,6 +340,37 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
   return Philox4{c0, c1, c2, c3};
 }
 
+// Two Philox4x32-10 blocks whose counters differ only in the first word,
+// with their rounds interleaved (two independent dependency chains).
+__device__ __forceinline__ void philox4x32_10_pair(uint32_t c0a, uint32_t c0b, uint32_t c1, uint32_t c2,
+                                                   uint32_t c3, uint32_t k0, uint32_t k1, Philox4& ra,
+                                                   Philox4& rb) {
+  uint32_t a1 = c1, a2 = c2, a3 = c3, b1 = c1, b2 = c2, b3 = c3;
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t pa0 = (uint64_t)0xD2511F53u * c0a, pa2 = (uint64_t)0xCD9E8D57u * a2;
+    const uint64_t pb0 = (uint64_t)0xD2511F53u * c0b, pb2 = (uint64_t)0xCD9E8D57u * b2;
+    const uint32_t na0 = __builtin_amdgcn_bitop3_b32((uint32_t)(pa2 >> 32), a1, k0, 0x96);
+    const uint32_t na2 = __builtin_amdgcn_bitop3_b32((uint32_t)(pa0 >> 32), a3, k1, 0x96);
+    const uint32_t nb0 = __builtin_amdgcn_bitop3_b32((uint32_t)(pb2 >> 32), b1, k0, 0x96);
+    const uint32_t nb2 = __builtin_amdgcn_bitop3_b32((uint32_t)(pb0 >> 32), b3, k1, 0x96);
+    a1 = (uint32_t)pa2;
+    a3 = (uint32_t)pa0;
+    b1 = (uint32_t)pb2;
+    b3 = (uint32_t)pb0;
+    c0a = na0;
+    a2 = na2;
+    c0b = nb0;
+    b2 = nb2;
+  }
+  ra = Philox4{c0a, a1, a2, a3};
+  rb = Philox4{c0b, b1, b2, b3};
+}
+
 // Base-2 Gumbel noise from one Philox word: u = (2*(w >> 9) + 1) * 2^-24 lies
 // in [2^-24, 1 - 2^-24] (exact in fp32), g = -log2(-log2(u)) with the
 // hardware log2 (v_log_f32).

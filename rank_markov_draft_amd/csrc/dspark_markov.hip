@@ -21,10 +21,12 @@ thread_local std::string g_last_error;
 //                 synchronisation-failure count of the persistent chain and
 //                 its test hook, each on its own 64-byte line;
 //   chain area    arrival counters (kChainSyncBytes), then the device-wide
-//                 argmax keys per (step, key group, row) for up to
-//                 kChainMaxSteps steps.  Only the persistent chain writes
-//                 here, and it leaves the area zeroed: its keys and counters
-//                 must start at zero, so no other path may put data in it;
+//                 argmax keys per (step, key group, row): 64-byte slots for
+//                 up to kChainMaxSteps steps of 64 rows (greedy chain), or
+//                 16-byte slots for up to 4096 step-rows (temperature
+//                 chain).  Only the persistent chains write here, and they
+//                 leave the area zeroed: their keys and counters must start
+//                 at zero, so no other path may put data in it;
 //   data          from kDataOffset: the apply kernels' store sink, or the
 //                 sampling steps' per-(row, vocabulary slice) argmax keys
 //                 (B * ceil(V/128) words), or the backward's and the gated
@@ -363,6 +365,36 @@ dspark_status_t sample_block_impl(const void* base_logits, dspark_dtype_t logits
     const hipError_t e = dspark::launch_chain_greedy(c, cus, s);
     if (e == hipSuccess) return DSPARK_OK;
     (void)hipGetLastError();  // not launchable here: take the step-by-step path
+  }
+  // Temperature bf16 chains that fit the persistent sampling kernel too.
+  if (tile && !greedy && cus > 0 && B <= dspark::chain_sample_max_rows() &&
+      M * B <= dspark::chain_sample_max_step_rows() &&
+      (V + 31) / 32 <= (int64_t)cus * dspark::chain_sample_slices_per_group()) {
+    dspark::ChainSampleParams c{};
+    c.base = (const uint16_t*)base_logits;
+    c.out = (uint16_t*)corrected_logits;
+    c.first_prev = first_prev_token_ids;
+    c.tokens = sampled_tokens;
+    c.w1 = (const uint16_t*)w1;
+    c.w2 = (const uint16_t*)w2;
+    c.sync = (uint32_t*)((char*)workspace + kControlBytes);
+    c.keys = (uint64_t*)((char*)c.sync + dspark::kChainSyncBytes);
+    c.bad_rows = &ctl->bad_rows;
+    c.sync_failures = &ctl->sync_failures;
+    c.test_hook = &ctl->chain_test_hook;
+    c.B = B;
+    c.M = M;
+    c.V = V;
+    c.r = r;
+    c.S = (V + 31) / 32;
+    c.kappa = p.kappa;
+    c.k_abs0 = (uint32_t)position_offset;
+    c.batch_offset = (uint32_t)batch_offset;
+    c.seed_lo = p.seed_lo;
+    c.seed_hi = p.seed_hi;
+    const hipError_t e = dspark::launch_chain_sample(c, cus, s);
+    if (e == hipSuccess) return DSPARK_OK;
+    (void)hipGetLastError();
   }
   for (int64_t k = 0; k < M; ++k) {
     p.k = k;

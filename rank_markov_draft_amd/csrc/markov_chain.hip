@@ -44,6 +44,7 @@
 // tokens.  A
 // launch that finds the failure count already nonzero (a failure nobody has
 // read back and cleared) does no work and also returns -1 tokens.
+#include "chain_common.h"
 #include "device_common.h"
 #include "markov_chain.h"
 
@@ -60,9 +61,8 @@ constexpr int kSlots = 5;
 constexpr int kMaxGroups = 4;                 // row groups of a call at most
 constexpr int kGroupRows = 16;                // rows of a group at most (the MFMA N tile)
 constexpr int kMaxRows = 64;                  // batch rows of one call
-constexpr int kGroups = 8;                    // key slots / arrival counters per row group
+constexpr int kGroups = kChainKeyGroups;      // key slots / arrival counters per row group
 constexpr int kPitch = 2 * 32 * kWaves + 16;  // LDS bytes of a staged row (512 columns + pad)
-constexpr uint64_t kSpinTicks = 100000000;    // 1 s of the 100 MHz realtime clock
 static_assert(kMaxGroups * kGroupRows >= kMaxRows && kMaxGroups <= kSlots, "row groups");
 
 // Synchronisation area, one 64-byte line per word: the arrival counters
@@ -87,57 +87,6 @@ __device__ __forceinline__ uint32_t argmax_code_bf16(uint32_t h) {
   c = (mag == 0u) ? 0x8000u : c;
   c = (mag > 0x7F80u) ? 0xFFFFu : c;
   return c;
-}
-
-// Arrival counters of row group rg: lanes 0..kGroups-1 load one each
-// (arrival_load), arrival_sum adds them up, uniform over the wave.  Split so
-// that a poll can be issued early and summed later.
-__device__ __forceinline__ uint32_t arrival_load(uint32_t* sync, int rg, int lane) {
-  return lane < kGroups ? __hip_atomic_load(arrival_counter(sync, rg, lane), __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT)
-                        : 0u;
-}
-__device__ __forceinline__ uint32_t arrival_sum(uint32_t v) {
-#pragma unroll
-  for (int d = 1; d < kGroups; d <<= 1) v += (uint32_t)__shfl_xor((int)v, d);
-  return (uint32_t)__builtin_amdgcn_readfirstlane(v);
-}
-__device__ __forceinline__ uint32_t arrivals(uint32_t* sync, int rg, int lane) {
-  return arrival_sum(arrival_load(sync, rg, lane));
-}
-
-// Spins until the arrival counters of row group rg sum to at least target;
-// false after kSpinTicks.
-__device__ bool wait_arrivals(uint32_t* sync, int rg, int lane, uint32_t target) {
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  while (arrivals(sync, rg, lane) < target) {
-    if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) return false;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  return true;
-}
-
-// s_waitcnt vmcnt(n) for a count known only at run time (0..16).
-__device__ __forceinline__ void wait_vmcnt_upto16(int n) {
-  switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 11: wait_vmcnt<11>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    case 13: wait_vmcnt<13>(); break;
-    case 14: wait_vmcnt<14>(); break;
-    case 15: wait_vmcnt<15>(); break;
-    default: wait_vmcnt<16>(); break;
-  }
 }
 
 }  // namespace
@@ -459,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
 #pragma unroll
       for (int x = 0; x < kGroups; ++x) seen += (uint32_t)__builtin_amdgcn_readlane((int)cx, x);
       if (force_timeout) ok = false;
-      else if (seen < target) ok = wait_arrivals(sync, u2 % kSlots, lane, target);
+      else if (seen < target) ok = chain_wait_arrivals<16>(arrival_counter(sync, u2 % kSlots, 0), lane, target);
       // the key slots arrive during the next window
       if (ok) load_keys(u2 & 1, u2 % kSlots, u2 / kSlots - 1);
       else if (lane == 0) {

@@ -1,7 +1,7 @@
 """The persistent chain's failure path, forced from the host.
 
 A workspace control word (byte 128) makes every device-wide wait of the
-persistent greedy chain give up at once, as a real 1 s timeout would, while
+persistent chains (greedy and temperature) give up at once, as a real 1 s timeout would, while
 every workgroup still exits normally.  The call must then return -1 for
 every token, the library must report DSPARK_ERR_DEVICE on the next read of
 the workspace's error words, and later persistent calls on the unread
@@ -27,21 +27,23 @@ def _raw_read(ws):
     return st, int(n.value)
 
 
-def test_forced_chain_timeout_gives_sentinel_tokens(native):
-    B, M, V, r = 8, 5, 4096, 256            # greedy bf16, B <= 64: the persistent chain
+@pytest.mark.parametrize("T,B", [(0.0, 8), (0.7, 8), (0.7, 40)])
+def test_forced_chain_timeout_gives_sentinel_tokens(native, T, B):
+    M, V, r = 5, 4096, 256                   # bf16: the persistent chains
     inp = wl.make_inputs(wl.WORKLOADS["greedy_draft_64x5"], B=B, M=M, V=V, r=r, seed=21)
     d = device_inputs({k: inp[k] for k in ("base", "first_prev", "w1", "w2")})
     ws = rmd.Workspace(B, M, V, r, sample=True)
 
     def call(**kw):
-        return rmd.sample_block_tokens(d["base"], d["first_prev"], d["w1"], d["w2"], 0.0, workspace=ws, **kw)
+        return rmd.sample_block_tokens(d["base"], d["first_prev"], d["w1"], d["w2"], T, seed=4, workspace=ws,
+                                       **kw)
 
     good, _ = call()
     assert rmd.read_device_error(ws) == 0
     good = from_dev(good)
     assert good.min() >= 0
 
-    print("[chain failure] forced timeout, B=8 M=5 V=4096 r=256", flush=True)
+    print(f"[chain failure] forced timeout, T={T} B={B} M=5 V=4096 r=256", flush=True)
     ws.set_chain_test_hook(True)
     tok, _ = call()
     torch.cuda.synchronize()

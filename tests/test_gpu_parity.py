@@ -259,6 +259,25 @@ def test_sample_shapes(native, T, B, M, V, r, dtype):
     check_chain(inp, T, 11, tok, corr, name=f"sample T{T} B{B} M{M} V{V} r{r} dt{dtype}")
 
 
+@pytest.mark.parametrize("B,M,V,r", [
+    (200, 3, 20000, 256),     # 13 groups of 16 rows (the last of 8), slices past the waves
+    (17, 2, 8200, 128),       # two groups of 9 rows; a vocabulary of 256 + 8 slices
+    (64, 1, 4096, 256),       # one step: only the first tokens' rows
+    (5, 7, 65544, 32),        # one short group, seven steps, a ragged last slice
+    (256, 2, 512, 64),        # 16 slices: most workgroups own no column
+])
+def test_temperature_chain_shapes(native, B, M, V, r):
+    """Temperature chains on the persistent sampling kernel (bf16, B <= 256,
+    M * B <= 4096): every token and corrected logit against the oracle, and
+    the tokens-only call gives the same tokens."""
+    w = wl.WORKLOADS["temperature_draft_256x8"]
+    inp = wl.make_inputs(w, B=B, M=M, V=V, r=r, seed=40 + B + M)
+    tok, corr = run_sample(inp, 0.7, seed=77)
+    check_chain(inp, 0.7, 77, tok, corr, name=f"temperature chain B{B} M{M} V{V} r{r}")
+    tok2, _ = run_sample(inp, 0.7, seed=77, return_logits=False)
+    assert np.array_equal(tok2, tok)
+
+
 def _mixed_inputs(ldt, wdt, B, M, V, r, seed):
     """Workload-shaped inputs with the logits in ldt and the weights in wdt."""
     w = dataclasses.replace(wl.WORKLOADS["teacher_forced_320"], dtype=wl.F32)
