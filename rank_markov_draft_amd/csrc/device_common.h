@@ -373,9 +373,13 @@ __device__ __forceinline__ void philox4x32_10_pair(uint32_t c0a, uint32_t c0b, u
 
 // Base-2 Gumbel noise from one Philox word: u = (2*(w >> 9) + 1) * 2^-24 lies
 // in [2^-24, 1 - 2^-24] (exact in fp32), g = -log2(-log2(u)) with the
-// hardware log2 (v_log_f32).
+// hardware log2 (v_log_f32).  u is formed in two instructions: the 23 bits
+// w >> 9 as the mantissa of x = 1 + (w >> 9) 2^-23 (one v_alignbit_b32),
+// then u = x - (1 - 2^-24), exact since x and 1 - 2^-24 lie within a factor
+// of two of each other.
 __device__ __forceinline__ float gumbel2_from_word(uint32_t w) {
-  const float u = (float)(2u * (w >> 9) + 1u) * 0x1p-24f;
+  const float x = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, w, 9u));
+  const float u = x - 0x1.fffffep-1f;
   return -__builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
 }
 

@@ -343,16 +343,19 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
         Philox4 qa, qb;
         philox4x32_10_pair(vcol >> 2, (vcol >> 2) + 1u, kabs, brow, 0u, seed_lo, seed_hi, qa, qb);
         const uint32_t words[8] = {qa.x0, qa.x1, qa.x2, qa.x3, qb.x0, qb.x1, qb.x2, qb.x3};
-        float best = 0.0f, sumc = 0.0f;
-        uint32_t bi = 0;
+        float sc[8], sumc = 0.0f;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           sumc += cv[q];
-          const float sc = __builtin_fmaf(cv[q], p.kappa, gumbel2_from_word(words[q]));
-          const bool gt = q == 0 || sc > best;
-          best = gt ? sc : best;
-          bi = gt ? (uint32_t)q : bi;
+          sc[q] = __builtin_fmaf(cv[q], p.kappa, gumbel2_from_word(words[q]));
         }
+        // the best score, then its first column (a NaN score only comes
+        // with a NaN corrected value, which the pass below handles)
+        const float best = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                                 fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        uint32_t bi = 7;
+#pragma unroll
+        for (int q = 6; q >= 0; --q) bi = sc[q] == best ? (uint32_t)q : bi;
         uint64_t k1 = argmax_key(best, vcol + bi);
         if (sumc != sumc) {
           // a score is NaN exactly when its corrected value is (the noise is
