@@ -31,9 +31,13 @@ KERNEL_SOURCES = [os.path.join(ROOT, "rank_markov_draft_amd", "csrc", name)
                   for name in ("markov_chain.hip", "chain_common.h", "device_common.h", "markov_chain.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 VALU_FILE = os.path.join(ROOT, "profiles", "valu.json")
-VALU_KERNEL = "markov_step_bf16<8, 2, 1, false>"  # temperature steps at rank 256, bf16 logits
+VALU_KERNEL = "markov_chain_sample_bf16<8>"   # persistent temperature chain at rank 256
 VALU_SOURCES = [os.path.join(ROOT, "rank_markov_draft_amd", "csrc", name)
-                for name in ("markov_step.hip", "device_common.h", "markov_kernels.h")]
+                for name in ("markov_chain_sample.hip", "chain_common.h", "device_common.h", "markov_chain.h")]
+# Issue cost (SIMD cycles) of a wave64 instruction, measured with a
+# throughput microbenchmark at the measured shader clock: plain VALU 4 (16
+# lanes per cycle), v_mad_u64_u32 (the Philox multiply) 4.5, v_log_f32 9.6.
+VALU_COST, INT64_COST, TRANS_COST = 4.0, 4.5, 9.6
 # Vector issue: 256 CUs x 4 SIMDs at 2.4 GHz; a wave64 VALU instruction holds
 # its SIMD for 4 cycles (16 lanes per cycle, the non-packed rate behind the
 # 157.3 TFLOP/s fp32 vector peak), a transcendental one for 16 (quarter rate).
@@ -167,8 +171,9 @@ def write_traffic(fetch_csv: str, write_csv: str) -> dict:
 
 def write_valu(csv_path: str) -> dict:
     """profiles/valu.json from one SQ_INSTS_VALU / SQ_INSTS_VALU_TRANS_F32 /
-    SQ_INSTS_VALU_MFMA_BF16 counter run: the step kernel's vector issue
-    cycles per dispatch."""
+    SQ_INSTS_VALU_MFMA_BF16 / SQ_INSTS_VALU_INT64 counter run: the temperature
+    chain's vector issue cycles per dispatch at the measured instruction
+    costs (MFMA instructions run on the matrix cores beside the VALU)."""
     import collections
     import csv
     import json as _json
@@ -179,11 +184,13 @@ def write_valu(csv_path: str) -> dict:
                 acc[row["Counter_Name"]].append(float(row["Counter_Value"]))
     avg = {k: sum(v) / len(v) for k, v in acc.items()}
     valu, trans, mfma = avg["SQ_INSTS_VALU"], avg["SQ_INSTS_VALU_TRANS_F32"], avg["SQ_INSTS_VALU_MFMA_BF16"]
+    int64 = avg["SQ_INSTS_VALU_INT64"]
     t = {"kernel": VALU_KERNEL, "workload": "temperature_draft_256x8",
          "kernel_source_sha256_16": source_hash(VALU_SOURCES),
          "dispatches": len(acc["SQ_INSTS_VALU"]),
-         "valu_wave_insts": valu, "trans_wave_insts": trans, "mfma_wave_insts": mfma,
-         "simd_issue_cycles": (valu - mfma - trans) * 4 + trans * 16}
+         "valu_wave_insts": valu, "trans_wave_insts": trans, "mfma_wave_insts": mfma, "int64_wave_insts": int64,
+         "cost_cycles": {"valu": VALU_COST, "int64": INT64_COST, "trans": TRANS_COST},
+         "simd_issue_cycles": (valu - mfma - trans - int64) * VALU_COST + int64 * INT64_COST + trans * TRANS_COST}
     with open(VALU_FILE, "w") as f:
         _json.dump(t, f, indent=1)
         f.write("\n")
@@ -191,8 +198,8 @@ def write_valu(csv_path: str) -> dict:
 
 
 def measured_valu():
-    """Vector issue cycles per step-kernel dispatch (profiles/valu.json), or
-    None once the step kernel's source changed."""
+    """Vector issue cycles per temperature-chain dispatch (profiles/valu.json),
+    or None once the kernel's source changed."""
     import json as _json
     if not os.path.exists(VALU_FILE):
         return None
@@ -300,6 +307,7 @@ def measure_extra(name, rmd, wl, torch, np, steps=20, warmup=3):
     """Time one other workload (a parity case, reported beside the main line)."""
     w = wl.WORKLOADS[name]
     inp = wl.make_inputs(w)
+    distinct = len(np.unique(inp["token_ids"]))
     lbytes = 2 if w.ldtype == 1 else 4
     wbytes = 2 if w.dtype == 1 else 4
     per_set = 2 * w.B * w.M * w.V * lbytes + 2 * w.V * w.r * wbytes
@@ -366,12 +374,22 @@ def measure_extra(name, rmd, wl, torch, np, steps=20, warmup=3):
                            "frac": flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, "flops_per_call": flops}
     cycles = measured_valu() if name == "temperature_draft_256x8" else None
     if cycles:
-        # vector-issue roofline of the whole call (M step kernels; the
-        # reductions and launch gaps count against it)
-        achieved = cycles * w.M / (ms * 1e-3) / 1e9
-        res["roofline"] = {"bound": "alu", "kernel": "markov_step_bf16 (one per step)", "achieved": achieved,
+        # vector-issue roofline of the whole call (one persistent launch;
+        # its prologue, exchange waits and launch gap count against it)
+        achieved = cycles / (ms * 1e-3) / 1e9
+        res["roofline"] = {"bound": "alu", "kernel": VALU_KERNEL, "achieved": achieved,
                            "peak": SIMD_CYCLES_PEAK_G, "unit": "G SIMD issue cycles/s",
-                           "frac": achieved / SIMD_CYCLES_PEAK_G}
+                           "frac": achieved / SIMD_CYCLES_PEAK_G,
+                           "cost_cycles": {"valu": VALU_COST, "int64": INT64_COST, "trans": TRANS_COST}}
+    if w.mode == "apply" and not w.lm_head and not w.hidden:
+        # the bias products on the matrix cores: 2 U V r flops, U the rows'
+        # distinct predecessors where the grouped kernel plans (>= 1024 rows),
+        # else every row
+        U = distinct if w.B * w.M >= 1024 else w.B * w.M
+        flops = 2.0 * U * w.V * w.r
+        res["mfma"] = {"flops_per_call": flops, "distinct_rows": U,
+                       "achieved": flops / (ms * 1e-3) / 1e12, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
     del sets
     torch.cuda.empty_cache()
     return res
