@@ -38,9 +38,9 @@ VALU_SOURCES = [os.path.join(ROOT, "rank_markov_draft_amd", "csrc", name)
 # throughput microbenchmark at the measured shader clock: plain VALU 4 (16
 # lanes per cycle), v_mad_u64_u32 (the Philox multiply) 4.5, v_log_f32 9.6.
 VALU_COST, INT64_COST, TRANS_COST = 4.0, 4.5, 9.6
-# Vector issue: 256 CUs x 4 SIMDs at 2.4 GHz; a wave64 VALU instruction holds
-# its SIMD for 4 cycles (16 lanes per cycle, the non-packed rate behind the
-# 157.3 TFLOP/s fp32 vector peak), a transcendental one for 16 (quarter rate).
+# Vector issue: 256 CUs x 4 SIMDs at 2.4 GHz, each SIMD issuing one cycle's
+# worth of the costs above per cycle (a plain wave64 VALU instruction holds
+# it for 4 cycles: 16 lanes per cycle, the non-packed rate).
 SIMD_CYCLES_PEAK_G = 256 * 4 * 2.4
 EXTRA_WORKLOADS = ("teacher_forced_320", "teacher_forced_2560_zipf", "temperature_draft_256x8",
                    "teacher_forced_320_f32logits", "greedy_draft_64x5_f32logits",

@@ -128,7 +128,7 @@ dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_
  * M == 0 or B == 0 is a successful no-op.  V == 0 with B*M > 0 is invalid.
  *
  * Greedy bf16 calls with B <= 64, M <= 16 and r <= 256, and temperature bf16
- * calls with B <= 256, M * B <= 4096, r <= 256 and V <= 768 * CUs, run as
+ * calls with B <= 256, M * B <= 4096, r <= 256 and V <= 640 * CUs, run as
  * one persistent launch whose workgroups (one per CU) exchange each step's
  * tokens through the workspace; the host takes that path only when the
  * occupancy query says a CU can hold one of its workgroups (other calls run

@@ -7,11 +7,15 @@
 // fmaf(c_v, log2(e) / T, g_v), g_v base-2 Gumbel noise from Philox4x32-10 of
 // (v / 4, k_abs, b_abs, 0) under the seed.  A kernel per position re-reads W2
 // (78 MB at V=151936, r=256) every step; this kernel runs all M positions in
-// one launch with W2 in VGPRs, one workgroup of 8 waves per CU:
+// one launch with W2 resident on the CUs, one workgroup of 16 waves per CU:
 //
-//   * the workgroup's columns are cut into 32-column slices; wave w owns
-//     slices w, w + 8 and w + 16 of them (so the four SIMDs share the
-//     slices evenly) and keeps their W2 rows in VGPRs for all M steps;
+//   * the workgroup's columns are cut into 32-column slices (up to 20);
+//     wave w keeps the W2 rows of slice w in VGPRs for all M steps, and the
+//     rows of slices 16.. sit in LDS, each multiplied as two 16-column tiles
+//     by two of waves 4..11, so that no wave scores more than one and a half
+//     slices and the SIMDs carrying the exchange waves get the fewest tiles.
+//     Four waves per SIMD (128 VGPRs each) hide the latency of the scoring's
+//     dependent chains (the Philox rounds);
 //   * the batch rows are dealt into row groups of up to 16 (the MFMA N
 //     tile); unit u = S k + g is step k of group g, S = max(groups, 5)
 //     slots per step (slots past the groups are idle), and window w
@@ -19,7 +23,7 @@
 //     by its slices on the matrix cores, rounds the bias to bf16, adds it to
 //     the staged base logits, scores every column and folds each row's best
 //     key into LDS.  One barrier ends the window;
-//   * waves 2..7 stage the base rows of unit w+2 into LDS (buffer loads to
+//   * waves 2..15 stage the base rows of unit w+2 into LDS (buffer loads to
 //     LDS), and when the corrected logits are returned they first send the
 //     rows of unit w-1 from LDS to HBM;
 //   * waves 0 and 1 run the exchange of the greedy chain (markov_chain.hip):
@@ -40,11 +44,14 @@ namespace dspark {
 
 namespace {
 
-constexpr int kTWaves = 8;
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kTWaves = 16;
 constexpr int kTThreads = kTWaves * 64;
-constexpr int kTSpw = 3;                     // slices per wave
-constexpr int kTSlices = kTWaves * kTSpw;    // slices of a workgroup at most (768 columns)
-constexpr int kTPitch = 2048 + 16;           // LDS bytes of a staged row (two 1 KB segments + pad)
+constexpr int kTExtra = 4;                   // slices whose W2 rows sit in LDS
+constexpr int kTSlices = kTWaves + kTExtra;  // slices of a workgroup at most (640 columns)
+constexpr int kTPitch = 64 * kTSlices + 16;  // LDS bytes of a staged row (+ pad)
+constexpr int kTBulk = kTWaves - 2;          // staging waves (2 .. 15)
 constexpr int kTRing = 3;                    // staged units (rows of unit w+2 load during window w)
 constexpr int kTGroupRows = 16;              // rows of a group at most
 constexpr int kTMaxGroups = 16;              // row groups of a call at most (256 rows)
@@ -61,6 +68,54 @@ __device__ __forceinline__ uint32_t* t_exit_counter(uint32_t* sync) {
   return sync + kTStride * (kTMaxGroups * kChainKeyGroups);
 }
 static_assert((kTMaxGroups * kChainKeyGroups + 1) * kTStride * 4 <= (int)kChainSyncBytes, "sync area");
+// The 16-column tile q = 2 e + t of LDS slice e (tile t: columns 16 t ..
+// 16 t + 15 in the matrix instruction's order) is multiplied by wave
+// 6, 7, 10, 11, 4, 5, 8, 9 (q = 0..7): with three LDS slices SIMDs 2 and 3
+// take two tiles and SIMDs 0 and 1, whose waves 0 and 1 run the exchange,
+// one each.  -1 for the other waves.
+__device__ __forceinline__ int extra_tile_of_wave(int wave) {
+  switch (wave) {
+    case 6: return 0;
+    case 7: return 1;
+    case 10: return 2;
+    case 11: return 3;
+    case 4: return 4;
+    case 5: return 5;
+    case 8: return 6;
+    case 9: return 7;
+    default: return -1;
+  }
+}
+// The best key of a lane's N consecutive columns vcol .. vcol + N - 1 with
+// corrected values cv and noise words w: the first column of the highest
+// score fmaf(cv, kappa, g); a NaN corrected value (the only source of a NaN
+// score, the noise being finite) ranks above all, the first one winning.
+template <int N>
+__device__ __forceinline__ uint64_t score_key(const float (&cv)[N], const uint32_t (&w)[N], float kappa,
+                                              uint32_t vcol) {
+  float sc[N], sumc = 0.0f;
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    sumc += cv[q];
+    sc[q] = __builtin_fmaf(cv[q], kappa, gumbel2_from_word(w[q]));
+  }
+  float best = sc[0];
+#pragma unroll
+  for (int q = 1; q < N; ++q) best = fmaxf(best, sc[q]);
+  uint32_t bi = N - 1;
+#pragma unroll
+  for (int q = N - 2; q >= 0; --q) bi = sc[q] == best ? (uint32_t)q : bi;
+  uint64_t k = argmax_key(best, vcol + bi);
+  if (sumc != sumc) {
+    // without a NaN value (+inf met -inf in the sum) the scan above stands
+    uint32_t first = N;
+#pragma unroll
+    for (int q = N - 1; q >= 0; --q)
+      if (cv[q] != cv[q]) first = (uint32_t)q;
+    if (first < N) k = (0xFFFFFFFFull << 32) | (uint64_t)(0xFFFFFFFFu - (vcol + first));
+  }
+  return k;
+}
 // the key slots of M * B <= kTMaxStepRows step-rows fit the chain area's keys
 // (16 steps x 8 key groups x 64 rows of 64-byte slots)
 static_assert(kTMaxStepRows * kChainKeyGroups * kTKeyWords * 8 <= 16 * 8 * 64 * kKeyPad * 8, "key area");
@@ -75,6 +130,9 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
   __shared__ __attribute__((aligned(16))) unsigned char lds_e[2][K32 * 1024];
   // Staged logits of units u (slot u % kTRing): base, then corrected.
   __shared__ __attribute__((aligned(16))) unsigned char lds_x[kTRing][kTGroupRows * kTPitch];
+  // W2 rows of the LDS slices, block (kk, t) at (2 kk + t) * 1024 in the
+  // A-operand order of the register slices (lane l's 16 bytes).
+  __shared__ __attribute__((aligned(16))) unsigned char lds_w2[kTExtra][2 * K32 * 1024];
   __shared__ uint64_t lds_key[2][16];  // row keys of units u (buffer u % 2)
   // Key slots loaded for a merge, two buffers of [lane] 16 bytes each, the
   // key in the first 8 (row l % 16, key group 2 (l / 16) + j).
@@ -94,7 +152,7 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
       __builtin_amdgcn_readfirstlane((int)__hip_atomic_load(p.sync_failures, __ATOMIC_RELAXED,
                                                             __HIP_MEMORY_SCOPE_AGENT)) != 0;
   const bool force_timeout = __builtin_amdgcn_readfirstlane((int)*p.test_hook) != 0;
-  // The host guarantees B <= 256, M * B <= 4096, V % 8 == 0, V <= 768 * CUs
+  // The host guarantees B <= 256, M * B <= 4096, V % 8 == 0, V <= 640 * CUs
   // and B * M * V < 2^30, so every index below fits in 32 bits.
   const int B = (int)p.B, M = (int)p.M, V = (int)p.V, r = (int)p.r;
   const int NR = (B + kTGroupRows - 1) / kTGroupRows;
@@ -105,13 +163,16 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
   uint32_t* const sync = p.sync;
   const bool ret = p.out != nullptr;
 
-  // The workgroup's columns [vbeg, vend): slices s_begin .. s_end - 1; wave
-  // w's slice i is slice w + 8 i of the workgroup.
+  // The workgroup's columns [vbeg, vend): slices s_begin .. s_end - 1;
+  // wave w's register slice is slice w of the workgroup, its LDS tile (if
+  // any) tile extra_tile_of_wave(w) of slices 16...
   const int s_begin = (int)(((int64_t)g * p.S) / G);
   const int s_end = (int)(((int64_t)(g + 1) * p.S) / G);
   const uint32_t vbeg = (uint32_t)(s_begin * 32);
   const uint32_t vend = (uint32_t)(s_end * 32 < V ? s_end * 32 : V);
-  const int nseg = (int)((vend - vbeg + 511) / 512);  // 1 KB row segments (1 or 2)
+  const int ncols = (int)(vend - vbeg);               // <= 640, a multiple of 8
+  const int nseg = ncols > 512 ? 2 : 1;              // 1 KB row segments
+  const int xq = extra_tile_of_wave(wave);
 
   const uint32_t bytes = (uint32_t)(B * M * V * 2);
   const __amdgpu_buffer_rsrc_t rs_out = buffer_rsrc(p.out, ret ? bytes : 0u);
@@ -128,47 +189,66 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
   // W2w[col(t, n16)][32 kk + 8 g4 .. +7] with col(t, m) = 8 (m / 4) + 4 t +
   // m % 4, so a lane's 4 + 4 accumulators are the 8 consecutive columns
   // 8 g4 .. 8 g4 + 7 of the slice.
-  bf16x8_t a[kTSpw][2][K32];
-#pragma unroll
-  for (int i = 0; i < kTSpw; ++i) {
-    const int slice = s_begin + wave + kTWaves * i;
+  bf16x8_t a[2][K32];
+  {
+    const int slice = s_begin + wave;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int vrow = slice * 32 + 8 * (n16 >> 2) + 4 * t + (n16 & 3);
 #pragma unroll
       for (int kk = 0; kk < K32; ++kk) {
         const int kof = kk * 32 + 8 * g4;
-        a[i][t][kk] = (slice < s_end && vrow < V && kof < r) ? *(const bf16x8_t*)(p.w2 + (uint32_t)(vrow * r + kof))
-                                                            : bf16x8_t{};
+        a[t][kk] = (slice < s_end && vrow < V && kof < r) ? *(const bf16x8_t*)(p.w2 + (uint32_t)(vrow * r + kof))
+                                                         : bf16x8_t{};
       }
     }
   }
+  // the LDS slices' blocks, dealt over all waves (loads to LDS)
+  const BufferWords bw_w2 = buffer_words(p.w2, (uint32_t)(V * r * 2));
+  for (int d = wave; d < kTExtra * 2 * K32; d += kTWaves) {
+    const int e = d / (2 * K32), kk = (d % (2 * K32)) >> 1, t = d & 1;
+    const int slice = s_begin + kTWaves + e;
+    if (slice >= s_end) continue;
+    const int vrow = slice * 32 + 8 * (n16 >> 2) + 4 * t + (n16 & 3);
+    const int kof = kk * 32 + 8 * g4;
+    load_lds16(bw_w2, (vrow < V && kof < r) ? (uint32_t)(vrow * r + kof) * 2u : kBufferOob,
+               lds_address(&lds_w2[e][(2 * kk + t) * 1024]));
+  }
 
-  // ---- row staging by waves 2..7: segment j = 2 row + half of a unit (row
-  // 0..15, 512-column half) is moved by wave 2 + j % 6, lane l the 8 columns
-  // vbeg + 512 half + 8 l .. +7.  Offsets of masked-off lanes, rows or
-  // steps point past the buffer, so every instruction is unconditional.
+  // ---- row staging by waves 2..15: row i (0..15) of a unit is moved by
+  // wave 2 + i % 14 as one or two segments of 512 columns, lane l the 8
+  // columns base + 8 l .. +7, base = 0 for the first and ncols - 512 for
+  // the second (present when the workgroup has more than 512 columns).  The
+  // two overlap; one wave moves both, so a row's corrected values are read
+  // for the store before the next unit's loads overwrite any of them.
+  // Offsets of masked-off lanes, rows or steps point past the buffer, so
+  // every instruction is unconditional.
   const int bw = wave - 2;  // bulk index (negative for waves 0 and 1)
+  auto seg_base = [&](int j) __attribute__((always_inline)) -> uint32_t {
+    return (j & 1) ? (uint32_t)(ncols - 512) : 0u;
+  };
   auto seg_offset = [&](int u, int j) __attribute__((always_inline)) -> uint32_t {
-    const int row = j >> 1, half = j & 1;
+    const int row = j >> 1;
     const int gg = u % NS, kd = u / NS;
     const int b = gg * rpg + row;
-    const uint32_t col = vbeg + 512u * (uint32_t)half + 8u * (uint32_t)lane;
-    const bool ok = row < rpg && b < B && kd < M && col < vend && half < nseg;
+    const uint32_t col = vbeg + seg_base(j) + 8u * (uint32_t)lane;
+    const bool ok = row < rpg && b < B && kd < M && col < vend;
     return ok ? (uint32_t)((b * M + kd) * V) * 2u + 2u * col : kBufferOob;
   };
   // the segment's LDS base (a load to LDS puts lane l's 16 bytes at base + 16 l)
   auto seg_lds = [&](int u, int j) __attribute__((always_inline)) -> unsigned char* {
-    return &lds_x[u % kTRing][(j >> 1) * kTPitch + (j & 1) * 1024];
+    return &lds_x[u % kTRing][(j >> 1) * kTPitch + 2 * seg_base(j)];
   };
   // bulk operations this wave issues per staged unit
-  const int my_segs = bw < 0 ? 0 : (2 * kTGroupRows - bw + 5) / 6;
+  const int my_segs = bw < 0 ? 0 : nseg * ((kTGroupRows - bw + kTBulk - 1) / kTBulk);
   auto load_unit = [&](int u) __attribute__((always_inline)) {
-    for (int j = bw; j < 2 * kTGroupRows; j += 6) load_lds16(bw_base, seg_offset(u, j), lds_address(seg_lds(u, j)));
+    for (int i = bw; i < kTGroupRows; i += kTBulk)
+      for (int h = 0; h < nseg; ++h) load_lds16(bw_base, seg_offset(u, 2 * i + h), lds_address(seg_lds(u, 2 * i + h)));
   };
   auto flush_unit = [&](int u) __attribute__((always_inline)) {
-    for (int j = bw; j < 2 * kTGroupRows; j += 6)
-      buffer_store16(rs_out, seg_offset(u, j), *(const u32x4_t*)(seg_lds(u, j) + lane * 16));
+    for (int i = bw; i < kTGroupRows; i += kTBulk)
+      for (int h = 0; h < nseg; ++h)
+        buffer_store16(rs_out, seg_offset(u, 2 * i + h), *(const u32x4_t*)(seg_lds(u, 2 * i + h) + lane * 16));
   };
 
   // ---- exchange pieces (waves 0 and 1)
@@ -249,7 +329,11 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
   lds_barrier();
 
   bool ok = true;  // this wave's exchange waits have not timed out
+  // Issue priority: the exchange waves first, then the waves with an LDS
+  // tile (one and a half slices), so that the waves with one slice, not
+  // those with more, end the window.
   if (wave < 2) __builtin_amdgcn_s_setprio(3);
+  else if (xq >= 0 && xq < 2 * (s_end - s_begin - kTWaves)) __builtin_amdgcn_s_setprio(2);
 
   for (int w = 0; w < (poisoned ? 0 : U); ++w) {
     const bool role_a = wave == ((w + 1) & 1);
@@ -295,28 +379,42 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
       const uint32_t brow = p.batch_offset + (uint32_t)row;
       const uint32_t kabs = p.k_abs0 + (uint32_t)kd;
       uint64_t key = 0ull;
+      // opaque per window: else the compiler keeps loop-invariant Philox
+      // products and the ten round keys live across the windows (and spills
+      // them)
+      uint32_t seed_lo = p.seed_lo, seed_hi = p.seed_hi;
+      __asm__ volatile("" : "+s"(seed_lo), "+s"(seed_hi));
+      const bool has_reg = s_begin + wave < s_end;
+      const int xs = kTWaves + (xq >> 1);  // the LDS tile's slice within the workgroup
+      const bool has_tile = xq >= 0 && s_begin + xs < s_end;
+      const unsigned char* ab = &lds_w2[xq >= 0 ? xq >> 1 : 0][(xq & 1) * 1024 + lane * 16];
+      f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{}, acc2 = f32x4_t{};
+      constexpr int KB = (K32 < 2) ? K32 : 2;
 #pragma unroll
-      for (int i = 0; i < kTSpw; ++i) {
-        const int sl = wave + kTWaves * i;  // slice within the workgroup
-        if (s_begin + sl >= s_end) continue;
-        f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{};
-        constexpr int KB = (K32 < 2) ? K32 : 2;  // the W2 slices leave few registers
+      for (int k0 = 0; k0 < K32; k0 += KB) {
+        bf16x8_t bop[KB], aop[KB];
 #pragma unroll
-        for (int k0 = 0; k0 < K32; k0 += KB) {
-          bf16x8_t bop[KB];
+        for (int q = 0; q < KB; ++q) bop[q] = *(const bf16x8_t*)(eb + (k0 + q) * 1024);
+        if (has_tile) {
 #pragma unroll
-          for (int q = 0; q < KB; ++q) bop[q] = *(const bf16x8_t*)(eb + (k0 + q) * 1024);
-          __builtin_amdgcn_sched_barrier(0);  // the reads ahead of the products
-#pragma unroll
-          for (int q = 0; q < KB; ++q) {
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][0][k0 + q], bop[q], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][1][k0 + q], bop[q], acc1, 0, 0, 0);
-          }
+          for (int q = 0; q < KB; ++q) aop[q] = *(const bf16x8_t*)(ab + (k0 + q) * 2048);
         }
-        const uint32_t colw = (uint32_t)(sl * 32 + 8 * g4);  // the lane's first column in the workgroup
-        if (!row_ok || vbeg + colw >= vend) continue;
-        // corrected values: the bias rounded to bf16 (the Linear's output
-        // dtype), the sum rounded to the bf16 logits
+        __builtin_amdgcn_sched_barrier(0);  // the reads ahead of the products
+#pragma unroll
+        for (int q = 0; q < KB; ++q) {
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0][k0 + q], bop[q], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1][k0 + q], bop[q], acc1, 0, 0, 0);
+        }
+        if (has_tile) {
+#pragma unroll
+          for (int q = 0; q < KB; ++q) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[q], bop[q], acc2, 0, 0, 0);
+        }
+      }
+      // corrected values: the bias rounded to bf16 (the Linear's output
+      // dtype), the sum rounded to the bf16 logits
+      // the register slice: the lane's 8 columns 32 wave + 8 g4 .. +7
+      const uint32_t colw = (uint32_t)(wave * 32 + 8 * g4);
+      if (has_reg && row_ok && vbeg + colw < vend) {
         unsigned char* xp = xrow + colw * 2;
         const u32x4_t bb = *(const u32x4_t*)xp;
         const uint32_t bw4[4] = {pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
@@ -330,44 +428,33 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
         float cv[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) cv[q] = (q & 1) ? bf16_hi(ow[q >> 1]) : bf16_lo(ow[q >> 1]);
-        // the lane's best score (first column on ties)
         uint32_t vcol = vbeg + colw;
-        // opaque per slice: else the compiler keeps loop-invariant Philox
-        // products and the ten round keys live across the windows (and
-        // spills them)
-        __asm__ volatile("" : "+v"(vcol));
-        uint32_t seed_lo = p.seed_lo, seed_hi = p.seed_hi;
-        __asm__ volatile("" : "+s"(seed_lo), "+s"(seed_hi));
+        __asm__ volatile("" : "+v"(vcol));  // opaque, as the seeds
         // columns vcol .. + 3 and vcol + 4 .. + 7 are the words of two Philox
         // blocks, computed as two interleaved chains
         Philox4 qa, qb;
         philox4x32_10_pair(vcol >> 2, (vcol >> 2) + 1u, kabs, brow, 0u, seed_lo, seed_hi, qa, qb);
         const uint32_t words[8] = {qa.x0, qa.x1, qa.x2, qa.x3, qb.x0, qb.x1, qb.x2, qb.x3};
-        float sc[8], sumc = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          sumc += cv[q];
-          sc[q] = __builtin_fmaf(cv[q], p.kappa, gumbel2_from_word(words[q]));
-        }
-        // the best score, then its first column (a NaN score only comes
-        // with a NaN corrected value, which the pass below handles)
-        const float best = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                                 fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-        uint32_t bi = 7;
-#pragma unroll
-        for (int q = 6; q >= 0; --q) bi = sc[q] == best ? (uint32_t)q : bi;
-        uint64_t k1 = argmax_key(best, vcol + bi);
-        if (sumc != sumc) {
-          // a score is NaN exactly when its corrected value is (the noise is
-          // finite): the first NaN wins, as a NaN's key ranks above all;
-          // without one (+inf met -inf in the sum) the scan above stands
-          uint32_t first = 8;
-#pragma unroll
-          for (int q = 7; q >= 0; --q)
-            if (cv[q] != cv[q]) first = (uint32_t)q;
-          if (first < 8) k1 = (0xFFFFFFFFull << 32) | (uint64_t)(0xFFFFFFFFu - (vcol + first));
-        }
-        key = max_u64(key, k1);
+        key = score_key<8>(cv, words, p.kappa, vcol);
+      }
+      // the LDS tile: the lane's 4 columns 32 xs + 8 g4 + 4 t .. +3 (one
+      // Philox block)
+      const uint32_t colt = (uint32_t)(xs * 32 + 8 * g4 + 4 * (xq & 1));
+      if (has_tile && row_ok && vbeg + colt < vend) {
+        unsigned char* xp = xrow + colt * 2;
+        const u32x2_t bb = *(const u32x2_t*)xp;
+        const uint32_t ow[2] = {
+            pack_bf16x2(bf16_lo(bb.x) + bf16_lo(pack_bf16x2(acc2[0], acc2[1])),
+                        bf16_hi(bb.x) + bf16_hi(pack_bf16x2(acc2[0], acc2[1]))),
+            pack_bf16x2(bf16_lo(bb.y) + bf16_lo(pack_bf16x2(acc2[2], acc2[3])),
+                        bf16_hi(bb.y) + bf16_hi(pack_bf16x2(acc2[2], acc2[3])))};
+        if (ret) *(u32x2_t*)xp = u32x2_t{ow[0], ow[1]};
+        const float cv[4] = {bf16_lo(ow[0]), bf16_hi(ow[0]), bf16_lo(ow[1]), bf16_hi(ow[1])};
+        uint32_t vcol = vbeg + colt;
+        __asm__ volatile("" : "+v"(vcol));
+        const Philox4 q4 = philox4x32_10(vcol >> 2, kabs, brow, 0u, seed_lo, seed_hi);
+        const uint32_t words[4] = {q4.x0, q4.x1, q4.x2, q4.x3};
+        key = max_u64(key, score_key<4>(cv, words, p.kappa, vcol));
       }
       // the row's four lanes, then one LDS max per row and wave
       key = max_u64(key, ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(key >> 32), 16) << 32) |
@@ -414,7 +501,7 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
       count_in(U - 1);
     }
   }
-  if (wave < 2) __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_s_setprio(0);
   wait_vmcnt<0>();
   lds_barrier();
 

@@ -265,6 +265,9 @@ def test_sample_shapes(native, T, B, M, V, r, dtype):
     (64, 1, 4096, 256),       # one step: only the first tokens' rows
     (5, 7, 65544, 32),        # one short group, seven steps, a ragged last slice
     (256, 2, 512, 64),        # 16 slices: most workgroups own no column
+    (3, 2, 163840, 256),      # 20 slices a workgroup on 256 CUs: four slices' W2 rows in LDS
+    (16, 2, 139264, 64),      # 17 slices a workgroup on 256 CUs: one LDS slice, rank 64
+    (9, 3, 151928, 256),      # a ragged last slice among the LDS slices
 ])
 def test_temperature_chain_shapes(native, B, M, V, r):
     """Temperature chains on the persistent sampling kernel (bf16, B <= 256,
