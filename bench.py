@@ -285,6 +285,30 @@ def time_calls(fn, n_sets, steps, warmup, torch, min_warm_s=0.0):
     return wall, per
 
 
+def time_region(fn, n_sets, steps, warmup, torch, min_warm_s=0.0):
+    """Warm up as time_calls does, then time exactly `steps` calls issued
+    back to back, with one event pair around the whole timed region on the
+    current stream (events between the calls would add gaps of their own);
+    returns (wall seconds, event ms per call)."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t0 < min_warm_s:
+        fn(i % n_sets)
+        i += 1
+        if min_warm_s > 0 and i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        fn(i % n_sets)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, start.elapsed_time(end) / steps
+
+
 def cpu_baseline(w, inp, np):
     """The oracle as it stands, on the host cores: the same workload, timed
     over a few whole calls (a bounded sample of seconds of CPU work)."""
@@ -303,7 +327,7 @@ def cpu_baseline(w, inp, np):
                       f"{reps} calls, {dt:.2f} s wall each", "tokens_per_s": w.B * w.M / dt}
 
 
-def measure_extra(name, rmd, wl, torch, np, steps=20, warmup=3):
+def measure_extra(name, rmd, wl, torch, np, steps=50, warmup=3):
     """Time one other workload (a parity case, reported beside the main line)."""
     w = wl.WORKLOADS[name]
     inp = wl.make_inputs(w)
@@ -350,8 +374,7 @@ def measure_extra(name, rmd, wl, torch, np, steps=20, warmup=3):
     # steady state: the first calls after a workload change run slower
     # (measured up to 10% on the apply kernels), so the warm-up runs for a
     # quarter second of calls
-    wall, per = time_calls(call, n_sets, steps, warmup, torch, min_warm_s=0.25)
-    ms = float(np.mean(per))
+    wall, ms = time_region(call, n_sets, steps, warmup, torch, min_warm_s=0.25)
     if w.lm_head:
         alg = algorithmic_bytes_lm_head(w)
     elif w.mode == "backward":
@@ -398,8 +421,8 @@ def measure_extra(name, rmd, wl, torch, np, steps=20, warmup=3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' timings")
     ap.add_argument("--extra", default=",".join(EXTRA_WORKLOADS),
@@ -455,10 +478,9 @@ def main():
         rmd.sample_block_tokens(d["base"], d["first_prev"], d["w1"], d["w2"], 0.0, tokens_out=d["tok"],
                                 logits_out=d["corr"], workspace=d["ws"])
 
-    wall, per = time_calls(step, n_sets, args.steps, args.warmup, torch)
+    wall, call_ms = time_region(step, n_sets, args.steps, args.warmup, torch)
     ms = wall * 1e3 / args.steps
     elems = w.B * w.M * w.V
-    call_ms = float(np.mean(per))
     alg = algorithmic_bytes_sample(w)
     achieved = alg / (call_ms * 1e-3) / 1e9
 

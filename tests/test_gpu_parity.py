@@ -511,6 +511,42 @@ def test_greedy_special_values(native, B):
     check_chain(inp, 0.0, 0, tok, corr, name=f"greedy special values B{B}")
 
 
+@pytest.mark.parametrize("V", [8192, 163840])
+def test_temperature_special_values(native, V):
+    """The temperature chain's selection on planted values (W2 = 0, so
+    corrected = base, T = 0.7): a NaN ranks above every score and the first
+    NaN wins, +inf scores tie and the first wins, all -inf rows take column
+    0, and a single finite value among -inf wins.  At V = 163840 the planted
+    columns 512..639 lie in the slices whose W2 rows sit in LDS."""
+    B, M, r = 16, 2, 32
+    w = wl.WORKLOADS["temperature_draft_256x8"]
+    inp = wl.make_inputs(w, B=B, M=M, V=V, r=r, seed=23)
+    base = wl.bf16_bits_to_f32(inp["base"]).copy()
+    nan, inf = np.float32(np.nan), np.float32(np.inf)
+    a, b2 = (600, 620) if V > 8192 else (777, 5000)
+    for b in range(B):
+        kind = b % 5
+        row = base[b]
+        if kind == 0:
+            row[:, b2] = nan
+            row[:, a] = nan
+        elif kind == 1:
+            row[:, [530, 515]] = inf
+        elif kind == 2:
+            row[:] = -inf
+        elif kind == 3:
+            row[:] = -inf
+            row[:, a] = -1e30
+    inp["base"] = wl.to_bf16_bits(base)
+    inp["w2"] = np.zeros_like(inp["w2"])
+    tok, corr = run_sample(inp, 0.7, seed=5)
+    expect = {0: min(a, b2), 1: 515, 2: 0, 3: a}
+    for b in range(B):
+        if b % 5 in expect:
+            assert (tok[b] == expect[b % 5]).all(), (b, tok[b])
+    check_chain(inp, 0.7, 5, tok, corr, name=f"temperature special values V{V}")
+
+
 def test_apply_beyond_31_bit_offsets(native):
     """16640 rows at V = 129280 (2.15e9 bf16 logits, 4.3 GB): element offsets
     pass 2^31, so the apply leaves the grouped and row-order kernels for the
