@@ -20,19 +20,17 @@
 // Operands.  The inner dimension is cut into chunks of 32: first the r/32
 // chunks of the bias (A: the gathered W1 rows of the tile's rows, B: the
 // tile's W2w rows), then the d/32 chunks of the head (A: hidden rows, B: head
-// weight rows).  The two operands take different roads into LDS:
-//   * B (8 KB a chunk, the HBM stream of the head weight) goes straight into
-//     LDS with buffer loads to LDS issued by waves 0-3, into one of five
-//     stages, four chunks ahead of use;
-//   * A (20 KB a chunk, the hidden rows every tile re-reads, L2-resident)
-//     is loaded into registers by waves 4-7 a chunk ahead and written to one
-//     of two LDS buffers: buffer loads to LDS issue far too slowly for 28 KB
-//     a chunk (measured ~1,500 cycles per 4 per wave), plain loads do not.
-// Each wave's memory counter thus holds one kind of load only, so the long
-// B lead survives the short A waits.  The chunk stream runs on across
-// tiles, so the pipeline never drains at a tile edge.  A row's four 16-byte
-// pieces sit at positions q ^ ((row / 2) % 4), which keeps the 16-lane
-// fragment reads free of bank conflicts.  After the bias chunks the
+// weight rows).  Both reach LDS by buffer loads to LDS (1 KB of 16 operand
+// rows per instruction), into one of five stages, four chunks ahead of use:
+// a chunk is 20 such loads for A (the hidden rows every tile re-reads,
+// L2-resident) and 8 for B (the HBM stream of the head weight), dealt over
+// all eight waves four each (the last four to a junk block, so that every
+// wave's memory counter holds the same count per chunk and one wait before
+// each barrier serves all).  Staging A through registers instead (a chunk
+// ahead, the register file being nearly full) measured 6% slower.  The
+// chunk stream runs on across tiles, so the pipeline never drains at a tile
+// edge.  A row's four 16-byte pieces sit at positions q ^ ((row / 2) % 4),
+// which keeps the 16-lane fragment reads free of bank conflicts.  After the bias chunks the
 // accumulators are rounded to bf16 (the Linear's output dtype), packed and
 // kept; after the head chunks the epilogue adds them in fp32 and stores.
 #include "device_common.h"
@@ -50,20 +48,19 @@ constexpr int kLmStages = 5;
 constexpr int kLmRowBytes = kLmK * 2;         // 64 bytes per operand row and chunk
 constexpr int kLmStageA = kLmRows * kLmRowBytes;   // 20 KB
 constexpr int kLmStageB = kLmCols * kLmRowBytes;   // 8 KB
-constexpr int kLmDmaB = kLmStageB / 1024;          // 1 KB loads to LDS per chunk for B: 8
-constexpr int kLmBWaves = 4;                       // waves 0-3: B loads, 2 each
-constexpr int kLmAPieces = kLmStageA / 16;         // 16-byte pieces of an A chunk: 1280
-constexpr int kLmAPer = kLmAPieces / (64 * (kLmWaves - kLmBWaves));  // per thread of waves 4-7: 5
+constexpr int kLmDmaA = kLmStageA / 1024;          // 1 KB loads to LDS per chunk for A: 20
+constexpr int kLmDmaB = kLmStageB / 1024;          // for B: 8
+constexpr int kLmDmaPer = 4;                       // per wave and chunk (28 real, 4 to a junk block)
 constexpr int kLmEpiStores = 20;                   // 16-byte stores of a wave's tile epilogue
-static_assert(kLmDmaB == 2 * kLmBWaves, "two B loads per B wave");
-static_assert(kLmAPer * 64 * (kLmWaves - kLmBWaves) == kLmAPieces, "A pieces over waves 4-7");
+static_assert(kLmDmaPer * kLmWaves >= kLmDmaA + kLmDmaB, "loads per chunk");
 }  // namespace
 
 __device__ __forceinline__ uint32_t lm_swz(int row, int q) { return (uint32_t)(row * kLmRowBytes + 16 * (q ^ ((row >> 1) & 3))); }
 
 __global__ __launch_bounds__(kLmThreads) void markov_lm_head_bf16(LmHeadParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_b[kLmStages * kLmStageB];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_a[2 * kLmStageA];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_a[kLmStages * kLmStageA];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_junk[1024];
   __shared__ int32_t lds_e[kLmRows];  // gathered W1 row of each tile row (element offset), -1: zero
 
   const int tid = threadIdx.x;
@@ -102,58 +99,49 @@ __global__ __launch_bounds__(kLmThreads) void markov_lm_head_bf16(LmHeadParams p
     *k0 = (*bias ? c : c - nb) * kLmK;
     *K = *bias ? r : d;
   };
-  // B of chunk g into its stage (waves 0-3): wave w's loads move B rows
-  // 16 (w + 4 j) .. +15; lane l moves piece position l % 4 of row l / 4
-  // (logical piece q = position ^ ((row / 2) % 4)).
-  auto issue_b = [&](int g) __attribute__((always_inline)) {
+  const BufferWords bw_w1 = buffer_words(p.w1, (uint32_t)V * (uint32_t)r * 2u);
+  const BufferWords bw_h = buffer_words(p.hidden, (uint32_t)R * (uint32_t)d * 2u);
+  // Chunk g's operands into stage g % kLmStages: load d = wave + 8 j moves
+  // 16 operand rows (1 KB): d < 20 the A rows 16 d .., d < 28 the B rows
+  // 16 (d - 20) .., the rest a junk block (every wave issues the same count,
+  // so the waits are uniform).  Lane l moves piece position l % 4 of row
+  // l / 4 (logical piece q = position ^ ((row / 2) % 4)).
+  auto issue = [&](int g) __attribute__((always_inline)) {
     int tile, k0, K;
     bool bias;
     chunk_of(g, &tile, &bias, &k0, &K);
-    const uint32_t stage = (uint32_t)(g % kLmStages) * kLmStageB;
+    const uint32_t st = (uint32_t)(g % kLmStages);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int i = wave + kLmBWaves * j;
-      const int row = 16 * i + (lane >> 2);
-      const int q = (lane & 3) ^ ((row >> 1) & 3);
-      const int k = k0 + 8 * q;
-      const int v = tile * kLmCols + row;
-      const uint32_t off = (v < V && k < K) ? 2u * ((uint32_t)v * (uint32_t)K + (uint32_t)k) : kBufferOob;
-      const uint32_t dst = lds_address(&lds_b[stage + (uint32_t)(16 * i) * kLmRowBytes]);
-      if (bias) load_lds16(bw_w2, off, dst);
-      else load_lds16(bw_lm, off, dst);
-    }
-  };
-  // A of chunk g into registers (waves 4-7): thread t of those waves loads
-  // pieces p = t + 256 j, row p / 4, logical piece p % 4
-  const __amdgpu_buffer_rsrc_t rs_w1 = buffer_rsrc(p.w1, (uint32_t)V * (uint32_t)r * 2u);
-  const __amdgpu_buffer_rsrc_t rs_h = buffer_rsrc(p.hidden, (uint32_t)R * (uint32_t)d * 2u);
-  const int ta = tid - 64 * kLmBWaves;
-  u32x4_t areg[kLmAPer];
-  auto load_a = [&](int g) __attribute__((always_inline)) {
-    int tile, k0, K;
-    bool bias;
-    chunk_of(g, &tile, &bias, &k0, &K);
-#pragma unroll
-    for (int j = 0; j < kLmAPer; ++j) {
-      const int pc = ta + 256 * j;
-      const int row = pc >> 2, k = k0 + 8 * (pc & 3);
-      const int n = row0 + row;
-      uint32_t off = kBufferOob;
-      if (bias) {
-        const int32_t e = lds_e[row];
-        if (e >= 0 && k < K) off = 2u * (uint32_t)(e + k);
-      } else if (n < R && k < K) {
-        off = 2u * ((uint32_t)n * (uint32_t)d + (uint32_t)k);
+    for (int j = 0; j < kLmDmaPer; ++j) {
+      const int dd = wave + kLmWaves * j;
+      if (dd < kLmDmaA) {
+        const int row = 16 * dd + (lane >> 2);
+        const int q = (lane & 3) ^ ((row >> 1) & 3);
+        const int k = k0 + 8 * q;
+        const int n = row0 + row;
+        uint32_t off = kBufferOob;
+        if (bias) {
+          const int32_t e = lds_e[row];
+          if (e >= 0 && k < K) off = 2u * (uint32_t)(e + k);
+        } else if (n < R && k < K) {
+          off = 2u * ((uint32_t)n * (uint32_t)d + (uint32_t)k);
+        }
+        const uint32_t dst = lds_address(&lds_a[st * kLmStageA + (uint32_t)(16 * dd) * kLmRowBytes]);
+        if (bias) load_lds16(bw_w1, off, dst);
+        else load_lds16(bw_h, off, dst);
+      } else if (dd < kLmDmaA + kLmDmaB) {
+        const int i = dd - kLmDmaA;
+        const int row = 16 * i + (lane >> 2);
+        const int q = (lane & 3) ^ ((row >> 1) & 3);
+        const int k = k0 + 8 * q;
+        const int v = tile * kLmCols + row;
+        const uint32_t off = (v < V && k < K) ? 2u * ((uint32_t)v * (uint32_t)K + (uint32_t)k) : kBufferOob;
+        const uint32_t dst = lds_address(&lds_b[st * kLmStageB + (uint32_t)(16 * i) * kLmRowBytes]);
+        if (bias) load_lds16(bw_w2, off, dst);
+        else load_lds16(bw_lm, off, dst);
+      } else {
+        load_lds16(bw_lm, kBufferOob, lds_address(&lds_junk[0]));
       }
-      areg[j] = __builtin_amdgcn_raw_buffer_load_b128(bias ? rs_w1 : rs_h, off, 0, 0);
-    }
-  };
-  auto store_a = [&](int g) __attribute__((always_inline)) {
-    const uint32_t buf = (uint32_t)(g & 1) * kLmStageA;
-#pragma unroll
-    for (int j = 0; j < kLmAPer; ++j) {
-      const int pc = ta + 256 * j;
-      *(u32x4_t*)&lds_a[buf + lm_swz(pc >> 2, pc & 3)] = areg[j];
     }
   };
 
@@ -167,35 +155,25 @@ __global__ __launch_bounds__(kLmThreads) void markov_lm_head_bf16(LmHeadParams p
       bias_pk[i][j][0] = bias_pk[i][j][1] = 0u;
     }
 
-  const bool bwave = wave < kLmBWaves;
-  if (bwave) {
-    for (int g = 0; g < kLmStages - 1 && g < G; ++g) issue_b(g);
-  } else if (G > 0) {
-    load_a(0);
-  }
+  for (int g = 0; g < kLmStages - 1 && g < G; ++g) issue(g);
   int last_epi = -kLmStages;  // iteration of the last epilogue (its stores count in the waits)
 
   for (int g = 0; g < G; ++g) {
-    if (bwave) {
-      // chunk g's B loads are in LDS: later chunks' loads (and epilogue
+    {
+      // chunk g's loads are in LDS: later chunks' loads (and epilogue
       // stores issued after them) may stay in flight
       const bool tail = g + kLmStages - 2 >= G;
       const bool epi = g > last_epi && g <= last_epi + kLmStages - 1;
       if (tail) wait_vmcnt<0>();
-      else if (epi) wait_vmcnt<2 * (kLmStages - 2) + kLmEpiStores>();
-      else wait_vmcnt<2 * (kLmStages - 2)>();
-    } else {
-      // chunk g's A rows (loaded a chunk ago) into their LDS buffer, then
-      // the next chunk's A rows into registers
-      store_a(g);
-      if (g + 1 < G) load_a(g + 1);
+      else if (epi) wait_vmcnt<kLmDmaPer * (kLmStages - 2) + kLmEpiStores>();
+      else wait_vmcnt<kLmDmaPer * (kLmStages - 2)>();
     }
     lds_barrier();
-    if (bwave && g + kLmStages - 1 < G) issue_b(g + kLmStages - 1);
+    if (g + kLmStages - 1 < G) issue(g + kLmStages - 1);
 
     // chunk g: 5 row blocks x 4 column blocks of this wave
     const uint32_t stage = (uint32_t)(g % kLmStages) * kLmStageB;
-    const uint32_t abuf = (uint32_t)(g & 1) * kLmStageA;
+    const uint32_t abuf = (uint32_t)(g % kLmStages) * kLmStageA;
     bf16x8_t fa[4], fb[5];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
