@@ -20,19 +20,25 @@
 // Operands.  The inner dimension is cut into chunks of 32: first the r/32
 // chunks of the bias (A: the gathered W1 rows of the tile's rows, B: the
 // tile's W2w rows), then the d/32 chunks of the head (A: hidden rows, B: head
-// weight rows).  Both reach LDS by buffer loads to LDS (1 KB of 16 operand
-// rows per instruction), into one of five stages, four chunks ahead of use:
-// a chunk is 20 such loads for A (the hidden rows every tile re-reads,
-// L2-resident) and 8 for B (the HBM stream of the head weight), dealt over
-// all eight waves four each (the last four to a junk block, so that every
-// wave's memory counter holds the same count per chunk and one wait before
-// each barrier serves all).  Staging A through registers instead (a chunk
-// ahead, the register file being nearly full) measured 6% slower.  The
-// chunk stream runs on across tiles, so the pipeline never drains at a tile
-// edge.  A row's four 16-byte pieces sit at positions q ^ ((row / 2) % 4),
-// which keeps the 16-lane fragment reads free of bank conflicts.  After the bias chunks the
-// accumulators are rounded to bf16 (the Linear's output dtype), packed and
-// kept; after the head chunks the epilogue adds them in fp32 and stores.
+// weight rows), each count padded to an even number with chunks whose
+// operands are zeros (they add exact zeros).  The operands take two roads
+// into LDS, both over all eight waves:
+//   * B (8 KB a chunk, the HBM stream of the head weight): one buffer load
+//     to LDS per wave and chunk, into one of five stages, four chunks ahead;
+//   * A (20 KB a chunk, the hidden rows every tile re-reads, L2-resident):
+//     two or three 16-byte register loads per thread, two chunks ahead in
+//     two register sets (even chunks in one, odd in the other, so both are
+//     named statically), written to one of two LDS buffers a step before
+//     use.  Loads to LDS alone for A as well measured 15-20% slower: they
+//     move about 16 bytes per cycle per CU, which at 28 KB a chunk is the
+//     chunk's whole time.
+// Every wave issues the same operations per chunk (the loads past the last
+// chunk go to a junk block or read zeros), so one wait count serves all.
+// A row's four 16-byte pieces sit at positions q ^ ((row / 2) % 4), which
+// keeps the 16-lane fragment reads free of bank conflicts.  After a tile's
+// bias chunks the accumulators are rounded to bf16 (the Linear's output
+// dtype), packed and kept; after its head chunks the epilogue adds them in
+// fp32 and stores; the chunk stream runs on across tiles.
 #include "device_common.h"
 #include "markov_kernels.h"
 
@@ -44,22 +50,23 @@ constexpr int kLmThreads = kLmWaves * 64;
 constexpr int kLmRows = 320;                  // rows of a tile (20 blocks of 16)
 constexpr int kLmCols = 128;                  // vocabulary columns of a tile (8 blocks of 16)
 constexpr int kLmK = 32;                      // inner-dimension chunk (one matrix instruction)
-constexpr int kLmStages = 5;
+constexpr int kLmStages = 5;                  // B stages in LDS (four chunks ahead)
 constexpr int kLmRowBytes = kLmK * 2;         // 64 bytes per operand row and chunk
 constexpr int kLmStageA = kLmRows * kLmRowBytes;   // 20 KB
 constexpr int kLmStageB = kLmCols * kLmRowBytes;   // 8 KB
-constexpr int kLmDmaA = kLmStageA / 1024;          // 1 KB loads to LDS per chunk for A: 20
-constexpr int kLmDmaB = kLmStageB / 1024;          // for B: 8
-constexpr int kLmDmaPer = 4;                       // per wave and chunk (28 real, 4 to a junk block)
+constexpr int kLmAPieces = kLmStageA / 16;         // 16-byte pieces of an A chunk: 1280
+constexpr int kLmAPer = 3;                         // A loads per thread and chunk (the last for threads < 256)
+constexpr int kLmOps = kLmAPer + 1;                // memory operations of a wave per chunk (A loads, one B load)
 constexpr int kLmEpiStores = 20;                   // 16-byte stores of a wave's tile epilogue
-static_assert(kLmDmaPer * kLmWaves >= kLmDmaA + kLmDmaB, "loads per chunk");
+static_assert(kLmStageB / 1024 == kLmWaves, "one B load per wave and chunk");
+static_assert(kLmAPer * kLmThreads >= kLmAPieces && (kLmAPer - 1) * kLmThreads < kLmAPieces, "A pieces");
 }  // namespace
 
 __device__ __forceinline__ uint32_t lm_swz(int row, int q) { return (uint32_t)(row * kLmRowBytes + 16 * (q ^ ((row >> 1) & 3))); }
 
 __global__ __launch_bounds__(kLmThreads) void markov_lm_head_bf16(LmHeadParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_b[kLmStages * kLmStageB];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_a[kLmStages * kLmStageA];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_a[2 * kLmStageA];
   __shared__ __attribute__((aligned(16))) unsigned char lds_junk[1024];
   __shared__ int32_t lds_e[kLmRows];  // gathered W1 row of each tile row (element offset), -1: zero
 
@@ -70,8 +77,11 @@ __global__ __launch_bounds__(kLmThreads) void markov_lm_head_bf16(LmHeadParams p
   const int R = (int)p.rows, V = (int)p.V, r = (int)p.r, d = (int)p.d;
   const int row0 = blockIdx.y * kLmRows;
   const int ntiles = (V + kLmCols - 1) / kLmCols;
-  const int nb = (r + kLmK - 1) / kLmK;         // bias chunks per tile
-  const int C = nb + (d + kLmK - 1) / kLmK;     // chunks per tile
+  // chunks per tile: the bias's, then the head's, each padded to an even
+  // count (a padded chunk's operands are zeros and add nothing), so the
+  // two register sets of the A stream alternate in a fixed order
+  const int nb = ((r + kLmK - 1) / kLmK + 1) & ~1;
+  const int C = nb + (((d + kLmK - 1) / kLmK + 1) & ~1);
   const int my_tiles = blockIdx.x < (unsigned)ntiles ? (ntiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
   const int G = my_tiles * C;                   // chunks of this workgroup
 
@@ -91,6 +101,8 @@ __global__ __launch_bounds__(kLmThreads) void markov_lm_head_bf16(LmHeadParams p
   const BufferWords bw_w2 = buffer_words(p.w2, (uint32_t)V * (uint32_t)r * 2u);
   const BufferWords bw_lm = buffer_words(p.lm, (uint32_t)V * (uint32_t)d * 2u);
   const __amdgpu_buffer_rsrc_t rs_out = buffer_rsrc(p.out, (uint32_t)R * (uint32_t)V * 4u);
+  const __amdgpu_buffer_rsrc_t rs_w1 = buffer_rsrc(p.w1, (uint32_t)V * (uint32_t)r * 2u);
+  const __amdgpu_buffer_rsrc_t rs_h = buffer_rsrc(p.hidden, (uint32_t)R * (uint32_t)d * 2u);
 
   auto chunk_of = [&](int g, int* tile, bool* bias, int* k0, int* K) __attribute__((always_inline)) {
     const int t = g / C, c = g - t * C;
@@ -99,49 +111,52 @@ __global__ __launch_bounds__(kLmThreads) void markov_lm_head_bf16(LmHeadParams p
     *k0 = (*bias ? c : c - nb) * kLmK;
     *K = *bias ? r : d;
   };
-  const BufferWords bw_w1 = buffer_words(p.w1, (uint32_t)V * (uint32_t)r * 2u);
-  const BufferWords bw_h = buffer_words(p.hidden, (uint32_t)R * (uint32_t)d * 2u);
-  // Chunk g's operands into stage g % kLmStages: load d = wave + 8 j moves
-  // 16 operand rows (1 KB): d < 20 the A rows 16 d .., d < 28 the B rows
-  // 16 (d - 20) .., the rest a junk block (every wave issues the same count,
-  // so the waits are uniform).  Lane l moves piece position l % 4 of row
-  // l / 4 (logical piece q = position ^ ((row / 2) % 4)).
-  auto issue = [&](int g) __attribute__((always_inline)) {
+  // B of chunk g into its stage: wave w moves B rows 16 w .. +15; lane l
+  // moves piece position l % 4 of row l / 4 (logical piece q = position ^
+  // ((row / 2) % 4)).  Past the last chunk a load to a junk block keeps the
+  // memory counts uniform.
+  auto issue_b = [&](int g) __attribute__((always_inline)) {
+    if (g >= G) {
+      load_lds16(bw_lm, kBufferOob, lds_address(&lds_junk[0]));
+      return;
+    }
     int tile, k0, K;
     bool bias;
     chunk_of(g, &tile, &bias, &k0, &K);
-    const uint32_t st = (uint32_t)(g % kLmStages);
+    const uint32_t stage = (uint32_t)(g % kLmStages) * kLmStageB;
+    const int row = 16 * wave + (lane >> 2);
+    const int q = (lane & 3) ^ ((row >> 1) & 3);
+    const int k = k0 + 8 * q;
+    const int v = tile * kLmCols + row;
+    const uint32_t off = (v < V && k < K) ? 2u * ((uint32_t)v * (uint32_t)K + (uint32_t)k) : kBufferOob;
+    const uint32_t dst = lds_address(&lds_b[stage + (uint32_t)(16 * wave) * kLmRowBytes]);
+    if (bias) load_lds16(bw_w2, off, dst);
+    else load_lds16(bw_lm, off, dst);
+  };
+  // A of chunk g into registers: thread t loads pieces t + 512 j (row
+  // piece / 4, logical piece piece % 4); zeros past the last chunk, past
+  // the 1280 pieces, for bad ids and past the rows
+  auto load_a = [&](int g, u32x4_t (&areg)[kLmAPer]) __attribute__((always_inline)) {
+    int tile, k0, K;
+    bool bias;
+    chunk_of(g < G ? g : 0, &tile, &bias, &k0, &K);
 #pragma unroll
-    for (int j = 0; j < kLmDmaPer; ++j) {
-      const int dd = wave + kLmWaves * j;
-      if (dd < kLmDmaA) {
-        const int row = 16 * dd + (lane >> 2);
-        const int q = (lane & 3) ^ ((row >> 1) & 3);
-        const int k = k0 + 8 * q;
-        const int n = row0 + row;
-        uint32_t off = kBufferOob;
-        if (bias) {
-          const int32_t e = lds_e[row];
-          if (e >= 0 && k < K) off = 2u * (uint32_t)(e + k);
-        } else if (n < R && k < K) {
-          off = 2u * ((uint32_t)n * (uint32_t)d + (uint32_t)k);
-        }
-        const uint32_t dst = lds_address(&lds_a[st * kLmStageA + (uint32_t)(16 * dd) * kLmRowBytes]);
-        if (bias) load_lds16(bw_w1, off, dst);
-        else load_lds16(bw_h, off, dst);
-      } else if (dd < kLmDmaA + kLmDmaB) {
-        const int i = dd - kLmDmaA;
-        const int row = 16 * i + (lane >> 2);
-        const int q = (lane & 3) ^ ((row >> 1) & 3);
-        const int k = k0 + 8 * q;
-        const int v = tile * kLmCols + row;
-        const uint32_t off = (v < V && k < K) ? 2u * ((uint32_t)v * (uint32_t)K + (uint32_t)k) : kBufferOob;
-        const uint32_t dst = lds_address(&lds_b[st * kLmStageB + (uint32_t)(16 * i) * kLmRowBytes]);
-        if (bias) load_lds16(bw_w2, off, dst);
-        else load_lds16(bw_lm, off, dst);
-      } else {
-        load_lds16(bw_lm, kBufferOob, lds_address(&lds_junk[0]));
-      }
+    for (int j = 0; j < kLmAPer; ++j) {
+      const int pc = tid + kLmThreads * j;
+      const int row = (pc >> 2) < kLmRows ? (pc >> 2) : 0, k = k0 + 8 * (pc & 3);
+      const int n = row0 + row;
+      const int32_t e = lds_e[row];
+      const bool ok = g < G && pc < kLmAPieces && k < K && (bias ? e >= 0 : n < R);
+      const uint32_t off = !ok ? kBufferOob : bias ? 2u * (uint32_t)(e + k) : 2u * ((uint32_t)n * (uint32_t)d + (uint32_t)k);
+      areg[j] = __builtin_amdgcn_raw_buffer_load_b128(bias ? rs_w1 : rs_h, off, 0, 0);
+    }
+  };
+  auto store_a = [&](int g, const u32x4_t (&areg)[kLmAPer]) __attribute__((always_inline)) {
+    const uint32_t buf = (uint32_t)(g & 1) * kLmStageA;
+#pragma unroll
+    for (int j = 0; j < kLmAPer; ++j) {
+      const int pc = tid + kLmThreads * j;
+      if (j < kLmAPer - 1 || pc < kLmAPieces) *(u32x4_t*)&lds_a[buf + lm_swz(pc >> 2, pc & 3)] = areg[j];
     }
   };
 
@@ -155,25 +170,34 @@ __global__ __launch_bounds__(kLmThreads) void markov_lm_head_bf16(LmHeadParams p
       bias_pk[i][j][0] = bias_pk[i][j][1] = 0u;
     }
 
-  for (int g = 0; g < kLmStages - 1 && g < G; ++g) issue(g);
-  int last_epi = -kLmStages;  // iteration of the last epilogue (its stores count in the waits)
+  // in flight before the loop: B of chunks 0..3, A of chunks 0..1; chunk
+  // g's step then issues A of g+2 and B of g+4 (kLmOps operations)
+  u32x4_t a0[kLmAPer], a1[kLmAPer];
+  issue_b(0);
+  issue_b(1);
+  load_a(0, a0);
+  issue_b(2);
+  load_a(1, a1);
+  issue_b(3);
+  int epi_left = 0;  // steps whose waits still see an epilogue's 20 stores
 
-  for (int g = 0; g < G; ++g) {
-    {
-      // chunk g's loads are in LDS: later chunks' loads (and epilogue
-      // stores issued after them) may stay in flight
-      const bool tail = g + kLmStages - 2 >= G;
-      const bool epi = g > last_epi && g <= last_epi + kLmStages - 1;
-      if (tail) wait_vmcnt<0>();
-      else if (epi) wait_vmcnt<kLmDmaPer * (kLmStages - 2) + kLmEpiStores>();
-      else wait_vmcnt<kLmDmaPer * (kLmStages - 2)>();
+  // one chunk's products (A of chunk g is in `areg`, register set g % 2)
+  auto mstep = [&](int g, u32x4_t (&areg)[kLmAPer]) __attribute__((always_inline)) {
+    // A of chunk g (and B of chunks g and g+1, issued before it) complete;
+    // the operations issued after them may stay in flight: B of g+2 and
+    // one step's worth, plus an epilogue's stores among them
+    if (epi_left > 0) {
+      wait_vmcnt<1 + kLmOps + kLmEpiStores>();
+      --epi_left;
+    } else {
+      wait_vmcnt<1 + kLmOps>();
     }
+    store_a(g, areg);
+    load_a(g + 2, areg);
     lds_barrier();
-    if (g + kLmStages - 1 < G) issue(g + kLmStages - 1);
-
-    // chunk g: 5 row blocks x 4 column blocks of this wave
+    issue_b(g + 4);
     const uint32_t stage = (uint32_t)(g % kLmStages) * kLmStageB;
-    const uint32_t abuf = (uint32_t)(g % kLmStages) * kLmStageA;
+    const uint32_t abuf = (uint32_t)(g & 1) * kLmStageA;
     bf16x8_t fa[4], fb[5];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -189,38 +213,48 @@ __global__ __launch_bounds__(kLmThreads) void markov_lm_head_bf16(LmHeadParams p
     for (int i = 0; i < 5; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[j], fb[i], acc[i][j], 0, 0, 0);
-
-    const int c = g % C;
-    if (c == nb - 1) {
-      // the bias of the tile: the Linear's bf16 output; the head starts at zero
-#pragma unroll
-      for (int i = 0; i < 5; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bias_pk[i][j][0] = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-          bias_pk[i][j][1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-          acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-    } else if (c == C - 1) {
-      // epilogue: lane l holds columns 4 (l / 16) .. +3 of row l % 16 of
-      // each block; U + bias in fp32, one 16-byte store per block
-      const int tile = (int)blockIdx.x + (g / C) * (int)gridDim.x;
-#pragma unroll
-      for (int i = 0; i < 5; ++i) {
-        const int n = row0 + 80 * wr + 16 * i + (lane & 15);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int v = tile * kLmCols + 64 * wc + 16 * j + 4 * (lane >> 4);
-          const uint32_t b0 = bias_pk[i][j][0], b1 = bias_pk[i][j][1];
-          const u32x4_t o = u32x4_t{__float_as_uint(acc[i][j][0] + bf16_lo(b0)), __float_as_uint(acc[i][j][1] + bf16_hi(b0)),
-                                    __float_as_uint(acc[i][j][2] + bf16_lo(b1)), __float_as_uint(acc[i][j][3] + bf16_hi(b1))};
-          buffer_store16(rs_out, (n < R && v < V) ? ((uint32_t)n * (uint32_t)V + (uint32_t)v) * 4u : kBufferOob, o);
-          acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-      }
-      last_epi = g;
+  };
+  // chunks g0 .. g0 + n - 1 (g0 and n even): register set a0 for even
+  // chunks, a1 for odd ones
+  auto span = [&](int g0, int n) __attribute__((always_inline)) {
+    for (int g = g0; g < g0 + n; g += 2) {
+      mstep(g, a0);
+      mstep(g + 1, a1);
     }
+  };
+
+  for (int t = 0; t < my_tiles; ++t) {
+    const int gt = t * C;
+    span(gt, nb);
+    // the bias of the tile: the Linear's bf16 output; the head starts at zero
+#pragma unroll
+    for (int i = 0; i < 5; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bias_pk[i][j][0] = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+        bias_pk[i][j][1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+        acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    span(gt + nb, C - nb);
+    // epilogue: lane l holds columns 4 (l / 16) .. +3 of row l % 16 of each
+    // block; U + bias in fp32, one 16-byte store per block
+    const int tile = (int)blockIdx.x + t * (int)gridDim.x;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int n = row0 + 80 * wr + 16 * i + (lane & 15);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v = tile * kLmCols + 64 * wc + 16 * j + 4 * (lane >> 4);
+        const uint32_t b0 = bias_pk[i][j][0], b1 = bias_pk[i][j][1];
+        const u32x4_t o = u32x4_t{__float_as_uint(acc[i][j][0] + bf16_lo(b0)), __float_as_uint(acc[i][j][1] + bf16_hi(b0)),
+                                  __float_as_uint(acc[i][j][2] + bf16_lo(b1)), __float_as_uint(acc[i][j][3] + bf16_hi(b1))};
+        buffer_store16(rs_out, (n < R && v < V) ? ((uint32_t)n * (uint32_t)V + (uint32_t)v) * 4u : kBufferOob, o);
+        acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+    epi_left = 2;
   }
+  wait_vmcnt<0>();
 }
 
 // One workgroup per CU (LDS holds one), the row bands spread over the grid's

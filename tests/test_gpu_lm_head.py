@@ -70,6 +70,7 @@ def test_lm_head_teacher_forced_320(native):
     (7, 100, 2048, 256, 256),     # 700 rows: three row bands
     (2, 3, 8, 8, 8),              # the smallest shape
     (4, 80, 4096, 512, 64),       # rank past the head's inner size
+    (2, 5, 40000, 24, 1032),      # odd bias and head chunk counts (padded), two tiles on some workgroups
 ])
 def test_lm_head_shapes(native, B, M, V, r, d):
     w = wl.WORKLOADS["lm_head_teacher_forced_320"]
