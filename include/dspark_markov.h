@@ -127,13 +127,15 @@ dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_
  *                        split across calls, reproduce one whole call.
  * M == 0 or B == 0 is a successful no-op.  V == 0 with B*M > 0 is invalid.
  *
- * Greedy bf16 calls with B <= 64, M <= 16 and r <= 256, and temperature bf16
- * calls with B <= 256, M * B <= 4096, r <= 256 and V <= 640 * CUs, run as
- * one persistent launch whose workgroups (one per CU) exchange each step's
- * tokens through the workspace; the host takes that path only when the
- * occupancy query says a CU can hold one of its workgroups (other calls run
- * one step kernel per position).  The tokens are the same on both paths.  Should a workgroup still be unable to
- * start (CUs held by other streams' kernels), the others give up waiting
+ * Greedy calls with bf16 weights (bf16 or fp32 logits), B <= 64, M <= 16
+ * and r <= 256, and temperature bf16 calls with B <= 256, M * B <= 4096,
+ * r <= 256 and V <= 640 * CUs, run as one persistent launch whose
+ * workgroups (one per CU) exchange each step's tokens through the
+ * workspace; the host takes that path only when the occupancy query says a
+ * CU can hold one of its workgroups (other calls run one step kernel per
+ * position).  The tokens are the same on both paths.  Should a workgroup
+ * still be unable to start (CUs held by other streams' kernels), the
+ * others give up waiting
  * after 1 s instead of hanging: the call then writes -1 to every token of
  * sampled_tokens (corrected_logits is then undefined) and records the
  * failure in the workspace.  Until dspark_markov_read_device_error reads

@@ -341,13 +341,15 @@ dspark_status_t sample_block_impl(const void* base_logits, dspark_dtype_t logits
   hipStream_t s = (hipStream_t)stream;
   Control* ctl = (Control*)workspace;
 
-  // Greedy bf16 chains that fit the persistent kernel run in one launch.
+  // Greedy chains with bf16 weights (bf16 or fp32 logits) that fit the
+  // persistent kernel run in one launch.
   const int cus = device_cus();
-  if (tile && greedy && cus > 0 && B <= dspark::chain_max_rows() && M <= kChainMaxSteps &&
+  if ((tile || f32_tile) && greedy && cus > 0 && B <= dspark::chain_max_rows() && M <= kChainMaxSteps &&
       (V + 31) / 32 <= (int64_t)cus * dspark::chain_waves_per_group()) {
     dspark::ChainParams c{};
-    c.base = (const uint16_t*)base_logits;
-    c.out = (uint16_t*)corrected_logits;
+    c.base = base_logits;
+    c.out = corrected_logits;
+    c.lf32 = !tile;
     c.first_prev = first_prev_token_ids;
     c.tokens = sampled_tokens;
     c.w1 = (const uint16_t*)w1;

@@ -20,8 +20,8 @@ constexpr int kKeyPad = 8;
 constexpr size_t kChainSyncBytes = 4096;
 
 struct ChainParams {
-  const uint16_t* base;       // [B, M, V]
-  uint16_t* out;              // [B, M, V] or null
+  const void* base;           // [B, M, V] bf16, or fp32 when lf32
+  void* out;                  // [B, M, V] like base, or null
   const int64_t* first_prev;  // [B]
   int64_t* tokens;            // [B, M]
   const uint16_t* w1;         // [V, r]
@@ -36,6 +36,7 @@ struct ChainParams {
   int64_t V;
   int64_t r;
   int64_t S;                  // 32-column vocabulary slices
+  bool lf32;                  // fp32 logits (bf16 weights either way)
 };
 
 // Arguments of the persistent temperature chain (bf16): keys holds one

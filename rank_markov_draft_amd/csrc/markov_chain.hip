@@ -19,7 +19,8 @@
 //     units to complete in;
 //   * window w: every wave multiplies group g's gathered W1 rows by its
 //     slice on the matrix cores (v_mfma_f32_16x16x32_bf16), rounds the bias
-//     to bf16, adds it to the group's base logits staged in LDS, writes the
+//     to bf16, adds it to the group's base logits staged in LDS (bf16, or
+//     fp32 as the drafter's vocabulary head produces them), writes the
 //     corrected values back in place and folds each row's best column into
 //     a per-row LDS key.  One barrier ends the window;
 //   * the memory traffic is issued around the matrix work and overlaps that
@@ -44,6 +45,8 @@
 // tokens.  A
 // launch that finds the failure count already nonzero (a failure nobody has
 // read back and cleared) does no work and also returns -1 tokens.
+#include <type_traits>
+
 #include "chain_common.h"
 #include "device_common.h"
 #include "markov_chain.h"
@@ -62,7 +65,6 @@ constexpr int kMaxGroups = 4;                 // row groups of a call at most
 constexpr int kGroupRows = 16;                // rows of a group at most (the MFMA N tile)
 constexpr int kMaxRows = 64;                  // batch rows of one call
 constexpr int kGroups = kChainKeyGroups;      // key slots / arrival counters per row group
-constexpr int kPitch = 2 * 32 * kWaves + 16;  // LDS bytes of a staged row (512 columns + pad)
 static_assert(kMaxGroups * kGroupRows >= kMaxRows && kMaxGroups <= kSlots, "row groups");
 
 // Synchronisation area, one 64-byte line per word: the arrival counters
@@ -91,15 +93,25 @@ __device__ __forceinline__ uint32_t argmax_code_bf16(uint32_t h) {
 
 }  // namespace
 
-template <int K32>
+template <int K32, bool LF32>
 __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams p) {
-  // Gathered W1 rows per group, in the B-operand order of the matrix
-  // instruction: block kk holds at lane l's 16 bytes row l % 16, rank
-  // elements 32 kk + 8 (l / 16) .. +7.
-  __shared__ __attribute__((aligned(16))) unsigned char lds_e[kMaxGroups][K32 * 1024];
+  // bf16 or (LF32) fp32 logits: bytes per logit, 1 KB segments of a staged
+  // row of 512 columns, LDS bytes of a staged row
+  constexpr int kEl = LF32 ? 4 : 2;
+  constexpr int kSegs = LF32 ? 2 : 1;
+  constexpr int kPitch = 32 * kWaves * kEl + 16;
+  // Gathered W1 rows, in the B-operand order of the matrix instruction:
+  // block kk holds at lane l's 16 bytes row l % 16, rank elements 32 kk +
+  // 8 (l / 16) .. +7.  One buffer per group with bf16 logits; with fp32
+  // logits (whose staged rows take twice the LDS) two, by unit parity.
+  constexpr int kEBufs = LF32 ? 2 : kMaxGroups;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_e[kEBufs][K32 * 1024];
   // Staged logits per group: base, then corrected in place.
   __shared__ __attribute__((aligned(16))) unsigned char lds_x[kMaxGroups][kGroupRows * kPitch];
-  __shared__ uint32_t lds_key[kMaxGroups][16];
+  // Per-row best keys: bf16 packs a 16-bit order code and the column in the
+  // workgroup into 32 bits; fp32 keeps the 64-bit argmax key.
+  using key_t = typename std::conditional<LF32, unsigned long long, uint32_t>::type;
+  __shared__ key_t lds_key[kMaxGroups][16];
   // Key slots loaded for a token merge, two buffers of [lane] 16 bytes each,
   // the key in the first 8 (row l % 16, key group 2 (l / 16) + j).
   __shared__ __attribute__((aligned(16))) unsigned char lds_kv[2][2 * 1024];
@@ -120,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
       __builtin_amdgcn_readfirstlane((int)__hip_atomic_load(p.sync_failures, __ATOMIC_RELAXED,
                                                             __HIP_MEMORY_SCOPE_AGENT)) != 0;
   const bool force_timeout = __builtin_amdgcn_readfirstlane((int)*p.test_hook) != 0;
-  // The host guarantees B <= 64, V <= 32 * 16 * CUs, B*M*V < 2^30 and
+  // The host guarantees B <= 64, V <= 32 * 16 * CUs, B*M*V*kEl < 2^31 and
   // M <= 4096, so every index below fits in 32 bits.
   const int B = (int)p.B, M = (int)p.M, V = (int)p.V, r = (int)p.r;
   // Rows are dealt into NR <= kMaxGroups groups of rpg <= 16.  A step has
@@ -140,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   const int slice = s_begin + wave;
   const bool has = slice < s_end;
 
-  const uint32_t bytes = (uint32_t)(B * M * V * 2);
+  const uint32_t bytes = (uint32_t)(B * M * V * kEl);
   const __amdgpu_buffer_rsrc_t rs_out = buffer_rsrc(p.out, p.out != nullptr ? bytes : 0u);
   const BufferWords bw_w1 = buffer_words(p.w1, (uint32_t)(V * r * 2));
   const BufferWords bw_keys = buffer_words(p.keys, (uint32_t)(M * kGroups * kMaxRows * kKeyPad * 8));
@@ -170,35 +182,44 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   // them; a wave waits for them only at the end of the window before that
   // unit.  Offsets of masked-off lanes, rows or steps point past the buffer
   // (see buffer_rsrc), so every instruction is issued unconditionally.
+  // Segment h of a row is its columns vbeg + 1024 h / kEl ..: lane l moves
+  // the 16 bytes of columns vbeg + (1024 h + 16 l) / kEl .. .
   const int nbulk = wave >= 2 ? (wave < 4 ? 2 : 1) : 0;
   const int brow0 = wave - 2, brow1 = wave + 12;
-  const bool col_ok = vbeg + 8u * (uint32_t)lane < vend;
-  const uint32_t lane_off = 2u * (vbeg + 8u * (uint32_t)lane);
-  auto row_offset = [&](int gg, int kd, int row) __attribute__((always_inline)) -> uint32_t {
+  auto row_offset = [&](int gg, int kd, int row, int h) __attribute__((always_inline)) -> uint32_t {
     const int b = gg * rpg + row;
-    const bool ok = row < rpg && b < B && kd < M && col_ok;
-    return ok ? (uint32_t)((b * M + kd) * V) * 2u + lane_off : kBufferOob;
+    const uint32_t col = vbeg + (uint32_t)((1024 * h + 16 * lane) / kEl);
+    const bool ok = row < rpg && b < B && kd < M && col < vend;
+    return ok ? (uint32_t)((b * M + kd) * V) * (uint32_t)kEl + (uint32_t)kEl * col : kBufferOob;
   };
   const BufferWords bw_base = buffer_words(p.base, bytes);
   auto load_row_lds = [&](int gg, int kd, int row) __attribute__((always_inline)) {
-    load_lds16(bw_base, row_offset(gg, kd, row), lds_address(&lds_x[gg][row * kPitch]));
+#pragma unroll
+    for (int h = 0; h < kSegs; ++h)
+      load_lds16(bw_base, row_offset(gg, kd, row, h), lds_address(&lds_x[gg][row * kPitch + 1024 * h]));
   };
   // Corrected row of unit (gg, kd) from LDS to HBM, then the group's next
-  // base row into the same LDS row (the store needs the LDS data first).
+  // base row into the same LDS row (the stores need the LDS data first).
+  auto store_row = [&](int gg, int kd, int row) __attribute__((always_inline)) {
+    u32x4_t v[kSegs];
+#pragma unroll
+    for (int h = 0; h < kSegs; ++h) v[h] = *(const u32x4_t*)&lds_x[gg][row * kPitch + 1024 * h + lane * 16];
+#pragma unroll
+    for (int h = 0; h < kSegs; ++h) buffer_store16(rs_out, row_offset(gg, kd, row, h), v[h]);
+  };
   auto flush_row = [&](int gg, int kd, int row) __attribute__((always_inline)) {
-    const u32x4_t v = *(const u32x4_t*)&lds_x[gg][row * kPitch + lane * 16];
-    buffer_store16(rs_out, row_offset(gg, kd, row), v);
+    store_row(gg, kd, row);
     load_row_lds(gg, kd + 1, row);
   };
 
-  // ---- gather (wave 1): W1 rows of tokens x (lane l: the token of row
-  // l % 16 of group gg, or -1 for a zero row) into lds_e[gg].
-  auto gather = [&](int gg, int x) __attribute__((always_inline)) {
+  // ---- gather: W1 rows of tokens x (lane l: the token of row l % 16 of the
+  // unit's group, or -1 for a zero row) into lds_e[buf].
+  auto gather = [&](int buf, int x) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < K32; ++kk) {
       const int kof = 32 * kk + 8 * g4;
       const uint32_t off = (x >= 0 && kof < r) ? 2u * (uint32_t)(x * r + kof) : kBufferOob;
-      load_lds16(bw_w1, off, lds_address(&lds_e[gg][kk * 1024]));
+      load_lds16(bw_w1, off, lds_address(&lds_e[buf][kk * 1024]));
     }
   };
   // Merge of the key slots in lds_kv[buf] into the tokens of group gg's
@@ -230,26 +251,34 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
                           lds_address(&lds_kv[buf][j * 1024]));
   };
 
+  // Lane l's first token (row l % 16 of group gg), or -1 (an invalid one is
+  // counted as a bad row once, by workgroup 0).
+  auto first_token = [&](int gg) __attribute__((always_inline)) -> int {
+    const int b = gg * rpg + n16;
+    int x = -1;
+    if (n16 < rpg && b < B) {
+      const int64_t x0 = p.first_prev[(uint32_t)b];
+      if (x0 >= 0 && x0 < V) x = (int)x0;
+      else if (g == 0 && g4 == 0) atomicAdd(p.bad_rows, 1u);
+    }
+    return x;
+  };
+  // The gathered rows of unit u: per group with bf16 logits, by parity with
+  // fp32 (where the first step's units past the first two are gathered in
+  // the windows, like the later steps').
+  auto ebuf = [&](int u) __attribute__((always_inline)) -> int { return LF32 ? (u & 1) : u % kSlots; };
+
   // ---- prologue: stage step 0 of every group, gather the first tokens.
   for (int gg = 0; gg < NR; ++gg) {
     if (nbulk >= 1) load_row_lds(gg, 0, brow0);
     if (nbulk >= 2) load_row_lds(gg, 0, brow1);
   }
   if (wave == 1 && !poisoned) {
-    for (int gg = 0; gg < NR; ++gg) {
-      const int b = gg * rpg + n16;
-      int x = -1;
-      if (n16 < rpg && b < B) {
-        const int64_t x0 = p.first_prev[(uint32_t)b];
-        if (x0 >= 0 && x0 < V) x = (int)x0;
-        else if (g == 0 && g4 == 0) atomicAdd(p.bad_rows, 1u);
-      }
-      gather(gg, x);
-    }
+    for (int gg = 0; gg < (LF32 ? (NR < 2 ? NR : 2) : NR); ++gg) gather(ebuf(gg), first_token(gg));
   } else if (wave == 0) {
     if (lane < 16) {
 #pragma unroll
-      for (int gg = 0; gg < kMaxGroups; ++gg) lds_key[gg][lane] = 0u;
+      for (int gg = 0; gg < kMaxGroups; ++gg) lds_key[gg][lane] = 0;
     }
     if (lane == 0) lds_flag = poisoned ? 0 : 1;
   }
@@ -270,14 +299,19 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   auto publish = [&](int u) __attribute__((always_inline)) {
     if (lane < 16) {
       const int gp = u % kSlots, kp = u / kSlots;
-      const uint32_t kw = lds_key[gp][lane];
-      lds_key[gp][lane] = 0u;
+      const key_t kw = lds_key[gp][lane];
+      lds_key[gp][lane] = 0;
       const int b = gp * rpg + lane;
-      if (kw != 0u && lane < rpg && b < B) {
-        const uint64_t code = kw >> 16;
-        const uint32_t col = vbeg + (0xFFFFu - (kw & 0xFFFFu));
-        __hip_atomic_fetch_max((uint64_t*)((unsigned char*)p.keys + key_offset(kp, xg, b)),
-                               (code << 32) | (uint64_t)(0xFFFFFFFFu - col), __ATOMIC_RELAXED,
+      if (kw != 0 && lane < rpg && b < B) {
+        uint64_t key;
+        if constexpr (LF32) {
+          key = kw;
+        } else {
+          const uint64_t code = kw >> 16;
+          const uint32_t col = vbeg + (0xFFFFu - (kw & 0xFFFFu));
+          key = (code << 32) | (uint64_t)(0xFFFFFFFFu - col);
+        }
+        __hip_atomic_fetch_max((uint64_t*)((unsigned char*)p.keys + key_offset(kp, xg, b)), key, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -308,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     const bool role_b = wave == (w & 1);
     const int u1 = w + 1, u2 = w + 2;
     const bool pub = role_a && w >= 1 && real(w - 1);
-    const bool do1 = role_a && u1 < U && u1 >= kSlots && real(u1);
+    const bool do1 = role_a && u1 < U && u1 >= (LF32 ? 2 : kSlots) && real(u1);
     const bool do2 = role_b && ok && u2 < U && u2 >= kSlots && real(u2);
 
     // Bulk rows first: the corrected rows of unit w-1 to HBM, and that
@@ -324,7 +358,12 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
       // the key slots of unit w+1 are in LDS; the gather first: its round
       // trip has the rest of the window
       wait_vmcnt<0>();
-      if (do1) gather(u1 % kSlots, merge(u1 & 1, u1 % kSlots, u1 / kSlots - 1));
+      if (do1) {
+        int x;
+        if constexpr (LF32) x = u1 < kSlots ? first_token(u1) : merge(u1 & 1, u1 % kSlots, u1 / kSlots - 1);
+        else x = merge(u1 & 1, u1 % kSlots, u1 / kSlots - 1);
+        gather(ebuf(u1), x);
+      }
       if (pub) publish(w - 1);
     } else if (do2) {
       // lane l < kGroups loads counter line l of unit w+2's slot
@@ -336,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     // staged base logits in place; each row's best column into lds_key.
     if (has && real(w)) {
       f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{};
-      const unsigned char* eb = &lds_e[gc][lane * 16];
+      const unsigned char* eb = &lds_e[ebuf(w)][lane * 16];
       constexpr int KB = (K32 < 4) ? K32 : 4;
 #pragma unroll
       for (int k0 = 0; k0 < K32; k0 += KB) {
@@ -353,7 +392,34 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
       const int colw = wave * 32 + 8 * g4;  // first of the lane's 8 columns in the workgroup
       // lanes of padding rows (past the group's rows or the batch) stay idle:
       // their all-zero values would send the wave down the exact pass below
-      if (n16 < rpg && gc * rpg + n16 < B) {
+      if constexpr (LF32) {
+        if (n16 < rpg && gc * rpg + n16 < B) {
+          // bias rounded to bf16 (the Linear's output dtype), widened and
+          // added to the fp32 logits with one rounding
+          unsigned char* xp = &lds_x[gc][n16 * kPitch + colw * 4];
+          unsigned long long key = 0ull;
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {  // columns colw + 4 t .. + 3 (accumulators of tile t)
+            const f32x4_t a4 = t ? acc1 : acc0;
+            const u32x4_t bq = *(const u32x4_t*)(xp + 16 * t);
+            const uint32_t bw4[4] = {bq.x, bq.y, bq.z, bq.w};
+            float c4[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              c4[q] = __uint_as_float(bw4[q]) + bf16_lo(pack_bf16x2(a4[q], 0.0f));
+              key = max_u64(key, argmax_key(c4[q], vbeg + (uint32_t)(colw + 4 * t + q)));
+            }
+            *(u32x4_t*)(xp + 16 * t) =
+                u32x4_t{__float_as_uint(c4[0]), __float_as_uint(c4[1]), __float_as_uint(c4[2]), __float_as_uint(c4[3])};
+          }
+          if (vbeg + (uint32_t)colw < vend) {
+            // the row's key slot from the lane count (recomputed here rather
+            // than kept live across the window)
+            const int row = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 15;
+            atomicMax(&lds_key[gc][row], key);
+          }
+        }
+      } else if (n16 < rpg && gc * rpg + n16 < B) {
         // bias rounded to bf16 (the Linear's output dtype)
         const uint32_t bw[4] = {pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
                                 pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
@@ -421,7 +487,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
     // since then issued a store and a load per row.
     if (nbulk > 0 && w + 1 < U && w + 1 >= kSlots && real(w + 1)) {
       int later = 0;
-      for (int x = w - kSlots + 3; x <= w; ++x) later += (x >= 1 && real(x - 1)) ? 2 * nbulk : 0;
+      for (int x = w - kSlots + 3; x <= w; ++x) later += (x >= 1 && real(x - 1)) ? 2 * kSegs * nbulk : 0;
       wait_vmcnt_upto16(later);
     }
     lds_barrier();
@@ -431,10 +497,8 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
   // and count (the last arrival)
   if (lds_flag && real(U - 1)) {
     const int gp = (U - 1) % kSlots, kp = (U - 1) / kSlots;
-    if (nbulk >= 1)
-      buffer_store16(rs_out, row_offset(gp, kp, brow0), *(const u32x4_t*)&lds_x[gp][brow0 * kPitch + lane * 16]);
-    if (nbulk >= 2)
-      buffer_store16(rs_out, row_offset(gp, kp, brow1), *(const u32x4_t*)&lds_x[gp][brow1 * kPitch + lane * 16]);
+    if (nbulk >= 1) store_row(gp, kp, brow0);
+    if (nbulk >= 2) store_row(gp, kp, brow1);
     if (wave == 0) {
       wait_vmcnt<0>();
       publish(U - 1);
@@ -494,9 +558,9 @@ namespace {
 // workgroup still cannot start while the others wait (CUs held by other
 // streams' kernels), their bounded waits end the launch with a recorded
 // synchronisation failure and -1 tokens instead of a hang.
-// Workgroups of markov_chain_greedy_bf16<K32> one CU of the current device
-// can hold, cached per device; the chain needs at least one.
-template <int K32>
+// Workgroups of markov_chain_greedy_bf16<K32, LF32> one CU of the current
+// device can hold, cached per device; the chain needs at least one.
+template <int K32, bool LF32>
 int chain_occupancy() {
   static int cache[64];
   static bool known[64];
@@ -504,7 +568,7 @@ int chain_occupancy() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   if (!known[dev]) {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, markov_chain_greedy_bf16<K32>, kThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, markov_chain_greedy_bf16<K32, LF32>, kThreads, 0) !=
         hipSuccess)
       blocks = 0;
     cache[dev] = blocks;
@@ -515,8 +579,13 @@ int chain_occupancy() {
 
 template <int K32>
 hipError_t launch_chain_k(const ChainParams& p, int grid, hipStream_t s) {
-  if (chain_occupancy<K32>() < 1) return hipErrorNotSupported;
-  hipLaunchKernelGGL((markov_chain_greedy_bf16<K32>), dim3(grid), dim3(kThreads), 0, s, p);
+  if (p.lf32) {
+    if (chain_occupancy<K32, true>() < 1) return hipErrorNotSupported;
+    hipLaunchKernelGGL((markov_chain_greedy_bf16<K32, true>), dim3(grid), dim3(kThreads), 0, s, p);
+  } else {
+    if (chain_occupancy<K32, false>() < 1) return hipErrorNotSupported;
+    hipLaunchKernelGGL((markov_chain_greedy_bf16<K32, false>), dim3(grid), dim3(kThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -530,7 +599,7 @@ int chain_waves_per_group() { return kWaves; }
 hipError_t launch_chain_greedy(const ChainParams& p, int num_cus, hipStream_t s) {
   const int ks = tile_ks_for_rank(p.r);
   if (p.B > kMaxRows || ks == 0 || ks > 16) return hipErrorNotSupported;
-  if (p.B * p.M * p.V >= ((int64_t)1 << 30)) return hipErrorNotSupported;  // byte offsets below 2^31
+  if (p.B * p.M * p.V * (p.lf32 ? 4 : 2) >= ((int64_t)1 << 31)) return hipErrorNotSupported;  // byte offsets below 2^31
   if (p.M > 4096) return hipErrorNotSupported;                              // key area below 2^31 bytes
   if (p.S > (int64_t)num_cus * kWaves) return hipErrorNotSupported;
   switch (ks) {  // rank blocks of 16 -> blocks of 32 (zero-padded)

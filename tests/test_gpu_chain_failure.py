@@ -27,10 +27,11 @@ def _raw_read(ws):
     return st, int(n.value)
 
 
-@pytest.mark.parametrize("T,B", [(0.0, 8), (0.7, 8), (0.7, 40)])
-def test_forced_chain_timeout_gives_sentinel_tokens(native, T, B):
-    M, V, r = 5, 4096, 256                   # bf16: the persistent chains
-    inp = wl.make_inputs(wl.WORKLOADS["greedy_draft_64x5"], B=B, M=M, V=V, r=r, seed=21)
+@pytest.mark.parametrize("T,B,name", [(0.0, 8, "greedy_draft_64x5"), (0.7, 8, "greedy_draft_64x5"),
+                                      (0.7, 40, "greedy_draft_64x5"), (0.0, 24, "greedy_draft_64x5_f32logits")])
+def test_forced_chain_timeout_gives_sentinel_tokens(native, T, B, name):
+    M, V, r = 5, 4096, 256                   # bf16 weights: the persistent chains
+    inp = wl.make_inputs(wl.WORKLOADS[name], B=B, M=M, V=V, r=r, seed=21)
     d = device_inputs({k: inp[k] for k in ("base", "first_prev", "w1", "w2")})
     ws = rmd.Workspace(B, M, V, r, sample=True)
 
@@ -43,7 +44,7 @@ def test_forced_chain_timeout_gives_sentinel_tokens(native, T, B):
     good = from_dev(good)
     assert good.min() >= 0
 
-    print(f"[chain failure] forced timeout, T={T} B={B} M=5 V=4096 r=256", flush=True)
+    print(f"[chain failure] forced timeout, T={T} B={B} M=5 V=4096 r=256 {name}", flush=True)
     ws.set_chain_test_hook(True)
     tok, _ = call()
     torch.cuda.synchronize()

@@ -281,6 +281,39 @@ def test_temperature_chain_shapes(native, B, M, V, r):
     assert np.array_equal(tok2, tok)
 
 
+@pytest.mark.parametrize("B,M,V,r", [
+    (17, 3, 8200, 128),       # two groups of 9 rows, a ragged last workgroup
+    (1, 7, 4096, 64),         # one row, seven steps
+    (64, 1, 20000, 32),       # four groups, one step
+    (33, 4, 65544, 256),      # three groups (the last of one row), a ragged last slice
+])
+def test_f32_logit_greedy_chain_shapes(native, B, M, V, r):
+    """Greedy drafts on fp32 logits with bf16 weights run on the persistent
+    chain's fp32-logit form: every token and corrected logit against the
+    oracle, and the tokens-only call gives the same tokens."""
+    w = wl.WORKLOADS["greedy_draft_64x5_f32logits"]
+    inp = wl.make_inputs(w, B=B, M=M, V=V, r=r, seed=50 + B + M)
+    assert inp["base"].dtype == np.float32
+    tok, corr = run_sample(inp, 0.0)
+    check_chain(inp, 0.0, 0, tok, corr, name=f"f32-logit chain B{B} M{M} V{V} r{r}")
+    tok2, _ = run_sample(inp, 0.0, return_logits=False)
+    assert np.array_equal(tok2, tok)
+
+
+def test_f32_logit_chain_equals_single_steps(native):
+    """The fp32-logit chain over M steps equals M one-step calls fed the
+    previous tokens (GPU against GPU, bitwise)."""
+    w = wl.WORKLOADS["greedy_draft_64x5_f32logits"]
+    inp = wl.make_inputs(w, B=40, M=5, V=8192, r=256)
+    full_t, full_c = run_sample(inp, 0.0)
+    prev = inp["first_prev"].copy()
+    for k in range(5):
+        step = dict(inp, base=np.ascontiguousarray(inp["base"][:, k:k + 1]), first_prev=prev)
+        t, c = run_sample(step, 0.0, position_offset=k)
+        assert np.array_equal(t[:, 0], full_t[:, k]) and np.array_equal(c[:, 0], full_c[:, k])
+        prev = t[:, 0].copy()
+
+
 def _mixed_inputs(ldt, wdt, B, M, V, r, seed):
     """Workload-shaped inputs with the logits in ldt and the weights in wdt."""
     w = dataclasses.replace(wl.WORKLOADS["teacher_forced_320"], dtype=wl.F32)
@@ -469,11 +502,13 @@ def test_deterministic_and_workspace_reuse(native):
     assert rmd.read_device_error(ws) == 0
 
 
+@pytest.mark.parametrize("ldt", [wl.BF16, wl.F32])
 @pytest.mark.parametrize("B", [8, 70])   # 8: persistent chain; 70: step-by-step kernels
-def test_greedy_special_values(native, B):
-    """Argmax semantics on planted values (W2 = 0, so corrected = base):
-    NaN ranks first (first NaN wins), exact ties go to the first column --
-    within a lane, across lanes and across workgroups -- and +-inf order."""
+def test_greedy_special_values(native, B, ldt):
+    """Argmax semantics on planted values (W2 = 0, so corrected = base), on
+    bf16 and fp32 logits: NaN ranks first (first NaN wins), exact ties go to
+    the first column -- within a lane, across lanes and across workgroups --,
+    -0 ties +0, and +-inf order."""
     V, M, r = 8192, 2, 32
     w = wl.WORKLOADS["greedy_draft_64x5"]
     inp = wl.make_inputs(w, B=B, M=M, V=V, r=r, seed=21)
@@ -501,14 +536,18 @@ def test_greedy_special_values(native, B):
             row[:, [300, 299]] = 0.0
         elif kind == 6:
             row[:, 8191] = nan
-    inp["base"] = wl.to_bf16_bits(base)
+        elif kind == 7:
+            row[:] = -np.abs(row) - 1.0
+            row[:, 4100] = np.float32(-0.0)   # -0 ties +0: the first column wins
+            row[:, 4200] = 0.0
+    inp["base"] = wl.to_bf16_bits(base) if ldt == wl.BF16 else base
     inp["w2"] = np.zeros_like(inp["w2"])
     tok, corr = run_sample(inp, 0.0)
-    expect = {0: 777, 1: 9, 2: 6000, 3: 8191, 4: 0, 5: 299, 6: 8191}
+    expect = {0: 777, 1: 9, 2: 6000, 3: 8191, 4: 0, 5: 299, 6: 8191, 7: 4100}
     for b in range(B):
         if b % 8 in expect:
             assert (tok[b] == expect[b % 8]).all(), (b, tok[b])
-    check_chain(inp, 0.0, 0, tok, corr, name=f"greedy special values B{B}")
+    check_chain(inp, 0.0, 0, tok, corr, name=f"greedy special values B{B} L{ldt}")
 
 
 @pytest.mark.parametrize("V", [8192, 163840])
