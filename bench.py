@@ -26,7 +26,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
 WORKLOAD = "greedy_draft_64x5"
-DOMINANT_KERNEL = "markov_chain_greedy_bf16"   # the whole sample call is this one launch
+DOMINANT_KERNEL = "markov_chain_greedy_bf16<8, false>"   # the whole sample call is this one launch
 KERNEL_SOURCES = [os.path.join(ROOT, "rank_markov_draft_amd", "csrc", name)
                   for name in ("markov_chain.hip", "chain_common.h", "device_common.h", "markov_chain.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
