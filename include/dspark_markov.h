@@ -128,8 +128,9 @@ dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_
  * M == 0 or B == 0 is a successful no-op.  V == 0 with B*M > 0 is invalid.
  *
  * Greedy calls with bf16 weights (bf16 or fp32 logits), B <= 64, M <= 16
- * and r <= 256, and temperature bf16 calls with B <= 256, M * B <= 4096,
- * r <= 256 and V <= 640 * CUs, run as one persistent launch whose
+ * and r <= 256, and temperature bf16 calls (greedy bf16 calls of 64 < B too)
+ * with B <= 256, M * B <= 4096, r <= 256 and V <= 640 * CUs, run as one
+ * persistent launch whose
  * workgroups (one per CU) exchange each step's tokens through the
  * workspace; the host takes that path only when the occupancy query says a
  * CU can hold one of its workgroups (other calls run one step kernel per

@@ -368,8 +368,10 @@ dspark_status_t sample_block_impl(const void* base_logits, dspark_dtype_t logits
     if (e == hipSuccess) return DSPARK_OK;
     (void)hipGetLastError();  // not launchable here: take the step-by-step path
   }
-  // Temperature bf16 chains that fit the persistent sampling kernel too.
-  if (tile && !greedy && cus > 0 && B <= dspark::chain_sample_max_rows() &&
+  // Temperature bf16 chains that fit the persistent sampling kernel too, and
+  // greedy bf16 chains of more rows than the greedy chain takes (the same
+  // kernel selecting without noise).
+  if (tile && (!greedy || B > dspark::chain_max_rows()) && cus > 0 && B <= dspark::chain_sample_max_rows() &&
       M * B <= dspark::chain_sample_max_step_rows() &&
       (V + 31) / 32 <= (int64_t)cus * dspark::chain_sample_slices_per_group()) {
     dspark::ChainSampleParams c{};
@@ -394,6 +396,7 @@ dspark_status_t sample_block_impl(const void* base_logits, dspark_dtype_t logits
     c.batch_offset = (uint32_t)batch_offset;
     c.seed_lo = p.seed_lo;
     c.seed_hi = p.seed_hi;
+    c.greedy = greedy;
     const hipError_t e = dspark::launch_chain_sample(c, cus, s);
     if (e == hipSuccess) return DSPARK_OK;
     (void)hipGetLastError();

@@ -64,6 +64,7 @@ struct ChainSampleParams {
   uint32_t batch_offset;      // absolute batch index of row 0 (noise counter)
   uint32_t seed_lo;
   uint32_t seed_hi;
+  bool greedy;                // argmax of the corrected values (no noise)
 };
 
 int chain_max_rows();

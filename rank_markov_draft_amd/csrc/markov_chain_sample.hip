@@ -116,13 +116,32 @@ __device__ __forceinline__ uint64_t score_key(const float (&cv)[N], const uint32
   }
   return k;
 }
+// The same for greedy selection: the score is the corrected value itself.
+template <int N>
+__device__ __forceinline__ uint64_t value_key(const float (&cv)[N], uint32_t vcol) {
+  float best = cv[0];
+#pragma unroll
+  for (int q = 1; q < N; ++q) best = fmaxf(best, cv[q]);
+  uint32_t bi = N - 1;
+#pragma unroll
+  for (int q = N - 2; q >= 0; --q) bi = cv[q] == best ? (uint32_t)q : bi;
+  uint64_t k = argmax_key(best, vcol + bi);
+  uint32_t first = N;
+#pragma unroll
+  for (int q = N - 1; q >= 0; --q)
+    if (cv[q] != cv[q]) first = (uint32_t)q;
+  if (first < N) k = (0xFFFFFFFFull << 32) | (uint64_t)(0xFFFFFFFFu - (vcol + first));
+  return k;
+}
 // the key slots of M * B <= kTMaxStepRows step-rows fit the chain area's keys
 // (16 steps x 8 key groups x 64 rows of 64-byte slots)
 static_assert(kTMaxStepRows * kChainKeyGroups * kTKeyWords * 8 <= 16 * 8 * 64 * kKeyPad * 8, "key area");
 
 }  // namespace
 
-template <int K32>
+// GREEDY: the same chain selecting the argmax of the corrected values (no
+// noise); it serves greedy calls of more rows than the greedy chain takes.
+template <int K32, bool GREEDY>
 __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampleParams p) {
   // Gathered W1 rows of units u (buffer u % 2), in the B-operand order of the
   // matrix instruction: block kk holds at lane l's 16 bytes row l % 16,
@@ -429,13 +448,17 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
 #pragma unroll
         for (int q = 0; q < 8; ++q) cv[q] = (q & 1) ? bf16_hi(ow[q >> 1]) : bf16_lo(ow[q >> 1]);
         uint32_t vcol = vbeg + colw;
-        __asm__ volatile("" : "+v"(vcol));  // opaque, as the seeds
-        // columns vcol .. + 3 and vcol + 4 .. + 7 are the words of two Philox
-        // blocks, computed as two interleaved chains
-        Philox4 qa, qb;
-        philox4x32_10_pair(vcol >> 2, (vcol >> 2) + 1u, kabs, brow, 0u, seed_lo, seed_hi, qa, qb);
-        const uint32_t words[8] = {qa.x0, qa.x1, qa.x2, qa.x3, qb.x0, qb.x1, qb.x2, qb.x3};
-        key = score_key<8>(cv, words, p.kappa, vcol);
+        if constexpr (GREEDY) {
+          key = value_key<8>(cv, vcol);
+        } else {
+          __asm__ volatile("" : "+v"(vcol));  // opaque, as the seeds
+          // columns vcol .. + 3 and vcol + 4 .. + 7 are the words of two
+          // Philox blocks, computed as two interleaved chains
+          Philox4 qa, qb;
+          philox4x32_10_pair(vcol >> 2, (vcol >> 2) + 1u, kabs, brow, 0u, seed_lo, seed_hi, qa, qb);
+          const uint32_t words[8] = {qa.x0, qa.x1, qa.x2, qa.x3, qb.x0, qb.x1, qb.x2, qb.x3};
+          key = score_key<8>(cv, words, p.kappa, vcol);
+        }
       }
       // the LDS tile: the lane's 4 columns 32 xs + 8 g4 + 4 t .. +3 (one
       // Philox block)
@@ -451,10 +474,14 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
         if (ret) *(u32x2_t*)xp = u32x2_t{ow[0], ow[1]};
         const float cv[4] = {bf16_lo(ow[0]), bf16_hi(ow[0]), bf16_lo(ow[1]), bf16_hi(ow[1])};
         uint32_t vcol = vbeg + colt;
-        __asm__ volatile("" : "+v"(vcol));
-        const Philox4 q4 = philox4x32_10(vcol >> 2, kabs, brow, 0u, seed_lo, seed_hi);
-        const uint32_t words[4] = {q4.x0, q4.x1, q4.x2, q4.x3};
-        key = max_u64(key, score_key<4>(cv, words, p.kappa, vcol));
+        if constexpr (GREEDY) {
+          key = max_u64(key, value_key<4>(cv, vcol));
+        } else {
+          __asm__ volatile("" : "+v"(vcol));
+          const Philox4 q4 = philox4x32_10(vcol >> 2, kabs, brow, 0u, seed_lo, seed_hi);
+          const uint32_t words[4] = {q4.x0, q4.x1, q4.x2, q4.x3};
+          key = max_u64(key, score_key<4>(cv, words, p.kappa, vcol));
+        }
       }
       // the row's four lanes, then one LDS max per row and wave
       key = max_u64(key, ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(key >> 32), 16) << 32) |
@@ -547,9 +574,9 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
 // ---------------------------------------------------------------- launcher
 namespace {
 
-// Workgroups of markov_chain_sample_bf16<K32> one CU of the current device
-// can hold, cached per device; the chain needs at least one.
-template <int K32>
+// Workgroups of markov_chain_sample_bf16<K32, GREEDY> one CU of the current
+// device can hold, cached per device; the chain needs at least one.
+template <int K32, bool GREEDY>
 int chain_sample_occupancy() {
   static int cache[64];
   static bool known[64];
@@ -557,7 +584,7 @@ int chain_sample_occupancy() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   if (!known[dev]) {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, markov_chain_sample_bf16<K32>, kTThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, markov_chain_sample_bf16<K32, GREEDY>, kTThreads, 0) !=
         hipSuccess)
       blocks = 0;
     cache[dev] = blocks;
@@ -568,8 +595,13 @@ int chain_sample_occupancy() {
 
 template <int K32>
 hipError_t launch_chain_sample_k(const ChainSampleParams& p, int grid, hipStream_t s) {
-  if (chain_sample_occupancy<K32>() < 1) return hipErrorNotSupported;
-  hipLaunchKernelGGL((markov_chain_sample_bf16<K32>), dim3(grid), dim3(kTThreads), 0, s, p);
+  if (p.greedy) {
+    if (chain_sample_occupancy<K32, true>() < 1) return hipErrorNotSupported;
+    hipLaunchKernelGGL((markov_chain_sample_bf16<K32, true>), dim3(grid), dim3(kTThreads), 0, s, p);
+  } else {
+    if (chain_sample_occupancy<K32, false>() < 1) return hipErrorNotSupported;
+    hipLaunchKernelGGL((markov_chain_sample_bf16<K32, false>), dim3(grid), dim3(kTThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -300,6 +300,23 @@ def test_f32_logit_greedy_chain_shapes(native, B, M, V, r):
     assert np.array_equal(tok2, tok)
 
 
+@pytest.mark.parametrize("B,M,V,r", [
+    (65, 3, 20000, 256),      # one row past the greedy chain's 64: five groups
+    (128, 2, 163840, 256),    # 20 slices a workgroup on 256 CUs (four in LDS)
+    (256, 2, 8200, 64),       # 16 full groups, rank 64, a ragged last workgroup
+])
+def test_greedy_wide_batch_chain(native, B, M, V, r):
+    """Greedy drafts of 65..256 rows run on the sampling chain selecting the
+    argmax of the corrected values: every token and corrected logit against
+    the oracle, and the tokens-only call gives the same tokens."""
+    w = wl.WORKLOADS["greedy_draft_64x5"]
+    inp = wl.make_inputs(w, B=B, M=M, V=V, r=r, seed=60 + B + M)
+    tok, corr = run_sample(inp, 0.0)
+    check_chain(inp, 0.0, 0, tok, corr, name=f"greedy wide chain B{B} M{M} V{V} r{r}")
+    tok2, _ = run_sample(inp, 0.0, return_logits=False)
+    assert np.array_equal(tok2, tok)
+
+
 def test_f32_logit_chain_equals_single_steps(native):
     """The fp32-logit chain over M steps equals M one-step calls fed the
     previous tokens (GPU against GPU, bitwise)."""
@@ -503,7 +520,9 @@ def test_deterministic_and_workspace_reuse(native):
 
 
 @pytest.mark.parametrize("ldt", [wl.BF16, wl.F32])
-@pytest.mark.parametrize("B", [8, 70])   # 8: persistent chain; 70: step-by-step kernels
+# 8: the greedy chain; 70: the sampling chain selecting without noise; 300:
+# step-by-step kernels
+@pytest.mark.parametrize("B", [8, 70, 300])
 def test_greedy_special_values(native, B, ldt):
     """Argmax semantics on planted values (W2 = 0, so corrected = base), on
     bf16 and fp32 logits: NaN ranks first (first NaN wins), exact ties go to
