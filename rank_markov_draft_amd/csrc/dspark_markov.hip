@@ -369,9 +369,9 @@ dspark_status_t sample_block_impl(const void* base_logits, dspark_dtype_t logits
     (void)hipGetLastError();  // not launchable here: take the step-by-step path
   }
   // Temperature bf16 chains that fit the persistent sampling kernel too, and
-  // greedy bf16 chains of more rows than the greedy chain takes (the same
-  // kernel selecting without noise).
-  if (tile && (!greedy || B > dspark::chain_max_rows()) && cus > 0 && B <= dspark::chain_sample_max_rows() &&
+  // greedy bf16 chains the greedy chain did not take (more rows, or a wider
+  // vocabulary per CU): the same kernel selecting without noise.
+  if (tile && cus > 0 && B <= dspark::chain_sample_max_rows() &&
       M * B <= dspark::chain_sample_max_step_rows() &&
       (V + 31) / 32 <= (int64_t)cus * dspark::chain_sample_slices_per_group()) {
     dspark::ChainSampleParams c{};

@@ -304,11 +304,13 @@ def test_f32_logit_greedy_chain_shapes(native, B, M, V, r):
     (65, 3, 20000, 256),      # one row past the greedy chain's 64: five groups
     (128, 2, 163840, 256),    # 20 slices a workgroup on 256 CUs (four in LDS)
     (256, 2, 8200, 64),       # 16 full groups, rank 64, a ragged last workgroup
+    (48, 3, 163840, 256),     # a vocabulary past the greedy chain's 512 columns per CU (256 CUs)
 ])
 def test_greedy_wide_batch_chain(native, B, M, V, r):
-    """Greedy drafts of 65..256 rows run on the sampling chain selecting the
-    argmax of the corrected values: every token and corrected logit against
-    the oracle, and the tokens-only call gives the same tokens."""
+    """Greedy drafts the greedy chain does not take (65..256 rows, or more
+    than 512 columns per CU) run on the sampling chain selecting the argmax
+    of the corrected values: every token and corrected logit against the
+    oracle, and the tokens-only call gives the same tokens."""
     w = wl.WORKLOADS["greedy_draft_64x5"]
     inp = wl.make_inputs(w, B=B, M=M, V=V, r=r, seed=60 + B + M)
     tok, corr = run_sample(inp, 0.0)
