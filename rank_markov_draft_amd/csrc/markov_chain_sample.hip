@@ -35,7 +35,10 @@
 // Every wait on other workgroups is bounded; the last workgroup to leave
 // writes the last step's tokens, clears the keys and counters, and writes -1
 // to every token instead when a wait failed (or the workspace was already
-// poisoned by an unread failure).
+// poisoned by an unread failure).  Instantiated with GREEDY the kernel
+// selects the first argmax of the corrected values, without noise: the
+// greedy calls the greedy chain does not take (more rows, or more columns
+// per CU) run on it.
 #include "chain_common.h"
 #include "device_common.h"
 #include "markov_chain.h"
