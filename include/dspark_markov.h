@@ -127,10 +127,11 @@ dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_
  *                        split across calls, reproduce one whole call.
  * M == 0 or B == 0 is a successful no-op.  V == 0 with B*M > 0 is invalid.
  *
- * Greedy calls with bf16 weights (bf16 or fp32 logits), B <= 64, M <= 16
- * and r <= 256, and temperature bf16 calls (greedy bf16 calls of 64 < B too)
- * with B <= 256, M * B <= 4096, r <= 256 and V <= 640 * CUs, run as one
- * persistent launch whose
+ * Calls with bf16 weights (bf16 or fp32 logits) and r <= 256 run as one
+ * persistent launch when they fit one of two chains: greedy calls with
+ * B <= 64, M <= 16 and V <= 512 * CUs; then any call (temperature, or a
+ * greedy call the first did not take) with B <= 256, M * B <= 4096 and
+ * V <= 640 * CUs (bf16 logits) or V <= 608 * CUs (fp32 logits).  Their
  * workgroups (one per CU) exchange each step's tokens through the
  * workspace; the host takes that path only when the occupancy query says a
  * CU can hold one of its workgroups (other calls run one step kernel per

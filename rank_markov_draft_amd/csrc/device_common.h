@@ -77,10 +77,12 @@ __device__ __forceinline__ BufferWords buffer_words(const void* p, uint32_t byte
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
 }
+// lds must be the same in every lane; it is read through readfirstlane so a
+// uniform value the compiler keeps in a vector register still reaches m0.
 __device__ __forceinline__ void load_lds16(const BufferWords& r, uint32_t off, uint32_t lds) {
   uint32_t saved;
   __asm__ volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0"
-                   : "=&s"(saved) : "v"(off), "s"(r.w), "s"(lds) : "memory");
+                   : "=&s"(saved) : "v"(off), "s"(r.w), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 __device__ __forceinline__ void load_lds16_coherent(const BufferWords& r, uint32_t off, uint32_t lds) {
   uint32_t saved;

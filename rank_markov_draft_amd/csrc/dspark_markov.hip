@@ -368,15 +368,17 @@ dspark_status_t sample_block_impl(const void* base_logits, dspark_dtype_t logits
     if (e == hipSuccess) return DSPARK_OK;
     (void)hipGetLastError();  // not launchable here: take the step-by-step path
   }
-  // Temperature bf16 chains that fit the persistent sampling kernel too, and
-  // greedy bf16 chains the greedy chain did not take (more rows, or a wider
-  // vocabulary per CU): the same kernel selecting without noise.
-  if (tile && cus > 0 && B <= dspark::chain_sample_max_rows() &&
+  // Temperature chains with bf16 weights (bf16 or fp32 logits) that fit the
+  // persistent sampling kernel, and greedy chains the greedy chain did not
+  // take (more rows, or a wider vocabulary per CU): the same kernel
+  // selecting without noise.
+  if ((tile || f32_tile) && cus > 0 && B <= dspark::chain_sample_max_rows() &&
       M * B <= dspark::chain_sample_max_step_rows() &&
-      (V + 31) / 32 <= (int64_t)cus * dspark::chain_sample_slices_per_group()) {
+      (V + 31) / 32 <= (int64_t)cus * dspark::chain_sample_slices_per_group(!tile)) {
     dspark::ChainSampleParams c{};
-    c.base = (const uint16_t*)base_logits;
-    c.out = (uint16_t*)corrected_logits;
+    c.base = base_logits;
+    c.out = corrected_logits;
+    c.lf32 = !tile;
     c.first_prev = first_prev_token_ids;
     c.tokens = sampled_tokens;
     c.w1 = (const uint16_t*)w1;

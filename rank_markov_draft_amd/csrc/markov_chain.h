@@ -43,8 +43,8 @@ struct ChainParams {
 // 64-bit argmax key per (step, key group, row) in 16-byte slots, sync the
 // arrival counters; both are zero between calls.
 struct ChainSampleParams {
-  const uint16_t* base;       // [B, M, V]
-  uint16_t* out;              // [B, M, V] or null
+  const void* base;           // [B, M, V] bf16, or fp32 when lf32
+  void* out;                  // [B, M, V] like base, or null
   const int64_t* first_prev;  // [B]
   int64_t* tokens;            // [B, M]
   const uint16_t* w1;         // [V, r]
@@ -65,6 +65,7 @@ struct ChainSampleParams {
   uint32_t seed_lo;
   uint32_t seed_hi;
   bool greedy;                // argmax of the corrected values (no noise)
+  bool lf32;                  // fp32 logits (bf16 weights either way)
 };
 
 int chain_max_rows();
@@ -76,7 +77,7 @@ hipError_t launch_chain_greedy(const ChainParams& p, int num_cus, hipStream_t s)
 
 int chain_sample_max_rows();       // B at most
 int chain_sample_max_step_rows();  // M * B at most
-int chain_sample_slices_per_group();
+int chain_sample_slices_per_group(bool lf32);
 // hipErrorNotSupported when the shape does not fit the kernel or the device
 // cannot hold one of its workgroups per CU.
 hipError_t launch_chain_sample(const ChainSampleParams& p, int num_cus, hipStream_t s);

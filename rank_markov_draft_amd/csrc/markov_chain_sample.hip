@@ -38,7 +38,10 @@
 // poisoned by an unread failure).  Instantiated with GREEDY the kernel
 // selects the first argmax of the corrected values, without noise: the
 // greedy calls the greedy chain does not take (more rows, or more columns
-// per CU) run on it.
+// per CU) run on it.  Instantiated with LF32 it reads and writes fp32
+// logits (bf16 weights either way): the bf16 bias is widened and added in
+// fp32, a workgroup takes up to 19 slices, and the base rows of unit w+1
+// load during window w (a ring of two units, as the rows are twice as wide).
 #include "chain_common.h"
 #include "device_common.h"
 #include "markov_chain.h"
@@ -51,11 +54,20 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kTWaves = 16;
 constexpr int kTThreads = kTWaves * 64;
-constexpr int kTExtra = 4;                   // slices whose W2 rows sit in LDS
-constexpr int kTSlices = kTWaves + kTExtra;  // slices of a workgroup at most (640 columns)
-constexpr int kTPitch = 64 * kTSlices + 16;  // LDS bytes of a staged row (+ pad)
 constexpr int kTBulk = kTWaves - 2;          // staging waves (2 .. 15)
-constexpr int kTRing = 3;                    // staged units (rows of unit w+2 load during window w)
+// LDS layout by logits dtype: bf16 rows of up to 640 columns (four LDS
+// slices) in a ring of three units (the rows of unit w+2 load during window
+// w); fp32 rows, twice the bytes, of up to 608 columns (three LDS slices) in
+// a ring of two (the rows of unit w+1 load during window w).
+template <bool LF32>
+struct TLayout {
+  static constexpr int El = LF32 ? 4 : 2;              // bytes per logit
+  static constexpr int Extra = LF32 ? 3 : 4;           // slices whose W2 rows sit in LDS
+  static constexpr int Slices = kTWaves + Extra;       // slices of a workgroup at most
+  static constexpr int Pitch = 32 * Slices * El + 16;  // LDS bytes of a staged row (+ pad)
+  static constexpr int Ring = LF32 ? 2 : 3;            // staged units
+  static constexpr int SegCols = 1024 / El;            // columns of a 1 KB row segment
+};
 constexpr int kTGroupRows = 16;              // rows of a group at most
 constexpr int kTMaxGroups = 16;              // row groups of a call at most (256 rows)
 constexpr int kTMinSlots = 5;                // slots per step at least
@@ -144,8 +156,11 @@ static_assert(kTMaxStepRows * kChainKeyGroups * kTKeyWords * 8 <= 16 * 8 * 64 * 
 
 // GREEDY: the same chain selecting the argmax of the corrected values (no
 // noise); it serves greedy calls of more rows than the greedy chain takes.
-template <int K32, bool GREEDY>
+// LF32: fp32 logits (bf16 weights either way).
+template <int K32, bool GREEDY, bool LF32>
 __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampleParams p) {
+  using L = TLayout<LF32>;
+  constexpr int kTExtra = L::Extra, kTPitch = L::Pitch, kTRing = L::Ring;
   // Gathered W1 rows of units u (buffer u % 2), in the B-operand order of the
   // matrix instruction: block kk holds at lane l's 16 bytes row l % 16,
   // rank elements 32 kk + 8 (l / 16) .. +7.
@@ -193,10 +208,11 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
   const uint32_t vbeg = (uint32_t)(s_begin * 32);
   const uint32_t vend = (uint32_t)(s_end * 32 < V ? s_end * 32 : V);
   const int ncols = (int)(vend - vbeg);               // <= 640, a multiple of 8
-  const int nseg = ncols > 512 ? 2 : 1;              // 1 KB row segments
+  // 1 KB row segments (bf16: one or two, fp32: one to three)
+  const int nseg = LF32 ? (ncols > L::SegCols ? (ncols + L::SegCols - 1) / L::SegCols : 1) : (ncols > L::SegCols ? 2 : 1);
   const int xq = extra_tile_of_wave(wave);
 
-  const uint32_t bytes = (uint32_t)(B * M * V * 2);
+  const uint32_t bytes = (uint32_t)(B * M * V * L::El);
   const __amdgpu_buffer_rsrc_t rs_out = buffer_rsrc(p.out, ret ? bytes : 0u);
   const BufferWords bw_base = buffer_words(p.base, bytes);
   const BufferWords bw_w1 = buffer_words(p.w1, (uint32_t)(V * r * 2));
@@ -238,39 +254,39 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
   }
 
   // ---- row staging by waves 2..15: row i (0..15) of a unit is moved by
-  // wave 2 + i % 14 as one or two segments of 512 columns, lane l the 8
-  // columns base + 8 l .. +7, base = 0 for the first and ncols - 512 for
-  // the second (present when the workgroup has more than 512 columns).  The
-  // two overlap; one wave moves both, so a row's corrected values are read
-  // for the store before the next unit's loads overwrite any of them.
+  // wave 2 + i % 14 as nseg segments of SegCols columns (1 KB), lane l the
+  // 16 bytes at column base + 16 l / El, base = SegCols h for all but the
+  // last segment and ncols - SegCols for the last (which overlaps the one
+  // before).  One wave moves a row's segments, so its corrected values are
+  // read for the store before the next unit's loads overwrite any of them.
   // Offsets of masked-off lanes, rows or steps point past the buffer, so
   // every instruction is unconditional.
   const int bw = wave - 2;  // bulk index (negative for waves 0 and 1)
-  auto seg_base = [&](int j) __attribute__((always_inline)) -> uint32_t {
-    return (j & 1) ? (uint32_t)(ncols - 512) : 0u;
+  auto seg_base = [&](int h) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (LF32) return h < nseg - 1 ? (uint32_t)(L::SegCols * h) : (nseg > 1 ? (uint32_t)(ncols - L::SegCols) : 0u);
+    else return h ? (uint32_t)(ncols - L::SegCols) : 0u;
   };
-  auto seg_offset = [&](int u, int j) __attribute__((always_inline)) -> uint32_t {
-    const int row = j >> 1;
+  auto seg_offset = [&](int u, int row, int h) __attribute__((always_inline)) -> uint32_t {
     const int gg = u % NS, kd = u / NS;
     const int b = gg * rpg + row;
-    const uint32_t col = vbeg + seg_base(j) + 8u * (uint32_t)lane;
+    const uint32_t col = vbeg + seg_base(h) + (uint32_t)(16 / L::El) * (uint32_t)lane;
     const bool ok = row < rpg && b < B && kd < M && col < vend;
-    return ok ? (uint32_t)((b * M + kd) * V) * 2u + 2u * col : kBufferOob;
+    return ok ? (uint32_t)((b * M + kd) * V) * (uint32_t)L::El + (uint32_t)L::El * col : kBufferOob;
   };
   // the segment's LDS base (a load to LDS puts lane l's 16 bytes at base + 16 l)
-  auto seg_lds = [&](int u, int j) __attribute__((always_inline)) -> unsigned char* {
-    return &lds_x[u % kTRing][(j >> 1) * kTPitch + 2 * seg_base(j)];
+  auto seg_lds = [&](int u, int row, int h) __attribute__((always_inline)) -> unsigned char* {
+    return &lds_x[u % kTRing][row * kTPitch + L::El * seg_base(h)];
   };
   // bulk operations this wave issues per staged unit
   const int my_segs = bw < 0 ? 0 : nseg * ((kTGroupRows - bw + kTBulk - 1) / kTBulk);
   auto load_unit = [&](int u) __attribute__((always_inline)) {
     for (int i = bw; i < kTGroupRows; i += kTBulk)
-      for (int h = 0; h < nseg; ++h) load_lds16(bw_base, seg_offset(u, 2 * i + h), lds_address(seg_lds(u, 2 * i + h)));
+      for (int h = 0; h < nseg; ++h) load_lds16(bw_base, seg_offset(u, i, h), lds_address(seg_lds(u, i, h)));
   };
   auto flush_unit = [&](int u) __attribute__((always_inline)) {
     for (int i = bw; i < kTGroupRows; i += kTBulk)
       for (int h = 0; h < nseg; ++h)
-        buffer_store16(rs_out, seg_offset(u, 2 * i + h), *(const u32x4_t*)(seg_lds(u, 2 * i + h) + lane * 16));
+        buffer_store16(rs_out, seg_offset(u, i, h), *(const u32x4_t*)(seg_lds(u, i, h) + lane * 16));
   };
 
   // ---- exchange pieces (waves 0 and 1)
@@ -437,19 +453,34 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
       // the register slice: the lane's 8 columns 32 wave + 8 g4 .. +7
       const uint32_t colw = (uint32_t)(wave * 32 + 8 * g4);
       if (has_reg && row_ok && vbeg + colw < vend) {
-        unsigned char* xp = xrow + colw * 2;
-        const u32x4_t bb = *(const u32x4_t*)xp;
-        const uint32_t bw4[4] = {pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
-                                 pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
-        const uint32_t xw[4] = {bb.x, bb.y, bb.z, bb.w};
-        uint32_t ow[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          ow[q] = pack_bf16x2(bf16_lo(xw[q]) + bf16_lo(bw4[q]), bf16_hi(xw[q]) + bf16_hi(bw4[q]));
-        if (ret) *(u32x4_t*)xp = u32x4_t{ow[0], ow[1], ow[2], ow[3]};
         float cv[8];
+        if constexpr (LF32) {
+          // fp32 logits: the bf16 bias widened and added with one rounding
+          unsigned char* xp = xrow + colw * 4;
+          const u32x4_t b0 = *(const u32x4_t*)xp, b1 = *(const u32x4_t*)(xp + 16);
+          const uint32_t xw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+          const float a8[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
 #pragma unroll
-        for (int q = 0; q < 8; ++q) cv[q] = (q & 1) ? bf16_hi(ow[q >> 1]) : bf16_lo(ow[q >> 1]);
+          for (int q = 0; q < 8; ++q) cv[q] = __uint_as_float(xw[q]) + bf16_lo(pack_bf16x2(a8[q], 0.0f));
+          if (ret) {
+            *(u32x4_t*)xp = u32x4_t{__float_as_uint(cv[0]), __float_as_uint(cv[1]), __float_as_uint(cv[2]), __float_as_uint(cv[3])};
+            *(u32x4_t*)(xp + 16) =
+                u32x4_t{__float_as_uint(cv[4]), __float_as_uint(cv[5]), __float_as_uint(cv[6]), __float_as_uint(cv[7])};
+          }
+        } else {
+          unsigned char* xp = xrow + colw * 2;
+          const u32x4_t bb = *(const u32x4_t*)xp;
+          const uint32_t bw4[4] = {pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
+                                   pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
+          const uint32_t xw[4] = {bb.x, bb.y, bb.z, bb.w};
+          uint32_t ow[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            ow[q] = pack_bf16x2(bf16_lo(xw[q]) + bf16_lo(bw4[q]), bf16_hi(xw[q]) + bf16_hi(bw4[q]));
+          if (ret) *(u32x4_t*)xp = u32x4_t{ow[0], ow[1], ow[2], ow[3]};
+#pragma unroll
+          for (int q = 0; q < 8; ++q) cv[q] = (q & 1) ? bf16_hi(ow[q >> 1]) : bf16_lo(ow[q >> 1]);
+        }
         uint32_t vcol = vbeg + colw;
         if constexpr (GREEDY) {
           key = value_key<8>(cv, vcol);
@@ -467,15 +498,29 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
       // Philox block)
       const uint32_t colt = (uint32_t)(xs * 32 + 8 * g4 + 4 * (xq & 1));
       if (has_tile && row_ok && vbeg + colt < vend) {
-        unsigned char* xp = xrow + colt * 2;
-        const u32x2_t bb = *(const u32x2_t*)xp;
-        const uint32_t ow[2] = {
-            pack_bf16x2(bf16_lo(bb.x) + bf16_lo(pack_bf16x2(acc2[0], acc2[1])),
-                        bf16_hi(bb.x) + bf16_hi(pack_bf16x2(acc2[0], acc2[1]))),
-            pack_bf16x2(bf16_lo(bb.y) + bf16_lo(pack_bf16x2(acc2[2], acc2[3])),
-                        bf16_hi(bb.y) + bf16_hi(pack_bf16x2(acc2[2], acc2[3])))};
-        if (ret) *(u32x2_t*)xp = u32x2_t{ow[0], ow[1]};
-        const float cv[4] = {bf16_lo(ow[0]), bf16_hi(ow[0]), bf16_lo(ow[1]), bf16_hi(ow[1])};
+        float cv[4];
+        if constexpr (LF32) {
+          unsigned char* xp = xrow + colt * 4;
+          const u32x4_t bb = *(const u32x4_t*)xp;
+          const uint32_t xw[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) cv[q] = __uint_as_float(xw[q]) + bf16_lo(pack_bf16x2(acc2[q], 0.0f));
+          if (ret)
+            *(u32x4_t*)xp = u32x4_t{__float_as_uint(cv[0]), __float_as_uint(cv[1]), __float_as_uint(cv[2]), __float_as_uint(cv[3])};
+        } else {
+          unsigned char* xp = xrow + colt * 2;
+          const u32x2_t bb = *(const u32x2_t*)xp;
+          const uint32_t ow[2] = {
+              pack_bf16x2(bf16_lo(bb.x) + bf16_lo(pack_bf16x2(acc2[0], acc2[1])),
+                          bf16_hi(bb.x) + bf16_hi(pack_bf16x2(acc2[0], acc2[1]))),
+              pack_bf16x2(bf16_lo(bb.y) + bf16_lo(pack_bf16x2(acc2[2], acc2[3])),
+                          bf16_hi(bb.y) + bf16_hi(pack_bf16x2(acc2[2], acc2[3])))};
+          if (ret) *(u32x2_t*)xp = u32x2_t{ow[0], ow[1]};
+          cv[0] = bf16_lo(ow[0]);
+          cv[1] = bf16_hi(ow[0]);
+          cv[2] = bf16_lo(ow[1]);
+          cv[3] = bf16_hi(ow[1]);
+        }
         uint32_t vcol = vbeg + colt;
         if constexpr (GREEDY) {
           key = max_u64(key, value_key<4>(cv, vcol));
@@ -514,9 +559,13 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
         lds_flag = 0;
       }
     }
-    // bulk: the rows of unit w+1 (loaded a window ago) are in LDS before the
-    // barrier; this window's operations may stay in flight
-    if (bw >= 0) wait_vmcnt_upto16(issued);
+    // bulk: the rows of unit w+1 are in LDS before the barrier: with a ring
+    // of three they were loaded a window ago and this window's operations
+    // may stay in flight; with two they were loaded in this window
+    if (bw >= 0) {
+      if constexpr (kTRing == 2) wait_vmcnt<0>();
+      else wait_vmcnt_upto16(issued);
+    }
     lds_barrier();
     if (!lds_flag) break;
   }
@@ -577,9 +626,9 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
 // ---------------------------------------------------------------- launcher
 namespace {
 
-// Workgroups of markov_chain_sample_bf16<K32, GREEDY> one CU of the current
-// device can hold, cached per device; the chain needs at least one.
-template <int K32, bool GREEDY>
+// Workgroups of markov_chain_sample_bf16<K32, GREEDY, LF32> one CU of the
+// current device can hold, cached per device; the chain needs at least one.
+template <int K32, bool GREEDY, bool LF32>
 int chain_sample_occupancy() {
   static int cache[64];
   static bool known[64];
@@ -587,8 +636,8 @@ int chain_sample_occupancy() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   if (!known[dev]) {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, markov_chain_sample_bf16<K32, GREEDY>, kTThreads, 0) !=
-        hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, markov_chain_sample_bf16<K32, GREEDY, LF32>, kTThreads,
+                                                     0) != hipSuccess)
       blocks = 0;
     cache[dev] = blocks;
     known[dev] = true;
@@ -596,30 +645,34 @@ int chain_sample_occupancy() {
   return cache[dev];
 }
 
+template <int K32, bool GREEDY, bool LF32>
+hipError_t launch_chain_sample_i(const ChainSampleParams& p, int grid, hipStream_t s) {
+  if (chain_sample_occupancy<K32, GREEDY, LF32>() < 1) return hipErrorNotSupported;
+  hipLaunchKernelGGL((markov_chain_sample_bf16<K32, GREEDY, LF32>), dim3(grid), dim3(kTThreads), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int K32>
 hipError_t launch_chain_sample_k(const ChainSampleParams& p, int grid, hipStream_t s) {
-  if (p.greedy) {
-    if (chain_sample_occupancy<K32, true>() < 1) return hipErrorNotSupported;
-    hipLaunchKernelGGL((markov_chain_sample_bf16<K32, true>), dim3(grid), dim3(kTThreads), 0, s, p);
-  } else {
-    if (chain_sample_occupancy<K32, false>() < 1) return hipErrorNotSupported;
-    hipLaunchKernelGGL((markov_chain_sample_bf16<K32, false>), dim3(grid), dim3(kTThreads), 0, s, p);
-  }
-  return hipGetLastError();
+  if (p.lf32) return p.greedy ? launch_chain_sample_i<K32, true, true>(p, grid, s)
+                              : launch_chain_sample_i<K32, false, true>(p, grid, s);
+  return p.greedy ? launch_chain_sample_i<K32, true, false>(p, grid, s)
+                  : launch_chain_sample_i<K32, false, false>(p, grid, s);
 }
 
 }  // namespace
 
 int chain_sample_max_rows() { return kTGroupRows * kTMaxGroups; }
 int chain_sample_max_step_rows() { return kTMaxStepRows; }
-int chain_sample_slices_per_group() { return kTSlices; }
+int chain_sample_slices_per_group(bool lf32) { return lf32 ? TLayout<true>::Slices : TLayout<false>::Slices; }
 
 hipError_t launch_chain_sample(const ChainSampleParams& p, int num_cus, hipStream_t s) {
   const int ks = tile_ks_for_rank(p.r);
   if (p.B < 1 || p.B > chain_sample_max_rows() || p.M < 1 || p.M * p.B > kTMaxStepRows || ks == 0 || ks > 16)
     return hipErrorNotSupported;
-  if (p.V % 8 != 0 || p.B * p.M * p.V >= ((int64_t)1 << 30)) return hipErrorNotSupported;
-  if (p.S > (int64_t)num_cus * kTSlices) return hipErrorNotSupported;
+  // byte offsets below 2^31
+  if (p.V % 8 != 0 || p.B * p.M * p.V * (p.lf32 ? 4 : 2) >= ((int64_t)1 << 31)) return hipErrorNotSupported;
+  if (p.S > (int64_t)num_cus * chain_sample_slices_per_group(p.lf32)) return hipErrorNotSupported;
   switch (ks) {  // rank blocks of 16 -> blocks of 32 (zero-padded)
     case 1:
     case 2: return launch_chain_sample_k<1>(p, num_cus, s);

@@ -28,7 +28,8 @@ def _raw_read(ws):
 
 
 @pytest.mark.parametrize("T,B,name", [(0.0, 8, "greedy_draft_64x5"), (0.7, 8, "greedy_draft_64x5"),
-                                      (0.7, 40, "greedy_draft_64x5"), (0.0, 24, "greedy_draft_64x5_f32logits")])
+                                      (0.7, 40, "greedy_draft_64x5"), (0.0, 24, "greedy_draft_64x5_f32logits"),
+                                      (0.7, 24, "temperature_draft_256x8_f32logits")])
 def test_forced_chain_timeout_gives_sentinel_tokens(native, T, B, name):
     M, V, r = 5, 4096, 256                   # bf16 weights: the persistent chains
     inp = wl.make_inputs(wl.WORKLOADS[name], B=B, M=M, V=V, r=r, seed=21)

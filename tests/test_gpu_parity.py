@@ -282,6 +282,28 @@ def test_temperature_chain_shapes(native, B, M, V, r):
 
 
 @pytest.mark.parametrize("B,M,V,r", [
+    (200, 3, 20000, 256),     # 13 groups of 16 rows, one 1 KB segment a row
+    (5, 7, 65544, 32),        # nine slices a workgroup: two segments, a ragged last slice
+    (16, 2, 139264, 64),      # 17 slices on 256 CUs: one LDS slice, three segments (the last overlapping)
+    (3, 2, 155648, 256),      # 19 slices on 256 CUs: three LDS slices, 608 columns
+    (9, 3, 151928, 256),      # a ragged last slice among the LDS slices
+    (256, 2, 512, 64),        # 16 slices: most workgroups own no column
+])
+def test_f32_logit_temperature_chain_shapes(native, B, M, V, r):
+    """Temperature chains on fp32 logits (bf16 weights) run on the sampling
+    chain's fp32-logit form (two staged units, up to 608 columns a CU):
+    every token and corrected logit against the oracle, and the tokens-only
+    call gives the same tokens."""
+    w = wl.WORKLOADS["temperature_draft_256x8_f32logits"]
+    inp = wl.make_inputs(w, B=B, M=M, V=V, r=r, seed=70 + B + M)
+    assert inp["base"].dtype == np.float32
+    tok, corr = run_sample(inp, 0.7, seed=78)
+    check_chain(inp, 0.7, 78, tok, corr, name=f"f32-logit temperature chain B{B} M{M} V{V} r{r}")
+    tok2, _ = run_sample(inp, 0.7, seed=78, return_logits=False)
+    assert np.array_equal(tok2, tok)
+
+
+@pytest.mark.parametrize("B,M,V,r", [
     (17, 3, 8200, 128),       # two groups of 9 rows, a ragged last workgroup
     (1, 7, 4096, 64),         # one row, seven steps
     (64, 1, 20000, 32),       # four groups, one step
@@ -571,17 +593,18 @@ def test_greedy_special_values(native, B, ldt):
     check_chain(inp, 0.0, 0, tok, corr, name=f"greedy special values B{B} L{ldt}")
 
 
-@pytest.mark.parametrize("V", [8192, 163840])
-def test_temperature_special_values(native, V):
+@pytest.mark.parametrize("ldt,V", [(wl.BF16, 8192), (wl.BF16, 163840), (wl.F32, 8192), (wl.F32, 151552)])
+def test_temperature_special_values(native, ldt, V):
     """The temperature chain's selection on planted values (W2 = 0, so
     corrected = base, T = 0.7): a NaN ranks above every score and the first
     NaN wins, +inf scores tie and the first wins, all -inf rows take column
-    0, and a single finite value among -inf wins.  At V = 163840 the planted
-    columns 512..639 lie in the slices whose W2 rows sit in LDS."""
+    0, and a single finite value among -inf wins.  At the large vocabularies
+    the planted columns 512..639 lie in the slices whose W2 rows sit in LDS
+    (bf16 logits: 640 columns a CU on 256 CUs; fp32: 608)."""
     B, M, r = 16, 2, 32
-    w = wl.WORKLOADS["temperature_draft_256x8"]
+    w = wl.WORKLOADS["temperature_draft_256x8" if ldt == wl.BF16 else "temperature_draft_256x8_f32logits"]
     inp = wl.make_inputs(w, B=B, M=M, V=V, r=r, seed=23)
-    base = wl.bf16_bits_to_f32(inp["base"]).copy()
+    base = (wl.bf16_bits_to_f32(inp["base"]) if ldt == wl.BF16 else inp["base"]).copy()
     nan, inf = np.float32(np.nan), np.float32(np.inf)
     a, b2 = (600, 620) if V > 8192 else (777, 5000)
     for b in range(B):
@@ -597,14 +620,14 @@ def test_temperature_special_values(native, V):
         elif kind == 3:
             row[:] = -inf
             row[:, a] = -1e30
-    inp["base"] = wl.to_bf16_bits(base)
+    inp["base"] = wl.to_bf16_bits(base) if ldt == wl.BF16 else base
     inp["w2"] = np.zeros_like(inp["w2"])
     tok, corr = run_sample(inp, 0.7, seed=5)
     expect = {0: min(a, b2), 1: 515, 2: 0, 3: a}
     for b in range(B):
         if b % 5 in expect:
             assert (tok[b] == expect[b % 5]).all(), (b, tok[b])
-    check_chain(inp, 0.7, 5, tok, corr, name=f"temperature special values V{V}")
+    check_chain(inp, 0.7, 5, tok, corr, name=f"temperature special values L{ldt} V{V}")
 
 
 def test_apply_beyond_31_bit_offsets(native):
