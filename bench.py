@@ -31,7 +31,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "rank_markov_draft_amd", "csrc", name)
                   for name in ("markov_chain.hip", "chain_common.h", "device_common.h", "markov_chain.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 VALU_FILE = os.path.join(ROOT, "profiles", "valu.json")
-VALU_KERNEL = "markov_chain_sample_bf16<8, false>"   # persistent temperature chain at rank 256
+VALU_KERNEL = "markov_chain_sample_bf16<8, false, false>"   # persistent temperature chain at rank 256
 VALU_SOURCES = [os.path.join(ROOT, "rank_markov_draft_amd", "csrc", name)
                 for name in ("markov_chain_sample.hip", "chain_common.h", "device_common.h", "markov_chain.h")]
 # Issue cost (SIMD cycles) of a wave64 instruction, measured with a

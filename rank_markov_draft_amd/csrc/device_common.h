@@ -103,6 +103,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, t);
 }
 
+// x rounded to bf16 (nearest, ties to even), as a float: one
+// v_cvt_pk_bf16_f32 with the rounded value in the upper half and +0 in the
+// lower, which is that float's bit pattern.  (The packing helper above makes
+// the compiler convert into the lower half and then move it up.)
+__device__ __forceinline__ float bf16_rne(float x) {
+  float y;
+  __asm__("v_cvt_pk_bf16_f32 %0, 0, %1" : "=v"(y) : "v"(x));
+  return y;
+}
+// Two bf16-valued floats (lower halves zero) packed into one word, lo first.
+__device__ __forceinline__ uint32_t join_bf16(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
 // corrected = round(fp32(base) + fp32(bias)) for a pair of bf16 logits, with
 // the bias first rounded to bf16 (the Linear's output dtype).
 __device__ __forceinline__ uint32_t add_bias_pair(uint32_t base2, float acc_lo, float acc_hi) {

@@ -461,25 +461,24 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
           const uint32_t xw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
           const float a8[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
 #pragma unroll
-          for (int q = 0; q < 8; ++q) cv[q] = __uint_as_float(xw[q]) + bf16_lo(pack_bf16x2(a8[q], 0.0f));
+          for (int q = 0; q < 8; ++q) cv[q] = __uint_as_float(xw[q]) + bf16_rne(a8[q]);
           if (ret) {
             *(u32x4_t*)xp = u32x4_t{__float_as_uint(cv[0]), __float_as_uint(cv[1]), __float_as_uint(cv[2]), __float_as_uint(cv[3])};
             *(u32x4_t*)(xp + 16) =
                 u32x4_t{__float_as_uint(cv[4]), __float_as_uint(cv[5]), __float_as_uint(cv[6]), __float_as_uint(cv[7])};
           }
         } else {
+          // both roundings in the float domain (one instruction each)
           unsigned char* xp = xrow + colw * 2;
           const u32x4_t bb = *(const u32x4_t*)xp;
-          const uint32_t bw4[4] = {pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
-                                   pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
           const uint32_t xw[4] = {bb.x, bb.y, bb.z, bb.w};
-          uint32_t ow[4];
+          const float a8[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            ow[q] = pack_bf16x2(bf16_lo(xw[q]) + bf16_lo(bw4[q]), bf16_hi(xw[q]) + bf16_hi(bw4[q]));
-          if (ret) *(u32x4_t*)xp = u32x4_t{ow[0], ow[1], ow[2], ow[3]};
-#pragma unroll
-          for (int q = 0; q < 8; ++q) cv[q] = (q & 1) ? bf16_hi(ow[q >> 1]) : bf16_lo(ow[q >> 1]);
+          for (int q = 0; q < 8; ++q)
+            cv[q] = bf16_rne(((q & 1) ? bf16_hi(xw[q >> 1]) : bf16_lo(xw[q >> 1])) + bf16_rne(a8[q]));
+          if (ret)
+            *(u32x4_t*)xp = u32x4_t{join_bf16(cv[0], cv[1]), join_bf16(cv[2], cv[3]), join_bf16(cv[4], cv[5]),
+                                    join_bf16(cv[6], cv[7])};
         }
         uint32_t vcol = vbeg + colw;
         if constexpr (GREEDY) {
@@ -504,22 +503,17 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
           const u32x4_t bb = *(const u32x4_t*)xp;
           const uint32_t xw[4] = {bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) cv[q] = __uint_as_float(xw[q]) + bf16_lo(pack_bf16x2(acc2[q], 0.0f));
+          for (int q = 0; q < 4; ++q) cv[q] = __uint_as_float(xw[q]) + bf16_rne(acc2[q]);
           if (ret)
             *(u32x4_t*)xp = u32x4_t{__float_as_uint(cv[0]), __float_as_uint(cv[1]), __float_as_uint(cv[2]), __float_as_uint(cv[3])};
         } else {
           unsigned char* xp = xrow + colt * 2;
           const u32x2_t bb = *(const u32x2_t*)xp;
-          const uint32_t ow[2] = {
-              pack_bf16x2(bf16_lo(bb.x) + bf16_lo(pack_bf16x2(acc2[0], acc2[1])),
-                          bf16_hi(bb.x) + bf16_hi(pack_bf16x2(acc2[0], acc2[1]))),
-              pack_bf16x2(bf16_lo(bb.y) + bf16_lo(pack_bf16x2(acc2[2], acc2[3])),
-                          bf16_hi(bb.y) + bf16_hi(pack_bf16x2(acc2[2], acc2[3])))};
-          if (ret) *(u32x2_t*)xp = u32x2_t{ow[0], ow[1]};
-          cv[0] = bf16_lo(ow[0]);
-          cv[1] = bf16_hi(ow[0]);
-          cv[2] = bf16_lo(ow[1]);
-          cv[3] = bf16_hi(ow[1]);
+          const uint32_t xw[2] = {bb.x, bb.y};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            cv[q] = bf16_rne(((q & 1) ? bf16_hi(xw[q >> 1]) : bf16_lo(xw[q >> 1])) + bf16_rne(acc2[q]));
+          if (ret) *(u32x2_t*)xp = u32x2_t{join_bf16(cv[0], cv[1]), join_bf16(cv[2], cv[3])};
         }
         uint32_t vcol = vbeg + colt;
         if constexpr (GREEDY) {
