@@ -27,11 +27,14 @@ __device__ __forceinline__ uint32_t chain_arrival_load(uint32_t* slot, int lane)
 }
 
 // Sum of the counters loaded by lanes 0 .. kChainKeyGroups - 1, uniform over
-// the wave.
+// the wave: read lane by lane into scalar registers (a few cycles each)
+// rather than by shuffles through LDS (a round trip each, on the poll's
+// critical path).
 __device__ __forceinline__ uint32_t chain_arrival_sum(uint32_t v) {
+  uint32_t s = 0;
 #pragma unroll
-  for (int d = 1; d < kChainKeyGroups; d <<= 1) v += (uint32_t)__shfl_xor((int)v, d);
-  return (uint32_t)__builtin_amdgcn_readfirstlane(v);
+  for (int x = 0; x < kChainKeyGroups; ++x) s += (uint32_t)__builtin_amdgcn_readlane((int)v, x);
+  return s;
 }
 
 // Spins until the counters of a slot sum to at least target; false after

@@ -147,6 +147,24 @@ __device__ __forceinline__ int64_t key_index(uint64_t key) {
 
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
+// Max over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four lanes of one row of
+// a 16 x 16 matrix-instruction result), every lane getting the result: two
+// lane-swap instructions (v_permlane16_swap_b32, v_permlane32_swap_b32)
+// pair each lane's value with its partner's without a trip through LDS.
+// Each swap leaves a lane holding its own word and its partner's, in one
+// order or the other; the max does not care which.
+__device__ __forceinline__ uint64_t max_row_lanes(uint64_t k) {
+  uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+  auto l16 = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  auto h16 = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  k = max_u64(((uint64_t)h16[0] << 32) | l16[0], ((uint64_t)h16[1] << 32) | l16[1]);
+  lo = (uint32_t)k;
+  hi = (uint32_t)(k >> 32);
+  auto l32 = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  auto h32 = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  return max_u64(((uint64_t)h32[0] << 32) | l32[0], ((uint64_t)h32[1] << 32) | l32[1]);
+}
+
 // Max over the lanes of groups of `width` consecutive lanes (width a power
 // of two <= 64); every lane of the group gets the result.
 template <int width>

@@ -533,8 +533,7 @@ __global__ __launch_bounds__(kThreads) void markov_chain_greedy_bf16(ChainParams
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                  : 0;
       const uint64_t best = max_u64(k0, k1);
-      const uint64_t b2 = max_u64(best, (uint64_t)__shfl_xor((long long)best, 16));
-      const uint64_t merged = max_u64(b2, (uint64_t)__shfl_xor((long long)b2, 32));
+      const uint64_t merged = max_row_lanes(best);
       if (g4 == 0 && row_ok) p.tokens[(uint32_t)(b * M + M - 1)] = key_index(merged);
     }
     lds_barrier();  // the last keys are read before they are cleared

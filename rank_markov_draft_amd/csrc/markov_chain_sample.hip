@@ -108,26 +108,25 @@ __device__ __forceinline__ int extra_tile_of_wave(int wave) {
 template <int N>
 __device__ __forceinline__ uint64_t score_key(const float (&cv)[N], const uint32_t (&w)[N], float kappa,
                                               uint32_t vcol) {
-  float sc[N], sumc = 0.0f;
+  float sc[N];
 #pragma unroll
-  for (int q = 0; q < N; ++q) {
-    sumc += cv[q];
-    sc[q] = __builtin_fmaf(cv[q], kappa, gumbel2_from_word(w[q]));
-  }
+  for (int q = 0; q < N; ++q) sc[q] = __builtin_fmaf(cv[q], kappa, gumbel2_from_word(w[q]));
+  // NaN-propagating maximum (v_maximum3_f32): a score is NaN exactly when
+  // its corrected value is (the noise and kappa are finite), so a NaN best
+  // flags the lane's NaN columns at no extra cost
   float best = sc[0];
 #pragma unroll
-  for (int q = 1; q < N; ++q) best = fmaxf(best, sc[q]);
+  for (int q = 1; q < N; ++q) best = __builtin_elementwise_maximum(best, sc[q]);
   uint32_t bi = N - 1;
 #pragma unroll
   for (int q = N - 2; q >= 0; --q) bi = sc[q] == best ? (uint32_t)q : bi;
   uint64_t k = argmax_key(best, vcol + bi);
-  if (sumc != sumc) {
-    // without a NaN value (+inf met -inf in the sum) the scan above stands
-    uint32_t first = N;
+  if (best != best) {
+    uint32_t first = N - 1;
 #pragma unroll
-    for (int q = N - 1; q >= 0; --q)
+    for (int q = N - 2; q >= 0; --q)
       if (cv[q] != cv[q]) first = (uint32_t)q;
-    if (first < N) k = (0xFFFFFFFFull << 32) | (uint64_t)(0xFFFFFFFFu - (vcol + first));
+    k = (0xFFFFFFFFull << 32) | (uint64_t)(0xFFFFFFFFu - (vcol + first));
   }
   return k;
 }
@@ -525,11 +524,8 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
           key = max_u64(key, score_key<4>(cv, words, p.kappa, vcol));
         }
       }
-      // the row's four lanes, then one LDS max per row and wave
-      key = max_u64(key, ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(key >> 32), 16) << 32) |
-                             (uint32_t)__shfl_xor((int)(uint32_t)key, 16));
-      key = max_u64(key, ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(key >> 32), 32) << 32) |
-                             (uint32_t)__shfl_xor((int)(uint32_t)key, 32));
+      // the row's four lanes (n16 + 16 j), then one LDS max per row and wave
+      key = max_row_lanes(key);
       if (g4 == 0 && key != 0ull) atomicMax((unsigned long long*)&lds_key[w & 1][n16], (unsigned long long)key);
     }
 
@@ -602,8 +598,7 @@ __global__ __launch_bounds__(kTThreads) void markov_chain_sample_bf16(ChainSampl
                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                    : 0;
         const uint64_t best = max_u64(k0, k1);
-        const uint64_t b2 = max_u64(best, (uint64_t)__shfl_xor((long long)best, 16));
-        const uint64_t merged = max_u64(b2, (uint64_t)__shfl_xor((long long)b2, 32));
+        const uint64_t merged = max_row_lanes(best);
         if (g4 == 0 && row_ok) p.tokens[(uint32_t)(b * M + M - 1)] = key_index(merged);
       }
     }
