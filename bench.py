@@ -136,6 +136,31 @@ def copy_ceiling(torch, np, bw):
             "torch_copy_GBps": nbytes / (ms_t * 1e-3) / 1e9}
 
 
+def same_size_ceiling(torch, np, bw, read_bytes, write_bytes, steps=200, warmup=100):
+    """The read-mix probe at one launch's own bytes (read_bytes read,
+    write_bytes written), timed like the kernel: back to back, one event pair
+    around `steps` launches, over four rotating buffer sets (so the 256 MB
+    Infinity Cache serves none of them).  A copy this size carries the same
+    launch ramp-up and drain as the kernel, which a 2 GiB copy hides."""
+    import ctypes
+    read_bytes, write_bytes = (read_bytes // 16) * 16, (write_bytes // 16) * 16
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    srcs = [torch.empty(read_bytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0) for _ in range(4)]
+    dsts = [torch.empty(write_bytes // 2, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+
+    def launch(i):
+        st = bw.dspark_bandwidth_read_mix(ctypes.c_void_p(dsts[i].data_ptr()), write_bytes,
+                                          ctypes.c_void_p(srcs[i].data_ptr()), read_bytes, stream)
+        if st != 0:
+            raise RuntimeError(f"dspark_bandwidth_read_mix: status {st}")
+
+    _, ms = time_region(launch, 4, steps, warmup, torch)
+    del srcs, dsts
+    torch.cuda.empty_cache()
+    return {"read_bytes": read_bytes, "write_bytes": write_bytes, "us_per_launch": ms * 1e3,
+            "GBps": (read_bytes + write_bytes) / (ms * 1e-3) / 1e9}
+
+
 def write_traffic(fetch_csv: str, write_csv: str) -> dict:
     """Turn two rocprofv3 counter runs of `bench.py --calibrate-copy` (one with
     FETCH_SIZE, one with WRITE_SIZE, KiB per dispatch) into HBM bytes per
@@ -512,6 +537,10 @@ def main():
     result["copy_ceiling"] = ceiling
     result["roofline"]["frac_of_copy_ceiling"] = achieved / ceiling["GBps"]
     result["roofline"]["frac_of_read_mix_ceiling"] = achieved / ceiling["read_mix_GBps"]
+    written = w.B * w.M * w.V * 2
+    same = same_size_ceiling(torch, np, _lib.load_bandwidth(), alg - written, written)
+    result["copy_ceiling"]["same_size"] = same
+    result["roofline"]["frac_of_same_size_copy"] = achieved / same["GBps"]
     if not args.no_extra:
         names = [n for n in args.extra.split(",") if n]
         unknown = [n for n in names if n not in wl.WORKLOADS]
