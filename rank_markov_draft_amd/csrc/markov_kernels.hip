@@ -393,6 +393,184 @@ __global__ __launch_bounds__(256) void markov_rows_fma(KernelParams p, int64_t c
   }
 }
 
+// ---------------------------------------------------------------- fp32 weights on the matrix cores
+// The projection of fp32 weights with v_mfma_f32_16x16x4_f32 (fp32 in, fp32
+// accumulate), for r and V multiples of 4 and 16-byte aligned operands.  A
+// workgroup of eight waves owns 64 rows x 128 columns (one key tile per row,
+// as markov_rows_fma); wave w the columns v0 + 16 w .. + 15 for all 64 rows
+// (four 16-row tiles, 16 accumulators per lane).
+//
+// The rank is walked in chunks of 64.  Lane (i, g) = (lane % 16, lane / 16)
+// loads W2w[v0 + 16 w + i][16 b + 4 g .. + 3] (one 16-byte load per block b
+// of 16 ranks, straight from HBM, one chunk ahead in registers) and feeds
+// element q of it to step q of block b: step (b, q) contracts ranks
+// {16 b + 4 g + q : g = 0..3}, a partition of the block.  The B operand of
+// row j uses the same ranks, read from the 64 rows staged in LDS per chunk
+// (two buffers; each chunk's rows are loaded into registers while the
+// previous chunk multiplies).  The sum over the rank thus runs in another
+// order than the FMA kernel's, inside the admissible interval of an fp32
+// sum.  The epilogue is the FMA kernel's: lane (j, g) of row tile t holds
+// rows n0 + 16 t + j, columns v0 + 16 w + 4 g .. + 3 (one Philox block).
+namespace {
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kFwWaves = 8;
+constexpr int kFwThreads = 64 * kFwWaves;
+constexpr int kFwCols = 16 * kFwWaves;  // = kFmaCols: the same key tiles
+constexpr int kFwRows = 64;
+constexpr int kFwK = 64;
+constexpr int kFwPitch = kFwK + 4;      // floats per staged row (16-byte aligned, offset banks)
+static_assert(kFwCols == kFmaCols, "key tiles");
+}  // namespace
+
+template <int MODE, bool L_BF16>
+__global__ __launch_bounds__(kFwThreads) void markov_rows_mfma_f32w(KernelParams p, int64_t chunk0) {
+  __shared__ __attribute__((aligned(16))) float lds_e[2][kFwRows * kFwPitch];
+  __shared__ int64_t lds_src[kFwRows];
+  __shared__ uint64_t lds_key[kFwRows];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int j16 = lane & 15, g = lane >> 4;
+  const int64_t V = p.V, r = p.r;
+  const int64_t v0 = (int64_t)blockIdx.x * kFwCols;
+  const int64_t n0 = (chunk0 + blockIdx.y) * kFwRows;
+  const bool count_bad = blockIdx.x == 0 && (MODE == MODE_APPLY || p.k == 0);
+  const float* const erow = (const float*)(p.latent != nullptr ? p.latent : p.w1);
+  const float* const w2 = (const float*)p.w2;
+
+  if (tid < kFwRows) {
+    const int64_t n = n0 + tid;
+    int64_t src = -1;
+    if (n < p.rows) {
+      const int64_t x = predecessor(p, n);
+      const bool ok = x >= 0 && x < V;
+      if (!ok && count_bad) atomicAdd(p.bad_rows, 1u);
+      if (ok) src = p.latent != nullptr ? n * p.latent_ld : x * r;
+    }
+    lds_src[tid] = src;
+    lds_key[tid] = 0ull;
+  }
+  __syncthreads();
+
+  // staged rows: 64 rows x 64 ranks = 1024 vectors of 4, two per thread
+  f32x4_t ev[2];
+  auto load_e = [&](int64_t k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int piece = tid + kFwThreads * q;
+      const int row = piece >> 4, kp = (piece & 15) * 4;
+      const int64_t src = lds_src[row], k = k0 + kp;
+      ev[q] = (src >= 0 && k < r) ? *(const f32x4_t*)(erow + src + k) : f32x4_t{};
+    }
+  };
+  auto store_e = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int piece = tid + kFwThreads * q;
+      *(f32x4_t*)&lds_e[buf][(piece >> 4) * kFwPitch + (piece & 15) * 4] = ev[q];
+    }
+  };
+  const int64_t vrow = v0 + 16 * wave + j16;
+  const bool vok = vrow < V;
+  f32x4_t a_cur[4], a_nxt[4];
+  auto load_a = [&](int64_t k0, f32x4_t (&a)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t k = k0 + 16 * b + 4 * g;
+      a[b] = (vok && k < r) ? __builtin_nontemporal_load((const f32x4_t*)(w2 + vrow * r + k)) : f32x4_t{};
+    }
+  };
+
+  f32x4_t acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{};
+  load_a(0, a_cur);
+  load_e(0);
+  store_e(0);
+  __syncthreads();
+  for (int64_t k0 = 0, c = 0; k0 < r; k0 += kFwK, ++c) {
+    const int buf = (int)(c & 1);
+    const bool more = k0 + kFwK < r;
+    if (more) {
+      load_a(k0 + kFwK, a_nxt);
+      load_e(k0 + kFwK);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f32x4_t bv = *(const f32x4_t*)&lds_e[buf][(16 * t + j16) * kFwPitch + 16 * b + 4 * g];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_cur[b][q], bv[q], acc[t], 0, 0, 0);
+      }
+    }
+    if (more) store_e(buf ^ 1);  // the other buffer's last reads ended at the previous barrier
+    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) a_cur[b] = a_nxt[b];
+    }
+  }
+
+  // epilogue: lane (j16, g), row tile t: row n0 + 16 t + j16, columns
+  // v0 + 16 wave + 4 g .. + 3 (accumulator element e = column + e)
+  const int64_t vc = v0 + 16 * wave + 4 * g;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int64_t n = n0 + 16 * t + j16;
+    const bool row_ok = n < p.rows;
+    uint64_t key = 0;
+    if (row_ok && vc < V) {
+      const int64_t off = base_row_offset(p, n) + vc;
+      float b4[4];
+      if constexpr (L_BF16) {
+        const u32x2_t w = *(const u32x2_t*)((const uint16_t*)p.base + off);
+        b4[0] = bf16_lo(w.x); b4[1] = bf16_hi(w.x); b4[2] = bf16_lo(w.y); b4[3] = bf16_hi(w.y);
+      } else {
+        const f32x4_t w = *(const f32x4_t*)((const float*)p.base + off);
+        b4[0] = w[0]; b4[1] = w[1]; b4[2] = w[2]; b4[3] = w[3];
+      }
+      float cv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float bias = acc[t][e];
+        if (L_BF16) bias = round_bf16_value(bias);
+        cv[e] = b4[e] + bias;
+        if (L_BF16) cv[e] = round_bf16_value(cv[e]);
+      }
+      if (p.out != nullptr) {
+        if constexpr (L_BF16)
+          *(u32x2_t*)((uint16_t*)p.out + off) =
+              u32x2_t{(__float_as_uint(cv[0]) >> 16) | (__float_as_uint(cv[1]) & 0xFFFF0000u),
+                      (__float_as_uint(cv[2]) >> 16) | (__float_as_uint(cv[3]) & 0xFFFF0000u)};
+        else
+          *(f32x4_t*)((float*)p.out + off) = f32x4_t{cv[0], cv[1], cv[2], cv[3]};
+      }
+      if constexpr (MODE == MODE_GREEDY) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key = max_u64(key, argmax_key(cv[e], (uint32_t)(vc + e)));
+      }
+      if constexpr (MODE == MODE_TEMPERATURE) {
+        const Philox4 q4 = philox4x32_10((uint32_t)((uint64_t)vc >> 2), p.k_abs, (uint32_t)(p.batch_offset + n), 0u,
+                                         p.seed_lo, p.seed_hi);
+        const uint32_t words[4] = {q4.x0, q4.x1, q4.x2, q4.x3};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          key = max_u64(key, argmax_key(__builtin_fmaf(cv[e], p.kappa, gumbel2_from_word(words[e])),
+                                        (uint32_t)(vc + e)));
+      }
+    }
+    if constexpr (MODE != MODE_APPLY) {
+      key = max_row_lanes(key);  // the row's four lanes (g) in this wave
+      if (g == 0 && key != 0ull) atomicMax((unsigned long long*)&lds_key[16 * t + j16], (unsigned long long)key);
+    }
+  }
+  if constexpr (MODE != MODE_APPLY) {
+    __syncthreads();
+    if (tid < kFwRows && n0 + tid < p.rows) p.partials[(n0 + tid) * p.nparts + blockIdx.x] = lds_key[tid];
+  }
+}
+
 // ---------------------------------------------------------------- reduction
 // One workgroup per batch row: the token of step k is the index in the
 // largest of the row's slice keys.
@@ -473,9 +651,33 @@ static hipError_t launch_rows_fma(const KernelParams& p, hipStream_t s) {
   return hipSuccess;
 }
 
+// The matrix-core kernel for fp32 weights when the shapes allow 16-byte
+// vectors: r, V (and the latent row pitch) multiples of 4, operands 16-byte
+// aligned; hipErrorNotSupported otherwise (the FMA kernel takes the call).
+template <int MODE, bool LBF>
+static hipError_t launch_rows_mfma_f32w(const KernelParams& p, hipStream_t s) {
+  const void* erow = p.latent != nullptr ? p.latent : p.w1;
+  auto a16 = [](const void* q) { return ((uintptr_t)q & 15u) == 0; };
+  if (p.r % 4 != 0 || p.V % 4 != 0 || (p.latent != nullptr && p.latent_ld % 4 != 0)) return hipErrorNotSupported;
+  if (!a16(p.w2) || !a16(erow) || !a16(p.base) || (p.out != nullptr && !a16(p.out))) return hipErrorNotSupported;
+  const int64_t chunks = (p.rows + kFwRows - 1) / kFwRows;
+  const unsigned tiles = (unsigned)((p.V + kFwCols - 1) / kFwCols);
+  for (int64_t c0 = 0; c0 < chunks; c0 += 65535) {  // grid.y holds at most 65535 row chunks
+    const int64_t nc = chunks - c0 < 65535 ? chunks - c0 : 65535;
+    hipLaunchKernelGGL((markov_rows_mfma_f32w<MODE, LBF>), dim3(tiles, (unsigned)nc), dim3(kFwThreads), 0, s, p, c0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <int MODE>
 static hipError_t launch_generic_mode(const KernelParams& p, bool lbf, bool wbf, hipStream_t s) {
   if (p.mode != MODE_APPLY && p.nparts != generic_parts(p.V)) return hipErrorInvalidValue;
+  if (!wbf) {
+    const hipError_t e = lbf ? launch_rows_mfma_f32w<MODE, true>(p, s) : launch_rows_mfma_f32w<MODE, false>(p, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   if (lbf && wbf) return launch_rows_fma<MODE, true, true>(p, s);
   if (!lbf && !wbf) return launch_rows_fma<MODE, false, false>(p, s);
   if (lbf) return launch_rows_fma<MODE, true, false>(p, s);

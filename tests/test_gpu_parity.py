@@ -374,16 +374,20 @@ def test_apply_mixed_dtypes(native, ldt, wdt, B, M, V, r):
 
 
 @pytest.mark.parametrize("ldt,wdt,B,M,V,r,T", [
-    (wl.F32, wl.F32, 16, 3, 129280, 256, 0.0),     # fp32 weights at the full vocabulary: row-tile FMA kernel
+    (wl.F32, wl.F32, 16, 3, 129280, 256, 0.0),     # fp32 weights at the full vocabulary: matrix-core kernel
     (wl.F32, wl.F32, 8, 3, 129280, 256, 0.7),
     (wl.BF16, wl.F32, 12, 3, 129280, 256, 0.0),
-    (wl.F32, wl.F32, 3, 4, 3001, 20, 0.7),         # ragged columns and a rank that is not a multiple of 8
-    (wl.F32, wl.F32, 37, 2, 1000, 1040, 0.0),      # rank past 1024: many rank chunks; rows past one tile
+    (wl.F32, wl.F32, 3, 4, 3001, 20, 0.7),         # V not a multiple of 4: the row-tile FMA kernel
+    (wl.F32, wl.F32, 37, 2, 1000, 1040, 0.0),      # rank past 1024: 17 rank chunks; apply rows past one tile
+    (wl.F32, wl.F32, 70, 2, 5000, 36, 0.7),        # 70 rows (two row tiles), a part rank chunk, an 8-column last tile
+    (wl.BF16, wl.F32, 5, 3, 4100, 64, 0.7),        # bf16 logits, temperature, a ragged last tile
+    (wl.F32, wl.F32, 2, 2, 1024, 4, 0.0),          # rank 4: one step of one block
 ])
 def test_fp32_weight_kernel(native, ldt, wdt, B, M, V, r, T):
-    """fp32 weights (and bf16 logits with fp32 weights) go to the row-tile FMA
-    kernel: sampling and the teacher-forced apply against the oracle on every
-    row."""
+    """fp32 weights (and bf16 logits with fp32 weights) go to the
+    matrix-core kernel (fp32 products, v_mfma_f32_16x16x4_f32) when r and V
+    are multiples of 4, else to the row-tile FMA kernel: sampling and the
+    teacher-forced apply against the oracle on every row."""
     inp = _mixed_inputs(ldt, wdt, B, M, V, r, seed=B * 31 + V)
     tok, corr = run_sample(inp, T, seed=3)
     check_chain(inp, T, 3, tok, corr, name=f"fp32-weight sample L{ldt} B{B} M{M} V{V} r{r} T{T}")
