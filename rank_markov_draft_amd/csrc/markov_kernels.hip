@@ -407,7 +407,8 @@ __global__ __launch_bounds__(256) void markov_rows_fma(KernelParams p, int64_t c
 // {16 b + 4 g + q : g = 0..3}, a partition of the block.  The B operand of
 // row j uses the same ranks, read from the 64 rows staged in LDS per chunk
 // (two buffers; each chunk's rows are loaded into registers while the
-// previous chunk multiplies).  The sum over the rank thus runs in another
+// previous chunk multiplies), or, at ranks up to 256 (WHOLE), all of the 64
+// rows staged once before the products, which then run without barriers.  The sum over the rank thus runs in another
 // order than the FMA kernel's, inside the admissible interval of an fp32
 // sum.  The epilogue is the FMA kernel's: lane (j, g) of row tile t holds
 // rows n0 + 16 t + j, columns v0 + 16 w + 4 g .. + 3 (one Philox block).
@@ -419,12 +420,15 @@ constexpr int kFwCols = 16 * kFwWaves;  // = kFmaCols: the same key tiles
 constexpr int kFwRows = 64;
 constexpr int kFwK = 64;
 constexpr int kFwPitch = kFwK + 4;      // floats per staged row (16-byte aligned, offset banks)
+constexpr int kFwWholeK = 256;           // ranks up to which all of a row is staged at once
+constexpr int kFwWholePitch = kFwWholeK + 4;
 static_assert(kFwCols == kFmaCols, "key tiles");
 }  // namespace
 
-template <int MODE, bool L_BF16>
+template <int MODE, bool L_BF16, bool WHOLE>
 __global__ __launch_bounds__(kFwThreads) void markov_rows_mfma_f32w(KernelParams p, int64_t chunk0) {
-  __shared__ __attribute__((aligned(16))) float lds_e[2][kFwRows * kFwPitch];
+  constexpr int kBuf = WHOLE ? kFwRows * kFwWholePitch : kFwRows * kFwPitch;  // floats of a staging buffer
+  __shared__ __attribute__((aligned(16))) float lds_e[WHOLE ? 1 : 2][kBuf];
   __shared__ int64_t lds_src[kFwRows];
   __shared__ uint64_t lds_key[kFwRows];
   const int tid = threadIdx.x;
@@ -451,22 +455,24 @@ __global__ __launch_bounds__(kFwThreads) void markov_rows_mfma_f32w(KernelParams
   }
   __syncthreads();
 
-  // staged rows: 64 rows x 64 ranks = 1024 vectors of 4, two per thread
-  f32x4_t ev[2];
-  auto load_e = [&](int64_t k0) __attribute__((always_inline)) {
+  // staged rows: a chunk of 64 rows x 64 ranks = 1024 vectors of 4, two
+  // per thread; row j, rank k of a chunk at lds_e[buf][j * pitch + kofs + k]
+  constexpr int kPitch = WHOLE ? kFwWholePitch : kFwPitch;
+  f32x4_t ev[WHOLE ? kFwWholeK / kFwK : 1][2];
+  auto load_e = [&](int64_t k0, f32x4_t (&e)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int piece = tid + kFwThreads * q;
       const int row = piece >> 4, kp = (piece & 15) * 4;
       const int64_t src = lds_src[row], k = k0 + kp;
-      ev[q] = (src >= 0 && k < r) ? *(const f32x4_t*)(erow + src + k) : f32x4_t{};
+      e[q] = (src >= 0 && k < r) ? *(const f32x4_t*)(erow + src + k) : f32x4_t{};
     }
   };
-  auto store_e = [&](int buf) __attribute__((always_inline)) {
+  auto store_e = [&](int buf, int kofs, const f32x4_t (&e)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int piece = tid + kFwThreads * q;
-      *(f32x4_t*)&lds_e[buf][(piece >> 4) * kFwPitch + (piece & 15) * 4] = ev[q];
+      *(f32x4_t*)&lds_e[buf][(piece >> 4) * kPitch + kofs + (piece & 15) * 4] = e[q];
     }
   };
   const int64_t vrow = v0 + 16 * wave + j16;
@@ -484,28 +490,39 @@ __global__ __launch_bounds__(kFwThreads) void markov_rows_mfma_f32w(KernelParams
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{};
   load_a(0, a_cur);
-  load_e(0);
-  store_e(0);
+  if constexpr (WHOLE) {
+    // every chunk's rows in flight at once, then into LDS
+#pragma unroll
+    for (int c = 0; c < kFwWholeK / kFwK; ++c) load_e(c * kFwK, ev[c]);
+#pragma unroll
+    for (int c = 0; c < kFwWholeK / kFwK; ++c) store_e(0, c * kFwK, ev[c]);
+  } else {
+    load_e(0, ev[0]);
+    store_e(0, 0, ev[0]);
+  }
   __syncthreads();
   for (int64_t k0 = 0, c = 0; k0 < r; k0 += kFwK, ++c) {
-    const int buf = (int)(c & 1);
+    const int buf = WHOLE ? 0 : (int)(c & 1);
+    const int kofs = WHOLE ? (int)k0 : 0;
     const bool more = k0 + kFwK < r;
     if (more) {
       load_a(k0 + kFwK, a_nxt);
-      load_e(k0 + kFwK);
+      if constexpr (!WHOLE) load_e(k0 + kFwK, ev[0]);
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const f32x4_t bv = *(const f32x4_t*)&lds_e[buf][(16 * t + j16) * kFwPitch + 16 * b + 4 * g];
+        const f32x4_t bv = *(const f32x4_t*)&lds_e[buf][(16 * t + j16) * kPitch + kofs + 16 * b + 4 * g];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_cur[b][q], bv[q], acc[t], 0, 0, 0);
       }
     }
-    if (more) store_e(buf ^ 1);  // the other buffer's last reads ended at the previous barrier
-    __syncthreads();
+    if constexpr (!WHOLE) {
+      if (more) store_e(buf ^ 1, 0, ev[0]);  // the other buffer's last reads ended at the previous barrier
+      __syncthreads();
+    }
     if (more) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) a_cur[b] = a_nxt[b];
@@ -664,7 +681,11 @@ static hipError_t launch_rows_mfma_f32w(const KernelParams& p, hipStream_t s) {
   const unsigned tiles = (unsigned)((p.V + kFwCols - 1) / kFwCols);
   for (int64_t c0 = 0; c0 < chunks; c0 += 65535) {  // grid.y holds at most 65535 row chunks
     const int64_t nc = chunks - c0 < 65535 ? chunks - c0 : 65535;
-    hipLaunchKernelGGL((markov_rows_mfma_f32w<MODE, LBF>), dim3(tiles, (unsigned)nc), dim3(kFwThreads), 0, s, p, c0);
+    if (p.r <= kFwWholeK)
+      hipLaunchKernelGGL((markov_rows_mfma_f32w<MODE, LBF, true>), dim3(tiles, (unsigned)nc), dim3(kFwThreads), 0, s, p, c0);
+    else
+      hipLaunchKernelGGL((markov_rows_mfma_f32w<MODE, LBF, false>), dim3(tiles, (unsigned)nc), dim3(kFwThreads), 0, s, p,
+                         c0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
