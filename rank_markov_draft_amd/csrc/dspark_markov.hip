@@ -99,7 +99,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 int64_t vocab_slices(int64_t V) { return (V + 127) / 128; }
 
-// The generic kernel keeps one gathered W1 row (r floats) in LDS.
+// Largest rank the row-tile kernels take (they walk the rank in chunks; the
+// limit is the documented one of the C ABI).
 constexpr int64_t kGenericMaxRank = 16384;
 
 // The bf16 tile kernel takes the call when both dtypes are bf16, the rank is

@@ -145,7 +145,9 @@ constexpr int64_t kGroupedApplyMaxRows = 4096;
 // B <= 4096 and the logits and V * r * 2 within 2^31 bytes (hipErrorNotSupported).
 int64_t sample_step_parts(int64_t V);
 hipError_t launch_sample_step(const KernelParams& p, bool logits_f32, int num_cus, hipStream_t s);
-// Row-tile FMA kernel for any dtype pair and rank (32 rows x 128 columns per
+// fp32 weights on the matrix cores when r and V are multiples of 4 and the
+// operands 16-byte aligned (64 rows x 128 columns per workgroup), else the
+// row-tile FMA kernel for any dtype pair and rank (32 rows x 128 columns per
 // workgroup, the rank in chunks through LDS); sampling writes
 // generic_parts(V) keys per row (p.nparts must equal it).
 int64_t generic_parts(int64_t V);

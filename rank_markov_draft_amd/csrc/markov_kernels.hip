@@ -21,7 +21,10 @@
 //     coalesced 16-byte accesses, 256 contiguous bytes per row and tile;
 //   * in sampling steps the same pass folds the corrected values (or their
 //     Gumbel scores) into one argmax key per row and slice.
-// markov_generic handles fp32 and shapes the tile kernel does not take.
+// fp32 weights go to markov_rows_mfma_f32w (fp32 products on the matrix
+// cores, 64 rows x 128 columns per workgroup) when r and V are multiples of
+// 4; markov_rows_fma (scalar FMA, 32 rows x 128 columns, any dtype pair and
+// rank) takes every other shape that no faster kernel takes.
 // reduce_row_keys finishes a sampling step: one token per row.
 #include "device_common.h"
 #include "markov_kernels.h"
