@@ -98,7 +98,8 @@ dspark_status_t dspark_markov_workspace_init(void* workspace, size_t bytes, void
  *   w1, w2           device, [V, r] each, weight_dtype.
  *   corrected_logits device, [B, M, V], logits_dtype; may equal base_logits
  *                    (in place); any other overlap with an input is invalid.
- * B, M, V >= 0; r > 0 (the page's constructor asserts a positive rank).
+ * B, M, V >= 0; r > 0 (the page's constructor asserts a positive rank);
+ * ranks above 16384 return DSPARK_ERR_UNSUPPORTED.
  * B*M*V == 0 is a successful no-op (the page returns base_logits itself). */
 dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_t logits_dtype,
                                           const int64_t* token_ids, const void* w1,
@@ -125,7 +126,8 @@ dspark_status_t dspark_markov_apply_block(const void* base_logits, dspark_dtype_
  *   position_offset,     absolute step and batch indices of position 0 / row 0
  *   batch_offset         for the noise, so that M one-step calls, or a batch
  *                        split across calls, reproduce one whole call.
- * M == 0 or B == 0 is a successful no-op.  V == 0 with B*M > 0 is invalid.
+ * M == 0 or B == 0 is a successful no-op.  V == 0 with B*M > 0 is invalid;
+ * ranks above 16384 return DSPARK_ERR_UNSUPPORTED.
  *
  * Calls with bf16 weights (bf16 or fp32 logits) and r <= 256 run as one
  * persistent launch when they fit one of two chains: greedy calls with
