@@ -272,3 +272,14 @@ def test_static_scratch_entry_point_rejects_oversize_on_the_host(L):
     assert b"static scratch" in L.dspark_markov_last_error()
     # no work at all is a successful no-op, as for the workspace entry point
     assert L.dspark_markov_sample_block_static(f, 1, f, f, f, 1, 0, 5, 151936, 256, 0.0, 0, 0, 0, f, None, None) == 0
+
+
+def test_rank_above_the_limit_is_unsupported(L):
+    """Ranks above 16384 return DSPARK_ERR_UNSUPPORTED, on the host, before
+    anything is enqueued (distinct fake buffers pass the overlap checks)."""
+    mb = 1 << 24
+    base, ids, w1, w2, out, ws = (ctypes.c_void_p(mb * (i + 1)) for i in range(6))
+    for ldt, wdt in ((0, 0), (1, 0), (1, 1)):
+        assert L.dspark_markov_apply_block(base, ldt, ids, w1, w2, wdt, 2, 3, 64, 16385, out, ws, 1 << 20, None) == 2
+        assert L.dspark_markov_sample_block(base, ldt, ids, w1, w2, wdt, 2, 3, 64, 16385, 0.0, 0, 0, 0,
+                                            ctypes.c_void_p(mb * 8), None, ws, 1 << 20, None) == 2
