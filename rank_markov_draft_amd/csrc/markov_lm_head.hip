@@ -24,21 +24,28 @@
 // operands are zeros (they add exact zeros).  The operands take two roads
 // into LDS, both over all eight waves:
 //   * B (8 KB a chunk, the HBM stream of the head weight): one buffer load
-//     to LDS per wave and chunk, into one of five stages, four chunks ahead;
+//     to LDS per wave and chunk, into one of four stages, four chunks ahead;
 //   * A (20 KB a chunk, the hidden rows every tile re-reads, L2-resident):
-//     two or three 16-byte register loads per thread, two chunks ahead in
+//     two or three 16-byte register loads per thread, four chunks ahead in
 //     two register sets (even chunks in one, odd in the other, so both are
-//     named statically), written to one of two LDS buffers a step before
-//     use.  Loads to LDS alone for A as well measured 15-20% slower: they
-//     move about 16 bytes per cycle per CU, which at 28 KB a chunk is the
-//     chunk's whole time.
-// Every wave issues the same operations per chunk (the loads past the last
-// chunk go to a junk block or read zeros), so one wait count serves all.
-// A row's four 16-byte pieces sit at positions q ^ ((row / 2) % 4), which
-// keeps the 16-lane fragment reads free of bank conflicts.  After a tile's
-// bias chunks the accumulators are rounded to bf16 (the Linear's output
-// dtype), packed and kept; after its head chunks the epilogue adds them in
-// fp32 and stores; the chunk stream runs on across tiles.
+//     named statically), written to one of two LDS buffers two steps
+//     before use.  Loads to LDS alone for A as well measured 15-20% slower:
+//     they move about 16 bytes per cycle per CU, which at 28 KB a chunk is
+//     the chunk's whole time.
+// One barrier a chunk.  After it a wave issues B of chunk g+4, the
+// fragment reads of chunk g+1, the stores of A of chunk g+2 and the loads
+// of A of chunk g+4, and the products of chunk g on the fragments it read
+// a step earlier, so the next chunks' LDS and memory traffic runs beside
+// this chunk's matrix work.  Every wave issues the same operations per
+// chunk (the loads past the last chunk go to a junk block or read zeros),
+// so one wait count serves all.  A row's four 16-byte pieces sit at
+// positions q ^ ((row / 2) % 4), which keeps the fragment reads free of
+// bank conflicts (the variant q ^ ((row / 4) % 4) measured 5% slower).
+// After a tile's bias chunks the accumulators are rounded to bf16 (the
+// Linear's output dtype) and parked in a wave-private LDS region (which
+// frees their registers for the second fragment set); after its head
+// chunks the epilogue adds them in fp32 and stores; the chunk stream runs
+// on across tiles.
 #include "device_common.h"
 #include "markov_kernels.h"
 
@@ -50,7 +57,7 @@ constexpr int kLmThreads = kLmWaves * 64;
 constexpr int kLmRows = 320;                  // rows of a tile (20 blocks of 16)
 constexpr int kLmCols = 128;                  // vocabulary columns of a tile (8 blocks of 16)
 constexpr int kLmK = 32;                      // inner-dimension chunk (one matrix instruction)
-constexpr int kLmStages = 5;                  // B stages in LDS (four chunks ahead)
+constexpr int kLmStages = 4;                  // B stages in LDS (issued four chunks ahead)
 constexpr int kLmRowBytes = kLmK * 2;         // 64 bytes per operand row and chunk
 constexpr int kLmStageA = kLmRows * kLmRowBytes;   // 20 KB
 constexpr int kLmStageB = kLmCols * kLmRowBytes;   // 8 KB
@@ -58,6 +65,7 @@ constexpr int kLmAPieces = kLmStageA / 16;         // 16-byte pieces of an A chu
 constexpr int kLmAPer = 3;                         // A loads per thread and chunk (the last for threads < 256)
 constexpr int kLmOps = kLmAPer + 1;                // memory operations of a wave per chunk (A loads, one B load)
 constexpr int kLmEpiStores = 20;                   // 16-byte stores of a wave's tile epilogue
+constexpr int kLmBiasBytes = 20 * 64 * 8;          // a wave's rounded bias of a tile: 20 blocks x 64 lanes x 4 bf16
 static_assert(kLmStageB / 1024 == kLmWaves, "one B load per wave and chunk");
 static_assert(kLmAPer * kLmThreads >= kLmAPieces && (kLmAPer - 1) * kLmThreads < kLmAPieces, "A pieces");
 }  // namespace
@@ -69,6 +77,8 @@ __global__ __launch_bounds__(kLmThreads) void markov_lm_head_bf16(LmHeadParams p
   __shared__ __attribute__((aligned(16))) unsigned char lds_a[2 * kLmStageA];
   __shared__ __attribute__((aligned(16))) unsigned char lds_junk[1024];
   __shared__ int32_t lds_e[kLmRows];  // gathered W1 row of each tile row (element offset), -1: zero
+  // each wave's rounded bias of its current tile (wave-private)
+  __shared__ __attribute__((aligned(16))) unsigned char lds_bias[kLmWaves * kLmBiasBytes];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -136,6 +146,17 @@ __global__ __launch_bounds__(kLmThreads) void markov_lm_head_bf16(LmHeadParams p
   // A of chunk g into registers: thread t loads pieces t + 512 j (row
   // piece / 4, logical piece piece % 4); zeros past the last chunk, past
   // the 1280 pieces, for bad ids and past the rows
+  // the rows of the thread's A pieces t + 512 j are fixed for the launch:
+  // their W1 element offsets (or -1) and whether the hidden row exists
+  int32_t a_e[kLmAPer];
+  bool a_n[kLmAPer];
+#pragma unroll
+  for (int j = 0; j < kLmAPer; ++j) {
+    const int pc = tid + kLmThreads * j;
+    const int row = (pc >> 2) < kLmRows ? (pc >> 2) : 0;
+    a_e[j] = pc < kLmAPieces ? lds_e[row] : -1;
+    a_n[j] = pc < kLmAPieces && row0 + row < R;
+  }
   auto load_a = [&](int g, u32x4_t (&areg)[kLmAPer]) __attribute__((always_inline)) {
     int tile, k0, K;
     bool bias;
@@ -143,11 +164,10 @@ __global__ __launch_bounds__(kLmThreads) void markov_lm_head_bf16(LmHeadParams p
 #pragma unroll
     for (int j = 0; j < kLmAPer; ++j) {
       const int pc = tid + kLmThreads * j;
-      const int row = (pc >> 2) < kLmRows ? (pc >> 2) : 0, k = k0 + 8 * (pc & 3);
-      const int n = row0 + row;
-      const int32_t e = lds_e[row];
-      const bool ok = g < G && pc < kLmAPieces && k < K && (bias ? e >= 0 : n < R);
-      const uint32_t off = !ok ? kBufferOob : bias ? 2u * (uint32_t)(e + k) : 2u * ((uint32_t)n * (uint32_t)d + (uint32_t)k);
+      const int k = k0 + 8 * (pc & 3);
+      const uint32_t n = (uint32_t)(row0 + (pc >> 2));
+      const bool ok = g < G && k < K && (bias ? a_e[j] >= 0 : a_n[j]);
+      const uint32_t off = !ok ? kBufferOob : bias ? 2u * (uint32_t)(a_e[j] + k) : 2u * (n * (uint32_t)d + (uint32_t)k);
       areg[j] = __builtin_amdgcn_raw_buffer_load_b128(bias ? rs_w1 : rs_h, off, 0, 0);
     }
   };
@@ -161,78 +181,99 @@ __global__ __launch_bounds__(kLmThreads) void markov_lm_head_bf16(LmHeadParams p
   };
 
   f32x4_t acc[5][4];
-  uint32_t bias_pk[5][4][2];  // the rounded bias of each block, two bf16 per word
 #pragma unroll
   for (int i = 0; i < 5; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      bias_pk[i][j][0] = bias_pk[i][j][1] = 0u;
-    }
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // in flight before the loop: B of chunks 0..3, A of chunks 0..1; chunk
-  // g's step then issues A of g+2 and B of g+4 (kLmOps operations)
-  u32x4_t a0[kLmAPer], a1[kLmAPer];
-  issue_b(0);
-  issue_b(1);
-  load_a(0, a0);
-  issue_b(2);
-  load_a(1, a1);
-  issue_b(3);
-  int epi_left = 0;  // steps whose waits still see an epilogue's 20 stores
-
-  // one chunk's products (A of chunk g is in `areg`, register set g % 2)
-  auto mstep = [&](int g, u32x4_t (&areg)[kLmAPer]) __attribute__((always_inline)) {
-    // A of chunk g (and B of chunks g and g+1, issued before it) complete;
-    // the operations issued after them may stay in flight: B of g+2 and
-    // one step's worth, plus an epilogue's stores among them
-    if (epi_left > 0) {
-      wait_vmcnt<1 + kLmOps + kLmEpiStores>();
-      --epi_left;
-    } else {
-      wait_vmcnt<1 + kLmOps>();
-    }
-    store_a(g, areg);
-    load_a(g + 2, areg);
-    lds_barrier();
-    issue_b(g + 4);
+  // Operand fragments of one chunk: fa the four 16-column blocks of B, fb
+  // the five 16-row blocks of A of the wave's 80 x 64 part of the tile.
+  struct Frags {
+    bf16x8_t fa[4], fb[5];
+  };
+  auto read_frags = [&](int g, Frags& f) __attribute__((always_inline)) {
     const uint32_t stage = (uint32_t)(g % kLmStages) * kLmStageB;
     const uint32_t abuf = (uint32_t)(g & 1) * kLmStageA;
-    bf16x8_t fa[4], fb[5];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = 64 * wc + 16 * j + (lane & 15);
-      fa[j] = *(const bf16x8_t*)&lds_b[stage + lm_swz(col, lane >> 4)];
+      f.fa[j] = *(const bf16x8_t*)&lds_b[stage + lm_swz(col, lane >> 4)];
     }
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
       const int row = 80 * wr + 16 * i + (lane & 15);
-      fb[i] = *(const bf16x8_t*)&lds_a[abuf + lm_swz(row, lane >> 4)];
-    }
-#pragma unroll
-    for (int i = 0; i < 5; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[j], fb[i], acc[i][j], 0, 0, 0);
-  };
-  // chunks g0 .. g0 + n - 1 (g0 and n even): register set a0 for even
-  // chunks, a1 for odd ones
-  auto span = [&](int g0, int n) __attribute__((always_inline)) {
-    for (int g = g0; g < g0 + n; g += 2) {
-      mstep(g, a0);
-      mstep(g + 1, a1);
+      f.fb[i] = *(const bf16x8_t*)&lds_a[abuf + lm_swz(row, lane >> 4)];
     }
   };
 
+  // Pipeline.  After the barrier of step g a wave issues, all independent
+  // of one another: B of chunk g+4 into the stage chunk g used, the
+  // fragment reads of chunk g+1, the LDS stores of A of chunk g+2 (into the
+  // buffer chunk g used) and the register loads of A of chunk g+4, and the
+  // products of chunk g on the fragments read a step earlier; so the LDS
+  // and memory traffic of the next chunks runs under the matrix work of
+  // this one, one barrier a chunk.  A of chunk c sits in register set c % 2
+  // from its load (four steps ahead) to its store (two steps ahead).
+  u32x4_t a0[kLmAPer], a1[kLmAPer];
+  issue_b(0);
+  load_a(0, a0);
+  load_a(1, a1);
+#pragma unroll
+  for (int j = 1; j < kLmStages; ++j) issue_b(j);
+  wait_vmcnt<0>();  // once: B of chunks 0..3, A of chunks 0 and 1
+  store_a(0, a0);
+  store_a(1, a1);
+  load_a(2, a0);
+  load_a(3, a1);
+  lds_barrier();
+  Frags f0, f1;
+  read_frags(0, f0);
+  int epi_left = 0;  // steps whose waits still see an epilogue's 20 stores
+
+  // step g: `aset` holds A of chunk g+2 (set g % 2), `cur` the fragments of
+  // chunk g; `nxt` receives those of chunk g+1
+  auto step = [&](int g, u32x4_t (&aset)[kLmAPer], Frags& cur, Frags& nxt) __attribute__((always_inline)) {
+    // B of chunk g+1 (issued three steps ago) has landed; two steps of
+    // operations and A of the step before (and an epilogue's stores) may
+    // stay in flight
+    if (epi_left > 0) {
+      wait_vmcnt<2 * kLmOps + kLmAPer + kLmEpiStores>();
+      --epi_left;
+    } else {
+      wait_vmcnt<2 * kLmOps + kLmAPer>();
+    }
+    lds_barrier();
+    issue_b(g + kLmStages);
+    read_frags(g + 1, nxt);
+    store_a(g + 2, aset);
+    load_a(g + 4, aset);
+#pragma unroll
+    for (int i = 0; i < 5; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.fa[j], cur.fb[i], acc[i][j], 0, 0, 0);
+  };
+  // chunks g0 .. g0 + n - 1 (g0 and n even)
+  auto span = [&](int g0, int n) __attribute__((always_inline)) {
+    for (int g = g0; g < g0 + n; g += 2) {
+      step(g, a0, f0, f1);
+      step(g + 1, a1, f1, f0);
+    }
+  };
+
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  unsigned char* const my_bias = &lds_bias[wave * kLmBiasBytes + lane * 8];
   for (int t = 0; t < my_tiles; ++t) {
     const int gt = t * C;
     span(gt, nb);
-    // the bias of the tile: the Linear's bf16 output; the head starts at zero
+    // the bias of the tile: the Linear's bf16 output, into the wave's LDS
+    // region; the head starts at zero
 #pragma unroll
     for (int i = 0; i < 5; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        bias_pk[i][j][0] = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-        bias_pk[i][j][1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+        *(u32x2_t*)(my_bias + (i * 4 + j) * 512) =
+            u32x2_t{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
         acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       }
     span(gt + nb, C - nb);
@@ -244,15 +285,15 @@ __global__ __launch_bounds__(kLmThreads) void markov_lm_head_bf16(LmHeadParams p
       const int n = row0 + 80 * wr + 16 * i + (lane & 15);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        const u32x2_t bp = *(const u32x2_t*)(my_bias + (i * 4 + j) * 512);
         const int v = tile * kLmCols + 64 * wc + 16 * j + 4 * (lane >> 4);
-        const uint32_t b0 = bias_pk[i][j][0], b1 = bias_pk[i][j][1];
-        const u32x4_t o = u32x4_t{__float_as_uint(acc[i][j][0] + bf16_lo(b0)), __float_as_uint(acc[i][j][1] + bf16_hi(b0)),
-                                  __float_as_uint(acc[i][j][2] + bf16_lo(b1)), __float_as_uint(acc[i][j][3] + bf16_hi(b1))};
+        const u32x4_t o = u32x4_t{__float_as_uint(acc[i][j][0] + bf16_lo(bp.x)), __float_as_uint(acc[i][j][1] + bf16_hi(bp.x)),
+                                  __float_as_uint(acc[i][j][2] + bf16_lo(bp.y)), __float_as_uint(acc[i][j][3] + bf16_hi(bp.y))};
         buffer_store16(rs_out, (n < R && v < V) ? ((uint32_t)n * (uint32_t)V + (uint32_t)v) * 4u : kBufferOob, o);
         acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       }
     }
-    epi_left = 2;
+    epi_left = kLmStages - 1;
   }
   wait_vmcnt<0>();
 }
