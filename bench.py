@@ -136,6 +136,30 @@ def copy_ceiling(torch, np, bw):
             "torch_copy_GBps": nbytes / (ms_t * 1e-3) / 1e9}
 
 
+def mfma_ceiling(torch, np, bw, iters=4000):
+    """The matrix-core throughput each bf16 product form reaches on this
+    device, from libdspark_bandwidth.so's probe (eight independent
+    accumulators per wave, 16 waves per CU on every CU; 2 warm-up and 5
+    timed launches, median): the kernels here use the 16 x 16 x 32 form."""
+    import ctypes
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    waves = 16
+    out = torch.empty(cus * waves * 64, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for form, name, flops in ((0, "v_mfma_f32_16x16x32_bf16", 16384), (1, "v_mfma_f32_32x32x16_bf16", 32768)):
+        def run(i):
+            st = bw.dspark_bandwidth_mfma(ctypes.c_void_p(out.data_ptr()), out.numel() * 4, form, waves, iters, stream)
+            if st != 0:
+                raise RuntimeError(f"dspark_bandwidth_mfma: status {st}")
+        _, per = time_calls(run, 1, 5, 2, torch)
+        ms = float(np.median(per))
+        res[name] = cus * waves * iters * 8 * flops / (ms * 1e-3) / 1e12
+    return {"unit": "TFLOP/s", "kind": "bf16 product throughput per instruction form (dspark_bandwidth_mfma)",
+            **res, "frac_of_peak_16x16x32": res["v_mfma_f32_16x16x32_bf16"] / BF16_MFMA_PEAK_TFLOPS,
+            "frac_of_peak_32x32x16": res["v_mfma_f32_32x32x16_bf16"] / BF16_MFMA_PEAK_TFLOPS}
+
+
 def same_size_ceiling(torch, np, bw, read_bytes, write_bytes, steps=200, warmup=100):
     """The read-mix probe at one launch's own bytes (read_bytes read,
     write_bytes written), timed like the kernel: back to back, one event pair
@@ -547,6 +571,14 @@ def main():
         if unknown:
             raise SystemExit(f"unknown workloads: {unknown}")
         result["other_workloads"] = {n: measure_extra(n, rmd, wl, torch, np) for n in names}
+        # matrix-core fractions also against what their instruction form
+        # reaches here (every bf16 product kernel uses 16 x 16 x 32)
+        mc = mfma_ceiling(torch, np, _lib.load_bandwidth())
+        result["mfma_ceiling"] = mc
+        for res in result["other_workloads"].values():
+            for key in ("mfma", "roofline"):
+                if key in res and res[key].get("unit") == "TFLOP/s":
+                    res[key]["frac_of_instruction_ceiling"] = res[key]["achieved"] / mc["v_mfma_f32_16x16x32_bf16"]
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, np)
     print(json.dumps(result))

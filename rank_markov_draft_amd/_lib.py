@@ -117,8 +117,9 @@ _bw = None
 
 
 def load_bandwidth():
-    """The streaming probes the benchmark times as HBM ceilings (not part of
-    the head): dspark_bandwidth_copy and dspark_bandwidth_read_mix."""
+    """The probes the benchmark times as HBM and matrix-core ceilings (not
+    part of the head): dspark_bandwidth_copy, dspark_bandwidth_read_mix and
+    dspark_bandwidth_mfma."""
     global _bw
     if _bw is None:
         if not os.path.exists(BANDWIDTH_LIB_PATH):
@@ -129,6 +130,8 @@ def load_bandwidth():
         L.dspark_bandwidth_copy.restype = i32
         L.dspark_bandwidth_read_mix.argtypes = [p, sz, p, sz, p]
         L.dspark_bandwidth_read_mix.restype = i32
+        L.dspark_bandwidth_mfma.argtypes = [p, sz, i32, i32, i32, p]
+        L.dspark_bandwidth_mfma.restype = i32
         _bw = L
     return _bw
 

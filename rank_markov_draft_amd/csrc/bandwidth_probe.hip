@@ -12,6 +12,13 @@
 //       the head's read : write mix (base logits and W2 in, corrected out).
 // Both use the streaming (non-temporal) cache policy of the head's logit
 // traffic, 16-byte vectors, and keep four vectors per thread in flight.
+//   dspark_bandwidth_mfma(out, out_bytes, form, waves_per_cu, iters, stream)
+//       the matrix-core counterpart: every wave of waves_per_cu (4, 8 or 16)
+//       per CU runs `iters` rounds of eight independent bf16 products of
+//       one form (0: v_mfma_f32_16x16x32_bf16, 16384 flops; 1:
+//       v_mfma_f32_32x32x16_bf16, 32768 flops) and writes one float per
+//       thread to out (out_bytes >= CUs * waves_per_cu * 64 * 4), so the
+//       caller can time each form's throughput.
 // Buffers: device memory, 16-byte aligned, sizes multiples of 16, not
 // overlapping.  Returns 0, 1 for an invalid argument, 4 for a launch failure.
 // Asynchronous on `stream` (a hipStream_t).
@@ -66,6 +73,44 @@ __global__ __launch_bounds__(256) void read_mix_kernel(const u32x4_t* __restrict
   }
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// eight independent accumulators per wave, operands fixed in registers
+template <int FORM>
+__global__ __launch_bounds__(256) void mfma_probe_kernel(float* out, int iters) {
+  bf16x8_t a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (float)(threadIdx.x + i));
+    b[i] = (__bf16)(0.002f * (float)i);
+  }
+  float sum = 0.0f;
+  if constexpr (FORM == 0) {
+    f32x4_t acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) sum += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  } else {
+    f32x16_t acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[c][e] = 0.0f;
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sum += acc[c][e];
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = sum;
+}
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -109,6 +154,22 @@ int dspark_bandwidth_read_mix(void* dst, size_t dst_bytes, const void* src, size
     case 4: hipLaunchKernelGGL(read_mix_kernel<4>, grid, block, 0, s, (const u32x4_t*)src, m, (u32x4_t*)dst, n); break;
     default: return 1;
   }
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int dspark_bandwidth_mfma(float* out, size_t out_bytes, int form, int waves_per_cu, int iters, void* stream) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 4;
+  if (!out || (form != 0 && form != 1) || (waves_per_cu != 4 && waves_per_cu != 8 && waves_per_cu != 16) ||
+      iters < 1)
+    return 1;
+  const int blocks = cus * waves_per_cu / 4;
+  if (out_bytes < (size_t)blocks * 256 * sizeof(float)) return 1;
+  hipStream_t s = (hipStream_t)stream;
+  if (form == 0) hipLaunchKernelGGL(mfma_probe_kernel<0>, dim3(blocks), dim3(256), 0, s, out, iters);
+  else hipLaunchKernelGGL(mfma_probe_kernel<1>, dim3(blocks), dim3(256), 0, s, out, iters);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
