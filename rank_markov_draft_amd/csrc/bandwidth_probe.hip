@@ -158,13 +158,13 @@ int dspark_bandwidth_read_mix(void* dst, size_t dst_bytes, const void* src, size
 }
 
 int dspark_bandwidth_mfma(float* out, size_t out_bytes, int form, int waves_per_cu, int iters, void* stream) {
+  if (!out || !aligned16(out) || (form != 0 && form != 1) ||
+      (waves_per_cu != 4 && waves_per_cu != 8 && waves_per_cu != 16) || iters < 1)
+    return 1;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     return 4;
-  if (!out || (form != 0 && form != 1) || (waves_per_cu != 4 && waves_per_cu != 8 && waves_per_cu != 16) ||
-      iters < 1)
-    return 1;
   const int blocks = cus * waves_per_cu / 4;
   if (out_bytes < (size_t)blocks * 256 * sizeof(float)) return 1;
   hipStream_t s = (hipStream_t)stream;

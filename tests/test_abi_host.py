@@ -238,9 +238,10 @@ def test_backward_argument_errors(L):
 
 
 def test_bandwidth_probe_argument_errors():
-    """The bandwidth probes (a separate library, not the head's ABI) take
-    16-byte aligned, non-overlapping buffers and whole 16-byte pieces; zero
-    bytes is a no-op.  Every call here is rejected before any launch."""
+    """The bandwidth and matrix-core probes (a separate library, not the
+    head's ABI) take 16-byte aligned, non-overlapping buffers and whole
+    16-byte pieces; zero bytes is a no-op.  Every call here is rejected
+    before any launch or device query."""
     from rank_markov_draft_amd import _lib
     bw = _lib.load_bandwidth()
     a, b = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
@@ -257,6 +258,13 @@ def test_bandwidth_probe_argument_errors():
     assert bw.dspark_bandwidth_read_mix(b, 4096, a, 4096 * 5, None) == bad               # more than four passes
     assert bw.dspark_bandwidth_read_mix(b, 4096, a, 4100, None) == bad
     assert bw.dspark_bandwidth_read_mix(ctypes.c_void_p(0x100800), 4096, a, 8192, None) == bad
+    # the matrix-core probe: one of two product forms, 4, 8 or 16 waves per
+    # CU, at least one round, an aligned output buffer
+    assert bw.dspark_bandwidth_mfma(None, 1 << 20, 0, 16, 10, None) == bad
+    assert bw.dspark_bandwidth_mfma(ctypes.c_void_p(0x100004), 1 << 20, 0, 16, 10, None) == bad
+    assert bw.dspark_bandwidth_mfma(a, 1 << 20, 2, 16, 10, None) == bad
+    assert bw.dspark_bandwidth_mfma(a, 1 << 20, 1, 12, 10, None) == bad
+    assert bw.dspark_bandwidth_mfma(a, 1 << 20, 0, 16, 0, None) == bad
 
 
 def test_product_abi_has_no_benchmark_utility(L):
